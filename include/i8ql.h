@@ -1,0 +1,197 @@
+/*
+ * i8ql.h — C ABI of the int8 quantized linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow three web pages:
+ *   [P5a]   "Phase 5a: int8 weight-only quantization" (dispatch pull request #5), Summary.
+ *   [W8A8]  "feat(quantization): support compressed-tensors W8A8 and mixed modules"
+ *           (InfiniLM pull request #582), section "Design and Supported Execution Scheme".
+ *   [Day6]  "Day 6 — Quantize It Yourself", section "The mechanism", blocks 1 and 5.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device pointers must point to device memory (or memory the device
+ *     can access); host-side arguments are plain integers and enums.
+ *   - Every tensor is dense and row-major with no padding: a [R, C] tensor has row stride C
+ *     elements.  Weights use the nn.Linear layout [N, K] (output channel, input channel);
+ *     activations are [M, K] (one row per token).  Y = X * W^T has shape [M, N].
+ *   - Ownership: the caller owns every buffer.  The library allocates no device or host
+ *     memory, keeps no pointer after a call returns and holds no mutable global state apart
+ *     from the thread-local error slot read by i8ql_last_hip_error().
+ *   - Asynchrony: a call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (a hipStream_t passed as void*; NULL selects the null stream) and returns.
+ *     It never synchronizes.  Results are ready once the stream reaches that point.
+ *   - Errors fail closed: an unsupported dtype, shape, alignment or combination returns an
+ *     error code before any device work, and the outputs are left untouched.  There is no
+ *     fallback path.  Only I8QL_ERR_HIP can follow a launch attempt.
+ *   - A zero dimension (m, n, t or the row count) makes the call a no-op returning I8QL_OK.
+ *     Negative dimensions return I8QL_ERR_SHAPE.
+ *   - Outputs must not overlap inputs or each other.
+ *   - Results are deterministic: the same inputs give bitwise the same outputs on every
+ *     call (no atomics take part in any output).
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified (but in-bounds) results.
+ */
+#ifndef I8QL_H
+#define I8QL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  I8QL_F32 = 0,  /* IEEE binary32 */
+  I8QL_BF16 = 1, /* bfloat16 (upper half of binary32) */
+  I8QL_F16 = 2,  /* IEEE binary16 */
+  I8QL_I8 = 3,   /* signed 8-bit integer */
+  I8QL_I32 = 4   /* signed 32-bit integer */
+} i8ql_dtype;
+
+typedef enum {
+  I8QL_OK = 0,
+  I8QL_ERR_NULL = 1,        /* a required pointer is NULL */
+  I8QL_ERR_SHAPE = 2,       /* a dimension is negative, or k < 1, or a size overflows */
+  I8QL_ERR_DTYPE = 3,       /* a dtype this entry point does not accept */
+  I8QL_ERR_ALIGN = 4,       /* GEMM: k % 16 != 0, or an operand base pointer is not 16-byte aligned */
+  I8QL_ERR_K_TOO_LARGE = 5, /* w8a8_gemm: k > 133144, so an int32 accumulator could overflow */
+  I8QL_ERR_ARG = 6,         /* invalid combination: bias with I32 output, topk < 1, experts < 1, ... */
+  I8QL_ERR_HIP = 7          /* the HIP runtime reported an error; see i8ql_last_hip_error() */
+} i8ql_status;
+
+/* Largest K for which k * 127 * 127 fits in a signed 32-bit accumulator (133144 * 16129 =
+ * 2147479576 < 2^31). */
+#define I8QL_W8A8_MAX_K 133144
+
+/*
+ * quantize_per_channel_int8 — symmetric per-output-channel int8 weight quantization.
+ *
+ * Defines: [Day6] block 1 (codes q = clamp(round(w / s)), shared scale s = absmax of the
+ * group / largest representable code, reconstruction w ~ s * q, one scale per output
+ * channel); [P5a] Summary (the quantizer of the grouped int8 kernel; its second bug fix puts
+ * the arithmetic in float32, its third limits the zero-channel guard to all-zero channels);
+ * [W8A8] "Design and Supported Execution Scheme" (static symmetric INT8 per-channel weights).
+ *
+ * For each row r of w[n, k] (one output channel):
+ *   amax = max_j |w[r, j]|  (inputs widened exactly to float32)
+ *   s    = amax / 127        (float32 division, round to nearest even)
+ *   if s == 0:  scale_out[r] = 1.0f and q_out[r, :] = 0      (all-zero channel guard)
+ *   else:       q_out[r, j] = clamp(rne(w[r, j] / s), -127, 127) (float32 division per
+ *               element, ties to even); scale_out[r] = s.
+ *   The code -128 is never produced.
+ *
+ * w          device, [n, k] of w_dtype in {I8QL_F32, I8QL_BF16, I8QL_F16}, element-aligned.
+ * q_out      device, [n, k] int8.       scale_out  device, [n] float32.
+ * n >= 0 rows, k >= 1 columns; n * k < 2^62.
+ * Errors: NULL pointer -> I8QL_ERR_NULL; n < 0 or k < 1 -> I8QL_ERR_SHAPE; other dtype ->
+ * I8QL_ERR_DTYPE; a pointer not aligned to its element size -> I8QL_ERR_ALIGN.
+ */
+i8ql_status quantize_per_channel_int8(const void* w, i8ql_dtype w_dtype, int64_t n, int64_t k,
+                                      int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * quantize_per_token_int8 — dynamic symmetric per-token int8 activation quantization.
+ *
+ * Defines: [W8A8] "Design and Supported Execution Scheme" (dynamic symmetric INT8 per-token
+ * input activations); [Day6] block 5 (activations quantized on the fly with per-token
+ * dynamic scales) and "Reading-share post" fact 2 (each token's scale is computed at run
+ * time, an extra step of every forward pass).
+ *
+ * Exactly the row rule of quantize_per_channel_int8, applied to each row (token) of x[m, k]:
+ * one float32 scale per token.  Arguments as above with m rows.
+ */
+i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m, int64_t k,
+                                    int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * w8a8_gemm — int8 x int8 GEMM with int32 accumulation and a fused scale epilogue.
+ *
+ * Defines: [W8A8] "Design and Supported Execution Scheme" (per-channel int8 weights,
+ * per-token int8 activations, no quantization of the output); [Day6] block 5 (W8A8: both
+ * operands 8-bit, the product runs on 8-bit matrix units).  Biases travel with the output
+ * channels ([W8A8] Summary: scales and biases shard together by output channel).
+ *
+ *   acc[i, j] = sum_c xq[i, c] * wq[j, c]                  (exact, int32)
+ *   y_dtype == I8QL_I32 :  y[i, j] = acc[i, j]              (bias must be NULL)
+ *   otherwise           :  y[i, j] = ((float)acc * x_scale[i]) * w_scale[j] (+ bias[j]),
+ *                          float32 arithmetic, then stored as float32 (I8QL_F32) or rounded
+ *                          to nearest even bfloat16 (I8QL_BF16).
+ *
+ * xq       device, [m, k] int8, 16-byte aligned.   x_scale  device, [m] float32.
+ * wq       device, [n, k] int8, 16-byte aligned.   w_scale  device, [n] float32.
+ * bias     device, [n] float32, or NULL.
+ * y        device, [m, n] of y_dtype in {I8QL_BF16, I8QL_F32, I8QL_I32}.
+ * m, n >= 0; 16 <= k <= 133144 and k % 16 == 0.
+ * Errors: NULL (x_scale/w_scale may be NULL only with I32 output) -> I8QL_ERR_NULL;
+ * negative m/n, k < 1 -> I8QL_ERR_SHAPE; k % 16 or misaligned xq/wq -> I8QL_ERR_ALIGN;
+ * k > 133144 -> I8QL_ERR_K_TOO_LARGE; other y_dtype -> I8QL_ERR_DTYPE; bias with I32 ->
+ * I8QL_ERR_ARG.
+ */
+i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
+                      int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * w8a16_gemm — weight-only int8 GEMM for decode: int8 weights are dequantized in registers
+ * and multiplied with 16-bit activations.
+ *
+ * Defines: [P5a] Summary (weight-only int8 saves memory bandwidth, not arithmetic);
+ * [Day6] block 5 (W4A16-style weight-only: codes are expanded to bf16 inside the kernel,
+ * the product runs at 16 bits, a pure bandwidth win that helps decode).
+ *
+ *   y[i, j] = w_scale[j] * sum_c x[i, c] * wq[j, c]  (+ bias[j])
+ *   Each product of a bf16 value and an int8 code is exact; the sum is accumulated in
+ *   float32 (its order is unspecified but fixed); stored as float32 or rne bfloat16.
+ *
+ * x        device, [m, k] bfloat16, 16-byte aligned.
+ * wq       device, [n, k] int8, 16-byte aligned.   w_scale  device, [n] float32.
+ * bias     device, [n] float32, or NULL.           y        device, [m, n] of y_dtype.
+ * y_dtype in {I8QL_BF16, I8QL_F32}.  m, n >= 0; k >= 16, k % 16 == 0.  Any m is accepted;
+ * the kernel is built for m <= 16 and stays correct (slower per row) above it.
+ * Errors as for w8a8_gemm (no k upper limit: float32 accumulation).
+ */
+i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
+                       void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                       void* stream);
+
+/*
+ * grouped_w8a16_gemm — one launch of weight-only int8 GEMMs over routed experts, with the
+ * expert-grouped dispatch done inside the kernel.
+ *
+ * Defines: [P5a] Summary (a grouped GEMM over all experts of a mixture-of-experts block with
+ * per-output-channel int8 expert weights, stacked into one shared tensor per projection).
+ *
+ * Assignment p = i * topk + j (token i, routing slot j) uses expert e = expert_ids[i, j]:
+ *   xrow(p)  = x[i, :]  when x_per_assignment == 0  (gate/up projections: token rows)
+ *            = x[p, :]  when x_per_assignment == 1  (down projection: one row per assignment)
+ *   if 0 <= e < num_experts:  y[p, c] = w_scale[e, c] * sum_d xrow(p)[d] * wq[e, c, d]
+ *   else:                     y[p, :] = 0   (a caller-contract violation, made visible)
+ *   float32 accumulation, stored as float32 or rne bfloat16.  Always-on shared experts are
+ *   passed as extra experts appended to every token's id list.
+ *
+ * x           device, bfloat16, [t, k] (x_per_assignment == 0) or [t * topk, k] (== 1),
+ *             16-byte aligned.
+ * wq          device, [num_experts, n, k] int8, 16-byte aligned.
+ * w_scale     device, [num_experts, n] float32.
+ * expert_ids  device, [t, topk] int32.
+ * y           device, [t * topk, n] of y_dtype in {I8QL_BF16, I8QL_F32}.
+ * t, n >= 0; 1 <= topk <= 64; t * topk <= 65536; 1 <= num_experts <= 65535;
+ * k >= 16, k % 16 == 0.
+ * Errors: as for w8a16_gemm; x_per_assignment not 0/1, topk or num_experts out of range ->
+ * I8QL_ERR_ARG; t * topk > 65536 -> I8QL_ERR_SHAPE.
+ */
+i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t* wq,
+                               const float* w_scale, int64_t num_experts,
+                               const int32_t* expert_ids, int64_t t, int64_t topk, void* y,
+                               i8ql_dtype y_dtype, int64_t n, int64_t k, void* stream);
+
+/* Host: a static, human-readable name for a status code ("I8QL_OK", ...). */
+const char* i8ql_status_string(i8ql_status s);
+
+/* Host: the hipError_t (as int) recorded by the most recent call on this thread that
+ * returned I8QL_ERR_HIP, or 0. */
+int i8ql_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8QL_H */

@@ -1,0 +1,214 @@
+/*
+ * ref.c — CPU oracle of the int8 quantized linear layer: plain loops, written from the pages.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark may load or call it.  It shares no code with the HIP library.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.  Float32 work is
+ * IEEE binary32 with round to nearest even and no flush-to-zero (x86-64 SSE defaults).
+ * OpenMP only splits independent output rows across threads; it changes no arithmetic.
+ *
+ * Mutants (teeth for the pins; never built into the normal library):
+ *   -DREF_MUTANT_BF16_ARITH  do the quantizer arithmetic in bfloat16, the first precision
+ *                            bug that "Phase 5a: int8 weight-only quantization" (Summary)
+ *                            reports;
+ *   -DREF_MUTANT_FLOOR_SCALE floor every small scale at a dtype-dependent minimum, the
+ *                            second bug that the same Summary reports.
+ */
+#include "ref.h"
+
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <string.h>
+
+void ref_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int ref_get_threads(void) { return omp_get_max_threads(); }
+
+/* ---- exact widening of the input formats to float32 ---------------------------------- */
+
+static float bf16_to_f32(uint16_t b) {
+  /* bfloat16 is the upper half of a binary32 word. */
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float f16_to_f32(uint16_t h) {
+  /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  float mag;
+  if (e == 0)
+    mag = ldexpf((float)f, -24); /* subnormal: f * 2^-24 */
+  else if (e == 31)
+    mag = f ? NAN : INFINITY;
+  else
+    mag = ldexpf((float)(f | 0x400), e - 25); /* (1024 + f) * 2^(e - 25) */
+  return sign ? -mag : mag;
+}
+
+static float load_elem(const void* a, int dtype, int64_t i) {
+  switch (dtype) {
+    case REF_F32: return ((const float*)a)[i];
+    case REF_BF16: return bf16_to_f32(((const uint16_t*)a)[i]);
+    default: return f16_to_f32(((const uint16_t*)a)[i]);
+  }
+}
+
+/* ---- the quantizer ---------------------------------------------------------------------- */
+
+/* Round to the nearest integer, ties to the even one.  |t| < 2^23, so t - floor(t) is exact. */
+static float round_half_even(float t) {
+  float f = floorf(t);
+  float d = t - f;
+  if (d > 0.5f) return f + 1.0f;
+  if (d < 0.5f) return f;
+  return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+}
+
+#ifdef REF_MUTANT_BF16_ARITH
+/* Round a float32 to the nearest bfloat16 (ties to even), kept as float32. */
+static float to_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u = (u + 0x7fffu + lsb) & 0xffff0000u;
+  memcpy(&x, &u, sizeof x);
+  return x;
+}
+#endif
+
+/*
+ * One scale per row, the symmetric absmax rule of "Day 6 — Quantize It Yourself" (The
+ * mechanism, block 1): s = absmax / largest code, q = clamp(round(w / s)).  The grid is
+ * symmetric, so the largest code is 127 and -128 is never used.  "Phase 5a: int8
+ * weight-only quantization" (Summary, bug fixes) fixes two details: every step is float32
+ * arithmetic, whatever the weight's own dtype, and the guard against 0/0 applies only to a
+ * channel whose scale is zero; its stored scale is 1 and its codes are 0.
+ */
+int ref_quantize_rows(const void* a, int dtype, int64_t r, int64_t k, int8_t* q, float* s) {
+  if (dtype != REF_F32 && dtype != REF_BF16 && dtype != REF_F16) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < r; ++row) {
+    const int64_t base = row * k;
+    float amax = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      float v = fabsf(load_elem(a, dtype, base + j));
+      if (v > amax) amax = v;
+    }
+    float scale = amax / 127.0f;
+#ifdef REF_MUTANT_BF16_ARITH
+    if (dtype != REF_F32) scale = to_bf16(scale);
+#endif
+#ifdef REF_MUTANT_FLOOR_SCALE
+    {
+      /* smallest normal number of the input format, divided by the largest code */
+      float floor_v = (dtype == REF_F16) ? ldexpf(1.0f, -14) / 127.0f
+                                          : ldexpf(1.0f, -126) / 127.0f;
+      if (scale < floor_v) scale = floor_v;
+    }
+#endif
+    if (scale == 0.0f) {
+      s[row] = 1.0f;
+      for (int64_t j = 0; j < k; ++j) q[base + j] = 0;
+      continue;
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      float t = load_elem(a, dtype, base + j) / scale;
+#ifdef REF_MUTANT_BF16_ARITH
+      if (dtype != REF_F32) t = to_bf16(t);
+#endif
+      float c = round_half_even(t);
+      if (c > 127.0f) c = 127.0f;
+      if (c < -127.0f) c = -127.0f;
+      q[base + j] = (int8_t)c;
+    }
+    s[row] = scale;
+  }
+  return 0;
+}
+
+/* ---- W8A8 ------------------------------------------------------------------------------- */
+
+/*
+ * int8 x int8 products summed exactly, then the per-token scale, the per-channel scale and
+ * the bias ("feat(quantization): support compressed-tensors W8A8 and mixed modules", Design
+ * and Supported Execution Scheme: per-channel weights, per-token activations, no output
+ * quantization).  The sum is formed in int64 and checked against the int32 range.
+ */
+int ref_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+             const float* bias, int64_t m, int64_t n, int64_t k, int32_t* acc, double* y) {
+  int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+  for (int64_t i = 0; i < m; ++i) {
+    const int8_t* xr = xq + i * k;
+    for (int64_t j = 0; j < n; ++j) {
+      const int8_t* wr = wq + j * k;
+      int64_t sum = 0;
+      for (int64_t c = 0; c < k; ++c) sum += (int64_t)xr[c] * (int64_t)wr[c];
+      if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+      acc[i * n + j] = (int32_t)sum;
+      if (y) {
+        double v = (double)sum * (double)x_scale[i] * (double)w_scale[j];
+        if (bias) v += (double)bias[j];
+        y[i * n + j] = v;
+      }
+    }
+  }
+  return overflow ? -1 : 0;
+}
+
+/* ---- W8A16 ------------------------------------------------------------------------------ */
+
+/*
+ * Weight-only: y = x * dequant(W)^T with dequant(W)[j, c] = w_scale[j] * wq[j, c]
+ * ("Phase 5a: int8 weight-only quantization", Summary; "Day 6 — Quantize It Yourself", The
+ * mechanism, block 5).  Each bf16 * int8 product is exact in double; the sum is double.
+ */
+void ref_w8a16(const uint16_t* x, const int8_t* wq, const float* w_scale, const float* bias,
+               int64_t m, int64_t n, int64_t k, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    const uint16_t* xr = x + i * k;
+    for (int64_t j = 0; j < n; ++j) {
+      const int8_t* wr = wq + j * k;
+      double sum = 0.0;
+      for (int64_t c = 0; c < k; ++c) sum += (double)bf16_to_f32(xr[c]) * (double)wr[c];
+      double v = (double)w_scale[j] * sum;
+      if (bias) v += (double)bias[j];
+      y[i * n + j] = v;
+    }
+  }
+}
+
+/* ---- grouped W8A16 ---------------------------------------------------------------------- */
+
+/*
+ * Grouped GEMM over routed experts ("Phase 5a: int8 weight-only quantization", Summary):
+ * assignment p = (token i, slot j) multiplies its input row by the stacked weights of expert
+ * ids[i, j].  An id outside [0, e) yields a zero row.
+ */
+void ref_grouped_w8a16(const uint16_t* x, int x_per_assignment, const int8_t* wq,
+                       const float* w_scale, int64_t e, const int32_t* ids, int64_t t,
+                       int64_t topk, int64_t n, int64_t k, double* y) {
+  const int64_t rows = t * topk;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < rows; ++p) {
+    const int64_t tok = p / topk;
+    const int32_t ex = ids[p];
+    const uint16_t* xr = x + (x_per_assignment ? p : tok) * k;
+    for (int64_t j = 0; j < n; ++j) {
+      if (ex < 0 || ex >= e) {
+        y[p * n + j] = 0.0;
+        continue;
+      }
+      const int8_t* wr = wq + ((int64_t)ex * n + j) * k;
+      double sum = 0.0;
+      for (int64_t c = 0; c < k; ++c) sum += (double)bf16_to_f32(xr[c]) * (double)wr[c];
+      y[p * n + j] = (double)w_scale[(int64_t)ex * n + j] * sum;
+    }
+  }
+}

@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle: checks against facts the pages and the mathematics fix.
+
+None of these re-types the oracle's formulas: they use exact rational brute force, Python
+big integers, numpy's independent float64/int64 matmuls, closed forms printed on the pages
+(tests/golden/), metamorphic identities, and deliberately wrong oracle builds (mutants)
+that the pins must reject.  Pages cited by title and section:
+
+* "Day 6 — Quantize It Yourself", The mechanism, block 1 (q = clamp(round(w/s)), s = absmax
+  over the largest code, w ~ s*q) and block 5 (W8A8 vs weight-only);
+* "Phase 5a: int8 weight-only quantization", Summary (float32 arithmetic fix with its
+  "1.5x the ideal bound", the all-zero-channel guard fix, 49.89% expert memory reduction);
+* "feat(quantization): support compressed-tensors W8A8 and mixed modules", Design and
+  Supported Execution Scheme (per-channel weights, per-token activations).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from int8_quantized_linear_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+H = 0.5 + 2.0 ** -16  # rounding bound in units of s: 1/2 plus the float32 quotient's slack
+
+
+# ---------------------------------------------------------------------------------------
+# exact helpers (rational arithmetic, independent of the oracle)
+
+def nearest_f32(fr: Fraction) -> np.float32:
+    """The float32 nearest to the rational ``fr``, ties to the even significand."""
+    c = np.float32(float(fr))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - fr),
+                                     int(np.array(v, np.float32).view(np.uint32)) & 1))
+
+
+def brute_row(row32: np.ndarray, all_codes: bool = True):
+    """Quantize one row by exhaustive search: correctly rounded float32 scale and quotient,
+    then the code nearest to the quotient among all 255 codes, ties to the even code."""
+    vals = [Fraction(float(v)) for v in row32]
+    amax = max(abs(v) for v in vals)
+    s = nearest_f32(amax / 127)
+    if s == 0:
+        return np.zeros(len(vals), np.int8), np.float32(1.0)
+    S = Fraction(float(s))
+    out = []
+    for v in vals:
+        T = Fraction(float(nearest_f32(v / S)))
+        if all_codes:
+            codes = range(-127, 128)
+        else:
+            f = int(np.floor(float(T)))
+            codes = [c for c in range(f - 1, f + 3) if -127 <= c <= 127] or [127 if T > 0 else -127]
+        out.append(min(codes, key=lambda c: (abs(T - c), c & 1)))
+    return np.array(out, np.int8), s
+
+
+def widen(a, dtype):
+    if dtype == "f32":
+        return np.asarray(a, np.float32)
+    if dtype == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return np.asarray(a, np.uint16).view(np.float16).astype(np.float32)
+
+
+def as_dtype(x32: np.ndarray, dtype: str):
+    if dtype == "f32":
+        return x32.astype(np.float32)
+    if dtype == "bf16":
+        return wl.bits16(wl.to_bf16(x32))
+    return wl.bits16(wl.to_f16(x32))
+
+
+# ---------------------------------------------------------------------------------------
+# P1  brute force on tiny rows
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_p1_brute_force_all_codes(ref, dtype):
+    g = wl.rng(11)
+    rows = as_dtype(g.standard_normal((48, 12), dtype=np.float32) *
+                    np.exp(g.uniform(-6, 3, size=(48, 1))).astype(np.float32), dtype)
+    q, s = ref.quantize_rows(rows, dtype)
+    w = widen(rows, dtype)
+    for r in range(w.shape[0]):
+        bq, bs = brute_row(w[r], all_codes=True)
+        assert s[r] == bs, r
+        np.testing.assert_array_equal(q[r], bq)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_p1_brute_force_many_rows(ref, dtype):
+    g = wl.rng(12)
+    x = g.standard_normal((600, 24), dtype=np.float32)
+    x[::7] *= 1e-3
+    x[::11, 3] *= 100.0
+    rows = as_dtype(x, dtype)
+    q, s = ref.quantize_rows(rows, dtype)
+    w = widen(rows, dtype)
+    for r in range(w.shape[0]):
+        bq, bs = brute_row(w[r], all_codes=False)
+        assert s[r] == bs, r
+        np.testing.assert_array_equal(q[r], bq)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_p1_exact_ties_go_to_even(ref, dtype):
+    # amax = 127 * 2^-7 makes s = 2^-7 exactly, so (c + 1/2) * 2^-7 gives quotient c + 1/2.
+    s = 2.0 ** -7
+    halves = np.array([0.5, 1.5, 2.5, 3.5, 62.5, 63.5, 125.5, 126.5], np.float64)
+    row = np.concatenate([[127.0], halves, -halves]) * s
+    rows = as_dtype(row[None, :].astype(np.float32), dtype)
+    assert np.array_equal(widen(rows, dtype)[0], row.astype(np.float32))
+    q, sc = ref.quantize_rows(rows, dtype)
+    assert sc[0] == np.float32(s)
+    even = np.array([0, 2, 2, 4, 62, 64, 126, 126])
+    np.testing.assert_array_equal(q[0], np.concatenate([[127], even, -even]))
+    bq, _ = brute_row(widen(rows, dtype)[0])
+    np.testing.assert_array_equal(q[0], bq)
+
+
+def test_p1_near_ties_and_tiny_scales(ref):
+    s = np.float32(2.0 ** -7)
+    near = []
+    for c in (0.5, 1.5, 64.5, 126.5):
+        v = np.float32(c * float(s))
+        near += [np.nextafter(v, np.float32(-1)), np.nextafter(v, np.float32(2))]
+    rows = [np.array([127 * float(s)] + near, np.float32)]
+    # subnormal magnitudes: scale underflows to zero (guard) or stays a tiny subnormal
+    rows.append(np.array([1e-44, -5e-45] + [0.0] * 8, np.float32))
+    rows.append(np.array([3 * 2.0 ** -126, -2.0 ** -127] + [1e-40] * 8, np.float32))
+    for row in rows:
+        q, sc = ref.quantize_rows(row[None, :], "f32")
+        bq, bs = brute_row(row)
+        assert sc[0] == bs
+        np.testing.assert_array_equal(q[0], bq)
+
+
+def test_f16_and_bf16_widening_is_exact(ref):
+    # every finite binary16 pattern, as rows: the oracle's own decoding must agree with
+    # numpy's binary16 -> binary32 conversion bit for bit.
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(pats.view(np.float16))
+    pats = pats[finite][: (finite.sum() // 64) * 64].reshape(-1, 64)
+    q1, s1 = ref.quantize_rows(pats, "f16")
+    q2, s2 = ref.quantize_rows(pats.view(np.float16).astype(np.float32), "f32")
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s1, s2)
+    b = wl.bits16(wl.to_bf16(wl.rng(3).standard_normal((64, 64), dtype=np.float32)))
+    q1, s1 = ref.quantize_rows(b, "bf16")
+    q2, s2 = ref.quantize_rows(widen(b, "bf16"), "f32")
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------------------
+# P2 round-trip bound, P3 largest code, P6 scale invariance
+
+def _matrix(dtype, seed=5, r=256, k=1024):
+    g = wl.rng(seed)
+    w = wl.weight(g, r, k)
+    w[:, g.choice(k, 3, replace=False)] *= 50.0
+    w[[0, 77, r - 1]] = 0.0
+    w[5] *= 1e-3
+    return as_dtype(w, dtype)
+
+
+def round_trip_ratio(a, q, s):
+    """max over nonzero rows of |w - s*q| / s, in float64 (exact here)."""
+    w = a.astype(np.float64)
+    sc = s.astype(np.float64)[:, None]
+    nz = np.abs(w).max(axis=1) > 0
+    return float((np.abs(w - sc * q)[nz] / sc[nz]).max())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_p2_round_trip_bound(ref, dtype):
+    rows = _matrix(dtype)
+    q, s = ref.quantize_rows(rows, dtype)
+    assert round_trip_ratio(widen(rows, dtype), q, s) <= H
+    assert q.min() >= -127 and q.max() <= 127
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_p3_largest_code_and_sign(ref, dtype):
+    rows = _matrix(dtype, seed=6)
+    q, s = ref.quantize_rows(rows, dtype)
+    w = widen(rows, dtype)
+    for r in range(w.shape[0]):
+        amax = np.abs(w[r]).max()
+        if amax == 0:
+            continue
+        at = np.abs(w[r]) == amax
+        assert np.all(np.abs(q[r][at]) == 127)
+        assert np.all(np.sign(q[r][at]) == np.sign(w[r][at]))
+    nz = q != 0
+    assert np.all(np.sign(q[nz]) == np.sign(w[nz]))
+
+
+@pytest.mark.parametrize("j", [-20, -3, 4, 30])
+def test_p6_power_of_two_invariance(ref, j):
+    w = wl.weight(wl.rng(7), 64, 300, std=1.0)
+    q1, s1 = ref.quantize_rows(w, "f32")
+    q2, s2 = ref.quantize_rows(np.ldexp(w, j).astype(np.float32), "f32")
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(np.ldexp(s1, j).astype(np.float32), s2)
+
+
+# ---------------------------------------------------------------------------------------
+# P4 / P5: the two precision bugs of the Phase 5a page, as mutants the pins reject
+
+def test_p4_bf16_arithmetic_mutant_hits_one_and_a_half_bound(ref, mutant):
+    gold = json.load(open(os.path.join(GOLDEN, "bf16_arith_bound.json")))
+    bad = mutant("REF_MUTANT_BF16_ARITH")
+    rows = as_dtype(wl.rng(8).standard_normal((256, 2048), dtype=np.float32), "bf16")
+    w = widen(rows, "bf16")
+    q, s = ref.quantize_rows(rows, "bf16")
+    assert round_trip_ratio(w, q, s) <= H
+    qb, sb = bad.quantize_rows(rows, "bf16")
+    ratio = round_trip_ratio(w, qb, sb) / gold["ideal_bound_in_scale_units"]
+    # the mutant breaks the ideal bound, and by no more than the page's 1.5x
+    assert ratio > 1.25
+    assert ratio <= gold["bf16_worst_ratio"] + 2.0 ** -14
+    # brute force sides with the oracle on a row where the two disagree
+    r = int(np.flatnonzero((q != qb).any(axis=1) | (s != sb))[0])
+    bq, bs = brute_row(w[r], all_codes=False)
+    assert bs == s[r] and np.array_equal(bq, q[r])
+    assert not (bs == sb[r] and np.array_equal(bq, qb[r]))
+
+
+def test_p5_zero_channels_and_floor_mutant(ref, mutant):
+    t = wl.tiny_w8a8(0)
+    q, s = ref.quantize_rows(t["w"], "f32")
+    for r in t["zero_rows"]:
+        assert s[r] == 1.0 and not np.any(q[r])
+    assert np.all(np.isfinite(s))
+    # small but nonzero fp16 channels must keep the full int8 range (the guard is only for
+    # all-zero channels); a floored scale loses it and fails the largest-code pin.
+    g = wl.rng(9)
+    small = (g.standard_normal((16, 256), dtype=np.float32) * 1e-5).astype(np.float32)
+    rows = as_dtype(small, "f16")
+    q, s = ref.quantize_rows(rows, "f16")
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    qb, sb = mutant("REF_MUTANT_FLOOR_SCALE").quantize_rows(rows, "f16")
+    assert np.any(np.abs(qb).max(axis=1) < 127)
+
+
+# ---------------------------------------------------------------------------------------
+# P7 exact integer GEMM, P8 epilogue special case, P9 a-priori error
+
+def test_p7_big_int_triple_loop(ref):
+    g = wl.rng(10)
+    xq = g.integers(-127, 128, size=(3, 48), dtype=np.int8)
+    wq = g.integers(-127, 128, size=(5, 48), dtype=np.int8)
+    acc, _ = ref.w8a8(xq, None, wq, None, want_y=False)
+    for i in range(3):
+        for j in range(5):
+            assert acc[i, j] == sum(int(xq[i, c]) * int(wq[j, c]) for c in range(48))
+
+
+def test_p7_numpy_int64_matmul(ref):
+    g = wl.rng(13)
+    xq = g.integers(-127, 128, size=(37, 1040), dtype=np.int8)
+    wq = g.integers(-127, 128, size=(53, 1040), dtype=np.int8)
+    acc, _ = ref.w8a8(xq, None, wq, None, want_y=False)
+    np.testing.assert_array_equal(acc, xq.astype(np.int64) @ wq.astype(np.int64).T)
+
+
+def test_p7_int32_limit(ref):
+    k = 133144
+    xq = np.full((2, k), 127, np.int8)
+    wq = np.stack([np.full(k, 127, np.int8), np.full(k, -127, np.int8)])
+    acc, _ = ref.w8a8(xq, None, wq, None, want_y=False)
+    assert acc[0, 0] == 2147479576 and acc[0, 1] == -2147479576
+    with pytest.raises(OverflowError):
+        ref.w8a8(np.full((1, k + 16), 127, np.int8), None, np.full((1, k + 16), 127, np.int8),
+                 None, want_y=False)
+
+
+def test_p8_unit_scales_give_the_accumulator(ref):
+    g = wl.rng(14)
+    xq = g.integers(-127, 128, size=(9, 4096), dtype=np.int8)
+    wq = g.integers(-127, 128, size=(11, 4096), dtype=np.int8)
+    one_m, one_n = np.ones(9, np.float32), np.ones(11, np.float32)
+    acc, y = ref.w8a8(xq, one_m, wq, one_n)
+    np.testing.assert_array_equal(y, acc.astype(np.float64))
+    b = np.linspace(-3, 3, 11).astype(np.float32)
+    _, yb = ref.w8a8(xq, one_m, wq, one_n, bias=b)
+    np.testing.assert_array_equal(yb, acc.astype(np.float64) + b.astype(np.float64))
+
+
+def apriori_bound(qx, sx, qw, sw):
+    """|x.w - y| <= sx*sw*sum(|qx|*h + h*|qw| + h*h) with h the per-element rounding bound."""
+    ax = np.abs(qx.astype(np.float64))
+    aw = np.abs(qw.astype(np.float64))
+    k = qx.shape[1]
+    core = ax.sum(1)[:, None] * H + H * aw.sum(1)[None, :] + k * H * H
+    return core * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+
+
+def test_p9_tiny_workload_error_is_within_the_quantization_bound(ref):
+    t = wl.tiny_w8a8(0)
+    qw, sw = ref.quantize_rows(t["w"], "f32")
+    qx, sx = ref.quantize_rows(t["x"], "f32")
+    acc, y = ref.w8a8(qx, sx, qw, sw)
+    exact = t["x"].astype(np.float64) @ t["w"].astype(np.float64).T
+    bound = apriori_bound(qx, sx, qw, sw) * (1 + 1e-9)
+    assert np.all(np.abs(y - exact) <= bound)
+    for r in t["zero_rows"]:
+        assert np.all(y[:, r] == 0.0)
+    # a mistake that drops the weight scale or transposes an operand is far outside it
+    assert np.any(np.abs(y / sw[None, :] - exact) > bound)
+
+
+def test_p9_bf16_outlier_activations(ref):
+    g = wl.rng(15)
+    w = wl.to_bf16(wl.weight(g, 96, 2560))
+    x = wl.to_bf16(wl.activations(g, 17, 2560, outlier_frac=0.001))
+    qw, sw = ref.quantize_rows(wl.bits16(w), "bf16")
+    qx, sx = ref.quantize_rows(wl.bits16(x), "bf16")
+    _, y = ref.w8a8(qx, sx, qw, sw)
+    exact = x.double().numpy() @ w.double().numpy().T
+    assert np.all(np.abs(y - exact) <= apriori_bound(qx, sx, qw, sw) * (1 + 1e-9))
+
+
+# ---------------------------------------------------------------------------------------
+# P10 closed form printed on the Phase 5a page
+
+def test_p10_expert_memory_reduction_matches_the_page(ref):
+    gold = json.load(open(os.path.join(GOLDEN, "expert_footprint.json")))
+    g = wl.rng(16)
+    before = after = 0
+    for name, (n, k) in gold["expert_projections"].items():
+        w = wl.bits16(wl.to_bf16(wl.weight(g, n, k)))
+        q, s = ref.quantize_rows(w, "bf16")
+        before += n * k * gold["bf16_bytes_per_weight"]
+        after += q.nbytes + s.nbytes
+    pct = round(100.0 * (1 - after / before), gold["decimals"])
+    assert pct == gold["printed_reduction_percent"]
+    # a 2-byte scale would print a different number: the page pins float32 scales
+    alt = sum(n * k + 2 * n for n, k in gold["expert_projections"].values())
+    assert round(100.0 * (1 - alt / before), 2) != gold["printed_reduction_percent"]
+
+
+# ---------------------------------------------------------------------------------------
+# P11 weight-only and grouped products against numpy's float64 matmul
+
+def _w8a16_case(ref, g, m, n, k, bias):
+    x = wl.to_bf16(wl.activations(g, m, k))
+    q, s = ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+    b = (g.standard_normal(n, dtype=np.float32) * 0.02).astype(np.float32) if bias else None
+    return x, q, s, b
+
+
+@pytest.mark.parametrize("m,n,k,bias", [(1, 64, 512, False), (8, 200, 4096, True), (5, 33, 48, True)])
+def test_p11_w8a16_is_x_times_dequantized_weight(ref, m, n, k, bias):
+    g = wl.rng(17)
+    x, q, s, b = _w8a16_case(ref, g, m, n, k, bias)
+    y = ref.w8a16(wl.bits16(x), q, s, b)
+    deq = s.astype(np.float64)[:, None] * q.astype(np.float64)
+    xd = x.double().numpy()
+    want = xd @ deq.T + (0.0 if b is None else b.astype(np.float64))
+    scale = np.abs(xd) @ np.abs(deq).T + 1.0
+    assert np.all(np.abs(y - want) <= 1e-12 * scale)
+    # dropping the last 16 input channels is visible at this tolerance
+    short = xd[:, :-16] @ deq[:, :-16].T + (0.0 if b is None else b.astype(np.float64))
+    assert np.any(np.abs(short - y) > 1e-6 * scale)
+
+
+def test_p11_grouped_reduces_to_w8a16_and_per_expert_matmul(ref):
+    g = wl.rng(18)
+    e, n, k, t, topk = 7, 40, 256, 9, 3
+    wf = wl.moe_weights(g, n, k, experts=e)
+    q, s = ref.quantize_rows(wl.bits16(wl.to_bf16(wf.reshape(e * n, k))), "bf16")
+    q, s = q.reshape(e, n, k), s.reshape(e, n)
+    ids = np.stack([g.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    ids[2, 1] = -1
+    ids[4, 0] = e  # out of range
+    for per_assign in (0, 1):
+        x = wl.to_bf16(wl.activations(g, t * topk if per_assign else t, k))
+        y = ref.grouped_w8a16(wl.bits16(x), per_assign, q, s, ids)
+        xd = x.double().numpy()
+        for p in range(t * topk):
+            ex = ids.flat[p]
+            if not 0 <= ex < e:
+                assert np.all(y[p] == 0.0)
+                continue
+            xr = xd[p if per_assign else p // topk]
+            want = (s[ex].astype(np.float64)[:, None] * q[ex].astype(np.float64)) @ xr
+            np.testing.assert_allclose(y[p], want, rtol=1e-12, atol=1e-12)
+    # one expert, one slot: the grouped product is the plain weight-only product
+    x = wl.to_bf16(wl.activations(g, 6, k))
+    yg = ref.grouped_w8a16(wl.bits16(x), 0, q[:1], s[:1], np.zeros((6, 1), np.int32))
+    np.testing.assert_array_equal(yg, ref.w8a16(wl.bits16(x), q[0], s[0]))
+
+
+def test_p11_grouped_token_permutation(ref):
+    g = wl.rng(19)
+    e, n, k, t, topk = 5, 24, 128, 8, 2
+    q, s = ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, e * n, k))), "bf16")
+    q, s = q.reshape(e, n, k), s.reshape(e, n)
+    ids = g.integers(0, e, size=(t, topk), dtype=np.int32)
+    x = wl.bits16(wl.to_bf16(wl.activations(g, t, k)))
+    perm = g.permutation(t)
+    y = ref.grouped_w8a16(x, 0, q, s, ids).reshape(t, topk, n)
+    yp = ref.grouped_w8a16(x[perm], 0, q, s, ids[perm]).reshape(t, topk, n)
+    np.testing.assert_array_equal(yp, y[perm])
