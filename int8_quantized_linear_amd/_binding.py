@@ -1,0 +1,193 @@
+"""ctypes binding of ``libi8ql.so``: argument marshalling only.
+
+Every function takes torch tensors on the GPU, checks that they are dense and of the dtype
+the C entry point expects, allocates outputs with torch when the caller passes none, and
+forwards raw device pointers plus ``torch.cuda.current_stream().cuda_stream`` to the C ABI
+of ``include/i8ql.h``.  All arithmetic happens in the HIP kernels.  There is no fallback:
+a missing library or a non-OK status raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libi8ql.so")
+
+I8QL_F32, I8QL_BF16, I8QL_F16, I8QL_I8, I8QL_I32 = 0, 1, 2, 3, 4
+_DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8QL_F16,
+          torch.int8: I8QL_I8, torch.int32: I8QL_I32}
+EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
+           "grouped_w8a16_gemm", "i8ql_status_string", "i8ql_last_hip_error")
+
+
+class I8qlError(RuntimeError):
+    def __init__(self, fn: str, status: int, lib):
+        name = lib.i8ql_status_string(status).decode()
+        hip = lib.i8ql_last_hip_error() if name == "I8QL_ERR_HIP" else 0
+        super().__init__(f"{fn} failed: {name}" + (f" (hipError {hip})" if hip else ""))
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libi8ql.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python __graft_entry__.py build` "
+                               "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        for fn in ("quantize_per_channel_int8", "quantize_per_token_int8"):
+            getattr(lib, fn).argtypes = [P, I, I64, I64, P, P, P]
+            getattr(lib, fn).restype = I
+        lib.w8a8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a8_gemm.restype = I
+        lib.w8a16_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a16_gemm.restype = I
+        lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
+        lib.grouped_w8a16_gemm.restype = I
+        lib.i8ql_status_string.argtypes = [I]
+        lib.i8ql_status_string.restype = ctypes.c_char_p
+        lib.i8ql_last_hip_error.argtypes = []
+        lib.i8ql_last_hip_error.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtypes, dim: int | None = None, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(fn: str, *args):
+    lib = load_library()
+    st = getattr(lib, fn)(*args)
+    if st != 0:
+        raise I8qlError(fn, st, lib)
+
+
+def _quantize(fn: str, a: torch.Tensor, q_out=None, scale_out=None):
+    _check(a, "input", (torch.float32, torch.bfloat16, torch.float16), 2)
+    r, k = a.shape
+    q = q_out if q_out is not None else torch.empty((r, k), dtype=torch.int8, device=a.device)
+    s = scale_out if scale_out is not None else torch.empty((r,), dtype=torch.float32,
+                                                            device=a.device)
+    _check(q, "q_out", (torch.int8,), 2, a.device)
+    _check(s, "scale_out", (torch.float32,), 1, a.device)
+    if tuple(q.shape) != (r, k) or tuple(s.shape) != (r,):
+        raise ValueError("output shapes do not match the input")
+    with torch.cuda.device(a.device):
+        _call(fn, _ptr(a), _DTYPE[a.dtype], r, k, _ptr(q), _ptr(s), _stream(a.device))
+    return q, s
+
+
+def quantize_per_channel_int8(w: torch.Tensor, q_out=None, scale_out=None):
+    """Per-output-channel symmetric int8: ``w`` [N, K] fp32/bf16/fp16 -> (q int8 [N, K],
+    scale fp32 [N])."""
+    return _quantize("quantize_per_channel_int8", w, q_out, scale_out)
+
+
+def quantize_per_token_int8(x: torch.Tensor, q_out=None, scale_out=None):
+    """Dynamic per-token symmetric int8: ``x`` [M, K] -> (q int8 [M, K], scale fp32 [M])."""
+    return _quantize("quantize_per_token_int8", x, q_out, scale_out)
+
+
+def _out(out, shape, dtype, dev):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _check(out, "out", (dtype,), len(shape), dev)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out
+
+
+def w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):
+    """``y = (xq @ wq.T) * x_scale[:, None] * w_scale[None, :] (+ bias)``; int32 when
+    ``out_dtype`` is torch.int32 (then scales may be None and bias must be None)."""
+    _check(xq, "xq", (torch.int8,), 2)
+    dev = xq.device
+    _check(wq, "wq", (torch.int8,), 2, dev)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError("xq and wq disagree on K")
+    for t, nm, ln in ((x_scale, "x_scale", m), (w_scale, "w_scale", n), (bias, "bias", n)):
+        if t is not None:
+            _check(t, nm, (torch.float32,), 1, dev)
+            if t.shape[0] != ln:
+                raise ValueError(f"{nm} must have {ln} entries")
+    y = _out(out, (m, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("w8a8_gemm", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+              _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
+    return y
+
+
+def w8a16_gemm(x, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):
+    """``y = x @ (w_scale[:, None] * wq).T (+ bias)`` with bf16 ``x`` [M, K]."""
+    _check(x, "x", (torch.bfloat16,), 2)
+    dev = x.device
+    _check(wq, "wq", (torch.int8,), 2, dev)
+    _check(w_scale, "w_scale", (torch.float32,), 1, dev)
+    m, k = x.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k or w_scale.shape[0] != n:
+        raise ValueError("x, wq and w_scale disagree")
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), 1, dev)
+        if bias.shape[0] != n:
+            raise ValueError("bias must have N entries")
+    y = _out(out, (m, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("w8a16_gemm", _ptr(x), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y),
+              _DTYPE[out_dtype], m, n, k, _stream(dev))
+    return y
+
+
+def grouped_w8a16_gemm(x, wq, w_scale, expert_ids, x_per_assignment=False,
+                       out_dtype=torch.bfloat16, out=None):
+    """Grouped weight-only GEMM over experts: ``wq`` [E, N, K], ``w_scale`` [E, N],
+    ``expert_ids`` [T, topk] int32, ``x`` [T, K] (or [T*topk, K] when
+    ``x_per_assignment``) -> [T*topk, N]."""
+    _check(x, "x", (torch.bfloat16,), 2)
+    dev = x.device
+    _check(wq, "wq", (torch.int8,), 3, dev)
+    _check(w_scale, "w_scale", (torch.float32,), 2, dev)
+    _check(expert_ids, "expert_ids", (torch.int32,), 2, dev)
+    e, n, k = wq.shape
+    t, topk = expert_ids.shape
+    if tuple(w_scale.shape) != (e, n) or x.shape[1] != k:
+        raise ValueError("x, wq and w_scale disagree")
+    if x.shape[0] != (t * topk if x_per_assignment else t):
+        raise ValueError("x has the wrong number of rows for x_per_assignment")
+    y = _out(out, (t * topk, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("grouped_w8a16_gemm", _ptr(x), int(bool(x_per_assignment)), _ptr(wq),
+              _ptr(w_scale), e, _ptr(expert_ids), t, topk, _ptr(y), _DTYPE[out_dtype], n, k,
+              _stream(dev))
+    return y

@@ -1,0 +1,145 @@
+// api.cpp — the C ABI of libi8ql: argument validation (fail closed) and kernel dispatch.
+//
+// Every entry point checks its arguments on the host before any HIP call, in this order:
+// dtype, negative or degenerate dimensions, the zero-size no-op, NULL pointers, alignment
+// and limits.  Unsupported input never reaches a kernel and never selects a different
+// kernel: it returns an error, as the fail-closed scheme resolution of
+// "feat(quantization): support compressed-tensors W8A8 and mixed modules" (Summary, Notes
+// for Reviewers) does for unsupported checkpoints.  Only I8QL_ERR_HIP follows a launch.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "i8ql.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+constexpr int64_t kMaxGridX = 2147483647;
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(i8ql_dtype d) {
+  switch (d) {
+    case I8QL_F32: return 4;
+    case I8QL_BF16: return 2;
+    case I8QL_F16: return 2;
+    case I8QL_I8: return 1;
+    case I8QL_I32: return 4;
+  }
+  return 0;
+}
+
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
+
+i8ql_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return I8QL_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return I8QL_ERR_HIP;
+}
+
+i8ql_status quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
+                          int8_t* q, float* scale, void* stream) {
+  if (dtype != I8QL_F32 && dtype != I8QL_BF16 && dtype != I8QL_F16) return I8QL_ERR_DTYPE;
+  if (rows < 0 || k < 1) return I8QL_ERR_SHAPE;
+  if (!mul_ok(rows, k) || (rows + 3) / 4 > kMaxGridX) return I8QL_ERR_SHAPE;
+  if (rows == 0) return I8QL_OK;
+  if (!a || !q || !scale) return I8QL_ERR_NULL;
+  if (!aligned(a, elem_bytes(dtype)) || !aligned(scale, 4)) return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_quantize_rows(a, dtype, rows, k, q, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+i8ql_status quantize_per_channel_int8(const void* w, i8ql_dtype w_dtype, int64_t n, int64_t k,
+                                      int8_t* q_out, float* scale_out, void* stream) {
+  return quantize_rows(w, w_dtype, n, k, q_out, scale_out, stream);
+}
+
+i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m, int64_t k,
+                                    int8_t* q_out, float* scale_out, void* stream) {
+  return quantize_rows(x, x_dtype, m, k, q_out, scale_out, stream);
+}
+
+i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
+                      int64_t m, int64_t n, int64_t k, void* stream) {
+  if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32 && y_dtype != I8QL_I32) return I8QL_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
+  if ((n + 127) / 128 > kMaxGridX || (m + 127) / 128 > kMaxGridY) return I8QL_ERR_SHAPE;
+  if (m == 0 || n == 0) return I8QL_OK;
+  if (!xq || !wq || !y) return I8QL_ERR_NULL;
+  if (y_dtype != I8QL_I32 && (!x_scale || !w_scale)) return I8QL_ERR_NULL;
+  if (y_dtype == I8QL_I32 && bias) return I8QL_ERR_ARG;
+  if (k % 16 != 0 || !aligned(xq, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(y, elem_bytes(y_dtype)) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(bias, 4))
+    return I8QL_ERR_ALIGN;
+  if (k > I8QL_W8A8_MAX_K) return I8QL_ERR_K_TOO_LARGE;
+  return hip_status(i8ql::launch_w8a8_gemm(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
+                       void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                       void* stream) {
+  if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32) return I8QL_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
+  if ((n + 15) / 16 > kMaxGridX || (m + 63) / 64 > kMaxGridY) return I8QL_ERR_SHAPE;
+  if (m == 0 || n == 0) return I8QL_OK;
+  if (!x || !wq || !w_scale || !y) return I8QL_ERR_NULL;
+  if (k % 16 != 0 || !aligned(x, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(y, elem_bytes(y_dtype)) || !aligned(w_scale, 4) || !aligned(bias, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_w8a16_gemm(x, wq, w_scale, bias, y, y_dtype, m, n, k,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t* wq,
+                               const float* w_scale, int64_t num_experts,
+                               const int32_t* expert_ids, int64_t t, int64_t topk, void* y,
+                               i8ql_dtype y_dtype, int64_t n, int64_t k, void* stream) {
+  if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32) return I8QL_ERR_DTYPE;
+  if (x_per_assignment != 0 && x_per_assignment != 1) return I8QL_ERR_ARG;
+  if (topk < 1 || topk > 64 || num_experts < 1 || num_experts > kMaxGridY - 1) return I8QL_ERR_ARG;
+  if (t < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
+  if (t * topk > 65536) return I8QL_ERR_SHAPE;
+  if (!mul_ok(num_experts, n) || !mul_ok(num_experts * n, k) || !mul_ok(t * topk, k) ||
+      !mul_ok(t * topk, n) || (n + 15) / 16 > kMaxGridX)
+    return I8QL_ERR_SHAPE;
+  if (t == 0 || n == 0) return I8QL_OK;
+  if (!x || !wq || !w_scale || !expert_ids || !y) return I8QL_ERR_NULL;
+  if (k % 16 != 0 || !aligned(x, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(y, elem_bytes(y_dtype)) || !aligned(w_scale, 4) || !aligned(expert_ids, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_grouped_w8a16_gemm(x, x_per_assignment, wq, w_scale,
+                                                    num_experts, expert_ids, t, topk, y,
+                                                    y_dtype, n, k,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+const char* i8ql_status_string(i8ql_status s) {
+  switch (s) {
+    case I8QL_OK: return "I8QL_OK";
+    case I8QL_ERR_NULL: return "I8QL_ERR_NULL";
+    case I8QL_ERR_SHAPE: return "I8QL_ERR_SHAPE";
+    case I8QL_ERR_DTYPE: return "I8QL_ERR_DTYPE";
+    case I8QL_ERR_ALIGN: return "I8QL_ERR_ALIGN";
+    case I8QL_ERR_K_TOO_LARGE: return "I8QL_ERR_K_TOO_LARGE";
+    case I8QL_ERR_ARG: return "I8QL_ERR_ARG";
+    case I8QL_ERR_HIP: return "I8QL_ERR_HIP";
+  }
+  return "I8QL_UNKNOWN_STATUS";
+}
+
+int i8ql_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// dequant_mma.hpp — the inner loop shared by the weight-only (W8A16) kernels on gfx950.
+//
+// Weight-only int8 saves HBM bytes, not arithmetic ("Phase 5a: int8 weight-only
+// quantization", Summary): the int8 codes are expanded to bf16 in registers and the product
+// runs on the bf16 matrix cores ("Day 6 — Quantize It Yourself", The mechanism, block 5).
+// The expansion is exact: every code in [-127, 127] is a bf16 value.
+//
+// Tile shape: one wavefront owns 16 weight rows (output channels) and up to MT x 16
+// activation rows.  v_mfma_f32_16x16x32_bf16 takes the weights as operand A (row i = lane
+// % 16) and the activations as operand B (column j = lane % 16); lanes 16g .. 16g+15 carry
+// k-slots 8g .. 8g+7.  Only the pairing of A and B slots matters for the sum, so each lane
+// feeds both operands from the same 32 consecutive input channels: k0 + 32 * (lane / 16)
+// + [0, 32), i.e. one 128-channel step is four MFMAs.  A step reads 16 rows x 128 bytes of
+// weights: every lane issues two 16-byte loads and each row's 128-byte line is read whole
+// by four lanes.  The accumulator holds D[n][m]: lane l, register r is channel
+// 4 * (l / 16) + r of the tile and activation row l % 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8ql {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kStepK = 128;  // input channels per wavefront step
+
+// Four int8 codes -> two dwords holding four bf16 values (exact).
+__device__ __forceinline__ void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const float f0 = static_cast<float>(static_cast<int8_t>(w));
+  const float f1 = static_cast<float>(static_cast<int8_t>(w >> 8));
+  const float f2 = static_cast<float>(static_cast<int8_t>(w >> 16));
+  const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
+  // |code| < 256: the low 16 bits of each float32 are zero, so the high half is the bf16.
+  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+}
+
+// 16 codes -> two 8-wide bf16 MFMA operands.
+__device__ __forceinline__ void i8x16_to_bf16(const uint4 w, v8bf& a0, v8bf& a1) {
+  uint4 p, q;
+  i8x4_to_bf16x4(w.x, p.x, p.y);
+  i8x4_to_bf16x4(w.y, p.z, p.w);
+  i8x4_to_bf16x4(w.z, q.x, q.y);
+  i8x4_to_bf16x4(w.w, q.z, q.w);
+  a0 = __builtin_bit_cast(v8bf, p);
+  a1 = __builtin_bit_cast(v8bf, q);
+}
+
+__device__ __forceinline__ v8bf as_v8bf(const uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+// Accumulate the wavefront's partial product over steps [s_begin, s_end).
+//   wrow : this lane's weight row (row n0 + lane % 16, clamped into the matrix)
+//   xrow : this lane's activation row for each m-tile (lane % 16 within the tile), or
+//          nullptr when that row does not exist (its column of the MFMA is then zero)
+// Chunks past k (k % 16 == 0) are neither read nor counted.
+template <int MT, int U>
+__device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wrow,
+                                                  const uint16_t* const (&xrow)[MT], int64_t k,
+                                                  int s_begin, int s_end, v4f (&acc)[MT]) {
+  const int lane = threadIdx.x % 64;
+  const int sub = 32 * (lane / 16);  // this lane's 32 channels within a step
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  for (int s = s_begin; s < s_end; s += U) {
+    uint4 w[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
+      const bool in = (s + u) < s_end;
+      w[u][0] = (in && kk < k) ? *reinterpret_cast<const uint4*>(wrow + kk) : zero;
+      w[u][1] = (in && kk + 16 < k) ? *reinterpret_cast<const uint4*>(wrow + kk + 16) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
+      const bool in = (s + u) < s_end;
+      v8bf a[4];
+      i8x16_to_bf16(w[u][0], a[0], a[1]);
+      i8x16_to_bf16(w[u][1], a[2], a[3]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint16_t* xr = xrow[mt];
+        uint4 xb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t kc = kk + 8 * c;
+          xb[c] = (in && xr != nullptr && kc < k) ? *reinterpret_cast<const uint4*>(xr + kc)
+                                                  : zero;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_v8bf(xb[c]), acc[mt], 0,
+                                                            0, 0);
+      }
+    }
+  }
+}
+
+// Split the steps of k among the waves of a workgroup: wave w gets [begin, end).
+__device__ __forceinline__ void wave_step_range(int64_t k, int waves, int wave, int& begin,
+                                                int& end) {
+  const int steps = static_cast<int>((k + kStepK - 1) / kStepK);
+  const int per = (steps + waves - 1) / waves;
+  begin = min(steps, wave * per);
+  end = min(steps, begin + per);
+}
+
+// Round a float32 to the nearest-even bfloat16 bit pattern (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+}  // namespace i8ql

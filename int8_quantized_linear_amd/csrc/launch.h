@@ -1,0 +1,33 @@
+// launch.h — host-side launchers of the gfx950 kernels (internal to libi8ql).
+//
+// Each launcher assumes its arguments were validated by the C ABI layer (api.cpp): shapes
+// non-negative and non-empty, dtypes supported, pointers non-NULL and aligned as the kernel
+// requires.  Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i8ql.h"
+
+namespace i8ql {
+
+hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
+                                int8_t* q, float* scale, hipStream_t stream);
+
+hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, const float* bias, void* y,
+                            i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                            hipStream_t stream);
+
+hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
+                             const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
+                             int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t* wq,
+                                     const float* w_scale, int64_t num_experts,
+                                     const int32_t* expert_ids, int64_t t, int64_t topk,
+                                     void* y, i8ql_dtype y_dtype, int64_t n, int64_t k,
+                                     hipStream_t stream);
+
+}  // namespace i8ql

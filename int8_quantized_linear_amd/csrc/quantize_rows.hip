@@ -1,0 +1,235 @@
+// quantize_rows.hip — symmetric absmax int8 quantization of the rows of a matrix (gfx950).
+//
+// One kernel serves both quantizers: per-output-channel weights and dynamic per-token
+// activations apply the same rule to every row ("Day 6 — Quantize It Yourself", The
+// mechanism, block 1: q = clamp(round(w / s)), s = absmax / largest code; "Phase 5a: int8
+// weight-only quantization", Summary: float32 arithmetic and an all-zero-channel guard).
+//
+// Work layout: one 64-lane wavefront per row, four rows per 256-thread workgroup.  Pass 1
+// streams the row with 16-byte loads (kept in registers when the row fits, up to 24 KiB),
+// reduces |a| to the row maximum with cross-lane shuffles; pass 2 divides, rounds and
+// packs 4 or 8 codes per store.  The row is read from HBM once; the op is HBM-bound
+// (2 + 1 bytes per bf16 element).
+//
+// Arithmetic (identical for every dtype): the input is widened exactly to float32;
+// s = amax / 127 is a correctly rounded float32 division; s == 0 stores scale 1 and zero
+// codes; otherwise each code is rint(a / s) (correctly rounded division, then round half to
+// even via v_rndne_f32) clamped to [-127, 127].  The file must not be built with fast-math.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace i8ql {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kRowsPerBlock = 4;
+constexpr int kCacheChunks = 24;  // 16-byte chunks per lane kept in registers (24 KiB rows)
+
+template <int DT>
+struct Fmt;
+template <>
+struct Fmt<I8QL_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerChunk = 4;
+};
+template <>
+struct Fmt<I8QL_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;
+};
+template <>
+struct Fmt<I8QL_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;
+};
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  _Float16 v;
+  uint16_t b = static_cast<uint16_t>(h);
+  __builtin_memcpy(&v, &b, 2);
+  return static_cast<float>(v);
+}
+
+// Widen one 16-byte chunk to float32 (exact for every input format).
+template <int DT>
+__device__ __forceinline__ void widen_chunk(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (DT == I8QL_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  } else if constexpr (DT == I8QL_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = half_bits_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = half_bits_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float widen_one(const void* base, int64_t i) {
+  if constexpr (DT == I8QL_F32) {
+    return static_cast<const float*>(base)[i];
+  } else if constexpr (DT == I8QL_BF16) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
+  } else {
+    return half_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// The code of one element: correctly rounded float32 quotient, ties-to-even, clamp.
+__device__ __forceinline__ int code_of(float a, float s) {
+  float t = rintf(a / s);
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return static_cast<int>(t);
+}
+
+__device__ __forceinline__ float chunk_absmax(const float* f, int n, float m) {
+  for (int i = 0; i < n; ++i) m = fmaxf(m, fabsf(f[i]));
+  return m;
+}
+
+// Vector path: row bytes are a multiple of 16 and the base is 16-byte aligned.
+template <int DT>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel(
+    const uint8_t* __restrict__ a, int64_t rows, int64_t k, int8_t* __restrict__ q,
+    float* __restrict__ scale) {
+  constexpr int E = Fmt<DT>::kPerChunk;
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int64_t chunks = k / E;
+  const uint4* src = reinterpret_cast<const uint4*>(a + row * k * Fmt<DT>::kBytes);
+  int8_t* dst = q + row * k;
+  const bool cached = chunks <= static_cast<int64_t>(kCacheChunks) * kWave;
+
+  uint4 cache[kCacheChunks];
+  float amax = 0.0f;
+  float f[E];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kCacheChunks; ++i) {
+      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
+      if (c < chunks) cache[i] = src[c];
+    }
+#pragma unroll
+    for (int i = 0; i < kCacheChunks; ++i) {
+      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
+      if (c < chunks) {
+        widen_chunk<DT>(cache[i], f);
+        amax = chunk_absmax(f, E, amax);
+      }
+    }
+  } else {
+    for (int64_t c = lane; c < chunks; c += kWave) {
+      widen_chunk<DT>(src[c], f);
+      amax = chunk_absmax(f, E, amax);
+    }
+  }
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+
+  if (s == 0.0f) {  // all-zero channel: scale 1, codes 0
+    for (int64_t j = lane * 4; j < k; j += kWave * 4)
+      *reinterpret_cast<uint32_t*>(dst + j) = 0u;  // k % 4 == 0 on this path
+    if (lane == 0) scale[row] = 1.0f;
+    return;
+  }
+
+  auto emit = [&](const uint4 v, int64_t c) {
+    widen_chunk<DT>(v, f);
+    uint32_t packed[E / 4];
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        p |= (static_cast<uint32_t>(code_of(f[4 * g + b], s)) & 0xffu) << (8 * b);
+      packed[g] = p;
+    }
+    if constexpr (E == 4) {
+      *reinterpret_cast<uint32_t*>(dst + c * 4) = packed[0];
+    } else {
+      *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(packed[0], packed[1]);
+    }
+  };
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kCacheChunks; ++i) {
+      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
+      if (c < chunks) emit(cache[i], c);
+    }
+  } else {
+    for (int64_t c = lane; c < chunks; c += kWave) emit(src[c], c);
+  }
+  if (lane == 0) scale[row] = s;
+}
+
+// Scalar path: any k and any element-aligned base.
+template <int DT>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_scalar_kernel(
+    const void* __restrict__ a, int64_t rows, int64_t k, int8_t* __restrict__ q,
+    float* __restrict__ scale) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int64_t base = row * k;
+  float amax = 0.0f;
+  for (int64_t j = lane; j < k; j += kWave) amax = fmaxf(amax, fabsf(widen_one<DT>(a, base + j)));
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+  if (s == 0.0f) {
+    for (int64_t j = lane; j < k; j += kWave) q[base + j] = 0;
+    if (lane == 0) scale[row] = 1.0f;
+    return;
+  }
+  for (int64_t j = lane; j < k; j += kWave)
+    q[base + j] = static_cast<int8_t>(code_of(widen_one<DT>(a, base + j), s));
+  if (lane == 0) scale[row] = s;
+}
+
+template <int DT>
+hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* scale,
+                     hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 block(kWave * kRowsPerBlock);
+  const bool vec = (k * Fmt<DT>::kBytes) % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a) % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(q) % 8) == 0;
+  if (vec) {
+    hipLaunchKernelGGL(quantize_rows_vec_kernel<DT>, grid, block, 0, stream,
+                       static_cast<const uint8_t*>(a), rows, k, q, scale);
+  } else {
+    hipLaunchKernelGGL(quantize_rows_scalar_kernel<DT>, grid, block, 0, stream, a, rows, k, q,
+                       scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
+                                int8_t* q, float* scale, hipStream_t stream) {
+  switch (dtype) {
+    case I8QL_F32: return launch_dt<I8QL_F32>(a, rows, k, q, scale, stream);
+    case I8QL_BF16: return launch_dt<I8QL_BF16>(a, rows, k, q, scale, stream);
+    case I8QL_F16: return launch_dt<I8QL_F16>(a, rows, k, q, scale, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace i8ql

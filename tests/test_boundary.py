@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header declares, and
+rejects bad arguments before any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i8ql.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, KBIG, ARG = 0, 1, 2, 3, 4, 5, 6
+F32, BF16, F16, I8, I32 = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from int8_quantized_linear_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from int8_quantized_linear_amd import build
+        build.build()
+    return _binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined", "sizeof"})
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm",
+                          "w8a16_gemm", "grouped_w8a16_gemm", "i8ql_status_string",
+                          "i8ql_last_hip_error"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["I8QL_OK", "I8QL_ERR_NULL", "I8QL_ERR_SHAPE", "I8QL_ERR_DTYPE",
+                                 "I8QL_ERR_ALIGN", "I8QL_ERR_K_TOO_LARGE", "I8QL_ERR_ARG",
+                                 "I8QL_ERR_HIP"]):
+        assert lib.i8ql_status_string(code).decode() == name
+    assert lib.i8ql_last_hip_error() == 0
+
+
+# Fake, never-dereferenced addresses: every call below fails validation before any HIP call.
+A16 = ctypes.c_void_p(0x10000)          # 16-byte aligned
+A4 = ctypes.c_void_p(0x10004)           # 4-byte aligned only
+A2 = ctypes.c_void_p(0x10002)
+NUL = None
+
+
+@pytest.mark.parametrize("fn", ["quantize_per_channel_int8", "quantize_per_token_int8"])
+def test_quantizer_validation(lib, fn):
+    f = getattr(lib, fn)
+    assert f(A16, I8, 4, 8, A16, A16, NUL) == DTYPE
+    assert f(A16, I32, 4, 8, A16, A16, NUL) == DTYPE
+    assert f(A16, 9, 4, 8, A16, A16, NUL) == DTYPE
+    assert f(A16, F32, -1, 8, A16, A16, NUL) == SHAPE
+    assert f(A16, F32, 4, 0, A16, A16, NUL) == SHAPE
+    assert f(A16, F32, 1 << 40, 1 << 30, A16, A16, NUL) == SHAPE
+    assert f(NUL, F32, 0, 8, NUL, NUL, NUL) == OK      # zero rows: no-op
+    assert f(NUL, F32, 4, 8, A16, A16, NUL) == NULL
+    assert f(A16, F32, 4, 8, NUL, A16, NUL) == NULL
+    assert f(A16, F32, 4, 8, A16, NUL, NUL) == NULL
+    assert f(A2, F32, 4, 8, A16, A16, NUL) == ALIGN
+    assert f(ctypes.c_void_p(0x10001), BF16, 4, 8, A16, A16, NUL) == ALIGN
+    assert f(A16, F32, 4, 8, A16, A2, NUL) == ALIGN
+
+
+def test_w8a8_validation(lib):
+    f = lib.w8a8_gemm
+    args = lambda **kw: dict(dict(xq=A16, sx=A16, wq=A16, sw=A16, b=NUL, y=A16, yt=BF16,
+                                  m=4, n=8, k=64), **kw)
+    call = lambda a: f(a["xq"], a["sx"], a["wq"], a["sw"], a["b"], a["y"], a["yt"], a["m"],
+                       a["n"], a["k"], NUL)
+    assert call(args(yt=F16)) == DTYPE
+    assert call(args(yt=I8)) == DTYPE
+    assert call(args(m=-1)) == SHAPE
+    assert call(args(n=-2)) == SHAPE
+    assert call(args(k=0)) == SHAPE
+    assert call(args(m=0, xq=NUL, y=NUL)) == OK
+    assert call(args(n=0)) == OK
+    assert call(args(xq=NUL)) == NULL
+    assert call(args(wq=NUL)) == NULL
+    assert call(args(y=NUL)) == NULL
+    assert call(args(sx=NUL)) == NULL
+    assert call(args(sw=NUL, yt=F32)) == NULL
+    assert call(args(yt=I32, b=A16)) == ARG
+    assert call(args(k=72)) == ALIGN
+    assert call(args(k=8)) == ALIGN
+    assert call(args(xq=A4)) == ALIGN
+    assert call(args(wq=ctypes.c_void_p(0x10008))) == ALIGN
+    assert call(args(y=ctypes.c_void_p(0x10001))) == ALIGN
+    assert call(args(y=A2, yt=F32)) == ALIGN
+    assert call(args(b=A2, yt=F32)) == ALIGN
+    assert call(args(k=133152)) == KBIG
+
+
+def test_w8a8_int32_limit_is_exactly_the_header_constant():
+    # 133144 * 127 * 127 fits in int32; 133160 (next multiple of 16) would not.
+    assert 133144 * 127 * 127 < 2 ** 31 <= 133160 * 127 * 127
+    assert "#define I8QL_W8A8_MAX_K 133144" in open(HEADER).read()
+
+
+def test_w8a16_validation(lib):
+    f = lib.w8a16_gemm
+    base = dict(x=A16, wq=A16, sw=A16, b=NUL, y=A16, yt=BF16, m=1, n=8, k=64)
+    call = lambda **kw: (lambda a: f(a["x"], a["wq"], a["sw"], a["b"], a["y"], a["yt"], a["m"],
+                                     a["n"], a["k"], NUL))(dict(base, **kw))
+    assert call(yt=I32) == DTYPE
+    assert call(yt=F16) == DTYPE
+    assert call(m=-1) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(m=0, x=NUL) == OK
+    assert call(x=NUL) == NULL
+    assert call(sw=NUL) == NULL
+    assert call(k=40) == ALIGN
+    assert call(x=A4) == ALIGN
+    assert call(wq=A4) == ALIGN
+    assert call(b=A2) == ALIGN
+
+
+def test_grouped_validation(lib):
+    f = lib.grouped_w8a16_gemm
+    base = dict(x=A16, pa=0, wq=A16, sw=A16, e=66, ids=A16, t=4, topk=8, y=A16, yt=BF16, n=16,
+                k=64)
+    call = lambda **kw: (lambda a: f(a["x"], a["pa"], a["wq"], a["sw"], a["e"], a["ids"], a["t"],
+                                     a["topk"], a["y"], a["yt"], a["n"], a["k"], NUL))(dict(base, **kw))
+    assert call(yt=I32) == DTYPE
+    assert call(pa=2) == ARG
+    assert call(topk=0) == ARG
+    assert call(topk=65) == ARG
+    assert call(e=0) == ARG
+    assert call(e=65535) == ARG
+    assert call(t=-1) == SHAPE
+    assert call(t=8193, topk=8) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(t=0, x=NUL) == OK
+    assert call(ids=NUL) == NULL
+    assert call(x=NUL) == NULL
+    assert call(k=24) == ALIGN
+    assert call(x=A4) == ALIGN
+    assert call(ids=A2) == ALIGN
+
+
+def test_binding_fails_loudly_without_a_gpu_tensor():
+    import torch
+    import int8_quantized_linear_amd as i8
+    with pytest.raises(ValueError, match="GPU"):
+        i8.quantize_per_channel_int8(torch.zeros(4, 8))

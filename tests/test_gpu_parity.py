@@ -1,0 +1,370 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the same seeded
+inputs.  Codes, scales and int32 accumulators must be bitwise equal; float outputs follow
+the rules in tests/parity.py.  Small cases span several tiles and ragged tails; the
+decoder-shaped workloads run at full size (sampled rows where the oracle would be slow)."""
+import numpy as np
+import pytest
+import torch
+
+import int8_quantized_linear_amd as i8
+from int8_quantized_linear_amd import workloads as wl
+from parity import check_float, to_np, w8a16_tol, w8a8_tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    i8.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+
+
+def host(dtype, a32):
+    """Host tensor of the given dtype from float32 numpy + the oracle's view of it."""
+    if dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(a32, np.float32))
+        return t, t.numpy()
+    t = wl.to_bf16(a32) if dtype == "bf16" else wl.to_f16(a32)
+    return t, wl.bits16(t)
+
+
+def quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token=False):
+    fn = i8.quantize_per_token_int8 if per_token else i8.quantize_per_channel_int8
+    q, s = fn(t.to(dev))
+    qr, sr = ref.quantize_rows(view, dtype)
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    return q, s, qr, sr
+
+
+# ---------------------------------------------------------------------------------------
+# quantizers
+
+QSHAPES = [(1, 1), (3, 7), (5, 16), (37, 1001), (130, 1000), (64, 2560), (9, 12288),
+           (6, 16384), (4, 24600)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", QSHAPES)
+def test_quantize_rows_small(ref, dev, dtype, shape):
+    g = wl.rng(100 + shape[0])
+    a = g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+    if shape[0] > 2:
+        a[1] = 0.0                       # all-zero channel
+        a[2] *= np.float32(1e-4)         # small channel keeps its full range
+    a[:, g.choice(shape[1], 1)] *= np.float32(50.0)
+    t, view = host(dtype, a)
+    for per_token in (False, True):
+        quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token)
+
+
+def test_quantize_ties_and_subnormals(ref, dev):
+    s = 2.0 ** -7
+    halves = np.array([0.5, 1.5, 2.5, 62.5, 125.5, 126.5])
+    row = (np.concatenate([[127.0], halves, -halves, np.zeros(3)]) * s).astype(np.float32)
+    sub = np.array([1e-44, -5e-45, 3e-40, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0], np.float32)
+    a = np.stack([row, sub, np.ldexp(row, -130).astype(np.float32)])
+    for dtype in ("f32", "bf16"):
+        t, view = host(dtype, a)
+        quant_gpu_vs_ref(ref, dev, t, view, dtype)
+
+
+def test_quantize_unaligned_base_uses_the_general_path(ref, dev):
+    a = wl.weight(wl.rng(5), 33, 520)
+    t, view = host("bf16", a)
+    big = torch.empty(t.numel() + 1, dtype=torch.bfloat16, device=dev)
+    big[1:] = t.reshape(-1).to(dev)
+    q, s = i8.quantize_per_channel_int8(big[1:].view(33, 520))
+    qr, sr = ref.quantize_rows(view, "bf16")
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy(), sr)
+
+
+def test_quantize_guard_bands(ref, dev):
+    a = wl.weight(wl.rng(6), 45, 264)
+    t, view = host("bf16", a)
+    qbuf = torch.full((45 * 264 + 512,), 0x5A, dtype=torch.int8, device=dev)
+    sbuf = torch.full((45 + 64,), 7.0, dtype=torch.float32, device=dev)
+    q, s = i8.quantize_per_channel_int8(t.to(dev), qbuf[256:256 + 45 * 264].view(45, 264),
+                                        sbuf[32:32 + 45])
+    qr, sr = ref.quantize_rows(view, "bf16")
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    assert torch.all(qbuf[:256] == 0x5A) and torch.all(qbuf[256 + 45 * 264:] == 0x5A)
+    assert torch.all(sbuf[:32] == 7.0) and torch.all(sbuf[32 + 45:] == 7.0)
+
+
+WEIGHT_SHAPES = sorted(set(wl.DENSE_4B.values()) | set(wl.DENSE_8B.values()))
+
+
+@pytest.mark.parametrize("shape", WEIGHT_SHAPES)
+def test_quantize_decoder_weights_full(ref, dev, shape):
+    t, view = host("bf16", wl.weight(wl.rng(shape[0] + shape[1]), *shape))
+    quant_gpu_vs_ref(ref, dev, t, view, "bf16")
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_quantize_moe_expert_stack_full(ref, dev, proj):
+    n, k = wl.MOE_16B[proj]
+    w = wl.moe_weights(wl.rng(7), n, k).reshape(-1, k)
+    t, view = host("bf16", w)
+    quant_gpu_vs_ref(ref, dev, t, view, "bf16")
+
+
+@pytest.mark.parametrize("m,k,frac", [(2048, 2560, 0.001), (2048, 9728, 0.001),
+                                      (16384, 4096, 0.01), (16384, 12288, 0.01)])
+def test_quantize_prefill_activations_full(ref, dev, m, k, frac):
+    t, view = host("bf16", wl.activations(wl.rng(m + k), m, k, outlier_frac=frac))
+    quant_gpu_vs_ref(ref, dev, t, view, "bf16", per_token=True)
+
+
+# ---------------------------------------------------------------------------------------
+# W8A8
+
+def w8a8_case(g, m, n, k, wdtype="bf16"):
+    w = wl.weight(g, n, k)
+    x = wl.activations(g, m, k, outlier_frac=0.001)
+    return host(wdtype, w), host(wdtype, x)
+
+
+def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bfloat16),
+             seed=0, with_bias=(False, True)):
+    g = wl.rng(seed)
+    (wt, wv), (xt, xv) = w8a8_case(g, m, n, k)
+    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
+    qx, sx, qxr, sxr = quant_gpu_vs_ref(ref, dev, xt, xv, "bf16", per_token=True)
+    bias_np = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    for use_bias in with_bias:
+        b_np = bias_np if use_bias else None
+        acc, yref = ref.w8a8(qxr, sxr, qwr, swr, b_np)
+        for od in out_dtypes:
+            if od == torch.int32:
+                if use_bias:
+                    continue
+                y = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+                np.testing.assert_array_equal(y.cpu().numpy(), acc)
+                continue
+            b = torch.from_numpy(b_np).to(dev) if use_bias else None
+            y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=od)
+            check_float(y, yref, w8a8_tol(acc, sxr, swr, b_np), f"w8a8 {m}x{n}x{k} {od}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (4, 256, 512), (3, 130, 48), (130, 200, 272),
+                                   (257, 385, 1040), (128, 128, 128), (64, 700, 4096),
+                                   (300, 33, 2576)])
+def test_w8a8_small(ref, dev, m, n, k):
+    run_w8a8(ref, dev, m, n, k, seed=m * 7 + n)
+
+
+def test_w8a8_tiny_workload_end_to_end(ref, dev):
+    """fp32 weight [256,512] with 2 zero channels and a x50 column; 4 tokens with 2 x100
+    dims; per-channel + per-token int8, int32 GEMM, fp32 output; seed 0."""
+    t = wl.tiny_w8a8(0)
+    wt, wv = host("f32", t["w"])
+    xt, xv = host("f32", t["x"])
+    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "f32")
+    qx, sx, qxr, sxr = quant_gpu_vs_ref(ref, dev, xt, xv, "f32", per_token=True)
+    acc, yref = ref.w8a8(qxr, sxr, qwr, swr)
+    y = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32)
+    check_float(y, yref, w8a8_tol(acc, sxr, swr, None), "tiny w8a8")
+    yc = y.cpu().numpy()
+    for r in t["zero_rows"]:
+        assert np.all(yc[:, r] == 0.0)
+    np.testing.assert_array_equal(i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+                                  .cpu().numpy(), acc)
+
+
+def test_w8a8_extreme_accumulator(ref, dev):
+    k = 133136  # largest multiple of 16 below the int32 limit
+    xq = torch.full((2, k), 127, dtype=torch.int8, device=dev)
+    xq[1] = -127
+    wq = torch.full((3, k), 127, dtype=torch.int8, device=dev)
+    wq[2] = -127
+    y = i8.w8a8_gemm(xq, None, wq, None, out_dtype=torch.int32).cpu().numpy()
+    v = k * 127 * 127
+    np.testing.assert_array_equal(y, [[v, v, -v], [-v, -v, v]])
+
+
+def test_w8a8_deterministic_and_guarded(ref, dev):
+    g = wl.rng(3)
+    qx = torch.from_numpy(g.integers(-127, 128, (200, 1024), dtype=np.int8)).to(dev)
+    qw = torch.from_numpy(g.integers(-127, 128, (300, 1024), dtype=np.int8)).to(dev)
+    sx = torch.rand(200, device=dev) * 0.01
+    sw = torch.rand(300, device=dev) * 0.01
+    buf = torch.full((200 * 300 + 1024,), -7.0, dtype=torch.float32, device=dev)
+    y1 = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32, out=buf[512:512 + 60000].view(200, 300))
+    y2 = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32)
+    assert torch.equal(y1, y2)
+    assert torch.all(buf[:512] == -7.0) and torch.all(buf[512 + 60000:] == -7.0)
+
+
+def sampled_rows(m, n_rand=256, seed=0):
+    g = wl.rng(seed)
+    rows = set(range(min(8, m))) | set(range(max(0, m - 8), m))
+    rows |= set(g.choice(m, min(n_rand, m), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+PREFILL_4B = [(m, n, k) for m in wl.PREFILL_4B_TOKENS for (n, k) in wl.DENSE_4B.values()]
+PREFILL_8B = [(m, n, k) for m in wl.PREFILL_8B_TOKENS
+              for (n, k) in sorted(set(wl.DENSE_8B.values()))]
+
+
+def run_w8a8_full(ref, dev, m, n, k, frac, bias, seed):
+    g = wl.rng(seed)
+    wt, wv = host("bf16", wl.weight(g, n, k))
+    xt, xv = host("bf16", wl.activations(g, m, k, outlier_frac=frac))
+    b_np = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)) if bias else None
+    qw, sw = i8.quantize_per_channel_int8(wt.to(dev))
+    qx, sx = i8.quantize_per_token_int8(xt.to(dev))
+    b = torch.from_numpy(b_np).to(dev) if bias else None
+    y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=torch.bfloat16)
+    yi = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+    rows = sampled_rows(m, seed=seed)
+    qwr, swr = ref.quantize_rows(wv, "bf16")
+    np.testing.assert_array_equal(qw.cpu().numpy(), qwr)
+    np.testing.assert_array_equal(sw.cpu().numpy(), swr)
+    qxr, sxr = ref.quantize_rows(xv[rows], "bf16")
+    np.testing.assert_array_equal(qx[torch.from_numpy(rows).to(dev)].cpu().numpy(), qxr)
+    acc, yref = ref.w8a8(qxr, sxr, qwr, swr, b_np)
+    np.testing.assert_array_equal(yi.cpu().numpy()[rows], acc)
+    check_float(y[torch.from_numpy(rows).to(dev)], yref, w8a8_tol(acc, sxr, swr, b_np),
+                f"w8a8 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", PREFILL_4B)
+def test_w8a8_dense_4b_prefill_full(ref, dev, m, n, k):
+    run_w8a8_full(ref, dev, m, n, k, 0.001, False, seed=m + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", PREFILL_8B)
+def test_w8a8_dense_8b_prefill_full(ref, dev, m, n, k):
+    run_w8a8_full(ref, dev, m, n, k, 0.01, True, seed=m + n + k)
+
+
+# ---------------------------------------------------------------------------------------
+# W8A16
+
+def run_w8a16(ref, dev, m, n, k, bias, out_dtype, seed):
+    g = wl.rng(seed)
+    wt, wv = host("bf16", wl.weight(g, n, k))
+    xt, xv = host("bf16", wl.activations(g, m, k))
+    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
+    b_np = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)) if bias else None
+    b = torch.from_numpy(b_np).to(dev) if bias else None
+    y = i8.w8a16_gemm(xt.to(dev), qw, sw, b, out_dtype=out_dtype)
+    yref = ref.w8a16(xv, qwr, swr, b_np)
+    absdot = np.abs(xt.double().numpy()) @ (np.abs(qwr.astype(np.float64)) * swr[:, None]).T
+    check_float(y, yref, w8a16_tol(yref, absdot, k, b_np), f"w8a16 {m}x{n}x{k}")
+    return y
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 16), (1, 50, 208), (3, 130, 1040), (8, 256, 4096),
+                                   (16, 1000, 4096), (17, 100, 512), (33, 70, 272),
+                                   (70, 100, 256), (130, 45, 128)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_w8a16_small(ref, dev, m, n, k, out_dtype):
+    run_w8a16(ref, dev, m, n, k, bias=(m % 2 == 1), out_dtype=out_dtype, seed=m + n)
+
+
+DECODE_8B = [(m, n, k) for m in wl.DECODE_8B_BATCH for (n, k) in sorted(set(wl.DENSE_8B.values()))]
+
+
+@pytest.mark.parametrize("m,n,k", DECODE_8B)
+def test_w8a16_dense_8b_decode_full(ref, dev, m, n, k):
+    y1 = run_w8a16(ref, dev, m, n, k, bias=False, out_dtype=torch.bfloat16, seed=m * n + k)
+    # same inputs, same bits
+    g = wl.rng(m * n + k)
+    wt, _ = host("bf16", wl.weight(g, n, k))
+    xt, _ = host("bf16", wl.activations(g, m, k))
+    qw, sw = i8.quantize_per_channel_int8(wt.to(dev))
+    assert torch.equal(i8.w8a16_gemm(xt.to(dev), qw, sw), y1)
+
+
+# ---------------------------------------------------------------------------------------
+# grouped W8A16 over experts
+
+def moe_stack(ref, dev, g, n, k, e):
+    w = wl.moe_weights(g, n, k, experts=e).reshape(e * n, k)
+    wt, wv = host("bf16", w)
+    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
+    return qw.view(e, n, k), sw.view(e, n), qwr.reshape(e, n, k), swr.reshape(e, n)
+
+
+def run_grouped(ref, dev, qw, sw, qwr, swr, ids, x_rows, per_assign, out_dtype, g):
+    e, n, k = qwr.shape
+    xt, xv = host("bf16", wl.activations(g, x_rows, k))
+    y = i8.grouped_w8a16_gemm(xt.to(dev), qw, sw, torch.from_numpy(ids).to(dev),
+                              x_per_assignment=per_assign, out_dtype=out_dtype)
+    yref = ref.grouped_w8a16(xv, per_assign, qwr, swr, ids)
+    t, topk = ids.shape
+    xd = np.abs(xt.double().numpy())
+    absdot = np.zeros_like(yref)
+    for p in range(t * topk):
+        ex = ids.flat[p]
+        if 0 <= ex < e:
+            absdot[p] = (np.abs(qwr[ex].astype(np.float64)) * swr[ex][:, None]) @ \
+                xd[p if per_assign else p // topk]
+    check_float(y, yref, w8a16_tol(yref, absdot, k), f"grouped e={e} n={n} k={k} t={t}")
+    yc = to_np(y)
+    for p in range(t * topk):
+        if not 0 <= ids.flat[p] < e:
+            assert np.all(yc[p] == 0.0)
+    return y
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_small_edge_cases(ref, dev, out_dtype):
+    g = wl.rng(21)
+    e, n, k = 7, 40, 272
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.stack([g.choice(e, 3, replace=False) for _ in range(11)]).astype(np.int32)
+    ids[2, 1] = -1
+    ids[4, 0] = e      # out of range -> zero rows
+    ids[5] = 6         # one token routed three times to the same expert
+    for per_assign in (False, True):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, 33 if per_assign else 11, per_assign,
+                    out_dtype, g)
+
+
+def test_grouped_one_expert_equals_w8a16(ref, dev):
+    g = wl.rng(22)
+    n, k = 100, 512
+    qw, sw, _, _ = moe_stack(ref, dev, g, n, k, 1)
+    x = wl.to_bf16(wl.activations(g, 19, k)).to(dev)
+    yg = i8.grouped_w8a16_gemm(x, qw, sw, torch.zeros((19, 1), dtype=torch.int32, device=dev))
+    yd = i8.w8a16_gemm(x, qw[0], sw[0])
+    check_float(yg, to_np(yd).astype(np.float64), np.abs(to_np(yd)) * 1e-2 + 1e-3, "E=1")
+
+
+def test_grouped_many_rows_per_expert(ref, dev):
+    """More than 64 rows for one expert (several 64-row passes) and more than one 1024-entry
+    scan window."""
+    g = wl.rng(23)
+    e, n, k = 3, 48, 256
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = g.integers(0, e, size=(700, 2), dtype=np.int32)
+    ids[::97, 1] = 9
+    run_grouped(ref, dev, qw, sw, qwr, swr, ids, 700, False, torch.float32, g)
+
+
+@pytest.mark.parametrize("t", wl.MOE_TOKENS)
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_grouped_moe_16b_full(ref, dev, t, proj):
+    g = wl.rng(30 + t)
+    n, k = wl.MOE_16B[proj]
+    e = wl.MOE_ROUTED + wl.MOE_SHARED
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = wl.moe_expert_ids(g, t)
+    per_assign = proj == "down"
+    run_grouped(ref, dev, qw, sw, qwr, swr, ids, t * ids.shape[1] if per_assign else t,
+                per_assign, torch.bfloat16, g)
