@@ -1,0 +1,494 @@
+"""Benchmark of the int8 quantized linear hot path on one MI355X.
+
+A step is one pass of the W8A8 prefill path over the dense 4B decoder layer (q, k, v, o,
+gate, up, down projections) at M = 128, 512 and 2048 tokens: per-token int8 quantization
+of the four distinct layer inputs, then the seven int8 MFMA GEMMs with the fused scale
+epilogue to bf16.  ``value`` is the step's int8 throughput (2*M*N*K ops per GEMM summed,
+over the whole step time, quantization included), with every input resident in HBM.  Weight
+copies are rotated so every GEMM reads weights that are not in the 256 MB Infinity Cache.
+
+The same JSON line also carries the other rows of the path, each timed on its own workload:
+W8A16 decode on 8B shapes (M = 1, 4, 8), the grouped MoE W8A16 GEMM (T = 1..64 tokens),
+W8A8 prefill at scale on 8B shapes (M = 4096, 16384, with bias), and the per-channel weight
+quantizer; plus ``roofline`` for the dominant kernel (HIP-event durations of every launch
+of it in a second timed pass) and ``cpu_baseline`` (the CPU oracle on a bounded sample of
+the step).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections a,b,...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 GEMM TOPS (prefill) + decode GB/s, % of MI355X roofline"
+PEAK_INT8_TOPS = 5000.0     # dense int8 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0       # HBM3E, MI355X
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30      # rotate weight copies over at least this much memory
+
+KERNEL_SOURCES = {
+    "w8a8_kernel": "int8_quantized_linear_amd/csrc/w8a8_gemm.hip",
+    "w8a16_kernel": "int8_quantized_linear_amd/csrc/w8a16_gemm.hip",
+    "grouped_w8a16_kernel": "int8_quantized_linear_amd/csrc/grouped_w8a16.hip",
+    "quantize_rows_vec_kernel": "int8_quantized_linear_amd/csrc/quantize_rows.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    paths = [KERNEL_SOURCES[kernel]]
+    if "w8a16" in kernel:
+        paths.append("int8_quantized_linear_amd/csrc/dequant_mma.hpp")
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work (what the method must move or compute)
+
+def w8a8_ops(m, n, k):
+    return 2.0 * m * n * k
+
+
+def w8a8_bytes(m, n, k, out_bytes=2, bias=False):
+    return n * k + m * k + 4 * n + 4 * m + m * n * out_bytes + (4 * n if bias else 0)
+
+
+def w8a16_bytes(m, n, k, out_bytes=2, bias=False):
+    return n * k + 4 * n + 2 * m * k + m * n * out_bytes + (4 * n if bias else 0)
+
+
+def quant_bytes(r, k, in_bytes=2):
+    return r * k * in_bytes + r * k + 4 * r
+
+
+def grouped_bytes(distinct, n, k, x_rows, assignments, out_bytes=2):
+    return distinct * (n * k + 4 * n) + x_rows * k * 2 + assignments * n * out_bytes
+
+
+# ---------------------------------------------------------------------------------------
+
+class Timer:
+    """Per-launch HIP-event timing on torch's current stream (the kernels' stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, tag, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((tag, a, b))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        out = {}
+        for tag, a, b in self.pairs:
+            out.setdefault(tag, []).append(a.elapsed_time(b) * 1e-3)
+        return out
+
+
+def time_loop(torch, body, steps, warmup):
+    for i in range(warmup):
+        body(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        body(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3
+
+
+# ---------------------------------------------------------------------------------------
+# sections
+
+def prefill_4b_setup(torch, i8, wl, dev):
+    g = wl.rng(0)
+    names = list(wl.DENSE_4B)
+    q0, s0 = {}, {}
+    layer_bytes = 0
+    for nm in names:
+        n, k = wl.DENSE_4B[nm]
+        w = wl.to_bf16(wl.weight(g, n, k)).to(dev)
+        q0[nm], s0[nm] = i8.quantize_per_channel_int8(w)
+        layer_bytes += n * k
+        del w
+    copies = max(2, -(-ROTATE_BYTES // layer_bytes))
+    qs = [q0] + [{nm: q0[nm].clone() for nm in names} for _ in range(copies - 1)]
+    # layer inputs: attention input (q/k/v), attention output (o), MLP input (gate/up),
+    # MLP hidden (down); N(0,1) with 0.1% outlier dims x100
+    xs = {}
+    for m in wl.PREFILL_4B_TOKENS:
+        xs[m] = {
+            "attn_in": wl.to_bf16(wl.activations(g, m, 2560, 0.001)).to(dev),
+            "attn_out": wl.to_bf16(wl.activations(g, m, 4096, 0.001)).to(dev),
+            "mlp_in": wl.to_bf16(wl.activations(g, m, 2560, 0.001)).to(dev),
+            "mlp_mid": wl.to_bf16(wl.activations(g, m, 9728, 0.001)).to(dev),
+        }
+    src = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out", "gate": "mlp_in",
+           "up": "mlp_in", "down": "mlp_mid"}
+    # preallocated outputs
+    outs = {m: {nm: torch.empty((m, wl.DENSE_4B[nm][0]), dtype=torch.bfloat16, device=dev)
+                for nm in names} for m in wl.PREFILL_4B_TOKENS}
+    qx = {m: {key: (torch.empty(x.shape, dtype=torch.int8, device=dev),
+                    torch.empty((x.shape[0],), dtype=torch.float32, device=dev))
+              for key, x in xs[m].items()} for m in wl.PREFILL_4B_TOKENS}
+    return dict(qs=qs, s=s0, xs=xs, src=src, outs=outs, qx=qx, names=names, copies=copies)
+
+
+def prefill_4b_step(i8, wl, st, step, timer=None):
+    run = (lambda tag, f: timer.run(tag, f)) if timer else (lambda tag, f: f())
+    for mi, m in enumerate(wl.PREFILL_4B_TOKENS):
+        wq = st["qs"][(step * len(wl.PREFILL_4B_TOKENS) + mi) % st["copies"]]
+        for key, x in st["xs"][m].items():
+            q, s = st["qx"][m][key]
+            run("quantize_rows_vec_kernel", lambda x=x, q=q, s=s: i8.quantize_per_token_int8(x, q, s))
+        for nm in st["names"]:
+            q, s = st["qx"][m][st["src"][nm]]
+            run("w8a8_kernel", lambda nm=nm, q=q, s=s: i8.w8a8_gemm(
+                q, s, wq[nm], st["s"][nm], None, out=st["outs"][m][nm]))
+
+
+def prefill_4b_work():
+    import int8_quantized_linear_amd.workloads as wl
+    ops = sum(w8a8_ops(m, n, k) for m in wl.PREFILL_4B_TOKENS for (n, k) in wl.DENSE_4B.values())
+    return ops
+
+
+def section_step(torch, i8, wl, dev, args, result):
+    st = prefill_4b_setup(torch, i8, wl, dev)
+    ops = prefill_4b_work()
+    log(f"[step] dense 4B W8A8 prefill, {st['copies']} weight copies; warmup {args.warmup}, "
+        f"steps {args.steps}")
+    secs = time_loop(torch, lambda i: prefill_4b_step(i8, wl, st, i), args.steps, args.warmup)
+    ms = secs / args.steps * 1e3
+    result.update(value=ops / (secs / args.steps) / 1e12, ms_per_step=ms)
+    log(f"[step] {ms:.4f} ms/step, {result['value']:.1f} TOPS")
+
+    # second timed pass: every launch bracketed by HIP events, per kernel
+    timer = Timer(torch)
+    for i in range(args.steps):
+        prefill_4b_step(i8, wl, st, args.warmup + args.steps + i, timer)
+    durs = timer.summary()
+    gemm_ops_per_step = ops
+    n_gemm = len(durs["w8a8_kernel"])
+    avg = float(np.mean(durs["w8a8_kernel"]))
+    ach = gemm_ops_per_step * args.steps / n_gemm / avg / 1e12
+    result["roofline"] = {
+        "kernel": "w8a8_kernel", "bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS,
+        "unit": "TFLOP/s", "frac": ach / PEAK_INT8_TOPS,
+        "traffic": traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"),
+        "avg_launch_us": avg * 1e6, "launches": n_gemm,
+        "ops_per_launch": gemm_ops_per_step * args.steps / n_gemm,
+    }
+    qd = durs["quantize_rows_vec_kernel"]
+    qbytes = sum(quant_bytes(m, k) for m in wl.PREFILL_4B_TOKENS for k in (2560, 4096, 2560, 9728))
+    result["parts"] = {
+        "w8a8_gemm_ms_per_step": float(np.sum(durs["w8a8_kernel"])) / args.steps * 1e3,
+        "quantize_per_token_ms_per_step": float(np.sum(qd)) / args.steps * 1e3,
+        "quantize_per_token_GBs": qbytes * args.steps / float(np.sum(qd)) / 1e9,
+    }
+    # per shape (median over steps)
+    per = {}
+    names = st["names"]
+    idx = 0
+    shapes = [(m, nm) for m in wl.PREFILL_4B_TOKENS for nm in names]
+    gem = durs["w8a8_kernel"]
+    for s_i in range(args.steps):
+        for (m, nm) in shapes:
+            per.setdefault((m, nm), []).append(gem[idx])
+            idx += 1
+    result["per_shape"] = []
+    for (m, nm), d in per.items():
+        n, k = wl.DENSE_4B[nm]
+        t = float(np.median(d))
+        result["per_shape"].append({
+            "m": m, "n": n, "k": k, "proj": nm, "us": t * 1e6,
+            "TOPS": w8a8_ops(m, n, k) / t / 1e12,
+            "frac_mfma": w8a8_ops(m, n, k) / t / 1e12 / PEAK_INT8_TOPS,
+            "frac_hbm": w8a8_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS})
+    return st
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    ent = data.get(kernel, {}).get(workload)
+    if not ent or ent.get("source_sha") != source_sha(kernel):
+        return None
+    return ent["bytes_per_launch"]
+
+
+def section_cpu_baseline(i8, wl, args, result):
+    import oracle
+    ref = oracle.load()
+    threads = len(os.sched_getaffinity(0))
+    ref.set_threads(threads)
+    g = wl.rng(0)
+    frac = 4
+    ws = {nm: wl.bits16(wl.to_bf16(wl.weight(g, n, k))) for nm, (n, k) in wl.DENSE_4B.items()}
+    wq = {nm: ref.quantize_rows(w, "bf16") for nm, w in ws.items()}
+    ins = {"q": 2560, "k": 2560, "v": 2560, "o": 4096, "gate": 2560, "up": 2560, "down": 9728}
+    keys = {"attn_in": 2560, "attn_out": 4096, "mlp_in": 2560, "mlp_mid": 9728}
+    src = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out", "gate": "mlp_in",
+           "up": "mlp_in", "down": "mlp_mid"}
+    rows_total = 0
+    xs = {}
+    for m in wl.PREFILL_4B_TOKENS:
+        r = m // frac
+        rows_total += r
+        xs[m] = {key: wl.bits16(wl.to_bf16(wl.activations(g, r, k, 0.001)))
+                 for key, k in keys.items()}
+    ops = 0.0
+    t0 = time.perf_counter()
+    for m in wl.PREFILL_4B_TOKENS:
+        qx = {key: ref.quantize_rows(x, "bf16") for key, x in xs[m].items()}
+        for nm in wl.DENSE_4B:
+            q, s = qx[src[nm]]
+            n, k = wl.DENSE_4B[nm]
+            ref.w8a8(q, s, wq[nm][0], wq[nm][1])
+            ops += w8a8_ops(q.shape[0], n, k)
+    dt = time.perf_counter() - t0
+    result["cpu_baseline"] = {
+        "value": ops / dt / 1e12, "unit": "TOPS", "cores": ref.threads(), "kind": "oracle",
+        "sample": f"the step's first 1/{frac} of tokens at each M ({rows_total} of "
+                  f"{sum(wl.PREFILL_4B_TOKENS)} token rows, all 7 projections): per-token "
+                  f"quantization + int32 GEMM + float64 epilogue; {dt:.1f} s",
+        "seconds": dt}
+    log(f"[cpu_baseline] {ops/dt/1e12*1e3:.2f} GOP/s on {ref.threads()} threads, {dt:.1f} s")
+
+
+def section_decode(torch, i8, wl, dev, args, result):
+    g = wl.rng(1)
+    shapes = wl.DENSE_8B
+    names = list(shapes)
+    layer = sum(n * k for n, k in shapes.values())
+    copies = max(2, -(-ROTATE_BYTES // layer))
+    q0, s0 = {}, {}
+    for nm in names:
+        n, k = shapes[nm]
+        q0[nm], s0[nm] = i8.quantize_per_channel_int8(wl.to_bf16(wl.weight(g, n, k)).to(dev))
+    qs = [q0] + [{nm: q0[nm].clone() for nm in names} for _ in range(copies - 1)]
+    out = {"copies": copies, "per_m": {}}
+    for m in wl.DECODE_8B_BATCH:
+        xs = {k: wl.to_bf16(wl.activations(g, m, k)).to(dev) for k in (4096, 12288)}
+        ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in names}
+        timer = Timer(torch)
+
+        def body(i, timer=None):
+            wq = qs[i % copies]
+            for nm in names:
+                n, k = shapes[nm]
+                f = lambda nm=nm, k=k: i8.w8a16_gemm(xs[k], wq[nm], s0[nm], out=ys[nm])
+                timer.run(nm, f) if timer else f()
+        secs = time_loop(torch, body, args.steps, args.warmup)
+        for i in range(args.steps):
+            body(args.warmup + args.steps + i, timer)
+        durs = timer.summary()
+        nbytes = sum(w8a16_bytes(m, n, k) for n, k in shapes.values())
+        per = {}
+        for nm in names:
+            n, k = shapes[nm]
+            t = float(np.median(durs[nm]))
+            per[nm] = {"n": n, "k": k, "us": t * 1e6,
+                       "GBs": w8a16_bytes(m, n, k) / t / 1e9,
+                       "frac_hbm": w8a16_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS}
+        allk = sum(float(np.sum(d)) for d in durs.values())
+        gbs_kernels = nbytes * args.steps / allk / 1e9
+        out["per_m"][m] = {"layer_us": secs / args.steps * 1e6,
+                           "GBs_layer": nbytes / (secs / args.steps) / 1e9,
+                           "GBs_kernels": gbs_kernels,
+                           "frac_hbm_kernels": gbs_kernels / PEAK_HBM_GBS,
+                           "per_proj": per}
+        log(f"[decode] M={m}: {secs/args.steps*1e6:.1f} us/layer, kernels {gbs_kernels:.0f} GB/s")
+    m1 = out["per_m"][1]
+    result["decode"] = {"workload": "dense 8B decoder projections, W8A16 decode, M in {1,4,8}",
+                        "value": m1["GBs_kernels"], "unit": "GB/s",
+                        "frac_hbm": m1["frac_hbm_kernels"], **out}
+
+
+def section_moe(torch, i8, wl, dev, args, result):
+    g = wl.rng(2)
+    e = wl.MOE_ROUTED + wl.MOE_SHARED
+    stacks = {}
+    for proj, (n, k) in wl.MOE_16B.items():
+        w = wl.to_bf16(wl.moe_weights(g, n, k).reshape(e * n, k)).to(dev)
+        q, s = i8.quantize_per_channel_int8(w)
+        del w
+        stacks[proj] = (q.view(e, n, k), s.view(e, n))
+    per_layer = sum(e * n * k for n, k in wl.MOE_16B.values())
+    copies = max(2, -(-ROTATE_BYTES // per_layer))
+    rot = [stacks] + [{p: (q.clone(), s) for p, (q, s) in stacks.items()} for _ in range(copies - 1)]
+    out = {"copies": copies, "per_t": {}}
+    for t in wl.MOE_TOKENS:
+        ids = wl.moe_expert_ids(g, t)
+        distinct = len(np.unique(ids))
+        ids_d = torch.from_numpy(ids).to(dev)
+        topk = ids.shape[1]
+        x_in = wl.to_bf16(wl.activations(g, t, 2048)).to(dev)
+        x_mid = wl.to_bf16(wl.activations(g, t * topk, 1408)).to(dev)
+        ys = {p: torch.empty((t * topk, wl.MOE_16B[p][0]), dtype=torch.bfloat16, device=dev)
+              for p in wl.MOE_16B}
+        timer = Timer(torch)
+
+        def body(i, timer=None):
+            st = rot[i % copies]
+            for p in ("gate", "up", "down"):
+                q, s = st[p]
+                x, pa = (x_mid, True) if p == "down" else (x_in, False)
+                f = lambda q=q, s=s, x=x, pa=pa, p=p: i8.grouped_w8a16_gemm(
+                    x, q, s, ids_d, x_per_assignment=pa, out=ys[p])
+                timer.run(p, f) if timer else f()
+        secs = time_loop(torch, body, args.steps, args.warmup)
+        for i in range(args.steps):
+            body(args.warmup + args.steps + i, timer)
+        durs = timer.summary()
+        nbytes = 0.0
+        per = {}
+        for p, (n, k) in wl.MOE_16B.items():
+            xr = t * topk if p == "down" else t
+            b = grouped_bytes(distinct, n, k, xr, t * topk)
+            nbytes += b
+            d = float(np.median(durs[p]))
+            per[p] = {"us": d * 1e6, "GBs": b / d / 1e9, "frac_hbm": b / d / 1e9 / PEAK_HBM_GBS}
+        allk = sum(float(np.sum(d)) for d in durs.values())
+        out["per_t"][t] = {"distinct_experts": distinct, "layer_us": secs / args.steps * 1e6,
+                           "GBs_kernels": nbytes * args.steps / allk / 1e9,
+                           "frac_hbm_kernels": nbytes * args.steps / allk / 1e9 / PEAK_HBM_GBS,
+                           "per_proj": per}
+        log(f"[moe] T={t}: {distinct} experts, {secs/args.steps*1e6:.1f} us/layer, "
+            f"{out['per_t'][t]['GBs_kernels']:.0f} GB/s")
+    result["moe"] = {"workload": "16B MoE block (64 routed + 2 shared experts, top-6), grouped "
+                     "W8A16 gate/up/down, T in {1,4,16,64}", "unit": "GB/s", **out}
+
+
+def section_prefill_8b(torch, i8, wl, dev, args, result):
+    g = wl.rng(3)
+    shapes = wl.DENSE_8B
+    qw, sw, bias = {}, {}, {}
+    for nm, (n, k) in shapes.items():
+        qw[nm], sw[nm] = i8.quantize_per_channel_int8(wl.to_bf16(wl.weight(g, n, k)).to(dev))
+        bias[nm] = torch.from_numpy(g.standard_normal(n, dtype=np.float32) * np.float32(0.02)).to(dev)
+    out = {"per_m": {}}
+    steps = max(3, args.steps // 10)
+    for m in wl.PREFILL_8B_TOKENS:
+        xq = {}
+        for k in (4096, 12288):
+            x = wl.to_bf16(wl.activations(g, m, k, 0.01)).to(dev)
+            xq[k] = i8.quantize_per_token_int8(x)
+            del x
+        ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in shapes}
+        timer = Timer(torch)
+
+        def body(i, timer=None):
+            for nm, (n, k) in shapes.items():
+                q, s = xq[k]
+                f = lambda nm=nm, q=q, s=s: i8.w8a8_gemm(q, s, qw[nm], sw[nm], bias[nm], out=ys[nm])
+                timer.run(nm, f) if timer else f()
+        secs = time_loop(torch, body, steps, max(1, args.warmup // 5))
+        for i in range(steps):
+            body(i, timer)
+        durs = timer.summary()
+        ops = sum(w8a8_ops(m, n, k) for n, k in shapes.values())
+        per = {}
+        for nm, (n, k) in shapes.items():
+            d = float(np.median(durs[nm]))
+            per[nm] = {"us": d * 1e6, "TOPS": w8a8_ops(m, n, k) / d / 1e12,
+                       "frac_mfma": w8a8_ops(m, n, k) / d / 1e12 / PEAK_INT8_TOPS}
+        out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": ops / (secs / steps) / 1e12,
+                           "frac_mfma": ops / (secs / steps) / 1e12 / PEAK_INT8_TOPS,
+                           "per_proj": per}
+        log(f"[prefill_8b] M={m}: {out['per_m'][m]['TOPS']:.0f} TOPS")
+    result["prefill_8b"] = {"workload": "dense 8B decoder projections, W8A8 prefill with bias, "
+                            "M in {4096,16384}", "unit": "TOPS", **out}
+
+
+def section_weight_quant(torch, i8, wl, dev, args, result):
+    g = wl.rng(4)
+    ws = {nm: wl.to_bf16(wl.weight(g, n, k)).to(dev) for nm, (n, k) in wl.DENSE_8B.items()}
+    outs = {nm: (torch.empty(w.shape, dtype=torch.int8, device=dev),
+                 torch.empty((w.shape[0],), dtype=torch.float32, device=dev)) for nm, w in ws.items()}
+    steps = max(3, args.steps // 10)
+    secs = time_loop(torch, lambda i: [i8.quantize_per_channel_int8(w, *outs[nm]) for nm, w in ws.items()],
+                     steps, 2)
+    nbytes = sum(quant_bytes(*w.shape) for w in ws.values())
+    gbs = nbytes / (secs / steps) / 1e9
+    result["weight_quant"] = {"workload": "per-channel quantization of the dense 8B layer's bf16 "
+                              "weights", "GBs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    log(f"[weight_quant] {gbs:.0f} GB/s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sections", default="step,cpu_baseline,decode,moe,prefill_8b,weight_quant")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards as described in DESIGN.md, but only the 1-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_quantized_linear_amd as i8
+    from int8_quantized_linear_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    i8.load_library()
+    dev = torch.device("cuda:0")
+    sections = args.sections.split(",")
+    result = {"metric": METRIC, "value": None, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+              "config": {"workload": "dense 4B decoder projections (q 2560->4096, k/v "
+                         "2560->1024, o 4096->2560, gate/up 2560->9728, down 9728->2560), "
+                         "W8A8 prefill: per-token int8 quantization + int8 MFMA GEMM + "
+                         "scale epilogue to bf16, M in {128, 512, 2048} tokens per step",
+                         "tokens_per_step": sum(wl.PREFILL_4B_TOKENS),
+                         "weights": "bf16 N(0,0.02) -> per-channel int8",
+                         "activations": "bf16 N(0,1), 0.1% outlier dims x100"},
+              "device": torch.cuda.get_device_name(0)}
+    if "step" in sections:
+        section_step(torch, i8, wl, dev, args, result)
+    if "cpu_baseline" in sections:
+        section_cpu_baseline(i8, wl, args, result)
+    if "decode" in sections:
+        section_decode(torch, i8, wl, dev, args, result)
+    if "moe" in sections:
+        section_moe(torch, i8, wl, dev, args, result)
+    if "prefill_8b" in sections:
+        section_prefill_8b(torch, i8, wl, dev, args, result)
+    if "weight_quant" in sections:
+        section_weight_quant(torch, i8, wl, dev, args, result)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
