@@ -83,27 +83,9 @@ def grouped_bytes(distinct, n, k, x_rows, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------------------------------
 
-class Timer:
-    """Per-launch HIP-event timing on torch's current stream (the kernels' stream)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def run(self, tag, fn):
-        t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pairs.append((tag, a, b))
-
-    def summary(self):
-        self.torch.cuda.synchronize()
-        out = {}
-        for tag, a, b in self.pairs:
-            out.setdefault(tag, []).append(a.elapsed_time(b) * 1e-3)
-        return out
+def per_call(torch, fn, reps, warmup=2):
+    """Average seconds per call of fn(i), timed back to back between two HIP events."""
+    return time_loop(torch, fn, reps, warmup) / reps
 
 
 def time_loop(torch, body, steps, warmup):
@@ -156,17 +138,15 @@ def prefill_4b_setup(torch, i8, wl, dev):
     return dict(qs=qs, s=s0, xs=xs, src=src, outs=outs, qx=qx, names=names, copies=copies)
 
 
-def prefill_4b_step(i8, wl, st, step, timer=None):
-    run = (lambda tag, f: timer.run(tag, f)) if timer else (lambda tag, f: f())
+def prefill_4b_step(i8, wl, st, step):
     for mi, m in enumerate(wl.PREFILL_4B_TOKENS):
         wq = st["qs"][(step * len(wl.PREFILL_4B_TOKENS) + mi) % st["copies"]]
         for key, x in st["xs"][m].items():
             q, s = st["qx"][m][key]
-            run("quantize_rows_vec_kernel", lambda x=x, q=q, s=s: i8.quantize_per_token_int8(x, q, s))
+            i8.quantize_per_token_int8(x, q, s)
         for nm in st["names"]:
             q, s = st["qx"][m][st["src"][nm]]
-            run("w8a8_kernel", lambda nm=nm, q=q, s=s: i8.w8a8_gemm(
-                q, s, wq[nm], st["s"][nm], None, out=st["outs"][m][nm]))
+            i8.w8a8_gemm(q, s, wq[nm], st["s"][nm], None, out=st["outs"][m][nm])
 
 
 def prefill_4b_work():
@@ -185,43 +165,45 @@ def section_step(torch, i8, wl, dev, args, result):
     result.update(value=ops / (secs / args.steps) / 1e12, ms_per_step=ms)
     log(f"[step] {ms:.4f} ms/step, {result['value']:.1f} TOPS")
 
-    # second timed pass: every launch bracketed by HIP events, per kernel
-    timer = Timer(torch)
-    for i in range(args.steps):
-        prefill_4b_step(i8, wl, st, args.warmup + args.steps + i, timer)
-    durs = timer.summary()
-    gemm_ops_per_step = ops
-    n_gemm = len(durs["w8a8_kernel"])
-    avg = float(np.mean(durs["w8a8_kernel"]))
-    ach = gemm_ops_per_step * args.steps / n_gemm / avg / 1e12
+    # Roofline pass: every GEMM and quantizer launch of the step, each repeated `reps` times
+    # back to back between two HIP events on the kernels' stream (torch's current stream),
+    # with the weight copies rotating exactly as in the step.  Events around single launches
+    # would add their own overhead to every launch.
+    reps = max(5, args.steps // 5)
+    names = st["names"]
+    gemm_t, quant_t = {}, {}
+    for mi, m in enumerate(wl.PREFILL_4B_TOKENS):
+        for key, x in st["xs"][m].items():
+            q, s_ = st["qx"][m][key]
+            sec = time_loop(torch, lambda i, x=x, q=q, s_=s_: i8.quantize_per_token_int8(x, q, s_),
+                            reps, 2)
+            quant_t[(m, key)] = sec / reps
+        for nm in names:
+            q, s_ = st["qx"][m][st["src"][nm]]
+            sec = time_loop(torch, lambda i, nm=nm, q=q, s_=s_, m=m: i8.w8a8_gemm(
+                q, s_, st["qs"][i % st["copies"]][nm], st["s"][nm], None, out=st["outs"][m][nm]),
+                reps, 2)
+            gemm_t[(m, nm)] = sec / reps
+    n_gemm = len(gemm_t)
+    avg = sum(gemm_t.values()) / n_gemm
+    ach = ops / sum(gemm_t.values()) / 1e12
     result["roofline"] = {
-        "kernel": "w8a8_kernel", "bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS,
-        "unit": "TFLOP/s", "frac": ach / PEAK_INT8_TOPS,
+        "kernel": "w8a8_kernel (both tile instantiations)", "bound": "mfma", "achieved": ach,
+        "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": ach / PEAK_INT8_TOPS,
         "traffic": traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"),
-        "avg_launch_us": avg * 1e6, "launches": n_gemm,
-        "ops_per_launch": gemm_ops_per_step * args.steps / n_gemm,
+        "avg_launch_us": avg * 1e6, "launches_per_step": n_gemm,
+        "ops_per_launch": ops / n_gemm,
     }
-    qd = durs["quantize_rows_vec_kernel"]
+    qsum = sum(quant_t.values())
     qbytes = sum(quant_bytes(m, k) for m in wl.PREFILL_4B_TOKENS for k in (2560, 4096, 2560, 9728))
     result["parts"] = {
-        "w8a8_gemm_ms_per_step": float(np.sum(durs["w8a8_kernel"])) / args.steps * 1e3,
-        "quantize_per_token_ms_per_step": float(np.sum(qd)) / args.steps * 1e3,
-        "quantize_per_token_GBs": qbytes * args.steps / float(np.sum(qd)) / 1e9,
+        "w8a8_gemm_ms_per_step": sum(gemm_t.values()) * 1e3,
+        "quantize_per_token_ms_per_step": qsum * 1e3,
+        "quantize_per_token_GBs": qbytes / qsum / 1e9,
     }
-    # per shape (median over steps)
-    per = {}
-    names = st["names"]
-    idx = 0
-    shapes = [(m, nm) for m in wl.PREFILL_4B_TOKENS for nm in names]
-    gem = durs["w8a8_kernel"]
-    for s_i in range(args.steps):
-        for (m, nm) in shapes:
-            per.setdefault((m, nm), []).append(gem[idx])
-            idx += 1
     result["per_shape"] = []
-    for (m, nm), d in per.items():
+    for (m, nm), t in gemm_t.items():
         n, k = wl.DENSE_4B[nm]
-        t = float(np.median(d))
         result["per_shape"].append({
             "m": m, "n": n, "k": k, "proj": nm, "us": t * 1e6,
             "TOPS": w8a8_ops(m, n, k) / t / 1e12,
@@ -297,28 +279,24 @@ def section_decode(torch, i8, wl, dev, args, result):
     for m in wl.DECODE_8B_BATCH:
         xs = {k: wl.to_bf16(wl.activations(g, m, k)).to(dev) for k in (4096, 12288)}
         ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in names}
-        timer = Timer(torch)
-
-        def body(i, timer=None):
+        def body(i):
             wq = qs[i % copies]
             for nm in names:
                 n, k = shapes[nm]
-                f = lambda nm=nm, k=k: i8.w8a16_gemm(xs[k], wq[nm], s0[nm], out=ys[nm])
-                timer.run(nm, f) if timer else f()
+                i8.w8a16_gemm(xs[k], wq[nm], s0[nm], out=ys[nm])
         secs = time_loop(torch, body, args.steps, args.warmup)
-        for i in range(args.steps):
-            body(args.warmup + args.steps + i, timer)
-        durs = timer.summary()
+        reps = max(5, args.steps // 5)
+        durs = {nm: per_call(torch, lambda i, nm=nm: i8.w8a16_gemm(
+            xs[shapes[nm][1]], qs[i % copies][nm], s0[nm], out=ys[nm]), reps) for nm in names}
         nbytes = sum(w8a16_bytes(m, n, k) for n, k in shapes.values())
         per = {}
         for nm in names:
             n, k = shapes[nm]
-            t = float(np.median(durs[nm]))
+            t = durs[nm]
             per[nm] = {"n": n, "k": k, "us": t * 1e6,
                        "GBs": w8a16_bytes(m, n, k) / t / 1e9,
                        "frac_hbm": w8a16_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS}
-        allk = sum(float(np.sum(d)) for d in durs.values())
-        gbs_kernels = nbytes * args.steps / allk / 1e9
+        gbs_kernels = nbytes / sum(durs.values()) / 1e9
         out["per_m"][m] = {"layer_us": secs / args.steps * 1e6,
                            "GBs_layer": nbytes / (secs / args.steps) / 1e9,
                            "GBs_kernels": gbs_kernels,
@@ -353,32 +331,27 @@ def section_moe(torch, i8, wl, dev, args, result):
         x_mid = wl.to_bf16(wl.activations(g, t * topk, 1408)).to(dev)
         ys = {p: torch.empty((t * topk, wl.MOE_16B[p][0]), dtype=torch.bfloat16, device=dev)
               for p in wl.MOE_16B}
-        timer = Timer(torch)
+        def call(p, i):
+            q, s_ = rot[i % copies][p]
+            x, pa = (x_mid, True) if p == "down" else (x_in, False)
+            i8.grouped_w8a16_gemm(x, q, s_, ids_d, x_per_assignment=pa, out=ys[p])
 
-        def body(i, timer=None):
-            st = rot[i % copies]
-            for p in ("gate", "up", "down"):
-                q, s = st[p]
-                x, pa = (x_mid, True) if p == "down" else (x_in, False)
-                f = lambda q=q, s=s, x=x, pa=pa, p=p: i8.grouped_w8a16_gemm(
-                    x, q, s, ids_d, x_per_assignment=pa, out=ys[p])
-                timer.run(p, f) if timer else f()
-        secs = time_loop(torch, body, args.steps, args.warmup)
-        for i in range(args.steps):
-            body(args.warmup + args.steps + i, timer)
-        durs = timer.summary()
+        secs = time_loop(torch, lambda i: [call(p, i) for p in ("gate", "up", "down")],
+                         args.steps, args.warmup)
+        reps = max(5, args.steps // 5)
+        durs = {p: per_call(torch, lambda i, p=p: call(p, i), reps) for p in wl.MOE_16B}
         nbytes = 0.0
         per = {}
         for p, (n, k) in wl.MOE_16B.items():
             xr = t * topk if p == "down" else t
             b = grouped_bytes(distinct, n, k, xr, t * topk)
             nbytes += b
-            d = float(np.median(durs[p]))
+            d = durs[p]
             per[p] = {"us": d * 1e6, "GBs": b / d / 1e9, "frac_hbm": b / d / 1e9 / PEAK_HBM_GBS}
-        allk = sum(float(np.sum(d)) for d in durs.values())
+        allk = sum(durs.values())
         out["per_t"][t] = {"distinct_experts": distinct, "layer_us": secs / args.steps * 1e6,
-                           "GBs_kernels": nbytes * args.steps / allk / 1e9,
-                           "frac_hbm_kernels": nbytes * args.steps / allk / 1e9 / PEAK_HBM_GBS,
+                           "GBs_kernels": nbytes / allk / 1e9,
+                           "frac_hbm_kernels": nbytes / allk / 1e9 / PEAK_HBM_GBS,
                            "per_proj": per}
         log(f"[moe] T={t}: {distinct} experts, {secs/args.steps*1e6:.1f} us/layer, "
             f"{out['per_t'][t]['GBs_kernels']:.0f} GB/s")
@@ -402,21 +375,18 @@ def section_prefill_8b(torch, i8, wl, dev, args, result):
             xq[k] = i8.quantize_per_token_int8(x)
             del x
         ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in shapes}
-        timer = Timer(torch)
+        def call(nm):
+            n, k = shapes[nm]
+            q, s_ = xq[k]
+            i8.w8a8_gemm(q, s_, qw[nm], sw[nm], bias[nm], out=ys[nm])
 
-        def body(i, timer=None):
-            for nm, (n, k) in shapes.items():
-                q, s = xq[k]
-                f = lambda nm=nm, q=q, s=s: i8.w8a8_gemm(q, s, qw[nm], sw[nm], bias[nm], out=ys[nm])
-                timer.run(nm, f) if timer else f()
-        secs = time_loop(torch, body, steps, max(1, args.warmup // 5))
-        for i in range(steps):
-            body(i, timer)
-        durs = timer.summary()
+        secs = time_loop(torch, lambda i: [call(nm) for nm in shapes], steps,
+                         max(1, args.warmup // 5))
+        durs = {nm: per_call(torch, lambda i, nm=nm: call(nm), steps, 1) for nm in shapes}
         ops = sum(w8a8_ops(m, n, k) for n, k in shapes.values())
         per = {}
         for nm, (n, k) in shapes.items():
-            d = float(np.median(durs[nm]))
+            d = durs[nm]
             per[nm] = {"us": d * 1e6, "TOPS": w8a8_ops(m, n, k) / d / 1e12,
                        "frac_mfma": w8a8_ops(m, n, k) / d / 1e12 / PEAK_INT8_TOPS}
         out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": ops / (secs / steps) / 1e12,

@@ -12,33 +12,34 @@
 //               or acc itself for int32 output.
 //
 // Data movement.  Both operands are K-contiguous (the nn.Linear [out, in] layout and
-// row-major tokens).  A workgroup owns a BM x BN output tile and walks k in 64-byte steps.
-// Each step's A and B slices are copied global -> LDS by the gfx950 direct-to-LDS loads
-// (global_load_lds_dwordx4: 16 bytes per lane, a wavefront fills 1 KiB of LDS = 16 rows x 64
-// bytes), so no VGPRs hold staged data and STAGES - 1 future steps stay in flight while the
-// current one is multiplied.  Each iteration waits (s_waitcnt vmcnt) for its own step's
-// loads, passes one barrier (which also retires the reads of the stage about to be
-// refilled), issues the loads of step t + STAGES - 1, then runs the MFMAs.
+// row-major tokens).  A workgroup of 4 wavefronts owns a BM x BN output tile and walks k in
+// steps of BK bytes.  Each step's A and B slices are copied global -> LDS by the gfx950
+// direct-to-LDS loads (global_load_lds_dwordx4: 16 bytes per lane, one wavefront
+// instruction fills 1 KiB = 1024 / BK rows), so no VGPRs hold staged data and up to STAGES
+// steps are in flight.  Each step waits (s_waitcnt vmcnt) for its own loads, passes one
+// barrier, which also retires the reads of the stage about to be refilled, and refills that
+// stage with the step STAGES ahead.
 //
-// LDS layout.  A stage holds BM + BN rows of 64 bytes.  The four 16-byte chunks of row r are
-// stored XOR-swizzled (physical chunk = logical chunk ^ ((r >> 1) & 3)) so that the 16-byte
-// fragment reads of eight consecutive lanes hit eight distinct bank groups; the swizzle is
-// applied on the global side (each lane fetches the logical chunk that belongs in its
-// fixed LDS slot).
+// LDS layout.  A stage holds BM + BN rows of BK bytes.  The BK / 16 chunks of each row are
+// XOR-swizzled (see swizzle()) so that the 16-byte fragment reads of a wavefront are free
+// of bank conflicts; the swizzle is applied on the global side (each lane fetches the
+// logical chunk that belongs in its fixed LDS slot).
 //
-// MFMA.  Each wavefront owns a (BM / WAVES_M) x (BN / WAVES_N) sub-tile of 32 x 32 blocks of
+// MFMA.  Each wavefront owns a (BM / 2) x (BN / 2) sub-tile of 32 x 32 blocks of
 // v_mfma_i32_32x32x32_i8.  Fragment layout: lane l supplies row l % 32 of a 32-row block and
-// 16 consecutive k of the 32-k slice at offset 16 * (l / 32); A and B use the same k
+// 16 consecutive k of a 32-k slice at offset 16 * (l / 32); A and B use the same k
 // assignment, which is all the sum needs.  Accumulator: lane l, register r holds row
-// 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the block.
+// 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the block.  The k loop is
+// software-pipelined one 32-k slice ahead: the fragments of slice s + 1 are read while the
+// MFMAs of slice s run, and the barrier of step t + 1 sits between the last slice's reads
+// and its MFMAs.
 //
 // Tails.  Rows past m or n read a clamped valid row and are never stored.  Chunks past k
-// (k % 16 == 0, so chunks are whole) read the row start and are zeroed at fragment-read time
-// in the last step.
+// (k % 16 == 0, so chunks are whole) read the row start; once the last step has landed its
+// A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
-// Configurations: 256 x 256 with 8 wavefronts (128 x 64 each; 4 stages = 128 KiB of LDS,
-// one workgroup per CU) when the grid has enough tiles to fill the 256 CUs, else 128 x 128
-// with 4 wavefronts (64 x 64 each; 64 KiB, two workgroups per CU).
+// Configurations: 128 x 128 tiles, 128-byte steps, 2 stages (64 KiB of LDS, 64 x 64 per
+// wavefront); 64 x 128 tiles, 64-byte steps, 4 stages for at most 128 tokens.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -55,15 +56,29 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;        // bytes of k per step
-constexpr int kStages = 4;
-constexpr int kRowsPerLoad = 16;  // one wavefront load instruction = 16 rows x 64 bytes
+constexpr int kWaves = 4;  // 2 x 2 wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row`: c ^ swizzle<BK>(row).
+// BK = 64 (4 chunks per row): the reads of one logical chunk by any 8 consecutive rows
+// cover a whole 128-byte (32-bank) line, and by any 16 consecutive rows a whole 256-byte
+// (64-bank) line.  BK = 128 (8 chunks): the same for 8 rows, and each parity class of 16
+// consecutive rows covers all 8 slots of its half.  Both depend on row bits 0..4 only
+// (period 32), so a fragment's swizzle is that of its row within the 32-row block.
+template <int BK>
+__device__ __forceinline__ int swizzle(int row) {
+  if constexpr (BK == 64) {
+    return ((row >> 1) ^ (row >> 3)) & 3;
+  } else {
+    return (row & 7) ^ ((row >> 3) & 3);
+  }
 }
 
 // Linear workgroup id -> (tile row, tile column), XCD-contiguous and grouped.
@@ -83,51 +98,170 @@ __device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int64_
   return true;
 }
 
-// Wait until at most `pending` of this wavefront's load batches are outstanding, then
-// barrier.  The barrier carries no fence: LDS ordering is exactly the vmcnt wait plus the
-// MFMAs' own lgkmcnt waits, and the "memory" clobber keeps the compiler from moving LDS
-// accesses across it.
+// s_waitcnt immediate (gfx9 encoding): vmcnt(vm) lgkmcnt(lgkm), expcnt left at its maximum.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// Barrier with no memory fence.  A fence would wait for every load in flight; instead the
+// waits before it are explicit, and the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `pending` of this wavefront's load batches (LOADS instructions each)
+// are outstanding and its LDS reads are done, then barrier.  After it every wavefront's
+// loads of the awaited step have landed and every read of the stage about to be refilled
+// has completed.  The LDS drain is inline asm because the compiler would drop it (it only
+// tracks the reads' destination registers, not the reuse of the stage by other wavefronts);
+// the vmcnt wait uses the builtin so that the compiler knows the loads have landed.
 template <int LOADS>
 __device__ __forceinline__ void wait_and_barrier(int pending) {
-  if (pending >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (pending >= 3) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * LOADS, 15));
+  } else if (pending == 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LOADS, 15));
   } else if (pending == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS, 15));
   } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   }
+  bare_barrier();
 }
+
+// Tile geometry and per-thread addressing shared by the pieces of the kernel.
+template <int BM_, int BN_, int BK_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wavefront sub-tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int CHUNKS = BK / 16;            // 16-byte chunks per row
+  static constexpr int ROWS_PER_LOAD = 1024 / BK;   // rows per wavefront load instruction
+  static constexpr int LOADS = (BM + BN) / ROWS_PER_LOAD / kWaves;  // per wavefront per step
+  static constexpr int SLICES = BK / 32;
+  static constexpr int STAGE_BYTES = (BM + BN) * BK;
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
+  static_assert(BK == 64 || BK == 128, "BK is 64 or 128 bytes");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "sub-tile must be whole 32x32 blocks");
+  static_assert(LOADS * ROWS_PER_LOAD * kWaves == BM + BN, "loads must split over waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "wait_and_barrier handles up to 3 pending");
+  static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
+};
 
 // Issue this wavefront's direct-to-LDS loads of k step `step` into `stage`.  A chunk past
 // the end of the row (k % 16 == 0, so chunks are whole) reads the row start instead, which is
-// in bounds; its bytes are zeroed when the fragment is read.
-template <int LOADS>
+// in bounds; those A chunks are zeroed before use.
+template <class C>
 __device__ __forceinline__ void issue_step(int8_t* stage, const int8_t* const* src,
                                            const int* col, const int* dst, int step,
                                            int64_t k) {
-  const int64_t k0 = static_cast<int64_t>(step) * kBK;
+  const int64_t k0 = static_cast<int64_t>(step) * C::BK;
 #pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
+  for (int j = 0; j < C::LOADS; ++j) {
     const int64_t kk = k0 + col[j];
     const int8_t* g = src[j] + (kk < k ? kk : 0);
     __builtin_amdgcn_global_load_lds(g, stage + dst[j], 16, 0, 0);
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int YT>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void w8a8_kernel(
+// Read the fragments of 32-k slice `slice` of a step from an LDS stage.
+template <class C>
+__device__ __forceinline__ void read_slice(const int8_t* stage, int slice, int a_off,
+                                           int b_off, int fx, int lane, v4i (&a)[C::TM],
+                                           v4i (&b)[C::TN]) {
+  const int pofs = ((2 * slice + lane / 32) ^ fx) * 16;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+    a[i] = *reinterpret_cast<const v4i*>(stage + a_off + i * 32 * C::BK + pofs);
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+    b[j] = *reinterpret_cast<const v4i*>(stage + b_off + j * 32 * C::BK + pofs);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_slice(const v4i (&a)[C::TM], const v4i (&b)[C::TN],
+                                           v16i (&acc)[C::TM][C::TN]) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hint for the instructions just emitted in this basic block: one MFMA of the
+// slice whose fragments are already in registers (its operand wait then only covers reads
+// issued a slice earlier), then the next slice's TM + TN fragment reads, then the remaining
+// MFMAs, which hide the reads' latency.
+template <class C, int ID>
+__device__ __forceinline__ void reads_under_mfmas() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);                    // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, ID);        // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - 1, ID);    // MFMAs
+}
+
+// The last step of a k that is not a multiple of BK holds `valid` real chunks per row; its
+// other A chunks (loaded from the row start) are overwritten with zeros once the step has
+// landed.  Ends with the LDS writes drained and a barrier.
+template <class C>
+__device__ __forceinline__ void zero_tail(int8_t* stage, int valid) {
+  const int dead = C::CHUNKS - valid;
+  for (int e = threadIdx.x; e < C::BM * dead; e += kThreads) {
+    const int row = e / dead;
+    const int chunk = valid + e % dead;
+    *reinterpret_cast<v4i*>(stage + row * C::BK + (chunk ^ swizzle<C::BK>(row)) * 16) =
+        v4i{0, 0, 0, 0};
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bare_barrier();
+}
+
+// Slices 1 .. SLICES-1 of step t: each slice's fragments are read while the previous
+// slice's MFMAs run.  On return fragment set (SLICES - 1) % 2 holds the last slice.
+template <class C>
+__device__ __forceinline__ void step_inner(const int8_t* stage, int a_off, int b_off, int fx,
+                                           int lane, v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
+                                           v16i (&acc)[C::TM][C::TN]) {
+#pragma unroll
+  for (int s = 0; s + 1 < C::SLICES; ++s) {
+    read_slice<C>(stage, s + 1, a_off, b_off, fx, lane, fa[(s + 1) % 2], fb[(s + 1) % 2]);
+    mfma_slice<C>(fa[s % 2], fb[s % 2], acc);
+    reads_under_mfmas<C, 0>();
+  }
+}
+
+// One steady-state k step t (t + 1 < ksteps).  ZERO: step t + 1 is the partial last step.
+template <class C, bool ZERO>
+__device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, const int* col,
+                                       const int* dst, int a_off, int b_off, int fx, int lane,
+                                       int t, int ksteps, int64_t k, int tail_valid,
+                                       v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
+                                       v16i (&acc)[C::TM][C::TN]) {
+  step_inner<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
+  int8_t* next = lds + ((t + 1) % C::STAGES) * C::STAGE_BYTES;
+  // Keep this step's MFMAs in front of the LDS drain: they do not touch memory, so nothing
+  // else stops the scheduler from sinking them below it and waiting on the fresh reads.
+  __builtin_amdgcn_sched_barrier(0);
+  wait_and_barrier<C::LOADS>(min(C::STAGES - 2, ksteps - 2 - t));
+  if (t + C::STAGES < ksteps)
+    issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, t + C::STAGES, k);
+  if (ZERO && tail_valid != 0) zero_tail<C>(next, tail_valid);
+  constexpr int last = (C::SLICES - 1) % 2;  // SLICES is even, so set 0 is free
+  read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+  mfma_slice<C>(fa[last], fb[last], acc);
+  reads_under_mfmas<C, 1>();
+}
+
+template <int BM, int BN, int BK, int STAGES, int YT>
+__global__ __launch_bounds__(kThreads) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
     const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
-  constexpr int kWaves = WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wavefront sub-tile
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int kLoadsA = BM / kRowsPerLoad, kLoadsB = BN / kRowsPerLoad;
-  constexpr int LOADS = (kLoadsA + kLoadsB) / kWaves;  // per wavefront per step
-  static_assert(LOADS * kWaves == kLoadsA + kLoadsB, "loads must split evenly over waves");
-  static_assert(kStages == 4, "wait_and_barrier assumes 4 stages");
-  constexpr int kStageBytes = (BM + BN) * kBK;
-
+  using C = Cfg<BM, BN, BK, STAGES>;
+  constexpr int TM = C::TM, TN = C::TN;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
 
   int64_t tm, tn;
@@ -137,28 +271,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void w8a8_kernel(
 
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int ksteps = static_cast<int>((k + kBK - 1) / kBK);
+  const int wm = wave / 2, wn = wave % 2;
+  const int ksteps = static_cast<int>((k + BK - 1) / BK);
 
-  // This lane's part of each of the wavefront's load instructions: instruction j covers tile
-  // rows 16 * (wave + kWaves * j) .. +15 of the stacked [A; B] slice.
-  const int8_t* src[LOADS];
-  int col[LOADS];
-  int dst[LOADS];
+  // This lane's part of each of the wavefront's load instructions: instruction j covers
+  // rows ROWS_PER_LOAD * (wave + kWaves * j) + [0, ROWS_PER_LOAD) of the stacked [A; B] slice.
+  const int8_t* src[C::LOADS];
+  int col[C::LOADS];
+  int dst[C::LOADS];
 #pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
+  for (int j = 0; j < C::LOADS; ++j) {
     const int blk = wave + kWaves * j;
-    const int trow = blk * kRowsPerLoad + lane / 4;  // row of the stacked tile
-    const int pchunk = lane % 4;
-    const int lchunk = pchunk ^ ((trow >> 1) & 3);
-    col[j] = lchunk * 16;
+    const int trow = blk * C::ROWS_PER_LOAD + lane / C::CHUNKS;  // row of the stacked tile
+    const int pchunk = lane % C::CHUNKS;
+    col[j] = (pchunk ^ swizzle<BK>(trow)) * 16;
     if (trow < BM)
       src[j] = xq + min(m0 + trow, m - 1) * k;
     else
       src[j] = wq + min(n0 + (trow - BM), n - 1) * k;
-    dst[j] = blk * kRowsPerLoad * kBK;  // wave-uniform LDS offset of the instruction
+    dst[j] = blk * C::ROWS_PER_LOAD * BK;  // wave-uniform LDS offset of the instruction
   }
-
 
   v16i acc[TM][TN];
 #pragma unroll
@@ -169,47 +301,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void w8a8_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < ksteps) issue_step<LOADS>(lds + s * kStageBytes, src, col, dst, s, k);
+  for (int s = 0; s < STAGES; ++s)
+    if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, s, k);
 
   const int frow = lane % 32;
-  const int fx = (frow >> 1) & 3;  // swizzle of this lane's fragment rows
-  const int a_off = (wm * WTM + frow) * kBK;
-  const int b_off = (BM + wn * WTN + frow) * kBK;
+  const int fx = swizzle<BK>(frow);  // swizzle of this lane's fragment rows (period 32)
+  const int a_off = (wm * C::WTM + frow) * BK;
+  const int b_off = (BM + wn * C::WTN + frow) * BK;
+  const int tail_valid = static_cast<int>((k % BK) / 16);  // 0: no partial last step
 
-  for (int t = 0; t < ksteps; ++t) {
-    wait_and_barrier<LOADS>(min(kStages - 1, ksteps - t) - 1);
-    if (t + kStages - 1 < ksteps) {
-      const int nt = t + kStages - 1;
-      issue_step<LOADS>(lds + (nt % kStages) * kStageBytes, src, col, dst, nt, k);
-    }
-    const int8_t* stage = lds + (t % kStages) * kStageBytes;
-    const bool tail = static_cast<int64_t>(t + 1) * kBK > k;
-#pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-      const int lchunk = 2 * s + lane / 32;
-      const int pofs = ((lchunk ^ fx) * 16);
-      const bool live = !tail || static_cast<int64_t>(t) * kBK + lchunk * 16 < k;
-      v4i a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        a[i] = *reinterpret_cast<const v4i*>(stage + a_off + i * 32 * kBK + pofs);
-        if (!live) a[i] = v4i{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const v4i*>(stage + b_off + j * 32 * kBK + pofs);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+  v4i fa[2][TM], fb[2][TN];
+  wait_and_barrier<C::LOADS>(min(STAGES - 1, ksteps - 1));
+  if (tail_valid != 0 && ksteps == 1) zero_tail<C>(lds, tail_valid);
+  read_slice<C>(lds, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+  int t = 0;
+  for (; t + 2 < ksteps; ++t)
+    k_step<C, false>(lds, src, col, dst, a_off, b_off, fx, lane, t, ksteps, k, tail_valid,
+                     fa, fb, acc);
+  if (t + 1 < ksteps) {
+    k_step<C, true>(lds, src, col, dst, a_off, b_off, fx, lane, t, ksteps, k, tail_valid, fa,
+                    fb, acc);
+    ++t;
   }
+  step_inner<C>(lds + (t % STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
+  mfma_slice<C>(fa[(C::SLICES - 1) % 2], fb[(C::SLICES - 1) % 2], acc);
 
   // ---- fused epilogue ----------------------------------------------------------------
-  const int64_t row_base = m0 + wm * WTM + 4 * (lane / 32);
-  const int64_t col_base = n0 + wn * WTN + lane % 32;
+  const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
+  const int64_t col_base = n0 + wn * C::WTN + lane % 32;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t c = col_base + j * 32;
@@ -242,35 +361,39 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void w8a8_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int YT>
+template <int BM, int BN, int BK, int STAGES, int YT>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                       int64_t k, hipStream_t stream) {
-  auto kern = w8a8_kernel<BM, BN, WM, WN, YT>;
-  constexpr size_t lds = static_cast<size_t>(kStages) * (BM + BN) * kBK;
+  using C = Cfg<BM, BN, BK, STAGES>;
+  auto kern = w8a8_kernel<BM, BN, BK, STAGES, YT>;
   static bool configured = false;  // idempotent attribute set; a race only repeats it
   if (!configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(lds));
+                                             static_cast<int>(C::LDS_BYTES));
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), lds, stream,
-                     xq, x_scale, wq, w_scale, bias, y, m, n, k);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), C::LDS_BYTES,
+                     stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
   return hipGetLastError();
 }
 
+// Configuration by token count.  Measured on MI355X (M x N x K, TOPS): 128 x 128 tiles with
+// 128-byte steps and two stages (two or three workgroups per CU) beat 256 x 256 tiles (one
+// workgroup per CU) on every decoder shape, e.g. 1460 vs 1180 at 16384 x 12288 x 4096 and
+// 1170 vs 650 at 2048 x 9728 x 2560; for at most 128 tokens 64 x 128 tiles double the number
+// of workgroups (325 vs 285 at 128 x 9728 x 2560).
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                      int64_t k, hipStream_t stream) {
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (big_tiles >= 192)
-    return launch_cfg<256, 256, 2, 4, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_cfg<128, 128, 2, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  if (m <= 128)
+    return launch_cfg<64, 128, 64, 4, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_cfg<128, 128, 128, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace
