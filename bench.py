@@ -6,6 +6,10 @@ of the four distinct layer inputs, then the seven int8 MFMA GEMMs with the fused
 epilogue to bf16.  ``value`` is the step's int8 throughput (2*M*N*K ops per GEMM summed,
 over the whole step time, quantization included), with every input resident in HBM.  Weight
 copies are rotated so every GEMM reads weights that are not in the 256 MB Infinity Cache.
+After W eager warm-up steps, exactly K steps are captured in one HIP graph and replayed
+between two HIP events (after one untimed replay), as an inference engine would launch
+them; the graph holds the same kernels on the same stream, so host launch overhead does
+not enter the kernel timings.
 
 The same JSON line also carries the other rows of the path, each timed on its own workload:
 W8A16 decode on 8B shapes (M = 1, 4, 8), the grouped MoE W8A16 GEMM (T = 1..64 tokens),
@@ -83,22 +87,41 @@ def grouped_bytes(distinct, n, k, x_rows, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------------------------------
 
-def per_call(torch, fn, reps, warmup=2):
-    """Average seconds per call of fn(i), timed back to back between two HIP events."""
-    return time_loop(torch, fn, reps, warmup) / reps
-
-
-def time_loop(torch, body, steps, warmup):
-    for i in range(warmup):
-        body(i)
+def graph_time(torch, body, iters, warmup=1):
+    """Seconds for body(0 .. iters-1), launched from one captured HIP graph and timed with
+    two HIP events around its replay (no host launch overhead between kernels).  body(0) runs
+    once eagerly first so that one-time setup never happens under capture, and the graph is
+    replayed `warmup` times untimed before the timed replay."""
+    body(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            body(i)
+    for _ in range(warmup):
+        g.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        body(warmup + i)
+    g.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3
+    secs = start.elapsed_time(end) * 1e-3
+    del g
+    return secs
+
+
+def per_call(torch, fn, reps, warmup=1):
+    """Average seconds per call of fn(i), from a graph of `reps` calls."""
+    return graph_time(torch, fn, reps, warmup) / reps
+
+
+def time_loop(torch, body, steps, warmup):
+    """W eager warm-up steps, then exactly `steps` steps replayed from one HIP graph."""
+    for i in range(warmup):
+        body(i)
+    torch.cuda.synchronize()
+    return graph_time(torch, lambda i: body(warmup + i), steps, 1)
 
 
 # ---------------------------------------------------------------------------------------

@@ -27,71 +27,75 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kStepK = 128;  // input channels per wavefront step
 
 // Four int8 codes -> two dwords holding four bf16 values (exact).
-__device__ __forceinline__ void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ uint2 i8x4_to_bf16x4(uint32_t w) {
   const float f0 = static_cast<float>(static_cast<int8_t>(w));
   const float f1 = static_cast<float>(static_cast<int8_t>(w >> 8));
   const float f2 = static_cast<float>(static_cast<int8_t>(w >> 16));
   const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
   // |code| < 256: the low 16 bits of each float32 are zero, so the high half is the bf16.
-  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  return make_uint2((__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u),
+                    (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u));
 }
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // 16 codes -> two 8-wide bf16 MFMA operands.
-__device__ __forceinline__ void i8x16_to_bf16(const uint4 w, v8bf& a0, v8bf& a1) {
-  uint4 p, q;
-  i8x4_to_bf16x4(w.x, p.x, p.y);
-  i8x4_to_bf16x4(w.y, p.z, p.w);
-  i8x4_to_bf16x4(w.z, q.x, q.y);
-  i8x4_to_bf16x4(w.w, q.z, q.w);
-  a0 = __builtin_bit_cast(v8bf, p);
-  a1 = __builtin_bit_cast(v8bf, q);
+__device__ __forceinline__ void i8x16_to_bf16(const v4u w, v8bf& a0, v8bf& a1) {
+  const uint2 p0 = i8x4_to_bf16x4(w[0]), p1 = i8x4_to_bf16x4(w[1]);
+  const uint2 q0 = i8x4_to_bf16x4(w[2]), q1 = i8x4_to_bf16x4(w[3]);
+  a0 = __builtin_bit_cast(v8bf, v4u{p0.x, p0.y, p1.x, p1.y});
+  a1 = __builtin_bit_cast(v8bf, v4u{q0.x, q0.y, q1.x, q1.y});
 }
 
-__device__ __forceinline__ v8bf as_v8bf(const uint4 v) { return __builtin_bit_cast(v8bf, v); }
+// 16 bytes at p + (ok ? off : 0), replaced by zeros when !ok.  The address is always in
+// bounds and the load unconditional, so it compiles to one 16-byte load and a select (a
+// guarded load would become branches around 4-byte loads).
+__device__ __forceinline__ v4u load16_or_zero(const void* p, int64_t off, bool ok) {
+  const v4u v = *reinterpret_cast<const v4u*>(static_cast<const char*>(p) + (ok ? off : 0));
+  return ok ? v : v4u{0u, 0u, 0u, 0u};
+}
 
 // Accumulate the wavefront's partial product over steps [s_begin, s_end).
-//   wrow : this lane's weight row (row n0 + lane % 16, clamped into the matrix)
-//   xrow : this lane's activation row for each m-tile (lane % 16 within the tile), or
-//          nullptr when that row does not exist (its column of the MFMA is then zero)
-// Chunks past k (k % 16 == 0) are neither read nor counted.
+//   wrow      : this lane's weight row (row n0 + lane % 16, clamped into the matrix)
+//   xrow      : this lane's activation row for each m-tile (lane % 16 within the tile);
+//               always a valid row, xok says whether it is a real one (else the MFMA
+//               column is fed zeros)
+// Chunks past k (k % 16 == 0) are read from the row start and replaced by zeros.
 template <int MT, int U>
 __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wrow,
-                                                  const uint16_t* const (&xrow)[MT], int64_t k,
+                                                  const uint16_t* const (&xrow)[MT],
+                                                  const bool (&xok)[MT], int64_t k,
                                                   int s_begin, int s_end, v4f (&acc)[MT]) {
   const int lane = threadIdx.x % 64;
   const int sub = 32 * (lane / 16);  // this lane's 32 channels within a step
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   for (int s = s_begin; s < s_end; s += U) {
-    uint4 w[U][2];
+    v4u w[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
       const bool in = (s + u) < s_end;
-      w[u][0] = (in && kk < k) ? *reinterpret_cast<const uint4*>(wrow + kk) : zero;
-      w[u][1] = (in && kk + 16 < k) ? *reinterpret_cast<const uint4*>(wrow + kk + 16) : zero;
+      w[u][0] = load16_or_zero(wrow, kk, in && kk < k);
+      w[u][1] = load16_or_zero(wrow, kk + 16, in && kk + 16 < k);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (s + u >= s_end) break;
       const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
-      const bool in = (s + u) < s_end;
       v8bf a[4];
       i8x16_to_bf16(w[u][0], a[0], a[1]);
       i8x16_to_bf16(w[u][1], a[2], a[3]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t* xr = xrow[mt];
-        uint4 xb[4];
+        v4u xb[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int64_t kc = kk + 8 * c;
-          xb[c] = (in && xr != nullptr && kc < k) ? *reinterpret_cast<const uint4*>(xr + kc)
-                                                  : zero;
+          xb[c] = load16_or_zero(xrow[mt], kc * 2, xok[mt] && kc < k);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], as_v8bf(xb[c]), acc[mt], 0,
-                                                            0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[c], __builtin_bit_cast(v8bf, xb[c]), acc[mt], 0, 0, 0);
       }
     }
   }

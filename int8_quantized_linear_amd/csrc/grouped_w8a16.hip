@@ -89,15 +89,13 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
       const int64_t nc = n0 + 4 * (lane / 16);
       for (int g = 0; g < count; g += 16 * kMT) {
         const uint16_t* xrow[kMT];
+        bool xok[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const int li = g + mt * 16 + lane % 16;
-          if (li < count) {
-            const int64_t p = list[li];
-            xrow[mt] = x + (x_per_assignment ? p : p / topk) * k;
-          } else {
-            xrow[mt] = nullptr;
-          }
+          xok[mt] = li < count;
+          const int64_t p = xok[mt] ? list[li] : 0;
+          xrow[mt] = x + (x_per_assignment ? p : p / topk) * k;
         }
         v4f acc[kMT];
 #pragma unroll
@@ -107,11 +105,12 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
         const int live = min(kMT, (count - g + 15) / 16);
         if (live == 1) {
           const uint16_t* one[1] = {xrow[0]};
+          const bool one_ok[1] = {xok[0]};
           v4f a1[1] = {acc[0]};
-          dequant_mma_steps<1, kUnroll>(wrow, one, k, sb, se, a1);
+          dequant_mma_steps<1, kUnroll>(wrow, one, one_ok, k, sb, se, a1);
           acc[0] = a1[0];
         } else {
-          dequant_mma_steps<kMT, kUnroll>(wrow, xrow, k, sb, se, acc);
+          dequant_mma_steps<kMT, kUnroll>(wrow, xrow, xok, k, sb, se, acc);
         }
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) red[wave][mt][lane] = acc[mt];

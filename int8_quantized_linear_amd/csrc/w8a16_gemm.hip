@@ -6,11 +6,12 @@
 // ("Day 6 — Quantize It Yourself", the question it opens with), so the kernel is built to
 // read every weight byte from HBM exactly once at full bandwidth:
 //
-//   * a workgroup owns 16 output channels and up to 64 activation rows; its WAVES
+//   * a workgroup owns 16 output channels and up to 64 activation rows; its 4, 8 or 16
 //     wavefronts split the input channels (in-workgroup split-K) so each weight row is
 //     streamed by many waves at once, and sum their partial tiles through LDS in a fixed
 //     order (deterministic, no atomics);
-//   * each wave keeps U steps of 16 rows x 128 bytes in flight (two 16-byte loads per lane);
+//   * each wave issues the loads of up to 8 steps of 16 rows x 128 bytes (two 16-byte loads
+//     per lane per step) before it converts the first, so 16 KiB per wave are in flight;
 //   * the scale and bias are applied once, after the reduction over k.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,7 +22,7 @@
 namespace i8ql {
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;  // steps of k whose loads a wavefront keeps in flight
 
 template <int MT, int WAVES, int YT>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
@@ -37,10 +38,12 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   const int64_t wr = min(n0 + lane % 16, n - 1);
   const int8_t* wrow = wq + wr * k;
   const uint16_t* xrow[MT];
+  bool xok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int64_t r = m0 + mt * 16 + lane % 16;
-    xrow[mt] = r < m ? x + r * k : nullptr;
+    xok[mt] = r < m;
+    xrow[mt] = x + (xok[mt] ? r : 0) * k;
   }
 
   v4f acc[MT];
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   int sb, se;
   wave_step_range(k, WAVES, wave, sb, se);
-  dequant_mma_steps<MT, kUnroll>(wrow, xrow, k, sb, se, acc);
+  dequant_mma_steps<MT, kUnroll>(wrow, xrow, xok, k, sb, se, acc);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
@@ -86,14 +89,27 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   }
 }
 
+// Wavefronts per workgroup: enough that each streams at most kUnroll steps of k (all its
+// loads in flight at once), between 4 and 16.  One 16-channel tile per workgroup; with
+// N / 16 workgroups of this size the whole weight matrix is in flight in about one
+// occupancy round on 256 CUs for the decoder shapes.
 template <int MT, int YT>
 hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  constexpr int WAVES = 8;
   const dim3 grid(static_cast<unsigned>((n + 15) / 16),
                   static_cast<unsigned>((m + 16 * MT - 1) / (16 * MT)));
-  hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT>), grid, dim3(64 * WAVES), 0, stream,
-                     static_cast<const uint16_t*>(x), wq, w_scale, bias, y, m, n, k);
+  const int64_t steps = (k + kStepK - 1) / kStepK;
+  const auto* xx = static_cast<const uint16_t*>(x);
+  if (steps <= 4 * kUnroll) {
+    hipLaunchKernelGGL((w8a16_kernel<MT, 4, YT>), grid, dim3(64 * 4), 0, stream, xx, wq, w_scale,
+                       bias, y, m, n, k);
+  } else if (steps <= 8 * kUnroll) {
+    hipLaunchKernelGGL((w8a16_kernel<MT, 8, YT>), grid, dim3(64 * 8), 0, stream, xx, wq, w_scale,
+                       bias, y, m, n, k);
+  } else {
+    hipLaunchKernelGGL((w8a16_kernel<MT, 16, YT>), grid, dim3(64 * 16), 0, stream, xx, wq,
+                       w_scale, bias, y, m, n, k);
+  }
   return hipGetLastError();
 }
 

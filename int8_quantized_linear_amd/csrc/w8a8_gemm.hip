@@ -39,7 +39,10 @@
 // A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
 // Configurations: 128 x 128 tiles, 128-byte steps, 2 stages (64 KiB of LDS, 64 x 64 per
-// wavefront); 64 x 128 tiles, 64-byte steps, 4 stages for at most 128 tokens.
+// wavefront) for large grids; for small grids 64 x 64 tiles with four k-groups of 4
+// wavefronts (in-workgroup split-K: each group walks a quarter of k through its own LDS
+// stages and the partial int32 tiles are summed exactly through LDS), or 64 x 128 tiles
+// with 4 stages when k does not split evenly.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -56,8 +59,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;  // 2 x 2 wavefronts per workgroup
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;  // 2 x 2 wavefronts per k-group
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
@@ -134,9 +136,10 @@ __device__ __forceinline__ void wait_and_barrier(int pending) {
 }
 
 // Tile geometry and per-thread addressing shared by the pieces of the kernel.
-template <int BM_, int BN_, int BK_, int STAGES_>
+template <int BM_, int BN_, int BK_, int STAGES_, int KS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, KS = KS_;
+  static constexpr int THREADS = 64 * kWaves * KS;
   static constexpr int WTM = BM / 2, WTN = BN / 2;  // wavefront sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int CHUNKS = BK / 16;            // 16-byte chunks per row
@@ -144,7 +147,10 @@ struct Cfg {
   static constexpr int LOADS = (BM + BN) / ROWS_PER_LOAD / kWaves;  // per wavefront per step
   static constexpr int SLICES = BK / 32;
   static constexpr int STAGE_BYTES = (BM + BN) * BK;
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
+  static constexpr size_t GROUP_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
+  static constexpr size_t RED_BYTES = static_cast<size_t>(KS / 2) * BM * BN * 4;
+  static constexpr size_t LDS_BYTES = KS * GROUP_BYTES > RED_BYTES ? KS * GROUP_BYTES : RED_BYTES;
+  static_assert(KS == 1 || KS == 2 || KS == 4, "k-groups per workgroup");
   static_assert(BK == 64 || BK == 128, "BK is 64 or 128 bytes");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "sub-tile must be whole 32x32 blocks");
   static_assert(LOADS * ROWS_PER_LOAD * kWaves == BM + BN, "loads must split over waves");
@@ -205,11 +211,11 @@ __device__ __forceinline__ void reads_under_mfmas() {
 
 // The last step of a k that is not a multiple of BK holds `valid` real chunks per row; its
 // other A chunks (loaded from the row start) are overwritten with zeros once the step has
-// landed.  Ends with the LDS writes drained and a barrier.
+// landed.  Ends with the LDS writes drained and a barrier.  (Only used with one k-group.)
 template <class C>
 __device__ __forceinline__ void zero_tail(int8_t* stage, int valid) {
   const int dead = C::CHUNKS - valid;
-  for (int e = threadIdx.x; e < C::BM * dead; e += kThreads) {
+  for (int e = threadIdx.x % (64 * kWaves); e < C::BM * dead; e += 64 * kWaves) {
     const int row = e / dead;
     const int chunk = valid + e % dead;
     *reinterpret_cast<v4i*>(stage + row * C::BK + (chunk ^ swizzle<C::BK>(row)) * 16) =
@@ -233,11 +239,12 @@ __device__ __forceinline__ void step_inner(const int8_t* stage, int a_off, int b
   }
 }
 
-// One steady-state k step t (t + 1 < ksteps).  ZERO: step t + 1 is the partial last step.
+// One steady-state k step t of this k-group's ksteps steps (t + 1 < ksteps; global step
+// base + t).  ZERO: step t + 1 is the partial last step.
 template <class C, bool ZERO>
 __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, const int* col,
                                        const int* dst, int a_off, int b_off, int fx, int lane,
-                                       int t, int ksteps, int64_t k, int tail_valid,
+                                       int base, int t, int ksteps, int64_t k, int tail_valid,
                                        v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
                                        v16i (&acc)[C::TM][C::TN]) {
   step_inner<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
@@ -247,7 +254,8 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
   __builtin_amdgcn_sched_barrier(0);
   wait_and_barrier<C::LOADS>(min(C::STAGES - 2, ksteps - 2 - t));
   if (t + C::STAGES < ksteps)
-    issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, t + C::STAGES, k);
+    issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + t + C::STAGES,
+                  k);
   if (ZERO && tail_valid != 0) zero_tail<C>(next, tail_valid);
   constexpr int last = (C::SLICES - 1) % 2;  // SLICES is even, so set 0 is free
   read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
@@ -255,14 +263,14 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
   reads_under_mfmas<C, 1>();
 }
 
-template <int BM, int BN, int BK, int STAGES, int YT>
-__global__ __launch_bounds__(kThreads) void w8a8_kernel(
+template <int BM, int BN, int BK, int STAGES, int KS, int YT>
+__global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
     const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
-  using C = Cfg<BM, BN, BK, STAGES>;
+  using C = Cfg<BM, BN, BK, STAGES, KS>;
   constexpr int TM = C::TM, TN = C::TN;
-  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
 
   int64_t tm, tn;
   if (!tile_of((m + BM - 1) / BM, (n + BN - 1) / BN, tm, tn)) return;
@@ -270,9 +278,14 @@ __global__ __launch_bounds__(kThreads) void w8a8_kernel(
   const int64_t n0 = tn * BN;
 
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  const int group = threadIdx.x / (64 * kWaves);  // k-group (in-workgroup split-K)
+  const int wave = (threadIdx.x / 64) % kWaves;   // wavefront within the k-group
   const int wm = wave / 2, wn = wave % 2;
-  const int ksteps = static_cast<int>((k + BK - 1) / BK);
+  // Each k-group walks its own equal share of the steps (KS > 1 only when it divides
+  // evenly) in its own LDS stages; all groups pass the same barriers.
+  const int ksteps = static_cast<int>((k + BK - 1) / BK) / KS;
+  const int base = group * ksteps;
+  int8_t* lds = lds_all + group * C::GROUP_BYTES;
 
   // This lane's part of each of the wavefront's load instructions: instruction j covers
   // rows ROWS_PER_LOAD * (wave + kWaves * j) + [0, ROWS_PER_LOAD) of the stacked [A; B] slice.
@@ -302,13 +315,13 @@ __global__ __launch_bounds__(kThreads) void w8a8_kernel(
 
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
-    if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, s, k);
+    if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, base + s, k);
 
   const int frow = lane % 32;
   const int fx = swizzle<BK>(frow);  // swizzle of this lane's fragment rows (period 32)
   const int a_off = (wm * C::WTM + frow) * BK;
   const int b_off = (BM + wn * C::WTN + frow) * BK;
-  const int tail_valid = static_cast<int>((k % BK) / 16);  // 0: no partial last step
+  const int tail_valid = KS == 1 ? static_cast<int>((k % BK) / 16) : 0;  // 0: none
 
   v4i fa[2][TM], fb[2][TN];
   wait_and_barrier<C::LOADS>(min(STAGES - 1, ksteps - 1));
@@ -316,15 +329,49 @@ __global__ __launch_bounds__(kThreads) void w8a8_kernel(
   read_slice<C>(lds, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
   int t = 0;
   for (; t + 2 < ksteps; ++t)
-    k_step<C, false>(lds, src, col, dst, a_off, b_off, fx, lane, t, ksteps, k, tail_valid,
-                     fa, fb, acc);
+    k_step<C, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
+                     tail_valid, fa, fb, acc);
   if (t + 1 < ksteps) {
-    k_step<C, true>(lds, src, col, dst, a_off, b_off, fx, lane, t, ksteps, k, tail_valid, fa,
-                    fb, acc);
+    k_step<C, true>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
+                    tail_valid, fa, fb, acc);
     ++t;
   }
   step_inner<C>(lds + (t % STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
   mfma_slice<C>(fa[(C::SLICES - 1) % 2], fb[(C::SLICES - 1) % 2], acc);
+
+  if constexpr (KS > 1) {
+    // Sum the k-groups' partial tiles in a fixed tree through LDS (int32, exact): in each
+    // round the upper half of the groups stores its accumulators and the lower half adds
+    // its partner's.  Each wavefront's registers go to a lane-contiguous block.
+    constexpr int kRegs = TM * TN * 16;
+    int* red = reinterpret_cast<int*>(lds_all);
+#pragma unroll
+    for (int h = KS / 2; h >= 1; h /= 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bare_barrier();  // every group is done with its LDS stages / the previous round
+      if (group >= h && group < 2 * h) {
+        int* out = red + ((group - h) * kWaves + wave) * kRegs * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) out[((i * TN + j) * 16 + r) * 64] = acc[i][j][r];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bare_barrier();
+      if (group < h) {
+        const int* in = red + (group * kWaves + wave) * kRegs * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += in[((i * TN + j) * 16 + r) * 64];
+      }
+    }
+    if (group != 0) return;
+  }
 
   // ---- fused epilogue ----------------------------------------------------------------
   const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
@@ -361,12 +408,12 @@ __global__ __launch_bounds__(kThreads) void w8a8_kernel(
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, int YT>
+template <int BM, int BN, int BK, int STAGES, int KS, int YT>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                       int64_t k, hipStream_t stream) {
-  using C = Cfg<BM, BN, BK, STAGES>;
-  auto kern = w8a8_kernel<BM, BN, BK, STAGES, YT>;
+  using C = Cfg<BM, BN, BK, STAGES, KS>;
+  auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, YT>;
   static bool configured = false;  // idempotent attribute set; a race only repeats it
   if (!configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -377,23 +424,33 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
   }
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), C::LDS_BYTES,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), C::LDS_BYTES,
                      stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
   return hipGetLastError();
 }
 
-// Configuration by token count.  Measured on MI355X (M x N x K, TOPS): 128 x 128 tiles with
-// 128-byte steps and two stages (two or three workgroups per CU) beat 256 x 256 tiles (one
-// workgroup per CU) on every decoder shape, e.g. 1460 vs 1180 at 16384 x 12288 x 4096 and
-// 1170 vs 650 at 2048 x 9728 x 2560; for at most 128 tokens 64 x 128 tiles double the number
-// of workgroups (325 vs 285 at 128 x 9728 x 2560).
+// Configuration by grid size, from graph-timed MI355X measurements (us):
+//   shape (M x N x K)   64x64 tiles, 4 k-groups   64x128, 1 k-group   128x128, 128-byte steps
+//   128 x 1024 x 2560          12.1                      19.1                 23.5
+//   128 x 2560 x 9728          40.0                      54.1                 77.7
+//   512 x 2560 x 9728          50.1                      54.6                 75.2
+//   512 x 9728 x 2560          50.0                      40.0                 39.4
+//   2048 x 9728 x 2560        162.8                     132.8                101.7
+// Few tiles (<= 512 of 64 x 64): split k four ways inside the workgroup (when 256-byte
+// chunks divide k); otherwise 128 x 128 tiles, whose two to three workgroups per CU keep the
+// matrix cores busiest on large grids.
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                      int64_t k, hipStream_t stream) {
-  if (m <= 128)
-    return launch_cfg<64, 128, 64, 4, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_cfg<128, 128, 128, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  const int64_t tiles64 = ((m + 63) / 64) * ((n + 63) / 64);
+  if (tiles64 <= 512) {
+    if (k % (4 * 64) == 0)
+      return launch_cfg<64, 64, 64, 2, 4, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
+                                              stream);
+    return launch_cfg<64, 128, 64, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  }
+  return launch_cfg<128, 128, 128, 2, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace

@@ -368,3 +368,48 @@ def test_grouped_moe_16b_full(ref, dev, t, proj):
     per_assign = proj == "down"
     run_grouped(ref, dev, qw, sw, qwr, swr, ids, t * ids.shape[1] if per_assign else t,
                 per_assign, torch.bfloat16, g)
+
+
+# ---------------------------------------------------------------------------------------
+# HIP graph capture (the benchmark replays the path from graphs)
+
+def test_graph_replays_match_eager(ref, dev):
+    g = wl.rng(40)
+    w = wl.to_bf16(wl.weight(g, 320, 1024)).to(dev)
+    x = wl.to_bf16(wl.activations(g, 96, 1024, 0.001)).to(dev)
+    e_w = wl.to_bf16(wl.moe_weights(g, 64, 1024, experts=5).reshape(5 * 64, 1024)).to(dev)
+    ids = torch.from_numpy(np.stack([g.choice(5, 2, replace=False) for _ in range(7)])
+                           .astype(np.int32)).to(dev)
+    xd = wl.to_bf16(wl.activations(g, 3, 1024)).to(dev)
+    xg = wl.to_bf16(wl.activations(g, 7, 1024)).to(dev)
+
+    qw, sw = i8.quantize_per_channel_int8(w)
+    qe, se = i8.quantize_per_channel_int8(e_w)
+    qx = torch.empty((96, 1024), dtype=torch.int8, device=dev)
+    sx = torch.empty(96, dtype=torch.float32, device=dev)
+    y8 = torch.empty((96, 320), dtype=torch.bfloat16, device=dev)
+    y16 = torch.empty((3, 320), dtype=torch.bfloat16, device=dev)
+    yg = torch.empty((14, 64), dtype=torch.float32, device=dev)
+
+    def path():
+        i8.quantize_per_token_int8(x, qx, sx)
+        i8.w8a8_gemm(qx, sx, qw, sw, out=y8)
+        i8.w8a16_gemm(xd, qw, sw, out=y16)
+        i8.grouped_w8a16_gemm(xg, qe.view(5, 64, 1024), se.view(5, 64), ids,
+                              out_dtype=torch.float32, out=yg)
+
+    path()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (qx, sx, y8, y16, yg)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(3):
+        for t in (qx, sx, y8, y16, yg):
+            t.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((qx, sx, y8, y16, yg), eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        path()  # eager work between replays
+        torch.cuda.synchronize()
