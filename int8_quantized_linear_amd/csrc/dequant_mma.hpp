@@ -26,15 +26,17 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kStepK = 128;  // input channels per wavefront step
 
-// Four int8 codes -> two dwords holding four bf16 values (exact).
+// Four int8 codes -> two dwords holding four bf16 values (exact).  Each code converts to a
+// float32 whose low 16 bits are zero (|code| < 256), so its high half is the bf16; one byte
+// permute packs the high halves of two floats.
 __device__ __forceinline__ uint2 i8x4_to_bf16x4(uint32_t w) {
-  const float f0 = static_cast<float>(static_cast<int8_t>(w));
-  const float f1 = static_cast<float>(static_cast<int8_t>(w >> 8));
-  const float f2 = static_cast<float>(static_cast<int8_t>(w >> 16));
-  const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
-  // |code| < 256: the low 16 bits of each float32 are zero, so the high half is the bf16.
-  return make_uint2((__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u),
-                    (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u));
+  const uint32_t f0 = __float_as_uint(static_cast<float>(static_cast<int8_t>(w)));
+  const uint32_t f1 = __float_as_uint(static_cast<float>(static_cast<int8_t>(w >> 8)));
+  const uint32_t f2 = __float_as_uint(static_cast<float>(static_cast<int8_t>(w >> 16)));
+  const uint32_t f3 = __float_as_uint(static_cast<float>(static_cast<int8_t>(w >> 24)));
+  // v_perm_b32 selector: bytes 2, 3 of the second operand, then bytes 2, 3 of the first
+  return make_uint2(__builtin_amdgcn_perm(f1, f0, 0x07060302u),
+                    __builtin_amdgcn_perm(f3, f2, 0x07060302u));
 }
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -55,12 +57,73 @@ __device__ __forceinline__ v4u load16_or_zero(const void* p, int64_t off, bool o
   return ok ? v : v4u{0u, 0u, 0u, 0u};
 }
 
-// Accumulate the wavefront's partial product over steps [s_begin, s_end).
+// Issue the weight loads of steps [s, s + U): two 16-byte loads per lane per step, all
+// unconditional so that the compiler keeps them together ahead of their use instead of
+// sinking each into a branch.  Loads of steps at or past s_end, or of chunks past k, read
+// the row start instead (in bounds); the multiply gives them zero activations, which is
+// exact because int8 codes are always finite.  No select on the loaded values here: it
+// would make the wave wait for the loads before the batch is even issued.
+template <int U>
+__device__ __forceinline__ void load_weight_batch(const int8_t* __restrict__ wrow, int64_t k,
+                                                  int s, int s_end, v4u (&w)[U][2]) {
+  const int sub = 32 * ((threadIdx.x % 64) / 16);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
+    const bool in = (s + u) < s_end;
+    w[u][0] = *reinterpret_cast<const v4u*>(wrow + (in && kk < k ? kk : 0));
+    w[u][1] = *reinterpret_cast<const v4u*>(wrow + (in && kk + 16 < k ? kk + 16 : 0));
+  }
+}
+
+// Multiply a loaded batch (steps [s, s + U)) by activation rows staged in LDS: xrow[mt] is
+// this lane's row (input channel c at byte 2c), xzero 16 zero bytes.  Every step is
+// computed; for steps at or past s_end and for chunks past k the activations are read from
+// xzero.  The in-order vmcnt wait before step u covers only that step's two loads, so each
+// step is converted and multiplied while the later ones are still in flight.
+//
+// Only lanes whose activation row exists (live[mt]) read LDS: the others keep whatever xb
+// holds, which only reaches output columns that are never stored.  With one decode row
+// that is 4 of 64 lanes, so the fragment reads cost a sixteenth of the LDS bandwidth.
+template <int MT, int U>
+__device__ __forceinline__ void mma_batch_lds(const v4u (&w)[U][2], const char* const (&xrow)[MT],
+                                              const bool (&live)[MT], const char* xzero,
+                                              int64_t k, int s, int s_end, v4u (&xb)[MT][4],
+                                              v4f (&acc)[MT]) {
+  const int sub = 32 * ((threadIdx.x % 64) / 16);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
+    const bool in = (s + u) < s_end;
+    v8bf a[4];
+    i8x16_to_bf16(w[u][0], a[0], a[1]);
+    i8x16_to_bf16(w[u][1], a[2], a[3]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (live[mt]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t kc = kk + 8 * c;
+          const char* xp = in && kc < k ? xrow[mt] + 2 * kc : xzero;
+          xb[mt][c] = *reinterpret_cast<const v4u*>(xp);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a[c], __builtin_bit_cast(v8bf, xb[mt][c]), acc[mt], 0, 0, 0);
+    }
+  }
+}
+
+// Accumulate the wavefront's partial product over steps [s_begin, s_end), activations read
+// from global memory (L2-resident: every workgroup reads the same rows).
 //   wrow      : this lane's weight row (row n0 + lane % 16, clamped into the matrix)
 //   xrow      : this lane's activation row for each m-tile (lane % 16 within the tile);
 //               always a valid row, xok says whether it is a real one (else the MFMA
 //               column is fed zeros)
-// Chunks past k (k % 16 == 0) are read from the row start and replaced by zeros.
+// All loads of a batch of U steps are issued unconditionally (at in-bounds addresses) before
+// the first is used; steps past s_end, chunks past k and rows past m get zero activations.
 template <int MT, int U>
 __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wrow,
                                                   const uint16_t* const (&xrow)[MT],
@@ -70,33 +133,36 @@ __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wro
   const int sub = 32 * (lane / 16);  // this lane's 32 channels within a step
   for (int s = s_begin; s < s_end; s += U) {
     v4u w[U][2];
+    v4u xr[U][MT][4];
+    load_weight_batch<U>(wrow, k, s, s_end, w);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t kc = kk + 8 * c;
+          xr[u][mt][c] = *reinterpret_cast<const v4u*>(xrow[mt] + (kc < k ? kc : 0));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
       const bool in = (s + u) < s_end;
-      w[u][0] = load16_or_zero(wrow, kk, in && kk < k);
-      w[u][1] = load16_or_zero(wrow, kk + 16, in && kk + 16 < k);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s + u >= s_end) break;
-      const int64_t kk = static_cast<int64_t>(s + u) * kStepK + sub;
       v8bf a[4];
       i8x16_to_bf16(w[u][0], a[0], a[1]);
       i8x16_to_bf16(w[u][1], a[2], a[3]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        v4u xb[4];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int64_t kc = kk + 8 * c;
-          xb[c] = load16_or_zero(xrow[mt], kc * 2, xok[mt] && kc < k);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
+          const bool ok = in && xok[mt] && kk + 8 * c < k;
+          const v4u xb = ok ? xr[u][mt][c] : v4u{0u, 0u, 0u, 0u};
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a[c], __builtin_bit_cast(v8bf, xb[c]), acc[mt], 0, 0, 0);
-      }
+              a[c], __builtin_bit_cast(v8bf, xb), acc[mt], 0, 0, 0);
+        }
     }
   }
 }

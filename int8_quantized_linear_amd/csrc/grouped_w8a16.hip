@@ -20,7 +20,7 @@
 namespace i8ql {
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;  // steps per load batch with one m-tile (one step with four)
 constexpr int kMT = 4;          // m-tiles of 16 rows per pass
 constexpr int kList = 1024;     // assignments held in LDS per scan window
 
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
           dequant_mma_steps<1, kUnroll>(wrow, one, one_ok, k, sb, se, a1);
           acc[0] = a1[0];
         } else {
-          dequant_mma_steps<kMT, kUnroll>(wrow, xrow, xok, k, sb, se, acc);
+          dequant_mma_steps<kMT, 1>(wrow, xrow, xok, k, sb, se, acc);
         }
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) red[wave][mt][lane] = acc[mt];

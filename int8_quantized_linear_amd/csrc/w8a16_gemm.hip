@@ -12,24 +12,70 @@
 //     order (deterministic, no atomics);
 //   * each wave issues the loads of up to 8 steps of 16 rows x 128 bytes (two 16-byte loads
 //     per lane per step) before it converts the first, so 16 KiB per wave are in flight;
+//   * when they fit in LDS, the workgroup's activation rows are copied there by
+//     direct-to-LDS loads issued before the weight loads, so the weights are the only
+//     loads the multiply waits on and each step is multiplied as soon as its own bytes land;
 //   * the scale and bias are applied once, after the reduction over k.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "dequant_mma.hpp"
 #include "launch.h"
+#include "sync.hpp"
 
 namespace i8ql {
 namespace {
 
 constexpr int kUnroll = 8;  // steps of k whose loads a wavefront keeps in flight
+constexpr int kGlobalUnroll = 4;  // the same with activations loaded too (divided by MT)
+constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a function attribute
 
-template <int MT, int WAVES, int YT>
+// Dynamic LDS: the partial tiles of the WAVES wavefronts ([WAVES][MT][64] v4f), then, when
+// the activation rows are staged, rows of 2k + 16 bytes (consecutive rows shifted by one
+// 16-byte slot, so the row-parallel fragment reads do not collide on banks) and a 16-byte
+// zero block.
+template <int MT, int WAVES>
+constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * MT * 64 * sizeof(v4f); }
+
+// Direct-to-LDS copy instructions (1 KiB each) for `rows` staged activation rows: the area
+// is a run of 16-byte slots, slot q = r * (k / 8 + 1) + c holding chunk c of row r (the last
+// slot of each row is padding).
+__host__ __device__ inline int stage_insts(int rows, int64_t k) {
+  return static_cast<int>((rows * (k / 8 + 1) + 63) / 64);
+}
+
+// Issue the copy of activation rows m0 .. m0 + rows - 1 into xs (1 KiB-aligned).  Each
+// wavefront instruction fills one contiguous KiB, lane l its l-th slot; padding slots and
+// slots past the last row load row m0's first chunk, which is in bounds.
+template <int WAVES>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ x, int64_t m0, int rows,
+                                           int64_t k, char* xs) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int per_row = static_cast<int>(k / 8) + 1;
+  const int insts = stage_insts(rows, k);
+  int r = (wave * 64 + lane) / per_row, c = (wave * 64 + lane) % per_row;
+  const int adv_r = (64 * WAVES) / per_row, adv_c = (64 * WAVES) % per_row;
+  for (int i = wave; i < insts; i += WAVES) {
+    const bool ok = r < rows && c < per_row - 1;
+    const uint16_t* g = x + (ok ? (m0 + r) * k + 8 * c : m0 * k);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const int8_t*>(g), xs + 1024 * i, 16, 0,
+                                     0);
+    c += adv_c;
+    r += adv_r;
+    if (c >= per_row) {
+      c -= per_row;
+      ++r;
+    }
+  }
+}
+
+template <int MT, int WAVES, int YT, bool XLDS>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, const float* __restrict__ bias, void* __restrict__ y,
     int64_t m, int64_t n, int64_t k) {
-  __shared__ v4f red[WAVES][MT][64];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  v4f* red = reinterpret_cast<v4f*>(smem);
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
@@ -37,24 +83,59 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 
   const int64_t wr = min(n0 + lane % 16, n - 1);
   const int8_t* wrow = wq + wr * k;
-  const uint16_t* xrow[MT];
   bool xok[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t r = m0 + mt * 16 + lane % 16;
-    xok[mt] = r < m;
-    xrow[mt] = x + (xok[mt] ? r : 0) * k;
-  }
+  for (int mt = 0; mt < MT; ++mt) xok[mt] = m0 + mt * 16 + lane % 16 < m;
 
   v4f acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   int sb, se;
   wave_step_range(k, WAVES, wave, sb, se);
-  dequant_mma_steps<MT, kUnroll>(wrow, xrow, xok, k, sb, se, acc);
+
+  if constexpr (XLDS) {
+    // activation copy first, then the first batch of weight loads; wait for the copy only
+    // (the weight loads issued after it may stay in flight), then make it visible to all
+    char* xs = smem + red_bytes<MT, WAVES>();
+    const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m - m0));
+    char* xzero = xs + 1024 * stage_insts(rows, k);
+    if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
+    stage_rows<WAVES>(x, m0, rows, k, xs);
+    __builtin_amdgcn_sched_barrier(0);
+    v4u w[kUnroll][2];
+    load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
+    bare_barrier();
+    const int64_t pitch = 2 * k + 16;
+    const char* xrow[MT];
+    bool live[MT];
+    v4u xb[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = mt * 16 + lane % 16;
+      live[mt] = r < rows;
+      xrow[mt] = xs + (live[mt] ? r : 0) * pitch;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xb[mt][c] = v4u{0u, 0u, 0u, 0u};
+    }
+    mma_batch_lds<MT, kUnroll>(w, xrow, live, xzero, k, sb, se, xb, acc);
+    for (int s = sb + kUnroll; s < se; s += kUnroll) {
+      load_weight_batch<kUnroll>(wrow, k, s, se, w);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_batch_lds<MT, kUnroll>(w, xrow, live, xzero, k, s, se, xb, acc);
+    }
+  } else {
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      xrow[mt] = x + (xok[mt] ? m0 + mt * 16 + lane % 16 : 0) * k;
+    dequant_mma_steps<MT, (kGlobalUnroll / MT > 0 ? kGlobalUnroll / MT : 1)>(wrow, xrow, xok, k, sb,
+                                                                     se, acc);
+  }
 
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
   __syncthreads();
   if (wave != 0) return;
 
@@ -69,9 +150,9 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    v4f s = red[0][mt][lane];
+    v4f s = red[mt * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) s += red[w][mt][lane];
+    for (int w = 1; w < WAVES; ++w) s += red[(w * MT + mt) * 64 + lane];
     const int64_t row = m0 + mt * 16 + lane % 16;
     if (row >= m) continue;
 #pragma unroll
@@ -89,28 +170,43 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   }
 }
 
-// Wavefronts per workgroup: enough that each streams at most kUnroll steps of k (all its
-// loads in flight at once), between 4 and 16.  One 16-channel tile per workgroup; with
-// N / 16 workgroups of this size the whole weight matrix is in flight in about one
-// occupancy round on 256 CUs for the decoder shapes.
+template <int MT, int WAVES, int YT>
+hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
+                        const float* bias, void* y, int64_t m, int64_t n, int64_t k,
+                        hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 15) / 16),
+                  static_cast<unsigned>((m + 16 * MT - 1) / (16 * MT)));
+  const auto* xx = static_cast<const uint16_t*>(x);
+  const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m));
+  const size_t rbytes = red_bytes<MT, WAVES>();
+  const size_t xlds = rbytes + 1024 * static_cast<size_t>(stage_insts(rows, k)) + 16;
+  // (with more than 16 KiB of partial tiles, the rows of the k that calls for that many
+  // waves never fit)
+  constexpr bool can_stage = red_bytes<MT, WAVES>() <= kMaxDefaultLds / 4;
+  if (can_stage && xlds <= kMaxDefaultLds) {
+    hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, can_stage>), grid, dim3(64 * WAVES),
+                       xlds, stream, xx, wq, w_scale, bias, y, m, n, k);
+  } else {
+    hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, false>), grid, dim3(64 * WAVES),
+                       rbytes, stream, xx, wq, w_scale, bias, y, m, n, k);
+  }
+  return hipGetLastError();
+}
+
+// Wavefronts per workgroup: the fewest of 4, 8, 12 and 16 with which each streams at most
+// kUnroll steps of k (all its loads in flight at once; a wave with fewer real steps than
+// kUnroll still issues kUnroll steps of loads, so the count is matched to the steps).  One
+// 16-channel tile per workgroup: with N / 16 such workgroups the whole weight matrix is in
+// flight in about one occupancy round on 256 CUs for the decoder shapes.
 template <int MT, int YT>
 hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((n + 15) / 16),
-                  static_cast<unsigned>((m + 16 * MT - 1) / (16 * MT)));
   const int64_t steps = (k + kStepK - 1) / kStepK;
-  const auto* xx = static_cast<const uint16_t*>(x);
-  if (steps <= 4 * kUnroll) {
-    hipLaunchKernelGGL((w8a16_kernel<MT, 4, YT>), grid, dim3(64 * 4), 0, stream, xx, wq, w_scale,
-                       bias, y, m, n, k);
-  } else if (steps <= 8 * kUnroll) {
-    hipLaunchKernelGGL((w8a16_kernel<MT, 8, YT>), grid, dim3(64 * 8), 0, stream, xx, wq, w_scale,
-                       bias, y, m, n, k);
-  } else {
-    hipLaunchKernelGGL((w8a16_kernel<MT, 16, YT>), grid, dim3(64 * 16), 0, stream, xx, wq,
-                       w_scale, bias, y, m, n, k);
-  }
-  return hipGetLastError();
+  if (steps <= 4 * kUnroll) return launch_waves<MT, 4, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (steps <= 8 * kUnroll) return launch_waves<MT, 8, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (steps <= 12 * kUnroll)
+    return launch_waves<MT, 12, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_waves<MT, 16, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 template <int YT>

@@ -52,6 +52,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "sync.hpp"
 
 namespace i8ql {
 namespace {
@@ -98,20 +99,6 @@ __device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int64_
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
   return true;
-}
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt(vm) lgkmcnt(lgkm), expcnt left at its maximum.
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
-// Barrier with no memory fence.  A fence would wait for every load in flight; instead the
-// waits before it are explicit, and the empty asm statements keep the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Wait until at most `pending` of this wavefront's load batches (LOADS instructions each)
