@@ -5,10 +5,11 @@
 // mechanism, block 1: q = clamp(round(w / s)), s = absmax / largest code; "Phase 5a: int8
 // weight-only quantization", Summary: float32 arithmetic and an all-zero-channel guard).
 //
-// Work layout: one 64-lane wavefront per row, four rows per 256-thread workgroup.  Pass 1
-// streams the row with 16-byte loads (kept in registers when the row fits, up to 24 KiB),
-// reduces |a| to the row maximum with cross-lane shuffles; pass 2 divides, rounds and
-// packs 4 or 8 codes per store.  The row is read from HBM once; the op is HBM-bound
+// Work layout: one 64-lane wavefront per row, four rows per 256-thread workgroup, or, for
+// fewer than 1024 rows or rows of more than 768 chunks, a whole workgroup per row.  Pass 1 streams the row with 16-byte
+// loads (kept in registers when the row fits, up to 24 KiB per wavefront), reduces |a| to
+// the row maximum with cross-lane shuffles (and LDS across wavefronts); pass 2 divides,
+// rounds and packs 4 or 8 codes per store.  The row is read from HBM once; the op is HBM-bound
 // (2 + 1 bytes per bf16 element).
 //
 // Arithmetic (identical for every dtype): the input is widened exactly to float32;
@@ -26,6 +27,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kRowsPerBlock = 4;
 constexpr int kCacheChunks = 24;  // 16-byte chunks per lane kept in registers (24 KiB rows)
+constexpr int64_t kSplitRowsBelow = 1024;  // fewer rows: four wavefronts per row
 
 template <int DT>
 struct Fmt;
@@ -103,19 +105,27 @@ __device__ __forceinline__ float chunk_absmax(const float* f, int n, float m) {
   return m;
 }
 
-// Vector path: row bytes are a multiple of 16 and the base is 16-byte aligned.
-template <int DT>
+// Vector path: row bytes are a multiple of 16 and the base is 16-byte aligned.  W wavefronts
+// share a row (W = 4 when there are few rows, so that short launches still fill the CUs;
+// their maxima meet in LDS); a workgroup holds 4 / W rows.  Every lane loads all of its
+// chunks before it uses one: loads past the row's end re-read its last chunk (harmless to
+// the maximum, never stored), so they are unconditional and all in flight together.
+template <int DT, int W>
 __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel(
     const uint8_t* __restrict__ a, int64_t rows, int64_t k, int8_t* __restrict__ q,
     float* __restrict__ scale) {
   constexpr int E = Fmt<DT>::kPerChunk;
-  const int lane = threadIdx.x % kWave;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
-  if (row >= rows) return;
+  constexpr int T = kWave * W;  // threads per row
+  __shared__ float wmax[kRowsPerBlock];
+  const int t = threadIdx.x % T;
+  const int slot = threadIdx.x / T;  // row within the workgroup
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kRowsPerBlock / W) + slot;
+  const bool live = row < rows;  // whole rows only; a dead row still joins the barrier
+  const int64_t rr = live ? row : rows - 1;
   const int64_t chunks = k / E;
-  const uint4* src = reinterpret_cast<const uint4*>(a + row * k * Fmt<DT>::kBytes);
-  int8_t* dst = q + row * k;
-  const bool cached = chunks <= static_cast<int64_t>(kCacheChunks) * kWave;
+  const uint4* src = reinterpret_cast<const uint4*>(a + rr * k * Fmt<DT>::kBytes);
+  int8_t* dst = q + rr * k;
+  const bool cached = chunks <= static_cast<int64_t>(kCacheChunks) * T;
 
   uint4 cache[kCacheChunks];
   float amax = 0.0f;
@@ -123,30 +133,36 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel
   if (cached) {
 #pragma unroll
     for (int i = 0; i < kCacheChunks; ++i) {
-      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
-      if (c < chunks) cache[i] = src[c];
+      const int64_t c = t + static_cast<int64_t>(i) * T;
+      if (static_cast<int64_t>(i) * T < chunks) cache[i] = src[c < chunks ? c : chunks - 1];
     }
 #pragma unroll
     for (int i = 0; i < kCacheChunks; ++i) {
-      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
-      if (c < chunks) {
+      if (static_cast<int64_t>(i) * T < chunks) {
         widen_chunk<DT>(cache[i], f);
         amax = chunk_absmax(f, E, amax);
       }
     }
   } else {
-    for (int64_t c = lane; c < chunks; c += kWave) {
+    for (int64_t c = t; c < chunks; c += T) {
       widen_chunk<DT>(src[c], f);
       amax = chunk_absmax(f, E, amax);
     }
   }
   amax = wave_max(amax);
+  if constexpr (W > 1) {
+    if (threadIdx.x % kWave == 0) wmax[threadIdx.x / kWave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < W; ++w) amax = fmaxf(amax, wmax[slot * W + w]);
+  }
+  if (!live) return;
   const float s = amax / 127.0f;
 
   if (s == 0.0f) {  // all-zero channel: scale 1, codes 0
-    for (int64_t j = lane * 4; j < k; j += kWave * 4)
+    for (int64_t j = t * 4; j < k; j += T * 4)
       *reinterpret_cast<uint32_t*>(dst + j) = 0u;  // k % 4 == 0 on this path
-    if (lane == 0) scale[row] = 1.0f;
+    if (t == 0) scale[row] = 1.0f;
     return;
   }
 
@@ -170,13 +186,13 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel
   if (cached) {
 #pragma unroll
     for (int i = 0; i < kCacheChunks; ++i) {
-      const int64_t c = lane + static_cast<int64_t>(i) * kWave;
+      const int64_t c = t + static_cast<int64_t>(i) * T;
       if (c < chunks) emit(cache[i], c);
     }
   } else {
-    for (int64_t c = lane; c < chunks; c += kWave) emit(src[c], c);
+    for (int64_t c = t; c < chunks; c += T) emit(src[c], c);
   }
-  if (lane == 0) scale[row] = s;
+  if (t == 0) scale[row] = s;
 }
 
 // Scalar path: any k and any element-aligned base.
@@ -210,8 +226,15 @@ hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* s
   const bool vec = (k * Fmt<DT>::kBytes) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(a) % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(q) % 8) == 0;
-  if (vec) {
-    hipLaunchKernelGGL(quantize_rows_vec_kernel<DT>, grid, block, 0, stream,
+  // four wavefronts per row when one per row would leave the CUs short of wavefronts, or
+  // give each lane more than 12 chunks
+  const int64_t chunks = k / Fmt<DT>::kPerChunk;
+  if (vec && (rows < kSplitRowsBelow || chunks > 12 * kWave)) {
+    const dim3 grid4(static_cast<unsigned>(rows));
+    hipLaunchKernelGGL((quantize_rows_vec_kernel<DT, 4>), grid4, block, 0, stream,
+                       static_cast<const uint8_t*>(a), rows, k, q, scale);
+  } else if (vec) {
+    hipLaunchKernelGGL((quantize_rows_vec_kernel<DT, 1>), grid, block, 0, stream,
                        static_cast<const uint8_t*>(a), rows, k, q, scale);
   } else {
     hipLaunchKernelGGL(quantize_rows_scalar_kernel<DT>, grid, block, 0, stream, a, rows, k, q,

@@ -38,11 +38,11 @@
 // (k % 16 == 0, so chunks are whole) read the row start; once the last step has landed its
 // A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
-// Configurations: 128 x 128 tiles, 128-byte steps, 2 stages (64 KiB of LDS, 64 x 64 per
-// wavefront) for large grids; for small grids 64 x 64 tiles with four k-groups of 4
-// wavefronts (in-workgroup split-K: each group walks a quarter of k through its own LDS
-// stages and the partial int32 tiles are summed exactly through LDS), or 64 x 128 tiles
-// with 4 stages when k does not split evenly.
+// Configurations (all with 128-byte k steps): 64 x 64 tiles with two k-groups of 4
+// wavefronts (in-workgroup split-K: each group walks half of k through its own LDS stages and
+// the partial int32 tiles are summed exactly through LDS) for the fewest tiles, 64 x 64 and
+// 128 x 64 tiles with 4 and 3 stages for medium grids, 128 x 128 tiles with 2 stages (64 KiB
+// of LDS, 64 x 64 per wavefront, two workgroups per CU) for large ones.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -60,7 +60,6 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;  // 2 x 2 wavefronts per k-group
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
@@ -123,15 +122,17 @@ __device__ __forceinline__ void wait_and_barrier(int pending) {
 }
 
 // Tile geometry and per-thread addressing shared by the pieces of the kernel.
-template <int BM_, int BN_, int BK_, int STAGES_, int KS_>
+template <int BM_, int BN_, int BK_, int STAGES_, int KS_, int WM_, int WN_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, KS = KS_;
-  static constexpr int THREADS = 64 * kWaves * KS;
-  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wavefront sub-tile
+  static constexpr int WM = WM_, WN = WN_;          // wavefront grid of a k-group
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES * KS;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int CHUNKS = BK / 16;            // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / BK;   // rows per wavefront load instruction
-  static constexpr int LOADS = (BM + BN) / ROWS_PER_LOAD / kWaves;  // per wavefront per step
+  static constexpr int LOADS = (BM + BN) / ROWS_PER_LOAD / WAVES;  // per wavefront per step
   static constexpr int SLICES = BK / 32;
   static constexpr int STAGE_BYTES = (BM + BN) * BK;
   static constexpr size_t GROUP_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
@@ -140,7 +141,7 @@ struct Cfg {
   static_assert(KS == 1 || KS == 2 || KS == 4, "k-groups per workgroup");
   static_assert(BK == 64 || BK == 128, "BK is 64 or 128 bytes");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "sub-tile must be whole 32x32 blocks");
-  static_assert(LOADS * ROWS_PER_LOAD * kWaves == BM + BN, "loads must split over waves");
+  static_assert(LOADS * ROWS_PER_LOAD * WAVES == BM + BN, "loads must split over waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "wait_and_barrier handles up to 3 pending");
   static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
 };
@@ -202,7 +203,7 @@ __device__ __forceinline__ void reads_under_mfmas() {
 template <class C>
 __device__ __forceinline__ void zero_tail(int8_t* stage, int valid) {
   const int dead = C::CHUNKS - valid;
-  for (int e = threadIdx.x % (64 * kWaves); e < C::BM * dead; e += 64 * kWaves) {
+  for (int e = threadIdx.x % (64 * C::WAVES); e < C::BM * dead; e += 64 * C::WAVES) {
     const int row = e / dead;
     const int chunk = valid + e % dead;
     *reinterpret_cast<v4i*>(stage + row * C::BK + (chunk ^ swizzle<C::BK>(row)) * 16) =
@@ -250,12 +251,12 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
   reads_under_mfmas<C, 1>();
 }
 
-template <int BM, int BN, int BK, int STAGES, int KS, int YT>
-__global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
+template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT>
+__global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
     const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
-  using C = Cfg<BM, BN, BK, STAGES, KS>;
+  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN;
   extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
 
@@ -265,9 +266,9 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
   const int64_t n0 = tn * BN;
 
   const int lane = threadIdx.x % 64;
-  const int group = threadIdx.x / (64 * kWaves);  // k-group (in-workgroup split-K)
-  const int wave = (threadIdx.x / 64) % kWaves;   // wavefront within the k-group
-  const int wm = wave / 2, wn = wave % 2;
+  const int group = threadIdx.x / (64 * C::WAVES);  // k-group (in-workgroup split-K)
+  const int wave = (threadIdx.x / 64) % C::WAVES;   // wavefront within the k-group
+  const int wm = wave / WN, wn = wave % WN;
   // Each k-group walks its own equal share of the steps (KS > 1 only when it divides
   // evenly) in its own LDS stages; all groups pass the same barriers.
   const int ksteps = static_cast<int>((k + BK - 1) / BK) / KS;
@@ -275,13 +276,13 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
   int8_t* lds = lds_all + group * C::GROUP_BYTES;
 
   // This lane's part of each of the wavefront's load instructions: instruction j covers
-  // rows ROWS_PER_LOAD * (wave + kWaves * j) + [0, ROWS_PER_LOAD) of the stacked [A; B] slice.
+  // rows ROWS_PER_LOAD * (wave + WAVES * j) + [0, ROWS_PER_LOAD) of the stacked [A; B] slice.
   const int8_t* src[C::LOADS];
   int col[C::LOADS];
   int dst[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::LOADS; ++j) {
-    const int blk = wave + kWaves * j;
+    const int blk = wave + C::WAVES * j;
     const int trow = blk * C::ROWS_PER_LOAD + lane / C::CHUNKS;  // row of the stacked tile
     const int pchunk = lane % C::CHUNKS;
     col[j] = (pchunk ^ swizzle<BK>(trow)) * 16;
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       bare_barrier();  // every group is done with its LDS stages / the previous round
       if (group >= h && group < 2 * h) {
-        int* out = red + ((group - h) * kWaves + wave) * kRegs * 64 + lane;
+        int* out = red + ((group - h) * C::WAVES + wave) * kRegs * 64 + lane;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       bare_barrier();
       if (group < h) {
-        const int* in = red + (group * kWaves + wave) * kRegs * 64 + lane;
+        const int* in = red + (group * C::WAVES + wave) * kRegs * 64 + lane;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -361,17 +362,30 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
   }
 
   // ---- fused epilogue ----------------------------------------------------------------
+  // The scales are loaded up front at clamped (valid) indices, so that their loads are issued
+  // together and waited for once instead of one round trip per output row.
   const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
   const int64_t col_base = n0 + wn * C::WTN + lane % 32;
+  float sx[TM][16], sw[TN], bj[TN];
+  if constexpr (YT != I8QL_I32) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
+        sx[i][r] = x_scale[row < m ? row : m - 1];
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t c = col_base + j * 32;
+      sw[j] = w_scale[c < n ? c : n - 1];
+      bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t c = col_base + j * 32;
     if (c >= n) continue;
-    float sw = 0.0f, bj = 0.0f;
-    if constexpr (YT != I8QL_I32) {
-      sw = w_scale[c];
-      if (bias) bj = bias[c];
-    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -382,8 +396,8 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
         if constexpr (YT == I8QL_I32) {
           static_cast<int32_t*>(y)[row * n + c] = a;
         } else {
-          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), x_scale[row]), sw);
-          if (bias) v = __fadd_rn(v, bj);
+          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[i][r]), sw[j]);
+          if (bias) v = __fadd_rn(v, bj[j]);
           if constexpr (YT == I8QL_F32) {
             static_cast<float*>(y)[row * n + c] = v;
           } else {
@@ -395,12 +409,12 @@ __global__ __launch_bounds__(64 * kWaves * KS) void w8a8_kernel(
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, int KS, int YT>
+template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM = 2, int WN = 2>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                       int64_t k, hipStream_t stream) {
-  using C = Cfg<BM, BN, BK, STAGES, KS>;
-  auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, YT>;
+  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
+  auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT>;
   static bool configured = false;  // idempotent attribute set; a race only repeats it
   if (!configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -416,27 +430,29 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Configuration by grid size, from graph-timed MI355X measurements (us):
-//   shape (M x N x K)   64x64 tiles, 4 k-groups   64x128, 1 k-group   128x128, 128-byte steps
-//   128 x 1024 x 2560          12.1                      19.1                 23.5
-//   128 x 2560 x 9728          40.0                      54.1                 77.7
-//   512 x 2560 x 9728          50.1                      54.6                 75.2
-//   512 x 9728 x 2560          50.0                      40.0                 39.4
-//   2048 x 9728 x 2560        162.8                     132.8                101.7
-// Few tiles (<= 512 of 64 x 64): split k four ways inside the workgroup (when 256-byte
-// chunks divide k); otherwise 128 x 128 tiles, whose two to three workgroups per CU keep the
-// matrix cores busiest on large grids.
+// Configuration by grid size (tiles of 64 x 64), from graph-timed MI355X measurements (us):
+//   shape (M x N x K)  64x64 3st 2grp  64x64 4st   128x64 3st   128x128 2st   (all 128-byte steps)
+//   128 x 4096 x 2560        10.5          11.8         15.5          20.3
+//   128 x 2560 x 9728        27.8          29.9         42.0          73.7
+//   128 x 19456 x 2560       33.9          27.8         30.1          28.7
+//   512 x 6144 x 2560        31.7          25.4         24.8          26.6
+//   512 x 19456 x 2560       99.6          71.7         61.3          62.1
+//   2048 x 6144 x 2560      117.7          80.5         66.9          62.4
+// 128-byte steps read whole 128-byte lines of each row (64-byte steps reach about half the
+// per-CU load rate).  Few tiles: 64 x 64 tiles and two k-groups per workgroup (when
+// 256-byte chunks divide k), so that more CUs stream; then 64 x 64 tiles with 4 stages,
+// 128 x 64 with 3, and 128 x 128 tiles with 2 stages (two workgroups per CU) on large grids.
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                      int64_t k, hipStream_t stream) {
   const int64_t tiles64 = ((m + 63) / 64) * ((n + 63) / 64);
-  if (tiles64 <= 512) {
-    if (k % (4 * 64) == 0)
-      return launch_cfg<64, 64, 64, 2, 4, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
-                                              stream);
-    return launch_cfg<64, 128, 64, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  }
+  if (tiles64 <= 256 && k % (2 * 128) == 0)
+    return launch_cfg<64, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  if (tiles64 <= 768)
+    return launch_cfg<64, 64, 128, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  if (tiles64 <= 2048)
+    return launch_cfg<128, 64, 128, 3, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
   return launch_cfg<128, 128, 128, 2, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 

@@ -37,6 +37,11 @@ DENSE_8B = {
 MOE_16B = {"gate": (1408, 2048), "up": (1408, 2048), "down": (2048, 1408)}
 MOE_ROUTED, MOE_SHARED, MOE_TOP = 64, 2, 6
 
+# Projections that read the same layer input run as one GEMM over their concatenated
+# weights (per-channel scales concatenated alike): the same products as separate launches.
+DENSE_4B_FUSED = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"),
+                  "down": ("down",)}
+
 PREFILL_4B_TOKENS = (128, 512, 2048)
 DECODE_8B_BATCH = (1, 4, 8)
 MOE_TOKENS = (1, 4, 16, 64)
