@@ -50,12 +50,15 @@ KERNEL_SOURCES = {
 }
 
 
+CALIB_BYTES = 256 << 20  # calibration copy for the traffic counters
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
 def source_sha(kernel: str) -> str:
-    paths = [KERNEL_SOURCES[kernel]]
+    paths = [KERNEL_SOURCES[kernel], "int8_quantized_linear_amd/csrc/sync.hpp"]
     if "w8a16" in kernel:
         paths.append("int8_quantized_linear_amd/csrc/dequant_mma.hpp")
     h = hashlib.sha256()
@@ -429,6 +432,23 @@ def section_prefill_8b(torch, i8, wl, dev, args, result):
                             "M in {4096,16384}", "unit": "TOPS", **out}
 
 
+def section_counters(torch, i8, wl, dev, args, result):
+    """Eager launches for the hardware-counter runs (rocprofv3 --pmc FETCH_SIZE, then
+    WRITE_SIZE): first a 256 MiB device-to-device copy whose counter readings calibrate the
+    counters (it moves exactly 256 MiB each way), then two steps of the benchmark workload
+    with its weight rotation, each kernel launched on its own."""
+    st = prefill_4b_setup(torch, i8, wl, dev)
+    a = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    for step in range(2):
+        prefill_4b_step(i8, wl, st, step)
+    torch.cuda.synchronize()
+    result["counters"] = {"calibration_copy_bytes": CALIB_BYTES, "steps": 2}
+
+
 def section_weight_quant(torch, i8, wl, dev, args, result):
     g = wl.rng(4)
     ws = {nm: wl.to_bf16(wl.weight(g, n, k)).to(dev) for nm, (n, k) in wl.DENSE_8B.items()}
@@ -493,6 +513,8 @@ def main():
         section_prefill_8b(torch, i8, wl, dev, args, result)
     if "weight_quant" in sections:
         section_weight_quant(torch, i8, wl, dev, args, result)
+    if "counters" in sections:  # only for hardware-counter runs, not in the default list
+        section_counters(torch, i8, wl, dev, args, result)
     print(json.dumps(result), flush=True)
 
 

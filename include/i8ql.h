@@ -121,9 +121,9 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
  * y        device, [m, n] of y_dtype in {I8QL_BF16, I8QL_F32, I8QL_I32}.
  * m, n >= 0; 16 <= k <= 133144 and k % 16 == 0.
  * Errors: NULL (x_scale/w_scale may be NULL only with I32 output) -> I8QL_ERR_NULL;
- * negative m/n, k < 1 -> I8QL_ERR_SHAPE; k % 16 or misaligned xq/wq -> I8QL_ERR_ALIGN;
- * k > 133144 -> I8QL_ERR_K_TOO_LARGE; other y_dtype -> I8QL_ERR_DTYPE; bias with I32 ->
- * I8QL_ERR_ARG.
+ * negative m/n, k < 1, or more than 2^31 - 9 output tiles of 64 x 64 -> I8QL_ERR_SHAPE;
+ * k % 16 or misaligned xq/wq -> I8QL_ERR_ALIGN; k > 133144 -> I8QL_ERR_K_TOO_LARGE; other
+ * y_dtype -> I8QL_ERR_DTYPE; bias with I32 -> I8QL_ERR_ARG.
  */
 i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
@@ -173,7 +173,7 @@ i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, co
  * w_scale     device, [num_experts, n] float32.
  * expert_ids  device, [t, topk] int32.
  * y           device, [t * topk, n] of y_dtype in {I8QL_BF16, I8QL_F32}.
- * t, n >= 0; 1 <= topk <= 64; t * topk <= 65536; 1 <= num_experts <= 65535;
+ * t, n >= 0; 1 <= topk <= 64; t * topk <= 65536; 1 <= num_experts <= 65534;
  * k >= 16, k % 16 == 0.
  * Errors: as for w8a16_gemm; x_per_assignment not 0/1, topk or num_experts out of range ->
  * I8QL_ERR_ARG; t * topk > 65536 -> I8QL_ERR_SHAPE.

@@ -73,7 +73,9 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32 && y_dtype != I8QL_I32) return I8QL_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
   if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
-  if ((n + 127) / 128 > kMaxGridX || (m + 127) / 128 > kMaxGridY) return I8QL_ERR_SHAPE;
+  // one workgroup per output tile (64 x 64 at the smallest), in a one-dimensional grid
+  const int64_t tm = (m + 63) / 64, tn = (n + 63) / 64;
+  if (!mul_ok(tm, tn) || tm * tn > kMaxGridX - 8) return I8QL_ERR_SHAPE;
   if (m == 0 || n == 0) return I8QL_OK;
   if (!xq || !wq || !y) return I8QL_ERR_NULL;
   if (y_dtype != I8QL_I32 && (!x_scale || !w_scale)) return I8QL_ERR_NULL;

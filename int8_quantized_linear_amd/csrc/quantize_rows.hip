@@ -229,7 +229,7 @@ hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* s
   // four wavefronts per row when one per row would leave the CUs short of wavefronts, or
   // give each lane more than 12 chunks
   const int64_t chunks = k / Fmt<DT>::kPerChunk;
-  if (vec && (rows < kSplitRowsBelow || chunks > 12 * kWave)) {
+  if (vec && (rows < kSplitRowsBelow || chunks > 12 * kWave) && rows <= INT32_MAX) {
     const dim3 grid4(static_cast<unsigned>(rows));
     hipLaunchKernelGGL((quantize_rows_vec_kernel<DT, 4>), grid4, block, 0, stream,
                        static_cast<const uint8_t*>(a), rows, k, q, scale);

@@ -42,7 +42,8 @@
 // wavefronts (in-workgroup split-K: each group walks half of k through its own LDS stages and
 // the partial int32 tiles are summed exactly through LDS) for the fewest tiles, 64 x 64 and
 // 128 x 64 tiles with 4 and 3 stages for medium grids, 128 x 128 tiles with 2 stages (64 KiB
-// of LDS, 64 x 64 per wavefront, two workgroups per CU) for large ones.
+// of LDS, 64 x 64 per wavefront, two workgroups per CU) for large ones, and 256 x 256 tiles
+// of 8 wavefronts (64 x 128 each) for the largest.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -362,19 +363,12 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   }
 
   // ---- fused epilogue ----------------------------------------------------------------
-  // The scales are loaded up front at clamped (valid) indices, so that their loads are issued
-  // together and waited for once instead of one round trip per output row.
+  // Per 32-row block, the row scales are loaded up front at clamped (valid) indices, so that
+  // their loads are issued together and waited for once instead of once per output row.
   const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
   const int64_t col_base = n0 + wn * C::WTN + lane % 32;
-  float sx[TM][16], sw[TN], bj[TN];
+  float sw[TN], bj[TN];
   if constexpr (YT != I8QL_I32) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
-        sx[i][r] = x_scale[row < m ? row : m - 1];
-      }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t c = col_base + j * 32;
@@ -383,11 +377,19 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     }
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t c = col_base + j * 32;
-    if (c >= n) continue;
+  for (int i = 0; i < TM; ++i) {
+    float sx[16];
+    if constexpr (YT != I8QL_I32) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
+        sx[r] = x_scale[row < m ? row : m - 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t c = col_base + j * 32;
+      if (c >= n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
         if constexpr (YT == I8QL_I32) {
           static_cast<int32_t*>(y)[row * n + c] = a;
         } else {
-          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[i][r]), sw[j]);
+          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[r]), sw[j]);
           if (bias) v = __fadd_rn(v, bj[j]);
           if constexpr (YT == I8QL_F32) {
             static_cast<float*>(y)[row * n + c] = v;
@@ -438,6 +440,11 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 //   512 x 6144 x 2560        31.7          25.4         24.8          26.6
 //   512 x 19456 x 2560       99.6          71.7         61.3          62.1
 //   2048 x 6144 x 2560      117.7          80.5         66.9          62.4
+// and 256 x 256 tiles with 8 wavefronts of 64 x 128 (2 stages, 128 KiB of LDS, one workgroup
+// per CU) where there are at least 192 of them: 2048 x 6144 x 2560 59.5 (64.2 with
+// 128 x 128), 2048 x 19456 x 2560 165.9 (174.8), 4096 x 12288 x 4096 242.6 (287.1),
+// 16384 x 12288 x 4096 928 (1043); with fewer tiles too many CUs idle (2048 x 2560 x 9728:
+// 128.1 against 91.8).
 // 128-byte steps read whole 128-byte lines of each row (64-byte steps reach about half the
 // per-CU load rate).  Few tiles: 64 x 64 tiles and two k-groups per workgroup (when
 // 256-byte chunks divide k), so that more CUs stream; then 64 x 64 tiles with 4 stages,
@@ -451,8 +458,12 @@ hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
     return launch_cfg<64, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
   if (tiles64 <= 768)
     return launch_cfg<64, 64, 128, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  if (tiles64 <= 2048)
+  if (tiles64 <= 1024)
     return launch_cfg<128, 64, 128, 3, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+  if (tiles256 >= 192)
+    return launch_cfg<256, 256, 128, 2, 1, YT, 4, 2>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
+                                                      stream);
   return launch_cfg<128, 128, 128, 2, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 

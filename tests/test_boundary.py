@@ -81,6 +81,7 @@ def test_w8a8_validation(lib):
     assert call(args(m=-1)) == SHAPE
     assert call(args(n=-2)) == SHAPE
     assert call(args(k=0)) == SHAPE
+    assert call(args(m=1 << 30, n=1 << 30, k=16)) == SHAPE  # 2^48 output tiles
     assert call(args(m=0, xq=NUL, y=NUL)) == OK
     assert call(args(n=0)) == OK
     assert call(args(xq=NUL)) == NULL

@@ -158,9 +158,13 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
             check_float(y, yref, w8a8_tol(acc, sxr, swr, b_np), f"w8a8 {m}x{n}x{k} {od}")
 
 
+# Shapes chosen to reach every tile configuration with ragged edges and a partial last
+# k step: 64 x 64 with two k-groups, 64 x 64 / 4 stages, 128 x 64 / 3 stages (1100 x 3000),
+# 128 x 128 (2100 x 2600) and 256 x 256 (3000 x 4100).
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (4, 256, 512), (3, 130, 48), (130, 200, 272),
                                    (257, 385, 1040), (128, 128, 128), (64, 700, 4096),
-                                   (300, 33, 2576)])
+                                   (300, 33, 2576), (1100, 3000, 272), (2100, 2600, 1040),
+                                   (3000, 4100, 272)])
 def test_w8a8_small(ref, dev, m, n, k):
     run_w8a8(ref, dev, m, n, k, seed=m * 7 + n)
 
@@ -215,6 +219,10 @@ def sampled_rows(m, n_rand=256, seed=0):
 
 
 PREFILL_4B = [(m, n, k) for m in wl.PREFILL_4B_TOKENS for (n, k) in wl.DENSE_4B.values()]
+# the fused launches of the benchmark step (q/k/v and gate/up over concatenated weights)
+PREFILL_4B += [(m, sum(wl.DENSE_4B[p][0] for p in parts), wl.DENSE_4B[parts[0]][1])
+               for m in wl.PREFILL_4B_TOKENS for parts in wl.DENSE_4B_FUSED.values()
+               if len(parts) > 1]
 PREFILL_8B = [(m, n, k) for m in wl.PREFILL_8B_TOKENS
               for (n, k) in sorted(set(wl.DENSE_8B.values()))]
 
