@@ -167,6 +167,43 @@ __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wro
   }
 }
 
+// Staged activation rows in LDS: row r at r * (2k + 16) bytes (consecutive rows shifted by
+// one 16-byte slot, so the row-parallel fragment reads do not collide on banks), i.e. a run
+// of 16-byte slots where slot q = r * (k / 8 + 1) + c holds chunk c of row r and the last
+// slot of each row is padding.  Copy instructions (1 KiB each) needed for `rows` rows:
+__host__ __device__ inline int stage_insts(int rows, int64_t k) {
+  return static_cast<int>((rows * (k / 8 + 1) + 63) / 64);
+}
+
+// Issue the direct-to-LDS copy of `rows` activation rows into xs (1 KiB-aligned): row r is
+// x row r, or, with a gather list, x row list[r] / div.  Each wavefront instruction fills
+// one contiguous KiB, lane l its l-th slot; padding slots and slots past the last row load
+// the first chunk of the first row, which is in bounds.  The loads count in vmcnt like any
+// other: the caller waits for them before a barrier that publishes the rows.
+template <int WAVES>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ x, const int* list,
+                                           int div, int rows, int64_t k, char* xs) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int per_row = static_cast<int>(k / 8) + 1;
+  const int insts = stage_insts(rows, k);
+  int r = (wave * 64 + lane) / per_row, c = (wave * 64 + lane) % per_row;
+  const int adv_r = (64 * WAVES) / per_row, adv_c = (64 * WAVES) % per_row;
+  const int64_t first = list ? list[0] / div : 0;
+  for (int i = wave; i < insts; i += WAVES) {
+    const bool ok = r < rows && c < per_row - 1;
+    const int64_t xr = ok ? (list ? list[r] / div : r) : first;
+    const uint16_t* g = x + xr * k + (ok ? 8 * c : 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const int8_t*>(g), xs + 1024 * i, 16, 0,
+                                     0);
+    c += adv_c;
+    r += adv_r;
+    if (c >= per_row) {
+      c -= per_row;
+      ++r;
+    }
+  }
+}
+
 // Split the steps of k among the waves of a workgroup: wave w gets [begin, end).
 __device__ __forceinline__ void wave_step_range(int64_t k, int waves, int wave, int& begin,
                                                 int& end) {

@@ -37,38 +37,6 @@ constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a functi
 template <int MT, int WAVES>
 constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * MT * 64 * sizeof(v4f); }
 
-// Direct-to-LDS copy instructions (1 KiB each) for `rows` staged activation rows: the area
-// is a run of 16-byte slots, slot q = r * (k / 8 + 1) + c holding chunk c of row r (the last
-// slot of each row is padding).
-__host__ __device__ inline int stage_insts(int rows, int64_t k) {
-  return static_cast<int>((rows * (k / 8 + 1) + 63) / 64);
-}
-
-// Issue the copy of activation rows m0 .. m0 + rows - 1 into xs (1 KiB-aligned).  Each
-// wavefront instruction fills one contiguous KiB, lane l its l-th slot; padding slots and
-// slots past the last row load row m0's first chunk, which is in bounds.
-template <int WAVES>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ x, int64_t m0, int rows,
-                                           int64_t k, char* xs) {
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int per_row = static_cast<int>(k / 8) + 1;
-  const int insts = stage_insts(rows, k);
-  int r = (wave * 64 + lane) / per_row, c = (wave * 64 + lane) % per_row;
-  const int adv_r = (64 * WAVES) / per_row, adv_c = (64 * WAVES) % per_row;
-  for (int i = wave; i < insts; i += WAVES) {
-    const bool ok = r < rows && c < per_row - 1;
-    const uint16_t* g = x + (ok ? (m0 + r) * k + 8 * c : m0 * k);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const int8_t*>(g), xs + 1024 * i, 16, 0,
-                                     0);
-    c += adv_c;
-    r += adv_r;
-    if (c >= per_row) {
-      c -= per_row;
-      ++r;
-    }
-  }
-}
-
 template <int MT, int WAVES, int YT, bool XLDS>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
@@ -100,10 +68,12 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m - m0));
     char* xzero = xs + 1024 * stage_insts(rows, k);
     if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
-    stage_rows<WAVES>(x, m0, rows, k, xs);
+    stage_rows<WAVES>(x + m0 * k, nullptr, 1, rows, k, xs);
+    asm volatile("" ::: "memory");  // the weight loads stay behind the copy (wait count below)
     __builtin_amdgcn_sched_barrier(0);
     v4u w[kUnroll][2];
     load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
     bare_barrier();

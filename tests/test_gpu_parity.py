@@ -344,6 +344,18 @@ def test_grouped_small_edge_cases(ref, dev, out_dtype):
                     out_dtype, g)
 
 
+def test_grouped_single_token_repeated_expert(ref, dev):
+    """One token routed three times to one expert: the expert's rows exceed the token count
+    that sizes the staged passes, so it takes several passes."""
+    g = wl.rng(24)
+    e, n, k = 6, 72, 2048
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.array([[2, 2, 5, 2]], dtype=np.int32)
+    for per_assign in (False, True):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, 4 if per_assign else 1, per_assign,
+                    torch.bfloat16, g)
+
+
 def test_grouped_one_expert_equals_w8a16(ref, dev):
     g = wl.rng(22)
     n, k = 100, 512
