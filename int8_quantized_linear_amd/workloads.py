@@ -42,6 +42,9 @@ MOE_ROUTED, MOE_SHARED, MOE_TOP = 64, 2, 6
 DENSE_4B_FUSED = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"),
                   "down": ("down",)}
 
+DENSE_8B_FUSED = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"),
+                  "down": ("down",)}
+
 PREFILL_4B_TOKENS = (128, 512, 2048)
 DECODE_8B_BATCH = (1, 4, 8)
 MOE_TOKENS = (1, 4, 16, 64)

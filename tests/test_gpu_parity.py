@@ -285,6 +285,10 @@ def test_w8a16_small(ref, dev, m, n, k, out_dtype):
 
 
 DECODE_8B = [(m, n, k) for m in wl.DECODE_8B_BATCH for (n, k) in sorted(set(wl.DENSE_8B.values()))]
+# the fused launches of the benchmark's decode layer (q/k/v and gate/up concatenated)
+DECODE_8B += [(m, sum(wl.DENSE_8B[p][0] for p in parts), wl.DENSE_8B[parts[0]][1])
+              for m in wl.DECODE_8B_BATCH for parts in wl.DENSE_8B_FUSED.values()
+              if len(parts) > 1]
 
 
 @pytest.mark.parametrize("m,n,k", DECODE_8B)
