@@ -38,12 +38,14 @@
 // (k % 16 == 0, so chunks are whole) read the row start; once the last step has landed its
 // A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
-// Configurations (all with 128-byte k steps): 64 x 64 tiles with two k-groups of 4
-// wavefronts (in-workgroup split-K: each group walks half of k through its own LDS stages and
-// the partial int32 tiles are summed exactly through LDS) for the fewest tiles, 64 x 64 and
-// 128 x 64 tiles with 4 and 3 stages for medium grids, 128 x 128 tiles with 2 stages (64 KiB
-// of LDS, 64 x 64 per wavefront, two workgroups per CU) for large ones, and 256 x 256 tiles
-// of 8 wavefronts (64 x 128 each) for the largest.
+// Configurations (all with 128-byte k steps), by grid size: 64 x 64 or 128 x 64 tiles with
+// two k-groups of 4 wavefronts (in-workgroup split-K: each group walks half of k through its
+// own LDS stages and the partial int32 tiles are summed exactly through LDS) for the fewest
+// tiles, 128 x 128 tiles with 8 wavefronts of 64 x 32 for medium grids, 256 x 256 tiles of
+// 8 wavefronts (64 x 128 each, 2 stages, 128 KiB of LDS) or 256 x 128 tiles of 4 (128 x 64
+// each, 3 stages) for large ones.  With 3 or more stages the loads of the stage being
+// refilled are spread over the slices of a step between MFMAs; with 2 they follow the
+// barrier, interleaved with the last slice's MFMAs.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -163,6 +165,20 @@ __device__ __forceinline__ void issue_step(int8_t* stage, const int8_t* const* s
   }
 }
 
+// Loads [J0, J1) of issue_step (for spreading a step's loads over several slices).
+template <class C, int J0, int J1>
+__device__ __forceinline__ void issue_part(int8_t* stage, const int8_t* const* src,
+                                           const int* col, const int* dst, int step,
+                                           int64_t k) {
+  const int64_t k0 = static_cast<int64_t>(step) * C::BK;
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    const int64_t kk = k0 + col[j];
+    const int8_t* g = src[j] + (kk < k ? kk : 0);
+    __builtin_amdgcn_global_load_lds(g, stage + dst[j], 16, 0, 0);
+  }
+}
+
 // Read the fragments of 32-k slice `slice` of a step from an LDS stage.
 template <class C>
 __device__ __forceinline__ void read_slice(const int8_t* stage, int slice, int a_off,
@@ -228,28 +244,102 @@ __device__ __forceinline__ void step_inner(const int8_t* stage, int a_off, int b
   }
 }
 
+// With 3 or more stages the stage refilled during step t (step t + STAGES - 1, into the
+// stage freed by the previous barrier) is not needed for two more steps, so its loads are
+// spread over the slices of step t, a few between the MFMAs of each slice, instead of
+// queueing all at once behind the barrier.
+template <class C>
+struct Spread {
+  static constexpr int kParts = C::SLICES - 1;
+  static constexpr int kPer = (C::LOADS + kParts - 1) / kParts;
+  static constexpr int lo(int s) { return s * kPer < C::LOADS ? s * kPer : C::LOADS; }
+  static constexpr int hi(int s) { return lo(s + 1); }
+};
+
+template <class C, int S>
+__device__ __forceinline__ void spread_slice(const int8_t* stage, int8_t* fill,
+                                             const int8_t* const* src, const int* col,
+                                             const int* dst, int fill_step, int64_t k,
+                                             int a_off, int b_off, int fx, int lane,
+                                             v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
+                                             v16i (&acc)[C::TM][C::TN]) {
+  if constexpr (S + 1 < C::SLICES) {
+    using P = Spread<C>;
+    read_slice<C>(stage, S + 1, a_off, b_off, fx, lane, fa[(S + 1) % 2], fb[(S + 1) % 2]);
+    issue_part<C, P::lo(S), P::hi(S)>(fill, src, col, dst, fill_step, k);
+    mfma_slice<C>(fa[S % 2], fb[S % 2], acc);
+    constexpr int kLoads = P::hi(S) - P::lo(S);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, 2);           // DS reads
+    if constexpr (kLoads > 0) __builtin_amdgcn_sched_group_barrier(0x020, kLoads, 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - 1, 2);       // MFMAs
+    spread_slice<C, S + 1>(stage, fill, src, col, dst, fill_step, k, a_off, b_off, fx, lane,
+                           fa, fb, acc);
+  }
+}
+
+// Scheduling hint after the barrier of a step that refills a stage: one MFMA of the previous
+// step's last slice, the next slice's fragment reads, then the direct-to-LDS loads spread
+// between the remaining MFMAs.  Issued in one burst, the loads of all wavefronts queue in
+// the address unit (64 bytes per clock) and stall each wavefront for hundreds of cycles with
+// the matrix cores idle; spread out, the MFMAs cover that wait.
+template <class C, int ID>
+__device__ __forceinline__ void loads_under_mfmas() {
+  constexpr int kMfma = C::TM * C::TN;
+  // loads per remaining MFMA (all of them after the first MFMA when it is the only one)
+  constexpr int kPer = kMfma > 1 ? (C::LOADS + kMfma - 2) / (kMfma - 1) : C::LOADS;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);                // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, ID);    // DS reads
+  if constexpr (kMfma == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x020, kPer, ID);           // VMEM (LDS DMA) loads
+  } else {
+#pragma unroll
+    for (int i = 0; i + 1 < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, kPer, ID);         // VMEM (LDS DMA) loads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);            // MFMA
+    }
+  }
+}
+
 // One steady-state k step t of this k-group's ksteps steps (t + 1 < ksteps; global step
-// base + t).  ZERO: step t + 1 is the partial last step.
-template <class C, bool ZERO>
+// base + t).  ISSUE: a stage is refilled, with step t + STAGES - 1 spread over this step's
+// slices (3 or more stages) or with step t + STAGES right after this step's barrier (2
+// stages).  ZERO: step t + 1 is the partial last step.
+template <class C, bool ISSUE, bool ZERO>
 __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, const int* col,
                                        const int* dst, int a_off, int b_off, int fx, int lane,
                                        int base, int t, int ksteps, int64_t k, int tail_valid,
                                        v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
                                        v16i (&acc)[C::TM][C::TN]) {
-  step_inner<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
+  constexpr bool kSpread = C::STAGES >= 3;
+  if constexpr (ISSUE && kSpread) {
+    const int u = t + C::STAGES - 1;
+    spread_slice<C, 0>(lds + (t % C::STAGES) * C::STAGE_BYTES,
+                       lds + (u % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + u, k,
+                       a_off, b_off, fx, lane, fa, fb, acc);
+  } else {
+    step_inner<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
+  }
   int8_t* next = lds + ((t + 1) % C::STAGES) * C::STAGE_BYTES;
   // Keep this step's MFMAs in front of the LDS drain: they do not touch memory, so nothing
   // else stops the scheduler from sinking them below it and waiting on the fresh reads.
   __builtin_amdgcn_sched_barrier(0);
   wait_and_barrier<C::LOADS>(min(C::STAGES - 2, ksteps - 2 - t));
-  if (t + C::STAGES < ksteps)
-    issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + t + C::STAGES,
-                  k);
   if (ZERO && tail_valid != 0) zero_tail<C>(next, tail_valid);
   constexpr int last = (C::SLICES - 1) % 2;  // SLICES is even, so set 0 is free
-  read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
-  mfma_slice<C>(fa[last], fb[last], acc);
-  reads_under_mfmas<C, 1>();
+  if constexpr (ISSUE && !kSpread) {
+    // (the fragment reads come first in program order: the loads write LDS, so the compiler
+    // keeps reads that follow them in place)
+    read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+    issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + t + C::STAGES,
+                  k);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    loads_under_mfmas<C, 1>();
+  } else {
+    read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    reads_under_mfmas<C, 1>();
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT>
@@ -302,8 +392,11 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  // steps issued ahead of the first: all stages, but with 3 or more stages the last one is
+  // filled during step 0
+  constexpr int kAhead = STAGES >= 3 ? STAGES - 1 : STAGES;
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
+  for (int s = 0; s < kAhead; ++s)
     if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, base + s, k);
 
   const int frow = lane % 32;
@@ -313,16 +406,19 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   const int tail_valid = KS == 1 ? static_cast<int>((k % BK) / 16) : 0;  // 0: none
 
   v4i fa[2][TM], fb[2][TN];
-  wait_and_barrier<C::LOADS>(min(STAGES - 1, ksteps - 1));
+  wait_and_barrier<C::LOADS>(min(kAhead - 1, ksteps - 1));
   if (tail_valid != 0 && ksteps == 1) zero_tail<C>(lds, tail_valid);
   read_slice<C>(lds, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
   int t = 0;
+  for (; t + kAhead < ksteps; ++t)
+    k_step<C, true, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
+                           tail_valid, fa, fb, acc);
   for (; t + 2 < ksteps; ++t)
-    k_step<C, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
-                     tail_valid, fa, fb, acc);
+    k_step<C, false, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
+                            tail_valid, fa, fb, acc);
   if (t + 1 < ksteps) {
-    k_step<C, true>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
-                    tail_valid, fa, fb, acc);
+    k_step<C, false, true>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
+                           tail_valid, fa, fb, acc);
     ++t;
   }
   step_inner<C>(lds + (t % STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
@@ -432,39 +528,44 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Configuration by grid size (tiles of 64 x 64), from graph-timed MI355X measurements (us):
-//   shape (M x N x K)  64x64 3st 2grp  64x64 4st   128x64 3st   128x128 2st   (all 128-byte steps)
-//   128 x 4096 x 2560        10.5          11.8         15.5          20.3
-//   128 x 2560 x 9728        27.8          29.9         42.0          73.7
-//   128 x 19456 x 2560       33.9          27.8         30.1          28.7
-//   512 x 6144 x 2560        31.7          25.4         24.8          26.6
-//   512 x 19456 x 2560       99.6          71.7         61.3          62.1
-//   2048 x 6144 x 2560      117.7          80.5         66.9          62.4
-// and 256 x 256 tiles with 8 wavefronts of 64 x 128 (2 stages, 128 KiB of LDS, one workgroup
-// per CU) where there are at least 192 of them: 2048 x 6144 x 2560 59.5 (64.2 with
-// 128 x 128), 2048 x 19456 x 2560 165.9 (174.8), 4096 x 12288 x 4096 242.6 (287.1),
-// 16384 x 12288 x 4096 928 (1043); with fewer tiles too many CUs idle (2048 x 2560 x 9728:
-// 128.1 against 91.8).
-// 128-byte steps read whole 128-byte lines of each row (64-byte steps reach about half the
-// per-CU load rate).  Few tiles: 64 x 64 tiles and two k-groups per workgroup (when
-// 256-byte chunks divide k), so that more CUs stream; then 64 x 64 tiles with 4 stages,
-// 128 x 64 with 3, and 128 x 128 tiles with 2 stages (two workgroups per CU) on large grids.
+// Configuration by grid size, from graph-timed MI355X measurements (us; all configurations
+// with 128-byte k steps, 64-byte steps read half lines and reach about half the per-CU load
+// rate):
+//   shape (M x N x K)   64x64  64x64   128x64 128x128 128x128 256x128 256x256 | chosen
+//                       2 grp  4 st    2 grp  2 st    3 st 8w 3 st    2 st 8w |
+//   128 x 6144 x 2560    12.4   11.9    17.1   27.1    21.4    29.1    49.4   | 64x64 2 grp
+//   128 x 2560 x 9728    27.6   27.7    36.5   76.3    51.4    66.7   124.6   | 64x64 2 grp
+//   128 x 19456 x 2560   33.1   27.6    31.6   29.4    24.3    31.3    51.4   | 128x128 3 st
+//   512 x 2560 x 4096    21.6   17.0    15.1   28.8    19.8    36.2    59.5   | 128x64 2 grp
+//   512 x 2560 x 9728    50.8   43.6    34.4   74.0    48.8    68.0   128.3   | 128x64 2 grp
+//   512 x 6144 x 2560    31.6   25.6    28.8   28.1    20.3    30.0    52.4   | 128x128 3 st
+//   512 x 19456 x 2560   99.2   71.0    69.4   63.8    58.9    63.2    56.3   | 256x256
+//   2048 x 2560 x 9728  121.9  102.4    97.3   90.2    94.4    70.9   125.7   | 256x128
+//   2048 x 6144 x 2560  116.2   78.4    80.0   61.9    57.3    63.5    56.6   | 256x256
+//   2048 x 19456 x 2560 362.2  227.9   248.6  181.4   185.7   156.8   162.8   | 256x256
+// ("2 grp": two k-groups of 4 wavefronts each walking half of k; "8w": 8 wavefronts.)
+// Few tiles favour more workgroups in flight (split k inside the workgroup); many favour
+// larger tiles (fewer loaded bytes per MFMA) with enough tiles to fill 256 CUs.
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                      int64_t k, hipStream_t stream) {
   const int64_t tiles64 = ((m + 63) / 64) * ((n + 63) / 64);
-  if (tiles64 <= 256 && k % (2 * 128) == 0)
+  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const bool split2 = k % (2 * 128) == 0;  // two k-groups need whole steps each
+  if (tiles64 <= 256 && split2)
     return launch_cfg<64, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  if (tiles64 <= 768)
+  if (tiles64 <= 512 && split2)
+    return launch_cfg<128, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  if (tiles64 <= 512)
     return launch_cfg<64, 64, 128, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
   if (tiles64 <= 1024)
-    return launch_cfg<128, 64, 128, 3, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-  if (tiles256 >= 192)
+    return launch_cfg<128, 128, 128, 3, 1, YT, 2, 4>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
+                                                      stream);
+  if (tiles256 >= 150)
     return launch_cfg<256, 256, 128, 2, 1, YT, 4, 2>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
                                                       stream);
-  return launch_cfg<128, 128, 128, 2, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_cfg<256, 128, 128, 3, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace
