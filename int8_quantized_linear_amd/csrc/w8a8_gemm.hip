@@ -38,8 +38,8 @@
 // (k % 16 == 0, so chunks are whole) read the row start; once the last step has landed its
 // A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
-// Configurations (all with 128-byte k steps), by grid size: 64 x 64 or 128 x 64 tiles with
-// two k-groups of 4 wavefronts (in-workgroup split-K: each group walks half of k through its
+// Configurations (all with 128-byte k steps), by grid size: 64 x 32 tiles with four k-groups
+// of 2 wavefronts, 64 x 64 or 128 x 64 tiles with two k-groups of 4 wavefronts (in-workgroup split-K: each group walks half of k through its
 // own LDS stages and the partial int32 tiles are summed exactly through LDS) for the fewest
 // tiles, 128 x 128 tiles with 8 wavefronts of 64 x 32 for medium grids, 256 x 256 tiles of
 // 8 wavefronts (64 x 128 each, 2 stages, 128 KiB of LDS) or 256 x 128 tiles of 4 (128 x 64
@@ -544,6 +544,8 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 //   2048 x 6144 x 2560  116.2   78.4    80.0   61.9    57.3    63.5    56.6   | 256x256
 //   2048 x 19456 x 2560 362.2  227.9   248.6  181.4   185.7   156.8   162.8   | 256x256
 // ("2 grp": two k-groups of 4 wavefronts each walking half of k; "8w": 8 wavefronts.)
+// At most 128 such tiles: 64 x 32 tiles with four k-groups of 2 wavefronts (128 x 2560 x
+// 9728: 20.2; 128 x 2560 x 4096: 9.9 against 11.4 with 64 x 64 / 2 groups).
 // Few tiles favour more workgroups in flight (split k inside the workgroup); many favour
 // larger tiles (fewer loaded bytes per MFMA) with enough tiles to fill 256 CUs.
 template <int YT>
@@ -552,7 +554,11 @@ hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      int64_t k, hipStream_t stream) {
   const int64_t tiles64 = ((m + 63) / 64) * ((n + 63) / 64);
   const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-  const bool split2 = k % (2 * 128) == 0;  // two k-groups need whole steps each
+  const bool split2 = k % (2 * 128) == 0;  // k-groups need whole steps each
+  const bool split4 = k % (4 * 128) == 0;
+  if (tiles64 <= 128 && split4)
+    return launch_cfg<64, 32, 128, 3, 4, YT, 2, 1>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
+                                                    stream);
   if (tiles64 <= 256 && split2)
     return launch_cfg<64, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
   if (tiles64 <= 512 && split2)

@@ -159,13 +159,15 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
 
 
 # Shapes chosen to reach every tile configuration with ragged edges and partial last k steps:
-# 64 x 64 with two k-groups (4 x 256, 64 x 700), 128 x 64 with two k-groups (700 x 1500),
+# 64 x 32 with four k-groups (4 x 256, 64 x 700), 64 x 64 with two k-groups (600 x 1300),
+# 128 x 64 with two k-groups (700 x 1500),
 # 64 x 64 / 4 stages (k not a multiple of 256), 128 x 128 / 3 stages with 8 wavefronts
 # (1100 x 3000; 1, 2 and 3 k steps), 256 x 128 / 3 stages (2100 x 2600) and 256 x 256
 # (3000 x 4100).
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (4, 256, 512), (3, 130, 48), (130, 200, 272),
                                    (257, 385, 1040), (128, 128, 128), (64, 700, 4096),
-                                   (300, 33, 2576), (700, 1500, 512), (1100, 3000, 16),
+                                   (300, 33, 2576), (600, 1300, 768), (700, 1500, 512),
+                                   (1100, 3000, 16),
                                    (1100, 3000, 144), (1100, 3000, 272), (2100, 2600, 16),
                                    (2100, 2600, 1040), (3000, 4100, 272)])
 def test_w8a8_small(ref, dev, m, n, k):
