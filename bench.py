@@ -92,11 +92,26 @@ def grouped_bytes(distinct, n, k, x_rows, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------------------------------
 
-def graph_time(torch, body, iters, warmup=1):
+def gfx_clock_mhz():
+    """Mean current graphics clock over the GPU's XCDs as amd-smi reports it, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                           capture_output=True, text=True, timeout=60)
+        clk = json.loads(r.stdout)["gpu_data"][0]["clock"]
+        vals = [v["clk"]["value"] for name, v in clk.items() if name.startswith("gfx")]
+        return sum(vals) / len(vals) if vals else None
+    except Exception:  # tool missing or output format changed: report no reading
+        return None
+
+
+def graph_time(torch, body, iters, warmup=1, clock=None):
     """Seconds for body(0 .. iters-1), launched from one captured HIP graph and timed with
     two HIP events around its replay (no host launch overhead between kernels).  body(0) runs
     once eagerly first so that one-time setup never happens under capture, and the graph is
-    replayed `warmup` times untimed before the timed replay."""
+    replayed `warmup` times untimed before the timed replay.  With a `clock` dict, the graph
+    is then queued again for about two seconds (untimed) and the graphics clock is read while
+    it runs: clock["mhz"]."""
     body(0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -112,6 +127,12 @@ def graph_time(torch, body, iters, warmup=1):
     end.record()
     torch.cuda.synchronize()
     secs = start.elapsed_time(end) * 1e-3
+    if clock is not None:
+        for _ in range(max(1, int(2.0 / max(secs, 1e-6)))):
+            g.replay()
+        time.sleep(0.3)
+        clock["mhz"] = gfx_clock_mhz()
+        torch.cuda.synchronize()
     del g
     return secs
 
@@ -121,12 +142,12 @@ def per_call(torch, fn, reps, warmup=1):
     return graph_time(torch, fn, reps, warmup) / reps
 
 
-def time_loop(torch, body, steps, warmup):
+def time_loop(torch, body, steps, warmup, clock=None):
     """W eager warm-up steps, then exactly `steps` steps replayed from one HIP graph."""
     for i in range(warmup):
         body(i)
     torch.cuda.synchronize()
-    return graph_time(torch, lambda i: body(warmup + i), steps, 1)
+    return graph_time(torch, lambda i: body(warmup + i), steps, 1, clock)
 
 
 # ---------------------------------------------------------------------------------------
@@ -195,9 +216,12 @@ def section_step(torch, i8, wl, dev, args, result):
     ops = prefill_4b_work()
     log(f"[step] dense 4B W8A8 prefill, {st['copies']} weight copies; warmup {args.warmup}, "
         f"steps {args.steps}")
-    secs = time_loop(torch, lambda i: prefill_4b_step(i8, wl, st, i), args.steps, args.warmup)
+    clock = {}
+    secs = time_loop(torch, lambda i: prefill_4b_step(i8, wl, st, i), args.steps, args.warmup,
+                     clock)
     ms = secs / args.steps * 1e3
     result.update(value=ops / (secs / args.steps) / 1e12, ms_per_step=ms)
+    result["gfx_clock_mhz_during_step"] = clock.get("mhz")
     log(f"[step] {ms:.4f} ms/step, {result['value']:.1f} TOPS")
 
     # Roofline pass: every GEMM and quantizer launch of the step, each repeated `reps` times
@@ -266,7 +290,7 @@ def section_cpu_baseline(i8, wl, args, result):
     threads = len(os.sched_getaffinity(0))
     ref.set_threads(threads)
     g = wl.rng(0)
-    frac = 4
+    frac = 1  # the whole step (about 6 s on 16 threads)
     ws = {nm: wl.bits16(wl.to_bf16(wl.weight(g, n, k))) for nm, (n, k) in wl.DENSE_4B.items()}
     wq = {nm: ref.quantize_rows(w, "bf16") for nm, w in ws.items()}
     ins = {"q": 2560, "k": 2560, "v": 2560, "o": 4096, "gate": 2560, "up": 2560, "down": 9728}
@@ -290,13 +314,31 @@ def section_cpu_baseline(i8, wl, args, result):
             ref.w8a8(q, s, wq[nm][0], wq[nm][1])
             ops += w8a8_ops(q.shape[0], n, k)
     dt = time.perf_counter() - t0
+    # one thread: the tiny fp32 case and the 128-token q projection
+    single = {}
+    ref.set_threads(1)
+    t = wl.tiny_w8a8(0)
+    t0 = time.perf_counter()
+    qw, sw = ref.quantize_rows(t["w"], "f32")
+    qx, sx = ref.quantize_rows(t["x"], "f32")
+    ref.w8a8(qx, sx, qw, sw)
+    single["tiny 4x256x512 (quantize both + GEMM)"] = time.perf_counter() - t0
+    n, k = wl.DENSE_4B["q"]
+    xq = wl.bits16(wl.to_bf16(wl.activations(g, 128, k, 0.001)))
+    t0 = time.perf_counter()
+    q, s_ = ref.quantize_rows(xq, "bf16")
+    ref.w8a8(q, s_, wq["q"][0], wq["q"][1])
+    single["q 128x4096x2560 (quantize tokens + GEMM)"] = time.perf_counter() - t0
+    ref.set_threads(threads)
+    name = "the whole step" if frac == 1 else f"the step's first 1/{frac} of tokens at each M"
     result["cpu_baseline"] = {
         "value": ops / dt / 1e12, "unit": "TOPS", "cores": ref.threads(), "kind": "oracle",
-        "sample": f"the step's first 1/{frac} of tokens at each M ({rows_total} of "
-                  f"{sum(wl.PREFILL_4B_TOKENS)} token rows, all 7 projections): per-token "
-                  f"quantization + int32 GEMM + float64 epilogue; {dt:.1f} s",
-        "seconds": dt}
-    log(f"[cpu_baseline] {ops/dt/1e12*1e3:.2f} GOP/s on {ref.threads()} threads, {dt:.1f} s")
+        "sample": f"{name} ({rows_total} of {sum(wl.PREFILL_4B_TOKENS)} token rows, all 7 "
+                  f"projections): per-token quantization + int32 GEMM + float64 epilogue; "
+                  f"{dt:.1f} s",
+        "seconds": dt, "single_thread_seconds": single}
+    log(f"[cpu_baseline] {ops/dt/1e12*1e3:.2f} GOP/s on {ref.threads()} threads, {dt:.1f} s; "
+        f"1 thread: {single}")
 
 
 def section_decode(torch, i8, wl, dev, args, result):
@@ -344,6 +386,7 @@ def section_decode(torch, i8, wl, dev, args, result):
                            "frac_hbm_kernels": gbs_kernels / PEAK_HBM_GBS,
                            "per_proj": per}
         log(f"[decode] M={m}: {secs/args.steps*1e6:.1f} us/layer, kernels {gbs_kernels:.0f} GB/s")
+    out["traffic_m1"] = traffic_for("w8a16_kernel", "dense 8B decode layer M=1")
     m1 = out["per_m"][1]
     result["decode"] = {"workload": "dense 8B decoder projections, W8A16 decode, M in {1,4,8}; "
                                     "q/k/v and gate/up as fused GEMMs (N 6144 and 24576)",
@@ -456,6 +499,34 @@ def section_counters(torch, i8, wl, dev, args, result):
     result["counters"] = {"calibration_copy_bytes": CALIB_BYTES, "steps": 2}
 
 
+def section_counters_decode(torch, i8, wl, dev, args, result):
+    """Like `counters`, for the W8A16 decode layer: the calibration copy, then two passes of
+    the fused 8B decode projections at M = 1 with rotating weight copies, kernel by kernel."""
+    g = wl.rng(1)
+    pq, ps = {}, {}
+    for nm, (n, k) in wl.DENSE_8B.items():
+        pq[nm], ps[nm] = i8.quantize_per_channel_int8(wl.to_bf16(wl.weight(g, n, k)).to(dev))
+    q0 = {f: torch.cat([pq[p] for p in parts]).contiguous()
+          for f, parts in wl.DENSE_8B_FUSED.items()}
+    s0 = {f: torch.cat([ps[p] for p in parts]).contiguous()
+          for f, parts in wl.DENSE_8B_FUSED.items()}
+    del pq, ps
+    layer = sum(q.numel() for q in q0.values())
+    copies = max(2, -(-ROTATE_BYTES // layer))
+    qs = [q0] + [{nm: q.clone() for nm, q in q0.items()} for _ in range(copies - 1)]
+    xs = {k: wl.to_bf16(wl.activations(g, 1, k)).to(dev) for k in (4096, 12288)}
+    a = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for nm, q in qs[rep % copies].items():
+            i8.w8a16_gemm(xs[q.shape[1]], q, s0[nm])
+    torch.cuda.synchronize()
+    result["counters_decode"] = {"calibration_copy_bytes": CALIB_BYTES, "passes": 2}
+
+
 def section_weight_quant(torch, i8, wl, dev, args, result):
     g = wl.rng(4)
     ws = {nm: wl.to_bf16(wl.weight(g, n, k)).to(dev) for nm, (n, k) in wl.DENSE_8B.items()}
@@ -522,6 +593,8 @@ def main():
         section_weight_quant(torch, i8, wl, dev, args, result)
     if "counters" in sections:  # only for hardware-counter runs, not in the default list
         section_counters(torch, i8, wl, dev, args, result)
+    if "counters_decode" in sections:
+        section_counters_decode(torch, i8, wl, dev, args, result)
     print(json.dumps(result), flush=True)
 
 
