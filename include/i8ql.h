@@ -121,13 +121,43 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
  * y        device, [m, n] of y_dtype in {I8QL_BF16, I8QL_F32, I8QL_I32}.
  * m, n >= 0; 16 <= k <= 133144 and k % 16 == 0.
  * Errors: NULL (x_scale/w_scale may be NULL only with I32 output) -> I8QL_ERR_NULL;
- * negative m/n, k < 1, or more than 2^31 - 9 output tiles of 64 x 64 -> I8QL_ERR_SHAPE;
+ * negative m/n, k < 1, or more than 2^31 - 9 output tiles of 64 x 32 -> I8QL_ERR_SHAPE;
  * k % 16 or misaligned xq/wq -> I8QL_ERR_ALIGN; k > 133144 -> I8QL_ERR_K_TOO_LARGE; other
  * y_dtype -> I8QL_ERR_DTYPE; bias with I32 -> I8QL_ERR_ARG.
  */
 i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
                       int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * W8A8 tile configurations: introspection and explicit selection, for tuning and for tests
+ * that cover every configuration.
+ *
+ * w8a8_gemm launches one of I8QL_W8A8_NUM_CONFIGS tile configurations, chosen per call by
+ * a cost model of the launch time on MI355X (rounds of output tiles over the device's
+ * compute units, k steps per tile).  Every configuration computes bitwise the same outputs
+ * (exact int32 accumulation, the same float32 epilogue), so the choice affects only speed.
+ *
+ * w8a8_gemm_config_info(config, out3): writes {tile rows, tile columns, k-groups} of the
+ *   configuration to out3 (host, 3 int32).  A configuration with g > 1 k-groups splits k
+ *   inside the workgroup and accepts only k % (128 * g) == 0.
+ *   Errors: out3 NULL -> I8QL_ERR_NULL; config outside [0, I8QL_W8A8_NUM_CONFIGS) ->
+ *   I8QL_ERR_ARG.
+ * w8a8_gemm_choose_config(m, n, k, cus): the configuration w8a8_gemm launches for an
+ *   m x n x k product on a device with `cus` compute units (host arithmetic only, no HIP
+ *   call); -1 if the sizes are not a valid non-empty w8a8_gemm call or cus < 1.
+ * w8a8_gemm_with_config(config, ...): w8a8_gemm with the given configuration (config == -1:
+ *   the cost model's choice, exactly w8a8_gemm).  Arguments, results and errors as for
+ *   w8a8_gemm, plus: config outside [-1, I8QL_W8A8_NUM_CONFIGS), or a configuration with
+ *   g > 1 k-groups and k % (128 * g) != 0 -> I8QL_ERR_ARG.
+ */
+#define I8QL_W8A8_NUM_CONFIGS 12
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out3);
+int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus);
+i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
+                                  const int8_t* wq, const float* w_scale, const float* bias,
+                                  void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                  void* stream);
 
 /*
  * w8a16_gemm — weight-only int8 GEMM for decode: int8 weights are dequantized in registers

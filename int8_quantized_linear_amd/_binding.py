@@ -20,7 +20,9 @@ I8QL_F32, I8QL_BF16, I8QL_F16, I8QL_I8, I8QL_I32 = 0, 1, 2, 3, 4
 _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8QL_F16,
           torch.int8: I8QL_I8, torch.int32: I8QL_I32}
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
-           "grouped_w8a16_gemm", "i8ql_status_string", "i8ql_last_hip_error")
+           "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
+           "w8a8_gemm_with_config", "i8ql_status_string", "i8ql_last_hip_error")
+W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 
 
 class I8qlError(RuntimeError):
@@ -49,6 +51,12 @@ def load_library(path: str = LIB_PATH):
             getattr(lib, fn).restype = I
         lib.w8a8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a8_gemm.restype = I
+        lib.w8a8_gemm_with_config.argtypes = [I, P, P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a8_gemm_with_config.restype = I
+        lib.w8a8_gemm_config_info.argtypes = [I, P]
+        lib.w8a8_gemm_config_info.restype = I
+        lib.w8a8_gemm_choose_config.argtypes = [I64, I64, I64, I]
+        lib.w8a8_gemm_choose_config.restype = I
         lib.w8a16_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a16_gemm.restype = I
         lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
@@ -129,6 +137,12 @@ def _out(out, shape, dtype, dev):
 def w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):
     """``y = (xq @ wq.T) * x_scale[:, None] * w_scale[None, :] (+ bias)``; int32 when
     ``out_dtype`` is torch.int32 (then scales may be None and bias must be None)."""
+    return w8a8_gemm_with_config(-1, xq, x_scale, wq, w_scale, bias, out_dtype, out)
+
+
+def w8a8_gemm_with_config(config, xq, x_scale, wq, w_scale, bias=None,
+                          out_dtype=torch.bfloat16, out=None):
+    """``w8a8_gemm`` with tile configuration ``config`` (-1: the cost model's choice)."""
     _check(xq, "xq", (torch.int8,), 2)
     dev = xq.device
     _check(wq, "wq", (torch.int8,), 2, dev)
@@ -143,9 +157,25 @@ def w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out
                 raise ValueError(f"{nm} must have {ln} entries")
     y = _out(out, (m, n), out_dtype, dev)
     with torch.cuda.device(dev):
-        _call("w8a8_gemm", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
-              _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
+        _call("w8a8_gemm_with_config", int(config), _ptr(xq), _ptr(x_scale), _ptr(wq),
+              _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
     return y
+
+
+def w8a8_gemm_config_info(config: int):
+    """(tile rows, tile columns, k-groups) of W8A8 tile configuration ``config``."""
+    lib = load_library()
+    out = (ctypes.c_int32 * 3)()
+    st = lib.w8a8_gemm_config_info(int(config), ctypes.cast(out, ctypes.c_void_p))
+    if st != 0:
+        raise I8qlError("w8a8_gemm_config_info", st, lib)
+    return tuple(out)
+
+
+def w8a8_gemm_choose_config(m: int, n: int, k: int, cus: int = 256) -> int:
+    """The configuration ``w8a8_gemm`` launches for an m x n x k product on ``cus`` compute
+    units (-1 for sizes ``w8a8_gemm`` rejects); host arithmetic only."""
+    return load_library().w8a8_gemm_choose_config(m, n, k, cus)
 
 
 def w8a16_gemm(x, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):

@@ -67,15 +67,22 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
   return quantize_rows(x, x_dtype, m, k, q_out, scale_out, stream);
 }
 
-i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                      const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
-                      int64_t m, int64_t n, int64_t k, void* stream) {
+i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
+                                  const int8_t* wq, const float* w_scale, const float* bias,
+                                  void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                  void* stream) {
   if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32 && y_dtype != I8QL_I32) return I8QL_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
   if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
-  // one workgroup per output tile (64 x 64 at the smallest), in a one-dimensional grid
-  const int64_t tm = (m + 63) / 64, tn = (n + 63) / 64;
+  // one workgroup per output tile (64 x 32 at the smallest), in a one-dimensional grid
+  const int64_t tm = (m + 63) / 64, tn = (n + 31) / 32;
   if (!mul_ok(tm, tn) || tm * tn > kMaxGridX - 8) return I8QL_ERR_SHAPE;
+  if (config < -1 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
+  if (config >= 0) {
+    int32_t geo[3];
+    i8ql::w8a8_config_geometry(config, geo);
+    if (k % (128 * static_cast<int64_t>(geo[2])) != 0 && geo[2] > 1) return I8QL_ERR_ARG;
+  }
   if (m == 0 || n == 0) return I8QL_OK;
   if (!xq || !wq || !y) return I8QL_ERR_NULL;
   if (y_dtype != I8QL_I32 && (!x_scale || !w_scale)) return I8QL_ERR_NULL;
@@ -86,7 +93,28 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
     return I8QL_ERR_ALIGN;
   if (k > I8QL_W8A8_MAX_K) return I8QL_ERR_K_TOO_LARGE;
   return hip_status(i8ql::launch_w8a8_gemm(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
-                                           static_cast<hipStream_t>(stream)));
+                                           config, static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
+                      int64_t m, int64_t n, int64_t k, void* stream) {
+  return w8a8_gemm_with_config(-1, xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k, stream);
+}
+
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out3) {
+  if (!out3) return I8QL_ERR_NULL;
+  if (config < 0 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
+  i8ql::w8a8_config_geometry(config, out3);
+  return I8QL_OK;
+}
+
+int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus) {
+  if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || k > I8QL_W8A8_MAX_K || cus < 1) return -1;
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return -1;
+  const int64_t tm = (m + 63) / 64, tn = (n + 31) / 32;
+  if (!mul_ok(tm, tn) || tm * tn > kMaxGridX - 8) return -1;
+  return i8ql::w8a8_choose_config(m, n, k, cus);
 }
 
 i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, const float* bias,

@@ -15,10 +15,17 @@ namespace i8ql {
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream);
 
+// W8A8: `config` is one of the I8QL_W8A8_NUM_CONFIGS tile configurations, or -1 for the
+// one the cost model chooses for this shape on the current device.
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                             const float* w_scale, const float* bias, void* y,
-                            i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                            i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k, int config,
                             hipStream_t stream);
+
+// The cost model's configuration for an m x n x k product on `cus` compute units (host
+// only), and the {tile rows, tile columns, k-groups} of a configuration.
+int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus);
+void w8a8_config_geometry(int config, int32_t* out3);
 
 hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,

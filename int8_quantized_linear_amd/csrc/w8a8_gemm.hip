@@ -64,6 +64,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
+constexpr int64_t kMaxGrid = 2147483647;  // workgroups per launch (x dimension)
 constexpr int kGroupM = 8;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -528,62 +529,138 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Configuration by grid size, from graph-timed MI355X measurements (us; all configurations
-// with 128-byte k steps, 64-byte steps read half lines and reach about half the per-CU load
-// rate):
-//   shape (M x N x K)   64x64  64x64   128x64 128x128 128x128 256x128 256x256 | chosen
-//                       2 grp  4 st    2 grp  2 st    3 st 8w 3 st    2 st 8w |
-//   128 x 6144 x 2560    12.4   11.9    17.1   27.1    21.4    29.1    49.4   | 64x64 2 grp
-//   128 x 2560 x 9728    27.6   27.7    36.5   76.3    51.4    66.7   124.6   | 64x64 2 grp
-//   128 x 19456 x 2560   33.1   27.6    31.6   29.4    24.3    31.3    51.4   | 128x128 3 st
-//   512 x 2560 x 4096    21.6   17.0    15.1   28.8    19.8    36.2    59.5   | 128x64 2 grp
-//   512 x 2560 x 9728    50.8   43.6    34.4   74.0    48.8    68.0   128.3   | 128x64 2 grp
-//   512 x 6144 x 2560    31.6   25.6    28.8   28.1    20.3    30.0    52.4   | 128x128 3 st
-//   512 x 19456 x 2560   99.2   71.0    69.4   63.8    58.9    63.2    56.3   | 256x256
-//   2048 x 2560 x 9728  121.9  102.4    97.3   90.2    94.4    70.9   125.7   | 256x128
-//   2048 x 6144 x 2560  116.2   78.4    80.0   61.9    57.3    63.5    56.6   | 256x256
-//   2048 x 19456 x 2560 362.2  227.9   248.6  181.4   185.7   156.8   162.8   | 256x256
-// ("2 grp": two k-groups of 4 wavefronts each walking half of k; "8w": 8 wavefronts.)
-// At most 128 such tiles: 64 x 32 tiles with four k-groups of 2 wavefronts (128 x 2560 x
-// 9728: 20.2; 128 x 2560 x 4096: 9.9 against 11.4 with 64 x 64 / 2 groups).
-// Few tiles favour more workgroups in flight (split k inside the workgroup); many favour
-// larger tiles (fewer loaded bytes per MFMA) with enough tiles to fill 256 CUs.
+// Tile configuration by a cost model.  Every configuration computes the same products; they
+// differ in how well one shape fills the 256 CUs and in how many loaded bytes each MFMA
+// costs.  Large tiles load fewer bytes per MFMA, but a shape whose tile count is just above a
+// multiple of the CU count leaves most CUs idle in its last round, so tile shapes that are not
+// powers of two (192, 160 and 320 wide) are candidates too, as are small tiles whose k is split
+// between k-groups inside the workgroup (few tiles, long k).  A launch's time is modelled as
+//   t = t_step * R * S + t_round * R + t0,   R = ceil(tiles / CUs), S = k steps per k-group,
+// one workgroup per CU and round; the coefficients (us) are a least-squares fit (relative
+// error) to graph-timed MI355X measurements of every candidate on 44 shapes (M 16..16384,
+// N 1024..28672, K 1024..18944, bf16 output).  On those shapes the chosen configurations
+// take 0.4% longer in total than the per-shape best (each shape predicted from a fit that
+// left it out), and 5.5% less time than a fixed rule by tile count; examples (us, chosen
+// against the former 256x256 / 256x128 choice): 2048x19456x2560 139 vs 165 (256x320),
+// 2048x6144x2560 49 vs 55 (256x192), 2048x2560x4096 32 vs 41 and 2048x2560x9728 62 vs 76
+// (128x160), 16384x12288x4096 822 vs 939 (320x256).
+struct Candidate {
+  int bm, bn, ks;                // tile and k-groups
+  double t_step, t_round, t0;    // cost model (us)
+};
+constexpr Candidate kCandidates[] = {
+    {256, 256, 1, 1.4331, 33.257, -12.695},  // 0: 2 stages, 8 wavefronts 64x128
+    {256, 320, 1, 2.1818, 26.906, -14.422},  // 1: 2 stages, 8 wavefronts 64x160
+    {256, 192, 1, 1.2271, 22.170, -6.538},   // 2: 2 stages, 8 wavefronts 64x96
+    {128, 320, 1, 1.2967, 17.301, -4.637},   // 3: 2 stages, 8 wavefronts 32x160
+    {128, 160, 1, 0.6088, 10.434, -1.136},   // 4: 3 stages, 4 wavefronts 32x160
+    {256, 128, 1, 0.7876, 18.964, -9.088},   // 5: 3 stages, 8 wavefronts 64x64
+    {128, 128, 1, 0.5396, 7.867, -1.050},    // 6: 3 stages, 8 wavefronts 64x32
+    {128, 64, 2, 0.7266, 6.048, -0.105},     // 7: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 64, 2, 0.5120, 3.413, 2.510},       // 8: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 32, 4, 0.6634, 3.775, 2.426},       // 9: 3 stages, 4 k-groups of 2 wavefronts
+    {64, 64, 1, 0.2248, 1.206, 6.164},       // 10: 4 stages, 4 wavefronts
+    {320, 256, 1, 1.5890, 30.289, -14.814},  // 11: 2 stages, 8 wavefronts 160x64
+};
+constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
+
+template <int YT>
+hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, const float* bias, void* y, int64_t m,
+                            int64_t n, int64_t k, hipStream_t stream) {
+#define I8QL_W8A8_CFG(...) \
+  launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
+  switch (c) {
+    case 0: return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2);
+    case 1: return I8QL_W8A8_CFG(256, 320, 128, 2, 1, YT, 4, 2);
+    case 2: return I8QL_W8A8_CFG(256, 192, 128, 2, 1, YT, 4, 2);
+    case 3: return I8QL_W8A8_CFG(128, 320, 128, 2, 1, YT, 4, 2);
+    case 4: return I8QL_W8A8_CFG(128, 160, 128, 3, 1, YT, 4, 1);
+    case 5: return I8QL_W8A8_CFG(256, 128, 128, 3, 1, YT, 4, 2);
+    case 6: return I8QL_W8A8_CFG(128, 128, 128, 3, 1, YT, 2, 4);
+    case 7: return I8QL_W8A8_CFG(128, 64, 128, 3, 2, YT, 2, 2);
+    case 8: return I8QL_W8A8_CFG(64, 64, 128, 3, 2, YT, 2, 2);
+    case 9: return I8QL_W8A8_CFG(64, 32, 128, 3, 4, YT, 2, 1);
+    case 10: return I8QL_W8A8_CFG(64, 64, 128, 4, 1, YT, 2, 2);
+    default: return I8QL_W8A8_CFG(320, 256, 128, 2, 1, YT, 2, 4);
+  }
+#undef I8QL_W8A8_CFG
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;  // idempotent; a race only repeats the query
+  }
+  return cached[dev];
+}
+
+// Index of the candidate with the lowest modelled time for an m x n x k product.  k-groups
+// need whole k steps each (k a multiple of 128 times the group count); a candidate whose grid
+// would exceed the launch limit is skipped (the 320 x 256 tile, with the fewest tiles, always
+// fits when the caller's limit check on 64 x 64 tiles has passed).
+int choose_candidate(int64_t m, int64_t n, int64_t k, int cus) {
+  int best = kNumCandidates - 1;
+  double best_t = 0.0;
+  bool found = false;
+  const int64_t ksteps = (k + 127) / 128;
+  for (int c = 0; c < kNumCandidates; ++c) {
+    const Candidate& d = kCandidates[c];
+    if (d.ks > 1 && k % (128 * d.ks) != 0) continue;
+    const int64_t tiles = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
+    if (tiles > kMaxGrid - kXcds) continue;
+    const double rounds = static_cast<double>((tiles + cus - 1) / cus);
+    const double steps = static_cast<double>(ksteps / d.ks);
+    const double t = d.t_step * rounds * steps + d.t_round * rounds + d.t0;
+    if (!found || t < best_t) {
+      best = c;
+      best_t = t;
+      found = true;
+    }
+  }
+  return best;
+}
+
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
-                     int64_t k, hipStream_t stream) {
-  const int64_t tiles64 = ((m + 63) / 64) * ((n + 63) / 64);
-  const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-  const bool split2 = k % (2 * 128) == 0;  // k-groups need whole steps each
-  const bool split4 = k % (4 * 128) == 0;
-  if (tiles64 <= 128 && split4)
-    return launch_cfg<64, 32, 128, 3, 4, YT, 2, 1>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
-                                                    stream);
-  if (tiles64 <= 256 && split2)
-    return launch_cfg<64, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  if (tiles64 <= 512 && split2)
-    return launch_cfg<128, 64, 128, 3, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  if (tiles64 <= 512)
-    return launch_cfg<64, 64, 128, 4, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-  if (tiles64 <= 1024)
-    return launch_cfg<128, 128, 128, 3, 1, YT, 2, 4>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
-                                                      stream);
-  if (tiles256 >= 150)
-    return launch_cfg<256, 256, 128, 2, 1, YT, 4, 2>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
-                                                      stream);
-  return launch_cfg<256, 128, 128, 3, 1, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+                     int64_t k, int config, hipStream_t stream) {
+  const int c = config >= 0 ? config : choose_candidate(m, n, k, device_cus());
+  return launch_candidate<YT>(c, xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace
 
+static_assert(kNumCandidates == I8QL_W8A8_NUM_CONFIGS, "configuration count of the C ABI");
+
+int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus) {
+  return choose_candidate(m, n, k, cus);
+}
+
+void w8a8_config_geometry(int config, int32_t* out3) {
+  out3[0] = kCandidates[config].bm;
+  out3[1] = kCandidates[config].bn;
+  out3[2] = kCandidates[config].ks;
+}
+
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                             const float* w_scale, const float* bias, void* y,
-                            i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                            i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k, int config,
                             hipStream_t stream) {
   switch (y_dtype) {
-    case I8QL_I32: return launch_yt<I8QL_I32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-    case I8QL_F32: return launch_yt<I8QL_F32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-    default: return launch_yt<I8QL_BF16>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+    case I8QL_I32:
+      return launch_yt<I8QL_I32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
+    case I8QL_F32:
+      return launch_yt<I8QL_F32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
+    default:
+      return launch_yt<I8QL_BF16>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
   }
 }
 

@@ -81,7 +81,7 @@ def test_w8a8_validation(lib):
     assert call(args(m=-1)) == SHAPE
     assert call(args(n=-2)) == SHAPE
     assert call(args(k=0)) == SHAPE
-    assert call(args(m=1 << 30, n=1 << 30, k=16)) == SHAPE  # 2^48 output tiles
+    assert call(args(m=1 << 30, n=1 << 30, k=16)) == SHAPE  # 2^49 output tiles of 64 x 32
     assert call(args(m=0, xq=NUL, y=NUL)) == OK
     assert call(args(n=0)) == OK
     assert call(args(xq=NUL)) == NULL
@@ -98,6 +98,59 @@ def test_w8a8_validation(lib):
     assert call(args(y=A2, yt=F32)) == ALIGN
     assert call(args(b=A2, yt=F32)) == ALIGN
     assert call(args(k=133152)) == KBIG
+
+
+def test_w8a8_with_config_validation(lib):
+    f = lib.w8a8_gemm_with_config
+    call = lambda c, m=4, n=8, k=64, xq=A16, y=A16: f(c, xq, A16, A16, A16, NUL, y, BF16, m, n,
+                                                      k, NUL)
+    assert call(12) == ARG
+    assert call(-2) == ARG
+    assert call(12, m=0) == ARG             # checked before the zero-size no-op
+    assert call(-1, m=0, xq=NUL, y=NUL) == OK
+    assert call(0, xq=NUL) == NULL
+    assert call(0, k=72) == ALIGN
+    for c in range(12):
+        geo = (ctypes.c_int32 * 3)()
+        assert lib.w8a8_gemm_config_info(c, ctypes.cast(geo, ctypes.c_void_p)) == OK
+        if geo[2] > 1:                      # k-groups need k % (128 * groups) == 0
+            assert call(c, k=64) == ARG
+            assert call(c, k=128 * geo[2] + 16) == ARG
+            assert call(c, m=0, k=64) == ARG
+    assert lib.w8a8_gemm_config_info(12, ctypes.cast((ctypes.c_int32 * 3)(), ctypes.c_void_p)) == ARG
+    assert lib.w8a8_gemm_config_info(0, NUL) == NULL
+
+
+def test_w8a8_config_table_and_choices():
+    import int8_quantized_linear_amd as i8
+    geos = [i8.w8a8_gemm_config_info(c) for c in range(i8.W8A8_NUM_CONFIGS)]
+    assert len(set(geos)) == len(geos)
+    assert "#define I8QL_W8A8_NUM_CONFIGS %d" % i8.W8A8_NUM_CONFIGS in open(HEADER).read()
+    # invalid sizes
+    for m, n, k, cus in [(0, 8, 64, 256), (4, 0, 64, 256), (4, 8, 8, 256), (4, 8, 72, 256),
+                         (4, 8, 133152, 256), (4, 8, 64, 0), (1 << 30, 1 << 30, 16, 256)]:
+        assert i8.w8a8_gemm_choose_config(m, n, k, cus) == -1
+    # every choice is a valid configuration; k-groups only where k splits into whole steps
+    for m in (1, 16, 128, 512, 777, 2048, 4096, 16384):
+        for n in (32, 1000, 2560, 6144, 19456):
+            for k in (16, 272, 2560, 4096, 9728):
+                c = i8.w8a8_gemm_choose_config(m, n, k, 256)
+                bm, bn, g = geos[c]
+                assert g == 1 or k % (128 * g) == 0
+    # the benchmark step's fused 4B projections at 2048 tokens take the 256x320, 256x192 and
+    # 128x160 tiles that fill the 256 CUs in whole rounds
+    pick = lambda m, n, k, cus=256: geos[i8.w8a8_gemm_choose_config(m, n, k, cus)]
+    assert pick(2048, 19456, 2560) == (256, 320, 1)
+    assert pick(2048, 6144, 2560) == (256, 192, 1)
+    assert pick(2048, 2560, 4096) == (128, 160, 1)
+    assert pick(2048, 2560, 9728) == (128, 160, 1)
+    assert pick(16384, 12288, 4096) == (320, 256, 1)
+    # few tiles and a long k: k split over k-groups inside the workgroup
+    assert pick(128, 2560, 9728)[2] == 4
+    assert pick(512, 2560, 9728)[2] == 2
+    # fewer compute units: the same shape needs more rounds, and the choice may change
+    assert all(0 <= i8.w8a8_gemm_choose_config(2048, 19456, 2560, cus) < i8.W8A8_NUM_CONFIGS
+               for cus in (1, 32, 80, 304))
 
 
 def test_w8a8_int32_limit_is_exactly_the_header_constant():

@@ -137,7 +137,7 @@ def w8a8_case(g, m, n, k, wdtype="bf16"):
 
 
 def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bfloat16),
-             seed=0, with_bias=(False, True)):
+             seed=0, with_bias=(False, True), config=-1):
     g = wl.rng(seed)
     (wt, wv), (xt, xv) = w8a8_case(g, m, n, k)
     qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
@@ -150,20 +150,16 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
             if od == torch.int32:
                 if use_bias:
                     continue
-                y = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+                y = i8.w8a8_gemm_with_config(config, qx, None, qw, None, out_dtype=torch.int32)
                 np.testing.assert_array_equal(y.cpu().numpy(), acc)
                 continue
             b = torch.from_numpy(b_np).to(dev) if use_bias else None
-            y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=od)
+            y = i8.w8a8_gemm_with_config(config, qx, sx, qw, sw, b, out_dtype=od)
             check_float(y, yref, w8a8_tol(acc, sxr, swr, b_np), f"w8a8 {m}x{n}x{k} {od}")
 
 
-# Shapes chosen to reach every tile configuration with ragged edges and partial last k steps:
-# 64 x 32 with four k-groups (4 x 256, 64 x 700), 64 x 64 with two k-groups (600 x 1300),
-# 128 x 64 with two k-groups (700 x 1500),
-# 64 x 64 / 4 stages (k not a multiple of 256), 128 x 128 / 3 stages with 8 wavefronts
-# (1100 x 3000; 1, 2 and 3 k steps), 256 x 128 / 3 stages (2100 x 2600) and 256 x 256
-# (3000 x 4100).
+# Shapes through the cost model's choice of tile configuration (ragged edges, partial last
+# k steps, one to three k steps); every configuration is also run explicitly below.
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (4, 256, 512), (3, 130, 48), (130, 200, 272),
                                    (257, 385, 1040), (128, 128, 128), (64, 700, 4096),
                                    (300, 33, 2576), (600, 1300, 768), (700, 1500, 512),
@@ -172,6 +168,43 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
                                    (2100, 2600, 1040), (3000, 4100, 272)])
 def test_w8a8_small(ref, dev, m, n, k):
     run_w8a8(ref, dev, m, n, k, seed=m * 7 + n)
+
+
+@pytest.mark.parametrize("config", range(i8.W8A8_NUM_CONFIGS))
+def test_w8a8_every_tile_config(ref, dev, config):
+    """Each tile configuration, forced: two tiles and a ragged third in each direction with
+    four k steps (the last partial) and with one partial step; then more than one group of
+    eight tile rows of the workgroup-to-tile map.  k-group configurations take k in whole
+    steps per group."""
+    bm, bn, groups = i8.w8a8_gemm_config_info(config)
+    if groups == 1:
+        shapes = [(2 * bm + 37, 2 * bn + 19, 432), (2 * bm + 37, 2 * bn + 19, 16),
+                  (9 * bm + 5, 3 * bn + 7, 144)]
+    else:
+        shapes = [(2 * bm + 37, 2 * bn + 19, 256 * groups), (9 * bm + 5, 3 * bn + 7, 128 * groups)]
+    for (m, n, k) in shapes:
+        print(f"w8a8 config {config} ({bm}x{bn}, {groups} k-groups): {m}x{n}x{k}", flush=True)
+        run_w8a8(ref, dev, m, n, k, seed=config * 31 + m, config=config)
+
+
+def test_w8a8_configs_agree_bitwise(dev):
+    """All configurations give bitwise the same int32, float32 and bf16 outputs (exact int32
+    accumulation, one epilogue), on a shape every configuration accepts."""
+    g = wl.rng(11)
+    m, n, k = 1000, 1500, 1024
+    qx = torch.from_numpy(g.integers(-127, 128, (m, k), dtype=np.int8)).to(dev)
+    qw = torch.from_numpy(g.integers(-127, 128, (n, k), dtype=np.int8)).to(dev)
+    sx = torch.rand(m, device=dev) * 0.01
+    sw = torch.rand(n, device=dev) * 0.01
+    b = torch.randn(n, device=dev) * 0.02
+    want = {od: i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=od)
+            for od in (torch.float32, torch.bfloat16)}
+    want_i = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+    for c in range(i8.W8A8_NUM_CONFIGS):
+        for od, y in want.items():
+            assert torch.equal(i8.w8a8_gemm_with_config(c, qx, sx, qw, sw, b, out_dtype=od), y), c
+        assert torch.equal(i8.w8a8_gemm_with_config(c, qx, None, qw, None,
+                                                    out_dtype=torch.int32), want_i), c
 
 
 def test_w8a8_tiny_workload_end_to_end(ref, dev):
