@@ -12,9 +12,9 @@
 //               or acc itself for int32 output.
 //
 // Data movement.  Both operands are K-contiguous (the nn.Linear [out, in] layout and
-// row-major tokens).  A workgroup of 4 wavefronts owns a BM x BN output tile and walks k in
-// steps of BK bytes.  Each step's A and B slices are copied global -> LDS by the gfx950
-// direct-to-LDS loads (global_load_lds_dwordx4: 16 bytes per lane, one wavefront
+// row-major tokens).  A workgroup of 4 or 8 wavefronts (per k-group) owns a BM x BN output
+// tile and walks k in steps of BK bytes.  Each step's A and B slices are copied global -> LDS
+// by the gfx950 direct-to-LDS loads (global_load_lds_dwordx4: 16 bytes per lane, one wavefront
 // instruction fills 1 KiB = 1024 / BK rows), so no VGPRs hold staged data and up to STAGES
 // steps are in flight.  Each step waits (s_waitcnt vmcnt) for its own loads, passes one
 // barrier, which also retires the reads of the stage about to be refilled, and refills that
@@ -25,7 +25,7 @@
 // of bank conflicts; the swizzle is applied on the global side (each lane fetches the
 // logical chunk that belongs in its fixed LDS slot).
 //
-// MFMA.  Each wavefront owns a (BM / 2) x (BN / 2) sub-tile of 32 x 32 blocks of
+// MFMA.  Each wavefront owns a (BM / WM) x (BN / WN) sub-tile of 32 x 32 blocks of
 // v_mfma_i32_32x32x32_i8.  Fragment layout: lane l supplies row l % 32 of a 32-row block and
 // 16 consecutive k of a 32-k slice at offset 16 * (l / 32); A and B use the same k
 // assignment, which is all the sum needs.  Accumulator: lane l, register r holds row
@@ -38,14 +38,19 @@
 // (k % 16 == 0, so chunks are whole) read the row start; once the last step has landed its
 // A chunks past k are overwritten with zeros in LDS, so they add nothing.
 //
-// Configurations (all with 128-byte k steps), by grid size: 64 x 32 tiles with four k-groups
-// of 2 wavefronts, 64 x 64 or 128 x 64 tiles with two k-groups of 4 wavefronts (in-workgroup split-K: each group walks half of k through its
-// own LDS stages and the partial int32 tiles are summed exactly through LDS) for the fewest
-// tiles, 128 x 128 tiles with 8 wavefronts of 64 x 32 for medium grids, 256 x 256 tiles of
-// 8 wavefronts (64 x 128 each, 2 stages, 128 KiB of LDS) or 256 x 128 tiles of 4 (128 x 64
-// each, 3 stages) for large ones.  With 3 or more stages the loads of the stage being
-// refilled are spread over the slices of a step between MFMAs; with 2 they follow the
-// barrier, interleaved with the last slice's MFMAs.
+// Configurations (all with 128-byte k steps; see kCandidates): tiles from 64 x 32 to
+// 320 x 256, including widths that are not powers of two (160, 192, 320) so that more
+// shapes fill the 256 CUs in whole rounds, and, for the fewest tiles, 64 x 32 / 64 x 64 /
+// 128 x 64 tiles with 4 or 2 k-groups (in-workgroup split-K: each group walks its share of k
+// through its own LDS stages and the partial int32 tiles are summed exactly through LDS).
+// The launch picks one per shape by a fitted launch-time model.  With 3 or more stages the
+// loads of the stage being refilled are spread over the slices of a step between MFMAs;
+// with 2 they follow the barrier, interleaved with the last slice's MFMAs.
+//
+// Epilogue.  Scales (and bias) are applied in registers; the values then pass through a
+// per-wavefront LDS area so that the output is written with 16-byte row-contiguous stores
+// (see epilogue_lds).  Stored straight from registers (2 or 4 bytes per lane) the epilogue
+// took 10-29% of the kernel time on MI355X; 2048x19456x2560 went from 139 to 107 us.
 //
 // Tile order.  Consecutive workgroup ids are spread round-robin over the 8 XCDs, each with
 // its own L2.  The linear id is remapped so that every XCD receives a contiguous range of
@@ -343,6 +348,98 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
   }
 }
 
+// Epilogue through LDS.  A wavefront's accumulators hold one column per lane (32x32 MFMA
+// layout: lane l, register r -> row 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32), so
+// stored straight from registers every instruction writes 2 or 4 bytes per lane.  Instead,
+// each wavefront converts one 32-row block and up to two 32-column blocks of output values at
+// a time into a private LDS area (32-bit words, rows padded to 72 words so that the two half
+// wavefronts, 4 rows apart, write disjoint banks), then reads them back row-contiguous and
+// writes 16 bytes per lane (8 bf16 or 4 float32 / int32 values), eight or four lanes per
+// 128-byte row segment.  Needs rows of the output that are whole 16-byte chunks
+// (n * element size % 16 == 0) and a 16-byte aligned output.
+constexpr int kScrWords = 72;                   // words per scratch row (64 + padding)
+constexpr int kScrBytes = 32 * kScrWords * 4;   // scratch per wavefront
+
+template <class C, int YT>
+__device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], int* scr,
+                                             int lane, const float* __restrict__ x_scale,
+                                             const float* __restrict__ w_scale,
+                                             const float* __restrict__ bias, void* y,
+                                             int64_t m, int64_t n, int64_t r0, int64_t c0) {
+  constexpr int TM = C::TM, TN = C::TN;
+  constexpr int ES = YT == I8QL_BF16 ? 2 : 4;  // output element bytes
+  constexpr int PER = 16 / ES;                  // output elements per 16-byte store
+  float sw[TN], bj[TN];
+  if constexpr (YT != I8QL_I32) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t c = c0 + j * 32 + lane % 32;
+      sw[j] = w_scale[c < n ? c : n - 1];
+      bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float sx[16];
+    if constexpr (YT != I8QL_I32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = r0 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+        sx[r] = x_scale[row < m ? row : m - 1];
+      }
+    }
+#pragma unroll
+    for (int jc = 0; jc < TN; jc += 2) {
+      const int nb = TN - jc < 2 ? TN - jc : 2;  // 32-column blocks in this piece
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        if (jj >= nb) break;
+        const int j = jc + jj;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+          int bits;
+          if constexpr (YT == I8QL_I32) {
+            bits = acc[i][j][r];
+          } else {
+            float v = __fmul_rn(__fmul_rn(static_cast<float>(acc[i][j][r]), sx[r]), sw[j]);
+            if (bias) v = __fadd_rn(v, bj[j]);
+            bits = __float_as_int(v);
+          }
+          scr[row * kScrWords + jj * 32 + lane % 32] = bits;
+        }
+      }
+      const int cpr = nb * 32 / PER;  // 16-byte output chunks per row of this piece
+#pragma unroll
+      for (int u = 0; u < 32 * 64 / PER / 64; ++u) {  // up to 32 * cpr chunks, 64 per pass
+        const int q = u * 64 + lane;
+        if (q >= 32 * cpr) break;
+        const int row = q / cpr, cg = q % cpr;
+        const int* src = scr + row * kScrWords + cg * PER;
+        const int64_t rg = r0 + i * 32 + row;
+        const int64_t cgl = c0 + jc * 32 + cg * PER;
+        if (rg < m && cgl < n) {
+          v4i out;
+          if constexpr (ES == 4) {
+            out = *reinterpret_cast<const v4i*>(src);
+          } else {
+            const v4i a = *reinterpret_cast<const v4i*>(src);
+            const v4i b = *reinterpret_cast<const v4i*>(src + 4);
+            const int w8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              out[h] = static_cast<int>(
+                  static_cast<uint32_t>(f32_to_bf16_rne(__int_as_float(w8[2 * h]))) |
+                  (static_cast<uint32_t>(f32_to_bf16_rne(__int_as_float(w8[2 * h + 1])))
+                   << 16));
+          }
+          *reinterpret_cast<v4i*>(static_cast<char*>(y) + (rg * n + cgl) * ES) = out;
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT>
 __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
@@ -460,8 +557,22 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   }
 
   // ---- fused epilogue ----------------------------------------------------------------
-  // Per 32-row block, the row scales are loaded up front at clamped (valid) indices, so that
-  // their loads are issued together and waited for once instead of once per output row.
+  constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
+  if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
+    static_assert(C::RED_BYTES + C::WAVES * kScrBytes <= C::LDS_BYTES, "epilogue scratch");
+    if constexpr (KS == 1) {
+      // every wavefront is done reading the stages before any scratch is written
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bare_barrier();
+    }
+    int* scr = reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes);
+    epilogue_lds<C, YT>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM,
+                        n0 + wn * C::WTN);
+    return;
+  }
+  // Rows that are not whole 16-byte chunks: straight from registers.  Per 32-row block, the
+  // row scales are loaded up front at clamped (valid) indices, so that their loads are issued
+  // together and waited for once instead of once per output row.
   const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
   const int64_t col_base = n0 + wn * C::WTN + lane % 32;
   float sw[TN], bj[TN];
@@ -539,28 +650,27 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // one workgroup per CU and round; the coefficients (us) are a least-squares fit (relative
 // error) to graph-timed MI355X measurements of every candidate on 44 shapes (M 16..16384,
 // N 1024..28672, K 1024..18944, bf16 output).  On those shapes the chosen configurations
-// take 0.4% longer in total than the per-shape best (each shape predicted from a fit that
-// left it out), and 5.5% less time than a fixed rule by tile count; examples (us, chosen
-// against the former 256x256 / 256x128 choice): 2048x19456x2560 139 vs 165 (256x320),
-// 2048x6144x2560 49 vs 55 (256x192), 2048x2560x4096 32 vs 41 and 2048x2560x9728 62 vs 76
-// (128x160), 16384x12288x4096 822 vs 939 (320x256).
+// take 0.3% longer in total than the per-shape best, also when each shape is predicted from
+// a fit that left it out.  Examples (us): 2048x19456x2560 106.8 with 256x320 tiles (256x256:
+// 2 rounds + 96 tiles, 3 rounds), 2048x6144x2560 38.6 with 256x192 (256 tiles, one round),
+// 2048x2560x9728 56.3 with 128x160 (256 tiles), 16384x12288x4096 750 with 320x256.
 struct Candidate {
   int bm, bn, ks;                // tile and k-groups
   double t_step, t_round, t0;    // cost model (us)
 };
 constexpr Candidate kCandidates[] = {
-    {256, 256, 1, 1.4331, 33.257, -12.695},  // 0: 2 stages, 8 wavefronts 64x128
-    {256, 320, 1, 2.1818, 26.906, -14.422},  // 1: 2 stages, 8 wavefronts 64x160
-    {256, 192, 1, 1.2271, 22.170, -6.538},   // 2: 2 stages, 8 wavefronts 64x96
-    {128, 320, 1, 1.2967, 17.301, -4.637},   // 3: 2 stages, 8 wavefronts 32x160
-    {128, 160, 1, 0.6088, 10.434, -1.136},   // 4: 3 stages, 4 wavefronts 32x160
-    {256, 128, 1, 0.7876, 18.964, -9.088},   // 5: 3 stages, 8 wavefronts 64x64
-    {128, 128, 1, 0.5396, 7.867, -1.050},    // 6: 3 stages, 8 wavefronts 64x32
-    {128, 64, 2, 0.7266, 6.048, -0.105},     // 7: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 64, 2, 0.5120, 3.413, 2.510},       // 8: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 32, 4, 0.6634, 3.775, 2.426},       // 9: 3 stages, 4 k-groups of 2 wavefronts
-    {64, 64, 1, 0.2248, 1.206, 6.164},       // 10: 4 stages, 4 wavefronts
-    {320, 256, 1, 1.5890, 30.289, -14.814},  // 11: 2 stages, 8 wavefronts 160x64
+    {256, 256, 1, 1.3754, 20.937, -10.028},  // 0: 2 stages, 8 wavefronts 64x128
+    {256, 320, 1, 1.5622, 27.713, -14.539},  // 1: 2 stages, 8 wavefronts 64x160
+    {256, 192, 1, 1.1900, 13.434, -4.724},   // 2: 2 stages, 8 wavefronts 64x96
+    {128, 320, 1, 1.2197, 10.784, -2.978},   // 3: 2 stages, 8 wavefronts 32x160
+    {128, 160, 1, 0.5753, 7.470, 1.048},     // 4: 3 stages, 4 wavefronts 32x160
+    {256, 128, 1, 0.7672, 11.524, -5.692},   // 5: 3 stages, 8 wavefronts 64x64
+    {128, 128, 1, 0.5301, 5.133, 0.359},     // 6: 3 stages, 8 wavefronts 64x32
+    {128, 64, 2, 0.6940, 4.148, 0.642},      // 7: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 64, 2, 0.4840, 2.254, 3.057},       // 8: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 32, 4, 0.6286, 2.572, 2.824},       // 9: 3 stages, 4 k-groups of 2 wavefronts
+    {64, 64, 1, 0.2196, 0.597, 5.942},       // 10: 4 stages, 4 wavefronts
+    {320, 256, 1, 1.5221, 26.941, -12.879},  // 11: 2 stages, 8 wavefronts 160x64
 };
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
 

@@ -79,6 +79,52 @@ def test_quantize_ties_and_subnormals(ref, dev):
         quant_gpu_vs_ref(ref, dev, t, view, dtype)
 
 
+def near_tie_rows(dtype, rows, k, seed):
+    """Rows whose elements sit within a few ulps of half-integer multiples of the row scale
+    (element 0 holds the row maximum), so that a quotient taken through a rounded reciprocal
+    of the scale often rounds the other way than the correctly rounded quotient."""
+    g = wl.rng(seed)
+    f32 = np.float32
+    out = np.empty((rows, k), np.float32)
+    naive_differs = 0
+    for r in range(rows):
+        amax = f32(g.uniform(0.05, 50.0))
+        sc = f32(amax / f32(127.0))
+        if dtype == "f32":
+            n = g.integers(-127, 127, size=k - 1).astype(np.float64)
+            x = ((n + 0.5) * np.float64(sc)).astype(np.float32)
+            for _ in range(3):
+                step = g.integers(-1, 2, size=x.size)
+                x = np.where(step > 0, np.nextafter(x, f32(np.inf)),
+                             np.where(step < 0, np.nextafter(x, f32(-np.inf)), x))
+            x = np.clip(x, -amax, amax)
+        else:  # the bf16 values in [-amax, amax] whose quotients are closest to x.5
+            amax = (np.array([amax], np.float32).view(np.uint32) & 0xffff0000).view(np.float32)[0]
+            sc = f32(amax / f32(127.0))
+            vals = (np.arange(0, 0x10000, dtype=np.uint32) << 16).view(np.float32)
+            vals = vals[np.isfinite(vals) & (np.abs(vals) <= amax)]
+            qv = (vals / sc).astype(np.float32)
+            closest = vals[np.argsort(np.abs(np.abs(qv - np.rint(qv)) - 0.5))[:512]]
+            x = g.choice(closest, size=k - 1)
+        out[r, 0] = amax
+        out[r, 1:] = x
+        rec = f32(f32(1.0) / sc)
+        naive_differs += int(np.sum(np.rint((x * rec).astype(np.float32)) !=
+                                    np.rint((x / sc).astype(np.float32))))
+    return out, naive_differs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,k", [(1100, 512), (8, 4096)])
+def test_quantize_near_ties(ref, dev, dtype, rows, k):
+    """Codes of quotients within a few ulps of x.5 (one and four wavefronts per row)."""
+    a, naive_differs = near_tie_rows(dtype, rows, k, seed=rows + k)
+    assert naive_differs > 0  # the data does separate a reciprocal shortcut from division
+    t, view = host(dtype, a)
+    for per_token in (False, True):
+        quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token)
+
+
 def test_quantize_unaligned_base_uses_the_general_path(ref, dev):
     a = wl.weight(wl.rng(5), 33, 520)
     t, view = host("bf16", a)
@@ -175,13 +221,14 @@ def test_w8a8_every_tile_config(ref, dev, config):
     """Each tile configuration, forced: two tiles and a ragged third in each direction with
     four k steps (the last partial) and with one partial step; then more than one group of
     eight tile rows of the workgroup-to-tile map.  k-group configurations take k in whole
-    steps per group."""
+    steps per group.  N a multiple of 8 takes the LDS-staged 16-byte-store epilogue, an odd N
+    the per-element one."""
     bm, bn, groups = i8.w8a8_gemm_config_info(config)
     if groups == 1:
-        shapes = [(2 * bm + 37, 2 * bn + 19, 432), (2 * bm + 37, 2 * bn + 19, 16),
-                  (9 * bm + 5, 3 * bn + 7, 144)]
+        shapes = [(2 * bm + 37, 2 * bn + 24, 432), (2 * bm + 37, 2 * bn + 19, 16),
+                  (9 * bm + 5, 3 * bn + 8, 144)]
     else:
-        shapes = [(2 * bm + 37, 2 * bn + 19, 256 * groups), (9 * bm + 5, 3 * bn + 7, 128 * groups)]
+        shapes = [(2 * bm + 37, 2 * bn + 24, 256 * groups), (9 * bm + 5, 3 * bn + 7, 128 * groups)]
     for (m, n, k) in shapes:
         print(f"w8a8 config {config} ({bm}x{bn}, {groups} k-groups): {m}x{n}x{k}", flush=True)
         run_w8a8(ref, dev, m, n, k, seed=config * 31 + m, config=config)
@@ -247,6 +294,19 @@ def test_w8a8_deterministic_and_guarded(ref, dev):
     y2 = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32)
     assert torch.equal(y1, y2)
     assert torch.all(buf[:512] == -7.0) and torch.all(buf[512 + 60000:] == -7.0)
+    # an output 4 bytes off 16-byte alignment takes the per-element epilogue: same values,
+    # guard bands intact
+    buf.fill_(-7.0)
+    y3 = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32, out=buf[513:513 + 60000].view(200, 300))
+    assert torch.equal(y3, y2)
+    assert torch.all(buf[:513] == -7.0) and torch.all(buf[513 + 60000:] == -7.0)
+    hb = torch.zeros((200 * 304 + 64,), dtype=torch.bfloat16, device=dev)
+    y4 = i8.w8a8_gemm(qx[:, :1024], sx, qw[:4].repeat(76, 1), sw[:4].repeat(76),
+                      out_dtype=torch.bfloat16, out=hb[1:1 + 200 * 304].view(200, 304))
+    y5 = i8.w8a8_gemm(qx[:, :1024], sx, qw[:4].repeat(76, 1), sw[:4].repeat(76),
+                      out_dtype=torch.bfloat16)
+    assert torch.equal(y4, y5)
+    assert torch.all(hb[:1] == 0) and torch.all(hb[1 + 200 * 304:] == 0)
 
 
 def sampled_rows(m, n_rand=256, seed=0):
