@@ -67,6 +67,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
 constexpr int64_t kMaxGrid = 2147483647;  // workgroups per launch (x dimension)
@@ -427,11 +429,11 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
             const v4i b = *reinterpret_cast<const v4i*>(src + 4);
             const int w8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-              out[h] = static_cast<int>(
-                  static_cast<uint32_t>(f32_to_bf16_rne(__int_as_float(w8[2 * h]))) |
-                  (static_cast<uint32_t>(f32_to_bf16_rne(__int_as_float(w8[2 * h + 1])))
-                   << 16));
+            for (int h = 0; h < 4; ++h) {
+              // round to nearest even, two values per instruction (v_cvt_pk_bf16_f32)
+              const v2f pair = {__int_as_float(w8[2 * h]), __int_as_float(w8[2 * h + 1])};
+              out[h] = __builtin_bit_cast(int, __builtin_convertvector(pair, v2bf));
+            }
           }
           *reinterpret_cast<v4i*>(static_cast<char*>(y) + (rg * n + cgl) * ES) = out;
         }
