@@ -14,8 +14,11 @@
 //
 // Arithmetic (identical for every dtype): the input is widened exactly to float32;
 // s = amax / 127 is a correctly rounded float32 division; s == 0 stores scale 1 and zero
-// codes; otherwise each code is rint(a / s) (correctly rounded division, then round half to
-// even via v_rndne_f32) clamped to [-127, 127].  The file must not be built with fast-math.
+// codes; otherwise each code is rint(a / s) (the correctly rounded float32 quotient, then
+// round half to even via v_rndne_f32) clamped to [-127, 127].  The quotient comes from the
+// reciprocal and one FMA correction (see quotient_fma), which yields exactly the correctly
+// rounded quotient at a third of the instructions of a full division.  The file must not be
+// built with fast-math.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -87,10 +90,39 @@ __device__ __forceinline__ float widen_one(const void* base, int64_t i) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+// Maximum of a non-negative float over the 64 lanes, returned in every lane.  Non-negative
+// floats order like their bit patterns, so the reduction runs on integers with DPP moves
+// (swap within pairs and quads, mirror within 8 and 16 lanes, then broadcast lane 15 of each
+// row into the next row and lane 31 into the upper half); lane 63 ends with the maximum.
+__device__ __forceinline__ float wave_max(float f) {
+  int v = __float_as_int(f);
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));  // row_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));  // row_bcast15
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));  // row_bcast31
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
+// RN(a / s) from y = RN(1 / s) and fused multiply-adds: q0 = RN(a * y) is within one ulp of
+// a / s, the remainder r = a - s * q0 is then exactly representable (one FMA computes it
+// without rounding), and RN(q0 + r * y) is the correctly rounded quotient RN(a / s) whenever
+// no intermediate underflows (Markstein's theorem for division with an FMA, P. Markstein,
+// IBM J. Res. Dev. 34(1), 1990; also the division chapter of Muller et al., Handbook of
+// Floating-Point Arithmetic).  Here |a| <= 127 * s (a row's elements against its own scale)
+// and the caller takes this path only for s >= 2^-64, so every quotient whose code can be
+// nonzero has a remainder far above the subnormal range; a quotient small enough for the
+// remainder to underflow rounds to code 0 either way.
+__device__ __forceinline__ float quotient_fma(float a, float s, float y) {
+  const float q0 = a * y;
+  const float r = __builtin_fmaf(-s, q0, a);
+  return __builtin_fmaf(r, y, q0);
+}
+
+// The code of one element from a quotient: ties-to-even, clamp.
+__device__ __forceinline__ int code_from_quotient(float q) {
+  return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(q), -127.0f, 127.0f));
 }
 
 // The code of one element: correctly rounded float32 quotient, ties-to-even, clamp.
@@ -166,31 +198,41 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel
     return;
   }
 
-  auto emit = [&](const uint4 v, int64_t c) {
-    widen_chunk<DT>(v, f);
-    uint32_t packed[E / 4];
+  // Pass 2 with the quotients from the reciprocal (scales of 2^-64 and up: every row of
+  // practical data) or from full divisions (smaller scales); one branch per row.
+  auto emit_all = [&](auto code) {
+    auto emit = [&](const uint4 v, int64_t c) {
+      widen_chunk<DT>(v, f);
+      uint32_t packed[E / 4];
 #pragma unroll
-    for (int g = 0; g < E / 4; ++g) {
-      uint32_t p = 0;
+      for (int g = 0; g < E / 4; ++g) {
+        uint32_t p = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        p |= (static_cast<uint32_t>(code_of(f[4 * g + b], s)) & 0xffu) << (8 * b);
-      packed[g] = p;
-    }
-    if constexpr (E == 4) {
-      *reinterpret_cast<uint32_t*>(dst + c * 4) = packed[0];
+        for (int b = 0; b < 4; ++b)
+          p |= (static_cast<uint32_t>(code(f[4 * g + b])) & 0xffu) << (8 * b);
+        packed[g] = p;
+      }
+      if constexpr (E == 4) {
+        *reinterpret_cast<uint32_t*>(dst + c * 4) = packed[0];
+      } else {
+        *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(packed[0], packed[1]);
+      }
+    };
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kCacheChunks; ++i) {
+        const int64_t c = t + static_cast<int64_t>(i) * T;
+        if (c < chunks) emit(cache[i], c);
+      }
     } else {
-      *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(packed[0], packed[1]);
+      for (int64_t c = t; c < chunks; c += T) emit(src[c], c);
     }
   };
-  if (cached) {
-#pragma unroll
-    for (int i = 0; i < kCacheChunks; ++i) {
-      const int64_t c = t + static_cast<int64_t>(i) * T;
-      if (c < chunks) emit(cache[i], c);
-    }
+  if (s >= 0x1p-64f) {
+    const float y = 1.0f / s;  // RN(1 / s)
+    emit_all([&](float a) { return code_from_quotient(quotient_fma(a, s, y)); });
   } else {
-    for (int64_t c = t; c < chunks; c += T) emit(src[c], c);
+    emit_all([&](float a) { return code_of(a, s); });
   }
   if (t == 0) scale[row] = s;
 }
