@@ -110,10 +110,10 @@ __device__ __forceinline__ float wave_max(float f) {
 // without rounding), and RN(q0 + r * y) is the correctly rounded quotient RN(a / s) whenever
 // no intermediate underflows (Markstein's theorem for division with an FMA, P. Markstein,
 // IBM J. Res. Dev. 34(1), 1990; also the division chapter of Muller et al., Handbook of
-// Floating-Point Arithmetic).  Here |a| <= 127 * s (a row's elements against its own scale)
-// and the caller takes this path only for s >= 2^-64, so every quotient whose code can be
-// nonzero has a remainder far above the subnormal range; a quotient small enough for the
-// remainder to underflow rounds to code 0 either way.
+// Floating-Point Arithmetic).  The remainder can only underflow for |a| below about 2^-102.
+// The caller takes this path only for s >= 2^-64: an element whose code can be nonzero has
+// |a| >= s / 2 >= 2^-65, and a smaller |a| has a quotient below 1/2 in magnitude, which
+// rounds to code 0 whatever its last bits.
 __device__ __forceinline__ float quotient_fma(float a, float s, float y) {
   const float q0 = a * y;
   const float r = __builtin_fmaf(-s, q0, a);
