@@ -200,6 +200,29 @@ def test_grouped_validation(lib):
     assert call(ids=A2) == ALIGN
 
 
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0  # counts devices without initializing HIP
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="the fake pointers below must never reach a GPU")
+def test_valid_calls_without_a_device_report_hip_errors(lib):
+    """With no device, a call that passes validation fails at its first HIP call with
+    I8QL_ERR_HIP (and a recorded hipError), instead of crashing."""
+    HIP = 7
+    calls = [
+        lambda: lib.quantize_per_channel_int8(A16, BF16, 4, 64, A16, A16, NUL),
+        lambda: lib.quantize_per_token_int8(A16, F32, 4, 64, A16, A16, NUL),
+        lambda: lib.w8a8_gemm(A16, A16, A16, A16, NUL, A16, BF16, 4, 8, 64, NUL),
+        lambda: lib.w8a8_gemm_with_config(0, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 64, NUL),
+        lambda: lib.w8a16_gemm(A16, A16, A16, NUL, A16, BF16, 1, 16, 64, NUL),
+        lambda: lib.grouped_w8a16_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64, NUL),
+    ]
+    for call in calls:
+        assert call() == HIP
+        assert lib.i8ql_last_hip_error() != 0
+
+
 def test_binding_fails_loudly_without_a_gpu_tensor():
     import torch
     import int8_quantized_linear_amd as i8
