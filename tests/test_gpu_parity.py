@@ -38,6 +38,14 @@ def host(dtype, a32):
     return t, wl.bits16(t)
 
 
+def sentinel(shape, dtype, dev):
+    """Output buffer pre-filled so that an element the kernel fails to write cannot match:
+    NaN for float outputs, the 0xAAAAAAAA pattern for int32."""
+    if dtype == torch.int32:
+        return torch.full(shape, -0x55555556, dtype=torch.int32, device=dev)
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
+
+
 def quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token=False):
     fn = i8.quantize_per_token_int8 if per_token else i8.quantize_per_channel_int8
     q, s = fn(t.to(dev))
@@ -196,11 +204,13 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
             if od == torch.int32:
                 if use_bias:
                     continue
-                y = i8.w8a8_gemm_with_config(config, qx, None, qw, None, out_dtype=torch.int32)
+                y = i8.w8a8_gemm_with_config(config, qx, None, qw, None, out_dtype=torch.int32,
+                                             out=sentinel((m, n), torch.int32, dev))
                 np.testing.assert_array_equal(y.cpu().numpy(), acc)
                 continue
             b = torch.from_numpy(b_np).to(dev) if use_bias else None
-            y = i8.w8a8_gemm_with_config(config, qx, sx, qw, sw, b, out_dtype=od)
+            y = i8.w8a8_gemm_with_config(config, qx, sx, qw, sw, b, out_dtype=od,
+                                         out=sentinel((m, n), od, dev))
             check_float(y, yref, w8a8_tol(acc, sxr, swr, b_np), f"w8a8 {m}x{n}x{k} {od}")
 
 
@@ -333,8 +343,11 @@ def run_w8a8_full(ref, dev, m, n, k, frac, bias, seed):
     qw, sw = i8.quantize_per_channel_int8(wt.to(dev))
     qx, sx = i8.quantize_per_token_int8(xt.to(dev))
     b = torch.from_numpy(b_np).to(dev) if bias else None
-    y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=torch.bfloat16)
-    yi = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32)
+    y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=torch.bfloat16,
+                     out=sentinel((m, n), torch.bfloat16, dev))
+    yi = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32,
+                      out=sentinel((m, n), torch.int32, dev))
+    assert not torch.isnan(y).any()  # every element written (rows not sampled included)
     rows = sampled_rows(m, seed=seed)
     qwr, swr = ref.quantize_rows(wv, "bf16")
     np.testing.assert_array_equal(qw.cpu().numpy(), qwr)
@@ -367,7 +380,8 @@ def run_w8a16(ref, dev, m, n, k, bias, out_dtype, seed):
     qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
     b_np = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)) if bias else None
     b = torch.from_numpy(b_np).to(dev) if bias else None
-    y = i8.w8a16_gemm(xt.to(dev), qw, sw, b, out_dtype=out_dtype)
+    y = i8.w8a16_gemm(xt.to(dev), qw, sw, b, out_dtype=out_dtype,
+                      out=sentinel((m, n), out_dtype, dev))
     yref = ref.w8a16(xv, qwr, swr, b_np)
     absdot = np.abs(xt.double().numpy()) @ (np.abs(qwr.astype(np.float64)) * swr[:, None]).T
     check_float(y, yref, w8a16_tol(yref, absdot, k, b_np), f"w8a16 {m}x{n}x{k}")
@@ -414,7 +428,8 @@ def run_grouped(ref, dev, qw, sw, qwr, swr, ids, x_rows, per_assign, out_dtype, 
     e, n, k = qwr.shape
     xt, xv = host("bf16", wl.activations(g, x_rows, k))
     y = i8.grouped_w8a16_gemm(xt.to(dev), qw, sw, torch.from_numpy(ids).to(dev),
-                              x_per_assignment=per_assign, out_dtype=out_dtype)
+                              x_per_assignment=per_assign, out_dtype=out_dtype,
+                              out=sentinel((ids.size, n), out_dtype, dev))
     yref = ref.grouped_w8a16(xv, per_assign, qwr, swr, ids)
     t, topk = ids.shape
     xd = np.abs(xt.double().numpy())
