@@ -4,7 +4,8 @@
 // single grouped GEMM over expert weights that are stacked into one tensor per projection,
 // with per-output-channel int8 codes.  Here the expert-grouped dispatch happens inside the
 // kernel: workgroup (tile, e) covers 16 output channels of expert e.  Wavefront 0 scans the
-// routing ids in order (ballot + prefix popcount, so the row list is deterministic) and
+// routing ids in order (loads batched, ballot + prefix popcount, so the row list is
+// deterministic) and
 // collects the assignments p = token * topk + slot routed to e into an LDS list; a
 // workgroup whose list is empty exits at once, so only the experts that received tokens
 // cost HBM bytes.  The listed rows are then processed in passes of up to 8: each pass
@@ -25,6 +26,7 @@ namespace {
 
 constexpr int kUnroll = 8;  // steps of k whose weight loads a wavefront keeps in flight
 constexpr int kList = 1024;     // assignments held in LDS per scan window
+constexpr int kScanBatch = 8;   // 64-id groups whose loads a scan keeps in flight together
 constexpr int kMaxPassRows = 8;  // activation rows staged in LDS per pass
 
 template <int WAVES>
@@ -59,29 +61,55 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
   const bool invalid_row = (e == num_experts);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
+  // This lane's 4 output-channel scales (wavefront 0 applies them), requested before the
+  // scan so that their latency overlaps it.
+  const int64_t nc = n0 + 4 * (lane / 16);
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0 && !invalid_row) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = w_scale[e * n + min(nc + r, n - 1)];
+  }
 
   int64_t p_next = 0;
   while (true) {
     // ---- expert-grouped dispatch: collect the next window of assignments for e --------
+    // The ids are read kScanBatch * 64 at a time, every load of a batch in flight at once
+    // (one memory round trip per batch instead of one per 64 ids), then matched 64 at a time
+    // in order.
     if (wave == 0) {
       int base = 0;
       int64_t p = p_next;
-      while (p < total) {
-        const int64_t mine = p + lane;
-        bool match = false;
-        if (mine < total) {
-          const int32_t id = ids[mine];
-          match = invalid_row ? (id < 0 || id >= num_experts) : (id == e);
+      bool full = false;
+      while (p < total && !full) {
+        int32_t idv[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          idv[j] = -1;
+          if (p + 64 * j < total) {  // groups past the end are neither loaded nor matched
+            const int64_t q = p + 64 * j + lane;
+            idv[j] = ids[q < total ? q : total - 1];
+          }
         }
-        const uint64_t mask = __ballot(match);
-        const int cnt = __popcll(mask);
-        if (base + cnt > kList) break;  // the window is full; resume at p next time
-        if (match) {
-          const uint64_t below = lane == 0 ? 0ull : (mask & ((~0ull) >> (64 - lane)));
-          list[base + __popcll(below)] = static_cast<int>(mine);
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          const int64_t mine = p + lane;
+          if (p >= total) break;
+          const int32_t id = idv[j];
+          const bool match =
+              mine < total && (invalid_row ? (id < 0 || id >= num_experts) : (id == e));
+          const uint64_t mask = __ballot(match);
+          const int cnt = __popcll(mask);
+          if (base + cnt > kList) {  // the window is full; resume at p next time
+            full = true;
+            break;
+          }
+          if (match) {
+            const uint64_t below = lane == 0 ? 0ull : (mask & ((~0ull) >> (64 - lane)));
+            list[base + __popcll(below)] = static_cast<int>(mine);
+          }
+          base += cnt;
+          p += 64;
         }
-        base += cnt;
-        p += 64;
       }
       if (lane == 0) {
         s_count = base;
@@ -106,7 +134,6 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
     } else if (count > 0) {
       const int64_t wr = min(n0 + lane % 16, n - 1);
       const int8_t* wrow = wq + (e * n + wr) * k;
-      const int64_t nc = n0 + 4 * (lane / 16);
       const int64_t pitch = 2 * k + 16;
       const int div = x_per_assignment ? 1 : static_cast<int>(topk);
       int sb, se;
@@ -144,9 +171,6 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
         red[wave * 64 + lane] = acc[0];
         __syncthreads();
         if (wave == 0 && lane % 16 < rows) {
-          float sc[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] = w_scale[e * n + min(nc + r, n - 1)];
           v4f sum = red[lane];
 #pragma unroll
           for (int w2 = 1; w2 < WAVES; ++w2) sum += red[w2 * 64 + lane];
