@@ -442,6 +442,80 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
   }
 }
 
+// Epilogue straight from registers, for outputs whose rows are not whole 16-byte chunks (or
+// a misaligned output).  Per 32-row block the row scales are loaded up front at clamped
+// (valid) indices, so that their loads are issued together and waited for once instead of
+// once per output row.  (r0, c0): the wavefront's first output row and column.
+template <class C, int YT>
+__device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], int lane,
+                                              const float* __restrict__ x_scale,
+                                              const float* __restrict__ w_scale,
+                                              const float* __restrict__ bias, void* y,
+                                              int64_t m, int64_t n, int64_t r0, int64_t c0) {
+  constexpr int TM = C::TM, TN = C::TN;
+  const int64_t row_base = r0 + 4 * (lane / 32);
+  const int64_t col_base = c0 + lane % 32;
+  float sw[TN], bj[TN];
+  if constexpr (YT != I8QL_I32) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t c = col_base + j * 32;
+      sw[j] = w_scale[c < n ? c : n - 1];
+      bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float sx[16];
+    if constexpr (YT != I8QL_I32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
+        sx[r] = x_scale[row < m ? row : m - 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t c = col_base + j * 32;
+      if (c >= n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
+        if (row >= m) continue;
+        const int a = acc[i][j][r];
+        if constexpr (YT == I8QL_I32) {
+          static_cast<int32_t*>(y)[row * n + c] = a;
+        } else {
+          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[r]), sw[j]);
+          if (bias) v = __fadd_rn(v, bj[j]);
+          if constexpr (YT == I8QL_F32) {
+            static_cast<float*>(y)[row * n + c] = v;
+          } else {
+            static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v);
+          }
+        }
+      }
+    }
+  }
+}
+
+// The fused epilogue of a wavefront's accumulators: through LDS with 16-byte stores when the
+// output allows it, else from registers.  `scr` is this wavefront's LDS scratch; the caller
+// has made sure no wavefront still reads the LDS it overlaps.
+template <class C, int YT>
+__device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* scr, int lane,
+                                         const float* __restrict__ x_scale,
+                                         const float* __restrict__ w_scale,
+                                         const float* __restrict__ bias, void* y, int64_t m,
+                                         int64_t n, int64_t r0, int64_t c0) {
+  constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
+  if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
+    epilogue_lds<C, YT>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+  } else {
+    epilogue_regs<C, YT>(acc, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+  }
+}
+
 template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT>
 __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
@@ -559,66 +633,208 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   }
 
   // ---- fused epilogue ----------------------------------------------------------------
-  constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
-  if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
-    static_assert(C::RED_BYTES + C::WAVES * kScrBytes <= C::LDS_BYTES, "epilogue scratch");
-    if constexpr (KS == 1) {
-      // every wavefront is done reading the stages before any scratch is written
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      bare_barrier();
-    }
-    int* scr = reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes);
-    epilogue_lds<C, YT>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM,
-                        n0 + wn * C::WTN);
-    return;
+  static_assert(C::RED_BYTES + C::WAVES * kScrBytes <= C::LDS_BYTES, "epilogue scratch");
+  if constexpr (KS == 1) {
+    // every wavefront is done reading the stages before any scratch is written
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bare_barrier();
   }
-  // Rows that are not whole 16-byte chunks: straight from registers.  Per 32-row block, the
-  // row scales are loaded up front at clamped (valid) indices, so that their loads are issued
-  // together and waited for once instead of once per output row.
-  const int64_t row_base = m0 + wm * C::WTM + 4 * (lane / 32);
-  const int64_t col_base = n0 + wn * C::WTN + lane % 32;
-  float sw[TN], bj[TN];
-  if constexpr (YT != I8QL_I32) {
+  epilogue<C, YT>(acc, reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes), lane,
+                  x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+}
+
+// ---- two LDS slots for A, three for B ---------------------------------------------------
+// With two stages of both operands only one step of loads is in flight while a step
+// computes, and the weight rows (read once from HBM) arrive late.  A third stage of both
+// does not fit in LDS for the large tiles, but a third one of B alone does (256x256: 2 x 32 +
+// 3 x 32 KiB; 256x192: 136 KiB; 128x320: 152 KiB).  Step t computes from A slot t % 2 and B
+// slot t % 3; after the barrier that ends step t the workgroup refills A slot t % 2 with step
+// t + 2 and B slot t % 3 with step t + 3, in that order, so the weight loads have two steps
+// to land and the activation loads one.  At the end of step u the only loads allowed to be
+// outstanding are then B(u + 2)'s.  Measured on MI355X against the same tile with two
+// stages of both: 4-20 % faster for 256x192 and 10-25 % for 128x320 over 44 shapes; for
+// 256x256 it helps long-k and few-row shapes but costs 2-3 % on large ones, which keep the
+// symmetric kernel.
+template <class C>
+struct SplitStages {
+  static constexpr int LA = C::BM / C::ROWS_PER_LOAD / C::WAVES;  // A loads per wave per step
+  static constexpr int LB = C::LOADS - LA;                         // B loads per wave per step
+  static constexpr int A_BYTES = C::BM * C::BK;
+  static constexpr int B_BYTES = C::BN * C::BK;
+  static constexpr size_t LDS_BYTES = 2 * static_cast<size_t>(A_BYTES) +
+                                      3 * static_cast<size_t>(B_BYTES);
+  static_assert(LA * C::ROWS_PER_LOAD * C::WAVES == C::BM, "A rows split evenly over waves");
+  static_assert(2 * LB + LA <= 63, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
+  static_assert(C::WAVES * kScrBytes <= LDS_BYTES, "epilogue scratch");
+};
+
+// Loads [J0, J1) of a step into one operand's slot (dst offsets relative to that slot).
+template <class C, int J0, int J1>
+__device__ __forceinline__ void issue_rows(int8_t* slot, const int8_t* const* src,
+                                           const int* col, const int* dst, int step,
+                                           int64_t k) {
+  const int64_t k0 = static_cast<int64_t>(step) * C::BK;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t c = col_base + j * 32;
-      sw[j] = w_scale[c < n ? c : n - 1];
-      bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
+  for (int j = J0; j < J1; ++j) {
+    const int64_t kk = k0 + col[j];
+    const int8_t* g = src[j] + (kk < k ? kk : 0);
+    __builtin_amdgcn_global_load_lds(g, slot + dst[j], 16, 0, 0);
+  }
+}
+
+// LDS drain, wait until at most `outstanding` loads of this wavefront are in flight, barrier.
+template <int OUTSTANDING>
+__device__ __forceinline__ void drain_wait_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(OUTSTANDING, 15));
+  bare_barrier();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int YT>
+__global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_split(
+    const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+    const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
+    const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
+  using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
+  using P = SplitStages<C>;
+  constexpr int TM = C::TM, TN = C::TN;
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
+
+  int64_t tm, tn;
+  if (!tile_of((m + BM - 1) / BM, (n + BN - 1) / BN, tm, tn)) return;
+  const int64_t m0 = tm * BM;
+  const int64_t n0 = tn * BN;
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int wm = wave / WN, wn = wave % WN;
+  const int ksteps = static_cast<int>((k + BK - 1) / BK);
+  int8_t* const aslots = lds_all;
+  int8_t* const bslots = lds_all + 2 * P::A_BYTES;
+
+  // Load instruction j covers rows ROWS_PER_LOAD * (wave + WAVES * j) + [0, ROWS_PER_LOAD) of
+  // the stacked [A; B] slice; the first LA instructions are A rows, the rest B rows.
+  const int8_t* src[C::LOADS];
+  int col[C::LOADS];
+  int dst[C::LOADS];
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int blk = wave + C::WAVES * j;
+    const int trow = blk * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+    col[j] = ((lane % C::CHUNKS) ^ swizzle<BK>(trow)) * 16;
+    if (j < P::LA) {
+      src[j] = xq + min(m0 + trow, m - 1) * k;
+      dst[j] = blk * C::ROWS_PER_LOAD * BK;
+    } else {
+      src[j] = wq + min(n0 + (trow - BM), n - 1) * k;
+      dst[j] = (blk * C::ROWS_PER_LOAD - BM) * BK;
     }
   }
+
+  v16i acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    float sx[16];
-    if constexpr (YT != I8QL_I32) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
-        sx[r] = x_scale[row < m ? row : m - 1];
-      }
-    }
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t c = col_base + j * 32;
-      if (c >= n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row_base + i * 32 + 8 * (r / 4) + r % 4;
-        if (row >= m) continue;
-        const int a = acc[i][j][r];
-        if constexpr (YT == I8QL_I32) {
-          static_cast<int32_t*>(y)[row * n + c] = a;
-        } else {
-          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[r]), sw[j]);
-          if (bias) v = __fadd_rn(v, bj[j]);
-          if constexpr (YT == I8QL_F32) {
-            static_cast<float*>(y)[row * n + c] = v;
-          } else {
-            static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v);
-          }
-        }
-      }
-    }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  // prologue: A0 B0, then B1 A1 B2 (B1 before A1, so that A1 landing implies B1 has)
+  issue_rows<C, 0, P::LA>(aslots, src, col, dst, 0, k);
+  issue_rows<C, P::LA, C::LOADS>(bslots, src, col, dst, 0, k);
+  if (ksteps > 1) {
+    issue_rows<C, P::LA, C::LOADS>(bslots + P::B_BYTES, src, col, dst, 1, k);
+    issue_rows<C, 0, P::LA>(aslots + P::A_BYTES, src, col, dst, 1, k);
   }
+  if (ksteps > 2) issue_rows<C, P::LA, C::LOADS>(bslots + 2 * P::B_BYTES, src, col, dst, 2, k);
+
+  const int frow = lane % 32;
+  const int fx = swizzle<BK>(frow);
+  const int a_off = (wm * C::WTM + frow) * BK;
+  const int b_rel = (wn * C::WTN + frow) * BK;
+  const int tail_valid = static_cast<int>((k % BK) / 16);  // 0: none
+  // fragment reads address step t's B rows from its A slot
+  auto b_off = [&](int t) {
+    return static_cast<int>((bslots + (t % 3) * P::B_BYTES) - (aslots + (t % 2) * P::A_BYTES)) +
+           b_rel;
+  };
+  auto a_slot = [&](int t) { return aslots + (t % 2) * P::A_BYTES; };
+
+  if (ksteps > 2) {
+    drain_wait_barrier<2 * P::LB + P::LA>();
+  } else if (ksteps == 2) {
+    drain_wait_barrier<P::LB + P::LA>();
+  } else {
+    drain_wait_barrier<0>();
+  }
+  if (tail_valid != 0 && ksteps == 1) zero_tail<C>(aslots, tail_valid);
+  v4i fa[2][TM], fb[2][TN];
+  read_slice<C>(aslots, 0, a_off, b_off(0), fx, lane, fa[0], fb[0]);
+  constexpr int last = (C::SLICES - 1) % 2;  // SLICES is even, so set 0 is free
+  int t = 0;
+  // steady state: refill A(t + 2) and B(t + 3)
+  for (; t + 3 < ksteps; ++t) {
+    step_inner<C>(a_slot(t), a_off, b_off(t), fx, lane, fa, fb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    drain_wait_barrier<P::LB>();
+    read_slice<C>(a_slot(t + 1), 0, a_off, b_off(t + 1), fx, lane, fa[0], fb[0]);
+    issue_rows<C, 0, P::LA>(a_slot(t), src, col, dst, t + 2, k);
+    issue_rows<C, P::LA, C::LOADS>(bslots + (t % 3) * P::B_BYTES, src, col, dst, t + 3, k);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    loads_under_mfmas<C, 1>();
+  }
+  // t = ksteps - 3: refill A only
+  if (t + 2 < ksteps) {
+    step_inner<C>(a_slot(t), a_off, b_off(t), fx, lane, fa, fb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    drain_wait_barrier<P::LB>();
+    read_slice<C>(a_slot(t + 1), 0, a_off, b_off(t + 1), fx, lane, fa[0], fb[0]);
+    issue_rows<C, 0, P::LA>(a_slot(t), src, col, dst, t + 2, k);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    reads_under_mfmas<C, 1>();
+    ++t;
+  }
+  // t = ksteps - 2: nothing left to load; the last step may be partial
+  if (t + 1 < ksteps) {
+    step_inner<C>(a_slot(t), a_off, b_off(t), fx, lane, fa, fb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    drain_wait_barrier<0>();
+    if (tail_valid != 0) zero_tail<C>(a_slot(t + 1), tail_valid);
+    read_slice<C>(a_slot(t + 1), 0, a_off, b_off(t + 1), fx, lane, fa[0], fb[0]);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    reads_under_mfmas<C, 1>();
+    ++t;
+  }
+  step_inner<C>(a_slot(t), a_off, b_off(t), fx, lane, fa, fb, acc);
+  mfma_slice<C>(fa[(C::SLICES - 1) % 2], fb[(C::SLICES - 1) % 2], acc);
+
+  // every wavefront is done reading the slots before any scratch is written
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  bare_barrier();
+  epilogue<C, YT>(acc, reinterpret_cast<int*>(lds_all + wave * kScrBytes), lane, x_scale,
+                  w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+}
+
+template <int BM, int BN, int BK, int YT, int WM, int WN>
+hipError_t launch_split(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                        const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
+                        int64_t k, hipStream_t stream) {
+  using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
+  using P = SplitStages<C>;
+  auto kern = w8a8_kernel_split<BM, BN, BK, WM, WN, YT>;
+  static bool configured = false;  // idempotent attribute set; a race only repeats it
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(P::LDS_BYTES));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), P::LDS_BYTES,
+                     stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM = 2, int WN = 2>
@@ -652,27 +868,28 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // one workgroup per CU and round; the coefficients (us) are a least-squares fit (relative
 // error) to graph-timed MI355X measurements of every candidate on 44 shapes (M 16..16384,
 // N 1024..28672, K 1024..18944, bf16 output).  On those shapes the chosen configurations
-// take 0.3% longer in total than the per-shape best, also when each shape is predicted from
-// a fit that left it out.  Examples (us): 2048x19456x2560 106.8 with 256x320 tiles (256x256:
-// 2 rounds + 96 tiles, 3 rounds), 2048x6144x2560 38.6 with 256x192 (256 tiles, one round),
-// 2048x2560x9728 56.3 with 128x160 (256 tiles), 16384x12288x4096 750 with 320x256.
+// take 0.9% longer in total than the per-shape best, also when each shape is predicted from
+// a fit that left it out.  Examples (us): 2048x19456x2560 106 with 256x320 tiles (256x256:
+// 2 rounds + 96 tiles, 3 rounds), 2048x6144x2560 37 with 256x192 (256 tiles, one round),
+// 2048x2560x9728 56 with 128x160 (256 tiles), 16384x12288x4096 750-765 with 256x256 or
+// 320x256.
 struct Candidate {
   int bm, bn, ks;                // tile and k-groups
   double t_step, t_round, t0;    // cost model (us)
 };
 constexpr Candidate kCandidates[] = {
-    {256, 256, 1, 1.3754, 20.937, -10.028},  // 0: 2 stages, 8 wavefronts 64x128
-    {256, 320, 1, 1.5622, 27.713, -14.539},  // 1: 2 stages, 8 wavefronts 64x160
-    {256, 192, 1, 1.1900, 13.434, -4.724},   // 2: 2 stages, 8 wavefronts 64x96
-    {128, 320, 1, 1.2197, 10.784, -2.978},   // 3: 2 stages, 8 wavefronts 32x160
-    {128, 160, 1, 0.5753, 7.470, 1.048},     // 4: 3 stages, 4 wavefronts 32x160
-    {256, 128, 1, 0.7672, 11.524, -5.692},   // 5: 3 stages, 8 wavefronts 64x64
-    {128, 128, 1, 0.5301, 5.133, 0.359},     // 6: 3 stages, 8 wavefronts 64x32
-    {128, 64, 2, 0.6940, 4.148, 0.642},      // 7: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 64, 2, 0.4840, 2.254, 3.057},       // 8: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 32, 4, 0.6286, 2.572, 2.824},       // 9: 3 stages, 4 k-groups of 2 wavefronts
-    {64, 64, 1, 0.2196, 0.597, 5.942},       // 10: 4 stages, 4 wavefronts
-    {320, 256, 1, 1.5221, 26.941, -12.879},  // 11: 2 stages, 8 wavefronts 160x64
+    {256, 256, 1, 1.3616, 21.063, -10.348},  // 0: 2 stages, 8 wavefronts 64x128
+    {256, 320, 1, 1.5576, 27.308, -14.718},  // 1: 2 stages, 8 wavefronts 64x160
+    {256, 192, 1, 1.0216, 17.150, -7.651},   // 2: 2 A + 3 B slots, 8 wavefronts 64x96
+    {128, 320, 1, 0.9822, 13.467, -3.992},   // 3: 2 A + 3 B slots, 8 wavefronts 32x160
+    {128, 160, 1, 0.5742, 7.669, 0.439},     // 4: 3 stages, 4 wavefronts 32x160
+    {256, 128, 1, 0.7426, 12.247, -6.637},   // 5: 3 stages, 8 wavefronts 64x64
+    {128, 128, 1, 0.5263, 5.399, 0.071},     // 6: 3 stages, 8 wavefronts 64x32
+    {128, 64, 2, 0.6945, 4.216, 0.586},      // 7: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 64, 2, 0.4855, 2.353, 2.777},       // 8: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 32, 4, 0.6247, 2.558, 2.713},       // 9: 3 stages, 4 k-groups of 2 wavefronts
+    {64, 64, 1, 0.2183, 0.705, 5.779},       // 10: 4 stages, 4 wavefronts
+    {320, 256, 1, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
 };
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
 
@@ -682,11 +899,13 @@ hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const
                             int64_t n, int64_t k, hipStream_t stream) {
 #define I8QL_W8A8_CFG(...) \
   launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
+#define I8QL_W8A8_SPLIT(...) \
+  launch_split<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
   switch (c) {
     case 0: return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2);
     case 1: return I8QL_W8A8_CFG(256, 320, 128, 2, 1, YT, 4, 2);
-    case 2: return I8QL_W8A8_CFG(256, 192, 128, 2, 1, YT, 4, 2);
-    case 3: return I8QL_W8A8_CFG(128, 320, 128, 2, 1, YT, 4, 2);
+    case 2: return I8QL_W8A8_SPLIT(256, 192, 128, YT, 4, 2);
+    case 3: return I8QL_W8A8_SPLIT(128, 320, 128, YT, 4, 2);
     case 4: return I8QL_W8A8_CFG(128, 160, 128, 3, 1, YT, 4, 1);
     case 5: return I8QL_W8A8_CFG(256, 128, 128, 3, 1, YT, 4, 2);
     case 6: return I8QL_W8A8_CFG(128, 128, 128, 3, 1, YT, 2, 4);
@@ -697,6 +916,7 @@ hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const
     default: return I8QL_W8A8_CFG(320, 256, 128, 2, 1, YT, 2, 4);
   }
 #undef I8QL_W8A8_CFG
+#undef I8QL_W8A8_SPLIT
 }
 
 // Compute units of the current device (cached per device id).
