@@ -29,6 +29,7 @@ namespace {
 constexpr int kUnroll = 8;  // steps of k whose loads a wavefront keeps in flight
 constexpr int kGlobalUnroll = 4;  // the same with activations loaded too (divided by MT)
 constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a function attribute
+constexpr size_t kMaxStageLds = 96 * 1024;  // staged rows up to this much LDS (attribute set)
 
 // Dynamic LDS: the partial tiles of the WAVES wavefronts ([WAVES][MT][64] v4f), then, when
 // the activation rows are staged, rows of 2k + 16 bytes (consecutive rows shifted by one
@@ -153,9 +154,20 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
   // (with more than 16 KiB of partial tiles, the rows of the k that calls for that many
   // waves never fit)
   constexpr bool can_stage = red_bytes<MT, WAVES>() <= kMaxDefaultLds / 4;
-  if (can_stage && xlds <= kMaxDefaultLds) {
-    hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, can_stage>), grid, dim3(64 * WAVES),
-                       xlds, stream, xx, wq, w_scale, bias, y, m, n, k);
+  if (can_stage && xlds <= kMaxStageLds) {
+    auto kern = w8a16_kernel<MT, WAVES, YT, can_stage>;
+    if (xlds > kMaxDefaultLds) {  // e.g. 8 rows of k = 4096: 70 KiB
+      static bool configured = false;  // idempotent attribute set; a race only repeats it
+      if (!configured) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kMaxStageLds));
+        if (e != hipSuccess) return e;
+        configured = true;
+      }
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), xlds, stream, xx, wq, w_scale, bias, y, m,
+                       n, k);
   } else {
     hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, false>), grid, dim3(64 * WAVES),
                        rbytes, stream, xx, wq, w_scale, bias, y, m, n, k);
