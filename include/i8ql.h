@@ -204,10 +204,11 @@ i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, co
  * expert_ids  device, [t, topk] int32.
  * y           device, [t * topk, n] of y_dtype in {I8QL_BF16, I8QL_F32}.
  * t, n >= 0; 1 <= topk <= 64; t * topk <= 65536; 1 <= num_experts <= 65534;
- * k >= 16, k % 16 == 0.
+ * 16 <= k <= I8QL_GROUPED_MAX_K, k % 16 == 0 (an activation row is staged whole in LDS).
  * Errors: as for w8a16_gemm; x_per_assignment not 0/1, topk or num_experts out of range ->
- * I8QL_ERR_ARG; t * topk > 65536 -> I8QL_ERR_SHAPE.
+ * I8QL_ERR_ARG; t * topk > 65536 or k > I8QL_GROUPED_MAX_K -> I8QL_ERR_SHAPE.
  */
+#define I8QL_GROUPED_MAX_K 32768
 i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t* wq,
                                const float* w_scale, int64_t num_experts,
                                const int32_t* expert_ids, int64_t t, int64_t topk, void* y,

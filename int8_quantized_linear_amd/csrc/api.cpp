@@ -141,7 +141,7 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
   if (x_per_assignment != 0 && x_per_assignment != 1) return I8QL_ERR_ARG;
   if (topk < 1 || topk > 64 || num_experts < 1 || num_experts > kMaxGridY - 1) return I8QL_ERR_ARG;
   if (t < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
-  if (t * topk > 65536) return I8QL_ERR_SHAPE;
+  if (t * topk > 65536 || k > I8QL_GROUPED_MAX_K) return I8QL_ERR_SHAPE;
   if (!mul_ok(num_experts, n) || !mul_ok(num_experts * n, k) || !mul_ok(t * topk, k) ||
       !mul_ok(t * topk, n) || (n + 15) / 16 > kMaxGridX)
     return I8QL_ERR_SHAPE;

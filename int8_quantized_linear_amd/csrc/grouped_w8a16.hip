@@ -3,17 +3,21 @@
 // "Phase 5a: int8 weight-only quantization" (Summary) runs a mixture-of-experts block as a
 // single grouped GEMM over expert weights that are stacked into one tensor per projection,
 // with per-output-channel int8 codes.  Here the expert-grouped dispatch happens inside the
-// kernel: workgroup (tile, e) covers 16 output channels of expert e.  Wavefront 0 scans the
-// routing ids in order (loads batched, ballot + prefix popcount, so the row list is
-// deterministic) and
-// collects the assignments p = token * topk + slot routed to e into an LDS list; a
-// workgroup whose list is empty exits at once, so only the experts that received tokens
-// cost HBM bytes.  The listed rows are then processed in passes of up to 8: each pass
-// copies its (gathered) activation rows into LDS with direct-to-LDS loads issued ahead of
-// the weight loads, and runs the dense weight-only GEMM's inner loop (split-K across the
-// wavefronts, every weight load of a wave in flight at once, live-row-only fragment reads,
-// ordered reduction through LDS).  The extra row of workgroups (e == num_experts) collects
-// assignments whose id is outside [0, num_experts) and writes zeros for them.
+// kernel: workgroup (tile, slot) covers 16 output channels of one expert.  When there are at
+// least as many assignments as experts every expert gets a row of workgroups (slot = expert,
+// highest id first).  With fewer, most experts receive no token, so the grid has one row per
+// assignment only and a workgroup's expert is the slot-th largest id that occurs: every
+// workgroup marks the ids' experts in an LDS bitmap and picks from it, slots past the number
+// of distinct experts exit at once, and the picked expert's first batch of weight loads is
+// issued before the row scan.  Wavefront 0 scans the ids in order (ballot + prefix popcount,
+// so the row list is deterministic) and collects the assignments p = token * topk + slot
+// routed to the expert into an LDS list; a workgroup whose list is empty exits.  The listed
+// rows are then processed in passes of up to 8: each pass copies its (gathered) activation
+// rows into LDS with direct-to-LDS loads, and runs the dense weight-only GEMM's inner loop
+// (split-K across the wavefronts, every weight load of a wave in flight at once,
+// live-row-only fragment reads, ordered reduction through LDS).  The first row of
+// workgroups collects assignments whose id is outside [0, num_experts) and writes zeros for
+// them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,19 +30,76 @@ namespace {
 
 constexpr int kUnroll = 8;  // steps of k whose weight loads a wavefront keeps in flight
 constexpr int kList = 1024;     // assignments held in LDS per scan window
-constexpr int kScanBatch = 8;   // 64-id groups whose loads a scan keeps in flight together
+constexpr int kScanBatch = 8;   // 64-id groups whose loads a wavefront keeps in flight together
 constexpr int kMaxPassRows = 8;  // activation rows staged in LDS per pass
+constexpr size_t kMaxStageBytes = 128 * 1024;  // LDS for the staged rows of one pass
 
 template <int WAVES>
 constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * 64 * sizeof(v4f); }
 
 // Dynamic LDS: [WAVES][64] v4f partial tiles, the staged rows of one pass (pass_rows rows,
-// see stage_rows), a 16-byte zero block.
+// see stage_rows), a 16-byte zero block, the expert bitmap (one bit per expert, 16-byte
+// multiple).
 __host__ __device__ inline size_t xs_bytes(int pass_rows, int64_t k) {
   return 1024 * static_cast<size_t>(stage_insts(pass_rows, k)) + 16;
 }
+__host__ __device__ inline size_t bitmap_bytes(int64_t experts) {
+  return 16 * static_cast<size_t>((experts + 127) / 128);
+}
 
-template <int WAVES, int YT>
+// Ids [p, p + 64 * kScanBatch) for this lane, 64 apart: idv[j] = ids[p + 64 j + lane].
+// Groups that start past the end are not loaded (-1); lanes past the end of a partial group
+// re-read the last id and must be masked by the caller.
+__device__ __forceinline__ void load_id_batch(const int32_t* __restrict__ ids, int64_t total,
+                                              int64_t p, int lane,
+                                              int32_t (&idv)[kScanBatch]) {
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) {
+    idv[j] = -1;
+    if (p + 64 * j < total) {
+      const int64_t q = p + 64 * j + lane;
+      idv[j] = ids[q < total ? q : total - 1];
+    }
+  }
+}
+
+// The slot-th largest set bit of present[0, words) (wavefront-uniform), or -1 when fewer
+// bits are set.  Words are taken 64 at a time from the top; a prefix sum of their popcounts
+// across the lanes finds the word holding the bit.
+__device__ __forceinline__ int nth_present_from_top(const uint32_t* present, int words,
+                                                        int slot, int lane) {
+  int rem = slot;
+  for (int top = words - 1; top >= 0; top -= 64) {
+    const int w = top - lane;  // lane 0 holds the highest word of this group
+    const uint32_t bits = w >= 0 ? present[w] : 0u;
+    const int pc = __popc(bits);
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int in_group = __shfl(incl, 63);
+    if (rem < in_group) {
+      const uint64_t here = __ballot(incl > rem && incl - pc <= rem);
+      const int src = __ffsll(static_cast<unsigned long long>(here)) - 1;
+      int pick = -1;
+      if (lane == src) {
+        uint32_t b = bits;  // drop the set bits above the one wanted
+        for (int r = rem - (incl - pc); r > 0; --r) b &= ~(1u << (31 - __clz(static_cast<int>(b))));
+        pick = w * 32 + 31 - __clz(static_cast<int>(b));
+      }
+      return __shfl(pick, src);
+    }
+    rem -= in_group;
+  }
+  return -1;
+}
+
+// Workgroup: 16 output channels of one expert, split over WAVES wavefronts along k.  BITMAP:
+// the expert is the slot-th largest id present (fewer assignments than experts); otherwise
+// every expert has its own row of workgroups.
+template <int WAVES, bool BITMAP, int YT>
 __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
     const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
@@ -47,27 +108,87 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
   __shared__ int list[kList];
   __shared__ int s_count;
   __shared__ int64_t s_next;
+  __shared__ int64_t s_expert;
   v4f* red = reinterpret_cast<v4f*>(smem);
   char* xs = smem + red_bytes<WAVES>();
   char* xzero = xs + 1024 * stage_insts(pass_rows, k);
+  uint32_t* present = reinterpret_cast<uint32_t*>(xzero + 16);
 
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
-  // Expert blocks are dispatched from the highest id down: always-on shared experts are
-  // appended after the routed ones and receive every token, so they start first instead of
-  // forming the tail (T = 64, MoE 16B gate: 122 -> 94 us).  The extra invalid-id row comes
-  // first and normally exits at once.
-  const int64_t e = static_cast<int64_t>(gridDim.y) - 1 - blockIdx.y;
-  const bool invalid_row = (e == num_experts);
+  const bool invalid_row = blockIdx.y == 0;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
+
+  // Wavefront 0's first batch of ids, loaded once: the bitmap pass and the first window of
+  // the row scan both use it.
+  int32_t idv[kScanBatch];
+  bool idv_loaded = false;
+  int64_t e = num_experts;  // the invalid-id row matches ids outside [0, num_experts)
+  if constexpr (!BITMAP) {
+    // every expert has a row of workgroups, highest id first: the always-on shared experts
+    // are appended after the routed ones and receive every token, so they start first
+    // instead of forming the tail
+    if (!invalid_row) e = num_experts - static_cast<int64_t>(blockIdx.y);
+  } else if (!invalid_row) {
+    // ---- the expert of this slot: mark every expert named by an id, then pick ---------
+    const int words = static_cast<int>((num_experts + 31) / 32);
+    for (int i = threadIdx.x; i < words; i += 64 * WAVES) present[i] = 0u;
+    if (wave == 0) {
+      load_id_batch(ids, total, 0, lane, idv);
+      idv_loaded = true;
+    }
+    __syncthreads();  // the bitmap is clear
+    // 64-id groups: wavefront w marks groups w, w + WAVES, ..., kScanBatch loads in flight
+    const int64_t groups = (total + 63) / 64;
+    for (int64_t g0 = wave; g0 < groups; g0 += static_cast<int64_t>(WAVES) * kScanBatch) {
+      int32_t b[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        const int64_t g = g0 + static_cast<int64_t>(j) * WAVES;
+        const int64_t q = g * 64 + lane;
+        b[j] = g < groups ? ids[q < total ? q : total - 1] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        const int64_t q = (g0 + static_cast<int64_t>(j) * WAVES) * 64 + lane;
+        const int32_t id = b[j];
+        if (q < total && id >= 0 && id < num_experts)
+          atomicOr(present + (id >> 5), 1u << (id & 31));
+      }
+    }
+    __syncthreads();  // the bitmap is complete
+    if (wave == 0) {
+      // slots in decreasing id order, for the same reason as above
+      const int pick =
+          nth_present_from_top(present, words, static_cast<int>(blockIdx.y) - 1, lane);
+      if (lane == 0) s_expert = pick;
+    }
+    __syncthreads();
+    e = s_expert;
+    if (e < 0) return;  // fewer distinct experts than slots (uniform over the workgroup)
+  }
+
   // This lane's 4 output-channel scales (wavefront 0 applies them), requested before the
-  // scan so that their latency overlaps it.
+  // scan so that their latency overlaps it.  A picked expert has rows for certain, so its
+  // first batch of weight loads goes out before the scan too.
   const int64_t nc = n0 + 4 * (lane / 16);
   float sc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (wave == 0 && !invalid_row) {
+  const int64_t wr = min(n0 + lane % 16, n - 1);
+  const int8_t* wrow = wq + (invalid_row ? 0 : (e * n + wr) * k);
+  int sb, se;
+  wave_step_range(k, WAVES, wave, sb, se);
+  v4u w[kUnroll][2];
+  bool w_loaded = false;
+  if (!invalid_row && wave == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = w_scale[e * n + min(nc + r, n - 1)];
+  }
+  if (!invalid_row && BITMAP) {
+    load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+    w_loaded = true;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   int64_t p_next = 0;
@@ -81,15 +202,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
       int64_t p = p_next;
       bool full = false;
       while (p < total && !full) {
-        int32_t idv[kScanBatch];
-#pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) {
-          idv[j] = -1;
-          if (p + 64 * j < total) {  // groups past the end are neither loaded nor matched
-            const int64_t q = p + 64 * j + lane;
-            idv[j] = ids[q < total ? q : total - 1];
-          }
-        }
+        if (!(idv_loaded && p == 0)) load_id_batch(ids, total, p, lane, idv);
+        idv_loaded = false;
 #pragma unroll
         for (int j = 0; j < kScanBatch; ++j) {
           const int64_t mine = p + lane;
@@ -132,27 +246,27 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
         }
       }
     } else if (count > 0) {
-      const int64_t wr = min(n0 + lane % 16, n - 1);
-      const int8_t* wrow = wq + (e * n + wr) * k;
       const int64_t pitch = 2 * k + 16;
       const int div = x_per_assignment ? 1 : static_cast<int>(topk);
-      int sb, se;
-      wave_step_range(k, WAVES, wave, sb, se);
       for (int g = 0; g < count; g += pass_rows) {
-        // Activation rows of this pass first, then the first batch of weight loads (a later
-        // pass re-reads the same weights, from cache); wait for the rows only (the weight
-        // loads issued after them may stay in flight), then publish them to every
-        // wavefront.  The compiler barriers keep the weight loads behind the copy, which the
-        // wait count relies on.
+        // Activation rows of this pass, then (unless the first batch of weight loads is
+        // already in flight) the first batch of weight loads (a later pass re-reads the same
+        // weights, from cache); wait for the rows only (weight loads issued after them may
+        // stay in flight), then publish them to every wavefront.  The compiler barriers keep
+        // the weight loads behind the copy, which the wait count relies on.
         const int rows = min(pass_rows, count - g);
         stage_rows<WAVES>(x, list + g, div, rows, k, xs);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        v4u w[kUnroll][2];
-        load_weight_batch<kUnroll>(wrow, k, sb, se, w);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
+        if (w_loaded) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+          w_loaded = false;
+        } else {
+          load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
+        }
         bare_barrier();
         const char* xrow[1];
         bool live[1];
@@ -195,25 +309,43 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
   }
 }
 
+template <int WAVES, bool BITMAP, int YT>
+hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
+                       const float* w_scale, int64_t num_experts, const int32_t* ids,
+                       int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
+                       hipStream_t stream) {
+  auto kern = grouped_w8a16_kernel<WAVES, BITMAP, YT>;
+  // Rows staged per pass: an expert that each token picks at most once receives at most t
+  // rows; one that receives more takes more passes (any count is handled).  Long rows stage
+  // fewer per pass so that they fit the LDS budget (the caller bounds k so one row does).
+  int pass_rows = static_cast<int>(min(static_cast<int64_t>(kMaxPassRows), t));
+  while (pass_rows > 1 && xs_bytes(pass_rows, k) > kMaxStageBytes) --pass_rows;
+  const size_t lds = red_bytes<WAVES>() + xs_bytes(pass_rows, k) + bitmap_bytes(num_experts);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  // One row of workgroups per slot, after the row that handles invalid ids: one slot per
+  // expert, or, with fewer assignments than experts, one per assignment (the most distinct
+  // experts there can be).
+  const int64_t slots = BITMAP ? t * topk : num_experts;
+  const dim3 grid(static_cast<unsigned>((n + 15) / 16), static_cast<unsigned>(slots + 1));
+  hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, stream,
+                     static_cast<const uint16_t*>(x), x_per_assignment, wq, w_scale,
+                     num_experts, ids, t * topk, topk, y, n, k, pass_rows);
+  return hipGetLastError();
+}
+
 template <int WAVES, int YT>
 hipError_t launch_waves(const void* x, int x_per_assignment, const int8_t* wq,
                         const float* w_scale, int64_t num_experts, const int32_t* ids,
                         int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
                         hipStream_t stream) {
-  auto kern = grouped_w8a16_kernel<WAVES, YT>;
-  // Rows staged per pass: an expert that each token picks at most once receives at most t
-  // rows; one that receives more takes more passes (any count is handled).
-  const int pass_rows = static_cast<int>(min(static_cast<int64_t>(kMaxPassRows), t));
-  const size_t lds = red_bytes<WAVES>() + xs_bytes(pass_rows, k);
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>((n + 15) / 16), static_cast<unsigned>(num_experts + 1));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, stream,
-                     static_cast<const uint16_t*>(x), x_per_assignment, wq, w_scale,
-                     num_experts, ids, t * topk, topk, y, n, k, pass_rows);
-  return hipGetLastError();
+  if (t * topk < num_experts)
+    return launch_mode<WAVES, true, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                        topk, y, n, k, stream);
+  return launch_mode<WAVES, false, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                       topk, y, n, k, stream);
 }
 
 // Wavefronts per workgroup: the fewest of 1, 2, 4 and 8 with which each streams at most

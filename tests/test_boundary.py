@@ -192,6 +192,8 @@ def test_grouped_validation(lib):
     assert call(t=-1) == SHAPE
     assert call(t=8193, topk=8) == SHAPE
     assert call(k=0) == SHAPE
+    assert call(k=32768 + 16) == SHAPE   # past I8QL_GROUPED_MAX_K: one row no longer fits LDS
+    assert call(k=32768 + 16, t=0, x=NUL) == SHAPE
     assert call(t=0, x=NUL) == OK
     assert call(ids=NUL) == NULL
     assert call(x=NUL) == NULL

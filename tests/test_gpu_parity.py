@@ -494,6 +494,34 @@ def test_grouped_many_rows_per_expert(ref, dev):
     run_grouped(ref, dev, qw, sw, qwr, swr, ids, 700, False, torch.float32, g)
 
 
+def test_grouped_experts_picked_from_a_wide_bitmap(ref, dev):
+    """5000 experts: the presence bitmap spans 157 words, so a workgroup's expert is found in
+    the first, second or third group of 64 words; ids sit on word and group boundaries, next
+    to invalid ones, and several tokens share experts (fewer distinct experts than slots)."""
+    g = wl.rng(25)
+    e, n, k = 5000, 24, 128
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.array([[4999, 0, 31, 32, 2047],
+                    [2048, 4999, -3, 63, 64],
+                    [1, 4096, 4095, 5000, 0],
+                    [3000, 2, 4998, 1000, 31],
+                    [2047, 2048, 4064, 4063, 7]], dtype=np.int32)
+    for per_assign in (False, True):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, ids.size if per_assign else 5, per_assign,
+                    torch.float32, g)
+
+
+def test_grouped_every_slot_a_distinct_expert(ref, dev):
+    """As many distinct experts as assignments (every slot of the grid has an expert) and a
+    single token whose ids are all distinct."""
+    g = wl.rng(26)
+    e, n, k = 40, 56, 640
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    for t, topk in ((2, 6), (1, 8)):
+        ids = g.choice(e, t * topk, replace=False).astype(np.int32).reshape(t, topk)
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, t, False, torch.bfloat16, g)
+
+
 @pytest.mark.parametrize("t", wl.MOE_TOKENS)
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_grouped_moe_16b_full(ref, dev, t, proj):
