@@ -118,3 +118,10 @@ def moe_weights(g: np.random.Generator, n: int, k: int,
                 experts: int = MOE_ROUTED + MOE_SHARED) -> np.ndarray:
     """[experts, n, k] float32 ~ N(0, 0.02), to be cast to bf16 by the caller."""
     return (g.standard_normal((experts, n, k), dtype=np.float32) * np.float32(0.02))
+
+
+def router_logits(g: np.random.Generator, t: int, routed: int = MOE_ROUTED) -> np.ndarray:
+    """[t, routed] float32 router logits ~ N(0, 1): independent and identically distributed,
+    so the top-k experts are uniform over the routed ones, as the uniform-random expert ids
+    above are."""
+    return g.standard_normal((t, routed), dtype=np.float32)

@@ -10,7 +10,9 @@ which follow the pages:
 * "Phase 5a: int8 weight-only quantization", Summary (float32 quantizer arithmetic, the
   all-zero-channel guard, the grouped expert GEMM);
 * "feat(quantization): support compressed-tensors W8A8 and mixed modules", Design and
-  Supported Execution Scheme (per-channel weights, dynamic per-token activations).
+  Supported Execution Scheme (per-channel weights, dynamic per-token activations);
+* the mixture-of-experts block around the grouped GEMM (routing, SiLU·mul, combine), which
+  "Phase 5a" measures but no page spells out: readings stated in ``ref.c``.
 
 Parity pins: every function is pinned by ``tests/test_oracle_pins.py``; none is unpinned.
 """
@@ -59,6 +61,13 @@ class Oracle:
         lib.ref_grouped_w8a16.argtypes = [_P, ctypes.c_int, _P, _P, _I64, _P, _I64, _I64,
                                           _I64, _I64, _P]
         lib.ref_grouped_w8a16.restype = None
+        lib.ref_moe_route_topk.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
+        lib.ref_moe_route_topk.restype = None
+        lib.ref_grouped_w8a16_silu.argtypes = [_P, ctypes.c_int, _P, _P, _I64, _P, _I64, _I64,
+                                               _I64, _I64, _P]
+        lib.ref_grouped_w8a16_silu.restype = None
+        lib.ref_moe_combine.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+        lib.ref_moe_combine.restype = None
         lib.ref_set_threads.argtypes = [ctypes.c_int]
         lib.ref_get_threads.restype = ctypes.c_int
         self.lib = lib
@@ -139,6 +148,51 @@ class Oracle:
         self.lib.ref_grouped_w8a16(self._ptr(x), int(bool(x_per_assignment)), self._ptr(wq),
                                    self._ptr(sw), e, self._ptr(ids), t, topk, n, k,
                                    self._ptr(y))
+        return y
+
+
+    # -- mixture-of-experts steps around the grouped GEMM (readings stated in ref.c) -----
+    def moe_route_topk(self, logits, k_routed: int, n_shared: int):
+        """``(ids int32 [t, k_routed + n_shared], weights float64 [t, ...])`` from float32
+        router logits ``[t, e_routed]``: softmax, the k_routed largest kept by decreasing
+        logit (lower index first on ties), shared experts appended with weight 1."""
+        lg = np.ascontiguousarray(logits, np.float32)
+        t, e_routed = lg.shape
+        kk = k_routed + n_shared
+        ids = np.empty((t, kk), np.int32)
+        w = np.empty((t, kk), np.float64)
+        self.lib.ref_moe_route_topk(self._ptr(lg), t, e_routed, k_routed, n_shared,
+                                    self._ptr(ids), self._ptr(w))
+        return ids, w
+
+    def grouped_w8a16_silu(self, x_bf16_bits, x_per_assignment, wq, w_scale, expert_ids):
+        """float64 ``silu(gate) * up`` per assignment; ``wq`` is ``[e, 2n, k]`` with each
+        expert's gate rows before its up rows."""
+        x = np.ascontiguousarray(x_bf16_bits, np.uint16)
+        wq = np.ascontiguousarray(wq, np.int8)
+        sw = np.ascontiguousarray(w_scale, np.float32)
+        ids = np.ascontiguousarray(expert_ids, np.int32)
+        e, n2, k = wq.shape
+        assert n2 % 2 == 0
+        n = n2 // 2
+        t, topk = ids.shape
+        assert x.shape[1] == k
+        assert x.shape[0] == (t * topk if x_per_assignment else t)
+        h = np.empty((t * topk, n), np.float64)
+        self.lib.ref_grouped_w8a16_silu(self._ptr(x), int(bool(x_per_assignment)),
+                                        self._ptr(wq), self._ptr(sw), e, self._ptr(ids), t,
+                                        topk, n, k, self._ptr(h))
+        return h
+
+    def moe_combine(self, d, weights):
+        """float64 ``y[i] = sum_j weights[i, j] * d[i * topk + j]`` (``d`` float32 values)."""
+        dd = np.ascontiguousarray(d, np.float32)
+        w = np.ascontiguousarray(weights, np.float32)
+        t, topk = w.shape
+        assert dd.shape[0] == t * topk
+        n = dd.shape[1]
+        y = np.empty((t, n), np.float64)
+        self.lib.ref_moe_combine(self._ptr(dd), self._ptr(w), t, topk, n, self._ptr(y))
         return y
 
 

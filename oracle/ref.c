@@ -212,3 +212,98 @@ void ref_grouped_w8a16(const uint16_t* x, int x_per_assignment, const int8_t* wq
     }
   }
 }
+
+/* ---- the steps around the grouped GEMM in a mixture-of-experts block ------------------- */
+
+/*
+ * "Phase 5a: int8 weight-only quantization" (Summary) measures the grouped GEMM inside the
+ * mixture-of-experts block of deepseek-moe-16b, but no page spells out the block's other
+ * steps.  The three functions below take the plainest reading that the rest supports:
+ *   routing  — softmax over the routed experts' logits; the k_routed largest probabilities
+ *              (equivalently logits) are kept, unrenormalized, as the routing weights; equal
+ *              logits go to the lower expert index first; the always-on shared experts are
+ *              appended after them (ids e_routed .. e_routed + n_shared - 1, weight 1);
+ *   SiLU·mul — between the gate/up projections and the down projection,
+ *              h = silu(gate) * up with silu(v) = v / (1 + exp(-v));
+ *   combine  — each token's output is the routing-weighted sum of its assignments' rows.
+ * Everything is computed in double.
+ */
+
+/* Routing.  logits: [t, e_routed] float32; ids: [t, k_routed + n_shared]; w: same, double.
+ * Slots hold the selected experts by decreasing logit (ties: lower index first). */
+void ref_moe_route_topk(const float* logits, int64_t t, int64_t e_routed, int64_t k_routed,
+                        int64_t n_shared, int32_t* ids, double* w) {
+  const int64_t kk = k_routed + n_shared;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < t; ++i) {
+    const float* l = logits + i * e_routed;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < e_routed; ++j)
+      if ((double)l[j] > mx) mx = (double)l[j];
+    double den = 0.0;
+    for (int64_t j = 0; j < e_routed; ++j) den += exp((double)l[j] - mx);
+    /* selection: k_routed times, the largest logit not taken yet (first index on ties) */
+    for (int64_t s = 0; s < k_routed; ++s) {
+      int64_t best = -1;
+      for (int64_t j = 0; j < e_routed; ++j) {
+        int taken = 0;
+        for (int64_t u = 0; u < s; ++u)
+          if (ids[i * kk + u] == (int32_t)j) taken = 1;
+        if (taken) continue;
+        if (best < 0 || l[j] > l[best]) best = j;
+      }
+      ids[i * kk + s] = (int32_t)best;
+      w[i * kk + s] = exp((double)l[best] - mx) / den;
+    }
+    for (int64_t s = 0; s < n_shared; ++s) {
+      ids[i * kk + k_routed + s] = (int32_t)(e_routed + s);
+      w[i * kk + k_routed + s] = 1.0;
+    }
+  }
+}
+
+/* SiLU·mul after a grouped gate/up product: wq is [e, 2n, k] with the gate rows of each
+ * expert first and its up rows after them, w_scale [e, 2n].  h: [t * topk, n] double,
+ * h = silu(gate) * up of the exact double products (zero rows for invalid ids). */
+void ref_grouped_w8a16_silu(const uint16_t* x, int x_per_assignment, const int8_t* wq,
+                            const float* w_scale, int64_t e, const int32_t* ids, int64_t t,
+                            int64_t topk, int64_t n, int64_t k, double* h) {
+  const int64_t rows = t * topk;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < rows; ++p) {
+    const int64_t tok = p / topk;
+    const int32_t ex = ids[p];
+    const uint16_t* xr = x + (x_per_assignment ? p : tok) * k;
+    for (int64_t j = 0; j < n; ++j) {
+      if (ex < 0 || ex >= e) {
+        h[p * n + j] = 0.0;
+        continue;
+      }
+      const int8_t* wg = wq + ((int64_t)ex * 2 * n + j) * k;
+      const int8_t* wu = wq + ((int64_t)ex * 2 * n + n + j) * k;
+      double sg = 0.0, su = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        const double xv = (double)bf16_to_f32(xr[c]);
+        sg += xv * (double)wg[c];
+        su += xv * (double)wu[c];
+      }
+      const double g = (double)w_scale[(int64_t)ex * 2 * n + j] * sg;
+      const double u = (double)w_scale[(int64_t)ex * 2 * n + n + j] * su;
+      h[p * n + j] = g / (1.0 + exp(-g)) * u;
+    }
+  }
+}
+
+/* Combine: y[i, c] = sum_j w[i, j] * d[i * topk + j, c].  d: [t * topk, n] float32 values;
+ * w: [t, topk]; y: [t, n] double. */
+void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, int64_t n,
+                     double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < t; ++i)
+    for (int64_t c = 0; c < n; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < topk; ++j)
+        acc += (double)w[i * topk + j] * (double)d[(i * topk + j) * n + c];
+      y[i * n + c] = acc;
+    }
+}

@@ -47,6 +47,16 @@ void ref_grouped_w8a16(const uint16_t* x, int x_per_assignment, const int8_t* wq
                        const float* w_scale, int64_t e, const int32_t* ids, int64_t t,
                        int64_t topk, int64_t n, int64_t k, double* y);
 
+/* Mixture-of-experts steps around the grouped GEMM ([P5a] Summary names the block; its
+ * routing, activation and combine are readings, stated in ref.c). */
+void ref_moe_route_topk(const float* logits, int64_t t, int64_t e_routed, int64_t k_routed,
+                        int64_t n_shared, int32_t* ids, double* w);
+void ref_grouped_w8a16_silu(const uint16_t* x, int x_per_assignment, const int8_t* wq,
+                            const float* w_scale, int64_t e, const int32_t* ids, int64_t t,
+                            int64_t topk, int64_t n, int64_t k, double* h);
+void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, int64_t n,
+                     double* y);
+
 #ifdef __cplusplus
 }
 #endif

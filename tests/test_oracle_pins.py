@@ -10,7 +10,9 @@ that the pins must reject.  Pages cited by title and section:
 * "Phase 5a: int8 weight-only quantization", Summary (float32 arithmetic fix with its
   "1.5x the ideal bound", the all-zero-channel guard fix, 49.89% expert memory reduction);
 * "feat(quantization): support compressed-tensors W8A8 and mixed modules", Design and
-  Supported Execution Scheme (per-channel weights, per-token activations).
+  Supported Execution Scheme (per-channel weights, per-token activations);
+* the mixture-of-experts block of "Phase 5a" around its grouped GEMM (routing, SiLU·mul,
+  combine: readings, pinned against scipy's softmax/expit, brute-force sorting and einsum).
 """
 import json
 import os
@@ -406,3 +408,122 @@ def test_p11_grouped_token_permutation(ref):
     y = ref.grouped_w8a16(x, 0, q, s, ids).reshape(t, topk, n)
     yp = ref.grouped_w8a16(x[perm], 0, q, s, ids[perm]).reshape(t, topk, n)
     np.testing.assert_array_equal(yp, y[perm])
+
+
+# ---------------------------------------------------------------------------------------
+# P12–P14 the mixture-of-experts steps around the grouped GEMM.  "Phase 5a: int8 weight-only
+# quantization" (Summary) measures the block but does not spell these steps out; the
+# readings (softmax top-k routing with unrenormalized weights and shared experts appended,
+# h = silu(gate) * up, routing-weighted combine) are pinned here against independent
+# definitions: brute-force sorting, scipy's softmax and expit, numpy einsum.
+
+def _route_brute(logits, k_routed, n_shared):
+    from scipy.special import softmax
+    t, e = logits.shape
+    ids = np.empty((t, k_routed + n_shared), np.int64)
+    w = np.empty((t, k_routed + n_shared))
+    for i in range(t):
+        order = sorted(range(e), key=lambda j: (-float(logits[i, j]), j))[:k_routed]
+        p = softmax(logits[i].astype(np.float64))
+        ids[i, :k_routed] = order
+        w[i, :k_routed] = p[order]
+        ids[i, k_routed:] = np.arange(e, e + n_shared)
+        w[i, k_routed:] = 1.0
+    return ids, w
+
+
+@pytest.mark.parametrize("t,e,k,ns", [(9, 64, 6, 2), (3, 5, 5, 0), (4, 200, 17, 3), (1, 1, 1, 1)])
+def test_p12_routing_is_softmax_top_k(ref, t, e, k, ns):
+    g = wl.rng(60 + e)
+    logits = g.standard_normal((t, e), dtype=np.float32) * np.float32(2.0)
+    ids, w = ref.moe_route_topk(logits, k, ns)
+    bids, bw = _route_brute(logits, k, ns)
+    np.testing.assert_array_equal(ids, bids)
+    np.testing.assert_allclose(w, bw, rtol=1e-13, atol=0)
+
+
+def test_p12_routing_ties_shift_and_shared(ref):
+    # equal logits: the lower index first, every weight 1/e
+    ids, w = ref.moe_route_topk(np.zeros((2, 64), np.float32), 6, 2)
+    assert ids.tolist() == [[0, 1, 2, 3, 4, 5, 64, 65]] * 2
+    np.testing.assert_allclose(w[:, :6], 1.0 / 64, rtol=1e-15)
+    assert np.all(w[:, 6:] == 1.0)
+    # ties inside the selection and at its boundary
+    l = np.array([[1, 3, 3, 2, 3, 2, 0]], np.float32)
+    ids, _ = ref.moe_route_topk(l, 4, 0)
+    assert ids.tolist() == [[1, 2, 4, 3]]
+    # softmax is shift invariant: integer logits (exact in float32) moved by 7
+    g = wl.rng(64)
+    li = g.integers(-20, 20, size=(5, 64)).astype(np.float32)
+    a_ids, a_w = ref.moe_route_topk(li, 6, 2)
+    b_ids, b_w = ref.moe_route_topk(li + np.float32(7), 6, 2)
+    np.testing.assert_array_equal(a_ids, b_ids)
+    np.testing.assert_allclose(a_w, b_w, rtol=1e-13)
+    # the routed weights are probabilities of distinct experts: positive, summing below 1
+    assert np.all(a_w[:, :6] > 0) and np.all(a_w[:, :6].sum(axis=1) <= 1.0 + 1e-15)
+    assert all(len(set(r)) == len(r) for r in a_ids.tolist())
+
+
+def _silu_case(ref, g, e, n, k):
+    wf = wl.moe_weights(g, 2 * n, k, experts=e)
+    q, s = ref.quantize_rows(wl.bits16(wl.to_bf16(wf.reshape(e * 2 * n, k))), "bf16")
+    return q.reshape(e, 2 * n, k), s.reshape(e, 2 * n)
+
+
+def test_p13_silu_mul_of_the_gate_and_up_products(ref):
+    from scipy.special import expit
+    g = wl.rng(65)
+    e, n, k, t, topk = 6, 24, 192, 7, 3
+    q, s = _silu_case(ref, g, e, n, k)
+    ids = np.stack([g.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    ids[3, 2] = e   # invalid: zero row
+    for per_assign in (0, 1):
+        x = wl.bits16(wl.to_bf16(wl.activations(g, t * topk if per_assign else t, k)))
+        h = ref.grouped_w8a16_silu(x, per_assign, q, s, ids)
+        gate = ref.grouped_w8a16(x, per_assign, q[:, :n], s[:, :n], ids)
+        up = ref.grouped_w8a16(x, per_assign, q[:, n:], s[:, n:], ids)
+        want = gate * expit(gate) * up
+        np.testing.assert_allclose(h, want, rtol=1e-12, atol=1e-15)
+        assert np.all(h[3 * topk + 2] == 0.0)
+        # swapping the halves (up as gate) is a different function: the layout is pinned
+        swapped = up * expit(up) * gate
+        assert np.max(np.abs(swapped - h)) > 1e-3 * np.max(np.abs(h))
+
+
+def test_p13_silu_special_values(ref):
+    g = wl.rng(66)
+    e, n, k, t = 2, 16, 64, 3
+    q, s = _silu_case(ref, g, e, n, k)
+    ids = np.zeros((t, 1), np.int32)
+    x = wl.bits16(wl.to_bf16(wl.activations(g, t, k)))
+    # a zero gate row: silu(0) = 0 exactly, whatever the up row
+    qz = q.copy()
+    qz[0, 5] = 0
+    h = ref.grouped_w8a16_silu(x, 0, qz, s, ids)
+    assert np.all(h[:, 5] == 0.0)
+    # odd part: silu(-v) = silu(v) - v, so negating the gate codes gives (silu(v) - v) * up
+    qn = q.copy()
+    qn[0, :n] = -qn[0, :n]
+    hp = ref.grouped_w8a16_silu(x, 0, q, s, ids)
+    hn = ref.grouped_w8a16_silu(x, 0, qn, s, ids)
+    gate = ref.grouped_w8a16(x, 0, q[:, :n], s[:, :n], ids)
+    up = ref.grouped_w8a16(x, 0, q[:, n:], s[:, n:], ids)
+    np.testing.assert_allclose(hn, hp - gate * up, rtol=1e-10, atol=1e-14)
+
+
+def test_p14_combine_is_the_weighted_sum(ref):
+    g = wl.rng(67)
+    t, topk, n = 5, 8, 96
+    d = g.standard_normal((t * topk, n), dtype=np.float32)
+    w = g.random((t, topk), dtype=np.float32)
+    y = ref.moe_combine(d, w)
+    want = np.einsum("tj,tjc->tc", w.astype(np.float64),
+                     d.reshape(t, topk, n).astype(np.float64))
+    np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-14)
+    # one-hot weights pick the slot's row exactly; the wrong slot would be visible
+    oh = np.zeros((t, topk), np.float32)
+    oh[np.arange(t), np.arange(t) % topk] = 1.0
+    y1 = ref.moe_combine(d, oh)
+    for i in range(t):
+        np.testing.assert_array_equal(y1[i], d[i * topk + i % topk].astype(np.float64))
+        assert not np.array_equal(y1[i], d[i * topk + (i + 1) % topk].astype(np.float64))
