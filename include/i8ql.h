@@ -214,6 +214,72 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
                                const int32_t* expert_ids, int64_t t, int64_t topk, void* y,
                                i8ql_dtype y_dtype, int64_t n, int64_t k, void* stream);
 
+/*
+ * The mixture-of-experts steps on either side of grouped_w8a16_gemm.  [P5a] Summary runs the
+ * grouped GEMM inside the mixture-of-experts block of deepseek-moe-16b but does not spell out
+ * the block's routing, activation or combine; these entry points take the plainest reading
+ * (softmax top-k routing with unrenormalized weights and shared experts appended; SiLU·mul
+ * between the gate/up and down projections; a routing-weighted sum of each token's rows).
+ */
+
+#define I8QL_ROUTE_MAX_EXPERTS 256
+#define I8QL_ROUTE_MAX_K 32
+
+/*
+ * moe_route_topk — top-k routing from router logits.
+ *
+ * For token i: p = softmax(logits[i, :]) over the e_routed routed experts; slots
+ * 0 .. k_routed - 1 hold the k_routed experts with the largest logits in decreasing order
+ * (equal logits: lower expert index first) with weights p of those experts (not
+ * renormalized); slots k_routed .. k_routed + n_shared - 1 hold the shared experts
+ * e_routed .. e_routed + n_shared - 1 with weight 1.  The ids feed grouped_w8a16_gemm (with
+ * num_experts = e_routed + n_shared) and the weights moe_combine.  Float32 arithmetic; the
+ * ids are decided by exact comparisons of the logits.
+ *
+ * logits   device, [t, e_routed] of logits_dtype in {I8QL_F32, I8QL_BF16}; finite values.
+ * ids      device, [t, k_routed + n_shared] int32.
+ * weights  device, [t, k_routed + n_shared] float32.
+ * 1 <= e_routed <= I8QL_ROUTE_MAX_EXPERTS; 1 <= k_routed <= min(e_routed, I8QL_ROUTE_MAX_K);
+ * 0 <= n_shared <= I8QL_ROUTE_MAX_K; k_routed + n_shared <= 64; t >= 0.
+ * Errors: dtype -> I8QL_ERR_DTYPE; t < 0 -> I8QL_ERR_SHAPE; the expert counts out of range
+ * -> I8QL_ERR_ARG; NULL -> I8QL_ERR_NULL; misaligned element pointers -> I8QL_ERR_ALIGN.
+ */
+i8ql_status moe_route_topk(const void* logits, i8ql_dtype logits_dtype, int64_t t,
+                           int64_t e_routed, int64_t k_routed, int64_t n_shared, int32_t* ids,
+                           float* weights, void* stream);
+
+/*
+ * grouped_w8a16_silu_gemm — the gate and up projections of the experts as one grouped
+ * weight-only GEMM with the SiLU·mul fused into its epilogue.
+ *
+ * Each expert's weights are stacked [2n, k]: rows 0 .. n-1 are the gate projection, rows
+ * n .. 2n-1 the up projection (w_scale likewise [num_experts, 2n]).  For assignment p routed
+ * to a valid expert: g = grouped_w8a16_gemm's value of gate row c, u = that of up row c,
+ * h[p, c] = g / (1 + exp(-g)) * u (float32), stored as float32 or rne bfloat16; rows of
+ * invalid ids are 0.  Everything else (x, x_per_assignment, expert_ids, t, topk, k, limits,
+ * errors) as for grouped_w8a16_gemm, with wq [num_experts, 2n, k] and h [t * topk, n].
+ */
+i8ql_status grouped_w8a16_silu_gemm(const void* x, int x_per_assignment, const int8_t* wq,
+                                    const float* w_scale, int64_t num_experts,
+                                    const int32_t* expert_ids, int64_t t, int64_t topk, void* h,
+                                    i8ql_dtype h_dtype, int64_t n, int64_t k, void* stream);
+
+/*
+ * moe_combine — the routing-weighted sum of each token's assignment rows:
+ *   y[i, c] = sum_j weights[i, j] * d[i * topk + j, c],  j = 0 .. topk-1 in order, float32.
+ *
+ * d        device, [t * topk, n] of d_dtype in {I8QL_BF16, I8QL_F32} (e.g. the down
+ *          projection's grouped_w8a16_gemm output).
+ * weights  device, [t, topk] float32 (e.g. from moe_route_topk).
+ * y        device, [t, n] of y_dtype in {I8QL_BF16, I8QL_F32}; must not alias d.
+ * 1 <= topk <= 64; t, n >= 0.  Rows that are 16-byte aligned whole chunks take 16-byte
+ * accesses, any other layout the element path.
+ * Errors: dtype -> I8QL_ERR_DTYPE; topk -> I8QL_ERR_ARG; negative or too large t, n ->
+ * I8QL_ERR_SHAPE; NULL -> I8QL_ERR_NULL; misaligned element pointers -> I8QL_ERR_ALIGN.
+ */
+i8ql_status moe_combine(const void* d, i8ql_dtype d_dtype, const float* weights, int64_t t,
+                        int64_t topk, int64_t n, void* y, i8ql_dtype y_dtype, void* stream);
+
 /* Host: a static, human-readable name for a status code ("I8QL_OK", ...). */
 const char* i8ql_status_string(i8ql_status s);
 

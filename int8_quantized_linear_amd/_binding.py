@@ -21,7 +21,9 @@ _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8Q
           torch.int8: I8QL_I8, torch.int32: I8QL_I32}
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
-           "w8a8_gemm_with_config", "i8ql_status_string", "i8ql_last_hip_error")
+           "w8a8_gemm_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
+           "moe_combine", "i8ql_status_string", "i8ql_last_hip_error")
+ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
 W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 
 
@@ -61,6 +63,13 @@ def load_library(path: str = LIB_PATH):
         lib.w8a16_gemm.restype = I
         lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
         lib.grouped_w8a16_gemm.restype = I
+        lib.grouped_w8a16_silu_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64,
+                                                P]
+        lib.grouped_w8a16_silu_gemm.restype = I
+        lib.moe_route_topk.argtypes = [P, I, I64, I64, I64, I64, P, P, P]
+        lib.moe_route_topk.restype = I
+        lib.moe_combine.argtypes = [P, I, P, I64, I64, I64, P, I, P]
+        lib.moe_combine.restype = I
         lib.i8ql_status_string.argtypes = [I]
         lib.i8ql_status_string.restype = ctypes.c_char_p
         lib.i8ql_last_hip_error.argtypes = []
@@ -220,4 +229,63 @@ def grouped_w8a16_gemm(x, wq, w_scale, expert_ids, x_per_assignment=False,
         _call("grouped_w8a16_gemm", _ptr(x), int(bool(x_per_assignment)), _ptr(wq),
               _ptr(w_scale), e, _ptr(expert_ids), t, topk, _ptr(y), _DTYPE[out_dtype], n, k,
               _stream(dev))
+    return y
+
+
+def grouped_w8a16_silu_gemm(x, wq, w_scale, expert_ids, x_per_assignment=False,
+                            out_dtype=torch.bfloat16, out=None):
+    """Gate and up projections of the experts with SiLU·mul fused: ``wq`` [E, 2N, K] (gate
+    rows, then up rows, per expert), ``w_scale`` [E, 2N] -> ``silu(gate) * up`` [T*topk, N]."""
+    _check(x, "x", (torch.bfloat16,), 2)
+    dev = x.device
+    _check(wq, "wq", (torch.int8,), 3, dev)
+    _check(w_scale, "w_scale", (torch.float32,), 2, dev)
+    _check(expert_ids, "expert_ids", (torch.int32,), 2, dev)
+    e, n2, k = wq.shape
+    if n2 % 2:
+        raise ValueError("wq must stack gate and up rows: an even number of rows per expert")
+    n = n2 // 2
+    t, topk = expert_ids.shape
+    if tuple(w_scale.shape) != (e, n2) or x.shape[1] != k:
+        raise ValueError("x, wq and w_scale disagree")
+    if x.shape[0] != (t * topk if x_per_assignment else t):
+        raise ValueError("x has the wrong number of rows for x_per_assignment")
+    h = _out(out, (t * topk, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("grouped_w8a16_silu_gemm", _ptr(x), int(bool(x_per_assignment)), _ptr(wq),
+              _ptr(w_scale), e, _ptr(expert_ids), t, topk, _ptr(h), _DTYPE[out_dtype], n, k,
+              _stream(dev))
+    return h
+
+
+def moe_route_topk(logits, k_routed, n_shared=0, ids_out=None, weights_out=None):
+    """Top-k routing: ``logits`` [T, E] fp32/bf16 -> (ids int32 [T, k+shared], weights fp32
+    [T, k+shared]); softmax weights of the k largest logits, shared experts E.. appended with
+    weight 1."""
+    _check(logits, "logits", (torch.float32, torch.bfloat16), 2)
+    dev = logits.device
+    t, e = logits.shape
+    kk = k_routed + n_shared
+    ids = _out(ids_out, (t, kk), torch.int32, dev)
+    w = _out(weights_out, (t, kk), torch.float32, dev)
+    with torch.cuda.device(dev):
+        _call("moe_route_topk", _ptr(logits), _DTYPE[logits.dtype], t, e, k_routed, n_shared,
+              _ptr(ids), _ptr(w), _stream(dev))
+    return ids, w
+
+
+def moe_combine(d, weights, out_dtype=torch.bfloat16, out=None):
+    """Routing-weighted combine: ``d`` [T*topk, N] bf16/fp32, ``weights`` [T, topk] fp32 ->
+    ``y[i] = sum_j weights[i, j] * d[i*topk + j]`` [T, N]."""
+    _check(d, "d", (torch.bfloat16, torch.float32), 2)
+    dev = d.device
+    _check(weights, "weights", (torch.float32,), 2, dev)
+    t, topk = weights.shape
+    if d.shape[0] != t * topk:
+        raise ValueError("d must have t * topk rows")
+    n = d.shape[1]
+    y = _out(out, (t, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("moe_combine", _ptr(d), _DTYPE[d.dtype], _ptr(weights), t, topk, n, _ptr(y),
+              _DTYPE[out_dtype], _stream(dev))
     return y

@@ -25,7 +25,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
 SOURCES = ["api.cpp", "quantize_rows.hip", "w8a8_gemm.hip", "w8a16_gemm.hip",
-           "grouped_w8a16.hip"]
+           "grouped_w8a16.hip", "moe_steps.hip"]
 
 
 def _compile(src: str) -> str:

@@ -156,6 +156,64 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
                                                     static_cast<hipStream_t>(stream)));
 }
 
+i8ql_status grouped_w8a16_silu_gemm(const void* x, int x_per_assignment, const int8_t* wq,
+                                    const float* w_scale, int64_t num_experts,
+                                    const int32_t* expert_ids, int64_t t, int64_t topk, void* h,
+                                    i8ql_dtype h_dtype, int64_t n, int64_t k, void* stream) {
+  if (h_dtype != I8QL_BF16 && h_dtype != I8QL_F32) return I8QL_ERR_DTYPE;
+  if (x_per_assignment != 0 && x_per_assignment != 1) return I8QL_ERR_ARG;
+  if (topk < 1 || topk > 64 || num_experts < 1 || num_experts > kMaxGridY - 1) return I8QL_ERR_ARG;
+  if (t < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
+  if (t * topk > 65536 || k > I8QL_GROUPED_MAX_K) return I8QL_ERR_SHAPE;
+  if (!mul_ok(num_experts, 2 * n) || !mul_ok(num_experts * 2 * n, k) || !mul_ok(t * topk, k) ||
+      !mul_ok(t * topk, n) || (n + 15) / 16 > kMaxGridX)
+    return I8QL_ERR_SHAPE;
+  if (t == 0 || n == 0) return I8QL_OK;
+  if (!x || !wq || !w_scale || !expert_ids || !h) return I8QL_ERR_NULL;
+  if (k % 16 != 0 || !aligned(x, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(h, elem_bytes(h_dtype)) || !aligned(w_scale, 4) || !aligned(expert_ids, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_grouped_w8a16_silu_gemm(
+      x, x_per_assignment, wq, w_scale, num_experts, expert_ids, t, topk, h, h_dtype, n, k,
+      static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status moe_route_topk(const void* logits, i8ql_dtype logits_dtype, int64_t t,
+                           int64_t e_routed, int64_t k_routed, int64_t n_shared, int32_t* ids,
+                           float* weights, void* stream) {
+  if (logits_dtype != I8QL_F32 && logits_dtype != I8QL_BF16) return I8QL_ERR_DTYPE;
+  if (t < 0 || t > kMaxGridX) return I8QL_ERR_SHAPE;
+  if (e_routed < 1 || e_routed > I8QL_ROUTE_MAX_EXPERTS || k_routed < 1 ||
+      k_routed > I8QL_ROUTE_MAX_K || k_routed > e_routed || n_shared < 0 ||
+      n_shared > I8QL_ROUTE_MAX_K || k_routed + n_shared > 64)
+    return I8QL_ERR_ARG;
+  if (!mul_ok(t, e_routed) || !mul_ok(t, k_routed + n_shared)) return I8QL_ERR_SHAPE;
+  if (t == 0) return I8QL_OK;
+  if (!logits || !ids || !weights) return I8QL_ERR_NULL;
+  if (!aligned(logits, elem_bytes(logits_dtype)) || !aligned(ids, 4) || !aligned(weights, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_moe_route_topk(logits, logits_dtype, t, e_routed, k_routed,
+                                                n_shared, ids, weights,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status moe_combine(const void* d, i8ql_dtype d_dtype, const float* weights, int64_t t,
+                        int64_t topk, int64_t n, void* y, i8ql_dtype y_dtype, void* stream) {
+  if ((d_dtype != I8QL_BF16 && d_dtype != I8QL_F32) ||
+      (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32))
+    return I8QL_ERR_DTYPE;
+  if (topk < 1 || topk > 64) return I8QL_ERR_ARG;
+  if (t < 0 || n < 0 || t > kMaxGridX || (n + 255) / 256 > kMaxGridY) return I8QL_ERR_SHAPE;
+  if (!mul_ok(t * topk, n)) return I8QL_ERR_SHAPE;
+  if (t == 0 || n == 0) return I8QL_OK;
+  if (!d || !weights || !y) return I8QL_ERR_NULL;
+  if (!aligned(d, elem_bytes(d_dtype)) || !aligned(y, elem_bytes(y_dtype)) ||
+      !aligned(weights, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_moe_combine(d, d_dtype, weights, t, topk, n, y, y_dtype,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 const char* i8ql_status_string(i8ql_status s) {
   switch (s) {
     case I8QL_OK: return "I8QL_OK";

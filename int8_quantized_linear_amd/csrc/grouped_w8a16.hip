@@ -17,7 +17,10 @@
 // (split-K across the wavefronts, every weight load of a wave in flight at once,
 // live-row-only fragment reads, ordered reduction through LDS).  The first row of
 // workgroups collects assignments whose id is outside [0, num_experts) and writes zeros for
-// them.
+// them.  A second entry point fuses the SiLU·mul between the gate/up and down projections of
+// the mixture-of-experts block: gate and up are one call over weights stacked [2n, k] per
+// expert, each workgroup computes 16 gate and the 16 matching up channels and stores
+// silu(gate) * up (the block's activation step is a reading: no page spells it out).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,14 +99,18 @@ __device__ __forceinline__ int nth_present_from_top(const uint32_t* present, int
   return -1;
 }
 
-// Workgroup: 16 output channels of one expert, split over WAVES wavefronts along k.  BITMAP:
+// Workgroup: 16 output channels of one expert, split over KS wavefronts along k.  BITMAP:
 // the expert is the slot-th largest id present (fewer assignments than experts); otherwise
-// every expert has its own row of workgroups.
-template <int WAVES, bool BITMAP, int YT>
-__global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
+// every expert has its own row of workgroups.  SILU: each expert's weights are [2n, k], gate
+// rows then up rows; the workgroup computes the 16 gate channels with wavefronts [0, KS) and
+// the 16 matching up channels with [KS, 2 KS), and stores silu(gate) * up.
+template <int KS, bool BITMAP, bool SILU, int YT>
+__global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel(
     const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
     int64_t total, int64_t topk, void* __restrict__ y, int64_t n, int64_t k, int pass_rows) {
+  constexpr int TILES = SILU ? 2 : 1;
+  constexpr int WAVES = KS * TILES;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int list[kList];
   __shared__ int s_count;
@@ -173,16 +180,21 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
   // scan so that their latency overlaps it.  A picked expert has rows for certain, so its
   // first batch of weight loads goes out before the scan too.
   const int64_t nc = n0 + 4 * (lane / 16);
-  float sc[4] = {0.f, 0.f, 0.f, 0.f};
+  // Weight rows per expert: TILES * n; this wavefront's tile (0: the channels themselves or
+  // the gate rows, 1: the up rows) starts at row tile * n of its expert.
+  const int tile = wave / KS;
+  float sc[TILES][4] = {};
   const int64_t wr = min(n0 + lane % 16, n - 1);
-  const int8_t* wrow = wq + (invalid_row ? 0 : (e * n + wr) * k);
+  const int8_t* wrow = wq + (invalid_row ? 0 : ((e * TILES + tile) * n + wr) * k);
   int sb, se;
-  wave_step_range(k, WAVES, wave, sb, se);
+  wave_step_range(k, KS, wave % KS, sb, se);
   v4u w[kUnroll][2];
   bool w_loaded = false;
   if (!invalid_row && wave == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = w_scale[e * n + min(nc + r, n - 1)];
+    for (int ti = 0; ti < TILES; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[ti][r] = w_scale[(e * TILES + ti) * n + min(nc + r, n - 1)];
   }
   if (!invalid_row && BITMAP) {
     load_weight_batch<kUnroll>(wrow, k, sb, se, w);
@@ -285,15 +297,23 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
         red[wave * 64 + lane] = acc[0];
         __syncthreads();
         if (wave == 0 && lane % 16 < rows) {
-          v4f sum = red[lane];
+          v4f sum[TILES];
 #pragma unroll
-          for (int w2 = 1; w2 < WAVES; ++w2) sum += red[w2 * 64 + lane];
+          for (int ti = 0; ti < TILES; ++ti) {
+            sum[ti] = red[ti * KS * 64 + lane];
+#pragma unroll
+            for (int w2 = 1; w2 < KS; ++w2) sum[ti] += red[(ti * KS + w2) * 64 + lane];
+          }
           const int64_t row = list[g + lane % 16];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t c = nc + r;
             if (c >= n) continue;
-            const float v = sum[r] * sc[r];
+            float v = sum[0][r] * sc[0][r];
+            if constexpr (SILU) {
+              // silu(gate) * up, with silu(v) = v / (1 + exp(-v))
+              v = v / (1.0f + expf(-v)) * (sum[1][r] * sc[1][r]);
+            }
             if constexpr (YT == I8QL_F32) {
               static_cast<float*>(y)[row * n + c] = v;
             } else {
@@ -309,12 +329,13 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_w8a16_kernel(
   }
 }
 
-template <int WAVES, bool BITMAP, int YT>
+template <int KS, bool BITMAP, bool SILU, int YT>
 hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
                        const float* w_scale, int64_t num_experts, const int32_t* ids,
                        int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
                        hipStream_t stream) {
-  auto kern = grouped_w8a16_kernel<WAVES, BITMAP, YT>;
+  constexpr int WAVES = KS * (SILU ? 2 : 1);
+  auto kern = grouped_w8a16_kernel<KS, BITMAP, SILU, YT>;
   // Rows staged per pass: an expert that each token picks at most once receives at most t
   // rows; one that receives more takes more passes (any count is handled).  Long rows stage
   // fewer per pass so that they fit the LDS budget (the caller bounds k so one row does).
@@ -336,36 +357,39 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
   return hipGetLastError();
 }
 
-template <int WAVES, int YT>
+template <int KS, bool SILU, int YT>
 hipError_t launch_waves(const void* x, int x_per_assignment, const int8_t* wq,
                         const float* w_scale, int64_t num_experts, const int32_t* ids,
                         int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
                         hipStream_t stream) {
   if (t * topk < num_experts)
-    return launch_mode<WAVES, true, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
-                                        topk, y, n, k, stream);
-  return launch_mode<WAVES, false, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
-                                       topk, y, n, k, stream);
+    return launch_mode<KS, true, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids,
+                                           t, topk, y, n, k, stream);
+  return launch_mode<KS, false, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids,
+                                          t, topk, y, n, k, stream);
 }
 
-// Wavefronts per workgroup: the fewest of 1, 2, 4 and 8 with which each streams at most
-// kUnroll steps of k (one batch of loads in flight), 8 beyond.
-template <int YT>
+// Wavefronts per tile: the fewest of 1, 2, 4 and 8 with which each streams at most kUnroll
+// steps of k (one batch of loads in flight), 8 beyond; at most 4 with SiLU·mul, whose two
+// tiles would otherwise make workgroups of 1024 threads (128 registers each: spills).
+template <bool SILU, int YT>
 hipError_t launch_yt(const void* x, int x_per_assignment, const int8_t* wq,
                      const float* w_scale, int64_t num_experts, const int32_t* ids, int64_t t,
                      int64_t topk, void* y, int64_t n, int64_t k, hipStream_t stream) {
   const int64_t steps = (k + kStepK - 1) / kStepK;
   if (steps <= kUnroll)
-    return launch_waves<1, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk, y,
-                               n, k, stream);
+    return launch_waves<1, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                     topk, y, n, k, stream);
   if (steps <= 2 * kUnroll)
-    return launch_waves<2, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk, y,
-                               n, k, stream);
-  if (steps <= 4 * kUnroll)
-    return launch_waves<4, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk, y,
-                               n, k, stream);
-  return launch_waves<8, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk, y, n,
-                             k, stream);
+    return launch_waves<2, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                     topk, y, n, k, stream);
+  if (SILU || steps <= 4 * kUnroll)
+    return launch_waves<4, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                     topk, y, n, k, stream);
+  if constexpr (!SILU)
+    return launch_waves<8, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,
+                                     topk, y, n, k, stream);
+  return hipErrorInvalidValue;  // not reached
 }
 
 }  // namespace
@@ -376,10 +400,22 @@ hipError_t launch_grouped_w8a16_gemm(const void* x, int x_per_assignment, const 
                                      void* y, i8ql_dtype y_dtype, int64_t n, int64_t k,
                                      hipStream_t stream) {
   if (y_dtype == I8QL_F32)
-    return launch_yt<I8QL_F32>(x, x_per_assignment, wq, w_scale, num_experts, expert_ids, t,
-                               topk, y, n, k, stream);
-  return launch_yt<I8QL_BF16>(x, x_per_assignment, wq, w_scale, num_experts, expert_ids, t,
-                              topk, y, n, k, stream);
+    return launch_yt<false, I8QL_F32>(x, x_per_assignment, wq, w_scale, num_experts,
+                                      expert_ids, t, topk, y, n, k, stream);
+  return launch_yt<false, I8QL_BF16>(x, x_per_assignment, wq, w_scale, num_experts, expert_ids,
+                                     t, topk, y, n, k, stream);
+}
+
+hipError_t launch_grouped_w8a16_silu_gemm(const void* x, int x_per_assignment,
+                                          const int8_t* wq, const float* w_scale,
+                                          int64_t num_experts, const int32_t* expert_ids,
+                                          int64_t t, int64_t topk, void* h, i8ql_dtype h_dtype,
+                                          int64_t n, int64_t k, hipStream_t stream) {
+  if (h_dtype == I8QL_F32)
+    return launch_yt<true, I8QL_F32>(x, x_per_assignment, wq, w_scale, num_experts,
+                                     expert_ids, t, topk, h, n, k, stream);
+  return launch_yt<true, I8QL_BF16>(x, x_per_assignment, wq, w_scale, num_experts, expert_ids,
+                                    t, topk, h, n, k, stream);
 }
 
 }  // namespace i8ql

@@ -37,4 +37,20 @@ hipError_t launch_grouped_w8a16_gemm(const void* x, int x_per_assignment, const 
                                      void* y, i8ql_dtype y_dtype, int64_t n, int64_t k,
                                      hipStream_t stream);
 
+// Gate/up over weights stacked [num_experts, 2n, k] (gate rows, then up rows) with the
+// SiLU·mul fused: h [t * topk, n] = silu(gate) * up.
+hipError_t launch_grouped_w8a16_silu_gemm(const void* x, int x_per_assignment,
+                                          const int8_t* wq, const float* w_scale,
+                                          int64_t num_experts, const int32_t* expert_ids,
+                                          int64_t t, int64_t topk, void* h, i8ql_dtype h_dtype,
+                                          int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_moe_route_topk(const void* logits, i8ql_dtype dtype, int64_t t,
+                                 int64_t e_routed, int64_t k_routed, int64_t n_shared,
+                                 int32_t* ids, float* weights, hipStream_t stream);
+
+hipError_t launch_moe_combine(const void* d, i8ql_dtype d_dtype, const float* weights,
+                              int64_t t, int64_t topk, int64_t n, void* y, i8ql_dtype y_dtype,
+                              hipStream_t stream);
+
 }  // namespace i8ql

@@ -202,6 +202,71 @@ def test_grouped_validation(lib):
     assert call(ids=A2) == ALIGN
 
 
+def test_grouped_silu_validation(lib):
+    f = lib.grouped_w8a16_silu_gemm
+    base = dict(x=A16, pa=0, wq=A16, sw=A16, e=66, ids=A16, t=4, topk=8, h=A16, ht=BF16, n=16,
+                k=64)
+    call = lambda **kw: (lambda a: f(a["x"], a["pa"], a["wq"], a["sw"], a["e"], a["ids"], a["t"],
+                                     a["topk"], a["h"], a["ht"], a["n"], a["k"], NUL))(dict(base, **kw))
+    assert call(ht=I8) == DTYPE
+    assert call(pa=3) == ARG
+    assert call(topk=0) == ARG
+    assert call(e=0) == ARG
+    assert call(t=-1) == SHAPE
+    assert call(k=32768 + 16) == SHAPE
+    assert call(t=0, x=NUL) == OK
+    assert call(n=0, h=NUL) == OK
+    assert call(h=NUL) == NULL
+    assert call(k=40) == ALIGN
+    assert call(h=A2, ht=F32) == ALIGN
+
+
+def test_moe_route_validation(lib):
+    f = lib.moe_route_topk
+    base = dict(lg=A16, lt=F32, t=4, e=64, kr=6, ns=2, ids=A16, w=A16)
+    call = lambda **kw: (lambda a: f(a["lg"], a["lt"], a["t"], a["e"], a["kr"], a["ns"], a["ids"],
+                                     a["w"], NUL))(dict(base, **kw))
+    assert call(lt=I32) == DTYPE
+    assert call(lt=F16) == DTYPE
+    assert call(t=-1) == SHAPE
+    assert call(e=0) == ARG
+    assert call(e=257) == ARG
+    assert call(kr=0) == ARG
+    assert call(kr=33) == ARG
+    assert call(kr=7, e=6) == ARG         # more picks than experts
+    assert call(ns=-1) == ARG
+    assert call(ns=33) == ARG
+    assert call(kr=32, ns=32, e=256, t=0) == OK   # 64 slots: the largest allowed
+    assert call(t=0, lg=NUL) == OK
+    assert call(lg=NUL) == NULL
+    assert call(ids=NUL) == NULL
+    assert call(w=NUL) == NULL
+    assert call(lg=A2) == ALIGN
+    assert call(lg=ctypes.c_void_p(0x10001), lt=BF16) == ALIGN
+    assert call(ids=A2) == ALIGN
+
+
+def test_moe_combine_validation(lib):
+    f = lib.moe_combine
+    base = dict(d=A16, dt=BF16, w=A16, t=4, topk=8, n=2048, y=A16, yt=BF16)
+    call = lambda **kw: (lambda a: f(a["d"], a["dt"], a["w"], a["t"], a["topk"], a["n"], a["y"],
+                                     a["yt"], NUL))(dict(base, **kw))
+    assert call(dt=I8) == DTYPE
+    assert call(yt=I32) == DTYPE
+    assert call(topk=0) == ARG
+    assert call(topk=65) == ARG
+    assert call(t=-1) == SHAPE
+    assert call(n=-1) == SHAPE
+    assert call(t=0, d=NUL) == OK
+    assert call(n=0, y=NUL) == OK
+    assert call(d=NUL) == NULL
+    assert call(w=NUL) == NULL
+    assert call(y=NUL) == NULL
+    assert call(d=ctypes.c_void_p(0x10001)) == ALIGN
+    assert call(w=A2) == ALIGN
+    assert call(y=A2, yt=F32) == ALIGN
+
+
 def _gpu_visible():
     import torch
     return torch.cuda.device_count() > 0  # counts devices without initializing HIP
@@ -219,6 +284,10 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
         lambda: lib.w8a8_gemm_with_config(0, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 64, NUL),
         lambda: lib.w8a16_gemm(A16, A16, A16, NUL, A16, BF16, 1, 16, 64, NUL),
         lambda: lib.grouped_w8a16_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64, NUL),
+        lambda: lib.grouped_w8a16_silu_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64,
+                                            NUL),
+        lambda: lib.moe_route_topk(A16, F32, 4, 64, 6, 2, A16, A16, NUL),
+        lambda: lib.moe_combine(A16, BF16, A16, 4, 8, 2048, A16, BF16, NUL),
     ]
     for call in calls:
         assert call() == HIP
