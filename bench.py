@@ -440,8 +440,54 @@ def section_moe(torch, i8, wl, dev, args, result):
                            "per_proj": per}
         log(f"[moe] T={t}: {distinct} experts, {secs/args.steps*1e6:.1f} us/layer, "
             f"{out['per_t'][t]['GBs_kernels']:.0f} GB/s")
+    # The whole block: routing from router logits, gate and up as one grouped GEMM over
+    # weights stacked [E, 2 * 1408, 2048] with SiLU·mul fused, down, weighted combine.
+    gu = [(torch.cat([r["gate"][0], r["up"][0]], dim=1).contiguous(),
+           torch.cat([r["gate"][1], r["up"][1]], dim=1).contiguous()) for r in rot]
+    n_i, hid = wl.MOE_16B["gate"]
+    out["block"] = {}
+    for t in wl.MOE_TOKENS:
+        logits = torch.from_numpy(wl.router_logits(g, t)).to(dev)
+        x_in = wl.to_bf16(wl.activations(g, t, hid)).to(dev)
+        kk = wl.MOE_TOP + wl.MOE_SHARED
+        ids_d = torch.empty((t, kk), dtype=torch.int32, device=dev)
+        w_d = torch.empty((t, kk), dtype=torch.float32, device=dev)
+        h = torch.empty((t * kk, n_i), dtype=torch.bfloat16, device=dev)
+        dn = torch.empty((t * kk, hid), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((t, hid), dtype=torch.bfloat16, device=dev)
+        steps_of = {
+            "route": lambda i: i8.moe_route_topk(logits, wl.MOE_TOP, wl.MOE_SHARED,
+                                                 ids_out=ids_d, weights_out=w_d),
+            "gate_up_silu": lambda i: i8.grouped_w8a16_silu_gemm(
+                x_in, gu[i % copies][0], gu[i % copies][1], ids_d, out=h),
+            "down": lambda i: i8.grouped_w8a16_gemm(
+                h, rot[i % copies]["down"][0], rot[i % copies]["down"][1], ids_d,
+                x_per_assignment=True, out=dn),
+            "combine": lambda i: i8.moe_combine(dn, w_d, out=y),
+        }
+        steps_of["route"](0)
+        torch.cuda.synchronize()
+        distinct = len(np.unique(ids_d.cpu().numpy()))
+        secs = time_loop(torch, lambda i: [f(i) for f in steps_of.values()], args.steps,
+                         args.warmup)
+        reps = max(5, args.steps // 5)
+        durs = {nm: per_call(torch, f, reps) for nm, f in steps_of.items()}
+        nbytes = (grouped_bytes(distinct, 2 * n_i, hid, t, t * kk)
+                  + grouped_bytes(distinct, hid, n_i, t * kk, t * kk)
+                  + t * wl.MOE_ROUTED * 4 + t * kk * 8            # logits in, ids + weights out
+                  + t * kk * hid * 2 + t * kk * 4 + t * hid * 2)  # combine
+        us = secs / args.steps * 1e6
+        out["block"][t] = {"distinct_experts": distinct, "block_us": us,
+                           "GBs_block": nbytes / (secs / args.steps) / 1e9,
+                           "frac_hbm_block": nbytes / (secs / args.steps) / 1e9 / PEAK_HBM_GBS,
+                           "per_step_us": {nm: d * 1e6 for nm, d in durs.items()}}
+        log(f"[moe] block T={t}: {distinct} experts, {us:.1f} us "
+            f"(route {durs['route']*1e6:.1f}, gate/up+SiLU {durs['gate_up_silu']*1e6:.1f}, "
+            f"down {durs['down']*1e6:.1f}, combine {durs['combine']*1e6:.1f}), "
+            f"{out['block'][t]['GBs_block']:.0f} GB/s")
     result["moe"] = {"workload": "16B MoE block (64 routed + 2 shared experts, top-6), grouped "
-                     "W8A16 gate/up/down, T in {1,4,16,64}", "unit": "GB/s", **out}
+                     "W8A16 gate/up/down, T in {1,4,16,64}; 'block': routing + gate/up with "
+                     "SiLU·mul + down + combine", "unit": "GB/s", **out}
 
 
 def section_prefill_8b(torch, i8, wl, dev, args, result):

@@ -27,15 +27,44 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// (value, index) ordering of the selection: the larger logit wins, the lower index on ties.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Wavefront reductions with DPP moves (a few cycles each, instead of a round trip through
+// the LDS crossbar per step): combine within pairs and quads, mirror within 8 and 16 lanes
+// (every lane then holds its row of 16), then lane 15 of each row into rows 1 and 3 and lane
+// 31 into rows 2 and 3.  Lanes those two moves do not write get their own value back (for a
+// sum they double; only lane 63 is read): lane 63 ends with the result over all 64 lanes,
+// which readlane broadcasts.
+template <class Op>
+__device__ __forceinline__ int wave_reduce(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));  // row_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));  // row_bcast15
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));  // row_bcast31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float wave_fmax(float f) {
+  return __int_as_float(wave_reduce(__float_as_int(f), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
+}
+
+__device__ __forceinline__ float wave_fsum(float f) {
+  return __int_as_float(wave_reduce(__float_as_int(f), [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
+}
+
+__device__ __forceinline__ int wave_imin(int v) {
+  return wave_reduce(v, [](int a, int b) { return min(a, b); });
 }
 
 // One wavefront per token, four tokens per workgroup.  Lane l holds logits l, l + 64, ...;
-// the k_routed picks are k_routed rounds of a butterfly arg-max over the lanes' best
-// untaken candidates, so the order of the slots is the selection order.  Lane s keeps slot
-// s's id and weight and the wavefront stores all slots at once.
+// the k_routed picks are k_routed rounds of a wavefront arg-max over the lanes' best untaken
+// candidates (the largest value, then the lowest index holding it), so the order of the
+// slots is the selection order.  Lane s keeps slot s's id and weight and the wavefront
+// stores all slots at once.
 template <bool BF16>
 __global__ __launch_bounds__(256) void moe_route_kernel(const void* __restrict__ logits,
                                                         int64_t t, int e_routed, int k_routed,
@@ -61,35 +90,27 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const void* __restrict__
 #pragma unroll
   for (int i = 0; i < kRouteMaxPerLane; ++i)
     if (live[i]) mx = fmaxf(mx, v[i]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  mx = wave_fmax(mx);
   float den = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRouteMaxPerLane; ++i)
     if (live[i]) den += expf(v[i] - mx);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d);
+  den = wave_fsum(den);
 
   int my_id = -1;
   float my_w = 0.0f;
   for (int s = 0; s < k_routed; ++s) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    // this lane's best untaken logit (its indices ascend with i: the first of equal ones)
+    float lv = -INFINITY;
+    int li = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < kRouteMaxPerLane; ++i)
-      if (live[i] && better(v[i], lane + 64 * i, bv, bi)) {
-        bv = v[i];
-        bi = lane + 64 * i;
+      if (live[i] && (v[i] > lv || li == 0x7fffffff)) {
+        lv = v[i];
+        li = lane + 64 * i;
       }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d);
-      const int oi = __shfl_xor(bi, d);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    const float bv = wave_fmax(lv);
+    const int bi = wave_imin(lv == bv ? li : 0x7fffffff);
     // every lane now holds the pick; its owner retires it
 #pragma unroll
     for (int i = 0; i < kRouteMaxPerLane; ++i)
