@@ -36,6 +36,8 @@ constexpr int kList = 1024;     // assignments held in LDS per scan window
 constexpr int kScanBatch = 8;   // 64-id groups whose loads a wavefront keeps in flight together
 constexpr int kMaxPassRows = 8;  // activation rows staged in LDS per pass
 constexpr size_t kMaxStageBytes = 128 * 1024;  // LDS for the staged rows of one pass
+constexpr int kMaxTileSeq = 16;   // 16-channel tiles one workgroup walks, at most
+constexpr int64_t kCusPerGpu = 256;  // MI355X compute units (sizes the tiles per workgroup)
 
 template <int WAVES>
 constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * 64 * sizeof(v4f); }
@@ -108,7 +110,8 @@ template <int KS, bool BITMAP, bool SILU, int YT>
 __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel(
     const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
-    int64_t total, int64_t topk, void* __restrict__ y, int64_t n, int64_t k, int pass_rows) {
+    int64_t total, int64_t topk, void* __restrict__ y, int64_t n, int64_t k, int pass_rows,
+    int tseq) {
   constexpr int TILES = SILU ? 2 : 1;
   constexpr int WAVES = KS * TILES;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -122,9 +125,11 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   uint32_t* present = reinterpret_cast<uint32_t*>(xzero + 16);
 
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: a scalar
   const bool invalid_row = blockIdx.y == 0;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  // tseq consecutive 16-channel tiles, one after the other: the expert choice, the row scan
+  // and the staged activation rows serve all of them
+  const int64_t nb = static_cast<int64_t>(blockIdx.x) * ((BITMAP || SILU) ? tseq : 1) * 16;
   if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
 
   // Wavefront 0's first batch of ids, loaded once: the bitmap pass and the first window of
@@ -176,28 +181,36 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
     if (e < 0) return;  // fewer distinct experts than slots (uniform over the workgroup)
   }
 
-  // This lane's 4 output-channel scales (wavefront 0 applies them), requested before the
-  // scan so that their latency overlaps it.  A picked expert has rows for certain, so its
-  // first batch of weight loads goes out before the scan too.
-  const int64_t nc = n0 + 4 * (lane / 16);
   // Weight rows per expert: TILES * n; this wavefront's tile (0: the channels themselves or
-  // the gate rows, 1: the up rows) starts at row tile * n of its expert.
+  // the gate rows, 1: the up rows) starts at row tile * n of its expert.  Per 16-channel
+  // tile at n0: the weight row of this lane and (wavefront 0) the 4 output-channel scales
+  // of its lane group.
   const int tile = wave / KS;
   float sc[TILES][4] = {};
-  const int64_t wr = min(n0 + lane % 16, n - 1);
-  const int8_t* wrow = wq + (invalid_row ? 0 : ((e * TILES + tile) * n + wr) * k);
+  auto weight_row = [&](int64_t n0) {
+    return wq + (invalid_row ? 0 : ((e * TILES + tile) * n + min(n0 + lane % 16, n - 1)) * k);
+  };
+  auto load_scales = [&](int64_t n0) {
+    if (wave == 0) {
+      const int64_t nc = n0 + 4 * (lane / 16);
+#pragma unroll
+      for (int ti = 0; ti < TILES; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sc[ti][r] = w_scale[(e * TILES + ti) * n + min(nc + r, n - 1)];
+    }
+  };
   int sb, se;
   wave_step_range(k, KS, wave % KS, sb, se);
   v4u w[kUnroll][2];
   bool w_loaded = false;
-  if (!invalid_row && wave == 0) {
-#pragma unroll
-    for (int ti = 0; ti < TILES; ++ti)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[ti][r] = w_scale[(e * TILES + ti) * n + min(nc + r, n - 1)];
-  }
+  // The first tile's scales are requested before the scan so that their latency overlaps
+  // it; a picked expert has rows for certain, so its first batch of weight loads goes out
+  // before the scan too.
+  int64_t sc_n0 = nb;  // the tile whose scales sc holds
+  if (!invalid_row) load_scales(nb);
   if (!invalid_row && BITMAP) {
-    load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+    load_weight_batch<kUnroll>(weight_row(nb), k, sb, se, w);
     w_loaded = true;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -247,9 +260,10 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
     p_next = s_next;
 
     if (invalid_row) {
-      for (int i = threadIdx.x; i < count * 16; i += 64 * WAVES) {
-        const int64_t row = list[i / 16];
-        const int64_t c = n0 + i % 16;
+      const int nt = (BITMAP || SILU) ? tseq : 1;
+      for (int i = threadIdx.x; i < count * 16 * nt; i += 64 * WAVES) {
+        const int64_t row = list[i / (16 * nt)];
+        const int64_t c = nb + i % (16 * nt);
         if (c >= n) continue;
         if constexpr (YT == I8QL_F32) {
           static_cast<float*>(y)[row * n + c] = 0.0f;
@@ -261,25 +275,16 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
       const int64_t pitch = 2 * k + 16;
       const int div = x_per_assignment ? 1 : static_cast<int>(topk);
       for (int g = 0; g < count; g += pass_rows) {
-        // Activation rows of this pass, then (unless the first batch of weight loads is
-        // already in flight) the first batch of weight loads (a later pass re-reads the same
-        // weights, from cache); wait for the rows only (weight loads issued after them may
-        // stay in flight), then publish them to every wavefront.  The compiler barriers keep
-        // the weight loads behind the copy, which the wait count relies on.
+        // Activation rows of this pass, then the tiles one after the other.  For each tile
+        // (unless its first batch of weight loads is already in flight) its scales and first
+        // batch of weight loads (a later pass re-reads the same weights, from cache); on the
+        // first tile wait for the rows only (loads issued after them may stay in flight) and
+        // publish them to every wavefront.  The compiler barriers keep the weight loads
+        // behind the copy, which the wait count relies on.
         const int rows = min(pass_rows, count - g);
         stage_rows<WAVES>(x, list + g, div, rows, k, xs);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        if (w_loaded) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-          w_loaded = false;
-        } else {
-          load_weight_batch<kUnroll>(wrow, k, sb, se, w);
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
-        }
-        bare_barrier();
         const char* xrow[1];
         bool live[1];
         v4u xb[1][4];
@@ -287,41 +292,74 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
         xrow[0] = xs + (live[0] ? lane % 16 : 0) * pitch;
 #pragma unroll
         for (int c = 0; c < 4; ++c) xb[0][c] = v4u{0u, 0u, 0u, 0u};
-        v4f acc[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
-        mma_batch_lds<1, kUnroll>(w, xrow, live, xzero, k, sb, se, xb, acc);
-        for (int s = sb + kUnroll; s < se; s += kUnroll) {
-          load_weight_batch<kUnroll>(wrow, k, s, se, w);
-          __builtin_amdgcn_sched_barrier(0);
-          mma_batch_lds<1, kUnroll>(w, xrow, live, xzero, k, s, se, xb, acc);
-        }
-        red[wave * 64 + lane] = acc[0];
-        __syncthreads();
-        if (wave == 0 && lane % 16 < rows) {
-          v4f sum[TILES];
-#pragma unroll
-          for (int ti = 0; ti < TILES; ++ti) {
-            sum[ti] = red[ti * KS * 64 + lane];
-#pragma unroll
-            for (int w2 = 1; w2 < KS; ++w2) sum[ti] += red[(ti * KS + w2) * 64 + lane];
+        const int nt = (BITMAP || SILU) ? tseq : 1;  // one tile (a constant) in the plain direct mode
+        for (int ti = 0; ti < nt; ++ti) {
+          const int64_t n0 = nb + 16 * ti;
+          if (n0 >= n) break;  // uniform
+          // With SiLU·mul or several tiles, the step range and the row and staging pointers
+          // pass through opaque copies, so that the compiler derives the batch's addresses and
+          // bounds here, per tile, instead of holding them all in registers across the loops
+          // (SiLU·mul: 223 -> 163 VGPRs, 3 instead of 2 waves per SIMD, the MoE block 10 %
+          // faster at T = 16).  The plain kernel with one tile is faster without them.
+          const int8_t* wrow = weight_row(n0);
+          int s0 = sb, s1 = se;
+          const char* xr[1] = {xrow[0]};
+          if constexpr (SILU || BITMAP) {
+            asm volatile("" : "+s"(s0), "+s"(s1));
+            asm volatile("" : "+v"(wrow));
+            asm volatile("" : "+v"(xr[0]));
           }
-          const int64_t row = list[g + lane % 16];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t c = nc + r;
-            if (c >= n) continue;
-            float v = sum[0][r] * sc[0][r];
-            if constexpr (SILU) {
-              // silu(gate) * up, with silu(v) = v / (1 + exp(-v))
-              v = v / (1.0f + expf(-v)) * (sum[1][r] * sc[1][r]);
+          if (w_loaded) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            w_loaded = false;
+          } else {
+            if (sc_n0 != n0) {
+              load_scales(n0);
+              sc_n0 = n0;
             }
-            if constexpr (YT == I8QL_F32) {
-              static_cast<float*>(y)[row * n + c] = v;
-            } else {
-              static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v);
+            load_weight_batch<kUnroll>(wrow, k, s0, s1, w);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (ti == 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
+          }
+          if (ti == 0) bare_barrier();
+          v4f acc[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
+          mma_batch_lds<1, kUnroll>(w, xr, live, xzero, k, s0, s1, xb, acc);
+          for (int s = s0 + kUnroll; s < s1; s += kUnroll) {
+            load_weight_batch<kUnroll>(wrow, k, s, s1, w);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_batch_lds<1, kUnroll>(w, xr, live, xzero, k, s, s1, xb, acc);
+          }
+          red[wave * 64 + lane] = acc[0];
+          __syncthreads();
+          if (wave == 0 && lane % 16 < rows) {
+            v4f sum[TILES];
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+              sum[tt] = red[tt * KS * 64 + lane];
+#pragma unroll
+              for (int w2 = 1; w2 < KS; ++w2) sum[tt] += red[(tt * KS + w2) * 64 + lane];
+            }
+            const int64_t row = list[g + lane % 16];
+            const int64_t nc = n0 + 4 * (lane / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t c = nc + r;
+              if (c >= n) continue;
+              float v = sum[0][r] * sc[0][r];
+              if constexpr (SILU) {
+                // silu(gate) * up, with silu(v) = v / (1 + exp(-v))
+                v = v / (1.0f + expf(-v)) * (sum[1][r] * sc[1][r]);
+              }
+              if constexpr (YT == I8QL_F32) {
+                static_cast<float*>(y)[row * n + c] = v;
+              } else {
+                static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v);
+              }
             }
           }
+          __syncthreads();  // red[] (and, after the last tile, the staged rows) are reused
         }
-        __syncthreads();  // the staged rows and red[] are reused by the next pass
       }
     }
     if (p_next >= total) break;
@@ -350,10 +388,21 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
   // expert, or, with fewer assignments than experts, one per assignment (the most distinct
   // experts there can be).
   const int64_t slots = BITMAP ? t * topk : num_experts;
-  const dim3 grid(static_cast<unsigned>((n + 15) / 16), static_cast<unsigned>(slots + 1));
+  // Tiles per workgroup, walked one after the other.  With fewer assignments than experts
+  // (every expert has at most t rows, one pass) as many as keep about four workgroups per
+  // compute unit over the grid (at most 16), so that each workgroup's expert choice, row scan
+  // and staged rows serve more output channels.  Otherwise one: experts with many rows take
+  // several passes, and walking tiles would multiply those passes in one workgroup (at
+  // T = 64, 4 tiles per workgroup made the MoE gate/up/down layer 2.3x slower).
+  const int64_t tiles = (n + 15) / 16;
+  int64_t per = BITMAP ? tiles * slots / (4 * kCusPerGpu) : 1;
+  if (per > kMaxTileSeq) per = kMaxTileSeq;
+  const int tseq = per < 1 ? 1 : static_cast<int>(per);
+  const dim3 grid(static_cast<unsigned>((tiles + tseq - 1) / tseq),
+                  static_cast<unsigned>(slots + 1));
   hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, stream,
                      static_cast<const uint16_t*>(x), x_per_assignment, wq, w_scale,
-                     num_experts, ids, t * topk, topk, y, n, k, pass_rows);
+                     num_experts, ids, t * topk, topk, y, n, k, pass_rows, tseq);
   return hipGetLastError();
 }
 
