@@ -68,6 +68,10 @@ class Oracle:
         lib.ref_grouped_w8a16_silu.restype = None
         lib.ref_moe_combine.argtypes = [_P, _P, _I64, _I64, _I64, _P]
         lib.ref_moe_combine.restype = None
+        lib.ref_quantize_groups.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P]
+        lib.ref_quantize_groups.restype = ctypes.c_int
+        lib.ref_w8a16_grouped_scales.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+        lib.ref_w8a16_grouped_scales.restype = None
         lib.ref_set_threads.argtypes = [ctypes.c_int]
         lib.ref_get_threads.restype = ctypes.c_int
         self.lib = lib
@@ -150,6 +154,36 @@ class Oracle:
                                    self._ptr(y))
         return y
 
+
+    # -- one scale per group of input channels ("Day 6", The mechanism, block 1) ---------
+    def quantize_groups(self, a: np.ndarray, dtype: str, group: int = 128):
+        """Per-group symmetric int8 of ``a`` [r, k] (k % group == 0): ``(q int8 [r, k],
+        scale float32 [r, k // group])``, the row rule applied to every group."""
+        code = {"f32": REF_F32, "bf16": REF_BF16, "f16": REF_F16}[dtype]
+        want = np.float32 if code == REF_F32 else np.uint16
+        a = np.ascontiguousarray(a, dtype=want)
+        r, k = a.shape
+        q = np.empty((r, k), np.int8)
+        s = np.empty((r, k // group), np.float32)
+        rc = self.lib.ref_quantize_groups(self._ptr(a), code, r, k, group, self._ptr(q),
+                                          self._ptr(s))
+        if rc != 0:
+            raise ValueError("bad dtype or k not a multiple of the group")
+        return q, s
+
+    def w8a16_grouped_scales(self, x_bf16_bits, wq, w_scale, group: int = 128, bias=None):
+        """float64 ``sum_g w_scale[j, g] * sum_{c in g} x[i, c] * wq[j, c] (+ bias[j])``."""
+        x = np.ascontiguousarray(x_bf16_bits, np.uint16)
+        wq = np.ascontiguousarray(wq, np.int8)
+        sw = np.ascontiguousarray(w_scale, np.float32)
+        b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+        m, k = x.shape
+        n, k2 = wq.shape
+        assert k == k2 and k % group == 0 and sw.shape == (n, k // group)
+        y = np.empty((m, n), np.float64)
+        self.lib.ref_w8a16_grouped_scales(self._ptr(x), self._ptr(wq), self._ptr(sw),
+                                          self._ptr(b), m, n, k, group, self._ptr(y))
+        return y
 
     # -- mixture-of-experts steps around the grouped GEMM (readings stated in ref.c) -----
     def moe_route_topk(self, logits, k_routed: int, n_shared: int):

@@ -307,3 +307,68 @@ void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, in
       y[i * n + c] = acc;
     }
 }
+
+/* ---- one scale per group of input channels --------------------------------------------- */
+
+/*
+ * "Day 6 — Quantize It Yourself", The mechanism, block 1: the whole design space is who
+ * shares a scale — per tensor, per output channel, or per group of 128 weights along the
+ * input dimension.  Each group of `group` consecutive elements of a row gets the row
+ * quantizer's rule (float32 absmax / 127, float32 quotient, round half to even, clamp, the
+ * all-zero guard).  q: [r, k]; s: [r, k / group], k % group == 0.
+ */
+int ref_quantize_groups(const void* a, int dtype, int64_t r, int64_t k, int64_t group, int8_t* q,
+                        float* s) {
+  if (dtype != REF_F32 && dtype != REF_BF16 && dtype != REF_F16) return -1;
+  if (group < 1 || k % group != 0) return -1;
+  const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < r; ++row) {
+    for (int64_t g = 0; g < ng; ++g) {
+      const int64_t base = row * k + g * group;
+      float amax = 0.0f;
+      for (int64_t j = 0; j < group; ++j) {
+        float v = fabsf(load_elem(a, dtype, base + j));
+        if (v > amax) amax = v;
+      }
+      const float scale = amax / 127.0f;
+      if (scale == 0.0f) {
+        s[row * ng + g] = 1.0f;
+        for (int64_t j = 0; j < group; ++j) q[base + j] = 0;
+        continue;
+      }
+      for (int64_t j = 0; j < group; ++j) {
+        float c = round_half_even(load_elem(a, dtype, base + j) / scale);
+        if (c > 127.0f) c = 127.0f;
+        if (c < -127.0f) c = -127.0f;
+        q[base + j] = (int8_t)c;
+      }
+      s[row * ng + g] = scale;
+    }
+  }
+  return 0;
+}
+
+/* Weight-only product with one weight scale per (output channel, group of input channels):
+ * y[i, j] = sum_g w_scale[j, g] * sum_{c in g} x[i, c] * wq[j, c] (+ bias[j]), in double. */
+void ref_w8a16_grouped_scales(const uint16_t* x, const int8_t* wq, const float* w_scale,
+                              const float* bias, int64_t m, int64_t n, int64_t k, int64_t group,
+                              double* y) {
+  const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    const uint16_t* xr = x + i * k;
+    for (int64_t j = 0; j < n; ++j) {
+      const int8_t* wr = wq + j * k;
+      double v = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        double part = 0.0;
+        for (int64_t c = g * group; c < (g + 1) * group; ++c)
+          part += (double)bf16_to_f32(xr[c]) * (double)wr[c];
+        v += (double)w_scale[j * ng + g] * part;
+      }
+      if (bias) v += (double)bias[j];
+      y[i * n + j] = v;
+    }
+  }
+}

@@ -47,6 +47,15 @@ void ref_grouped_w8a16(const uint16_t* x, int x_per_assignment, const int8_t* wq
                        const float* w_scale, int64_t e, const int32_t* ids, int64_t t,
                        int64_t topk, int64_t n, int64_t k, double* y);
 
+/* One scale per group of `group` input channels ([Day6] block 1): the row rule per group.
+ * q: [r, k]; s: [r, k / group].  Returns 0, or -1 on a bad dtype or k % group != 0. */
+int ref_quantize_groups(const void* a, int dtype, int64_t r, int64_t k, int64_t group, int8_t* q,
+                        float* s);
+/* W8A16 with group scales w_scale [n, k / group]: y [m, n] double. */
+void ref_w8a16_grouped_scales(const uint16_t* x, const int8_t* wq, const float* w_scale,
+                              const float* bias, int64_t m, int64_t n, int64_t k, int64_t group,
+                              double* y);
+
 /* Mixture-of-experts steps around the grouped GEMM ([P5a] Summary names the block; its
  * routing, activation and combine are readings, stated in ref.c). */
 void ref_moe_route_topk(const float* logits, int64_t t, int64_t e_routed, int64_t k_routed,

@@ -527,3 +527,75 @@ def test_p14_combine_is_the_weighted_sum(ref):
     for i in range(t):
         np.testing.assert_array_equal(y1[i], d[i * topk + i % topk].astype(np.float64))
         assert not np.array_equal(y1[i], d[i * topk + (i + 1) % topk].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------------
+# P15–P16 one scale per group of 128 input channels ("Day 6 — Quantize It Yourself", The
+# mechanism, block 1: the design space is who shares a scale, down to groups of 128 weights
+# along the input dimension; Q1 there: an outlier only costs its own group's precision).
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_p15_group_quantizer_is_the_row_rule_per_group(ref, dtype):
+    g = wl.rng(130)
+    r, k, grp = 7, 1024, 128
+    w = wl.weight(g, r, k)
+    w[2, 128:256] = 0.0                       # an all-zero group: scale 1, codes 0
+    w[4, 5] = 3.0                             # an outlier inside the first group
+    if dtype == "f32":
+        a = w
+    else:
+        a = wl.bits16(wl.to_bf16(w) if dtype == "bf16" else wl.to_f16(w))
+    q, s = ref.quantize_groups(a, dtype, grp)
+    qr, sr = ref.quantize_rows(np.ascontiguousarray(a).reshape(r * k // grp, grp), dtype)
+    np.testing.assert_array_equal(q, qr.reshape(r, k))
+    np.testing.assert_array_equal(s.view(np.uint32), sr.reshape(r, k // grp).view(np.uint32))
+    assert s[2, 1] == 1.0 and np.all(q[2, 128:256] == 0)
+    # one group spanning the row is the per-channel quantizer
+    q1, s1 = ref.quantize_groups(a, dtype, k)
+    qc, sc = ref.quantize_rows(a, dtype)
+    np.testing.assert_array_equal(q1, qc)
+    np.testing.assert_array_equal(s1[:, 0], sc)
+
+
+def test_p15_an_outlier_costs_only_its_group(ref):
+    g = wl.rng(131)
+    k = 1024
+    w = wl.weight(g, 1, k)
+    wo = w.copy()
+    wo[0, 700] = 50.0                          # group 5 (640..767)
+    q, s = ref.quantize_groups(w, "f32")
+    qo, so = ref.quantize_groups(wo, "f32")
+    other = np.ones(k, bool)
+    other[640:768] = False
+    np.testing.assert_array_equal(qo[0, other], q[0, other])   # other groups untouched
+    assert np.count_nonzero(qo[0, 640:768]) < np.count_nonzero(q[0, 640:768])
+    # per-channel: the same outlier zeroes most codes of the whole row
+    qc, _ = ref.quantize_rows(wo, "f32")
+    assert np.count_nonzero(qc[0, other]) < 0.1 * np.count_nonzero(q[0, other])
+    # the round-trip bound holds per group
+    d = np.abs(wo.astype(np.float64) - np.repeat(so.astype(np.float64), 128, axis=1) * qo)
+    assert np.all(d <= np.repeat(so.astype(np.float64), 128, axis=1) * H)
+
+
+@pytest.mark.parametrize("m,n,k,bias", [(1, 64, 512, False), (8, 40, 4096, True), (3, 17, 128, True)])
+def test_p16_w8a16_group_scales_against_numpy(ref, m, n, k, bias):
+    g = wl.rng(132)
+    x = wl.to_bf16(wl.activations(g, m, k))
+    q, s = ref.quantize_groups(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+    b = (g.standard_normal(n, dtype=np.float32) * 0.02).astype(np.float32) if bias else None
+    y = ref.w8a16_grouped_scales(wl.bits16(x), q, s, 128, b)
+    deq = np.repeat(s.astype(np.float64), 128, axis=1) * q.astype(np.float64)
+    xd = x.double().numpy()
+    want = xd @ deq.T + (0.0 if b is None else b.astype(np.float64))
+    mag = np.abs(xd) @ np.abs(deq).T + 1.0
+    assert np.all(np.abs(y - want) <= 1e-12 * mag)
+    # a scale applied to the wrong group is visible
+    s2 = s.copy()
+    s2[:, [0, -1]] = s2[:, [-1, 0]]
+    if s.shape[1] > 1:
+        y2 = ref.w8a16_grouped_scales(wl.bits16(x), q, s2, 128, b)
+        assert np.max(np.abs(y2 - y)) > 1e-6 * np.max(np.abs(y))
+    # one group over the whole row is the per-channel product
+    qc, sc = ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+    np.testing.assert_array_equal(
+        ref.w8a16_grouped_scales(wl.bits16(x), qc, sc[:, None], k, b), ref.w8a16(wl.bits16(x), qc, sc, b))
