@@ -215,6 +215,39 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
                                i8ql_dtype y_dtype, int64_t n, int64_t k, void* stream);
 
 /*
+ * One scale per group of I8QL_GROUP_SIZE input channels.  Defines: [Day6] The mechanism,
+ * block 1 (who shares a scale: per tensor, per output channel, or per group of 128 weights
+ * along the input dimension; an outlier then costs only its own group's precision).
+ */
+#define I8QL_GROUP_SIZE 128
+
+/*
+ * quantize_per_group_int8 — the quantize_per_channel_int8 rule (float32 absmax / 127,
+ * correctly rounded float32 quotient, round half to even, clamp to [-127, 127], all-zero
+ * group -> scale 1 and codes 0) applied to every group of 128 consecutive elements of a row.
+ *
+ * w          device, [n, k] of w_dtype in {I8QL_F32, I8QL_BF16, I8QL_F16}, 16-byte aligned.
+ * q_out      device, [n, k] int8, 8-byte aligned.
+ * scale_out  device, [n, k / 128] float32 (group g of row i at i * (k / 128) + g).
+ * n >= 0, k >= 128, k % 128 == 0.
+ * Errors: dtype -> I8QL_ERR_DTYPE; n < 0 or k not a positive multiple of 128 ->
+ * I8QL_ERR_SHAPE; NULL -> I8QL_ERR_NULL; alignment -> I8QL_ERR_ALIGN.
+ */
+i8ql_status quantize_per_group_int8(const void* w, i8ql_dtype w_dtype, int64_t n, int64_t k,
+                                    int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * w8a16_gemm_g128 — w8a16_gemm with group scales:
+ *   y[i, j] = sum_g w_scale[j, g] * sum_{c in group g} x[i, c] * wq[j, c]  (+ bias[j])
+ * with float32 partial sums per group.  Arguments as for w8a16_gemm except
+ * w_scale [n, k / 128] float32 (from quantize_per_group_int8) and k % 128 == 0
+ * (I8QL_ERR_SHAPE otherwise).
+ */
+i8ql_status w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
+                            const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
+                            int64_t n, int64_t k, void* stream);
+
+/*
  * The mixture-of-experts steps on either side of grouped_w8a16_gemm.  [P5a] Summary runs the
  * grouped GEMM inside the mixture-of-experts block of deepseek-moe-16b but does not spell out
  * the block's routing, activation or combine; these entry points take the plainest reading

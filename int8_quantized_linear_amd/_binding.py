@@ -22,7 +22,9 @@ _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8Q
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
            "w8a8_gemm_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
-           "moe_combine", "i8ql_status_string", "i8ql_last_hip_error")
+           "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128", "i8ql_status_string",
+           "i8ql_last_hip_error")
+GROUP_SIZE = 128  # I8QL_GROUP_SIZE
 ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
 W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 
@@ -66,6 +68,10 @@ def load_library(path: str = LIB_PATH):
         lib.grouped_w8a16_silu_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64,
                                                 P]
         lib.grouped_w8a16_silu_gemm.restype = I
+        lib.quantize_per_group_int8.argtypes = [P, I, I64, I64, P, P, P]
+        lib.quantize_per_group_int8.restype = I
+        lib.w8a16_gemm_g128.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a16_gemm_g128.restype = I
         lib.moe_route_topk.argtypes = [P, I, I64, I64, I64, I64, P, P, P]
         lib.moe_route_topk.restype = I
         lib.moe_combine.argtypes = [P, I, P, I64, I64, I64, P, I, P]
@@ -288,4 +294,42 @@ def moe_combine(d, weights, out_dtype=torch.bfloat16, out=None):
     with torch.cuda.device(dev):
         _call("moe_combine", _ptr(d), _DTYPE[d.dtype], _ptr(weights), t, topk, n, _ptr(y),
               _DTYPE[out_dtype], _stream(dev))
+    return y
+
+
+def quantize_per_group_int8(w: torch.Tensor, q_out=None, scale_out=None):
+    """One int8 scale per group of 128 input channels: ``w`` [N, K] fp32/bf16/fp16 (K a
+    multiple of 128) -> (q int8 [N, K], scale fp32 [N, K/128])."""
+    _check(w, "w", (torch.float32, torch.bfloat16, torch.float16), 2)
+    n, k = w.shape
+    q = q_out if q_out is not None else torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = scale_out if scale_out is not None else torch.empty(
+        (n, k // GROUP_SIZE), dtype=torch.float32, device=w.device)
+    _check(q, "q_out", (torch.int8,), 2, w.device)
+    _check(s, "scale_out", (torch.float32,), 2, w.device)
+    if tuple(q.shape) != (n, k) or tuple(s.shape) != (n, k // GROUP_SIZE):
+        raise ValueError("output shapes do not match the input")
+    with torch.cuda.device(w.device):
+        _call("quantize_per_group_int8", _ptr(w), _DTYPE[w.dtype], n, k, _ptr(q), _ptr(s),
+              _stream(w.device))
+    return q, s
+
+
+def w8a16_gemm_g128(x, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):
+    """Weight-only GEMM with group scales: ``x`` [M, K] bf16, ``wq`` [N, K] int8,
+    ``w_scale`` [N, K/128] fp32 -> [M, N]."""
+    _check(x, "x", (torch.bfloat16,), 2)
+    dev = x.device
+    _check(wq, "wq", (torch.int8,), 2, dev)
+    _check(w_scale, "w_scale", (torch.float32,), 2, dev)
+    m, k = x.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k or tuple(w_scale.shape) != (n, k // GROUP_SIZE):
+        raise ValueError("x, wq and w_scale disagree")
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), 1, dev)
+    y = _out(out, (m, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("w8a16_gemm_g128", _ptr(x), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y),
+              _DTYPE[out_dtype], m, n, k, _stream(dev))
     return y

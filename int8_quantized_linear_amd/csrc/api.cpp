@@ -156,6 +156,34 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
                                                     static_cast<hipStream_t>(stream)));
 }
 
+i8ql_status quantize_per_group_int8(const void* w, i8ql_dtype w_dtype, int64_t n, int64_t k,
+                                    int8_t* q_out, float* scale_out, void* stream) {
+  if (w_dtype != I8QL_F32 && w_dtype != I8QL_BF16 && w_dtype != I8QL_F16) return I8QL_ERR_DTYPE;
+  if (n < 0 || k < 1 || k % I8QL_GROUP_SIZE != 0) return I8QL_ERR_SHAPE;
+  if (!mul_ok(n, k) || n * k / 8 / 256 >= kMaxGridX) return I8QL_ERR_SHAPE;
+  if (n == 0) return I8QL_OK;
+  if (!w || !q_out || !scale_out) return I8QL_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q_out, 8) || !aligned(scale_out, 4)) return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_quantize_groups128(w, w_dtype, n, k, q_out, scale_out,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
+                            const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
+                            int64_t n, int64_t k, void* stream) {
+  if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32) return I8QL_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 1 || k % I8QL_GROUP_SIZE != 0) return I8QL_ERR_SHAPE;
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
+  if ((n + 15) / 16 > kMaxGridX || (m + 63) / 64 > kMaxGridY) return I8QL_ERR_SHAPE;
+  if (m == 0 || n == 0) return I8QL_OK;
+  if (!x || !wq || !w_scale || !y) return I8QL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(y, elem_bytes(y_dtype)) || !aligned(w_scale, 4) || !aligned(bias, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_w8a16_gemm_g128(x, wq, w_scale, bias, y, y_dtype, m, n, k,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 i8ql_status grouped_w8a16_silu_gemm(const void* x, int x_per_assignment, const int8_t* wq,
                                     const float* w_scale, int64_t num_experts,
                                     const int32_t* expert_ids, int64_t t, int64_t topk, void* h,

@@ -85,11 +85,17 @@ __device__ __forceinline__ void load_weight_batch(const int8_t* __restrict__ wro
 // Only lanes whose activation row exists (live[mt]) read LDS: the others keep whatever xb
 // holds, which only reaches output columns that are never stored.  With one decode row
 // that is 4 of 64 lanes, so the fragment reads cost a sixteenth of the LDS bandwidth.
-template <int MT, int U>
+//
+// GS (one weight scale per step of 128 input channels, "Day 6 — Quantize It Yourself", The
+// mechanism, block 1: a scale per group of 128 weights along the input dimension): each
+// step's four MFMAs go into a zeroed partial tile, which is then multiplied by the step's
+// scales of the lane's 4 channels (gs: the workgroup's LDS table [step][16 channels]) and
+// added to the accumulator; steps past s_end add nothing.
+template <int MT, int U, bool GS = false>
 __device__ __forceinline__ void mma_batch_lds(const v4u (&w)[U][2], const char* const (&xrow)[MT],
                                               const bool (&live)[MT], const char* xzero,
                                               int64_t k, int s, int s_end, v4u (&xb)[MT][4],
-                                              v4f (&acc)[MT]) {
+                                              v4f (&acc)[MT], const float* gs = nullptr) {
   const int sub = 32 * ((threadIdx.x % 64) / 16);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -108,10 +114,23 @@ __device__ __forceinline__ void mma_batch_lds(const v4u (&w)[U][2], const char* 
           xb[mt][c] = *reinterpret_cast<const v4u*>(xp);
         }
       }
+      if constexpr (GS) {
+        v4f part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a[c], __builtin_bit_cast(v8bf, xb[mt][c]), acc[mt], 0, 0, 0);
+        for (int c = 0; c < 4; ++c)
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[c], __builtin_bit_cast(v8bf, xb[mt][c]), part, 0, 0, 0);
+        if (in) {
+          const v4f sc = *reinterpret_cast<const v4f*>(
+              gs + (s + u) * 16 + 4 * ((threadIdx.x % 64) / 16));
+          acc[mt] += part * sc;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[c], __builtin_bit_cast(v8bf, xb[mt][c]), acc[mt], 0, 0, 0);
+      }
     }
   }
 }
@@ -124,16 +143,28 @@ __device__ __forceinline__ void mma_batch_lds(const v4u (&w)[U][2], const char* 
 //               column is fed zeros)
 // All loads of a batch of U steps are issued unconditionally (at in-bounds addresses) before
 // the first is used; steps past s_end, chunks past k and rows past m get zero activations.
-template <int MT, int U>
+// GS: as in mma_batch_lds, with the step's scales of the lane's 4 channels read from global
+// memory with the batch (gsr[r]: the [k / 128] scale row of channel 4 * (lane / 16) + r).
+template <int MT, int U, bool GS = false>
 __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wrow,
                                                   const uint16_t* const (&xrow)[MT],
                                                   const bool (&xok)[MT], int64_t k,
-                                                  int s_begin, int s_end, v4f (&acc)[MT]) {
+                                                  int s_begin, int s_end, v4f (&acc)[MT],
+                                                  const float* const* gsr = nullptr) {
   const int lane = threadIdx.x % 64;
   const int sub = 32 * (lane / 16);  // this lane's 32 channels within a step
   for (int s = s_begin; s < s_end; s += U) {
     v4u w[U][2];
     v4u xr[U][MT][4];
+    v4f gsc[GS ? U : 1];
+    if constexpr (GS) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int st = min(s + u, s_end - 1);  // past the range: any valid scale (adds 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gsc[u][r] = gsr[r][st];
+      }
+    }
     load_weight_batch<U>(wrow, k, s, s_end, w);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -155,14 +186,20 @@ __device__ __forceinline__ void dequant_mma_steps(const int8_t* __restrict__ wro
       i8x16_to_bf16(w[u][0], a[0], a[1]);
       i8x16_to_bf16(w[u][1], a[2], a[3]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        v4f part = {0.f, 0.f, 0.f, 0.f};
+        v4f& dst = GS ? part : acc[mt];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const bool ok = in && xok[mt] && kk + 8 * c < k;
           const v4u xb = ok ? xr[u][mt][c] : v4u{0u, 0u, 0u, 0u};
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a[c], __builtin_bit_cast(v8bf, xb), acc[mt], 0, 0, 0);
+          dst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], __builtin_bit_cast(v8bf, xb), dst,
+                                                        0, 0, 0);
         }
+        if constexpr (GS) {
+          if (in) acc[mt] += part * gsc[u];
+        }
+      }
     }
   }
 }

@@ -37,6 +37,15 @@ hipError_t launch_grouped_w8a16_gemm(const void* x, int x_per_assignment, const 
                                      void* y, i8ql_dtype y_dtype, int64_t n, int64_t k,
                                      hipStream_t stream);
 
+// One scale per group of 128 input channels: q [n, k], scale [n, k / 128] (k % 128 == 0).
+hipError_t launch_quantize_groups128(const void* a, i8ql_dtype dtype, int64_t n, int64_t k,
+                                     int8_t* q, float* scale, hipStream_t stream);
+
+// W8A16 with w_scale [n, k / 128] (one scale per channel and group of 128 input channels).
+hipError_t launch_w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
+                                  const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream);
+
 // Gate/up over weights stacked [num_experts, 2n, k] (gate rows, then up rows) with the
 // SiLU·mul fused: h [t * topk, n] = silu(gate) * up.
 hipError_t launch_grouped_w8a16_silu_gemm(const void* x, int x_per_assignment,

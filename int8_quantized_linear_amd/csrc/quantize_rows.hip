@@ -285,7 +285,86 @@ hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* s
   return hipGetLastError();
 }
 
+// ---- one scale per group of 128 input channels ------------------------------------------
+// "Day 6 — Quantize It Yourself" (The mechanism, block 1): below per-output-channel scales
+// lies one scale per group of 128 weights along the input dimension.  The rule per group is
+// the row rule above.  Since k is a multiple of 128, the [n, k] matrix is a plain sequence
+// of groups and the [n, k / 128] scale matrix lists them in the same order: thread i takes
+// elements 8i .. 8i + 7, sixteen consecutive lanes (one DPP row) hold one group, and the
+// group maximum is a four-step DPP reduction inside that row.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_groups128_kernel(const uint8_t* __restrict__ a,
+                                                                 int64_t total,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  const bool live = e < total;  // whole groups: a group's 16 lanes are all live or all not
+  const int64_t ee = live ? e : 0;
+  float f[8];
+  if constexpr (DT == I8QL_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(a + ee * 4);
+    widen_chunk<DT>(p[0], f);
+    widen_chunk<DT>(p[1], f + 4);
+  } else {
+    widen_chunk<DT>(*reinterpret_cast<const uint4*>(a + ee * 2), f);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  // group maximum: non-negative floats order like their bit patterns
+  int v = __float_as_int(amax);
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false));  // row_mirror
+  amax = __int_as_float(v);
+  if (!live) return;
+  const float s = amax / 127.0f;
+  int c[8];
+  if (s == 0.0f) {  // all-zero group: scale 1, codes 0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = 0;
+  } else if (s >= 0x1p-64f) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = code_from_quotient(quotient_fma(f[i], s, y));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = code_of(f[i], s);
+  }
+  uint2 packed;
+  packed.x = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) |
+             (static_cast<uint32_t>(c[3] & 0xff) << 24);
+  packed.y = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) |
+             (static_cast<uint32_t>(c[7] & 0xff) << 24);
+  *reinterpret_cast<uint2*>(q + e) = packed;
+  if (threadIdx.x % 16 == 0) scale[e / 128] = s == 0.0f ? 1.0f : s;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_groups128(const void* a, i8ql_dtype dtype, int64_t n, int64_t k,
+                                     int8_t* q, float* scale, hipStream_t stream) {
+  const int64_t total = n * k;
+  const dim3 grid(static_cast<unsigned>((total / 8 + 255) / 256));
+  const auto* src = static_cast<const uint8_t*>(a);
+  switch (dtype) {
+    case I8QL_F32:
+      hipLaunchKernelGGL(quantize_groups128_kernel<I8QL_F32>, grid, dim3(256), 0, stream, src,
+                         total, q, scale);
+      break;
+    case I8QL_BF16:
+      hipLaunchKernelGGL(quantize_groups128_kernel<I8QL_BF16>, grid, dim3(256), 0, stream, src,
+                         total, q, scale);
+      break;
+    case I8QL_F16:
+      hipLaunchKernelGGL(quantize_groups128_kernel<I8QL_F16>, grid, dim3(256), 0, stream, src,
+                         total, q, scale);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream) {

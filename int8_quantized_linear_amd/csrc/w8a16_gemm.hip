@@ -38,7 +38,11 @@ constexpr size_t kMaxStageLds = 96 * 1024;  // staged rows up to this much LDS (
 template <int MT, int WAVES>
 constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * MT * 64 * sizeof(v4f); }
 
-template <int MT, int WAVES, int YT, bool XLDS>
+// GS: w_scale holds one scale per (channel, group of 128 input channels), [n, k / 128]; the
+// step loop applies them per step (k % 128 == 0) and the epilogue applies bias only.  With
+// staged rows the tile's scales are staged too, as an LDS table [step][16 channels] after
+// the zero block (one direct-to-LDS dword per lane, issued before everything else).
+template <int MT, int WAVES, int YT, bool XLDS, bool GS = false>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, const float* __restrict__ bias, void* __restrict__ y,
@@ -69,6 +73,16 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m - m0));
     char* xzero = xs + 1024 * stage_insts(rows, k);
     if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
+    float* gs = reinterpret_cast<float*>(xzero + 16);
+    if constexpr (GS) {
+      // instruction i: steps 4i .. 4i + 3 of the 16 channels, lane l -> [4i + l / 16][l % 16]
+      const int64_t groups = k / kStepK;
+      const int64_t ch = min(n0 + lane % 16, n - 1);
+      for (int i = wave; i < static_cast<int>((groups + 3) / 4); i += WAVES) {
+        const int64_t st = min(static_cast<int64_t>(4 * i + lane / 16), groups - 1);
+        __builtin_amdgcn_global_load_lds(w_scale + ch * groups + st, gs + 64 * i, 4, 0, 0);
+      }
+    }
     stage_rows<WAVES>(x + m0 * k, nullptr, 1, rows, k, xs);
     asm volatile("" ::: "memory");  // the weight loads stay behind the copy (wait count below)
     __builtin_amdgcn_sched_barrier(0);
@@ -90,19 +104,25 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) xb[mt][c] = v4u{0u, 0u, 0u, 0u};
     }
-    mma_batch_lds<MT, kUnroll>(w, xrow, live, xzero, k, sb, se, xb, acc);
+    mma_batch_lds<MT, kUnroll, GS>(w, xrow, live, xzero, k, sb, se, xb, acc, gs);
     for (int s = sb + kUnroll; s < se; s += kUnroll) {
       load_weight_batch<kUnroll>(wrow, k, s, se, w);
       __builtin_amdgcn_sched_barrier(0);
-      mma_batch_lds<MT, kUnroll>(w, xrow, live, xzero, k, s, se, xb, acc);
+      mma_batch_lds<MT, kUnroll, GS>(w, xrow, live, xzero, k, s, se, xb, acc, gs);
     }
   } else {
     const uint16_t* xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       xrow[mt] = x + (xok[mt] ? m0 + mt * 16 + lane % 16 : 0) * k;
-    dequant_mma_steps<MT, (kGlobalUnroll / MT > 0 ? kGlobalUnroll / MT : 1)>(wrow, xrow, xok, k, sb,
-                                                                     se, acc);
+    const float* gsr[4];
+    if constexpr (GS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        gsr[r] = w_scale + min(n0 + 4 * (lane / 16) + r, n - 1) * (k / kStepK);
+    }
+    dequant_mma_steps<MT, (kGlobalUnroll / MT > 0 ? kGlobalUnroll / MT : 1), GS>(
+        wrow, xrow, xok, k, sb, se, acc, gsr);
   }
 
 #pragma unroll
@@ -116,7 +136,7 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t c = min(nc + r, n - 1);
-    sc[r] = w_scale[c];
+    sc[r] = GS ? 1.0f : w_scale[c];  // group scales were applied per step
     bs[r] = bias ? bias[c] : 0.0f;
   }
 #pragma unroll
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   }
 }
 
-template <int MT, int WAVES, int YT>
+template <int MT, int WAVES, int YT, bool GS>
 hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
                         const float* bias, void* y, int64_t m, int64_t n, int64_t k,
                         hipStream_t stream) {
@@ -150,12 +170,13 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
   const auto* xx = static_cast<const uint16_t*>(x);
   const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m));
   const size_t rbytes = red_bytes<MT, WAVES>();
-  const size_t xlds = rbytes + 1024 * static_cast<size_t>(stage_insts(rows, k)) + 16;
+  const size_t gs_bytes = GS ? 256 * static_cast<size_t>((k / kStepK + 3) / 4) : 0;
+  const size_t xlds = rbytes + 1024 * static_cast<size_t>(stage_insts(rows, k)) + 16 + gs_bytes;
   // (with more than 16 KiB of partial tiles, the rows of the k that calls for that many
   // waves never fit)
   constexpr bool can_stage = red_bytes<MT, WAVES>() <= kMaxDefaultLds / 4;
   if (can_stage && xlds <= kMaxStageLds) {
-    auto kern = w8a16_kernel<MT, WAVES, YT, can_stage>;
+    auto kern = w8a16_kernel<MT, WAVES, YT, can_stage, GS>;
     if (xlds > kMaxDefaultLds) {  // e.g. 8 rows of k = 4096: 70 KiB
       static bool configured = false;  // idempotent attribute set; a race only repeats it
       if (!configured) {
@@ -169,7 +190,7 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
     hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), xlds, stream, xx, wq, w_scale, bias, y, m,
                        n, k);
   } else {
-    hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, false>), grid, dim3(64 * WAVES),
+    hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, false, GS>), grid, dim3(64 * WAVES),
                        rbytes, stream, xx, wq, w_scale, bias, y, m, n, k);
   }
   return hipGetLastError();
@@ -180,23 +201,25 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
 // kUnroll still issues kUnroll steps of loads, so the count is matched to the steps).  One
 // 16-channel tile per workgroup: with N / 16 such workgroups the whole weight matrix is in
 // flight in about one occupancy round on 256 CUs for the decoder shapes.
-template <int MT, int YT>
+template <int MT, int YT, bool GS>
 hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int64_t steps = (k + kStepK - 1) / kStepK;
-  if (steps <= 4 * kUnroll) return launch_waves<MT, 4, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
-  if (steps <= 8 * kUnroll) return launch_waves<MT, 8, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (steps <= 4 * kUnroll)
+    return launch_waves<MT, 4, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (steps <= 8 * kUnroll)
+    return launch_waves<MT, 8, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
   if (steps <= 12 * kUnroll)
-    return launch_waves<MT, 12, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_waves<MT, 16, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+    return launch_waves<MT, 12, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_waves<MT, 16, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
-template <int YT>
+template <int YT, bool GS>
 hipError_t launch_yt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  if (m <= 16) return launch_mt<1, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
-  if (m <= 32) return launch_mt<2, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_mt<4, YT>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (m <= 16) return launch_mt<1, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  if (m <= 32) return launch_mt<2, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_mt<4, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace
@@ -205,8 +228,16 @@ hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_sca
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
                              int64_t n, int64_t k, hipStream_t stream) {
   if (y_dtype == I8QL_F32)
-    return launch_yt<I8QL_F32>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_yt<I8QL_BF16>(x, wq, w_scale, bias, y, m, n, k, stream);
+    return launch_yt<I8QL_F32, false>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_yt<I8QL_BF16, false>(x, wq, w_scale, bias, y, m, n, k, stream);
+}
+
+hipError_t launch_w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
+                                  const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream) {
+  if (y_dtype == I8QL_F32)
+    return launch_yt<I8QL_F32, true>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_yt<I8QL_BF16, true>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 }  // namespace i8ql

@@ -221,6 +221,31 @@ def test_grouped_silu_validation(lib):
     assert call(h=A2, ht=F32) == ALIGN
 
 
+def test_group_scale_validation(lib):
+    f = lib.quantize_per_group_int8
+    assert f(A16, I8, 4, 256, A16, A16, NUL) == DTYPE
+    assert f(A16, BF16, -1, 256, A16, A16, NUL) == SHAPE
+    assert f(A16, BF16, 4, 200, A16, A16, NUL) == SHAPE    # not a multiple of 128
+    assert f(A16, BF16, 4, 0, A16, A16, NUL) == SHAPE
+    assert f(NUL, BF16, 0, 256, NUL, NUL, NUL) == OK
+    assert f(NUL, BF16, 4, 256, A16, A16, NUL) == NULL
+    assert f(A4, BF16, 4, 256, A16, A16, NUL) == ALIGN
+    assert f(A16, BF16, 4, 256, A4, A16, NUL) == ALIGN
+    assert f(A16, BF16, 4, 256, A16, A2, NUL) == ALIGN
+    g = lib.w8a16_gemm_g128
+    call = lambda **kw: (lambda a: g(a["x"], a["wq"], a["sw"], a["b"], a["y"], a["yt"], a["m"],
+                                     a["n"], a["k"], NUL))(dict(dict(x=A16, wq=A16, sw=A16, b=NUL,
+                                                                     y=A16, yt=BF16, m=1, n=16,
+                                                                     k=256), **kw))
+    assert call(yt=I32) == DTYPE
+    assert call(k=192) == SHAPE
+    assert call(m=-1) == SHAPE
+    assert call(m=0, x=NUL) == OK
+    assert call(sw=NUL) == NULL
+    assert call(x=A4) == ALIGN
+    assert call(b=A2) == ALIGN
+
+
 def test_moe_route_validation(lib):
     f = lib.moe_route_topk
     base = dict(lg=A16, lt=F32, t=4, e=64, kr=6, ns=2, ids=A16, w=A16)
@@ -287,6 +312,8 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
         lambda: lib.grouped_w8a16_silu_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64,
                                             NUL),
         lambda: lib.moe_route_topk(A16, F32, 4, 64, 6, 2, A16, A16, NUL),
+        lambda: lib.quantize_per_group_int8(A16, BF16, 4, 256, A16, A16, NUL),
+        lambda: lib.w8a16_gemm_g128(A16, A16, A16, NUL, A16, BF16, 1, 16, 256, NUL),
         lambda: lib.moe_combine(A16, BF16, A16, 4, 8, 2048, A16, BF16, NUL),
     ]
     for call in calls:
