@@ -386,10 +386,37 @@ def section_decode(torch, i8, wl, dev, args, result):
                            "frac_hbm_kernels": gbs_kernels / PEAK_HBM_GBS,
                            "per_proj": per}
         log(f"[decode] M={m}: {secs/args.steps*1e6:.1f} us/layer, kernels {gbs_kernels:.0f} GB/s")
+    # The same layer with one scale per group of 128 input channels (w8a16_gemm_g128).
+    gq, gs = {}, {}
+    for nm, (n, k) in wl.DENSE_8B.items():
+        gq[nm], gs[nm] = i8.quantize_per_group_int8(wl.to_bf16(wl.weight(g, n, k)).to(dev))
+    g0 = {f: torch.cat([gq[p] for p in parts]).contiguous()
+          for f, parts in wl.DENSE_8B_FUSED.items()}
+    gs0 = {f: torch.cat([gs[p] for p in parts]).contiguous()
+           for f, parts in wl.DENSE_8B_FUSED.items()}
+    del gq, gs
+    gqs = [g0] + [{nm: g0[nm].clone() for nm in names} for _ in range(copies - 1)]
+    out["g128"] = {"per_m": {}}
+    for m in wl.DECODE_8B_BATCH:
+        xs = {k: wl.to_bf16(wl.activations(g, m, k)).to(dev) for k in (4096, 12288)}
+        ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in names}
+        def body_g(i):
+            wq = gqs[i % copies]
+            for nm in names:
+                n, k = shapes[nm]
+                i8.w8a16_gemm_g128(xs[k], wq[nm], gs0[nm], out=ys[nm])
+        secs = time_loop(torch, body_g, args.steps, args.warmup)
+        nbytes = sum(w8a16_bytes(m, n, k) + n * (k // 128 - 1) * 4 for n, k in shapes.values())
+        out["g128"]["per_m"][m] = {"layer_us": secs / args.steps * 1e6,
+                                   "GBs_layer": nbytes / (secs / args.steps) / 1e9}
+        log(f"[decode] g128 M={m}: {secs/args.steps*1e6:.1f} us/layer, "
+            f"{nbytes / (secs / args.steps) / 1e9:.0f} GB/s")
     out["traffic_m1"] = traffic_for("w8a16_kernel", "dense 8B decode layer M=1")
     m1 = out["per_m"][1]
     result["decode"] = {"workload": "dense 8B decoder projections, W8A16 decode, M in {1,4,8}; "
-                                    "q/k/v and gate/up as fused GEMMs (N 6144 and 24576)",
+                                    "q/k/v and gate/up as fused GEMMs (N 6144 and 24576); "
+                                    "'g128': the same layer with one scale per 128 input "
+                                    "channels",
                         "value": m1["GBs_kernels"], "unit": "GB/s",
                         "frac_hbm": m1["frac_hbm_kernels"], **out}
 
