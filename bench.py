@@ -572,6 +572,23 @@ def section_counters(torch, i8, wl, dev, args, result):
     result["counters"] = {"calibration_copy_bytes": CALIB_BYTES, "steps": 2}
 
 
+def section_counters_w8a8_large(torch, i8, wl, dev, args, result):
+    """Eager launches for stall-counter runs of the W8A8 main loop: three 8192 x 8192 x 8192
+    GEMMs with 256 x 256 tiles (configuration 0), bf16 output, random codes."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    m = n = k = 8192
+    xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=dev, generator=g)
+    wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=dev, generator=g)
+    sx = torch.rand(m, device=dev, generator=g)
+    sw = torch.rand(n, device=dev, generator=g)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        i8.w8a8_gemm_with_config(0, xq, sx, wq, sw, out=y)
+    torch.cuda.synchronize()
+    result["counters_w8a8_large"] = {"shape": [m, n, k], "config": 0, "launches": 3}
+
+
 def section_counters_decode(torch, i8, wl, dev, args, result):
     """Like `counters`, for the W8A16 decode layer: the calibration copy, then two passes of
     the fused 8B decode projections at M = 1 with rotating weight copies, kernel by kernel."""
@@ -668,6 +685,8 @@ def main():
         section_counters(torch, i8, wl, dev, args, result)
     if "counters_decode" in sections:
         section_counters_decode(torch, i8, wl, dev, args, result)
+    if "counters_w8a8_large" in sections:
+        section_counters_w8a8_large(torch, i8, wl, dev, args, result)
     print(json.dumps(result), flush=True)
 
 
