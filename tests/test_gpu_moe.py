@@ -243,3 +243,50 @@ def test_moe_block_chain_16b(ref, dev, t):
                        for p in range(ids_np.size)])
     check_float(d, dref, w8a16_tol(dref, absdot, n_i), f"down t={t}")
     run_combine(ref, dev, d, w, torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------------------
+# the block and the group-scale path replayed from a HIP graph
+
+def test_graph_replays_of_the_block_match_eager(ref, dev):
+    g = wl.rng(170)
+    e, n_i, hid, t = 10, 64, 256, 5
+    qgu, sgu, _, _ = moe_stack(ref, dev, g, 2 * n_i, hid, e)
+    qd, sd, _, _ = moe_stack(ref, dev, g, hid, n_i, e)
+    logits = torch.from_numpy(wl.router_logits(g, t, routed=e - 2)).to(dev)
+    x = wl.to_bf16(wl.activations(g, t, hid)).to(dev)
+    wg = wl.to_bf16(wl.weight(g, 96, 512)).to(dev)
+    xg = wl.to_bf16(wl.activations(g, 3, 512)).to(dev)
+    ids = torch.empty((t, 6), dtype=torch.int32, device=dev)
+    w = torch.empty((t, 6), dtype=torch.float32, device=dev)
+    h = torch.empty((t * 6, n_i), dtype=torch.bfloat16, device=dev)
+    d = torch.empty((t * 6, hid), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((t, hid), dtype=torch.bfloat16, device=dev)
+    qg = torch.empty((96, 512), dtype=torch.int8, device=dev)
+    sg = torch.empty((96, 4), dtype=torch.float32, device=dev)
+    yg = torch.empty((3, 96), dtype=torch.float32, device=dev)
+
+    def path():
+        i8.moe_route_topk(logits, 4, 2, ids_out=ids, weights_out=w)
+        i8.grouped_w8a16_silu_gemm(x, qgu, sgu, ids, out=h)
+        i8.grouped_w8a16_gemm(h, qd, sd, ids, x_per_assignment=True, out=d)
+        i8.moe_combine(d, w, out=y)
+        i8.quantize_per_group_int8(wg, q_out=qg, scale_out=sg)
+        i8.w8a16_gemm_g128(xg, qg, sg, out_dtype=torch.float32, out=yg)
+
+    outs = (ids, w, h, d, y, qg, sg, yg)
+    path()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        path()  # eager work between replays
+        torch.cuda.synchronize()
