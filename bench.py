@@ -641,7 +641,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards as described in DESIGN.md, but only the 1-GPU path is built)",
+              "(only the single-GPU path is built: column-parallel projections would shard N, "
+              "row-parallel ones K with an all-reduce, the MoE block its experts)",
               file=sys.stderr)
         sys.exit(2)
 
