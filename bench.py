@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "int8 GEMM TOPS (prefill) + decode GB/s, % of MI355X roofline"
 PEAK_INT8_TOPS = 5000.0     # dense int8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0       # HBM3E, MI355X
+PEAK_GFX_MHZ = 2400.0       # graphics clock the int8 peak is quoted at
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30      # rotate weight copies over at least this much memory
 
@@ -110,8 +111,10 @@ def graph_time(torch, body, iters, warmup=1, clock=None):
     two HIP events around its replay (no host launch overhead between kernels).  body(0) runs
     once eagerly first so that one-time setup never happens under capture, and the graph is
     replayed `warmup` times untimed before the timed replay.  With a `clock` dict, the graph
-    is then queued again for about two seconds (untimed) and the graphics clock is read while
-    it runs: clock["mhz"]."""
+    is then queued again for about three seconds (untimed) while a thread reads the graphics
+    clock over and over; amd-smi's reading trails the load by up to a second, so readings
+    from the first second and the last 0.2 s are dropped and clock["mhz"] is the median of
+    the rest (clock["samples"] of them)."""
     body(0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -128,11 +131,30 @@ def graph_time(torch, body, iters, warmup=1, clock=None):
     torch.cuda.synchronize()
     secs = start.elapsed_time(end) * 1e-3
     if clock is not None:
-        for _ in range(max(1, int(2.0 / max(secs, 1e-6)))):
+        import statistics
+        import threading
+        samples, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                t = time.time() - t0
+                v = gfx_clock_mhz()
+                if v is None:
+                    return
+                samples.append((t, v))
+
+        t0 = time.time()
+        for _ in range(max(1, int(3.0 / max(secs, 1e-6)))):
             g.replay()
-        time.sleep(0.3)
-        clock["mhz"] = gfx_clock_mhz()
+        th = threading.Thread(target=sample)
+        th.start()
         torch.cuda.synchronize()
+        busy = time.time() - t0
+        stop.set()
+        th.join()
+        keep = [v for t, v in samples if 1.0 <= t <= busy - 0.2]
+        clock["mhz"] = statistics.median(keep) if keep else None
+        clock["samples"] = len(keep)
     del g
     return secs
 
@@ -222,6 +244,7 @@ def section_step(torch, i8, wl, dev, args, result):
     ms = secs / args.steps * 1e3
     result.update(value=ops / (secs / args.steps) / 1e12, ms_per_step=ms)
     result["gfx_clock_mhz_during_step"] = clock.get("mhz")
+    result["gfx_clock_samples"] = clock.get("samples")
     log(f"[step] {ms:.4f} ms/step, {result['value']:.1f} TOPS")
 
     # Roofline pass: every GEMM and quantizer launch of the step, each repeated `reps` times
@@ -538,8 +561,9 @@ def section_prefill_8b(torch, i8, wl, dev, args, result):
             q, s_ = xq[k]
             i8.w8a8_gemm(q, s_, qw[nm], sw[nm], bias[nm], out=ys[nm])
 
+        clk = {}
         secs = time_loop(torch, lambda i: [call(nm) for nm in shapes], steps,
-                         max(1, args.warmup // 5))
+                         max(1, args.warmup // 5), clk)
         durs = {nm: per_call(torch, lambda i, nm=nm: call(nm), steps, 1) for nm in shapes}
         ops = sum(w8a8_ops(m, n, k) for n, k in shapes.values())
         per = {}
@@ -547,8 +571,16 @@ def section_prefill_8b(torch, i8, wl, dev, args, result):
             d = durs[nm]
             per[nm] = {"us": d * 1e6, "TOPS": w8a8_ops(m, n, k) / d / 1e12,
                        "frac_mfma": w8a8_ops(m, n, k) / d / 1e12 / PEAK_INT8_TOPS}
-        out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": ops / (secs / steps) / 1e12,
-                           "frac_mfma": ops / (secs / steps) / 1e12 / PEAK_INT8_TOPS,
+        tops = ops / (secs / steps) / 1e12
+        mhz = clk.get("mhz")
+        out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": tops,
+                           "frac_mfma": tops / PEAK_INT8_TOPS,
+                           # the layer's graph replayed for ~2 s: the sustained clock, and
+                           # the fraction of the int8 rate at that clock
+                           "gfx_clock_mhz_sustained": mhz,
+                           "gfx_clock_samples": clk.get("samples"),
+                           "frac_mfma_at_sustained_clock":
+                               tops / (PEAK_INT8_TOPS * mhz / PEAK_GFX_MHZ) if mhz else None,
                            "per_proj": per}
         log(f"[prefill_8b] M={m}: {out['per_m'][m]['TOPS']:.0f} TOPS")
     result["prefill_8b"] = {"workload": "dense 8B decoder projections, W8A8 prefill with bias, "
