@@ -111,11 +111,11 @@ def graph_time(torch, body, iters, warmup=1, clock=None, passes=1):
     two HIP events around its replay (no host launch overhead between kernels).  body(0) runs
     once eagerly first so that one-time setup never happens under capture, and the graph is
     replayed `warmup` times untimed before the timed replay (the fastest of `passes` timed
-    replays when passes > 1).  With a `clock` dict, the graph
-    is then queued again for about three seconds (untimed) while a thread reads the graphics
-    clock over and over; amd-smi's reading trails the load by up to a second, so readings
-    from the first second and the last 0.2 s are dropped and clock["mhz"] is the median of
-    the rest (clock["samples"] of them)."""
+    replays when passes > 1).  With a `clock` dict, the graph is then queued again for about
+    three seconds (untimed) while a thread reads the graphics clock over and over; amd-smi's
+    reading trails the load by up to a second, so readings from the first second and the
+    last 0.2 s are dropped and clock["mhz"] is the median of the rest (clock["samples"] of
+    them)."""
     body(0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -581,7 +581,7 @@ def section_prefill_8b(torch, i8, wl, dev, args, result):
         mhz = clk.get("mhz")
         out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": tops,
                            "frac_mfma": tops / PEAK_INT8_TOPS,
-                           # the layer's graph replayed for ~2 s: the sustained clock, and
+                           # the layer's graph replayed for ~3 s: the sustained clock, and
                            # the fraction of the int8 rate at that clock
                            "gfx_clock_mhz_sustained": mhz,
                            "gfx_clock_samples": clk.get("samples"),
