@@ -216,8 +216,8 @@ i8ql_status grouped_w8a16_gemm(const void* x, int x_per_assignment, const int8_t
 
 /*
  * One scale per group of I8QL_GROUP_SIZE input channels.  Defines: [Day6] The mechanism,
- * block 1 (who shares a scale: per tensor, per output channel, or per group of 128 weights
- * along the input dimension; an outlier then costs only its own group's precision).
+ * block 1 (a scale can cover a tensor, a row, or a run of 128 consecutive input channels;
+ * an outlier then coarsens only the codes of its own run).
  */
 #define I8QL_GROUP_SIZE 128
 

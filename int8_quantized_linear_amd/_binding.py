@@ -328,6 +328,8 @@ def w8a16_gemm_g128(x, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=Non
         raise ValueError("x, wq and w_scale disagree")
     if bias is not None:
         _check(bias, "bias", (torch.float32,), 1, dev)
+        if bias.shape[0] != n:
+            raise ValueError("bias must have N entries")
     y = _out(out, (m, n), out_dtype, dev)
     with torch.cuda.device(dev):
         _call("w8a16_gemm_g128", _ptr(x), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y),

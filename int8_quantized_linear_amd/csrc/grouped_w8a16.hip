@@ -373,16 +373,14 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
                        int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
                        hipStream_t stream) {
   constexpr int WAVES = KS * (SILU ? 2 : 1);
-  auto kern = grouped_w8a16_kernel<KS, BITMAP, SILU, YT>;
+  constexpr auto kern = grouped_w8a16_kernel<KS, BITMAP, SILU, YT>;
   // Rows staged per pass: an expert that each token picks at most once receives at most t
   // rows; one that receives more takes more passes (any count is handled).  Long rows stage
   // fewer per pass so that they fit the LDS budget (the caller bounds k so one row does).
   int pass_rows = static_cast<int>(min(static_cast<int64_t>(kMaxPassRows), t));
   while (pass_rows > 1 && xs_bytes(pass_rows, k) > kMaxStageBytes) --pass_rows;
   const size_t lds = red_bytes<WAVES>() + xs_bytes(pass_rows, k) + bitmap_bytes(num_experts);
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds));
+  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (e != hipSuccess) return e;
   // One row of workgroups per slot, after the row that handles invalid ids: one slot per
   // expert, or, with fewer assignments than experts, one per assignment (the most distinct

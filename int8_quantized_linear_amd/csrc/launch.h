@@ -8,9 +8,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "i8ql.h"
 
 namespace i8ql {
+
+// Raise kernel KERN's dynamic-LDS limit to at least `bytes` on the current device.  The
+// attribute is set once per (kernel, device) and again only when a call needs more than was
+// granted, so steady-state launches make no attribute call; concurrent first calls may both
+// set it, which is harmless.
+constexpr int kMaxDevices = 64;
+template <auto KERN>
+hipError_t allow_dynamic_lds(int bytes) {
+  static std::atomic<int> granted[kMaxDevices];  // static storage: starts at zero
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && granted[dev].load(std::memory_order_relaxed) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && tracked) {
+    int prev = granted[dev].load(std::memory_order_relaxed);
+    while (prev < bytes && !granted[dev].compare_exchange_weak(prev, bytes)) {
+    }
+  }
+  return e;
+}
 
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream);

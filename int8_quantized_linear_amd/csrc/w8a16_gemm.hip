@@ -6,7 +6,7 @@
 // ("Day 6 — Quantize It Yourself", the question it opens with), so the kernel is built to
 // read every weight byte from HBM exactly once at full bandwidth:
 //
-//   * a workgroup owns 16 output channels and up to 64 activation rows; its 4, 8 or 16
+//   * a workgroup owns 16 output channels and up to 64 activation rows; its 4, 8 or 12
 //     wavefronts split the input channels (in-workgroup split-K) so each weight row is
 //     streamed by many waves at once, and sum their partial tiles through LDS in a fixed
 //     order (deterministic, no atomics);
@@ -176,16 +176,10 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
   // waves never fit)
   constexpr bool can_stage = red_bytes<MT, WAVES>() <= kMaxDefaultLds / 4;
   if (can_stage && xlds <= kMaxStageLds) {
-    auto kern = w8a16_kernel<MT, WAVES, YT, can_stage, GS>;
+    constexpr auto kern = w8a16_kernel<MT, WAVES, YT, can_stage, GS>;
     if (xlds > kMaxDefaultLds) {  // e.g. 8 rows of k = 4096: 70 KiB
-      static bool configured = false;  // idempotent attribute set; a race only repeats it
-      if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(kMaxStageLds));
-        if (e != hipSuccess) return e;
-        configured = true;
-      }
+      const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(kMaxStageLds));
+      if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), xlds, stream, xx, wq, w_scale, bias, y, m,
                        n, k);
@@ -196,11 +190,13 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
   return hipGetLastError();
 }
 
-// Wavefronts per workgroup: the fewest of 4, 8, 12 and 16 with which each streams at most
+// Wavefronts per workgroup: the fewest of 4, 8 and 12 with which each streams at most
 // kUnroll steps of k (all its loads in flight at once; a wave with fewer real steps than
-// kUnroll still issues kUnroll steps of loads, so the count is matched to the steps).  One
-// 16-channel tile per workgroup: with N / 16 such workgroups the whole weight matrix is in
-// flight in about one occupancy round on 256 CUs for the decoder shapes.
+// kUnroll still issues kUnroll steps of loads, so the count is matched to the steps).  Longer
+// k keeps 12 wavefronts, each walking several batches: 16 wavefronts of 1024 threads would
+// cap the kernel at 128 registers and spill.  One 16-channel tile per workgroup: with N / 16
+// such workgroups the whole weight matrix is in flight in about one occupancy round on 256
+// CUs for the decoder shapes.
 template <int MT, int YT, bool GS>
 hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
@@ -209,9 +205,7 @@ hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, cons
     return launch_waves<MT, 4, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
   if (steps <= 8 * kUnroll)
     return launch_waves<MT, 8, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
-  if (steps <= 12 * kUnroll)
-    return launch_waves<MT, 12, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_waves<MT, 16, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_waves<MT, 12, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 template <int YT, bool GS>

@@ -531,8 +531,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   const int64_t n0 = tn * BN;
 
   const int lane = threadIdx.x % 64;
-  const int group = threadIdx.x / (64 * C::WAVES);  // k-group (in-workgroup split-K)
-  const int wave = (threadIdx.x / 64) % C::WAVES;   // wavefront within the k-group
+  // (readfirstlane: wavefront-uniform, so per-wave addressing can live in scalar registers)
+  const int group = __builtin_amdgcn_readfirstlane(threadIdx.x / (64 * C::WAVES));
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) % C::WAVES);
   const int wm = wave / WN, wn = wave % WN;
   // Each k-group walks its own equal share of the steps (KS > 1 only when it divides
   // evenly) in its own LDS stages; all groups pass the same barriers.
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_split(
   const int64_t m0 = tm * BM;
   const int64_t n0 = tn * BN;
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int wm = wave / WN, wn = wave % WN;
   const int ksteps = static_cast<int>((k + BK - 1) / BK);
   int8_t* const aslots = lds_all;
@@ -821,15 +822,9 @@ hipError_t launch_split(const int8_t* xq, const float* x_scale, const int8_t* wq
                         int64_t k, hipStream_t stream) {
   using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
   using P = SplitStages<C>;
-  auto kern = w8a8_kernel_split<BM, BN, BK, WM, WN, YT>;
-  static bool configured = false;  // idempotent attribute set; a race only repeats it
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(P::LDS_BYTES));
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  constexpr auto kern = w8a8_kernel_split<BM, BN, BK, WM, WN, YT>;
+  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(P::LDS_BYTES));
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), P::LDS_BYTES,
@@ -842,15 +837,9 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                       int64_t k, hipStream_t stream) {
   using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
-  auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT>;
-  static bool configured = false;  // idempotent attribute set; a race only repeats it
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(C::LDS_BYTES));
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT>;
+  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(C::LDS_BYTES));
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), C::LDS_BYTES,

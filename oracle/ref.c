@@ -311,9 +311,9 @@ void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, in
 /* ---- one scale per group of input channels --------------------------------------------- */
 
 /*
- * "Day 6 — Quantize It Yourself", The mechanism, block 1: the whole design space is who
- * shares a scale — per tensor, per output channel, or per group of 128 weights along the
- * input dimension.  Each group of `group` consecutive elements of a row gets the row
+ * "Day 6 — Quantize It Yourself", The mechanism, block 1: the scale may be shared by a
+ * whole tensor, by one row (output channel), or by a run of 128 consecutive elements of a
+ * row (input channels).  Each group of `group` consecutive elements of a row gets the row
  * quantizer's rule (float32 absmax / 127, float32 quotient, round half to even, clamp, the
  * all-zero guard).  q: [r, k]; s: [r, k / group], k % group == 0.
  */

@@ -6,11 +6,17 @@
   from float32 rounding for values that cancel).
 * bfloat16 outputs: y must be a value that round-to-nearest-even can produce from some
   float32 in [r - tol, r + tol], i.e. rne(lo) <= y <= rne(hi) (rounding is monotone).
+
+Also the small input/output helpers the GPU parity modules share (host tensors with the
+oracle's view of them, sentinel-filled outputs, the quantize-and-compare step).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
+
+import int8_quantized_linear_amd as i8
+from int8_quantized_linear_amd import workloads as wl
 
 U32 = 2.0 ** -24  # float32 unit roundoff
 
@@ -65,3 +71,38 @@ def w8a16_tol(ref: np.ndarray, absdot: np.ndarray, k: int, bias=None) -> np.ndar
     if bias is not None:
         floor = floor + 2 * U32 * np.abs(bias.astype(np.float64))[None, :]
     return 1e-3 * np.abs(ref) + floor
+
+
+def host(dtype, a32):
+    """Host tensor of the given dtype from float32 numpy + the oracle's view of it."""
+    if dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(a32, np.float32))
+        return t, t.numpy()
+    t = wl.to_bf16(a32) if dtype == "bf16" else wl.to_f16(a32)
+    return t, wl.bits16(t)
+
+
+def sentinel(shape, dtype, dev):
+    """Output buffer pre-filled so that an element the kernel fails to write cannot match:
+    NaN for float outputs, the 0xAAAAAAAA pattern for int32."""
+    if dtype == torch.int32:
+        return torch.full(shape, -0x55555556, dtype=torch.int32, device=dev)
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
+
+
+def quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token=False):
+    """Quantize on the GPU and with the oracle; codes and scales must be bitwise equal."""
+    fn = i8.quantize_per_token_int8 if per_token else i8.quantize_per_channel_int8
+    q, s = fn(t.to(dev))
+    qr, sr = ref.quantize_rows(view, dtype)
+    np.testing.assert_array_equal(q.cpu().numpy(), qr)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    return q, s, qr, sr
+
+
+def moe_stack(ref, dev, g, n, k, e):
+    """A stacked [e, n, k] expert weight quantized on both sides (checked bitwise)."""
+    w = wl.moe_weights(g, n, k, experts=e).reshape(e * n, k)
+    wt, wv = host("bf16", w)
+    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
+    return qw.view(e, n, k), sw.view(e, n), qwr.reshape(e, n, k), swr.reshape(e, n)

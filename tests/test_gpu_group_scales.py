@@ -8,8 +8,7 @@ import torch
 
 import int8_quantized_linear_amd as i8
 from int8_quantized_linear_amd import workloads as wl
-from parity import check_float, w8a16_tol
-from test_gpu_parity import host, sentinel
+from parity import check_float, host, sentinel, w8a16_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +80,11 @@ def test_w8a16_g128_small(ref, dev, m, n, k, out_dtype):
 @pytest.mark.parametrize("n,k", [(4096, 4096), (4096, 12288)])
 def test_w8a16_g128_dense_8b_decode(ref, dev, m, n, k):
     run_g128(ref, dev, wl.rng(160 + m), m, n, k, False, torch.bfloat16)
+
+
+def test_w8a16_g128_rejects_a_bias_of_the_wrong_length(dev):
+    q = torch.zeros((32, 256), dtype=torch.int8, device=dev)
+    s = torch.ones((32, 2), dtype=torch.float32, device=dev)
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        i8.w8a16_gemm_g128(x, q, s, torch.zeros(31, dtype=torch.float32, device=dev))

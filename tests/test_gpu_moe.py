@@ -12,8 +12,7 @@ import torch
 
 import int8_quantized_linear_amd as i8
 from int8_quantized_linear_amd import workloads as wl
-from parity import U32, check_float, to_np, w8a16_tol
-from test_gpu_parity import moe_stack, quant_gpu_vs_ref, sentinel
+from parity import U32, check_float, moe_stack, quant_gpu_vs_ref, sentinel, to_np, w8a16_tol
 
 pytestmark = pytest.mark.gpu
 

@@ -1,14 +1,17 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, on the same seeded
 inputs.  Codes, scales and int32 accumulators must be bitwise equal; float outputs follow
 the rules in tests/parity.py.  Small cases span several tiles and ragged tails; the
-decoder-shaped workloads run at full size (sampled rows where the oracle would be slow)."""
+decoder-shaped workloads run at full size, every row compared up to 4096 tokens (sampled
+rows only at 16384 tokens), each shape in float32 as well as in its bf16 (and, for W8A8,
+int32) output mode."""
 import numpy as np
 import pytest
 import torch
 
 import int8_quantized_linear_amd as i8
 from int8_quantized_linear_amd import workloads as wl
-from parity import check_float, to_np, w8a16_tol, w8a8_tol
+from parity import check_float, host, moe_stack, quant_gpu_vs_ref, sentinel, to_np, \
+    w8a16_tol, w8a8_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -27,32 +30,6 @@ def _name_the_case(request):
     yield
     if torch.cuda.is_available():
         torch.cuda.synchronize()
-
-
-def host(dtype, a32):
-    """Host tensor of the given dtype from float32 numpy + the oracle's view of it."""
-    if dtype == "f32":
-        t = torch.from_numpy(np.ascontiguousarray(a32, np.float32))
-        return t, t.numpy()
-    t = wl.to_bf16(a32) if dtype == "bf16" else wl.to_f16(a32)
-    return t, wl.bits16(t)
-
-
-def sentinel(shape, dtype, dev):
-    """Output buffer pre-filled so that an element the kernel fails to write cannot match:
-    NaN for float outputs, the 0xAAAAAAAA pattern for int32."""
-    if dtype == torch.int32:
-        return torch.full(shape, -0x55555556, dtype=torch.int32, device=dev)
-    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
-
-
-def quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token=False):
-    fn = i8.quantize_per_token_int8 if per_token else i8.quantize_per_channel_int8
-    q, s = fn(t.to(dev))
-    qr, sr = ref.quantize_rows(view, dtype)
-    np.testing.assert_array_equal(q.cpu().numpy(), qr)
-    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
-    return q, s, qr, sr
 
 
 # ---------------------------------------------------------------------------------------
@@ -335,7 +312,15 @@ PREFILL_8B = [(m, n, k) for m in wl.PREFILL_8B_TOKENS
               for (n, k) in sorted(set(wl.DENSE_8B.values()))]
 
 
+# Every output row is compared up to this many tokens; above it (the 16384-token shapes)
+# the first and last 8 rows and 256 seeded random rows are, and every element is checked to
+# have been written.
+FULL_ROWS_MAX_M = 4096
+
+
 def run_w8a8_full(ref, dev, m, n, k, frac, bias, seed):
+    """One decoder-shaped W8A8 product at full size: codes and scales of both operands, the
+    int32 accumulators, and the bf16 and float32 outputs of the fused epilogue."""
     g = wl.rng(seed)
     wt, wv = host("bf16", wl.weight(g, n, k))
     xt, xv = host("bf16", wl.activations(g, m, k, outlier_frac=frac))
@@ -343,21 +328,36 @@ def run_w8a8_full(ref, dev, m, n, k, frac, bias, seed):
     qw, sw = i8.quantize_per_channel_int8(wt.to(dev))
     qx, sx = i8.quantize_per_token_int8(xt.to(dev))
     b = torch.from_numpy(b_np).to(dev) if bias else None
-    y = i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=torch.bfloat16,
-                     out=sentinel((m, n), torch.bfloat16, dev))
+    ys = {od: i8.w8a8_gemm(qx, sx, qw, sw, b, out_dtype=od, out=sentinel((m, n), od, dev))
+          for od in (torch.bfloat16, torch.float32)}
     yi = i8.w8a8_gemm(qx, None, qw, None, out_dtype=torch.int32,
                       out=sentinel((m, n), torch.int32, dev))
-    assert not torch.isnan(y).any()  # every element written (rows not sampled included)
-    rows = sampled_rows(m, seed=seed)
     qwr, swr = ref.quantize_rows(wv, "bf16")
     np.testing.assert_array_equal(qw.cpu().numpy(), qwr)
     np.testing.assert_array_equal(sw.cpu().numpy(), swr)
-    qxr, sxr = ref.quantize_rows(xv[rows], "bf16")
-    np.testing.assert_array_equal(qx[torch.from_numpy(rows).to(dev)].cpu().numpy(), qxr)
+    if m <= FULL_ROWS_MAX_M:
+        rows = None
+        qxr, sxr = ref.quantize_rows(xv, "bf16")
+        np.testing.assert_array_equal(qx.cpu().numpy(), qxr)
+        np.testing.assert_array_equal(sx.cpu().numpy(), sxr)
+    else:
+        for y in ys.values():
+            assert not torch.isnan(y).any()  # every element written
+        # |acc| <= k * 127^2 < 0x55555556 here, so the int32 sentinel cannot be a result
+        assert k * 127 * 127 < 0x55555556 and not (yi == -0x55555556).any()
+        rows = sampled_rows(m, seed=seed)
+        qxr, sxr = ref.quantize_rows(xv[rows], "bf16")
+        idx = torch.from_numpy(rows).to(dev)
+        np.testing.assert_array_equal(qx[idx].cpu().numpy(), qxr)
+        np.testing.assert_array_equal(sx[idx].cpu().numpy(), sxr)
+        ys = {od: y[idx] for od, y in ys.items()}
+        yi = yi[idx]
     acc, yref = ref.w8a8(qxr, sxr, qwr, swr, b_np)
-    np.testing.assert_array_equal(yi.cpu().numpy()[rows], acc)
-    check_float(y[torch.from_numpy(rows).to(dev)], yref, w8a8_tol(acc, sxr, swr, b_np),
-                f"w8a8 {m}x{n}x{k}")
+    np.testing.assert_array_equal(yi.cpu().numpy(), acc)
+    tol = w8a8_tol(acc, sxr, swr, b_np)
+    del acc
+    for od, y in ys.items():
+        check_float(y, yref, tol, f"w8a8 {m}x{n}x{k} {od}")
 
 
 @pytest.mark.parametrize("m,n,k", PREFILL_4B)
@@ -405,6 +405,7 @@ DECODE_8B += [(m, sum(wl.DENSE_8B[p][0] for p in parts), wl.DENSE_8B[parts[0]][1
 
 @pytest.mark.parametrize("m,n,k", DECODE_8B)
 def test_w8a16_dense_8b_decode_full(ref, dev, m, n, k):
+    run_w8a16(ref, dev, m, n, k, bias=False, out_dtype=torch.float32, seed=m * n + k)
     y1 = run_w8a16(ref, dev, m, n, k, bias=False, out_dtype=torch.bfloat16, seed=m * n + k)
     # same inputs, same bits
     g = wl.rng(m * n + k)
@@ -416,13 +417,6 @@ def test_w8a16_dense_8b_decode_full(ref, dev, m, n, k):
 
 # ---------------------------------------------------------------------------------------
 # grouped W8A16 over experts
-
-def moe_stack(ref, dev, g, n, k, e):
-    w = wl.moe_weights(g, n, k, experts=e).reshape(e * n, k)
-    wt, wv = host("bf16", w)
-    qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
-    return qw.view(e, n, k), sw.view(e, n), qwr.reshape(e, n, k), swr.reshape(e, n)
-
 
 def run_grouped(ref, dev, qw, sw, qwr, swr, ids, x_rows, per_assign, out_dtype, g):
     e, n, k = qwr.shape
@@ -531,8 +525,9 @@ def test_grouped_moe_16b_full(ref, dev, t, proj):
     qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
     ids = wl.moe_expert_ids(g, t)
     per_assign = proj == "down"
-    run_grouped(ref, dev, qw, sw, qwr, swr, ids, t * ids.shape[1] if per_assign else t,
-                per_assign, torch.bfloat16, g)
+    for od in (torch.bfloat16, torch.float32):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, t * ids.shape[1] if per_assign else t,
+                    per_assign, od, g)
 
 
 # ---------------------------------------------------------------------------------------

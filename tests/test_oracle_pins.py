@@ -531,8 +531,8 @@ def test_p14_combine_is_the_weighted_sum(ref):
 
 # ---------------------------------------------------------------------------------------
 # P15–P16 one scale per group of 128 input channels ("Day 6 — Quantize It Yourself", The
-# mechanism, block 1: the design space is who shares a scale, down to groups of 128 weights
-# along the input dimension; Q1 there: an outlier only costs its own group's precision).
+# mechanism, block 1: a scale can cover a tensor, a row, or 128 consecutive input channels;
+# with groups, an outlier coarsens only the codes of its own group).
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_p15_group_quantizer_is_the_row_rule_per_group(ref, dtype):
