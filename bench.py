@@ -1,24 +1,25 @@
 """Benchmark of the int8 quantized linear hot path on one MI355X.
 
-A step is one pass of the W8A8 prefill path over the dense 4B decoder layer (q, k, v, o,
-gate, up, down projections) at M = 128, 512 and 2048 tokens: per-token int8 quantization
-of the four distinct layer inputs, then the int8 MFMA GEMMs with the fused scale epilogue
-to bf16.  Projections that read the same input run as one GEMM over their concatenated
-weights (q/k/v: N = 6144; gate/up: N = 19456), as a serving engine launches them: four
-GEMMs per M with exactly the products of the seven projections.  ``value`` is the step's int8 throughput (2*M*N*K ops per GEMM summed,
-over the whole step time, quantization included), with every input resident in HBM.  Weight
-copies are rotated so every GEMM reads weights that are not in the 256 MB Infinity Cache.
-After W eager warm-up steps, exactly K steps are captured in one HIP graph and replayed
-between two HIP events (after one untimed replay), as an inference engine would launch
-them; the graph holds the same kernels on the same stream, so host launch overhead does
-not enter the kernel timings.
+The headline step is one W8A8 prefill pass of the dense 8B decoder layer (hidden 4096,
+intermediate 12288) over 16384 tokens: per-token int8 quantization of the layer's four
+distinct inputs, then the int8 MFMA GEMMs with the fused scale + bias epilogue to bf16.
+Projections that read the same input run as one GEMM over their concatenated weights
+(q/k/v: N = 6144; gate/up: N = 24576), as a serving engine launches them: four GEMMs with
+exactly the products of the seven projections.  ``value`` is the step's int8 throughput
+(2*M*N*K ops summed over the seven projections, over the whole step time, quantization
+included), with every input resident in HBM.  Weight copies are rotated so every GEMM reads
+weights that are not in the 256 MB Infinity Cache.  After W eager warm-up steps, exactly K
+steps are captured in one HIP graph and replayed between two HIP events (after one untimed
+replay), as an inference engine would launch them; the graph holds the same kernels on the
+same stream, so host launch overhead does not enter the kernel timings.
 
-The same JSON line also carries the other rows of the path, each timed on its own workload:
-W8A16 decode on 8B shapes (M = 1, 4, 8), the grouped MoE W8A16 GEMM (T = 1..64 tokens),
-W8A8 prefill at scale on 8B shapes (M = 4096, 16384, with bias), and the per-channel weight
-quantizer; plus ``roofline`` for the dominant kernel (HIP-event durations of every launch
-of it in a second timed pass) and ``cpu_baseline`` (the CPU oracle on a bounded sample of
-the step).
+The same JSON line also carries ``roofline`` (the W8A8 kernel over the step's launches, each
+repeated on its own between HIP events on the kernels' stream, classified MFMA- or HBM-bound
+by its algorithmic work), ``cpu_baseline`` (the CPU oracle on a bounded sample of the step),
+and the other rows of the path, each timed on its own workload: the same layer at 4096
+tokens, the dense 4B layer at 128/512/2048 tokens, W8A16 decode on 8B shapes (M = 1, 4, 8)
+next to a measured copy floor, the grouped MoE W8A16 GEMM and block (T = 1..64 tokens), and
+the per-channel weight quantizer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections a,b,...]
 """
@@ -181,123 +182,204 @@ def time_loop(torch, body, steps, warmup, clock=None):
 # ---------------------------------------------------------------------------------------
 # sections
 
-def prefill_4b_setup(torch, i8, wl, dev):
-    g = wl.rng(0)
-    # per-channel quantization of each projection's weights, then concatenation of the
-    # projections that share an input (row-wise quantization commutes with it)
-    pq, ps = {}, {}
-    layer_bytes = 0
-    for nm, (n, k) in wl.DENSE_4B.items():
-        w = wl.to_bf16(wl.weight(g, n, k)).to(dev)
-        pq[nm], ps[nm] = i8.quantize_per_channel_int8(w)
-        layer_bytes += n * k
-        del w
-    names = list(wl.DENSE_4B_FUSED)
-    q0 = {f: torch.cat([pq[p] for p in parts]).contiguous()
-          for f, parts in wl.DENSE_4B_FUSED.items()}
-    s0 = {f: torch.cat([ps[p] for p in parts]).contiguous()
-          for f, parts in wl.DENSE_4B_FUSED.items()}
-    del pq, ps
-    copies = max(2, -(-ROTATE_BYTES // layer_bytes))
-    qs = [q0] + [{nm: q0[nm].clone() for nm in names} for _ in range(copies - 1)]
-    # layer inputs: attention input (q/k/v), attention output (o), MLP input (gate/up),
-    # MLP hidden (down); N(0,1) with 0.1% outlier dims x100
-    xs = {}
-    for m in wl.PREFILL_4B_TOKENS:
-        xs[m] = {
-            "attn_in": wl.to_bf16(wl.activations(g, m, 2560, 0.001)).to(dev),
-            "attn_out": wl.to_bf16(wl.activations(g, m, 4096, 0.001)).to(dev),
-            "mlp_in": wl.to_bf16(wl.activations(g, m, 2560, 0.001)).to(dev),
-            "mlp_mid": wl.to_bf16(wl.activations(g, m, 9728, 0.001)).to(dev),
-        }
-    src = {"qkv": "attn_in", "o": "attn_out", "gate_up": "mlp_in", "down": "mlp_mid"}
-    shape = {f: (q0[f].shape[0], q0[f].shape[1]) for f in names}
-    # preallocated outputs
-    outs = {m: {nm: torch.empty((m, shape[nm][0]), dtype=torch.bfloat16, device=dev)
-                for nm in names} for m in wl.PREFILL_4B_TOKENS}
-    qx = {m: {key: (torch.empty(x.shape, dtype=torch.int8, device=dev),
-                    torch.empty((x.shape[0],), dtype=torch.float32, device=dev))
-              for key, x in xs[m].items()} for m in wl.PREFILL_4B_TOKENS}
-    return dict(qs=qs, s=s0, xs=xs, src=src, outs=outs, qx=qx, names=names, copies=copies,
-                shape=shape)
+def launch_bound(ops, nbytes, secs):
+    """Which roofline bounds one launch (the larger of its MFMA time at 5.0 POP/s and its
+    HBM time at 8 TB/s for the algorithmic work), and the fraction of that bound reached."""
+    t_mfma = ops / (PEAK_INT8_TOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    return ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm) / secs
 
 
-def prefill_4b_step(i8, wl, st, step):
-    for mi, m in enumerate(wl.PREFILL_4B_TOKENS):
-        wq = st["qs"][(step * len(wl.PREFILL_4B_TOKENS) + mi) % st["copies"]]
-        for key, x in st["xs"][m].items():
-            q, s = st["qx"][m][key]
-            i8.quantize_per_token_int8(x, q, s)
-        for nm in st["names"]:
-            q, s = st["qx"][m][st["src"][nm]]
-            i8.w8a8_gemm(q, s, wq[nm], st["s"][nm], None, out=st["outs"][m][nm])
+class PrefillWorkload:
+    """One W8A8 prefill layer: per-token quantization of its four distinct inputs (attention
+    in/out, MLP in/mid), then one GEMM per group of projections that read the same input
+    (q/k/v and gate/up over concatenated weights), with the fused scale (+bias) epilogue to
+    bf16.  Weight copies rotate over at least ROTATE_BYTES so that no timed GEMM reads its
+    weights from the Infinity Cache."""
+
+    INPUTS = ("attn_in", "attn_out", "mlp_in", "mlp_mid")
+    SRC = {"qkv": "attn_in", "o": "attn_out", "gate_up": "mlp_in", "down": "mlp_mid"}
+
+    def __init__(self, torch, i8, wl, dev, shapes, fused, tokens, frac, bias, seed):
+        self.torch, self.i8, self.wl = torch, i8, wl
+        self.tokens, self.shapes = tokens, shapes
+        g = wl.rng(seed)
+        pq, ps, pb = {}, {}, {}
+        layer_bytes = 0
+        for nm, (n, k) in shapes.items():
+            w = wl.to_bf16(wl.weight(g, n, k)).to(dev)
+            pq[nm], ps[nm] = i8.quantize_per_channel_int8(w)
+            layer_bytes += n * k
+            del w
+            if bias:
+                pb[nm] = torch.from_numpy(g.standard_normal(n, dtype=np.float32)
+                                          * np.float32(0.02)).to(dev)
+        self.names = list(fused)
+        # per-channel quantization is row-wise, so concatenated codes and scales are exactly
+        # those of the separate projections
+        q0 = {f: torch.cat([pq[p] for p in parts]).contiguous() for f, parts in fused.items()}
+        self.s = {f: torch.cat([ps[p] for p in parts]).contiguous() for f, parts in fused.items()}
+        self.b = ({f: torch.cat([pb[p] for p in parts]).contiguous() for f, parts in fused.items()}
+                  if bias else {f: None for f in fused})
+        del pq, ps, pb
+        self.copies = max(2, -(-ROTATE_BYTES // layer_bytes))
+        self.qs = [q0] + [{nm: q0[nm].clone() for nm in self.names}
+                          for _ in range(self.copies - 1)]
+        self.shape = {f: (q0[f].shape[0], q0[f].shape[1]) for f in self.names}
+        kin = {"attn_in": self.shape["qkv"][1], "attn_out": self.shape["o"][1],
+               "mlp_in": self.shape["gate_up"][1], "mlp_mid": self.shape["down"][1]}
+        self.kin = kin
+        self.xs, self.qx, self.outs = {}, {}, {}
+        for m in tokens:
+            self.xs[m] = {key: wl.to_bf16(wl.activations(g, m, kin[key], frac)).to(dev)
+                          for key in self.INPUTS}
+            self.qx[m] = {key: (torch.empty((m, kin[key]), dtype=torch.int8, device=dev),
+                                torch.empty((m,), dtype=torch.float32, device=dev))
+                          for key in self.INPUTS}
+            self.outs[m] = {nm: torch.empty((m, self.shape[nm][0]), dtype=torch.bfloat16,
+                                            device=dev) for nm in self.names}
+        self.bias = bias
+
+    def ops(self):
+        return sum(w8a8_ops(m, n, k) for m in self.tokens for (n, k) in self.shape.values())
+
+    def quantize(self, m, key):
+        q, s = self.qx[m][key]
+        self.i8.quantize_per_token_int8(self.xs[m][key], q, s)
+
+    def gemm(self, m, nm, copy):
+        q, s = self.qx[m][self.SRC[nm]]
+        self.i8.w8a8_gemm(q, s, self.qs[copy % self.copies][nm], self.s[nm], self.b[nm],
+                          out=self.outs[m][nm])
+
+    def step(self, i):
+        for mi, m in enumerate(self.tokens):
+            for key in self.INPUTS:
+                self.quantize(m, key)
+            for nm in self.names:
+                self.gemm(m, nm, i * len(self.tokens) + mi)
 
 
-def prefill_4b_work():
-    import int8_quantized_linear_amd.workloads as wl
-    ops = sum(w8a8_ops(m, n, k) for m in wl.PREFILL_4B_TOKENS for (n, k) in wl.DENSE_4B.values())
-    return ops
+def measure_prefill(torch, wl, wk, args, label, clock=True):
+    """Time `args.steps` steps from one HIP graph after `args.warmup` eager ones, then every
+    launch of the step on its own (repeated back to back in a graph between two HIP events on
+    the kernels' stream, weight copies rotating as in the step)."""
+    ops = wk.ops()
+    log(f"[{label}] {wk.copies} weight copies; warmup {args.warmup}, steps {args.steps}")
+    clk = {} if clock else None
+    secs = time_loop(torch, wk.step, args.steps, args.warmup, clk)
+    out = {"ms_per_step": secs / args.steps * 1e3, "TOPS": ops / (secs / args.steps) / 1e12}
+    if clock:
+        out["gfx_clock_mhz_during_step"] = clk.get("mhz")
+        out["gfx_clock_samples"] = clk.get("samples")
+    log(f"[{label}] {out['ms_per_step']:.4f} ms/step, {out['TOPS']:.1f} TOPS")
+    reps = max(5, args.steps // 5)
+    per, quant = [], []
+    for m in wk.tokens:
+        for key in wk.INPUTS:
+            sec = time_loop(torch, lambda i, m=m, key=key: wk.quantize(m, key), reps, 2) / reps
+            quant.append({"m": m, "k": wk.kin[key], "input": key, "us": sec * 1e6,
+                          "GBs": quant_bytes(m, wk.kin[key]) / sec / 1e9})
+        for nm in wk.names:
+            sec = time_loop(torch, lambda i, m=m, nm=nm: wk.gemm(m, nm, i), reps, 2) / reps
+            n, k = wk.shape[nm]
+            o, b = w8a8_ops(m, n, k), w8a8_bytes(m, n, k, bias=wk.bias)
+            bound, frac = launch_bound(o, b, sec)
+            per.append({"m": m, "n": n, "k": k, "proj": nm, "us": sec * 1e6, "ops": o,
+                        "bytes": b, "TOPS": o / sec / 1e12, "GBs": b / sec / 1e9,
+                        "bound": bound, "frac_of_bound": frac,
+                        "frac_mfma": o / sec / 1e12 / PEAK_INT8_TOPS,
+                        "frac_hbm": b / sec / 1e9 / PEAK_HBM_GBS})
+    t_gemm = sum(p["us"] for p in per) * 1e-6
+    t_quant = sum(q["us"] for q in quant) * 1e-6
+    qbytes = sum(quant_bytes(q["m"], q["k"]) for q in quant)
+    out["per_launch"] = per
+    out["quantize_per_token"] = {"launches": quant, "us_per_step": t_quant * 1e6,
+                                 "GBs": qbytes / t_quant / 1e9,
+                                 "frac_hbm": qbytes / t_quant / 1e9 / PEAK_HBM_GBS}
+    out["w8a8_gemm_us_per_step"] = t_gemm * 1e6
+    return out
+
+
+def w8a8_roofline(per, traffic):
+    """The roofline entry of the W8A8 kernel over a step's GEMM launches: the bound that
+    holds for most of the kernel time, achieved = algorithmic work / summed average launch
+    durations (int8 TOPS against 5.0 POP/s, or GB/s against 8 TB/s)."""
+    t = sum(p["us"] for p in per) * 1e-6
+    t_mfma = sum(p["us"] for p in per if p["bound"] == "mfma") * 1e-6
+    bound = "mfma" if t_mfma >= t / 2 else "hbm"
+    n = len(per)
+    if bound == "mfma":
+        ach, peak, unit = sum(p["ops"] for p in per) / t / 1e12, PEAK_INT8_TOPS, "TOPS"
+    else:
+        ach, peak, unit = sum(p["bytes"] for p in per) / t / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"kernel": "w8a8_kernel (all tile instantiations)", "bound": bound,
+            "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "traffic": traffic, "avg_launch_us": t / n * 1e6, "launches_per_step": n,
+            "ops_per_launch": sum(p["ops"] for p in per) / n,
+            "algorithmic_bytes_per_launch": sum(p["bytes"] for p in per) / n,
+            "launches_by_bound": {b: sum(1 for p in per if p["bound"] == b)
+                                  for b in ("mfma", "hbm")}}
+
+
+HEADLINE = "dense 8B W8A8 prefill step M=16384"
+
+
+def prefill_8b(torch, i8, wl, dev, tokens):
+    return PrefillWorkload(torch, i8, wl, dev, wl.DENSE_8B, wl.DENSE_8B_FUSED, tokens, 0.01,
+                           True, seed=3)
+
+
+def prefill_4b(torch, i8, wl, dev):
+    return PrefillWorkload(torch, i8, wl, dev, wl.DENSE_4B, wl.DENSE_4B_FUSED,
+                           wl.PREFILL_4B_TOKENS, 0.001, False, seed=0)
 
 
 def section_step(torch, i8, wl, dev, args, result):
-    st = prefill_4b_setup(torch, i8, wl, dev)
-    ops = prefill_4b_work()
-    log(f"[step] dense 4B W8A8 prefill, {st['copies']} weight copies; warmup {args.warmup}, "
-        f"steps {args.steps}")
-    clock = {}
-    secs = time_loop(torch, lambda i: prefill_4b_step(i8, wl, st, i), args.steps, args.warmup,
-                     clock)
-    ms = secs / args.steps * 1e3
-    result.update(value=ops / (secs / args.steps) / 1e12, ms_per_step=ms)
-    result["gfx_clock_mhz_during_step"] = clock.get("mhz")
-    result["gfx_clock_samples"] = clock.get("samples")
-    log(f"[step] {ms:.4f} ms/step, {result['value']:.1f} TOPS")
+    """The headline: the dense 8B decoder layer's W8A8 prefill at 16384 tokens."""
+    wk = prefill_8b(torch, i8, wl, dev, (16384,))
+    out = measure_prefill(torch, wl, wk, args, "step")
+    result.update(value=out["TOPS"], ms_per_step=out["ms_per_step"])
+    result["gfx_clock_mhz_during_step"] = out["gfx_clock_mhz_during_step"]
+    result["gfx_clock_samples"] = out["gfx_clock_samples"]
+    mhz = out["gfx_clock_mhz_during_step"]
+    result["frac_mfma_step"] = out["TOPS"] / PEAK_INT8_TOPS
+    result["frac_mfma_step_at_sustained_clock"] = (
+        out["TOPS"] / (PEAK_INT8_TOPS * mhz / PEAK_GFX_MHZ) if mhz else None)
+    result["roofline"] = w8a8_roofline(out["per_launch"], traffic_for("w8a8_kernel", HEADLINE))
+    result["per_launch"] = out["per_launch"]
+    result["quantize_per_token"] = out["quantize_per_token"]
+    result["parts_us_per_step"] = {"w8a8_gemm": out["w8a8_gemm_us_per_step"],
+                                   "quantize_per_token": out["quantize_per_token"]["us_per_step"]}
+    rf = result["roofline"]
+    log(f"[step] roofline {rf['bound']}: {rf['achieved']:.0f} {rf['unit']} = "
+        f"{100 * rf['frac']:.1f}% (avg launch {rf['avg_launch_us']:.2f} us)")
+    del wk
+    torch.cuda.empty_cache()
 
-    # Roofline pass: every GEMM and quantizer launch of the step, each repeated `reps` times
-    # back to back between two HIP events on the kernels' stream (torch's current stream),
-    # with the weight copies rotating exactly as in the step.  Events around single launches
-    # would add their own overhead to every launch.
-    reps = max(5, args.steps // 5)
-    names = st["names"]
-    gemm_t, quant_t = {}, {}
-    for mi, m in enumerate(wl.PREFILL_4B_TOKENS):
-        for key, x in st["xs"][m].items():
-            q, s_ = st["qx"][m][key]
-            sec = time_loop(torch, lambda i, x=x, q=q, s_=s_: i8.quantize_per_token_int8(x, q, s_),
-                            reps, 2)
-            quant_t[(m, key)] = sec / reps
-        for nm in names:
-            q, s_ = st["qx"][m][st["src"][nm]]
-            sec = time_loop(torch, lambda i, nm=nm, q=q, s_=s_, m=m: i8.w8a8_gemm(
-                q, s_, st["qs"][i % st["copies"]][nm], st["s"][nm], None, out=st["outs"][m][nm]),
-                reps, 2)
-            gemm_t[(m, nm)] = sec / reps
-    n_gemm = len(gemm_t)
-    avg = sum(gemm_t.values()) / n_gemm
-    ach = ops / sum(gemm_t.values()) / 1e12
-    result["roofline"] = {
-        "kernel": "w8a8_kernel (all tile instantiations)", "bound": "mfma", "achieved": ach,
-        "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": ach / PEAK_INT8_TOPS,
-        "traffic": traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"),
-        "avg_launch_us": avg * 1e6, "launches_per_step": n_gemm,
-        "ops_per_launch": ops / n_gemm,
-    }
-    qsum = sum(quant_t.values())
-    qbytes = sum(quant_bytes(m, k) for m in wl.PREFILL_4B_TOKENS for k in (2560, 4096, 2560, 9728))
-    result["parts"] = {
-        "w8a8_gemm_ms_per_step": sum(gemm_t.values()) * 1e3,
-        "quantize_per_token_ms_per_step": qsum * 1e3,
-        "quantize_per_token_GBs": qbytes / qsum / 1e9,
-    }
-    result["per_shape"] = []
-    for (m, nm), t in gemm_t.items():
-        n, k = st["shape"][nm]
-        result["per_shape"].append({
-            "m": m, "n": n, "k": k, "proj": nm, "us": t * 1e6,
-            "TOPS": w8a8_ops(m, n, k) / t / 1e12,
-            "frac_mfma": w8a8_ops(m, n, k) / t / 1e12 / PEAK_INT8_TOPS,
-            "frac_hbm": w8a8_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS})
-    return st
+
+def section_prefill_8b_m4096(torch, i8, wl, dev, args, result):
+    wk = prefill_8b(torch, i8, wl, dev, (4096,))
+    out = measure_prefill(torch, wl, wk, args, "prefill_8b_m4096")
+    out["roofline"] = w8a8_roofline(out["per_launch"], None)
+    result["prefill_8b_m4096"] = {
+        "workload": "dense 8B decoder layer, W8A8 prefill at 4096 tokens (the same step as the "
+                    "headline at its other token count)", "unit": "TOPS", **out}
+    del wk
+    torch.cuda.empty_cache()
+
+
+def section_prefill_4b(torch, i8, wl, dev, args, result):
+    wk = prefill_4b(torch, i8, wl, dev)
+    out = measure_prefill(torch, wl, wk, args, "prefill_4b", clock=False)
+    out["roofline"] = w8a8_roofline(out["per_launch"],
+                                    traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"))
+    result["prefill_4b"] = {
+        "workload": "dense 4B decoder layer (q 2560->4096, k/v 2560->1024, o 4096->2560, "
+                    "gate/up 2560->9728, down 9728->2560), W8A8 prefill at M in {128, 512, "
+                    "2048} per step, no bias, 0.1% outlier dims x100", "unit": "TOPS", **out}
+    del wk
+    torch.cuda.empty_cache()
 
 
 def traffic_for(kernel, workload):
@@ -313,61 +395,70 @@ def traffic_for(kernel, workload):
     return ent["bytes_per_launch"]
 
 
+CPU_SAMPLE_ROWS = 2048  # token rows of the headline step the oracle is timed on
+
+
 def section_cpu_baseline(i8, wl, args, result):
+    """The oracle as it stands, on a bounded sample of the headline workload: the first
+    CPU_SAMPLE_ROWS of the 16384 token rows through all seven projections of the 8B layer
+    (per-token quantization, exact int32 GEMM, float64 epilogue with bias), on every host
+    thread; rows are independent, so the rate is the step's rate."""
     import oracle
     ref = oracle.load()
     threads = len(os.sched_getaffinity(0))
     ref.set_threads(threads)
-    g = wl.rng(0)
-    frac = 1  # the whole step (about 6 s on 16 threads)
-    ws = {nm: wl.bits16(wl.to_bf16(wl.weight(g, n, k))) for nm, (n, k) in wl.DENSE_4B.items()}
-    wq = {nm: ref.quantize_rows(w, "bf16") for nm, w in ws.items()}
-    ins = {"q": 2560, "k": 2560, "v": 2560, "o": 4096, "gate": 2560, "up": 2560, "down": 9728}
-    keys = {"attn_in": 2560, "attn_out": 4096, "mlp_in": 2560, "mlp_mid": 9728}
+    g = wl.rng(5)
+    shapes = wl.DENSE_8B
+    ws = {nm: ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+          for nm, (n, k) in shapes.items()}
+    bias = {nm: (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+            for nm, (n, k) in shapes.items()}
     src = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out", "gate": "mlp_in",
            "up": "mlp_in", "down": "mlp_mid"}
-    rows_total = 0
-    xs = {}
-    for m in wl.PREFILL_4B_TOKENS:
-        r = m // frac
-        rows_total += r
-        xs[m] = {key: wl.bits16(wl.to_bf16(wl.activations(g, r, k, 0.001)))
-                 for key, k in keys.items()}
+    kin = {"attn_in": 4096, "attn_out": 4096, "mlp_in": 4096, "mlp_mid": 12288}
+    r = CPU_SAMPLE_ROWS
+    xs = {key: wl.bits16(wl.to_bf16(wl.activations(g, r, k, 0.01))) for key, k in kin.items()}
     ops = 0.0
     t0 = time.perf_counter()
-    for m in wl.PREFILL_4B_TOKENS:
-        qx = {key: ref.quantize_rows(x, "bf16") for key, x in xs[m].items()}
-        for nm in wl.DENSE_4B:
-            q, s = qx[src[nm]]
-            n, k = wl.DENSE_4B[nm]
-            ref.w8a8(q, s, wq[nm][0], wq[nm][1])
-            ops += w8a8_ops(q.shape[0], n, k)
+    qx = {key: ref.quantize_rows(x, "bf16") for key, x in xs.items()}
+    for nm, (n, k) in shapes.items():
+        q, s_ = qx[src[nm]]
+        ref.w8a8(q, s_, ws[nm][0], ws[nm][1], bias[nm])
+        ops += w8a8_ops(r, n, k)
     dt = time.perf_counter() - t0
-    # one thread: the tiny fp32 case and the 128-token q projection
     single = {}
     ref.set_threads(1)
     t = wl.tiny_w8a8(0)
     t0 = time.perf_counter()
     qw, sw = ref.quantize_rows(t["w"], "f32")
-    qx, sx = ref.quantize_rows(t["x"], "f32")
-    ref.w8a8(qx, sx, qw, sw)
+    qxt, sxt = ref.quantize_rows(t["x"], "f32")
+    ref.w8a8(qxt, sxt, qw, sw)
     single["tiny 4x256x512 (quantize both + GEMM)"] = time.perf_counter() - t0
-    n, k = wl.DENSE_4B["q"]
-    xq = wl.bits16(wl.to_bf16(wl.activations(g, 128, k, 0.001)))
     t0 = time.perf_counter()
-    q, s_ = ref.quantize_rows(xq, "bf16")
-    ref.w8a8(q, s_, wq["q"][0], wq["q"][1])
-    single["q 128x4096x2560 (quantize tokens + GEMM)"] = time.perf_counter() - t0
+    q, s_ = ref.quantize_rows(xs["attn_in"][:128], "bf16")
+    ref.w8a8(q, s_, ws["q"][0], ws["q"][1], bias["q"])
+    single["q 128x4096x4096 (quantize tokens + GEMM)"] = time.perf_counter() - t0
     ref.set_threads(threads)
-    name = "the whole step" if frac == 1 else f"the step's first 1/{frac} of tokens at each M"
     result["cpu_baseline"] = {
         "value": ops / dt / 1e12, "unit": "TOPS", "cores": ref.threads(), "kind": "oracle",
-        "sample": f"{name} ({rows_total} of {sum(wl.PREFILL_4B_TOKENS)} token rows, all 7 "
-                  f"projections): per-token quantization + int32 GEMM + float64 epilogue; "
-                  f"{dt:.1f} s",
+        "sample": f"the headline step's first {r} of 16384 token rows through all 7 "
+                  f"projections of the 8B layer: per-token quantization + int32 GEMM + "
+                  f"float64 epilogue with bias; {dt:.1f} s",
         "seconds": dt, "single_thread_seconds": single}
     log(f"[cpu_baseline] {ops/dt/1e12*1e3:.2f} GOP/s on {ref.threads()} threads, {dt:.1f} s; "
         f"1 thread: {single}")
+
+
+def copy_floor(torch, dev, nbytes, reps):
+    """Seconds per device-to-device copy of nbytes / 2 bytes (nbytes through HBM: half read,
+    half written), graph-replayed with the sources rotating over at least ROTATE_BYTES."""
+    half = max(16, int(nbytes) // 2 // 16 * 16)
+    copies = max(2, -(-ROTATE_BYTES // half))
+    src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    t = per_call(torch, lambda i: dst.copy_(src[i % copies]), reps)
+    del src, dst
+    return t
 
 
 def section_decode(torch, i8, wl, dev, args, result):
@@ -388,6 +479,14 @@ def section_decode(torch, i8, wl, dev, args, result):
     copies = max(2, -(-ROTATE_BYTES // layer))
     qs = [q0] + [{nm: q0[nm].clone() for nm in names} for _ in range(copies - 1)]
     out = {"copies": copies, "per_m": {}}
+    floors = {nm: copy_floor(torch, dev, w8a16_bytes(1, *shapes[nm]), max(5, args.steps // 5))
+              for nm in names}
+    out["floor_copy"] = {
+        "what": "a device-to-device copy (torch copy_, graph-replayed, sources rotating over "
+                ">= 1 GiB) that moves as many bytes through HBM as the projection's M=1 "
+                "algorithmic bytes: half of them read, half written",
+        "per_proj": {nm: {"us": t * 1e6, "GBs": w8a16_bytes(1, *shapes[nm]) / t / 1e9}
+                     for nm, t in floors.items()}}
     for m in wl.DECODE_8B_BATCH:
         xs = {k: wl.to_bf16(wl.activations(g, m, k)).to(dev) for k in (4096, 12288)}
         ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in names}
@@ -407,7 +506,8 @@ def section_decode(torch, i8, wl, dev, args, result):
             t = durs[nm]
             per[nm] = {"n": n, "k": k, "us": t * 1e6,
                        "GBs": w8a16_bytes(m, n, k) / t / 1e9,
-                       "frac_hbm": w8a16_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS}
+                       "frac_hbm": w8a16_bytes(m, n, k) / t / 1e9 / PEAK_HBM_GBS,
+                       "vs_copy_floor": t / floors[nm]}
         gbs_kernels = nbytes / sum(durs.values()) / 1e9
         out["per_m"][m] = {"layer_us": secs / args.steps * 1e6,
                            "GBs_layer": nbytes / (secs / args.steps) / 1e9,
@@ -546,68 +646,38 @@ def section_moe(torch, i8, wl, dev, args, result):
                      "SiLU·mul + down + combine", "unit": "GB/s", **out}
 
 
-def section_prefill_8b(torch, i8, wl, dev, args, result):
-    g = wl.rng(3)
-    shapes = wl.DENSE_8B
-    qw, sw, bias = {}, {}, {}
-    for nm, (n, k) in shapes.items():
-        qw[nm], sw[nm] = i8.quantize_per_channel_int8(wl.to_bf16(wl.weight(g, n, k)).to(dev))
-        bias[nm] = torch.from_numpy(g.standard_normal(n, dtype=np.float32) * np.float32(0.02)).to(dev)
-    out = {"per_m": {}}
-    steps = max(3, args.steps // 10)
-    for m in wl.PREFILL_8B_TOKENS:
-        xq = {}
-        for k in (4096, 12288):
-            x = wl.to_bf16(wl.activations(g, m, k, 0.01)).to(dev)
-            xq[k] = i8.quantize_per_token_int8(x)
-            del x
-        ys = {nm: torch.empty((m, shapes[nm][0]), dtype=torch.bfloat16, device=dev) for nm in shapes}
-        def call(nm):
-            n, k = shapes[nm]
-            q, s_ = xq[k]
-            i8.w8a8_gemm(q, s_, qw[nm], sw[nm], bias[nm], out=ys[nm])
-
-        clk = {}
-        secs = time_loop(torch, lambda i: [call(nm) for nm in shapes], steps,
-                         max(1, args.warmup // 5), clk)
-        durs = {nm: per_call(torch, lambda i, nm=nm: call(nm), steps, 1) for nm in shapes}
-        ops = sum(w8a8_ops(m, n, k) for n, k in shapes.values())
-        per = {}
-        for nm, (n, k) in shapes.items():
-            d = durs[nm]
-            per[nm] = {"us": d * 1e6, "TOPS": w8a8_ops(m, n, k) / d / 1e12,
-                       "frac_mfma": w8a8_ops(m, n, k) / d / 1e12 / PEAK_INT8_TOPS}
-        tops = ops / (secs / steps) / 1e12
-        mhz = clk.get("mhz")
-        out["per_m"][m] = {"layer_ms": secs / steps * 1e3, "TOPS": tops,
-                           "frac_mfma": tops / PEAK_INT8_TOPS,
-                           # the layer's graph replayed for ~3 s: the sustained clock, and
-                           # the fraction of the int8 rate at that clock
-                           "gfx_clock_mhz_sustained": mhz,
-                           "gfx_clock_samples": clk.get("samples"),
-                           "frac_mfma_at_sustained_clock":
-                               tops / (PEAK_INT8_TOPS * mhz / PEAK_GFX_MHZ) if mhz else None,
-                           "per_proj": per}
-        log(f"[prefill_8b] M={m}: {out['per_m'][m]['TOPS']:.0f} TOPS")
-    result["prefill_8b"] = {"workload": "dense 8B decoder projections, W8A8 prefill with bias, "
-                            "M in {4096,16384}", "unit": "TOPS", **out}
-
-
-def section_counters(torch, i8, wl, dev, args, result):
-    """Eager launches for the hardware-counter runs (rocprofv3 --pmc FETCH_SIZE, then
-    WRITE_SIZE): first a 256 MiB device-to-device copy whose counter readings calibrate the
-    counters (it moves exactly 256 MiB each way), then two steps of the benchmark workload
-    with its weight rotation, each kernel launched on its own."""
-    st = prefill_4b_setup(torch, i8, wl, dev)
+def calibration_copy(torch, dev):
+    """A device-to-device copy of CALIB_BYTES, whose counter readings calibrate FETCH_SIZE
+    and WRITE_SIZE (it moves exactly CALIB_BYTES each way)."""
     a = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
+    del a, b
+
+
+def section_counters(torch, i8, wl, dev, args, result):
+    """Eager launches for the hardware-counter runs of the headline step (rocprofv3 --pmc
+    FETCH_SIZE, then WRITE_SIZE): the calibration copy, then two steps of the workload with
+    its weight rotation, each kernel launched on its own."""
+    wk = prefill_8b(torch, i8, wl, dev, (16384,))
+    calibration_copy(torch, dev)
     for step in range(2):
-        prefill_4b_step(i8, wl, st, step)
+        wk.step(step)
     torch.cuda.synchronize()
-    result["counters"] = {"calibration_copy_bytes": CALIB_BYTES, "steps": 2}
+    result["counters"] = {"workload": HEADLINE, "calibration_copy_bytes": CALIB_BYTES,
+                          "steps": 2}
+
+
+def section_counters_4b(torch, i8, wl, dev, args, result):
+    """As `counters`, for the dense 4B prefill step."""
+    wk = prefill_4b(torch, i8, wl, dev)
+    calibration_copy(torch, dev)
+    for step in range(2):
+        wk.step(step)
+    torch.cuda.synchronize()
+    result["counters_4b"] = {"calibration_copy_bytes": CALIB_BYTES, "steps": 2}
 
 
 def section_counters_w8a8_large(torch, i8, wl, dev, args, result):
@@ -670,17 +740,35 @@ def section_weight_quant(torch, i8, wl, dev, args, result):
     log(f"[weight_quant] {gbs:.0f} GB/s")
 
 
+SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DEFAULT
+    "step": section_step, "prefill_8b_m4096": section_prefill_8b_m4096,
+    "prefill_4b": section_prefill_4b, "decode": section_decode, "moe": section_moe,
+    "weight_quant": section_weight_quant,
+    # hardware-counter runs only (eager launches, nothing timed)
+    "counters": section_counters, "counters_4b": section_counters_4b,
+    "counters_decode": section_counters_decode,
+    "counters_w8a8_large": section_counters_w8a8_large,
+}
+DEFAULT = "step,cpu_baseline,prefill_8b_m4096,prefill_4b,decode,moe,weight_quant"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sections", default="step,cpu_baseline,decode,moe,prefill_8b,weight_quant")
+    ap.add_argument("--sections", default=DEFAULT)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(only the single-GPU path is built: column-parallel projections would shard N, "
               "row-parallel ones K with an all-reduce, the MoE block its experts)",
+              file=sys.stderr)
+        sys.exit(2)
+    sections = args.sections.split(",")
+    unknown = [x for x in sections if x not in SECTIONS and x != "cpu_baseline"]
+    if unknown:
+        print(f"unknown sections {unknown}; known: cpu_baseline, {', '.join(SECTIONS)}",
               file=sys.stderr)
         sys.exit(2)
 
@@ -692,40 +780,31 @@ def main():
         sys.exit(1)
     i8.load_library()
     dev = torch.device("cuda:0")
-    sections = args.sections.split(",")
     result = {"metric": METRIC, "value": None, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-              "config": {"workload": "dense 4B decoder projections (q 2560->4096, k/v "
-                         "2560->1024, o 4096->2560, gate/up 2560->9728, down 9728->2560), "
-                         "W8A8 prefill: per-token int8 quantization + int8 MFMA GEMM + "
-                         "scale epilogue to bf16, M in {128, 512, 2048} tokens per step",
+              "config": {"workload": "W8A8 prefill at scale on the dense 8B decoder layer "
+                         "(hidden 4096, intermediate 12288: q/o 4096->4096, k/v 4096->1024, "
+                         "gate/up 4096->12288, down 12288->4096), 16384 tokens per step: "
+                         "per-token int8 quantization of the layer's 4 inputs + int8 MFMA "
+                         "GEMMs with the fused scale + bias epilogue to bf16",
                          "launches": "q/k/v and gate/up each run as one GEMM over their "
-                                     "concatenated weights (N 6144 and 19456): 4 quantizer + "
-                                     "4 GEMM launches per M, the same products as 7 "
+                                     "concatenated weights (N 6144 and 24576): 4 quantizer + "
+                                     "4 GEMM launches per step, the same products as 7 "
                                      "separate projections",
-                         "tokens_per_step": sum(wl.PREFILL_4B_TOKENS),
-                         "weights": "bf16 N(0,0.02) -> per-channel int8",
-                         "activations": "bf16 N(0,1), 0.1% outlier dims x100"},
+                         "tokens_per_step": 16384,
+                         "weights": "bf16 N(0,0.02) -> per-channel int8; bias fp32 N(0,0.02)",
+                         "activations": "bf16 N(0,1), 1% outlier dims x100",
+                         "also_measured": "the same layer at 4096 tokens (prefill_8b_m4096), "
+                                          "the dense 4B layer at 128/512/2048 tokens "
+                                          "(prefill_4b), W8A16 decode, the grouped MoE "
+                                          "GEMM and block, the weight quantizer"},
               "device": torch.cuda.get_device_name(0)}
-    if "step" in sections:
-        section_step(torch, i8, wl, dev, args, result)
-    if "cpu_baseline" in sections:
-        section_cpu_baseline(i8, wl, args, result)
-    if "decode" in sections:
-        section_decode(torch, i8, wl, dev, args, result)
-    if "moe" in sections:
-        section_moe(torch, i8, wl, dev, args, result)
-    if "prefill_8b" in sections:
-        section_prefill_8b(torch, i8, wl, dev, args, result)
-    if "weight_quant" in sections:
-        section_weight_quant(torch, i8, wl, dev, args, result)
-    if "counters" in sections:  # only for hardware-counter runs, not in the default list
-        section_counters(torch, i8, wl, dev, args, result)
-    if "counters_decode" in sections:
-        section_counters_decode(torch, i8, wl, dev, args, result)
-    if "counters_w8a8_large" in sections:
-        section_counters_w8a8_large(torch, i8, wl, dev, args, result)
+    for name in sections:
+        if name == "cpu_baseline":
+            section_cpu_baseline(i8, wl, args, result)
+        else:
+            SECTIONS[name](torch, i8, wl, dev, args, result)
     print(json.dumps(result), flush=True)
 
 
