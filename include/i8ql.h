@@ -13,9 +13,10 @@
  *   - Every tensor is dense and row-major with no padding: a [R, C] tensor has row stride C
  *     elements.  Weights use the nn.Linear layout [N, K] (output channel, input channel);
  *     activations are [M, K] (one row per token).  Y = X * W^T has shape [M, N].
- *   - Ownership: the caller owns every buffer.  The library allocates no device or host
- *     memory, keeps no pointer after a call returns and holds no mutable global state apart
- *     from the thread-local error slot read by i8ql_last_hip_error().
+ *   - Ownership: the caller owns every buffer, including the W8A8 workspace.  The library
+ *     allocates no device or host memory, keeps no pointer after a call returns and holds
+ *     no mutable global state apart from the thread-local error slot read by
+ *     i8ql_last_hip_error() and per-device caches of launch settings (set once, idempotent).
  *   - Asynchrony: a call validates its arguments on the host, enqueues its kernels on
  *     `stream` (a hipStream_t passed as void*; NULL selects the null stream) and returns.
  *     It never synchronizes.  Results are ready once the stream reaches that point.
@@ -26,7 +27,7 @@
  *     Negative dimensions return I8QL_ERR_SHAPE.
  *   - Outputs must not overlap inputs or each other.
  *   - Results are deterministic: the same inputs give bitwise the same outputs on every
- *     call (no atomics take part in any output).
+ *     call (the only atomics count arrivals; no output value depends on their order).
  *   - Inputs must be finite; NaN or Inf inputs give unspecified (but in-bounds) results.
  */
 #ifndef I8QL_H
@@ -54,7 +55,8 @@ typedef enum {
   I8QL_ERR_ALIGN = 4,       /* GEMM: k % 16 != 0, or an operand base pointer is not 16-byte aligned */
   I8QL_ERR_K_TOO_LARGE = 5, /* w8a8_gemm: k > 133144, so an int32 accumulator could overflow */
   I8QL_ERR_ARG = 6,         /* invalid combination: bias with I32 output, topk < 1, experts < 1, ... */
-  I8QL_ERR_HIP = 7          /* the HIP runtime reported an error; see i8ql_last_hip_error() */
+  I8QL_ERR_HIP = 7,         /* the HIP runtime reported an error; see i8ql_last_hip_error() */
+  I8QL_ERR_WORKSPACE = 8    /* the requested W8A8 plan needs more workspace than was given */
 } i8ql_status;
 
 /* Largest K for which k * 127 * 127 fits in a signed 32-bit accumulator (133144 * 16129 =
@@ -130,34 +132,73 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       int64_t m, int64_t n, int64_t k, void* stream);
 
 /*
- * W8A8 tile configurations: introspection and explicit selection, for tuning and for tests
- * that cover every configuration.
+ * W8A8 plans: tile configurations, k split across workgroups, the workspace a split needs;
+ * introspection and explicit selection, for tuning and for tests that cover every plan.
  *
- * w8a8_gemm launches one of I8QL_W8A8_NUM_CONFIGS tile configurations, chosen per call by
- * a cost model of the launch time on MI355X (rounds of output tiles over the device's
- * compute units, k steps per tile).  Every configuration computes bitwise the same outputs
- * (exact int32 accumulation, the same float32 epilogue), so the choice affects only speed.
+ * A plan is one of I8QL_W8A8_NUM_CONFIGS tile configurations and a split count p: with
+ * p > 1 the k steps of every output tile are divided between p workgroups, which store their
+ * int32 partial tiles in a caller-provided workspace; the last of them to finish adds the
+ * others' partials to its own and applies the epilogue.  int32 addition is exact, so every
+ * plan computes bitwise the same outputs (exact accumulation, the same float32 epilogue) and
+ * the choice affects only speed.  w8a8_gemm takes no workspace and launches the cost
+ * model's best plan without a split; w8a8_gemm_with_plan launches the best plan whose
+ * workspace fits in the one it is given (a model of the launch time on MI355X: rounds of
+ * work units over the device's compute units, k steps per unit, the split's fix-up).
  *
- * w8a8_gemm_config_info(config, out3): writes {tile rows, tile columns, k-groups} of the
- *   configuration to out3 (host, 3 int32).  A configuration with g > 1 k-groups splits k
- *   inside the workgroup and accepts only k % (128 * g) == 0.
- *   Errors: out3 NULL -> I8QL_ERR_NULL; config outside [0, I8QL_W8A8_NUM_CONFIGS) ->
+ * Workspace contract: device memory, 16-byte aligned, zero-filled before its first use.
+ * Its first bytes are per-tile arrival counters, which every call returns to zero, so the
+ * same workspace serves any later call without clearing.  Calls that may overlap in time
+ * (different streams) must not share a workspace.
+ *
+ * w8a8_gemm_config_info(config, out4): writes {tile rows, tile columns, k-groups, 1 if k may
+ *   be split across workgroups else 0} of the configuration (host, 4 int32).  A
+ *   configuration with g > 1 k-groups splits k inside the workgroup and accepts only
+ *   k % (128 * g) == 0.
+ *   Errors: out4 NULL -> I8QL_ERR_NULL; config outside [0, I8QL_W8A8_NUM_CONFIGS) ->
  *   I8QL_ERR_ARG.
  * w8a8_gemm_choose_config(m, n, k, cus): the configuration w8a8_gemm launches for an
  *   m x n x k product on a device with `cus` compute units (host arithmetic only, no HIP
  *   call); -1 if the sizes are not a valid non-empty w8a8_gemm call or cus < 1.
- * w8a8_gemm_with_config(config, ...): w8a8_gemm with the given configuration (config == -1:
- *   the cost model's choice, exactly w8a8_gemm).  Arguments, results and errors as for
- *   w8a8_gemm, plus: config outside [-1, I8QL_W8A8_NUM_CONFIGS), or a configuration with
- *   g > 1 k-groups and k % (128 * g) != 0 -> I8QL_ERR_ARG.
+ * w8a8_gemm_with_config(config, ...): w8a8_gemm with the given configuration and no split
+ *   (config == -1: the cost model's choice, exactly w8a8_gemm).  Arguments, results and
+ *   errors as for w8a8_gemm, plus: config outside [-1, I8QL_W8A8_NUM_CONFIGS), or a
+ *   configuration with g > 1 k-groups and k % (128 * g) != 0 -> I8QL_ERR_ARG.
+ * w8a8_gemm_choose_plan(m, n, k, cus, workspace_bytes, out2): writes {config, splits} of the
+ *   plan w8a8_gemm_with_plan(-1, -1, ...) launches with a workspace of workspace_bytes
+ *   (host, 2 int32).  Errors: out2 NULL -> I8QL_ERR_NULL; invalid sizes, cus < 1 or
+ *   workspace_bytes < 0 -> I8QL_ERR_ARG.
+ * w8a8_gemm_workspace_size(config, splits, m, n, k, cus): the workspace bytes plan
+ *   (config, splits) needs for an m x n x k product (0 without a split); with (-1, -1), those
+ *   of the plan the cost model prefers on `cus` compute units with no limit on the
+ *   workspace, which w8a8_gemm_with_plan(-1, -1, ...) then launches when given that much.
+ *   -1 for invalid sizes or an invalid plan.
+ * w8a8_gemm_with_plan(config, splits, ..., workspace, workspace_bytes, stream): w8a8_gemm
+ *   with plan (config, splits), or with (-1, -1) the cost model's best plan whose workspace
+ *   fits in workspace_bytes (workspace may be NULL with workspace_bytes 0: no split).
+ *   workspace: device, workspace_bytes bytes, per the workspace contract above.
+ *   Arguments, results and errors as for w8a8_gemm_with_config, plus: config == -1 with
+ *   splits != -1, config >= 0 with splits outside [1, I8QL_W8A8_MAX_SPLITS], splits > 1 on a
+ *   configuration that cannot split or with more splits than k steps of 128, or
+ *   workspace_bytes < 0 -> I8QL_ERR_ARG; the plan needs workspace but workspace is NULL ->
+ *   I8QL_ERR_NULL; workspace not 16-byte aligned -> I8QL_ERR_ALIGN; workspace_bytes below
+ *   what the plan needs -> I8QL_ERR_WORKSPACE.
  */
 #define I8QL_W8A8_NUM_CONFIGS 12
-i8ql_status w8a8_gemm_config_info(int config, int32_t* out3);
+#define I8QL_W8A8_MAX_SPLITS 8
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out4);
 int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus);
 i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
                                   const int8_t* wq, const float* w_scale, const float* bias,
                                   void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
                                   void* stream);
+i8ql_status w8a8_gemm_choose_plan(int64_t m, int64_t n, int64_t k, int cus,
+                                  int64_t workspace_bytes, int32_t* out2);
+int64_t w8a8_gemm_workspace_size(int config, int splits, int64_t m, int64_t n, int64_t k,
+                                 int cus);
+i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const float* x_scale,
+                                const int8_t* wq, const float* w_scale, const float* bias,
+                                void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * w8a16_gemm — weight-only int8 GEMM for decode: int8 weights are dequantized in registers

@@ -21,12 +21,14 @@ _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8Q
           torch.int8: I8QL_I8, torch.int32: I8QL_I32}
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
-           "w8a8_gemm_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
+           "w8a8_gemm_with_config", "w8a8_gemm_choose_plan", "w8a8_gemm_workspace_size",
+           "w8a8_gemm_with_plan", "grouped_w8a16_silu_gemm", "moe_route_topk",
            "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128", "i8ql_status_string",
            "i8ql_last_hip_error")
 GROUP_SIZE = 128  # I8QL_GROUP_SIZE
 ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
 W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
+W8A8_MAX_SPLITS = 8  # I8QL_W8A8_MAX_SPLITS
 
 
 class I8qlError(RuntimeError):
@@ -61,6 +63,12 @@ def load_library(path: str = LIB_PATH):
         lib.w8a8_gemm_config_info.restype = I
         lib.w8a8_gemm_choose_config.argtypes = [I64, I64, I64, I]
         lib.w8a8_gemm_choose_config.restype = I
+        lib.w8a8_gemm_choose_plan.argtypes = [I64, I64, I64, I, I64, P]
+        lib.w8a8_gemm_choose_plan.restype = I
+        lib.w8a8_gemm_workspace_size.argtypes = [I, I, I64, I64, I64, I]
+        lib.w8a8_gemm_workspace_size.restype = I64
+        lib.w8a8_gemm_with_plan.argtypes = [I, I, P, P, P, P, P, P, I, I64, I64, I64, P, I64, P]
+        lib.w8a8_gemm_with_plan.restype = I
         lib.w8a16_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a16_gemm.restype = I
         lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
@@ -149,15 +157,76 @@ def _out(out, shape, dtype, dev):
     return out
 
 
-def w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):
+def _cus(dev) -> int:
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _CUS:
+        _CUS[idx] = torch.cuda.get_device_properties(idx).multi_processor_count
+    return _CUS[idx]
+
+
+_CUS: dict = {}
+_WORKSPACE: dict = {}
+
+
+def w8a8_workspace(dev, nbytes: int) -> torch.Tensor:
+    """The W8A8 workspace this binding keeps for ``dev``: a zero-filled uint8 tensor of at
+    least ``nbytes``, grown (never inside a graph capture) when a call needs more.  The
+    kernels leave its counters at zero after every call, so it is reused without clearing.
+    Calls on several streams that may overlap must each pass a workspace of their own."""
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _WORKSPACE.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("w8a8_gemm needs a larger workspace during a graph capture: run "
+                               "the same call once before capturing it")
+        nbytes = max(int(nbytes), 1 << 20)
+        ws = torch.zeros(-(-nbytes // (1 << 20)) << 20, dtype=torch.uint8,
+                         device=torch.device("cuda", idx))
+        _WORKSPACE[idx] = ws
+    return ws
+
+
+def w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None,
+              workspace=None):
     """``y = (xq @ wq.T) * x_scale[:, None] * w_scale[None, :] (+ bias)``; int32 when
-    ``out_dtype`` is torch.int32 (then scales may be None and bias must be None)."""
-    return w8a8_gemm_with_config(-1, xq, x_scale, wq, w_scale, bias, out_dtype, out)
+    ``out_dtype`` is torch.int32 (then scales may be None and bias must be None).  Launches
+    the cost model's best plan, which may split k across workgroups through ``workspace``
+    (a zero-filled uint8 CUDA tensor) or, when None, the workspace kept per device."""
+    return w8a8_gemm_with_plan(-1, -1, xq, x_scale, wq, w_scale, bias, out_dtype, out,
+                               workspace)
 
 
 def w8a8_gemm_with_config(config, xq, x_scale, wq, w_scale, bias=None,
                           out_dtype=torch.bfloat16, out=None):
-    """``w8a8_gemm`` with tile configuration ``config`` (-1: the cost model's choice)."""
+    """``w8a8_gemm`` with tile configuration ``config`` and no split (-1: the cost model's
+    choice among plans without a split)."""
+    m, n, k, y, dev = _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out)
+    with torch.cuda.device(dev):
+        _call("w8a8_gemm_with_config", int(config), _ptr(xq), _ptr(x_scale), _ptr(wq),
+              _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
+    return y
+
+
+def w8a8_gemm_with_plan(config, splits, xq, x_scale, wq, w_scale, bias=None,
+                        out_dtype=torch.bfloat16, out=None, workspace=None):
+    """``w8a8_gemm`` with plan (``config``, ``splits``): k split across ``splits`` workgroups
+    per output tile; (-1, -1) is the cost model's best plan.  ``workspace``: a zero-filled
+    uint8 CUDA tensor, or None for the one kept per device."""
+    m, n, k, y, dev = _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out)
+    need = w8a8_gemm_workspace_size(m, n, k, _cus(dev), config, splits) if m and n else 0
+    if workspace is None:
+        workspace = w8a8_workspace(dev, need) if need > 0 else None
+    else:
+        _check(workspace, "workspace", (torch.uint8,), 1, dev)
+    nbytes = 0 if workspace is None else workspace.numel()
+    with torch.cuda.device(dev):
+        _call("w8a8_gemm_with_plan", int(config), int(splits), _ptr(xq), _ptr(x_scale),
+              _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k,
+              _ptr(workspace), nbytes, _stream(dev))
+    return y
+
+
+def _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out):
     _check(xq, "xq", (torch.int8,), 2)
     dev = xq.device
     _check(wq, "wq", (torch.int8,), 2, dev)
@@ -170,17 +239,14 @@ def w8a8_gemm_with_config(config, xq, x_scale, wq, w_scale, bias=None,
             _check(t, nm, (torch.float32,), 1, dev)
             if t.shape[0] != ln:
                 raise ValueError(f"{nm} must have {ln} entries")
-    y = _out(out, (m, n), out_dtype, dev)
-    with torch.cuda.device(dev):
-        _call("w8a8_gemm_with_config", int(config), _ptr(xq), _ptr(x_scale), _ptr(wq),
-              _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
-    return y
+    return m, n, k, _out(out, (m, n), out_dtype, dev), dev
 
 
 def w8a8_gemm_config_info(config: int):
-    """(tile rows, tile columns, k-groups) of W8A8 tile configuration ``config``."""
+    """(tile rows, tile columns, k-groups, splittable) of W8A8 tile configuration
+    ``config``."""
     lib = load_library()
-    out = (ctypes.c_int32 * 3)()
+    out = (ctypes.c_int32 * 4)()
     st = lib.w8a8_gemm_config_info(int(config), ctypes.cast(out, ctypes.c_void_p))
     if st != 0:
         raise I8qlError("w8a8_gemm_config_info", st, lib)
@@ -188,9 +254,30 @@ def w8a8_gemm_config_info(config: int):
 
 
 def w8a8_gemm_choose_config(m: int, n: int, k: int, cus: int = 256) -> int:
-    """The configuration ``w8a8_gemm`` launches for an m x n x k product on ``cus`` compute
-    units (-1 for sizes ``w8a8_gemm`` rejects); host arithmetic only."""
+    """The configuration ``w8a8_gemm`` launches without a workspace for an m x n x k product
+    on ``cus`` compute units (-1 for sizes ``w8a8_gemm`` rejects); host arithmetic only."""
     return load_library().w8a8_gemm_choose_config(m, n, k, cus)
+
+
+def w8a8_gemm_choose_plan(m: int, n: int, k: int, cus: int = 256,
+                          workspace_bytes: int = 1 << 62):
+    """(config, splits) the cost model launches with a workspace of ``workspace_bytes``."""
+    lib = load_library()
+    out = (ctypes.c_int32 * 2)()
+    st = lib.w8a8_gemm_choose_plan(m, n, k, cus, workspace_bytes,
+                                   ctypes.cast(out, ctypes.c_void_p))
+    if st != 0:
+        raise I8qlError("w8a8_gemm_choose_plan", st, lib)
+    return tuple(out)
+
+
+def w8a8_gemm_workspace_size(m: int, n: int, k: int, cus: int = 256, config: int = -1,
+                             splits: int = -1) -> int:
+    """Workspace bytes of plan (config, splits), or of the cost model's preferred plan."""
+    nb = load_library().w8a8_gemm_workspace_size(int(config), int(splits), m, n, k, cus)
+    if nb < 0:
+        raise ValueError(f"no valid W8A8 plan ({config}, {splits}) for {m}x{n}x{k}")
+    return nb
 
 
 def w8a16_gemm(x, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None):

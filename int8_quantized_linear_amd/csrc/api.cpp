@@ -35,6 +35,14 @@ int elem_bytes(i8ql_dtype d) {
 
 bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
 
+// W8A8 sizes: products within range, and one workgroup per 64 x 32 output tile (the
+// smallest tile) times the most splits within a one-dimensional grid.
+bool w8a8_sizes_ok(int64_t m, int64_t n, int64_t k) {
+  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return false;
+  const int64_t tm = (m + 63) / 64, tn = (n + 31) / 32;
+  return mul_ok(tm, tn) && tm * tn <= kMaxGridX - 8;
+}
+
 i8ql_status hip_status(hipError_t e) {
   if (e == hipSuccess) return I8QL_OK;
   g_last_hip_error = static_cast<int>(e);
@@ -67,21 +75,22 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
   return quantize_rows(x, x_dtype, m, k, q_out, scale_out, stream);
 }
 
-i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
-                                  const int8_t* wq, const float* w_scale, const float* bias,
-                                  void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
-                                  void* stream) {
+i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const float* x_scale,
+                                const int8_t* wq, const float* w_scale, const float* bias,
+                                void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
   if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32 && y_dtype != I8QL_I32) return I8QL_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
-  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return I8QL_ERR_SHAPE;
-  // one workgroup per output tile (64 x 32 at the smallest), in a one-dimensional grid
-  const int64_t tm = (m + 63) / 64, tn = (n + 31) / 32;
-  if (!mul_ok(tm, tn) || tm * tn > kMaxGridX - 8) return I8QL_ERR_SHAPE;
-  if (config < -1 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
+  if (!w8a8_sizes_ok(m, n, k)) return I8QL_ERR_SHAPE;
+  if (config < -1 || config >= I8QL_W8A8_NUM_CONFIGS || workspace_bytes < 0) return I8QL_ERR_ARG;
+  if (config == -1 ? splits != -1 : (splits < 1 || splits > I8QL_W8A8_MAX_SPLITS))
+    return I8QL_ERR_ARG;
   if (config >= 0) {
-    int32_t geo[3];
+    int32_t geo[4];
     i8ql::w8a8_config_geometry(config, geo);
     if (k % (128 * static_cast<int64_t>(geo[2])) != 0 && geo[2] > 1) return I8QL_ERR_ARG;
+    if (splits > 1 && (!geo[3] || splits > (k + 127) / 128)) return I8QL_ERR_ARG;
+    if (splits > 1 && !i8ql::w8a8_plan_valid(config, splits, m, n, k)) return I8QL_ERR_SHAPE;
   }
   if (m == 0 || n == 0) return I8QL_OK;
   if (!xq || !wq || !y) return I8QL_ERR_NULL;
@@ -92,29 +101,72 @@ i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_s
       !aligned(bias, 4))
     return I8QL_ERR_ALIGN;
   if (k > I8QL_W8A8_MAX_K) return I8QL_ERR_K_TOO_LARGE;
+  if (!workspace) workspace_bytes = 0;
+  if (config >= 0) {
+    const int64_t need = i8ql::w8a8_plan_workspace(config, splits, m, n);
+    if (need > 0 && !workspace) return I8QL_ERR_NULL;
+    if (need > workspace_bytes) return I8QL_ERR_WORKSPACE;
+  }
+  if (workspace && !aligned(workspace, 16)) return I8QL_ERR_ALIGN;
   return hip_status(i8ql::launch_w8a8_gemm(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
-                                           config, static_cast<hipStream_t>(stream)));
+                                           config, splits, workspace, workspace_bytes,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
+                                  const int8_t* wq, const float* w_scale, const float* bias,
+                                  void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                  void* stream) {
+  return w8a8_gemm_with_plan(config, config < 0 ? -1 : 1, xq, x_scale, wq, w_scale, bias, y,
+                             y_dtype, m, n, k, nullptr, 0, stream);
 }
 
 i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
                       int64_t m, int64_t n, int64_t k, void* stream) {
-  return w8a8_gemm_with_config(-1, xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k, stream);
+  return w8a8_gemm_with_plan(-1, -1, xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
+                             nullptr, 0, stream);
 }
 
-i8ql_status w8a8_gemm_config_info(int config, int32_t* out3) {
-  if (!out3) return I8QL_ERR_NULL;
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out4) {
+  if (!out4) return I8QL_ERR_NULL;
   if (config < 0 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
-  i8ql::w8a8_config_geometry(config, out3);
+  i8ql::w8a8_config_geometry(config, out4);
   return I8QL_OK;
 }
 
 int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus) {
   if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || k > I8QL_W8A8_MAX_K || cus < 1) return -1;
-  if (!mul_ok(m, k) || !mul_ok(n, k) || !mul_ok(m, n)) return -1;
-  const int64_t tm = (m + 63) / 64, tn = (n + 31) / 32;
-  if (!mul_ok(tm, tn) || tm * tn > kMaxGridX - 8) return -1;
+  if (!w8a8_sizes_ok(m, n, k)) return -1;
   return i8ql::w8a8_choose_config(m, n, k, cus);
+}
+
+i8ql_status w8a8_gemm_choose_plan(int64_t m, int64_t n, int64_t k, int cus,
+                                  int64_t workspace_bytes, int32_t* out2) {
+  if (!out2) return I8QL_ERR_NULL;
+  if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || k > I8QL_W8A8_MAX_K || cus < 1 ||
+      workspace_bytes < 0 || !w8a8_sizes_ok(m, n, k))
+    return I8QL_ERR_ARG;
+  int sp = 1;
+  out2[0] = i8ql::w8a8_choose_plan(m, n, k, cus, workspace_bytes, &sp);
+  out2[1] = sp;
+  return I8QL_OK;
+}
+
+int64_t w8a8_gemm_workspace_size(int config, int splits, int64_t m, int64_t n, int64_t k,
+                                 int cus) {
+  if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || k > I8QL_W8A8_MAX_K || cus < 1 ||
+      !w8a8_sizes_ok(m, n, k))
+    return -1;
+  if (config == -1 && splits == -1) {
+    int sp = 1;
+    const int c = i8ql::w8a8_choose_plan(m, n, k, cus, INT64_MAX, &sp);
+    return i8ql::w8a8_plan_workspace(c, sp, m, n);
+  }
+  if (config < 0 || config >= I8QL_W8A8_NUM_CONFIGS || splits < 1 ||
+      splits > I8QL_W8A8_MAX_SPLITS || !i8ql::w8a8_plan_valid(config, splits, m, n, k))
+    return -1;
+  return i8ql::w8a8_plan_workspace(config, splits, m, n);
 }
 
 i8ql_status w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
@@ -252,6 +304,7 @@ const char* i8ql_status_string(i8ql_status s) {
     case I8QL_ERR_K_TOO_LARGE: return "I8QL_ERR_K_TOO_LARGE";
     case I8QL_ERR_ARG: return "I8QL_ERR_ARG";
     case I8QL_ERR_HIP: return "I8QL_ERR_HIP";
+    case I8QL_ERR_WORKSPACE: return "I8QL_ERR_WORKSPACE";
   }
   return "I8QL_UNKNOWN_STATUS";
 }

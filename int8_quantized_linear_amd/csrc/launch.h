@@ -40,17 +40,24 @@ hipError_t allow_dynamic_lds(int bytes) {
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream);
 
-// W8A8: `config` is one of the I8QL_W8A8_NUM_CONFIGS tile configurations, or -1 for the
-// one the cost model chooses for this shape on the current device.
+// W8A8: plan (config, splits) = one of the I8QL_W8A8_NUM_CONFIGS tile configurations with
+// k split across `splits` workgroups per tile (workspace ws of ws_bytes, zero counters), or
+// config -1 for the plan the cost model chooses for this shape on the current device among
+// those whose workspace fits in ws_bytes (none when ws is NULL).
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                             const float* w_scale, const float* bias, void* y,
                             i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k, int config,
-                            hipStream_t stream);
+                            int splits, void* ws, int64_t ws_bytes, hipStream_t stream);
 
-// The cost model's configuration for an m x n x k product on `cus` compute units (host
-// only), and the {tile rows, tile columns, k-groups} of a configuration.
+// Host only: the cost model's configuration with no split (w8a8_choose_config) or its plan
+// within a workspace budget (w8a8_choose_plan), for `cus` compute units; the workspace a plan
+// needs; whether a plan is valid for a shape; {tile rows, tile columns, k-groups, splittable}
+// of a configuration.
 int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus);
-void w8a8_config_geometry(int config, int32_t* out3);
+int w8a8_choose_plan(int64_t m, int64_t n, int64_t k, int cus, int64_t ws_bytes, int* splits);
+int64_t w8a8_plan_workspace(int config, int splits, int64_t m, int64_t n);
+bool w8a8_plan_valid(int config, int splits, int64_t m, int64_t n, int64_t k);
+void w8a8_config_geometry(int config, int32_t* out4);
 
 hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,

@@ -94,20 +94,86 @@ __device__ __forceinline__ int swizzle(int row) {
   }
 }
 
-// Linear workgroup id -> (tile row, tile column), XCD-contiguous and grouped.
-__device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                        int64_t& tn) {
-  const int64_t total = tiles_m * tiles_n;
+// Linear workgroup id -> (tile row, tile column), XCD-contiguous and grouped.  With k split
+// across `splits` workgroups per tile, consecutive units of an XCD's range are the splits of
+// one tile (so they run at the same time, on the same XCD).
+__device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int splits,
+                                        int64_t& tm, int64_t& tn, int& split) {
+  const int64_t total = tiles_m * tiles_n * splits;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t b = blockIdx.x;
-  const int64_t t = (b % kXcds) * per_xcd + b / kXcds;
-  if (t >= total) return false;
+  const int64_t u = (b % kXcds) * per_xcd + b / kXcds;
+  if (u >= total) return false;
+  const int64_t t = u / splits;
+  split = static_cast<int>(u % splits);
   const int64_t group = t / (kGroupM * tiles_n);
   const int64_t first_m = group * kGroupM;
   const int64_t gsize = min(tiles_m - first_m, static_cast<int64_t>(kGroupM));
   const int64_t in_group = t % (kGroupM * tiles_n);
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+  return true;
+}
+
+// k split across workgroups.  The workspace holds one int32 arrival counter per output tile
+// (kCtrAlign-rounded), then one partial tile per (tile, split): [tiles][splits][WAVES][TM * TN
+// * 4][64 lanes][4] int32, so that every store and load instruction of a wavefront moves 1 KiB
+// of contiguous memory.  Each workgroup stores its partial accumulators, makes them visible
+// at device scope and counts itself in; the last of a tile's splits to arrive adds the other
+// splits' partials to its own (int32 addition is exact and associative, so the sum does not
+// depend on the arrival order), returns the counter to zero for the next call and applies
+// the epilogue.  No workgroup waits for another, so the kernel needs no co-residency.
+constexpr int64_t kCtrAlign = 64;  // counters: 256 bytes per 64 tiles
+
+template <class C>
+__device__ bool splitk_fixup(v16i (&acc)[C::TM][C::TN], int* __restrict__ ws, int64_t tile,
+                             int64_t tiles, int split, int splits, int wave, int lane,
+                             int* last_flag) {
+  constexpr int TM = C::TM, TN = C::TN;
+  constexpr int64_t kSlot = static_cast<int64_t>(C::WAVES) * TM * TN * 16 * 64;  // ints
+  int* ctr = ws;
+  int* part = ws + (tiles + kCtrAlign - 1) / kCtrAlign * kCtrAlign;
+  const int64_t wofs = static_cast<int64_t>(wave) * TM * TN * 16 * 64 + 4 * lane;
+  int* mine = part + (tile * splits + split) * kSlot + wofs;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4i*>(mine + ((i * TN + j) * 4 + q) * 256) =
+            v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                acc[i][j][4 * q + 3]};
+  __threadfence();  // this thread's partial is visible at device scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();  // (after the barrier: orders every thread's stores before the count)
+    const int prev = __hip_atomic_fetch_add(ctr + tile, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == splits - 1;
+    if (last) {
+      __threadfence();
+      __hip_atomic_store(ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *last_flag = last;
+  }
+  __syncthreads();
+  if (!*last_flag) return false;
+  __threadfence();  // acquire: the other splits' partials
+  for (int sp = 0; sp < splits; ++sp) {
+    if (sp == split) continue;
+    const int* other = part + (tile * splits + sp) * kSlot + wofs;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4i v = *reinterpret_cast<const v4i*>(other + ((i * TN + j) * 4 + q) * 256);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+        }
+  }
   return true;
 }
 
@@ -516,17 +582,28 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* s
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT>
+// XS (KS == 1 only): `splits` > 1 splits k across that many workgroups per output tile,
+// each walking an equal share (within one step) of the k steps; `ws` is the workspace of
+// splitk_fixup (zero counters on entry; they are zero again on exit).  Without XS the
+// fix-up is not compiled in (it would push the largest tiles past the register file) and
+// `splits` must be 1.
+template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT, bool XS>
 __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
-    const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
+    const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
+    int splits_arg, int* __restrict__ ws) {
+  static_assert(!XS || KS == 1, "k split across workgroups needs one k-group");
   using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
+  const int splits = XS ? splits_arg : 1;
   constexpr int TM = C::TM, TN = C::TN;
   extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
+  __shared__ int last_flag;  // (only used with XS)
 
+  const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
   int64_t tm, tn;
-  if (!tile_of((m + BM - 1) / BM, (n + BN - 1) / BN, tm, tn)) return;
+  int split;
+  if (!tile_of(tiles_m, tiles_n, splits, tm, tn, split)) return;
   const int64_t m0 = tm * BM;
   const int64_t n0 = tn * BN;
 
@@ -535,10 +612,14 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   const int group = __builtin_amdgcn_readfirstlane(threadIdx.x / (64 * C::WAVES));
   const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x / 64) % C::WAVES);
   const int wm = wave / WN, wn = wave % WN;
-  // Each k-group walks its own equal share of the steps (KS > 1 only when it divides
-  // evenly) in its own LDS stages; all groups pass the same barriers.
-  const int ksteps = static_cast<int>((k + BK - 1) / BK) / KS;
-  const int base = group * ksteps;
+  // This workgroup's share of the k steps (all of them without a split); each k-group walks
+  // its own equal share of those (KS > 1 only when it divides evenly) in its own LDS stages;
+  // all groups pass the same barriers.
+  const int64_t total_steps = (k + BK - 1) / BK;
+  const int sbeg = static_cast<int>(total_steps * split / splits);
+  const int send = static_cast<int>(total_steps * (split + 1) / splits);
+  const int ksteps = (send - sbeg) / KS;
+  const int base = sbeg + group * ksteps;
   int8_t* lds = lds_all + group * C::GROUP_BYTES;
 
   // This lane's part of each of the wavefront's load instructions: instruction j covers
@@ -578,7 +659,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
   const int fx = swizzle<BK>(frow);  // swizzle of this lane's fragment rows (period 32)
   const int a_off = (wm * C::WTM + frow) * BK;
   const int b_off = (BM + wn * C::WTN + frow) * BK;
-  const int tail_valid = KS == 1 ? static_cast<int>((k % BK) / 16) : 0;  // 0: none
+  // (the partial last step of k belongs to the last split)
+  const int tail_valid =
+      KS == 1 && split == splits - 1 ? static_cast<int>((k % BK) / 16) : 0;  // 0: none
 
   v4i fa[2][TM], fb[2][TN];
   wait_and_barrier<C::LOADS>(min(kAhead - 1, ksteps - 1));
@@ -631,6 +714,11 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
       }
     }
     if (group != 0) return;
+  }
+  if constexpr (XS) {
+    if (splits > 1 && !splitk_fixup<C>(acc, ws, tm * tiles_n + tn, tiles_m * tiles_n, split,
+                                       splits, wave, lane, &last_flag))
+      return;
   }
 
   // ---- fused epilogue ----------------------------------------------------------------
@@ -703,7 +791,8 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_split(
   extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
 
   int64_t tm, tn;
-  if (!tile_of((m + BM - 1) / BM, (n + BN - 1) / BN, tm, tn)) return;
+  int split;
+  if (!tile_of((m + BM - 1) / BM, (n + BN - 1) / BN, 1, tm, tn, split)) return;
   const int64_t m0 = tm * BM;
   const int64_t n0 = tn * BN;
   const int lane = threadIdx.x % 64;
@@ -832,18 +921,18 @@ hipError_t launch_split(const int8_t* xq, const float* x_scale, const int8_t* wq
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM = 2, int WN = 2>
+template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM, int WN, bool XS>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
-                      int64_t k, hipStream_t stream) {
+                      int64_t k, int splits, int* ws, hipStream_t stream) {
   using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
-  constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT>;
+  constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT, XS>;
   const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(C::LDS_BYTES));
   if (e != hipSuccess) return e;
-  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t units = ((m + BM - 1) / BM) * ((n + BN - 1) / BN) * splits;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), C::LDS_BYTES,
-                     stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
+                     stream, xq, x_scale, wq, w_scale, bias, y, m, n, k, splits, ws);
   return hipGetLastError();
 }
 
@@ -862,47 +951,54 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // 2 rounds + 96 tiles, 3 rounds), 2048x6144x2560 37 with 256x192 (256 tiles, one round),
 // 2048x2560x9728 56 with 128x160 (256 tiles), 16384x12288x4096 750-765 with 256x256 or
 // 320x256.
+//
+// Configurations with one k-group per workgroup can also split k across P workgroups per
+// tile (a plan (configuration, P)); then R counts tiles * P units, S is the steps of one
+// split, and the fix-up (partial tiles through the workspace, summed by the last arrival)
+// adds t_fix = f0 + f1 * P * BM * BN / 16384.
 struct Candidate {
   int bm, bn, ks;                // tile and k-groups
+  bool xsplit;                   // k may be split across workgroups
   double t_step, t_round, t0;    // cost model (us)
 };
 constexpr Candidate kCandidates[] = {
-    {256, 256, 1, 1.3616, 21.063, -10.348},  // 0: 2 stages, 8 wavefronts 64x128
-    {256, 320, 1, 1.5576, 27.308, -14.718},  // 1: 2 stages, 8 wavefronts 64x160
-    {256, 192, 1, 1.0216, 17.150, -7.651},   // 2: 2 A + 3 B slots, 8 wavefronts 64x96
-    {128, 320, 1, 0.9822, 13.467, -3.992},   // 3: 2 A + 3 B slots, 8 wavefronts 32x160
-    {128, 160, 1, 0.5742, 7.669, 0.439},     // 4: 3 stages, 4 wavefronts 32x160
-    {256, 128, 1, 0.7426, 12.247, -6.637},   // 5: 3 stages, 8 wavefronts 64x64
-    {128, 128, 1, 0.5263, 5.399, 0.071},     // 6: 3 stages, 8 wavefronts 64x32
-    {128, 64, 2, 0.6945, 4.216, 0.586},      // 7: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 64, 2, 0.4855, 2.353, 2.777},       // 8: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 32, 4, 0.6247, 2.558, 2.713},       // 9: 3 stages, 4 k-groups of 2 wavefronts
-    {64, 64, 1, 0.2183, 0.705, 5.779},       // 10: 4 stages, 4 wavefronts
-    {320, 256, 1, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
+    {256, 256, 1, true, 1.3616, 21.063, -10.348},   // 0: 2 stages, 8 wavefronts 64x128
+    {256, 320, 1, false, 1.5576, 27.308, -14.718},  // 1: 2 stages, 8 wavefronts 64x160
+    {256, 192, 1, false, 1.0216, 17.150, -7.651},   // 2: 2 A + 3 B slots, 8 wavefronts 64x96
+    {128, 320, 1, false, 0.9822, 13.467, -3.992},   // 3: 2 A + 3 B slots, 8 wavefronts 32x160
+    {128, 160, 1, true, 0.5742, 7.669, 0.439},      // 4: 3 stages, 4 wavefronts 32x160
+    {256, 128, 1, true, 0.7426, 12.247, -6.637},    // 5: 3 stages, 8 wavefronts 64x64
+    {128, 128, 1, true, 0.5263, 5.399, 0.071},      // 6: 3 stages, 8 wavefronts 64x32
+    {128, 64, 2, false, 0.6945, 4.216, 0.586},      // 7: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 64, 2, false, 0.4855, 2.353, 2.777},       // 8: 3 stages, 2 k-groups of 4 wavefronts
+    {64, 32, 4, false, 0.6247, 2.558, 2.713},       // 9: 3 stages, 4 k-groups of 2 wavefronts
+    {64, 64, 1, true, 0.2183, 0.705, 5.779},        // 10: 4 stages, 4 wavefronts
+    {320, 256, 1, false, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
 };
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
+constexpr double kFix0 = 2.0, kFix1 = 0.5;  // split fix-up cost model (us)
 
 template <int YT>
 hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const int8_t* wq,
                             const float* w_scale, const float* bias, void* y, int64_t m,
-                            int64_t n, int64_t k, hipStream_t stream) {
+                            int64_t n, int64_t k, int splits, int* ws, hipStream_t stream) {
 #define I8QL_W8A8_CFG(...) \
-  launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
+  launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, splits, ws, stream)
 #define I8QL_W8A8_SPLIT(...) \
   launch_split<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
   switch (c) {
-    case 0: return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2);
-    case 1: return I8QL_W8A8_CFG(256, 320, 128, 2, 1, YT, 4, 2);
+    case 0: return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2, true);
+    case 1: return I8QL_W8A8_CFG(256, 320, 128, 2, 1, YT, 4, 2, false);
     case 2: return I8QL_W8A8_SPLIT(256, 192, 128, YT, 4, 2);
     case 3: return I8QL_W8A8_SPLIT(128, 320, 128, YT, 4, 2);
-    case 4: return I8QL_W8A8_CFG(128, 160, 128, 3, 1, YT, 4, 1);
-    case 5: return I8QL_W8A8_CFG(256, 128, 128, 3, 1, YT, 4, 2);
-    case 6: return I8QL_W8A8_CFG(128, 128, 128, 3, 1, YT, 2, 4);
-    case 7: return I8QL_W8A8_CFG(128, 64, 128, 3, 2, YT, 2, 2);
-    case 8: return I8QL_W8A8_CFG(64, 64, 128, 3, 2, YT, 2, 2);
-    case 9: return I8QL_W8A8_CFG(64, 32, 128, 3, 4, YT, 2, 1);
-    case 10: return I8QL_W8A8_CFG(64, 64, 128, 4, 1, YT, 2, 2);
-    default: return I8QL_W8A8_CFG(320, 256, 128, 2, 1, YT, 2, 4);
+    case 4: return I8QL_W8A8_CFG(128, 160, 128, 3, 1, YT, 4, 1, true);
+    case 5: return I8QL_W8A8_CFG(256, 128, 128, 3, 1, YT, 4, 2, true);
+    case 6: return I8QL_W8A8_CFG(128, 128, 128, 3, 1, YT, 2, 4, true);
+    case 7: return I8QL_W8A8_CFG(128, 64, 128, 3, 2, YT, 2, 2, false);
+    case 8: return I8QL_W8A8_CFG(64, 64, 128, 3, 2, YT, 2, 2, false);
+    case 9: return I8QL_W8A8_CFG(64, 32, 128, 3, 4, YT, 2, 1, false);
+    case 10: return I8QL_W8A8_CFG(64, 64, 128, 4, 1, YT, 2, 2, true);
+    default: return I8QL_W8A8_CFG(320, 256, 128, 2, 1, YT, 2, 4, false);
   }
 #undef I8QL_W8A8_CFG
 #undef I8QL_W8A8_SPLIT
@@ -910,9 +1006,9 @@ hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const
 
 // Compute units of the current device (cached per device id).
 int device_cus() {
-  static int cached[64] = {};
+  static int cached[kMaxDevices] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   if (cached[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -923,38 +1019,63 @@ int device_cus() {
   return cached[dev];
 }
 
-// Index of the candidate with the lowest modelled time for an m x n x k product.  k-groups
-// need whole k steps each (k a multiple of 128 times the group count); a candidate whose grid
-// would exceed the launch limit is skipped (the 320 x 256 tile, with the fewest tiles, always
-// fits when the caller's limit check on 64 x 64 tiles has passed).
-int choose_candidate(int64_t m, int64_t n, int64_t k, int cus) {
-  int best = kNumCandidates - 1;
+int64_t plan_workspace(int c, int splits, int64_t m, int64_t n) {
+  if (splits <= 1) return 0;
+  const Candidate& d = kCandidates[c];
+  const int64_t tiles = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
+  return ((tiles + kCtrAlign - 1) / kCtrAlign * kCtrAlign +
+          tiles * splits * static_cast<int64_t>(d.bm) * d.bn) *
+         4;
+}
+
+// Modelled time of plan (c, splits); negative when the plan is not valid for the shape.
+double plan_time(int c, int splits, int64_t m, int64_t n, int64_t k, int cus) {
+  const Candidate& d = kCandidates[c];
+  const int64_t ksteps = (k + 127) / 128;
+  if (d.ks > 1 && k % (128 * d.ks) != 0) return -1.0;
+  if (splits > 1 && (!d.xsplit || splits > ksteps)) return -1.0;
+  const int64_t units = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn) * splits;
+  if (units > kMaxGrid - kXcds) return -1.0;
+  const double rounds = static_cast<double>((units + cus - 1) / cus);
+  const double steps = static_cast<double>((ksteps / d.ks + splits - 1) / splits);
+  double t = d.t_step * rounds * steps + d.t_round * rounds + d.t0;
+  if (splits > 1) t += kFix0 + kFix1 * splits * (d.bm * d.bn / 16384.0);
+  return t;
+}
+
+// The plan with the lowest modelled time whose workspace fits in ws_bytes (no split needs
+// none, so a plan always exists).  Every split count up to I8QL_W8A8_MAX_SPLITS is tried for
+// the configurations that allow one.
+int choose_plan(int64_t m, int64_t n, int64_t k, int cus, int64_t ws_bytes, int* splits_out) {
+  int best = kNumCandidates - 1, best_s = 1;
   double best_t = 0.0;
   bool found = false;
-  const int64_t ksteps = (k + 127) / 128;
   for (int c = 0; c < kNumCandidates; ++c) {
-    const Candidate& d = kCandidates[c];
-    if (d.ks > 1 && k % (128 * d.ks) != 0) continue;
-    const int64_t tiles = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
-    if (tiles > kMaxGrid - kXcds) continue;
-    const double rounds = static_cast<double>((tiles + cus - 1) / cus);
-    const double steps = static_cast<double>(ksteps / d.ks);
-    const double t = d.t_step * rounds * steps + d.t_round * rounds + d.t0;
-    if (!found || t < best_t) {
-      best = c;
-      best_t = t;
-      found = true;
+    for (int sp = 1; sp <= I8QL_W8A8_MAX_SPLITS; ++sp) {
+      if (sp > 1 && plan_workspace(c, sp, m, n) > ws_bytes) break;
+      const double t = plan_time(c, sp, m, n, k, cus);
+      if (t < 0.0) break;  // (more splits are not valid either)
+      if (!found || t < best_t) {
+        best = c;
+        best_s = sp;
+        best_t = t;
+        found = true;
+      }
     }
   }
+  *splits_out = best_s;
   return best;
 }
 
 template <int YT>
 hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                      const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
-                     int64_t k, int config, hipStream_t stream) {
-  const int c = config >= 0 ? config : choose_candidate(m, n, k, device_cus());
-  return launch_candidate<YT>(c, xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+                     int64_t k, int config, int splits, void* ws, int64_t ws_bytes,
+                     hipStream_t stream) {
+  int c = config, sp = splits;
+  if (c < 0) c = choose_plan(m, n, k, device_cus(), ws ? ws_bytes : 0, &sp);
+  return launch_candidate<YT>(c, xq, x_scale, wq, w_scale, bias, y, m, n, k, sp,
+                              static_cast<int*>(ws), stream);
 }
 
 }  // namespace
@@ -962,26 +1083,44 @@ hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
 static_assert(kNumCandidates == I8QL_W8A8_NUM_CONFIGS, "configuration count of the C ABI");
 
 int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus) {
-  return choose_candidate(m, n, k, cus);
+  int sp = 1;
+  return choose_plan(m, n, k, cus, 0, &sp);
 }
 
-void w8a8_config_geometry(int config, int32_t* out3) {
-  out3[0] = kCandidates[config].bm;
-  out3[1] = kCandidates[config].bn;
-  out3[2] = kCandidates[config].ks;
+int w8a8_choose_plan(int64_t m, int64_t n, int64_t k, int cus, int64_t ws_bytes,
+                     int* splits) {
+  return choose_plan(m, n, k, cus, ws_bytes, splits);
+}
+
+int64_t w8a8_plan_workspace(int config, int splits, int64_t m, int64_t n) {
+  return plan_workspace(config, splits, m, n);
+}
+
+bool w8a8_plan_valid(int config, int splits, int64_t m, int64_t n, int64_t k) {
+  return plan_time(config, splits, m, n, k, 256) >= 0.0;
+}
+
+void w8a8_config_geometry(int config, int32_t* out4) {
+  out4[0] = kCandidates[config].bm;
+  out4[1] = kCandidates[config].bn;
+  out4[2] = kCandidates[config].ks;
+  out4[3] = kCandidates[config].xsplit ? 1 : 0;
 }
 
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                             const float* w_scale, const float* bias, void* y,
                             i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k, int config,
-                            hipStream_t stream) {
+                            int splits, void* ws, int64_t ws_bytes, hipStream_t stream) {
   switch (y_dtype) {
     case I8QL_I32:
-      return launch_yt<I8QL_I32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
+      return launch_yt<I8QL_I32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, splits,
+                                 ws, ws_bytes, stream);
     case I8QL_F32:
-      return launch_yt<I8QL_F32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
+      return launch_yt<I8QL_F32>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, splits,
+                                 ws, ws_bytes, stream);
     default:
-      return launch_yt<I8QL_BF16>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, stream);
+      return launch_yt<I8QL_BF16>(xq, x_scale, wq, w_scale, bias, y, m, n, k, config, splits,
+                                  ws, ws_bytes, stream);
   }
 }
 

@@ -9,7 +9,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "i8ql.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, KBIG, ARG = 0, 1, 2, 3, 4, 5, 6
+OK, NULL, SHAPE, DTYPE, ALIGN, KBIG, ARG, WORKSPACE = 0, 1, 2, 3, 4, 5, 6, 8
 F32, BF16, F16, I8, I32 = 0, 1, 2, 3, 4
 
 
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     for code, name in enumerate(["I8QL_OK", "I8QL_ERR_NULL", "I8QL_ERR_SHAPE", "I8QL_ERR_DTYPE",
                                  "I8QL_ERR_ALIGN", "I8QL_ERR_K_TOO_LARGE", "I8QL_ERR_ARG",
-                                 "I8QL_ERR_HIP"]):
+                                 "I8QL_ERR_HIP", "I8QL_ERR_WORKSPACE"]):
         assert lib.i8ql_status_string(code).decode() == name
     assert lib.i8ql_last_hip_error() == 0
 
@@ -111,14 +111,77 @@ def test_w8a8_with_config_validation(lib):
     assert call(0, xq=NUL) == NULL
     assert call(0, k=72) == ALIGN
     for c in range(12):
-        geo = (ctypes.c_int32 * 3)()
+        geo = (ctypes.c_int32 * 4)()
         assert lib.w8a8_gemm_config_info(c, ctypes.cast(geo, ctypes.c_void_p)) == OK
         if geo[2] > 1:                      # k-groups need k % (128 * groups) == 0
             assert call(c, k=64) == ARG
             assert call(c, k=128 * geo[2] + 16) == ARG
             assert call(c, m=0, k=64) == ARG
-    assert lib.w8a8_gemm_config_info(12, ctypes.cast((ctypes.c_int32 * 3)(), ctypes.c_void_p)) == ARG
+    assert lib.w8a8_gemm_config_info(12, ctypes.cast((ctypes.c_int32 * 4)(), ctypes.c_void_p)) == ARG
     assert lib.w8a8_gemm_config_info(0, NUL) == NULL
+
+
+def plan_ws(geo, splits, m, n):
+    """Workspace of a split plan: tile counters (rounded to 64), then one int32 partial tile
+    per (tile, split)."""
+    if splits == 1:
+        return 0
+    tiles = -(-m // geo[0]) * -(-n // geo[1])
+    return (-(-tiles // 64) * 64 + tiles * splits * geo[0] * geo[1]) * 4
+
+
+def test_w8a8_with_plan_validation(lib):
+    import int8_quantized_linear_amd as i8
+    f = lib.w8a8_gemm_with_plan
+    W = ctypes.c_void_p(0x20000)
+
+    def call(c, s, m=300, n=200, k=1024, ws=W, wsb=1 << 30, xq=A16, y=A16, yt=BF16):
+        return f(c, s, xq, A16, A16, A16, NUL, y, yt, m, n, k, ws, wsb, NUL)
+
+    assert call(-1, 2) == ARG                 # auto plan takes no split count
+    assert call(-1, 1) == ARG
+    assert call(6, 0) == ARG
+    assert call(6, -1) == ARG
+    assert call(6, 9) == ARG                  # beyond I8QL_W8A8_MAX_SPLITS
+    assert call(6, 2, wsb=-1) == ARG
+    assert call(13, 1) == ARG
+    assert call(6, 9, m=0) == ARG             # checked before the zero-size no-op
+    assert call(6, 2, m=0, xq=NUL, y=NUL) == OK
+    assert call(6, 8, k=896) == ARG           # 7 steps of 128 cannot take 8 splits
+    for c in range(12):
+        geo = i8.w8a8_gemm_config_info(c)
+        if not geo[3]:
+            assert call(c, 2) == ARG          # configurations that cannot split k
+            continue
+        need = plan_ws(geo, 3, 300, 200)
+        assert i8.w8a8_gemm_workspace_size(300, 200, 1024, 256, c, 3) == need
+        assert i8.w8a8_gemm_workspace_size(300, 200, 1024, 256, c, 1) == 0
+        assert call(c, 3, ws=NUL) == NULL
+        assert call(c, 3, wsb=need - 4) == WORKSPACE
+        assert call(c, 3, ws=ctypes.c_void_p(0x20008)) == ALIGN
+    assert lib.w8a8_gemm_workspace_size(1, 3, 300, 200, 1024, 256) == -1  # cannot split
+    assert lib.w8a8_gemm_workspace_size(6, 9, 300, 200, 1024, 256) == -1
+    assert lib.w8a8_gemm_workspace_size(-1, -1, 0, 200, 1024, 256) == -1
+
+
+def test_w8a8_plan_choices():
+    import int8_quantized_linear_amd as i8
+    geos = [i8.w8a8_gemm_config_info(c) for c in range(i8.W8A8_NUM_CONFIGS)]
+    for m in (1, 16, 128, 512, 777, 2048, 16384):
+        for n in (32, 1000, 2560, 6144, 19456):
+            for k in (16, 272, 2560, 4096, 9728):
+                # no workspace: exactly the configuration w8a8_gemm launches
+                assert i8.w8a8_gemm_choose_plan(m, n, k, 256, 0) == (
+                    i8.w8a8_gemm_choose_config(m, n, k, 256), 1)
+                c, s = i8.w8a8_gemm_choose_plan(m, n, k, 256)
+                assert 1 <= s <= i8.W8A8_MAX_SPLITS and (s == 1 or geos[c][3])
+                assert s <= -(-k // 128)
+                need = i8.w8a8_gemm_workspace_size(m, n, k, 256)
+                assert need == plan_ws(geos[c], s, m, n)
+                # given exactly that much, the same plan; any budget gives a plan that fits
+                assert i8.w8a8_gemm_choose_plan(m, n, k, 256, need) == (c, s)
+                c2, s2 = i8.w8a8_gemm_choose_plan(m, n, k, 256, need // 2)
+                assert plan_ws(geos[c2], s2, m, n) <= need // 2
 
 
 def test_w8a8_config_table_and_choices():
@@ -135,16 +198,16 @@ def test_w8a8_config_table_and_choices():
         for n in (32, 1000, 2560, 6144, 19456):
             for k in (16, 272, 2560, 4096, 9728):
                 c = i8.w8a8_gemm_choose_config(m, n, k, 256)
-                bm, bn, g = geos[c]
+                bm, bn, g, _ = geos[c]
                 assert g == 1 or k % (128 * g) == 0
     # the benchmark step's fused 4B projections at 2048 tokens take the 256x320, 256x192 and
     # 128x160 tiles that fill the 256 CUs in whole rounds
     pick = lambda m, n, k, cus=256: geos[i8.w8a8_gemm_choose_config(m, n, k, cus)]
-    assert pick(2048, 19456, 2560) == (256, 320, 1)
-    assert pick(2048, 6144, 2560) == (256, 192, 1)
-    assert pick(2048, 2560, 4096) == (128, 160, 1)
-    assert pick(2048, 2560, 9728) == (128, 160, 1)
-    assert pick(16384, 12288, 4096) == (320, 256, 1)
+    assert pick(2048, 19456, 2560)[:3] == (256, 320, 1)
+    assert pick(2048, 6144, 2560)[:3] == (256, 192, 1)
+    assert pick(2048, 2560, 4096)[:3] == (128, 160, 1)
+    assert pick(2048, 2560, 9728)[:3] == (128, 160, 1)
+    assert pick(16384, 12288, 4096)[:3] == (320, 256, 1)
     # few tiles and a long k: k split over k-groups inside the workgroup
     assert pick(128, 2560, 9728)[2] == 4
     assert pick(512, 2560, 9728)[2] == 2
@@ -307,6 +370,8 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
         lambda: lib.quantize_per_token_int8(A16, F32, 4, 64, A16, A16, NUL),
         lambda: lib.w8a8_gemm(A16, A16, A16, A16, NUL, A16, BF16, 4, 8, 64, NUL),
         lambda: lib.w8a8_gemm_with_config(0, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 64, NUL),
+        lambda: lib.w8a8_gemm_with_plan(6, 2, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 256,
+                                        ctypes.c_void_p(0x20000), 1 << 20, NUL),
         lambda: lib.w8a16_gemm(A16, A16, A16, NUL, A16, BF16, 1, 16, 64, NUL),
         lambda: lib.grouped_w8a16_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64, NUL),
         lambda: lib.grouped_w8a16_silu_gemm(A16, 0, A16, A16, 66, A16, 4, 8, A16, BF16, 16, 64,

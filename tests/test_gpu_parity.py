@@ -168,7 +168,7 @@ def w8a8_case(g, m, n, k, wdtype="bf16"):
 
 
 def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bfloat16),
-             seed=0, with_bias=(False, True), config=-1):
+             seed=0, with_bias=(False, True), config=-1, splits=None, workspace=None):
     g = wl.rng(seed)
     (wt, wv), (xt, xv) = w8a8_case(g, m, n, k)
     qw, sw, qwr, swr = quant_gpu_vs_ref(ref, dev, wt, wv, "bf16")
@@ -181,14 +181,21 @@ def run_w8a8(ref, dev, m, n, k, out_dtypes=(torch.int32, torch.float32, torch.bf
             if od == torch.int32:
                 if use_bias:
                     continue
-                y = i8.w8a8_gemm_with_config(config, qx, None, qw, None, out_dtype=torch.int32,
-                                             out=sentinel((m, n), torch.int32, dev))
+                y = gemm(config, splits, workspace, qx, None, qw, None, None, torch.int32,
+                         sentinel((m, n), torch.int32, dev))
                 np.testing.assert_array_equal(y.cpu().numpy(), acc)
                 continue
             b = torch.from_numpy(b_np).to(dev) if use_bias else None
-            y = i8.w8a8_gemm_with_config(config, qx, sx, qw, sw, b, out_dtype=od,
-                                         out=sentinel((m, n), od, dev))
+            y = gemm(config, splits, workspace, qx, sx, qw, sw, b, od, sentinel((m, n), od, dev))
             check_float(y, yref, w8a8_tol(acc, sxr, swr, b_np), f"w8a8 {m}x{n}x{k} {od}")
+
+
+def gemm(config, splits, workspace, qx, sx, qw, sw, b, od, out):
+    """One W8A8 call: a tile configuration without a split (splits None), or a plan."""
+    if splits is None:
+        return i8.w8a8_gemm_with_config(config, qx, sx, qw, sw, b, out_dtype=od, out=out)
+    return i8.w8a8_gemm_with_plan(config, splits, qx, sx, qw, sw, b, out_dtype=od, out=out,
+                                  workspace=workspace)
 
 
 # Shapes through the cost model's choice of tile configuration (ragged edges, partial last
@@ -210,7 +217,7 @@ def test_w8a8_every_tile_config(ref, dev, config):
     eight tile rows of the workgroup-to-tile map.  k-group configurations take k in whole
     steps per group.  N a multiple of 8 takes the LDS-staged 16-byte-store epilogue, an odd N
     the per-element one."""
-    bm, bn, groups = i8.w8a8_gemm_config_info(config)
+    bm, bn, groups, _ = i8.w8a8_gemm_config_info(config)
     if groups == 1:
         shapes = [(2 * bm + 37, 2 * bn + 24, 432), (2 * bm + 37, 2 * bn + 19, 16),
                   (9 * bm + 5, 3 * bn + 8, 144)]
@@ -219,6 +226,55 @@ def test_w8a8_every_tile_config(ref, dev, config):
     for (m, n, k) in shapes:
         print(f"w8a8 config {config} ({bm}x{bn}, {groups} k-groups): {m}x{n}x{k}", flush=True)
         run_w8a8(ref, dev, m, n, k, seed=config * 31 + m, config=config)
+
+
+SPLITTABLE = [c for c in range(i8.W8A8_NUM_CONFIGS) if i8.w8a8_gemm_config_info(c)[3]]
+
+
+@pytest.mark.parametrize("config", SPLITTABLE)
+def test_w8a8_split_plans(ref, dev, config):
+    """k split across 2, 3, 5 and 8 workgroups per tile with each configuration that allows
+    it: ragged tiles in both directions, a partial last k step (owned by the last split),
+    splits of unequal step counts, and one workspace reused by every call, whose tile
+    counters must be back at zero after each."""
+    bm, bn, _, _ = i8.w8a8_gemm_config_info(config)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    for splits, (m, n, k) in [(2, (2 * bm + 37, 2 * bn + 24, 1040)),
+                              (3, (bm + 5, 3 * bn + 8, 2576)),
+                              (5, (3 * bm, bn + 16, 1152)),
+                              (8, (37, 2 * bn + 19, 8 * 128 + 16))]:
+        print(f"w8a8 plan ({config}, {splits}) {bm}x{bn}: {m}x{n}x{k}", flush=True)
+        need = i8.w8a8_gemm_workspace_size(m, n, k, 256, config, splits)
+        assert 0 < need <= ws.numel()
+        run_w8a8(ref, dev, m, n, k, seed=config * 17 + splits, config=config, splits=splits,
+                 workspace=ws)
+        torch.cuda.synchronize()
+        tiles = -(-m // bm) * -(-n // bn)
+        assert torch.all(ws[:4 * tiles] == 0), "arrival counters not returned to zero"
+
+
+def test_w8a8_split_plans_agree_with_unsplit(dev):
+    """Every split count of every splittable configuration gives bitwise the outputs of the
+    same configuration without a split, for int32, float32 and bf16 (with bias)."""
+    g = wl.rng(12)
+    m, n, k = 700, 900, 2048
+    qx = torch.from_numpy(g.integers(-127, 128, (m, k), dtype=np.int8)).to(dev)
+    qw = torch.from_numpy(g.integers(-127, 128, (n, k), dtype=np.int8)).to(dev)
+    sx = torch.rand(m, device=dev) * 0.01
+    sw = torch.rand(n, device=dev) * 0.01
+    b = torch.randn(n, device=dev) * 0.02
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    for c in SPLITTABLE:
+        want = {od: i8.w8a8_gemm_with_config(c, qx, sx, qw, sw, b, out_dtype=od)
+                for od in (torch.float32, torch.bfloat16)}
+        want_i = i8.w8a8_gemm_with_config(c, qx, None, qw, None, out_dtype=torch.int32)
+        for s in range(2, i8.W8A8_MAX_SPLITS + 1):
+            for od, y in want.items():
+                got = i8.w8a8_gemm_with_plan(c, s, qx, sx, qw, sw, b, out_dtype=od, workspace=ws)
+                assert torch.equal(got, y), (c, s, od)
+            got = i8.w8a8_gemm_with_plan(c, s, qx, None, qw, None, out_dtype=torch.int32,
+                                         workspace=ws)
+            assert torch.equal(got, want_i), (c, s)
 
 
 def test_w8a8_configs_agree_bitwise(dev):
@@ -551,25 +607,32 @@ def test_graph_replays_match_eager(ref, dev):
     y16 = torch.empty((3, 320), dtype=torch.bfloat16, device=dev)
     yg = torch.empty((14, 64), dtype=torch.float32, device=dev)
 
+    ys = torch.empty((96, 320), dtype=torch.float32, device=dev)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+
     def path():
         i8.quantize_per_token_int8(x, qx, sx)
         i8.w8a8_gemm(qx, sx, qw, sw, out=y8)
+        i8.w8a8_gemm_with_plan(6, 4, qx, sx, qw, sw, out_dtype=torch.float32, out=ys,
+                               workspace=ws)
         i8.w8a16_gemm(xd, qw, sw, out=y16)
         i8.grouped_w8a16_gemm(xg, qe.view(5, 64, 1024), se.view(5, 64), ids,
                               out_dtype=torch.float32, out=yg)
 
     path()
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (qx, sx, y8, y16, yg)]
+    outs = (qx, sx, y8, ys, y16, yg)
+    eager = [t.clone() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         path()
     for rep in range(3):
-        for t in (qx, sx, y8, y16, yg):
+        for t in outs:
             t.fill_(0)
         graph.replay()
         torch.cuda.synchronize()
-        for a, b in zip((qx, sx, y8, y16, yg), eager):
+        for a, b in zip(outs, eager):
             assert torch.equal(a, b), f"replay {rep} differs"
+        assert torch.all(ws == 0)
         path()  # eager work between replays
         torch.cuda.synchronize()
