@@ -146,9 +146,11 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
  * work units over the device's compute units, k steps per unit, the split's fix-up).
  *
  * Workspace contract: device memory, 16-byte aligned, zero-filled before its first use.
- * Its first bytes are per-tile arrival counters, which every call returns to zero, so the
- * same workspace serves any later call without clearing.  Calls that may overlap in time
- * (different streams) must not share a workspace.
+ * Its first 16 KiB are per-tile arrival counters (a split plan has at most
+ * I8QL_W8A8_SPLIT_MAX_TILES output tiles), which every call returns to zero; the partial
+ * tiles follow them.  So the same workspace serves any later call without clearing, as long
+ * as nothing else writes its first 16 KiB.  Calls that may overlap in time (different
+ * streams) must not share a workspace.
  *
  * w8a8_gemm_config_info(config, out4): writes {tile rows, tile columns, k-groups, 1 if k may
  *   be split across workgroups else 0} of the configuration (host, 4 int32).  A
@@ -179,12 +181,14 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
  *   Arguments, results and errors as for w8a8_gemm_with_config, plus: config == -1 with
  *   splits != -1, config >= 0 with splits outside [1, I8QL_W8A8_MAX_SPLITS], splits > 1 on a
  *   configuration that cannot split or with more splits than k steps of 128, or
- *   workspace_bytes < 0 -> I8QL_ERR_ARG; the plan needs workspace but workspace is NULL ->
+ *   workspace_bytes < 0 -> I8QL_ERR_ARG; a split plan with more than
+ *   I8QL_W8A8_SPLIT_MAX_TILES output tiles -> I8QL_ERR_SHAPE; the plan needs workspace but workspace is NULL ->
  *   I8QL_ERR_NULL; workspace not 16-byte aligned -> I8QL_ERR_ALIGN; workspace_bytes below
  *   what the plan needs -> I8QL_ERR_WORKSPACE.
  */
 #define I8QL_W8A8_NUM_CONFIGS 12
 #define I8QL_W8A8_MAX_SPLITS 8
+#define I8QL_W8A8_SPLIT_MAX_TILES 4096
 i8ql_status w8a8_gemm_config_info(int config, int32_t* out4);
 int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus);
 i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,

@@ -29,6 +29,7 @@ GROUP_SIZE = 128  # I8QL_GROUP_SIZE
 ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
 W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 W8A8_MAX_SPLITS = 8  # I8QL_W8A8_MAX_SPLITS
+W8A8_SPLIT_MAX_TILES = 4096  # I8QL_W8A8_SPLIT_MAX_TILES
 
 
 class I8qlError(RuntimeError):

@@ -115,24 +115,24 @@ __device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int sp
   return true;
 }
 
-// k split across workgroups.  The workspace holds one int32 arrival counter per output tile
-// (kCtrAlign-rounded), then one partial tile per (tile, split): [tiles][splits][WAVES][TM * TN
-// * 4][64 lanes][4] int32, so that every store and load instruction of a wavefront moves 1 KiB
-// of contiguous memory.  Each workgroup stores its partial accumulators, makes them visible
+// k split across workgroups.  The workspace starts with kSplitMaxTiles int32 arrival
+// counters (one per output tile; a fixed region, so that no call's partial tiles ever lie
+// where a later call with more tiles keeps counters), then one partial tile per (tile,
+// split): [tiles][splits][WAVES][TM * TN * 4][64 lanes][4] int32, so that every store and load
+// instruction of a wavefront moves 1 KiB of contiguous memory.  Each workgroup stores its partial accumulators, makes them visible
 // at device scope and counts itself in; the last of a tile's splits to arrive adds the other
 // splits' partials to its own (int32 addition is exact and associative, so the sum does not
 // depend on the arrival order), returns the counter to zero for the next call and applies
 // the epilogue.  No workgroup waits for another, so the kernel needs no co-residency.
-constexpr int64_t kCtrAlign = 64;  // counters: 256 bytes per 64 tiles
+constexpr int64_t kSplitMaxTiles = 4096;  // split plans have at most this many tiles
 
 template <class C>
 __device__ bool splitk_fixup(v16i (&acc)[C::TM][C::TN], int* __restrict__ ws, int64_t tile,
-                             int64_t tiles, int split, int splits, int wave, int lane,
-                             int* last_flag) {
+                             int split, int splits, int wave, int lane, int* last_flag) {
   constexpr int TM = C::TM, TN = C::TN;
   constexpr int64_t kSlot = static_cast<int64_t>(C::WAVES) * TM * TN * 16 * 64;  // ints
   int* ctr = ws;
-  int* part = ws + (tiles + kCtrAlign - 1) / kCtrAlign * kCtrAlign;
+  int* part = ws + kSplitMaxTiles;
   const int64_t wofs = static_cast<int64_t>(wave) * TM * TN * 16 * 64 + 4 * lane;
   int* mine = part + (tile * splits + split) * kSlot + wofs;
 #pragma unroll
@@ -716,8 +716,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     if (group != 0) return;
   }
   if constexpr (XS) {
-    if (splits > 1 && !splitk_fixup<C>(acc, ws, tm * tiles_n + tn, tiles_m * tiles_n, split,
-                                       splits, wave, lane, &last_flag))
+    if (splits > 1 &&
+        !splitk_fixup<C>(acc, ws, tm * tiles_n + tn, split, splits, wave, lane, &last_flag))
       return;
   }
 
@@ -1023,9 +1023,7 @@ int64_t plan_workspace(int c, int splits, int64_t m, int64_t n) {
   if (splits <= 1) return 0;
   const Candidate& d = kCandidates[c];
   const int64_t tiles = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
-  return ((tiles + kCtrAlign - 1) / kCtrAlign * kCtrAlign +
-          tiles * splits * static_cast<int64_t>(d.bm) * d.bn) *
-         4;
+  return (kSplitMaxTiles + tiles * splits * static_cast<int64_t>(d.bm) * d.bn) * 4;
 }
 
 // Modelled time of plan (c, splits); negative when the plan is not valid for the shape.
@@ -1034,7 +1032,9 @@ double plan_time(int c, int splits, int64_t m, int64_t n, int64_t k, int cus) {
   const int64_t ksteps = (k + 127) / 128;
   if (d.ks > 1 && k % (128 * d.ks) != 0) return -1.0;
   if (splits > 1 && (!d.xsplit || splits > ksteps)) return -1.0;
-  const int64_t units = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn) * splits;
+  const int64_t tiles = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
+  if (splits > 1 && tiles > kSplitMaxTiles) return -1.0;
+  const int64_t units = tiles * splits;
   if (units > kMaxGrid - kXcds) return -1.0;
   const double rounds = static_cast<double>((units + cus - 1) / cus);
   const double steps = static_cast<double>((ksteps / d.ks + splits - 1) / splits);

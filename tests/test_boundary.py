@@ -122,12 +122,12 @@ def test_w8a8_with_config_validation(lib):
 
 
 def plan_ws(geo, splits, m, n):
-    """Workspace of a split plan: tile counters (rounded to 64), then one int32 partial tile
-    per (tile, split)."""
+    """Workspace of a split plan: 4096 tile counters, then one int32 partial tile per (tile,
+    split)."""
     if splits == 1:
         return 0
     tiles = -(-m // geo[0]) * -(-n // geo[1])
-    return (-(-tiles // 64) * 64 + tiles * splits * geo[0] * geo[1]) * 4
+    return (4096 + tiles * splits * geo[0] * geo[1]) * 4
 
 
 def test_w8a8_with_plan_validation(lib):
@@ -159,6 +159,9 @@ def test_w8a8_with_plan_validation(lib):
         assert call(c, 3, ws=NUL) == NULL
         assert call(c, 3, wsb=need - 4) == WORKSPACE
         assert call(c, 3, ws=ctypes.c_void_p(0x20008)) == ALIGN
+    assert call(10, 2, m=64 * 65, n=64 * 64) == SHAPE  # 4160 tiles: too many to split
+    assert lib.w8a8_gemm_workspace_size(10, 2, 64 * 65, 64 * 64, 1024, 256) == -1
+    assert lib.w8a8_gemm_workspace_size(10, 2, 64 * 64, 64 * 64, 1024, 256) > 0  # 4096: fine
     assert lib.w8a8_gemm_workspace_size(1, 3, 300, 200, 1024, 256) == -1  # cannot split
     assert lib.w8a8_gemm_workspace_size(6, 9, 300, 200, 1024, 256) == -1
     assert lib.w8a8_gemm_workspace_size(-1, -1, 0, 200, 1024, 256) == -1
