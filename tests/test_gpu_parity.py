@@ -635,6 +635,6 @@ def test_graph_replays_match_eager(ref, dev):
         torch.cuda.synchronize()
         for a, b in zip(outs, eager):
             assert torch.equal(a, b), f"replay {rep} differs"
-        assert torch.all(ws == 0)
+        assert torch.all(ws[:16384] == 0)  # the arrival counters
         path()  # eager work between replays
         torch.cuda.synchronize()
