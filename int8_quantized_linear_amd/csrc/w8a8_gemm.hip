@@ -118,12 +118,21 @@ __device__ __forceinline__ bool tile_of(int64_t tiles_m, int64_t tiles_n, int sp
 // k split across workgroups.  The workspace starts with kSplitMaxTiles int32 arrival
 // counters (one per output tile; a fixed region, so that no call's partial tiles ever lie
 // where a later call with more tiles keeps counters), then one partial tile per (tile,
-// split): [tiles][splits][WAVES][TM * TN * 4][64 lanes][4] int32, so that every store and load
-// instruction of a wavefront moves 1 KiB of contiguous memory.  Each workgroup stores its partial accumulators, makes them visible
-// at device scope and counts itself in; the last of a tile's splits to arrive adds the other
-// splits' partials to its own (int32 addition is exact and associative, so the sum does not
-// depend on the arrival order), returns the counter to zero for the next call and applies
-// the epilogue.  No workgroup waits for another, so the kernel needs no co-residency.
+// split): [tiles][splits][WAVES][TM * TN * 16][64 lanes] int32, so that every store and load
+// instruction of a wavefront moves 256 contiguous bytes.  Each workgroup stores its partial
+// accumulators, waits until they are written and counts itself in; the last of a tile's
+// splits to arrive adds the other splits' partials to its own (int32 addition is exact and
+// associative, so the sum does not depend on the arrival order), returns the counter to
+// zero for the next call and applies the epilogue.  No workgroup waits for another, so the
+// kernel needs no co-residency.
+//
+// Visibility without cache-wide operations: the partial tiles are written and read with
+// device-scope (relaxed atomic) accesses, which the 8 XCDs' separate L2 caches keep
+// coherent, and each wavefront waits for its stores to complete before the barrier that
+// precedes the count.  The reader issues its loads only after it has seen the count.  A
+// device-scope fence instead writes back or invalidates a whole L2 per call, and with one
+// per workgroup those serialized: 128 x 128 tiles, 2 splits, 512 x 6144 x 2560 took 162 us
+// against 18 us without a split.
 constexpr int64_t kSplitMaxTiles = 4096;  // split plans have at most this many tiles
 
 template <class C>
@@ -133,33 +142,27 @@ __device__ bool splitk_fixup(v16i (&acc)[C::TM][C::TN], int* __restrict__ ws, in
   constexpr int64_t kSlot = static_cast<int64_t>(C::WAVES) * TM * TN * 16 * 64;  // ints
   int* ctr = ws;
   int* part = ws + kSplitMaxTiles;
-  const int64_t wofs = static_cast<int64_t>(wave) * TM * TN * 16 * 64 + 4 * lane;
+  const int64_t wofs = static_cast<int64_t>(wave) * TM * TN * 16 * 64 + lane;
   int* mine = part + (tile * splits + split) * kSlot + wofs;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<v4i*>(mine + ((i * TN + j) * 4 + q) * 256) =
-            v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                acc[i][j][4 * q + 3]};
-  __threadfence();  // this thread's partial is visible at device scope
+      for (int r = 0; r < 16; ++r)
+        __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();  // (after the barrier: orders every thread's stores before the count)
     const int prev = __hip_atomic_fetch_add(ctr + tile, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == splits - 1;
-    if (last) {
-      __threadfence();
-      __hip_atomic_store(ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (last) __hip_atomic_store(ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last_flag = last;
   }
   __syncthreads();
   if (!*last_flag) return false;
-  __threadfence();  // acquire: the other splits' partials
   for (int sp = 0; sp < splits; ++sp) {
     if (sp == split) continue;
     const int* other = part + (tile * splits + sp) * kSlot + wofs;
@@ -168,11 +171,9 @@ __device__ bool splitk_fixup(v16i (&acc)[C::TM][C::TN], int* __restrict__ ws, in
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4i v = *reinterpret_cast<const v4i*>(other + ((i * TN + j) * 4 + q) * 256);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-        }
+        for (int r = 0; r < 16; ++r)
+          acc[i][j][r] += __hip_atomic_load(other + ((i * TN + j) * 16 + r) * 64,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
 }
