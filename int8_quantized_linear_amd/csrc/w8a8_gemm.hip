@@ -956,7 +956,12 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // Configurations with one k-group per workgroup can also split k across P workgroups per
 // tile (a plan (configuration, P)); then R counts tiles * P units, S is the steps of one
 // split, and the fix-up (partial tiles through the workspace, summed by the last arrival)
-// adds t_fix = f0 + f1 * P * BM * BN / 16384.
+// adds t_fix = f0 + f1 * P * BM * BN / 16384, fitted (relative error) to graph-timed MI355X
+// sweeps of every plan on 45 shapes (M 128..2048, N 1024..24576, K 2560..12288, weights
+// rotating beyond the Infinity Cache): the model's picks take 0.12% longer in total than the
+// per-shape best, also with each shape predicted by a fit that left it out.  A split wins on
+// the long-k shapes: 512 x 2560 x 9728 27.6 us with 128 x 128 tiles and 3 splits (33.6
+// without), 128 x 2560 x 9728 15.1 us with 64 x 64 tiles and 3 splits (18.8).
 struct Candidate {
   int bm, bn, ks;                // tile and k-groups
   bool xsplit;                   // k may be split across workgroups
@@ -977,7 +982,7 @@ constexpr Candidate kCandidates[] = {
     {320, 256, 1, false, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
 };
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
-constexpr double kFix0 = 2.0, kFix1 = 0.5;  // split fix-up cost model (us)
+constexpr double kFix0 = 0.0, kFix1 = 2.1;  // split fix-up cost model (us)
 
 template <int YT>
 hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const int8_t* wq,
