@@ -199,6 +199,28 @@ i8ql_status w8a8_gemm_choose_plan(int64_t m, int64_t n, int64_t k, int cus,
                                   int64_t workspace_bytes, int32_t* out2);
 int64_t w8a8_gemm_workspace_size(int config, int splits, int64_t m, int64_t n, int64_t k,
                                  int cus);
+
+/*
+ * w8a8_gemm_noalloc — w8a8_gemm_with_plan with the library's own workspace instead of a
+ * caller's, for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates nothing.
+ *
+ * The workspace is a static device array of I8QL_W8A8_SCRATCH_BYTES, one copy per GPU,
+ * held until the process ends.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams or host threads) race: the caller serializes
+ * them.  The kernels return its arrival counters to zero after every call.  The first call
+ * on a device looks up the array's address and clears its counters with one small kernel
+ * on `stream`; make that first call outside graph capture.
+ *
+ * Plan (-1, -1): the cost model's best plan whose workspace fits in the array.  Arguments,
+ * results and errors as for w8a8_gemm_with_plan without the workspace arguments, plus: an
+ * explicit plan that needs more than I8QL_W8A8_SCRATCH_BYTES -> I8QL_ERR_WORKSPACE.
+ */
+#define I8QL_W8A8_SCRATCH_BYTES (32 * 1024 * 1024)
+i8ql_status w8a8_gemm_noalloc(int config, int splits, const int8_t* xq, const float* x_scale,
+                              const int8_t* wq, const float* w_scale, const float* bias, void* y,
+                              i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                              void* stream);
 i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const float* x_scale,
                                 const int8_t* wq, const float* w_scale, const float* bias,
                                 void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,

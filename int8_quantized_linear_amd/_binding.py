@@ -22,7 +22,7 @@ _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8Q
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
            "w8a8_gemm_with_config", "w8a8_gemm_choose_plan", "w8a8_gemm_workspace_size",
-           "w8a8_gemm_with_plan", "grouped_w8a16_silu_gemm", "moe_route_topk",
+           "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "grouped_w8a16_silu_gemm", "moe_route_topk",
            "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128", "i8ql_status_string",
            "i8ql_last_hip_error")
 GROUP_SIZE = 128  # I8QL_GROUP_SIZE
@@ -30,6 +30,7 @@ ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_M
 W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 W8A8_MAX_SPLITS = 8  # I8QL_W8A8_MAX_SPLITS
 W8A8_SPLIT_MAX_TILES = 4096  # I8QL_W8A8_SPLIT_MAX_TILES
+W8A8_SCRATCH_BYTES = 32 << 20  # I8QL_W8A8_SCRATCH_BYTES
 
 
 class I8qlError(RuntimeError):
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH):
         lib.w8a8_gemm_workspace_size.restype = I64
         lib.w8a8_gemm_with_plan.argtypes = [I, I, P, P, P, P, P, P, I, I64, I64, I64, P, I64, P]
         lib.w8a8_gemm_with_plan.restype = I
+        lib.w8a8_gemm_noalloc.argtypes = [I, I, P, P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a8_gemm_noalloc.restype = I
         lib.w8a16_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a16_gemm.restype = I
         lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
@@ -224,6 +227,19 @@ def w8a8_gemm_with_plan(config, splits, xq, x_scale, wq, w_scale, bias=None,
         _call("w8a8_gemm_with_plan", int(config), int(splits), _ptr(xq), _ptr(x_scale),
               _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k,
               _ptr(workspace), nbytes, _stream(dev))
+    return y
+
+
+def w8a8_gemm_noalloc(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16,
+                      out=None, config=-1, splits=-1):
+    """``w8a8_gemm_with_plan`` with the library's static scratch array as the workspace (the
+    C entry point allocates nothing; pass ``out`` to keep this wrapper from allocating the
+    output).  Calls that overlap in time on one GPU race on the scratch."""
+    m, n, k, y, dev = _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out)
+    with torch.cuda.device(dev):
+        _call("w8a8_gemm_noalloc", int(config), int(splits), _ptr(xq), _ptr(x_scale),
+              _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k,
+              _stream(dev))
     return y
 
 

@@ -75,10 +75,18 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
   return quantize_rows(x, x_dtype, m, k, q_out, scale_out, stream);
 }
 
-i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const float* x_scale,
-                                const int8_t* wq, const float* w_scale, const float* bias,
-                                void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
-                                void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the plan entry points; `workspace_bytes` is the workspace the plan may
+// use (the caller's, or the static scratch).  Returns I8QL_OK when the call may launch, or
+// the status to return (also I8QL_OK with *noop set for an empty product).
+i8ql_status w8a8_validate(int config, int splits, const int8_t* xq, const float* x_scale,
+                          const int8_t* wq, const float* w_scale, const float* bias,
+                          const void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                          bool has_workspace, int64_t workspace_bytes, bool* noop) {
+  *noop = false;
   if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32 && y_dtype != I8QL_I32) return I8QL_ERR_DTYPE;
   if (m < 0 || n < 0 || k < 1) return I8QL_ERR_SHAPE;
   if (!w8a8_sizes_ok(m, n, k)) return I8QL_ERR_SHAPE;
@@ -92,7 +100,10 @@ i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const 
     if (splits > 1 && (!geo[3] || splits > (k + 127) / 128)) return I8QL_ERR_ARG;
     if (splits > 1 && !i8ql::w8a8_plan_valid(config, splits, m, n, k)) return I8QL_ERR_SHAPE;
   }
-  if (m == 0 || n == 0) return I8QL_OK;
+  if (m == 0 || n == 0) {
+    *noop = true;
+    return I8QL_OK;
+  }
   if (!xq || !wq || !y) return I8QL_ERR_NULL;
   if (y_dtype != I8QL_I32 && (!x_scale || !w_scale)) return I8QL_ERR_NULL;
   if (y_dtype == I8QL_I32 && bias) return I8QL_ERR_ARG;
@@ -101,16 +112,46 @@ i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const 
       !aligned(bias, 4))
     return I8QL_ERR_ALIGN;
   if (k > I8QL_W8A8_MAX_K) return I8QL_ERR_K_TOO_LARGE;
-  if (!workspace) workspace_bytes = 0;
   if (config >= 0) {
     const int64_t need = i8ql::w8a8_plan_workspace(config, splits, m, n);
-    if (need > 0 && !workspace) return I8QL_ERR_NULL;
+    if (need > 0 && !has_workspace) return I8QL_ERR_NULL;
     if (need > workspace_bytes) return I8QL_ERR_WORKSPACE;
   }
+  return I8QL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+i8ql_status w8a8_gemm_with_plan(int config, int splits, const int8_t* xq, const float* x_scale,
+                                const int8_t* wq, const float* w_scale, const float* bias,
+                                void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+  if (workspace_bytes < 0) return I8QL_ERR_ARG;
+  if (!workspace) workspace_bytes = 0;
+  bool noop = false;
+  const i8ql_status st = w8a8_validate(config, splits, xq, x_scale, wq, w_scale, bias, y,
+                                       y_dtype, m, n, k, workspace != nullptr, workspace_bytes,
+                                       &noop);
+  if (st != I8QL_OK || noop) return st;
   if (workspace && !aligned(workspace, 16)) return I8QL_ERR_ALIGN;
   return hip_status(i8ql::launch_w8a8_gemm(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
                                            config, splits, workspace, workspace_bytes,
                                            static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a8_gemm_noalloc(int config, int splits, const int8_t* xq, const float* x_scale,
+                              const int8_t* wq, const float* w_scale, const float* bias, void* y,
+                              i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                              void* stream) {
+  bool noop = false;
+  const i8ql_status st = w8a8_validate(config, splits, xq, x_scale, wq, w_scale, bias, y,
+                                       y_dtype, m, n, k, true, I8QL_W8A8_SCRATCH_BYTES, &noop);
+  if (st != I8QL_OK || noop) return st;
+  return hip_status(i8ql::launch_w8a8_gemm_noalloc(xq, x_scale, wq, w_scale, bias, y, y_dtype,
+                                                   m, n, k, config, splits,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,

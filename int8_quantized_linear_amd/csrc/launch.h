@@ -49,6 +49,13 @@ hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t
                             i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k, int config,
                             int splits, void* ws, int64_t ws_bytes, hipStream_t stream);
 
+// launch_w8a8_gemm with the library's static scratch array (I8QL_W8A8_SCRATCH_BYTES per
+// device) as the workspace: allocates nothing.
+hipError_t launch_w8a8_gemm_noalloc(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                    const float* w_scale, const float* bias, void* y,
+                                    i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                    int config, int splits, hipStream_t stream);
+
 // Host only: the cost model's configuration with no split (w8a8_choose_config) or its plan
 // within a workspace budget (w8a8_choose_plan), for `cus` compute units; the workspace a plan
 // needs; whether a plan is valid for a shape; {tile rows, tile columns, k-groups, splittable}

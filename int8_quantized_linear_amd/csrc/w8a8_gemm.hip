@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "sync.hpp"
 
@@ -1084,9 +1086,60 @@ hipError_t launch_yt(const int8_t* xq, const float* x_scale, const int8_t* wq,
                               static_cast<int*>(ws), stream);
 }
 
+// ---- the allocation-free entry point's workspace ----------------------------------------
+// For callers that cannot allocate device memory, split plans keep their partial tiles and
+// counters in this file-scope array instead of a caller's workspace: one copy per GPU, held
+// until the process ends, shared by every such call on that GPU (calls that overlap in time
+// race on it).  In host code `scratch` names a host-side stand-in, not device memory: kernels
+// get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) int scratch[I8QL_W8A8_SCRATCH_BYTES / 4];
+
+__global__ void zero_ints(int* p, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0;
+}
+
+// The device address of `scratch` on the current device, looked up once per device (that
+// device current).  The first lookup also clears the counter region with a small kernel on
+// `stream` (static storage starts zeroed; every call leaves the counters at zero).
+hipError_t scratch_address(void** out, hipStream_t stream) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(zero_ints, dim3((kSplitMaxTiles + 255) / 256), dim3(256), 0, stream,
+                       static_cast<int*>(p), static_cast<int>(kSplitMaxTiles));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 static_assert(kNumCandidates == I8QL_W8A8_NUM_CONFIGS, "configuration count of the C ABI");
+static_assert(I8QL_W8A8_SCRATCH_BYTES % 256 == 0 && I8QL_W8A8_SCRATCH_BYTES > kSplitMaxTiles * 4,
+              "scratch holds the counters and at least some partial tiles");
+
+hipError_t launch_w8a8_gemm_noalloc(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                    const float* w_scale, const float* bias, void* y,
+                                    i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                    int config, int splits, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_w8a8_gemm(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k, config, splits,
+                          ws, I8QL_W8A8_SCRATCH_BYTES, stream);
+}
 
 int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus) {
   int sp = 1;
