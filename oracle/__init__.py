@@ -72,6 +72,8 @@ class Oracle:
         lib.ref_quantize_groups.restype = ctypes.c_int
         lib.ref_w8a16_grouped_scales.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ref_w8a16_grouped_scales.restype = None
+        lib.ref_w8a8_grouped_scales.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+        lib.ref_w8a8_grouped_scales.restype = None
         lib.ref_set_threads.argtypes = [ctypes.c_int]
         lib.ref_get_threads.restype = ctypes.c_int
         self.lib = lib
@@ -183,6 +185,23 @@ class Oracle:
         y = np.empty((m, n), np.float64)
         self.lib.ref_w8a16_grouped_scales(self._ptr(x), self._ptr(wq), self._ptr(sw),
                                           self._ptr(b), m, n, k, group, self._ptr(y))
+        return y
+
+    def w8a8_grouped_scales(self, xq, x_scale, wq, w_scale, group: int = 128, bias=None):
+        """float64 ``x_scale[i] * sum_g w_scale[j, g] * sum_{c in g} xq[i,c]*wq[j,c] (+ bias)``
+        with each group's code products summed exactly."""
+        xq = np.ascontiguousarray(xq, np.int8)
+        wq = np.ascontiguousarray(wq, np.int8)
+        sx = np.ascontiguousarray(x_scale, np.float32)
+        sw = np.ascontiguousarray(w_scale, np.float32)
+        b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+        m, k = xq.shape
+        n, k2 = wq.shape
+        assert k == k2 and k % group == 0 and sw.shape == (n, k // group) and sx.shape == (m,)
+        y = np.empty((m, n), np.float64)
+        self.lib.ref_w8a8_grouped_scales(self._ptr(xq), self._ptr(sx), self._ptr(wq),
+                                         self._ptr(sw), self._ptr(b), m, n, k, group,
+                                         self._ptr(y))
         return y
 
     # -- mixture-of-experts steps around the grouped GEMM (readings stated in ref.c) -----

@@ -372,3 +372,36 @@ void ref_w8a16_grouped_scales(const uint16_t* x, const int8_t* wq, const float* 
     }
   }
 }
+
+/*
+ * W8A8 with one weight scale per (output channel, group of `group` input channels): both
+ * operands int8 ("Day 6 — Quantize It Yourself", The mechanism, block 5), the weight scale
+ * shared by a run of consecutive input channels (same page, block 1), per-token activation
+ * scales ("feat(quantization): support compressed-tensors W8A8 and mixed modules", Design and
+ * Supported Execution Scheme).  Each group's code products are summed exactly (int64), the
+ * group sums are weighted by their scales and added in double, then the token's scale and
+ * the bias apply:
+ *   y[i, j] = x_scale[i] * sum_g w_scale[j, g] * sum_{c in g} xq[i, c] * wq[j, c] (+ bias[j])
+ */
+void ref_w8a8_grouped_scales(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                             const float* w_scale, const float* bias, int64_t m, int64_t n,
+                             int64_t k, int64_t group, double* y) {
+  const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    const int8_t* xr = xq + i * k;
+    for (int64_t j = 0; j < n; ++j) {
+      const int8_t* wr = wq + j * k;
+      double v = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        int64_t part = 0;
+        for (int64_t c = g * group; c < (g + 1) * group; ++c)
+          part += (int64_t)xr[c] * (int64_t)wr[c];
+        v += (double)w_scale[j * ng + g] * (double)part;
+      }
+      v *= (double)x_scale[i];
+      if (bias) v += (double)bias[j];
+      y[i * n + j] = v;
+    }
+  }
+}

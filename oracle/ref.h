@@ -56,6 +56,12 @@ void ref_w8a16_grouped_scales(const uint16_t* x, const int8_t* wq, const float* 
                               const float* bias, int64_t m, int64_t n, int64_t k, int64_t group,
                               double* y);
 
+/* W8A8 with group weight scales w_scale [n, k / group] ([Day6] blocks 1 and 5): y [m, n]
+ * double = x_scale[i] * sum_g w_scale[j, g] * (exact int sum of group g) (+ bias[j]). */
+void ref_w8a8_grouped_scales(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                             const float* w_scale, const float* bias, int64_t m, int64_t n,
+                             int64_t k, int64_t group, double* y);
+
 /* Mixture-of-experts steps around the grouped GEMM ([P5a] Summary names the block; its
  * routing, activation and combine are readings, stated in ref.c). */
 void ref_moe_route_topk(const float* logits, int64_t t, int64_t e_routed, int64_t k_routed,

@@ -599,3 +599,96 @@ def test_p16_w8a16_group_scales_against_numpy(ref, m, n, k, bias):
     qc, sc = ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
     np.testing.assert_array_equal(
         ref.w8a16_grouped_scales(wl.bits16(x), qc, sc[:, None], k, b), ref.w8a16(wl.bits16(x), qc, sc, b))
+
+
+# ---------------------------------------------------------------------------------------
+# P17 W8A8 with group-128 weight scales ("Day 6 — Quantize It Yourself", The mechanism,
+# block 1: one scale per group of input channels; block 5: both operands int8).
+
+def w8a8_g128_case(ref, g, m, n, k, bias):
+    w = wl.weight(g, n, k)
+    w[:, g.choice(k, 1)] *= np.float32(50.0)     # one outlier input column
+    x = wl.activations(g, m, k, outlier_frac=0.01)
+    qw, sw = ref.quantize_groups(wl.bits16(wl.to_bf16(w)), "bf16")
+    qx, sx = ref.quantize_rows(wl.bits16(wl.to_bf16(x)), "bf16")
+    b = (g.standard_normal(n, dtype=np.float32) * 0.02).astype(np.float32) if bias else None
+    return qx, sx, qw, sw, b
+
+
+def test_p17_w8a8_group_scales_exact_rational_brute_force(ref):
+    g = wl.rng(140)
+    m, n, k = 3, 5, 384
+    qx, sx, qw, sw, b = w8a8_g128_case(ref, g, m, n, k, True)
+    y = ref.w8a8_grouped_scales(qx, sx, qw, sw, 128, b)
+    for i in range(m):
+        for j in range(n):
+            tot = Fraction(0)
+            for gi in range(k // 128):
+                part = sum(int(qx[i, c]) * int(qw[j, c]) for c in range(128 * gi, 128 * gi + 128))
+                tot += Fraction(float(sw[j, gi])) * part
+            want = Fraction(float(sx[i])) * tot + Fraction(float(b[j]))
+            assert abs(Fraction(y[i, j]) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+@pytest.mark.parametrize("m,n,k,bias", [(4, 64, 512, False), (16, 40, 4096, True), (2, 9, 128, True)])
+def test_p17_w8a8_group_scales_against_numpy(ref, m, n, k, bias):
+    g = wl.rng(141 + k)
+    qx, sx, qw, sw, b = w8a8_g128_case(ref, g, m, n, k, bias)
+    y = ref.w8a8_grouped_scales(qx, sx, qw, sw, 128, b)
+    xd = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    wd = qw.astype(np.float64) * np.repeat(sw.astype(np.float64), 128, axis=1)
+    want = xd @ wd.T + (0.0 if b is None else b.astype(np.float64))
+    mag = np.abs(xd) @ np.abs(wd).T + 1.0
+    assert np.all(np.abs(y - want) <= 1e-12 * mag)
+    # the group scales of two groups exchanged, or applied per output channel transposed,
+    # are visible
+    if sw.shape[1] > 1:
+        s2 = sw.copy()
+        s2[:, [0, -1]] = s2[:, [-1, 0]]
+        y2 = ref.w8a8_grouped_scales(qx, sx, qw, s2, 128, b)
+        assert np.max(np.abs(y2 - y)) > 1e-6 * np.max(np.abs(y))
+
+
+def test_p17_w8a8_group_scales_reduce_to_per_channel(ref):
+    """Equal scales in every group of a row: the per-channel W8A8 value (the exact int32 sum
+    times both scales); and the result does not depend on the order of the groups."""
+    g = wl.rng(142)
+    m, n, k = 6, 20, 1024
+    qx, sx, qw, _, b = w8a8_g128_case(ref, g, m, n, k, True)
+    qc, sc = ref.quantize_rows(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+    same = np.repeat(sc[:, None], k // 128, axis=1)
+    y = ref.w8a8_grouped_scales(qx, sx, qc, same, 128, b)
+    _, y1 = ref.w8a8(qx, sx, qc, sc, b)
+    assert np.all(np.abs(y - y1) <= 1e-14 * (np.abs(y1) + 1e-30))
+    # permuting the groups of k (codes of both operands and the weight scales together)
+    perm = g.permutation(k // 128)
+    cols = (perm[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+    _, sw = ref.quantize_groups(wl.bits16(wl.to_bf16(wl.weight(g, n, k))), "bf16")
+    ya = ref.w8a8_grouped_scales(qx, sx, qc, sw, 128, b)
+    yb = ref.w8a8_grouped_scales(np.ascontiguousarray(qx[:, cols]), sx,
+                                 np.ascontiguousarray(qc[:, cols]),
+                                 np.ascontiguousarray(sw[:, perm]), 128, b)
+    assert np.all(np.abs(ya - yb) <= 1e-13 * (np.abs(ya) + 1e-30))
+
+
+def test_p17_w8a8_group_scales_quantization_error_bound(ref):
+    """Against the unquantized float64 product: per element, the quantization of each operand
+    moves a product term by at most half a code step of that operand's scale."""
+    g = wl.rng(143)
+    m, n, k = 8, 32, 2048
+    w = wl.weight(g, n, k)
+    x = wl.activations(g, m, k, outlier_frac=0.01)
+    wb, xb = wl.to_bf16(w), wl.to_bf16(x)
+    qw, sw = ref.quantize_groups(wl.bits16(wb), "bf16")
+    qx, sx = ref.quantize_rows(wl.bits16(xb), "bf16")
+    y = ref.w8a8_grouped_scales(qx, sx, qw, sw, 128, None)
+    wd, xd = wb.double().numpy(), xb.double().numpy()
+    exact = xd @ wd.T
+    swf = np.repeat(sw.astype(np.float64), 128, axis=1)     # [n, k] weight scale per element
+    sxf = sx.astype(np.float64)[:, None]                   # [m, 1]
+    # x = sx*qx + ex, w = sw*qw + ew with |ex| <= H*sx, |ew| <= H*sw, so per term
+    # |xw - (sx qx)(sw qw)| <= |sx qx| H sw + H sx |sw qw| + H^2 sx sw
+    bound = (np.abs(qx * sxf) @ (H * swf).T
+             + (H * sxf) * np.abs(qw * swf).sum(axis=1)[None, :]
+             + (H * sxf) * (H * swf).sum(axis=1)[None, :])
+    assert np.all(np.abs(y - exact) <= bound * (1 + 1e-9) + 1e-12)
