@@ -200,15 +200,18 @@ class PrefillWorkload:
     INPUTS = ("attn_in", "attn_out", "mlp_in", "mlp_mid")
     SRC = {"qkv": "attn_in", "o": "attn_out", "gate_up": "mlp_in", "down": "mlp_mid"}
 
-    def __init__(self, torch, i8, wl, dev, shapes, fused, tokens, frac, bias, seed):
+    def __init__(self, torch, i8, wl, dev, shapes, fused, tokens, frac, bias, seed,
+                 group_scales=False):
         self.torch, self.i8, self.wl = torch, i8, wl
         self.tokens, self.shapes = tokens, shapes
+        self.group_scales = group_scales  # weight scales per group of 128 input channels
         g = wl.rng(seed)
         pq, ps, pb = {}, {}, {}
         layer_bytes = 0
+        quant = i8.quantize_per_group_int8 if group_scales else i8.quantize_per_channel_int8
         for nm, (n, k) in shapes.items():
             w = wl.to_bf16(wl.weight(g, n, k)).to(dev)
-            pq[nm], ps[nm] = i8.quantize_per_channel_int8(w)
+            pq[nm], ps[nm] = quant(w)
             layer_bytes += n * k
             del w
             if bias:
@@ -249,8 +252,8 @@ class PrefillWorkload:
 
     def gemm(self, m, nm, copy):
         q, s = self.qx[m][self.SRC[nm]]
-        self.i8.w8a8_gemm(q, s, self.qs[copy % self.copies][nm], self.s[nm], self.b[nm],
-                          out=self.outs[m][nm])
+        f = self.i8.w8a8_gemm_g128 if self.group_scales else self.i8.w8a8_gemm
+        f(q, s, self.qs[copy % self.copies][nm], self.s[nm], self.b[nm], out=self.outs[m][nm])
 
     def step(self, i):
         for mi, m in enumerate(self.tokens):
@@ -284,6 +287,8 @@ def measure_prefill(torch, wl, wk, args, label, clock=True):
             sec = time_loop(torch, lambda i, m=m, nm=nm: wk.gemm(m, nm, i), reps, 2) / reps
             n, k = wk.shape[nm]
             o, b = w8a8_ops(m, n, k), w8a8_bytes(m, n, k, bias=wk.bias)
+            if wk.group_scales:
+                b += n * (k // 128 - 1) * 4  # a scale per group instead of one per channel
             bound, frac = launch_bound(o, b, sec)
             per.append({"m": m, "n": n, "k": k, "proj": nm, "us": sec * 1e6, "ops": o,
                         "bytes": b, "TOPS": o / sec / 1e12, "GBs": b / sec / 1e9,
@@ -365,6 +370,25 @@ def section_prefill_8b_m4096(torch, i8, wl, dev, args, result):
     result["prefill_8b_m4096"] = {
         "workload": "dense 8B decoder layer, W8A8 prefill at 4096 tokens (the same step as the "
                     "headline at its other token count)", "unit": "TOPS", **out}
+    del wk
+    torch.cuda.empty_cache()
+
+
+def section_prefill_8b_g128(torch, i8, wl, dev, args, result):
+    """The headline layer with weight scales per group of 128 input channels (W8A8-g128),
+    next to the per-channel numbers of the headline when both ran."""
+    wk = PrefillWorkload(torch, i8, wl, dev, wl.DENSE_8B, wl.DENSE_8B_FUSED, (16384,), 0.01,
+                         True, seed=3, group_scales=True)
+    out = measure_prefill(torch, wl, wk, args, "prefill_8b_g128", clock=False)
+    out["roofline"] = w8a8_roofline(out["per_launch"], None)
+    if result.get("per_launch"):
+        pc = {(p["m"], p["proj"]): p["us"] for p in result["per_launch"]}
+        for p in out["per_launch"]:
+            p["vs_per_channel"] = p["us"] / pc[(p["m"], p["proj"])]
+        out["vs_per_channel_step"] = out["ms_per_step"] / result["ms_per_step"]
+    result["prefill_8b_g128"] = {
+        "workload": "the headline step (dense 8B layer, 16384 tokens, bias) with weight scales "
+                    "per group of 128 input channels: w8a8_gemm_g128", "unit": "TOPS", **out}
     del wk
     torch.cuda.empty_cache()
 
@@ -742,6 +766,7 @@ def section_weight_quant(torch, i8, wl, dev, args, result):
 
 SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DEFAULT
     "step": section_step, "prefill_8b_m4096": section_prefill_8b_m4096,
+    "prefill_8b_g128": section_prefill_8b_g128,
     "prefill_4b": section_prefill_4b, "decode": section_decode, "moe": section_moe,
     "weight_quant": section_weight_quant,
     # hardware-counter runs only (eager launches, nothing timed)
@@ -749,7 +774,8 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters_decode": section_counters_decode,
     "counters_w8a8_large": section_counters_w8a8_large,
 }
-DEFAULT = "step,cpu_baseline,prefill_8b_m4096,prefill_4b,decode,moe,weight_quant"
+DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
+           "weight_quant")
 
 
 def main():

@@ -152,11 +152,11 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
  * as nothing else writes its first 16 KiB.  Calls that may overlap in time (different
  * streams) must not share a workspace.
  *
- * w8a8_gemm_config_info(config, out4): writes {tile rows, tile columns, k-groups, 1 if k may
- *   be split across workgroups else 0} of the configuration (host, 4 int32).  A
- *   configuration with g > 1 k-groups splits k inside the workgroup and accepts only
- *   k % (128 * g) == 0.
- *   Errors: out4 NULL -> I8QL_ERR_NULL; config outside [0, I8QL_W8A8_NUM_CONFIGS) ->
+ * w8a8_gemm_config_info(config, out5): writes {tile rows, tile columns, k-groups, 1 if k may
+ *   be split across workgroups else 0, 1 if it runs w8a8_gemm_g128 else 0} of the
+ *   configuration (host, 5 int32).  A configuration with g > 1 k-groups splits k inside the
+ *   workgroup and accepts only k % (128 * g) == 0.
+ *   Errors: out5 NULL -> I8QL_ERR_NULL; config outside [0, I8QL_W8A8_NUM_CONFIGS) ->
  *   I8QL_ERR_ARG.
  * w8a8_gemm_choose_config(m, n, k, cus): the configuration w8a8_gemm launches for an
  *   m x n x k product on a device with `cus` compute units (host arithmetic only, no HIP
@@ -189,7 +189,7 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
 #define I8QL_W8A8_NUM_CONFIGS 12
 #define I8QL_W8A8_MAX_SPLITS 8
 #define I8QL_W8A8_SPLIT_MAX_TILES 4096
-i8ql_status w8a8_gemm_config_info(int config, int32_t* out4);
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out5);
 int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus);
 i8ql_status w8a8_gemm_with_config(int config, const int8_t* xq, const float* x_scale,
                                   const int8_t* wq, const float* w_scale, const float* bias,
@@ -313,6 +313,37 @@ i8ql_status quantize_per_group_int8(const void* w, i8ql_dtype w_dtype, int64_t n
 i8ql_status w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
                             const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
                             int64_t n, int64_t k, void* stream);
+
+/*
+ * w8a8_gemm_g128 — W8A8 with one weight scale per group of I8QL_GROUP_SIZE input channels.
+ *
+ * Defines: [Day6] The mechanism, block 1 (a weight scale per run of 128 consecutive input
+ * channels, so an outlier coarsens only its own run) and block 5 (both operands int8, the
+ * product on the 8-bit matrix units); per-token activation scales as for w8a8_gemm.
+ *
+ *   part_g[i, j] = sum_{c in group g} xq[i, c] * wq[j, c]          (exact, int32)
+ *   y[i, j]      = x_scale[i] * sum_g w_scale[j, g] * part_g[i, j]  (+ bias[j])
+ *   in float32: each group's partial is converted (exactly) and multiplied by its scale with
+ *   one rounding into a running sum, in increasing g; the sum is then multiplied by
+ *   x_scale[i] and the bias added (round to nearest each); stored as float32 or rne bfloat16.
+ *
+ * xq [m, k] and wq [n, k] int8, 16-byte aligned; x_scale [m] float32; w_scale [n, k / 128]
+ * float32 (as quantize_per_group_int8 writes it); bias [n] float32 or NULL; y [m, n] of
+ * y_dtype in {I8QL_BF16, I8QL_F32}.  m, n >= 0; k >= 128, k % 128 == 0.
+ * Errors: y_dtype I32 or another dtype -> I8QL_ERR_DTYPE (the int32 accumulator of all groups
+ * is w8a8_gemm's); k not a positive multiple of 128 or too many tiles -> I8QL_ERR_SHAPE;
+ * NULL -> I8QL_ERR_NULL; alignment -> I8QL_ERR_ALIGN.
+ * w8a8_gemm_g128_with_config(config, ...): on configuration `config`, which must run group
+ * scales (w8a8_gemm_config_info), or -1 for the cost model's choice; other values ->
+ * I8QL_ERR_ARG.
+ */
+i8ql_status w8a8_gemm_g128(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                           const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
+                           int64_t m, int64_t n, int64_t k, void* stream);
+i8ql_status w8a8_gemm_g128_with_config(int config, const int8_t* xq, const float* x_scale,
+                                       const int8_t* wq, const float* w_scale,
+                                       const float* bias, void* y, i8ql_dtype y_dtype,
+                                       int64_t m, int64_t n, int64_t k, void* stream);
 
 /*
  * The mixture-of-experts steps on either side of grouped_w8a16_gemm.  [P5a] Summary runs the

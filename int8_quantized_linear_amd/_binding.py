@@ -22,7 +22,8 @@ _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8Q
 EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
            "w8a8_gemm_with_config", "w8a8_gemm_choose_plan", "w8a8_gemm_workspace_size",
-           "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "grouped_w8a16_silu_gemm", "moe_route_topk",
+           "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "w8a8_gemm_g128",
+           "w8a8_gemm_g128_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
            "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128", "i8ql_status_string",
            "i8ql_last_hip_error")
 GROUP_SIZE = 128  # I8QL_GROUP_SIZE
@@ -73,6 +74,10 @@ def load_library(path: str = LIB_PATH):
         lib.w8a8_gemm_with_plan.restype = I
         lib.w8a8_gemm_noalloc.argtypes = [I, I, P, P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a8_gemm_noalloc.restype = I
+        lib.w8a8_gemm_g128_with_config.argtypes = [I, P, P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a8_gemm_g128_with_config.restype = I
+        lib.w8a8_gemm_g128.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+        lib.w8a8_gemm_g128.restype = I
         lib.w8a16_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a16_gemm.restype = I
         lib.grouped_w8a16_gemm.argtypes = [P, I, P, P, I64, P, I64, I64, P, I, I64, I64, P]
@@ -243,6 +248,32 @@ def w8a8_gemm_noalloc(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloa
     return y
 
 
+def w8a8_gemm_g128(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.bfloat16, out=None,
+                   config=-1):
+    """W8A8 with weight scales per group of 128 input channels: ``w_scale`` [N, K/128]
+    (from ``quantize_per_group_int8``); ``y = x_scale[:, None] * sum_g w_scale[:, g] *
+    (xq_g @ wq_g.T) (+ bias)``, bf16 or float32."""
+    _check(xq, "xq", (torch.int8,), 2)
+    dev = xq.device
+    _check(wq, "wq", (torch.int8,), 2, dev)
+    _check(x_scale, "x_scale", (torch.float32,), 1, dev)
+    _check(w_scale, "w_scale", (torch.float32,), 2, dev)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k or x_scale.shape[0] != m or k % GROUP_SIZE or \
+            tuple(w_scale.shape) != (n, k // GROUP_SIZE):
+        raise ValueError("xq, x_scale, wq and w_scale disagree")
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), 1, dev)
+        if bias.shape[0] != n:
+            raise ValueError("bias must have N entries")
+    y = _out(out, (m, n), out_dtype, dev)
+    with torch.cuda.device(dev):
+        _call("w8a8_gemm_g128_with_config", int(config), _ptr(xq), _ptr(x_scale), _ptr(wq),
+              _ptr(w_scale), _ptr(bias), _ptr(y), _DTYPE[out_dtype], m, n, k, _stream(dev))
+    return y
+
+
 def _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out):
     _check(xq, "xq", (torch.int8,), 2)
     dev = xq.device
@@ -260,10 +291,10 @@ def _w8a8_args(xq, x_scale, wq, w_scale, bias, out_dtype, out):
 
 
 def w8a8_gemm_config_info(config: int):
-    """(tile rows, tile columns, k-groups, splittable) of W8A8 tile configuration
-    ``config``."""
+    """(tile rows, tile columns, k-groups, splittable, runs group scales) of W8A8 tile
+    configuration ``config``."""
     lib = load_library()
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 5)()
     st = lib.w8a8_gemm_config_info(int(config), ctypes.cast(out, ctypes.c_void_p))
     if st != 0:
         raise I8qlError("w8a8_gemm_config_info", st, lib)

@@ -94,7 +94,7 @@ i8ql_status w8a8_validate(int config, int splits, const int8_t* xq, const float*
   if (config == -1 ? splits != -1 : (splits < 1 || splits > I8QL_W8A8_MAX_SPLITS))
     return I8QL_ERR_ARG;
   if (config >= 0) {
-    int32_t geo[4];
+    int32_t geo[5];
     i8ql::w8a8_config_geometry(config, geo);
     if (k % (128 * static_cast<int64_t>(geo[2])) != 0 && geo[2] > 1) return I8QL_ERR_ARG;
     if (splits > 1 && (!geo[3] || splits > (k + 127) / 128)) return I8QL_ERR_ARG;
@@ -169,11 +169,41 @@ i8ql_status w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                              nullptr, 0, stream);
 }
 
-i8ql_status w8a8_gemm_config_info(int config, int32_t* out4) {
-  if (!out4) return I8QL_ERR_NULL;
+i8ql_status w8a8_gemm_config_info(int config, int32_t* out5) {
+  if (!out5) return I8QL_ERR_NULL;
   if (config < 0 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
-  i8ql::w8a8_config_geometry(config, out4);
+  i8ql::w8a8_config_geometry(config, out5);
   return I8QL_OK;
+}
+
+i8ql_status w8a8_gemm_g128_with_config(int config, const int8_t* xq, const float* x_scale,
+                                       const int8_t* wq, const float* w_scale,
+                                       const float* bias, void* y, i8ql_dtype y_dtype,
+                                       int64_t m, int64_t n, int64_t k, void* stream) {
+  if (y_dtype != I8QL_BF16 && y_dtype != I8QL_F32) return I8QL_ERR_DTYPE;
+  if (m < 0 || n < 0 || k < 1 || k % I8QL_GROUP_SIZE != 0) return I8QL_ERR_SHAPE;
+  if (!w8a8_sizes_ok(m, n, k)) return I8QL_ERR_SHAPE;
+  if (config < -1 || config >= I8QL_W8A8_NUM_CONFIGS) return I8QL_ERR_ARG;
+  if (config >= 0) {
+    int32_t geo[5];
+    i8ql::w8a8_config_geometry(config, geo);
+    if (!geo[4]) return I8QL_ERR_ARG;
+  }
+  if (m == 0 || n == 0) return I8QL_OK;
+  if (!xq || !wq || !y || !x_scale || !w_scale) return I8QL_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return I8QL_ERR_ALIGN;
+  if (!aligned(y, elem_bytes(y_dtype)) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(bias, 4))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_w8a8_gemm_g128(xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n,
+                                                k, config, static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status w8a8_gemm_g128(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                           const float* w_scale, const float* bias, void* y, i8ql_dtype y_dtype,
+                           int64_t m, int64_t n, int64_t k, void* stream) {
+  return w8a8_gemm_g128_with_config(-1, xq, x_scale, wq, w_scale, bias, y, y_dtype, m, n, k,
+                                    stream);
 }
 
 int w8a8_gemm_choose_config(int64_t m, int64_t n, int64_t k, int cus) {

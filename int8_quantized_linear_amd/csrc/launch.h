@@ -64,7 +64,15 @@ int w8a8_choose_config(int64_t m, int64_t n, int64_t k, int cus);
 int w8a8_choose_plan(int64_t m, int64_t n, int64_t k, int cus, int64_t ws_bytes, int* splits);
 int64_t w8a8_plan_workspace(int config, int splits, int64_t m, int64_t n);
 bool w8a8_plan_valid(int config, int splits, int64_t m, int64_t n, int64_t k);
-void w8a8_config_geometry(int config, int32_t* out4);
+void w8a8_config_geometry(int config, int32_t* out5);
+
+// W8A8 with weight scales per group of 128 input channels, w_scale [n, k / 128]
+// (k % 128 == 0), on a group-scale configuration (`config`, or -1 for the model's choice).
+int w8a8_choose_gs_config(int64_t m, int64_t n, int64_t k, int cus);
+hipError_t launch_w8a8_gemm_g128(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                 const float* w_scale, const float* bias, void* y,
+                                 i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                 int config, hipStream_t stream);
 
 hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,

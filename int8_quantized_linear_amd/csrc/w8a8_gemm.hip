@@ -69,6 +69,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -201,8 +202,10 @@ __device__ __forceinline__ void wait_and_barrier(int pending) {
   bare_barrier();
 }
 
-// Tile geometry and per-thread addressing shared by the pieces of the kernel.
-template <int BM_, int BN_, int BK_, int STAGES_, int KS_, int WM_, int WN_>
+// Tile geometry and per-thread addressing shared by the pieces of the kernel.  GS: weight
+// scales per group of 128 input channels; each stage then also holds the step's scales, one
+// 256-byte slot per wavefront (a dword per lane, loaded with the operand rows).
+template <int BM_, int BN_, int BK_, int STAGES_, int KS_, int WM_, int WN_, bool GS_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, KS = KS_;
   static constexpr int WM = WM_, WN = WN_;          // wavefront grid of a k-group
@@ -214,7 +217,10 @@ struct Cfg {
   static constexpr int ROWS_PER_LOAD = 1024 / BK;   // rows per wavefront load instruction
   static constexpr int LOADS = (BM + BN) / ROWS_PER_LOAD / WAVES;  // per wavefront per step
   static constexpr int SLICES = BK / 32;
-  static constexpr int STAGE_BYTES = (BM + BN) * BK;
+  static constexpr bool GS = GS_;
+  static constexpr int ROW_BYTES = (BM + BN) * BK;   // operand rows of a stage
+  static constexpr int STAGE_BYTES = ROW_BYTES + (GS ? WAVES * 256 : 0);
+  static constexpr int VM = LOADS + (GS ? 1 : 0);    // vector-memory loads per wave per step
   static constexpr size_t GROUP_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
   static constexpr size_t RED_BYTES = static_cast<size_t>(KS / 2) * BM * BN * 4;
   static constexpr size_t LDS_BYTES = KS * GROUP_BYTES > RED_BYTES ? KS * GROUP_BYTES : RED_BYTES;
@@ -223,8 +229,45 @@ struct Cfg {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "sub-tile must be whole 32x32 blocks");
   static_assert(LOADS * ROWS_PER_LOAD * WAVES == BM + BN, "loads must split over waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "wait_and_barrier handles up to 3 pending");
-  static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
+  static_assert(VM * (STAGES - 1) <= 63, "vmcnt range");
+  static_assert(!GS || (KS == 1 && STAGES >= 3 && BK == 128 && WTN <= 64),
+                "group scales: one k-group, spread refills, a step per group, one scale load");
 };
+
+// Group-scale state of a lane (GS only): where its column's scales are, this wavefront's
+// scale slot in a stage, the scales of the step being computed (one per 32-column block) and
+// the float accumulators, to which each step adds its exact int32 partial times its scale.
+template <class C>
+struct GroupScales {
+  const float* src;  // scales of this lane's load column: step g at src[g]
+  int slot;          // byte offset of this wavefront's scale slot within a stage
+  float cur[C::TN];
+  v16f facc[C::TM][C::TN];
+};
+
+// The scales of the step held in `stage`, for this lane's columns j * 32 + lane % 32.
+template <class C>
+__device__ __forceinline__ void gs_read(const int8_t* stage, GroupScales<C>& gs, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+    gs.cur[j] = *reinterpret_cast<const float*>(stage + gs.slot + (j * 32 + lane % 32) * 4);
+}
+
+// End of a step: facc += (float)acc * scale (the conversion is exact: a step's partial sum
+// is below 128 * 127^2 < 2^24 in magnitude), then acc = 0 for the next step.
+template <class C>
+__device__ __forceinline__ void gs_apply(v16i (&acc)[C::TM][C::TN], GroupScales<C>& gs) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        gs.facc[i][j][r] = __fmaf_rn(static_cast<float>(acc[i][j][r]), gs.cur[j],
+                                     gs.facc[i][j][r]);
+        acc[i][j][r] = 0;
+      }
+}
 
 // Issue this wavefront's direct-to-LDS loads of k step `step` into `stage`.  A chunk past
 // the end of the row (k % 16 == 0, so chunks are whole) reads the row start instead, which is
@@ -232,7 +275,7 @@ struct Cfg {
 template <class C>
 __device__ __forceinline__ void issue_step(int8_t* stage, const int8_t* const* src,
                                            const int* col, const int* dst, int step,
-                                           int64_t k) {
+                                           int64_t k, const GroupScales<C>& gs) {
   const int64_t k0 = static_cast<int64_t>(step) * C::BK;
 #pragma unroll
   for (int j = 0; j < C::LOADS; ++j) {
@@ -240,13 +283,14 @@ __device__ __forceinline__ void issue_step(int8_t* stage, const int8_t* const* s
     const int8_t* g = src[j] + (kk < k ? kk : 0);
     __builtin_amdgcn_global_load_lds(g, stage + dst[j], 16, 0, 0);
   }
+  if constexpr (C::GS) __builtin_amdgcn_global_load_lds(gs.src + step, stage + gs.slot, 4, 0, 0);
 }
 
 // Loads [J0, J1) of issue_step (for spreading a step's loads over several slices).
 template <class C, int J0, int J1>
 __device__ __forceinline__ void issue_part(int8_t* stage, const int8_t* const* src,
                                            const int* col, const int* dst, int step,
-                                           int64_t k) {
+                                           int64_t k, const GroupScales<C>& gs) {
   const int64_t k0 = static_cast<int64_t>(step) * C::BK;
 #pragma unroll
   for (int j = J0; j < J1; ++j) {
@@ -254,6 +298,9 @@ __device__ __forceinline__ void issue_part(int8_t* stage, const int8_t* const* s
     const int8_t* g = src[j] + (kk < k ? kk : 0);
     __builtin_amdgcn_global_load_lds(g, stage + dst[j], 16, 0, 0);
   }
+  // (the step's scales go with its first part)
+  if constexpr (C::GS && J0 == 0)
+    __builtin_amdgcn_global_load_lds(gs.src + step, stage + gs.slot, 4, 0, 0);
 }
 
 // Read the fragments of 32-k slice `slice` of a step from an LDS stage.
@@ -339,19 +386,20 @@ __device__ __forceinline__ void spread_slice(const int8_t* stage, int8_t* fill,
                                              const int* dst, int fill_step, int64_t k,
                                              int a_off, int b_off, int fx, int lane,
                                              v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
-                                             v16i (&acc)[C::TM][C::TN]) {
+                                             v16i (&acc)[C::TM][C::TN],
+                                             const GroupScales<C>& gs) {
   if constexpr (S + 1 < C::SLICES) {
     using P = Spread<C>;
     read_slice<C>(stage, S + 1, a_off, b_off, fx, lane, fa[(S + 1) % 2], fb[(S + 1) % 2]);
-    issue_part<C, P::lo(S), P::hi(S)>(fill, src, col, dst, fill_step, k);
+    issue_part<C, P::lo(S), P::hi(S)>(fill, src, col, dst, fill_step, k, gs);
     mfma_slice<C>(fa[S % 2], fb[S % 2], acc);
-    constexpr int kLoads = P::hi(S) - P::lo(S);
+    constexpr int kLoads = P::hi(S) - P::lo(S) + (C::GS && S == 0 ? 1 : 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                       // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, 2);           // DS reads
     if constexpr (kLoads > 0) __builtin_amdgcn_sched_group_barrier(0x020, kLoads, 2);
     __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - 1, 2);       // MFMAs
     spread_slice<C, S + 1>(stage, fill, src, col, dst, fill_step, k, a_off, b_off, fx, lane,
-                           fa, fb, acc);
+                           fa, fb, acc, gs);
   }
 }
 
@@ -387,13 +435,15 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
                                        const int* dst, int a_off, int b_off, int fx, int lane,
                                        int base, int t, int ksteps, int64_t k, int tail_valid,
                                        v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
-                                       v16i (&acc)[C::TM][C::TN]) {
+                                       v16i (&acc)[C::TM][C::TN], GroupScales<C>& gs) {
   constexpr bool kSpread = C::STAGES >= 3;
+  // (the stage of step t holds its scales until step t + 1 refills it, after this step)
+  if constexpr (C::GS) gs_read<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, gs, lane);
   if constexpr (ISSUE && kSpread) {
     const int u = t + C::STAGES - 1;
     spread_slice<C, 0>(lds + (t % C::STAGES) * C::STAGE_BYTES,
                        lds + (u % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + u, k,
-                       a_off, b_off, fx, lane, fa, fb, acc);
+                       a_off, b_off, fx, lane, fa, fb, acc, gs);
   } else {
     step_inner<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
   }
@@ -401,7 +451,7 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
   // Keep this step's MFMAs in front of the LDS drain: they do not touch memory, so nothing
   // else stops the scheduler from sinking them below it and waiting on the fresh reads.
   __builtin_amdgcn_sched_barrier(0);
-  wait_and_barrier<C::LOADS>(min(C::STAGES - 2, ksteps - 2 - t));
+  wait_and_barrier<C::VM>(min(C::STAGES - 2, ksteps - 2 - t));
   if (ZERO && tail_valid != 0) zero_tail<C>(next, tail_valid);
   constexpr int last = (C::SLICES - 1) % 2;  // SLICES is even, so set 0 is free
   if constexpr (ISSUE && !kSpread) {
@@ -409,7 +459,7 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
     // keeps reads that follow them in place)
     read_slice<C>(next, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
     issue_step<C>(lds + (t % C::STAGES) * C::STAGE_BYTES, src, col, dst, base + t + C::STAGES,
-                  k);
+                  k, gs);
     mfma_slice<C>(fa[last], fb[last], acc);
     loads_under_mfmas<C, 1>();
   } else {
@@ -417,6 +467,7 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
     mfma_slice<C>(fa[last], fb[last], acc);
     reads_under_mfmas<C, 1>();
   }
+  if constexpr (C::GS) gs_apply<C>(acc, gs);
 }
 
 // Epilogue through LDS.  A wavefront's accumulators hold one column per lane (32x32 MFMA
@@ -431,7 +482,15 @@ __device__ __forceinline__ void k_step(int8_t* lds, const int8_t* const* src, co
 constexpr int kScrWords = 72;                   // words per scratch row (64 + padding)
 constexpr int kScrBytes = 32 * kScrWords * 4;   // scratch per wavefront
 
-template <class C, int YT>
+// GS: the accumulators hold the float32 bits of the weight-scaled sums (the group scales
+// were applied per step), so only the token scale and the bias remain.
+template <int YT, bool GS>
+__device__ __forceinline__ float epilogue_value(int a, float sx, float sw) {
+  if constexpr (GS) return __fmul_rn(__int_as_float(a), sx);
+  return __fmul_rn(__fmul_rn(static_cast<float>(a), sx), sw);
+}
+
+template <class C, int YT, bool GS>
 __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], int* scr,
                                              int lane, const float* __restrict__ x_scale,
                                              const float* __restrict__ w_scale,
@@ -445,7 +504,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t c = c0 + j * 32 + lane % 32;
-      sw[j] = w_scale[c < n ? c : n - 1];
+      sw[j] = GS ? 1.0f : w_scale[c < n ? c : n - 1];
       bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
     }
   }
@@ -473,7 +532,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
           if constexpr (YT == I8QL_I32) {
             bits = acc[i][j][r];
           } else {
-            float v = __fmul_rn(__fmul_rn(static_cast<float>(acc[i][j][r]), sx[r]), sw[j]);
+            float v = epilogue_value<YT, GS>(acc[i][j][r], sx[r], sw[j]);
             if (bias) v = __fadd_rn(v, bj[j]);
             bits = __float_as_int(v);
           }
@@ -515,7 +574,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
 // a misaligned output).  Per 32-row block the row scales are loaded up front at clamped
 // (valid) indices, so that their loads are issued together and waited for once instead of
 // once per output row.  (r0, c0): the wavefront's first output row and column.
-template <class C, int YT>
+template <class C, int YT, bool GS>
 __device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], int lane,
                                               const float* __restrict__ x_scale,
                                               const float* __restrict__ w_scale,
@@ -529,7 +588,7 @@ __device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], i
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t c = col_base + j * 32;
-      sw[j] = w_scale[c < n ? c : n - 1];
+      sw[j] = GS ? 1.0f : w_scale[c < n ? c : n - 1];
       bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
     }
   }
@@ -555,7 +614,7 @@ __device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], i
         if constexpr (YT == I8QL_I32) {
           static_cast<int32_t*>(y)[row * n + c] = a;
         } else {
-          float v = __fmul_rn(__fmul_rn(static_cast<float>(a), sx[r]), sw[j]);
+          float v = epilogue_value<YT, GS>(a, sx[r], sw[j]);
           if (bias) v = __fadd_rn(v, bj[j]);
           if constexpr (YT == I8QL_F32) {
             static_cast<float*>(y)[row * n + c] = v;
@@ -571,7 +630,7 @@ __device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], i
 // The fused epilogue of a wavefront's accumulators: through LDS with 16-byte stores when the
 // output allows it, else from registers.  `scr` is this wavefront's LDS scratch; the caller
 // has made sure no wavefront still reads the LDS it overlaps.
-template <class C, int YT>
+template <class C, int YT, bool GS = false>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* scr, int lane,
                                          const float* __restrict__ x_scale,
                                          const float* __restrict__ w_scale,
@@ -579,9 +638,9 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* s
                                          int64_t n, int64_t r0, int64_t c0) {
   constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
   if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
-    epilogue_lds<C, YT>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+    epilogue_lds<C, YT, GS>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
   } else {
-    epilogue_regs<C, YT>(acc, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+    epilogue_regs<C, YT, GS>(acc, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
   }
 }
 
@@ -590,14 +649,20 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* s
 // splitk_fixup (zero counters on entry; they are zero again on exit).  Without XS the
 // fix-up is not compiled in (it would push the largest tiles past the register file) and
 // `splits` must be 1.
-template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT, bool XS>
+//
+// GS: w_scale holds one scale per (output channel, group of 128 input channels), [n, k / 128]
+// (k % 128 == 0); each k step is one group, and its exact int32 partial is converted and
+// multiplied by the step's scale into float32 accumulators (see gs_apply).
+template <int BM, int BN, int BK, int STAGES, int KS, int WM, int WN, int YT, bool XS,
+          bool GS = false>
 __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
     const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
     int splits_arg, int* __restrict__ ws) {
   static_assert(!XS || KS == 1, "k split across workgroups needs one k-group");
-  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
+  static_assert(!(XS && GS), "group scales are not combined with a split");
+  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN, GS>;
   const int splits = XS ? splits_arg : 1;
   constexpr int TM = C::TM, TN = C::TN;
   extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
@@ -650,13 +715,28 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+  GroupScales<C> gs;
+  if constexpr (GS) {
+    // lane l loads the scale of its wavefront sub-tile's column l % WTN (WTN <= 64), which
+    // lands at position l of the wavefront's slot: columns j * 32 + lane % 32 are then read
+    // back at that position
+    const int64_t groups = k / BK;
+    gs.src = w_scale + min(n0 + wn * C::WTN + lane % C::WTN, n - 1) * groups;
+    gs.slot = C::ROW_BYTES + wave * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gs.facc[i][j][r] = 0.0f;
+  }
 
   // steps issued ahead of the first: all stages, but with 3 or more stages the last one is
   // filled during step 0
   constexpr int kAhead = STAGES >= 3 ? STAGES - 1 : STAGES;
 #pragma unroll
   for (int s = 0; s < kAhead; ++s)
-    if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, base + s, k);
+    if (s < ksteps) issue_step<C>(lds + s * C::STAGE_BYTES, src, col, dst, base + s, k, gs);
 
   const int frow = lane % 32;
   const int fx = swizzle<BK>(frow);  // swizzle of this lane's fragment rows (period 32)
@@ -667,23 +747,33 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
       KS == 1 && split == splits - 1 ? static_cast<int>((k % BK) / 16) : 0;  // 0: none
 
   v4i fa[2][TM], fb[2][TN];
-  wait_and_barrier<C::LOADS>(min(kAhead - 1, ksteps - 1));
+  wait_and_barrier<C::VM>(min(kAhead - 1, ksteps - 1));
   if (tail_valid != 0 && ksteps == 1) zero_tail<C>(lds, tail_valid);
   read_slice<C>(lds, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
   int t = 0;
   for (; t + kAhead < ksteps; ++t)
     k_step<C, true, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
-                           tail_valid, fa, fb, acc);
+                           tail_valid, fa, fb, acc, gs);
   for (; t + 2 < ksteps; ++t)
     k_step<C, false, false>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
-                            tail_valid, fa, fb, acc);
+                            tail_valid, fa, fb, acc, gs);
   if (t + 1 < ksteps) {
     k_step<C, false, true>(lds, src, col, dst, a_off, b_off, fx, lane, base, t, ksteps, k,
-                           tail_valid, fa, fb, acc);
+                           tail_valid, fa, fb, acc, gs);
     ++t;
   }
+  if constexpr (GS) gs_read<C>(lds + (t % STAGES) * C::STAGE_BYTES, gs, lane);
   step_inner<C>(lds + (t % STAGES) * C::STAGE_BYTES, a_off, b_off, fx, lane, fa, fb, acc);
   mfma_slice<C>(fa[(C::SLICES - 1) % 2], fb[(C::SLICES - 1) % 2], acc);
+  if constexpr (GS) {
+    gs_apply<C>(acc, gs);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __float_as_int(gs.facc[i][j][r]);
+  }
 
   if constexpr (KS > 1) {
     // Sum the k-groups' partial tiles in a fixed tree through LDS (int32, exact): in each
@@ -731,8 +821,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     bare_barrier();
   }
-  epilogue<C, YT>(acc, reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes), lane,
-                  x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+  epilogue<C, YT, GS>(acc, reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes),
+                      lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
 }
 
 // ---- two LDS slots for A, three for B ---------------------------------------------------
@@ -924,12 +1014,13 @@ hipError_t launch_split(const int8_t* xq, const float* x_scale, const int8_t* wq
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM, int WN, bool XS>
+template <int BM, int BN, int BK, int STAGES, int KS, int YT, int WM, int WN, bool XS,
+          bool GS = false>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
                       int64_t k, int splits, int* ws, hipStream_t stream) {
-  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN>;
-  constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT, XS>;
+  using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN, GS>;
+  constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT, XS, GS>;
   const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(C::LDS_BYTES));
   if (e != hipSuccess) return e;
   const int64_t units = ((m + BM - 1) / BM) * ((n + BN - 1) / BN) * splits;
@@ -964,25 +1055,33 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // per-shape best, also with each shape predicted by a fit that left it out.  A split wins on
 // the long-k shapes: 512 x 2560 x 9728 27.6 us with 128 x 128 tiles and 3 splits (33.6
 // without), 128 x 2560 x 9728 15.1 us with 64 x 64 tiles and 3 splits (18.8).
+//
+// Group-scale products (w8a8_gemm_g128) run on the configurations marked `gs`: one k-group,
+// spread refills (3 or more stages) and wavefront sub-tiles at most 64 columns wide, so that
+// one dword load per wavefront carries a step's scales.  They use the same model with each
+// step's time scaled by kGsStep (the per-step conversion and fused multiply-add of the int32
+// partials).
 struct Candidate {
   int bm, bn, ks;                // tile and k-groups
   bool xsplit;                   // k may be split across workgroups
+  bool gs;                       // runs group-scale products
   double t_step, t_round, t0;    // cost model (us)
 };
 constexpr Candidate kCandidates[] = {
-    {256, 256, 1, true, 1.3616, 21.063, -10.348},   // 0: 2 stages, 8 wavefronts 64x128
-    {256, 320, 1, false, 1.5576, 27.308, -14.718},  // 1: 2 stages, 8 wavefronts 64x160
-    {256, 192, 1, false, 1.0216, 17.150, -7.651},   // 2: 2 A + 3 B slots, 8 wavefronts 64x96
-    {128, 320, 1, false, 0.9822, 13.467, -3.992},   // 3: 2 A + 3 B slots, 8 wavefronts 32x160
-    {128, 160, 1, true, 0.5742, 7.669, 0.439},      // 4: 3 stages, 4 wavefronts 32x160
-    {256, 128, 1, true, 0.7426, 12.247, -6.637},    // 5: 3 stages, 8 wavefronts 64x64
-    {128, 128, 1, true, 0.5263, 5.399, 0.071},      // 6: 3 stages, 8 wavefronts 64x32
-    {128, 64, 2, false, 0.6945, 4.216, 0.586},      // 7: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 64, 2, false, 0.4855, 2.353, 2.777},       // 8: 3 stages, 2 k-groups of 4 wavefronts
-    {64, 32, 4, false, 0.6247, 2.558, 2.713},       // 9: 3 stages, 4 k-groups of 2 wavefronts
-    {64, 64, 1, true, 0.2183, 0.705, 5.779},        // 10: 4 stages, 4 wavefronts
-    {320, 256, 1, false, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
+    {256, 256, 1, true, false, 1.3616, 21.063, -10.348},   // 0: 2 stages, 8 wavefronts 64x128
+    {256, 320, 1, false, false, 1.5576, 27.308, -14.718},  // 1: 2 stages, 8 wavefronts 64x160
+    {256, 192, 1, false, false, 1.0216, 17.150, -7.651},   // 2: 2 A + 3 B slots, 8 waves 64x96
+    {128, 320, 1, false, false, 0.9822, 13.467, -3.992},   // 3: 2 A + 3 B slots, 8 waves 32x160
+    {128, 160, 1, true, false, 0.5742, 7.669, 0.439},      // 4: 3 stages, 4 wavefronts 32x160
+    {256, 128, 1, true, true, 0.7426, 12.247, -6.637},     // 5: 3 stages, 8 wavefronts 64x64
+    {128, 128, 1, true, true, 0.5263, 5.399, 0.071},       // 6: 3 stages, 8 wavefronts 64x32
+    {128, 64, 2, false, false, 0.6945, 4.216, 0.586},      // 7: 3 stages, 2 k-groups of 4 waves
+    {64, 64, 2, false, false, 0.4855, 2.353, 2.777},       // 8: 3 stages, 2 k-groups of 4 waves
+    {64, 32, 4, false, false, 0.6247, 2.558, 2.713},       // 9: 3 stages, 4 k-groups of 2 waves
+    {64, 64, 1, true, true, 0.2183, 0.705, 5.779},         // 10: 4 stages, 4 wavefronts
+    {320, 256, 1, false, false, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
 };
+constexpr double kGsStep = 1.0;  // step-time factor of group-scale products
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
 constexpr double kFix0 = 0.0, kFix1 = 2.1;  // split fix-up cost model (us)
 
@@ -1010,6 +1109,20 @@ hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const
   }
 #undef I8QL_W8A8_CFG
 #undef I8QL_W8A8_SPLIT
+}
+
+template <int YT>
+hipError_t launch_candidate_gs(int c, const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, const float* bias, void* y, int64_t m,
+                               int64_t n, int64_t k, hipStream_t stream) {
+#define I8QL_W8A8_GS(...) \
+  launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, 1, nullptr, stream)
+  switch (c) {
+    case 5: return I8QL_W8A8_GS(256, 128, 128, 3, 1, YT, 4, 2, false, true);
+    case 6: return I8QL_W8A8_GS(128, 128, 128, 3, 1, YT, 2, 4, false, true);
+    default: return I8QL_W8A8_GS(64, 64, 128, 4, 1, YT, 2, 2, false, true);
+  }
+#undef I8QL_W8A8_GS
 }
 
 // Compute units of the current device (cached per device id).
@@ -1072,6 +1185,28 @@ int choose_plan(int64_t m, int64_t n, int64_t k, int cus, int64_t ws_bytes, int*
     }
   }
   *splits_out = best_s;
+  return best;
+}
+
+// The group-scale configuration with the lowest modelled time.
+int choose_gs(int64_t m, int64_t n, int64_t k, int cus) {
+  int best = 10;
+  double best_t = 0.0;
+  bool found = false;
+  const int64_t ksteps = (k + 127) / 128;
+  for (int c = 0; c < kNumCandidates; ++c) {
+    const Candidate& d = kCandidates[c];
+    if (!d.gs) continue;
+    const int64_t units = ((m + d.bm - 1) / d.bm) * ((n + d.bn - 1) / d.bn);
+    if (units > kMaxGrid - kXcds) continue;
+    const double rounds = static_cast<double>((units + cus - 1) / cus);
+    const double t = kGsStep * d.t_step * rounds * ksteps + d.t_round * rounds + d.t0;
+    if (!found || t < best_t) {
+      best = c;
+      best_t = t;
+      found = true;
+    }
+  }
   return best;
 }
 
@@ -1159,11 +1294,26 @@ bool w8a8_plan_valid(int config, int splits, int64_t m, int64_t n, int64_t k) {
   return plan_time(config, splits, m, n, k, 256) >= 0.0;
 }
 
-void w8a8_config_geometry(int config, int32_t* out4) {
-  out4[0] = kCandidates[config].bm;
-  out4[1] = kCandidates[config].bn;
-  out4[2] = kCandidates[config].ks;
-  out4[3] = kCandidates[config].xsplit ? 1 : 0;
+int w8a8_choose_gs_config(int64_t m, int64_t n, int64_t k, int cus) {
+  return choose_gs(m, n, k, cus);
+}
+
+void w8a8_config_geometry(int config, int32_t* out5) {
+  out5[0] = kCandidates[config].bm;
+  out5[1] = kCandidates[config].bn;
+  out5[2] = kCandidates[config].ks;
+  out5[3] = kCandidates[config].xsplit ? 1 : 0;
+  out5[4] = kCandidates[config].gs ? 1 : 0;
+}
+
+hipError_t launch_w8a8_gemm_g128(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                 const float* w_scale, const float* bias, void* y,
+                                 i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                 int config, hipStream_t stream) {
+  const int c = config >= 0 ? config : choose_gs(m, n, k, device_cus());
+  if (y_dtype == I8QL_F32)
+    return launch_candidate_gs<I8QL_F32>(c, xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_candidate_gs<I8QL_BF16>(c, xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
 }
 
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,

@@ -111,13 +111,13 @@ def test_w8a8_with_config_validation(lib):
     assert call(0, xq=NUL) == NULL
     assert call(0, k=72) == ALIGN
     for c in range(12):
-        geo = (ctypes.c_int32 * 4)()
+        geo = (ctypes.c_int32 * 5)()
         assert lib.w8a8_gemm_config_info(c, ctypes.cast(geo, ctypes.c_void_p)) == OK
         if geo[2] > 1:                      # k-groups need k % (128 * groups) == 0
             assert call(c, k=64) == ARG
             assert call(c, k=128 * geo[2] + 16) == ARG
             assert call(c, m=0, k=64) == ARG
-    assert lib.w8a8_gemm_config_info(12, ctypes.cast((ctypes.c_int32 * 4)(), ctypes.c_void_p)) == ARG
+    assert lib.w8a8_gemm_config_info(12, ctypes.cast((ctypes.c_int32 * 5)(), ctypes.c_void_p)) == ARG
     assert lib.w8a8_gemm_config_info(0, NUL) == NULL
 
 
@@ -201,7 +201,7 @@ def test_w8a8_config_table_and_choices():
         for n in (32, 1000, 2560, 6144, 19456):
             for k in (16, 272, 2560, 4096, 9728):
                 c = i8.w8a8_gemm_choose_config(m, n, k, 256)
-                bm, bn, g, _ = geos[c]
+                bm, bn, g, _, _ = geos[c]
                 assert g == 1 or k % (128 * g) == 0
     # the benchmark step's fused 4B projections at 2048 tokens take the 256x320, 256x192 and
     # 128x160 tiles that fill the 256 CUs in whole rounds

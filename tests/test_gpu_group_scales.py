@@ -88,3 +88,118 @@ def test_w8a16_g128_rejects_a_bias_of_the_wrong_length(dev):
     x = torch.zeros((1, 256), dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError):
         i8.w8a16_gemm_g128(x, q, s, torch.zeros(31, dtype=torch.float32, device=dev))
+
+
+# ---------------------------------------------------------------------------------------
+# W8A8 with group-128 weight scales ("Day 6 — Quantize It Yourself", The mechanism, blocks 1
+# and 5): codes and scales bitwise against the oracle; outputs within the float32 bound of
+# the kernel's arithmetic.  Each group's int32 partial is exact; the kernel adds the G = k/128
+# scaled partials with one rounding each, then multiplies by the token scale and adds the
+# bias, so |y - ref| <= (G + 3) u s_x sum_g |part_g| s_w[g] + 2 u |bias|, and
+# sum_g |part_g| s_w[g] <= (|q_x| @ (|q_w| * s_w per element).T).
+
+U32 = 2.0 ** -24
+GS_CONFIGS = [c for c in range(i8.W8A8_NUM_CONFIGS) if i8.w8a8_gemm_config_info(c)[4]]
+
+
+def w8a8_g128_tol(qx, sx, qw, sw, bias):
+    k = qx.shape[1]
+    wabs = np.abs(qw.astype(np.float64)) * np.repeat(sw.astype(np.float64), 128, axis=1)
+    tol = np.empty((qx.shape[0], qw.shape[0]), np.float64)
+    for r0 in range(0, qx.shape[0], 1024):
+        a = np.abs(qx[r0:r0 + 1024].astype(np.float64)) @ wabs.T
+        tol[r0:r0 + 1024] = (k // 128 + 3) * U32 * sx[r0:r0 + 1024, None].astype(np.float64) * a
+    if bias is not None:
+        tol += 2 * U32 * np.abs(bias.astype(np.float64))[None, :]
+    return tol
+
+
+def run_w8a8_g128(ref, dev, m, n, k, bias, seed, out_dtypes=(torch.bfloat16, torch.float32),
+                  config=-1, frac=0.001, rows=None):
+    g = wl.rng(seed)
+    w = wl.weight(g, n, k)
+    w[:, g.choice(k, 1)] *= np.float32(50.0)          # an outlier input column
+    wt, wv = host("bf16", w)
+    xt, xv = host("bf16", wl.activations(g, m, k, outlier_frac=frac))
+    qw, sw, qwr, swr = group_quant_vs_ref(ref, dev, wt, wv, "bf16")
+    qx, sx = i8.quantize_per_token_int8(xt.to(dev))
+    b_np = (g.standard_normal(n, dtype=np.float32) * np.float32(0.02)) if bias else None
+    b = torch.from_numpy(b_np).to(dev) if bias else None
+    ys = {od: i8.w8a8_gemm_g128(qx, sx, qw, sw, b, out_dtype=od, out=sentinel((m, n), od, dev),
+                                config=config) for od in out_dtypes}
+    if rows is None:
+        qxr, sxr = ref.quantize_rows(xv, "bf16")
+        np.testing.assert_array_equal(qx.cpu().numpy(), qxr)
+        np.testing.assert_array_equal(sx.cpu().numpy(), sxr)
+    else:
+        for y in ys.values():
+            assert not torch.isnan(y).any()           # every element written
+        qxr, sxr = ref.quantize_rows(xv[rows], "bf16")
+        idx = torch.from_numpy(rows).to(dev)
+        np.testing.assert_array_equal(qx[idx].cpu().numpy(), qxr)
+        ys = {od: y[idx] for od, y in ys.items()}
+    yref = ref.w8a8_grouped_scales(qxr, sxr, qwr, swr, 128, b_np)
+    tol = w8a8_g128_tol(qxr, sxr, qwr, swr, b_np)
+    for od, y in ys.items():
+        check_float(y, yref, tol, f"w8a8 g128 {m}x{n}x{k} {od}")
+
+
+@pytest.mark.parametrize("config", GS_CONFIGS)
+def test_w8a8_g128_every_config(ref, dev, config):
+    """Each group-scale configuration, forced: ragged tiles in both directions, one to 24
+    groups, more than one group of eight tile rows; an odd N takes the per-element epilogue."""
+    bm, bn = i8.w8a8_gemm_config_info(config)[:2]
+    for (m, n, k) in [(2 * bm + 37, 2 * bn + 24, 384), (bm - 3, bn + 19, 128),
+                      (9 * bm + 5, 3 * bn + 8, 3072)]:
+        print(f"w8a8 g128 config {config} ({bm}x{bn}): {m}x{n}x{k}", flush=True)
+        run_w8a8_g128(ref, dev, m, n, k, bias=(m % 2 == 1), seed=config * 13 + m, config=config)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (4, 256, 512), (130, 200, 384),
+                                   (300, 33, 2560), (257, 385, 1024), (1000, 1500, 4096)])
+def test_w8a8_g128_small(ref, dev, m, n, k):
+    run_w8a8_g128(ref, dev, m, n, k, bias=(n % 2 == 0), seed=m + n + k)
+
+
+G128_4B = [(m, n, k) for m in wl.PREFILL_4B_TOKENS for (n, k) in sorted(set(wl.DENSE_4B.values()))]
+G128_8B = [(m, n, k) for m in wl.PREFILL_8B_TOKENS for (n, k) in sorted(set(wl.DENSE_8B.values()))]
+
+
+@pytest.mark.parametrize("m,n,k", G128_4B)
+def test_w8a8_g128_dense_4b_prefill_full(ref, dev, m, n, k):
+    run_w8a8_g128(ref, dev, m, n, k, bias=False, seed=m + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", G128_8B)
+def test_w8a8_g128_dense_8b_prefill_full(ref, dev, m, n, k):
+    rows = None
+    if m > 4096:  # the 16384-token shapes: first and last 8 rows and 256 seeded random rows
+        g = wl.rng(m + n)
+        rows = np.array(sorted(set(range(8)) | set(range(m - 8, m)) |
+                               set(g.choice(m, 256, replace=False).tolist())))
+    run_w8a8_g128(ref, dev, m, n, k, bias=True, seed=m + n + k, frac=0.01, rows=rows)
+
+
+def test_w8a8_g128_equal_group_scales_match_per_channel(dev):
+    """Equal scales in all groups of a row: the same values as w8a8_gemm with that scale up to
+    the float32 summation of the group partials (here exact: every partial times a power of
+    two, sums below 2^24 of the scale's unit)."""
+    g = wl.rng(170)
+    m, n, k = 300, 260, 1024
+    qx = torch.from_numpy(g.integers(-127, 128, (m, k), dtype=np.int8)).to(dev)
+    qw = torch.from_numpy(g.integers(-127, 128, (n, k), dtype=np.int8)).to(dev)
+    sx = torch.full((m,), 2.0 ** -7, device=dev)
+    sw = torch.full((n,), 2.0 ** -9, device=dev)
+    swg = sw[:, None].repeat(1, k // 128).contiguous()
+    y1 = i8.w8a8_gemm(qx, sx, qw, sw, out_dtype=torch.float32)
+    y2 = i8.w8a8_gemm_g128(qx, sx, qw, swg, out_dtype=torch.float32)
+    assert torch.equal(y1, y2)
+
+
+def test_w8a8_g128_rejects_bad_arguments(dev):
+    q = torch.zeros((4, 256), dtype=torch.int8, device=dev)
+    s = torch.ones(4, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        i8.w8a8_gemm_g128(q, s, q, torch.ones((4, 3), device=dev))
+    with pytest.raises(i8.I8qlError, match="I8QL_ERR_ARG"):
+        i8.w8a8_gemm_g128(q, s, q, torch.ones((4, 2), device=dev), config=0)  # not a GS config

@@ -217,7 +217,7 @@ def test_w8a8_every_tile_config(ref, dev, config):
     eight tile rows of the workgroup-to-tile map.  k-group configurations take k in whole
     steps per group.  N a multiple of 8 takes the LDS-staged 16-byte-store epilogue, an odd N
     the per-element one."""
-    bm, bn, groups, _ = i8.w8a8_gemm_config_info(config)
+    bm, bn, groups, _, _ = i8.w8a8_gemm_config_info(config)
     if groups == 1:
         shapes = [(2 * bm + 37, 2 * bn + 24, 432), (2 * bm + 37, 2 * bn + 19, 16),
                   (9 * bm + 5, 3 * bn + 8, 144)]
@@ -237,7 +237,7 @@ def test_w8a8_split_plans(ref, dev, config):
     it: ragged tiles in both directions, a partial last k step (owned by the last split),
     splits of unequal step counts, and one workspace reused by every call, whose tile
     counters must be back at zero after each."""
-    bm, bn, _, _ = i8.w8a8_gemm_config_info(config)
+    bm, bn, _, _, _ = i8.w8a8_gemm_config_info(config)
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
     for splits, (m, n, k) in [(2, (2 * bm + 37, 2 * bn + 24, 1040)),
                               (3, (bm + 5, 3 * bn + 8, 2576)),
