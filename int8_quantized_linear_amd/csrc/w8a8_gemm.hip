@@ -254,19 +254,18 @@ __device__ __forceinline__ void gs_read(const int8_t* stage, GroupScales<C>& gs,
 }
 
 // End of a step: facc += (float)acc * scale (the conversion is exact: a step's partial sum
-// is below 128 * 127^2 < 2^24 in magnitude), then acc = 0 for the next step.
+// is below 128 * 127^2 < 2^24 in magnitude).  The next step's first slice starts from a
+// zero C operand instead of a cleared acc.
 template <class C>
-__device__ __forceinline__ void gs_apply(v16i (&acc)[C::TM][C::TN], GroupScales<C>& gs) {
+__device__ __forceinline__ void gs_apply(const v16i (&acc)[C::TM][C::TN], GroupScales<C>& gs) {
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r)
         gs.facc[i][j][r] = __fmaf_rn(static_cast<float>(acc[i][j][r]), gs.cur[j],
                                      gs.facc[i][j][r]);
-        acc[i][j][r] = 0;
-      }
 }
 
 // Issue this wavefront's direct-to-LDS loads of k step `step` into `stage`.  A chunk past
@@ -317,14 +316,17 @@ __device__ __forceinline__ void read_slice(const int8_t* stage, int slice, int a
     b[j] = *reinterpret_cast<const v4i*>(stage + b_off + j * 32 * C::BK + pofs);
 }
 
-template <class C>
+// FRESH: the slice starts new sums (C operand zero, an inline constant), so a group-scale
+// step needs no clearing of the previous step's accumulators.
+template <class C, bool FRESH = false>
 __device__ __forceinline__ void mfma_slice(const v4i (&a)[C::TM], const v4i (&b)[C::TN],
                                            v16i (&acc)[C::TM][C::TN]) {
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], FRESH ? v16i{} : acc[i][j],
+                                                        0, 0, 0);
 }
 
 // Scheduling hint for the instructions just emitted in this basic block: one MFMA of the
@@ -360,8 +362,12 @@ template <class C>
 __device__ __forceinline__ void step_inner(const int8_t* stage, int a_off, int b_off, int fx,
                                            int lane, v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
                                            v16i (&acc)[C::TM][C::TN]) {
+  // slice 0 (with group scales it starts the step's own sums)
+  read_slice<C>(stage, 1, a_off, b_off, fx, lane, fa[1], fb[1]);
+  mfma_slice<C, C::GS>(fa[0], fb[0], acc);
+  reads_under_mfmas<C, 0>();
 #pragma unroll
-  for (int s = 0; s + 1 < C::SLICES; ++s) {
+  for (int s = 1; s + 1 < C::SLICES; ++s) {
     read_slice<C>(stage, s + 1, a_off, b_off, fx, lane, fa[(s + 1) % 2], fb[(s + 1) % 2]);
     mfma_slice<C>(fa[s % 2], fb[s % 2], acc);
     reads_under_mfmas<C, 0>();
@@ -392,7 +398,7 @@ __device__ __forceinline__ void spread_slice(const int8_t* stage, int8_t* fill,
     using P = Spread<C>;
     read_slice<C>(stage, S + 1, a_off, b_off, fx, lane, fa[(S + 1) % 2], fb[(S + 1) % 2]);
     issue_part<C, P::lo(S), P::hi(S)>(fill, src, col, dst, fill_step, k, gs);
-    mfma_slice<C>(fa[S % 2], fb[S % 2], acc);
+    mfma_slice<C, C::GS && S == 0>(fa[S % 2], fb[S % 2], acc);
     constexpr int kLoads = P::hi(S) - P::lo(S) + (C::GS && S == 0 ? 1 : 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                       // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, C::TM + C::TN, 2);           // DS reads
