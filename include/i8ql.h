@@ -104,6 +104,35 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
                                     int8_t* q_out, float* scale_out, void* stream);
 
 /*
+ * quantize_per_token_int8_multi — quantize_per_token_int8 of up to I8QL_QUANT_MAX_JOBS
+ * independent activation matrices of one dtype in a single launch (one kernel instead of one
+ * per matrix; each matrix's codes and scales are bitwise those quantize_per_token_int8
+ * writes).  For callers that hold several activation tensors at once; the per-token scale
+ * is computed at run time for each of them ([W8A8] "Design and Supported Execution Scheme";
+ * [Day6] "Reading-share post" fact 2: the extra work of every forward pass).
+ *
+ * jobs   host, `count` descriptors: x (device, [rows, k] of x_dtype), rows >= 0, k >= 1,
+ *        q_out (device, [rows, k] int8), scale_out (device, [rows] float32).  The matrices
+ *        must not overlap one another's outputs.
+ * 1 <= count <= I8QL_QUANT_MAX_JOBS; x_dtype in {I8QL_F32, I8QL_BF16, I8QL_F16}.
+ * Every x is 16-byte aligned with k * element size a multiple of 16, q_out 8-byte aligned
+ * (the vector layout; quantize_per_token_int8 takes any other layout).
+ * Errors: count or NULL jobs -> I8QL_ERR_ARG; dtype -> I8QL_ERR_DTYPE; a job's rows < 0, k < 1
+ * or sizes out of range -> I8QL_ERR_SHAPE; a NULL pointer of a non-empty job -> I8QL_ERR_NULL;
+ * alignment -> I8QL_ERR_ALIGN.  Nothing is launched unless every job is valid.
+ */
+#define I8QL_QUANT_MAX_JOBS 8
+typedef struct {
+  const void* x;
+  int64_t rows;
+  int64_t k;
+  int8_t* q_out;
+  float* scale_out;
+} i8ql_quant_job;
+i8ql_status quantize_per_token_int8_multi(const i8ql_quant_job* jobs, int count,
+                                          i8ql_dtype x_dtype, void* stream);
+
+/*
  * w8a8_gemm — int8 x int8 GEMM with int32 accumulation and a fused scale epilogue.
  *
  * Defines: [W8A8] "Design and Supported Execution Scheme" (per-channel int8 weights,

@@ -8,7 +8,8 @@ from ._binding import (EXPORTS, GROUP_SIZE, ROUTE_MAX_EXPERTS, ROUTE_MAX_K,  # n
                        grouped_w8a16_gemm,
                        grouped_w8a16_silu_gemm, load_library, moe_combine, moe_route_topk,
                        quantize_per_channel_int8, quantize_per_group_int8,
-                       quantize_per_token_int8, w8a8_gemm, w8a8_gemm_choose_config,
+                       quantize_per_token_int8, quantize_per_token_int8_multi, w8a8_gemm,
+                       w8a8_gemm_choose_config,
                        w8a8_gemm_choose_plan, w8a8_gemm_config_info, w8a8_gemm_g128,
                        w8a8_gemm_noalloc,
                        w8a8_gemm_with_config,

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libi8ql.so")
 I8QL_F32, I8QL_BF16, I8QL_F16, I8QL_I8, I8QL_I32 = 0, 1, 2, 3, 4
 _DTYPE = {torch.float32: I8QL_F32, torch.bfloat16: I8QL_BF16, torch.float16: I8QL_F16,
           torch.int8: I8QL_I8, torch.int32: I8QL_I32}
-EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8", "w8a8_gemm", "w8a16_gemm",
+EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8",
+           "quantize_per_token_int8_multi", "w8a8_gemm", "w8a16_gemm",
            "grouped_w8a16_gemm", "w8a8_gemm_config_info", "w8a8_gemm_choose_config",
            "w8a8_gemm_with_config", "w8a8_gemm_choose_plan", "w8a8_gemm_workspace_size",
            "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "w8a8_gemm_g128",
@@ -32,6 +33,13 @@ W8A8_NUM_CONFIGS = 12  # I8QL_W8A8_NUM_CONFIGS
 W8A8_MAX_SPLITS = 8  # I8QL_W8A8_MAX_SPLITS
 W8A8_SPLIT_MAX_TILES = 4096  # I8QL_W8A8_SPLIT_MAX_TILES
 W8A8_SCRATCH_BYTES = 32 << 20  # I8QL_W8A8_SCRATCH_BYTES
+QUANT_MAX_JOBS = 8  # I8QL_QUANT_MAX_JOBS
+
+
+class QuantJob(ctypes.Structure):
+    """i8ql_quant_job."""
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("q_out", ctypes.c_void_p), ("scale_out", ctypes.c_void_p)]
 
 
 class I8qlError(RuntimeError):
@@ -58,6 +66,8 @@ def load_library(path: str = LIB_PATH):
         for fn in ("quantize_per_channel_int8", "quantize_per_token_int8"):
             getattr(lib, fn).argtypes = [P, I, I64, I64, P, P, P]
             getattr(lib, fn).restype = I
+        lib.quantize_per_token_int8_multi.argtypes = [P, I, I, P]
+        lib.quantize_per_token_int8_multi.restype = I
         lib.w8a8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
         lib.w8a8_gemm.restype = I
         lib.w8a8_gemm_with_config.argtypes = [I, P, P, P, P, P, P, I, I64, I64, I64, P]
@@ -155,6 +165,32 @@ def quantize_per_channel_int8(w: torch.Tensor, q_out=None, scale_out=None):
 def quantize_per_token_int8(x: torch.Tensor, q_out=None, scale_out=None):
     """Dynamic per-token symmetric int8: ``x`` [M, K] -> (q int8 [M, K], scale fp32 [M])."""
     return _quantize("quantize_per_token_int8", x, q_out, scale_out)
+
+
+def quantize_per_token_int8_multi(xs, outs=None):
+    """``quantize_per_token_int8`` of several activation matrices (one dtype, up to
+    QUANT_MAX_JOBS) in one launch: a list of (q int8 [M, K], scale fp32 [M]), bitwise those
+    of the separate calls.  ``outs``: optional list of (q, scale) to write into."""
+    if not 1 <= len(xs) <= QUANT_MAX_JOBS:
+        raise ValueError(f"1 to {QUANT_MAX_JOBS} matrices per launch")
+    dev, dt = xs[0].device, xs[0].dtype
+    res, jobs = [], (QuantJob * len(xs))()
+    for i, x in enumerate(xs):
+        _check(x, f"xs[{i}]", (dt,), 2, dev)
+        r, k = x.shape
+        q, s = outs[i] if outs is not None else (
+            torch.empty((r, k), dtype=torch.int8, device=dev),
+            torch.empty((r,), dtype=torch.float32, device=dev))
+        _check(q, "q_out", (torch.int8,), 2, dev)
+        _check(s, "scale_out", (torch.float32,), 1, dev)
+        if tuple(q.shape) != (r, k) or tuple(s.shape) != (r,):
+            raise ValueError("output shapes do not match the input")
+        jobs[i] = QuantJob(x.data_ptr(), r, k, q.data_ptr(), s.data_ptr())
+        res.append((q, s))
+    with torch.cuda.device(dev):
+        _call("quantize_per_token_int8_multi", ctypes.cast(jobs, ctypes.c_void_p), len(xs),
+              _DTYPE[dt], _stream(dev))
+    return res
 
 
 def _out(out, shape, dtype, dev):

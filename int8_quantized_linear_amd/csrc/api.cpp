@@ -75,6 +75,28 @@ i8ql_status quantize_per_token_int8(const void* x, i8ql_dtype x_dtype, int64_t m
   return quantize_rows(x, x_dtype, m, k, q_out, scale_out, stream);
 }
 
+i8ql_status quantize_per_token_int8_multi(const i8ql_quant_job* jobs, int count,
+                                          i8ql_dtype x_dtype, void* stream) {
+  if (!jobs || count < 1 || count > I8QL_QUANT_MAX_JOBS) return I8QL_ERR_ARG;
+  if (x_dtype != I8QL_F32 && x_dtype != I8QL_BF16 && x_dtype != I8QL_F16) return I8QL_ERR_DTYPE;
+  const int eb = elem_bytes(x_dtype);
+  for (int i = 0; i < count; ++i) {
+    const i8ql_quant_job& j = jobs[i];
+    if (j.rows < 0 || j.k < 1 || !mul_ok(j.rows, j.k) || j.rows > kMaxGridX)
+      return I8QL_ERR_SHAPE;
+  }
+  for (int i = 0; i < count; ++i) {
+    const i8ql_quant_job& j = jobs[i];
+    if (j.rows == 0) continue;
+    if (!j.x || !j.q_out || !j.scale_out) return I8QL_ERR_NULL;
+    if (!aligned(j.x, 16) || (j.k * eb) % 16 != 0 || !aligned(j.q_out, 8) ||
+        !aligned(j.scale_out, 4))
+      return I8QL_ERR_ALIGN;
+  }
+  return hip_status(i8ql::launch_quantize_rows_multi(jobs, count, x_dtype,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {

@@ -40,6 +40,10 @@ hipError_t allow_dynamic_lds(int bytes) {
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream);
 
+// Several matrices (validated for the vector path) in one launch.
+hipError_t launch_quantize_rows_multi(const i8ql_quant_job* jobs, int count, i8ql_dtype dtype,
+                                      hipStream_t stream);
+
 // W8A8: plan (config, splits) = one of the I8QL_W8A8_NUM_CONFIGS tile configurations with
 // k split across `splits` workgroups per tile (workspace ws of ws_bytes, zero counters), or
 // config -1 for the plan the cost model chooses for this shape on the current device among

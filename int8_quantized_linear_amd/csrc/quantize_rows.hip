@@ -142,16 +142,17 @@ __device__ __forceinline__ float chunk_absmax(const float* f, int n, float m) {
 // their maxima meet in LDS); a workgroup holds 4 / W rows.  Every lane loads all of its
 // chunks before it uses one: loads past the row's end re-read its last chunk (harmless to
 // the maximum, never stored), so they are unconditional and all in flight together.
+// The rows of workgroup `block` of one matrix (used by the single-matrix kernel and, per
+// matrix, by the kernel that quantizes several in one launch).
 template <int DT, int W>
-__global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel(
-    const uint8_t* __restrict__ a, int64_t rows, int64_t k, int8_t* __restrict__ q,
-    float* __restrict__ scale) {
+__device__ __forceinline__ void vec_rows(const uint8_t* __restrict__ a, int64_t rows, int64_t k,
+                                         int8_t* __restrict__ q, float* __restrict__ scale,
+                                         int64_t block, float* wmax) {
   constexpr int E = Fmt<DT>::kPerChunk;
   constexpr int T = kWave * W;  // threads per row
-  __shared__ float wmax[kRowsPerBlock];
   const int t = threadIdx.x % T;
   const int slot = threadIdx.x / T;  // row within the workgroup
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kRowsPerBlock / W) + slot;
+  const int64_t row = block * (kRowsPerBlock / W) + slot;
   const bool live = row < rows;  // whole rows only; a dead row still joins the barrier
   const int64_t rr = live ? row : rows - 1;
   const int64_t chunks = k / E;
@@ -237,6 +238,40 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel
   if (t == 0) scale[row] = s;
 }
 
+template <int DT, int W>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_vec_kernel(
+    const uint8_t* __restrict__ a, int64_t rows, int64_t k, int8_t* __restrict__ q,
+    float* __restrict__ scale) {
+  __shared__ float wmax[kRowsPerBlock];
+  vec_rows<DT, W>(a, rows, k, q, scale, blockIdx.x, wmax);
+}
+
+// Several matrices in one launch: matrix j owns workgroups [first[j], first[j + 1]) and is
+// quantized exactly as by itself (the same rows per workgroup and wavefronts per row).
+struct MultiJobs {
+  const uint8_t* a[I8QL_QUANT_MAX_JOBS];
+  int8_t* q[I8QL_QUANT_MAX_JOBS];
+  float* scale[I8QL_QUANT_MAX_JOBS];
+  int64_t rows[I8QL_QUANT_MAX_JOBS];
+  int64_t k[I8QL_QUANT_MAX_JOBS];
+  int64_t first[I8QL_QUANT_MAX_JOBS + 1];
+  int w4[I8QL_QUANT_MAX_JOBS];  // 1: four wavefronts per row
+  int count;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_multi_kernel(MultiJobs jobs) {
+  __shared__ float wmax[kRowsPerBlock];
+  const int64_t b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < jobs.count && b >= jobs.first[j + 1]) ++j;
+  const int64_t block = b - jobs.first[j];
+  if (jobs.w4[j])
+    vec_rows<DT, 4>(jobs.a[j], jobs.rows[j], jobs.k[j], jobs.q[j], jobs.scale[j], block, wmax);
+  else
+    vec_rows<DT, 1>(jobs.a[j], jobs.rows[j], jobs.k[j], jobs.q[j], jobs.scale[j], block, wmax);
+}
+
 // Scalar path: any k and any element-aligned base.
 template <int DT>
 __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_scalar_kernel(
@@ -260,6 +295,14 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void quantize_rows_scalar_ker
   if (lane == 0) scale[row] = s;
 }
 
+// four wavefronts per row when one per row would leave the CUs short of wavefronts, or
+// give each lane more than 12 chunks
+template <int DT>
+bool four_waves_per_row(int64_t rows, int64_t k) {
+  const int64_t chunks = k / Fmt<DT>::kPerChunk;
+  return (rows < kSplitRowsBelow || chunks > 12 * kWave) && rows <= INT32_MAX;
+}
+
 template <int DT>
 hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* scale,
                      hipStream_t stream) {
@@ -268,10 +311,7 @@ hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* s
   const bool vec = (k * Fmt<DT>::kBytes) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(a) % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(q) % 8) == 0;
-  // four wavefronts per row when one per row would leave the CUs short of wavefronts, or
-  // give each lane more than 12 chunks
-  const int64_t chunks = k / Fmt<DT>::kPerChunk;
-  if (vec && (rows < kSplitRowsBelow || chunks > 12 * kWave) && rows <= INT32_MAX) {
+  if (vec && four_waves_per_row<DT>(rows, k)) {
     const dim3 grid4(static_cast<unsigned>(rows));
     hipLaunchKernelGGL((quantize_rows_vec_kernel<DT, 4>), grid4, block, 0, stream,
                        static_cast<const uint8_t*>(a), rows, k, q, scale);
@@ -364,6 +404,43 @@ hipError_t launch_quantize_groups128(const void* a, i8ql_dtype dtype, int64_t n,
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_multi_dt(const i8ql_quant_job* jobs, int count, hipStream_t stream) {
+  MultiJobs mj = {};
+  int64_t blocks = 0;
+  int live = 0;
+  for (int i = 0; i < count; ++i) {
+    if (jobs[i].rows == 0) continue;  // nothing to quantize
+    const bool w4 = four_waves_per_row<DT>(jobs[i].rows, jobs[i].k);
+    mj.a[live] = static_cast<const uint8_t*>(jobs[i].x);
+    mj.q[live] = jobs[i].q_out;
+    mj.scale[live] = jobs[i].scale_out;
+    mj.rows[live] = jobs[i].rows;
+    mj.k[live] = jobs[i].k;
+    mj.w4[live] = w4 ? 1 : 0;
+    mj.first[live] = blocks;
+    blocks += w4 ? jobs[i].rows : (jobs[i].rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    ++live;
+  }
+  if (live == 0) return hipSuccess;
+  mj.first[live] = blocks;
+  mj.count = live;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_rows_multi_kernel<DT>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(kWave * kRowsPerBlock), 0, stream, mj);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_multi(const i8ql_quant_job* jobs, int count, i8ql_dtype dtype,
+                                      hipStream_t stream) {
+  switch (dtype) {
+    case I8QL_F32: return launch_multi_dt<I8QL_F32>(jobs, count, stream);
+    case I8QL_BF16: return launch_multi_dt<I8QL_BF16>(jobs, count, stream);
+    case I8QL_F16: return launch_multi_dt<I8QL_F16>(jobs, count, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,

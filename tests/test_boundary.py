@@ -70,6 +70,29 @@ def test_quantizer_validation(lib, fn):
     assert f(A16, F32, 4, 8, A16, A2, NUL) == ALIGN
 
 
+def test_quantizer_multi_validation(lib):
+    from int8_quantized_linear_amd._binding import QuantJob
+    f = lib.quantize_per_token_int8_multi
+
+    def call(jobs, count=None, dt=BF16):
+        arr = (QuantJob * max(1, len(jobs)))(*jobs)
+        return f(ctypes.cast(arr, ctypes.c_void_p), len(jobs) if count is None else count, dt,
+                 NUL)
+
+    ok = QuantJob(0x10000, 4, 64, 0x20000, 0x30000)
+    assert f(NUL, 1, BF16, NUL) == ARG
+    assert call([ok], count=0) == ARG
+    assert call([ok] * 9) == ARG
+    assert call([ok], dt=I8) == DTYPE
+    assert call([ok, QuantJob(0x10000, -1, 64, 0x20000, 0x30000)]) == SHAPE
+    assert call([ok, QuantJob(0x10000, 4, 0, 0x20000, 0x30000)]) == SHAPE
+    assert call([QuantJob(0, 0, 64, 0, 0)]) == OK                 # empty: nothing to do
+    assert call([ok, QuantJob(0, 4, 64, 0x20000, 0x30000)]) == NULL
+    assert call([ok, QuantJob(0x10008, 4, 64, 0x20000, 0x30000)]) == ALIGN   # x 8-aligned
+    assert call([ok, QuantJob(0x10000, 4, 60, 0x20000, 0x30000)]) == ALIGN   # 120-byte rows
+    assert call([ok, QuantJob(0x10000, 4, 64, 0x20004, 0x30000)]) == ALIGN   # q 4-aligned
+
+
 def test_w8a8_validation(lib):
     f = lib.w8a8_gemm
     args = lambda **kw: dict(dict(xq=A16, sx=A16, wq=A16, sw=A16, b=NUL, y=A16, yt=BF16,
@@ -368,9 +391,13 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
     """With no device, a call that passes validation fails at its first HIP call with
     I8QL_ERR_HIP (and a recorded hipError), instead of crashing."""
     HIP = 7
+    from int8_quantized_linear_amd._binding import QuantJob as QJ
     calls = [
         lambda: lib.quantize_per_channel_int8(A16, BF16, 4, 64, A16, A16, NUL),
         lambda: lib.quantize_per_token_int8(A16, F32, 4, 64, A16, A16, NUL),
+        lambda: lib.quantize_per_token_int8_multi(
+            ctypes.cast((QJ * 1)(QJ(0x10000, 4, 64, 0x20000, 0x30000)), ctypes.c_void_p), 1,
+            BF16, NUL),
         lambda: lib.w8a8_gemm(A16, A16, A16, A16, NUL, A16, BF16, 4, 8, 64, NUL),
         lambda: lib.w8a8_gemm_with_config(0, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 64, NUL),
         lambda: lib.w8a8_gemm_with_plan(6, 2, A16, A16, A16, A16, NUL, A16, F32, 4, 8, 256,

@@ -110,6 +110,33 @@ def test_quantize_near_ties(ref, dev, dtype, rows, k):
         quant_gpu_vs_ref(ref, dev, t, view, dtype, per_token)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_multi_matches_the_oracle_and_single_launches(ref, dev, dtype):
+    """Several matrices in one launch: one and four wavefronts per row, rows up to 24 KiB
+    and beyond (the streamed path), an empty matrix; codes and scales bitwise the oracle's
+    and those of quantize_per_token_int8 one matrix at a time."""
+    g = wl.rng(60)
+    shapes = [(128, 2560), (0, 512), (2048, 9728), (1100, 4096), (3, 16384), (700, 13000),
+              (2, 53248)]
+    ts, views = [], []
+    for (r, k) in shapes:
+        a = wl.activations(g, r, k, outlier_frac=0.01)
+        if r > 2:
+            a[1] = 0.0                                     # an all-zero token
+        t, v = host(dtype, a)
+        ts.append(t.to(dev))
+        views.append(v)
+    got = i8.quantize_per_token_int8_multi(ts)
+    for t, v, (q, s) in zip(ts, views, got):
+        qr, sr = ref.quantize_rows(v, dtype) if t.shape[0] else (np.zeros(t.shape, np.int8),
+                                                                np.zeros(0, np.float32))
+        np.testing.assert_array_equal(q.cpu().numpy(), qr)
+        np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+        if t.shape[0]:
+            q1, s1 = i8.quantize_per_token_int8(t)
+            assert torch.equal(q1, q) and torch.equal(s1, s)
+
+
 def test_quantize_unaligned_base_uses_the_general_path(ref, dev):
     a = wl.weight(wl.rng(5), 33, 520)
     t, view = host("bf16", a)
