@@ -172,9 +172,10 @@ def per_call(torch, fn, reps, warmup=1):
 
 
 def mean_call(torch, fn, reps):
-    """Average seconds per call of fn(i): a graph of `reps` calls, replayed once untimed, then
-    the mean of three timed replays (an average over launches, as a kernel trace reports)."""
-    return graph_time(torch, fn, reps, 1, passes=3, reduce=lambda t: sum(t) / len(t)) / reps
+    """Average seconds per call of fn(i): a graph of `reps` calls, replayed three times
+    untimed (the first graph timed after a long run of other work can run slow), then the
+    mean of three timed replays (an average over launches, as a kernel trace reports)."""
+    return graph_time(torch, fn, reps, 3, passes=3, reduce=lambda t: sum(t) / len(t)) / reps
 
 
 def time_loop(torch, body, steps, warmup, clock=None):
@@ -256,10 +257,19 @@ class PrefillWorkload:
         q, s = self.qx[m][key]
         self.i8.quantize_per_token_int8(self.xs[m][key], q, s)
 
+    # below this many tokens the four inputs of a token count are quantized in one launch
+    # (the launches are latency-bound); from it on one launch each (bandwidth-bound: at
+    # 16384 tokens the single launch took 229 us against 220 us for four)
+    MULTI_BELOW = 4096
+
     def quantize_all(self, m):
-        """The four inputs of one token count quantized in one launch."""
-        self.i8.quantize_per_token_int8_multi([self.xs[m][key] for key in self.INPUTS],
-                                              [self.qx[m][key] for key in self.INPUTS])
+        """The four inputs of one token count, quantized per token."""
+        if m < self.MULTI_BELOW:
+            self.i8.quantize_per_token_int8_multi([self.xs[m][key] for key in self.INPUTS],
+                                                  [self.qx[m][key] for key in self.INPUTS])
+        else:
+            for key in self.INPUTS:
+                self.quantize(m, key)
 
     def gemm(self, m, nm, copy):
         q, s = self.qx[m][self.SRC[nm]]
@@ -316,8 +326,8 @@ def measure_prefill(torch, wl, wk, args, label, clock=True):
     out["quantize_per_token"] = {
         "launches": multi, "us_per_step": t_quant * 1e6, "GBs": qbytes / t_quant / 1e9,
         "frac_hbm": qbytes / t_quant / 1e9 / PEAK_HBM_GBS,
-        "what": "the step's four inputs of each token count quantized in one launch "
-                "(quantize_per_token_int8_multi)",
+        "what": "the step's four inputs of each token count: one quantize_per_token_int8_multi "
+                "launch below 4096 tokens, else one quantize_per_token_int8 each",
         "separate": {"what": "one quantize_per_token_int8 launch per input", "launches": quant,
                      "us_per_step": t_sep * 1e6, "GBs": qbytes / t_sep / 1e9}}
     out["w8a8_gemm_us_per_step"] = t_gemm * 1e6
