@@ -135,6 +135,77 @@ __device__ __forceinline__ void mma_batch_lds(const v4u (&w)[U][2], const char* 
   }
 }
 
+// A buffer resource over the `bytes` bytes at `base` (wavefront-uniform; bytes < 2^31):
+// loads through it at offsets at or past `bytes` return zeros instead of reading memory.
+// Dword 3 is the raw (untyped) format of the CDNA buffer descriptor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const int8_t* base,
+                                                              int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0,
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// load_weight_batch through a buffer resource over one 16-row weight tile: voff is this
+// lane's byte offset in the tile (row (lane % 16) * k plus its 32-channel slot), s the first
+// step.  Every load of the batch shares the one offset register (steps and halves differ by
+// immediate offsets), no bounds select is needed: rows past the tile and bytes past its end
+// read as zeros, and chunks past k or steps past the caller's range read other codes of the
+// tile, which the caller never multiplies by a nonzero activation (mma_batch_staged skips
+// such steps and feeds zeros past k).
+template <int U>
+__device__ __forceinline__ void load_weight_batch_rsrc(__amdgpu_buffer_rsrc_t rs, int voff,
+                                                       int s, v4u (&w)[U][2]) {
+  const int soff = s * kStepK;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    w[u][0] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + u * kStepK, soff, 0));
+    w[u][1] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + u * kStepK + 16, soff, 0));
+  }
+}
+
+// mma_batch_lds for one activation tile, with the bounds handled by wavefront-uniform
+// branches instead of per-read selects: a step that lies wholly below k reads its four
+// fragments at the staged row's base plus immediate offsets, only a step that straddles k (k
+// not a multiple of 128) reads xzero for the chunks past k, and a step at or past s_end is
+// multiplied by zeros.  Every step of the batch is converted and multiplied, so every load of
+// the batch has an unconditional use: the compiler keeps the loads where load_weight_batch_rsrc
+// issued them, which the callers' vmcnt arithmetic relies on.  xrow: this lane's staged row
+// (input channel c at byte 2c), read only when `live`.
+template <int U>
+__device__ __forceinline__ void mma_batch_staged(const v4u (&w)[U][2], const char* xrow,
+                                                 bool live, const char* xzero, int64_t k, int s,
+                                                 int s_end, v4u (&xb)[4], v4f& acc) {
+  const int sub = 32 * ((threadIdx.x % 64) / 16);
+  const char* xp = xrow + 2 * (static_cast<int64_t>(s) * kStepK + sub);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    v8bf a[4];
+    i8x16_to_bf16(w[u][0], a[0], a[1]);
+    i8x16_to_bf16(w[u][1], a[2], a[3]);
+    if (s + u >= s_end) {  // uniform
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xb[c] = v4u{0u, 0u, 0u, 0u};
+    } else if (live) {
+      if (static_cast<int64_t>(s + u + 1) * kStepK <= k) {  // uniform
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          xb[c] = *reinterpret_cast<const v4u*>(xp + u * 2 * kStepK + 16 * c);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t kc = static_cast<int64_t>(s + u) * kStepK + sub + 8 * c;
+          xb[c] = *reinterpret_cast<const v4u*>(kc < k ? xp + u * 2 * kStepK + 16 * c : xzero);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], __builtin_bit_cast(v8bf, xb[c]), acc,
+                                                    0, 0, 0);
+  }
+}
+
 // Accumulate the wavefront's partial product over steps [s_begin, s_end), activations read
 // from global memory (L2-resident: every workgroup reads the same rows).
 //   wrow      : this lane's weight row (row n0 + lane % 16, clamped into the matrix)

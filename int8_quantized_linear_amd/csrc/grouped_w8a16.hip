@@ -183,13 +183,16 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
 
   // Weight rows per expert: TILES * n; this wavefront's tile (0: the channels themselves or
   // the gate rows, 1: the up rows) starts at row tile * n of its expert.  Per 16-channel
-  // tile at n0: the weight row of this lane and (wavefront 0) the 4 output-channel scales
-  // of its lane group.
+  // tile at n0: a buffer resource over the tile's weight rows (rows past n read as zeros;
+  // their channels are never stored) and (wavefront 0) the 4 output-channel scales of its
+  // lane group.  voff: this lane's row and 32-channel slot within any tile.
   const int tile = wave / KS;
   float sc[TILES][4] = {};
-  auto weight_row = [&](int64_t n0) {
-    return wq + (invalid_row ? 0 : ((e * TILES + tile) * n + min(n0 + lane % 16, n - 1)) * k);
+  auto weight_tile = [&](int64_t n0) {
+    const int64_t rows = invalid_row ? 0 : min(static_cast<int64_t>(16), n - n0);
+    return weight_rsrc(wq + (invalid_row ? 0 : ((e * TILES + tile) * n + n0) * k), rows * k);
   };
+  const int voff = (lane % 16) * static_cast<int>(k) + 32 * (lane / 16);
   auto load_scales = [&](int64_t n0) {
     if (wave == 0) {
       const int64_t nc = n0 + 4 * (lane / 16);
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   int64_t sc_n0 = nb;  // the tile whose scales sc holds
   if (!invalid_row) load_scales(nb);
   if (!invalid_row && BITMAP) {
-    load_weight_batch<kUnroll>(weight_row(nb), k, sb, se, w);
+    load_weight_batch_rsrc<kUnroll>(weight_tile(nb), voff, sb, w);
     w_loaded = true;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -285,30 +288,29 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
         stage_rows<WAVES>(x, list + g, div, rows, k, xs);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        const char* xrow[1];
-        bool live[1];
-        v4u xb[1][4];
-        live[0] = lane % 16 < rows;
-        xrow[0] = xs + (live[0] ? lane % 16 : 0) * pitch;
+        const bool live = lane % 16 < rows;
+        const char* xrow = xs + (live ? lane % 16 : 0) * pitch;
+        v4u xb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xb[0][c] = v4u{0u, 0u, 0u, 0u};
+        for (int c = 0; c < 4; ++c) xb[c] = v4u{0u, 0u, 0u, 0u};
         const int nt = (BITMAP || SILU) ? tseq : 1;  // one tile (a constant) in the plain direct mode
         for (int ti = 0; ti < nt; ++ti) {
           const int64_t n0 = nb + 16 * ti;
           if (n0 >= n) break;  // uniform
-          // With SiLU·mul or several tiles, the step range and the row and staging pointers
-          // pass through opaque copies, so that the compiler derives the batch's addresses and
-          // bounds here, per tile, instead of holding them all in registers across the loops
-          // (SiLU·mul: 223 -> 163 VGPRs, 3 instead of 2 waves per SIMD, the MoE block 10 %
-          // faster at T = 16).  The plain kernel with one tile is faster without them.
-          const int8_t* wrow = weight_row(n0);
-          int s0 = sb, s1 = se;
-          const char* xr[1] = {xrow[0]};
+          // With SiLU·mul or several tiles, the step range, the weight offset and the staged
+          // row pass through opaque copies, so that the compiler derives the batch's offsets
+          // here, per tile, instead of holding them all in registers across the loops.
+          const __amdgpu_buffer_rsrc_t wt = weight_tile(n0);
+          // (the staged row as an LDS byte offset: a pointer through the copy would lose its
+          // address space and turn the fragment reads into flat loads)
+          int s0 = sb, s1 = se, vo = voff;
+          int xo = static_cast<int>(xrow - smem);
           if constexpr (SILU || BITMAP) {
             asm volatile("" : "+s"(s0), "+s"(s1));
-            asm volatile("" : "+v"(wrow));
-            asm volatile("" : "+v"(xr[0]));
+            asm volatile("" : "+v"(vo));
+            asm volatile("" : "+v"(xo));
           }
+          const char* xr = smem + xo;
           if (w_loaded) {
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
             w_loaded = false;
@@ -317,20 +319,20 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
               load_scales(n0);
               sc_n0 = n0;
             }
-            load_weight_batch<kUnroll>(wrow, k, s0, s1, w);
+            load_weight_batch_rsrc<kUnroll>(wt, vo, s0, w);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             if (ti == 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
           }
           if (ti == 0) bare_barrier();
-          v4f acc[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
-          mma_batch_lds<1, kUnroll>(w, xr, live, xzero, k, s0, s1, xb, acc);
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+          mma_batch_staged<kUnroll>(w, xr, live, xzero, k, s0, s1, xb, acc);
           for (int s = s0 + kUnroll; s < s1; s += kUnroll) {
-            load_weight_batch<kUnroll>(wrow, k, s, s1, w);
+            load_weight_batch_rsrc<kUnroll>(wt, vo, s, w);
             __builtin_amdgcn_sched_barrier(0);
-            mma_batch_lds<1, kUnroll>(w, xr, live, xzero, k, s, s1, xb, acc);
+            mma_batch_staged<kUnroll>(w, xr, live, xzero, k, s, s1, xb, acc);
           }
-          red[wave * 64 + lane] = acc[0];
+          red[wave * 64 + lane] = acc;
           __syncthreads();
           if (wave == 0 && lane % 16 < rows) {
             v4f sum[TILES];
