@@ -114,6 +114,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
     int tseq) {
   constexpr int TILES = SILU ? 2 : 1;
   constexpr int WAVES = KS * TILES;
+  constexpr int kEpiWave = WAVES - 1;  // reduces the partial tiles and stores the outputs
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int list[kList];
   __shared__ int s_count;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   const bool invalid_row = blockIdx.y == 0;
   // tseq consecutive 16-channel tiles, one after the other: the expert choice, the row scan
   // and the staged activation rows serve all of them
-  const int64_t nb = static_cast<int64_t>(blockIdx.x) * ((BITMAP || SILU) ? tseq : 1) * 16;
+  const int64_t nb = static_cast<int64_t>(blockIdx.x) * tseq * 16;
   if (threadIdx.x == 0) *reinterpret_cast<v4u*>(xzero) = v4u{0u, 0u, 0u, 0u};
 
   // Wavefront 0's first batch of ids, loaded once: the bitmap pass and the first window of
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
       load_id_batch(ids, total, 0, lane, idv);
       idv_loaded = true;
     }
-    __syncthreads();  // the bitmap is clear
+    lds_barrier();  // the bitmap is clear
     // 64-id groups: wavefront w marks groups w, w + WAVES, ..., kScanBatch loads in flight
     const int64_t groups = (total + 63) / 64;
     for (int64_t g0 = wave; g0 < groups; g0 += static_cast<int64_t>(WAVES) * kScanBatch) {
@@ -169,14 +170,14 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
           atomicOr(present + (id >> 5), 1u << (id & 31));
       }
     }
-    __syncthreads();  // the bitmap is complete
+    lds_barrier();  // the bitmap is complete
     if (wave == 0) {
       // slots in decreasing id order, for the same reason as above
       const int pick =
           nth_present_from_top(present, words, static_cast<int>(blockIdx.y) - 1, lane);
       if (lane == 0) s_expert = pick;
     }
-    __syncthreads();
+    lds_barrier();
     e = s_expert;
     if (e < 0) return;  // fewer distinct experts than slots (uniform over the workgroup)
   }
@@ -184,8 +185,8 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   // Weight rows per expert: TILES * n; this wavefront's tile (0: the channels themselves or
   // the gate rows, 1: the up rows) starts at row tile * n of its expert.  Per 16-channel
   // tile at n0: a buffer resource over the tile's weight rows (rows past n read as zeros;
-  // their channels are never stored) and (wavefront 0) the 4 output-channel scales of its
-  // lane group.  voff: this lane's row and 32-channel slot within any tile.
+  // their channels are never stored) and (the epilogue's wavefront) the 4 output-channel
+  // scales of its lane group.  voff: this lane's row and 32-channel slot within any tile.
   const int tile = wave / KS;
   float sc[TILES][4] = {};
   auto weight_tile = [&](int64_t n0) {
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   };
   const int voff = (lane % 16) * static_cast<int>(k) + 32 * (lane / 16);
   auto load_scales = [&](int64_t n0) {
-    if (wave == 0) {
+    if (wave == kEpiWave) {
       const int64_t nc = n0 + 4 * (lane / 16);
 #pragma unroll
       for (int ti = 0; ti < TILES; ++ti)
@@ -208,8 +209,9 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   v4u w[kUnroll][2];
   bool w_loaded = false;
   // The first tile's scales are requested before the scan so that their latency overlaps
-  // it; a picked expert has rows for certain, so its first batch of weight loads goes out
-  // before the scan too.
+  // it; they go to the last wavefront, which runs the epilogue, so that the scan on
+  // wavefront 0 never waits for them (with one wavefront it does).  A picked expert has rows
+  // for certain, so its first batch of weight loads goes out before the scan too.
   int64_t sc_n0 = nb;  // the tile whose scales sc holds
   if (!invalid_row) load_scales(nb);
   if (!invalid_row && BITMAP) {
@@ -258,12 +260,12 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
         s_next = p;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int count = s_count;
     p_next = s_next;
 
     if (invalid_row) {
-      const int nt = (BITMAP || SILU) ? tseq : 1;
+      const int nt = tseq;
       for (int i = threadIdx.x; i < count * 16 * nt; i += 64 * WAVES) {
         const int64_t row = list[i / (16 * nt)];
         const int64_t c = nb + i % (16 * nt);
@@ -293,23 +295,21 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
         v4u xb[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) xb[c] = v4u{0u, 0u, 0u, 0u};
-        const int nt = (BITMAP || SILU) ? tseq : 1;  // one tile (a constant) in the plain direct mode
+        const int nt = tseq;
         for (int ti = 0; ti < nt; ++ti) {
           const int64_t n0 = nb + 16 * ti;
           if (n0 >= n) break;  // uniform
-          // With SiLU·mul or several tiles, the step range, the weight offset and the staged
-          // row pass through opaque copies, so that the compiler derives the batch's offsets
-          // here, per tile, instead of holding them all in registers across the loops.
+          // The step range, the weight offset and the staged row pass through opaque copies,
+          // so that the compiler derives the batch's offsets here, per tile, instead of
+          // holding them all in registers across the loops (the staged row as an LDS byte
+          // offset: a pointer through the copy would lose its address space and turn the
+          // fragment reads into flat loads).
           const __amdgpu_buffer_rsrc_t wt = weight_tile(n0);
-          // (the staged row as an LDS byte offset: a pointer through the copy would lose its
-          // address space and turn the fragment reads into flat loads)
           int s0 = sb, s1 = se, vo = voff;
           int xo = static_cast<int>(xrow - smem);
-          if constexpr (SILU || BITMAP) {
-            asm volatile("" : "+s"(s0), "+s"(s1));
-            asm volatile("" : "+v"(vo));
-            asm volatile("" : "+v"(xo));
-          }
+          asm volatile("" : "+s"(s0), "+s"(s1));
+          asm volatile("" : "+v"(vo));
+          asm volatile("" : "+v"(xo));
           const char* xr = smem + xo;
           if (w_loaded) {
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -333,8 +333,8 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
             mma_batch_staged<kUnroll>(w, xr, live, xzero, k, s, s1, xb, acc);
           }
           red[wave * 64 + lane] = acc;
-          __syncthreads();
-          if (wave == 0 && lane % 16 < rows) {
+          lds_barrier();
+          if (wave == kEpiWave && lane % 16 < rows) {
             v4f sum[TILES];
 #pragma unroll
             for (int tt = 0; tt < TILES; ++tt) {
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
               }
             }
           }
-          __syncthreads();  // red[] (and, after the last tile, the staged rows) are reused
+          lds_barrier();  // red[] (and, after the last tile, the staged rows) are reused
         }
       }
     }
@@ -388,14 +388,17 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
   // expert, or, with fewer assignments than experts, one per assignment (the most distinct
   // experts there can be).
   const int64_t slots = BITMAP ? t * topk : num_experts;
-  // Tiles per workgroup, walked one after the other.  With fewer assignments than experts
-  // (every expert has at most t rows, one pass) as many as keep about four workgroups per
-  // compute unit over the grid (at most 16), so that each workgroup's expert choice, row scan
-  // and staged rows serve more output channels.  Otherwise one: experts with many rows take
-  // several passes, and walking tiles would multiply those passes in one workgroup (at
-  // T = 64, 4 tiles per workgroup made the MoE gate/up/down layer 2.3x slower).
+  // Tiles per workgroup, walked one after the other, so that each workgroup's expert choice,
+  // row scan and staged rows serve more output channels.  With fewer assignments than
+  // experts (every expert has at most t rows, one pass) as many as keep about four
+  // workgroups per compute unit over the grid (at most 16).  Otherwise an expert with many
+  // rows takes several passes, and walking tiles multiplies those passes in one workgroup:
+  // two tiles while no expert can need more than two passes (an expert that each token picks
+  // at most once gets at most t rows), else one (at T = 64, 2 tiles per workgroup made the
+  // 16B MoE gate projection 9 % slower and 4 tiles 1.7x slower, the shared experts' 8-pass
+  // workgroups becoming the tail; at T = 16, 2 tiles made gate and down 12-15 % faster).
   const int64_t tiles = (n + 15) / 16;
-  int64_t per = BITMAP ? tiles * slots / (4 * kCusPerGpu) : 1;
+  int64_t per = BITMAP ? tiles * slots / (4 * kCusPerGpu) : (t <= 2 * pass_rows ? 2 : 1);
   if (per > kMaxTileSeq) per = kMaxTileSeq;
   const int tseq = per < 1 ? 1 : static_cast<int>(per);
   const dim3 grid(static_cast<unsigned>((tiles + tseq - 1) / tseq),

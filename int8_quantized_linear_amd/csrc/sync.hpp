@@ -20,4 +20,14 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier that publishes LDS writes only: each wavefront waits for its own LDS operations
+// (and scalar loads), not for the global loads and stores it has in flight, which a fence
+// (__syncthreads) would wait for as well.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace i8ql
