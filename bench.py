@@ -434,9 +434,9 @@ def section_prefill_4b(torch, i8, wl, dev, args, result):
     torch.cuda.empty_cache()
 
 
-def traffic_for(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; else None."""
+def traffic_entry(kernel, workload):
+    """The committed rocprofv3 counter summary of a kernel on a workload (profiles/
+    traffic.json), if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -444,7 +444,13 @@ def traffic_for(kernel, workload):
     ent = data.get(kernel, {}).get(workload)
     if not ent or ent.get("source_sha") != source_sha(kernel):
         return None
-    return ent["bytes_per_launch"]
+    return ent
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    ent = traffic_entry(kernel, workload)
+    return None if ent is None else ent["bytes_per_launch"]
 
 
 CPU_SAMPLE_ROWS = 2048  # token rows of the headline step the oracle is timed on
@@ -646,6 +652,12 @@ def section_moe(torch, i8, wl, dev, args, result):
                            "GBs_kernels": nbytes / allk / 1e9,
                            "frac_hbm_kernels": nbytes / allk / 1e9 / PEAK_HBM_GBS,
                            "per_proj": per}
+        ent = traffic_entry("grouped_w8a16_kernel", moe_traffic_workload(t))
+        if ent is not None:  # HBM bytes per launch (FETCH_SIZE + WRITE_SIZE) vs algorithmic
+            out["per_t"][t]["traffic"] = {
+                "hbm_bytes_per_launch": ent["bytes_per_launch"],
+                "algorithmic_bytes_per_launch": ent["algorithmic_bytes_per_launch"],
+                "ratio": ent["bytes_per_launch"] / ent["algorithmic_bytes_per_launch"]}
         log(f"[moe] T={t}: {distinct} experts, {secs/args.steps*1e6:.1f} us/layer, "
             f"{out['per_t'][t]['GBs_kernels']:.0f} GB/s")
     # The whole block: routing from router logits, gate and up as one grouped GEMM over
@@ -777,6 +789,55 @@ def section_counters_decode(torch, i8, wl, dev, args, result):
     result["counters_decode"] = {"calibration_copy_bytes": CALIB_BYTES, "passes": 2}
 
 
+MOE_COUNTER_TOKENS = (16, 64)
+
+
+def moe_traffic_workload(t):
+    return f"16B MoE grouped W8A16 gate/up/down T={t}"
+
+
+def section_counters_moe(torch, i8, wl, dev, args, result):
+    """Like `counters`, for the grouped W8A16 GEMMs of the 16B MoE block: the calibration
+    copy, then for T in MOE_COUNTER_TOKENS two passes of gate, up and down (each launched on
+    its own, weight copies rotating over >= 1 GiB), with each launch's algorithmic bytes."""
+    g = wl.rng(2)
+    e = wl.MOE_ROUTED + wl.MOE_SHARED
+    stacks = {}
+    for proj, (n, k) in wl.MOE_16B.items():
+        w = wl.to_bf16(wl.moe_weights(g, n, k).reshape(e * n, k)).to(dev)
+        q, s = i8.quantize_per_channel_int8(w)
+        del w
+        stacks[proj] = (q.view(e, n, k), s.view(e, n))
+    per_layer = sum(e * n * k for n, k in wl.MOE_16B.values())
+    copies = max(2, -(-ROTATE_BYTES // per_layer))
+    rot = [stacks] + [{p: (q.clone(), s) for p, (q, s) in stacks.items()} for _ in range(copies - 1)]
+    inputs = {}
+    for t in MOE_COUNTER_TOKENS:
+        ids = wl.moe_expert_ids(g, t)
+        topk = ids.shape[1]
+        inputs[t] = (torch.from_numpy(ids).to(dev), len(np.unique(ids)), topk,
+                     wl.to_bf16(wl.activations(g, t, 2048)).to(dev),
+                     wl.to_bf16(wl.activations(g, t * topk, 1408)).to(dev))
+    calibration_copy(torch, dev)
+    launches = []
+    i = 0
+    for t in MOE_COUNTER_TOKENS:
+        ids_d, distinct, topk, x_in, x_mid = inputs[t]
+        for rep in range(2):
+            for p in ("gate", "up", "down"):
+                n, k = wl.MOE_16B[p]
+                q, s_ = rot[i % copies][p]
+                x, pa = (x_mid, True) if p == "down" else (x_in, False)
+                i8.grouped_w8a16_gemm(x, q, s_, ids_d, x_per_assignment=pa)
+                xr = t * topk if p == "down" else t
+                launches.append({"tokens": t, "proj": p,
+                                 "algorithmic_bytes": grouped_bytes(distinct, n, k, xr,
+                                                                    t * topk)})
+            i += 1
+    torch.cuda.synchronize()
+    result["counters_moe"] = {"calibration_copy_bytes": CALIB_BYTES, "launches": launches}
+
+
 def section_weight_quant(torch, i8, wl, dev, args, result):
     g = wl.rng(4)
     ws = {nm: wl.to_bf16(wl.weight(g, n, k)).to(dev) for nm, (n, k) in wl.DENSE_8B.items()}
@@ -801,6 +862,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters": section_counters, "counters_4b": section_counters_4b,
     "counters_decode": section_counters_decode,
     "counters_w8a8_large": section_counters_w8a8_large,
+    "counters_moe": section_counters_moe,
 }
 DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
            "weight_quant")
