@@ -68,6 +68,7 @@ namespace i8ql {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -831,6 +832,329 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
                       lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
 }
 
+// ---- persistent variant (two stages of both operands, one k-group) ---------------------
+// With 128 KiB of stages a compute unit holds one workgroup, so a kernel that ends with its
+// tile idles the matrix cores twice per tile: while the first stage's loads travel (the next
+// workgroup starts from empty stages) and while the epilogue converts and writes the output.
+// At 16384 x 24576 x 4096 with 256 x 256 tiles that is about 12 us of a 63 us round (time
+// against k: 1.59 us per k step plus a fixed 12 us per round of 256 tiles).  Here each
+// workgroup walks tiles v, v + G, ... (G workgroups, a multiple of the 8 XCDs, so a workgroup
+// stays on its XCD's share of the tile order) and keeps the two-stage pipeline running
+// across tiles: during the second-to-last k step the freed stage is refilled with the next
+// tile's step 0, and after the last step's fragment reads (and a barrier) the last stage is
+// refilled with its step 1, so those loads travel while the epilogue runs.  The epilogue
+// therefore cannot use the stages: it goes through a small per-wavefront area after them
+// (16 rows x 32 columns of 32-bit values at a time) with the tile's row scales, column scales
+// and bias copied there by direct-to-LDS loads when the tile starts.  Its output stores are
+// buffer stores: stores of rows past m or columns past n are sent past the buffer's end,
+// where the hardware drops them.  The last tile refills from itself (in-bounds loads of no
+// use) and the kernel drains every load before it ends.  Needs k > BK (two steps at least), output rows of whole
+// 16-byte chunks and a 16-byte aligned output.
+constexpr int kPScrWords = 40;                   // words per scratch row (32 + padding)
+constexpr int kPScrBytes = 16 * kPScrWords * 4;  // 16 rows of output values
+
+template <class C, int YT>
+struct Persist {
+  static constexpr int ES = YT == I8QL_BF16 ? 2 : 4;  // output element bytes
+  static constexpr int PER = 16 / ES;                  // output elements per 16-byte store
+  static constexpr int PIECE_STORES = 16 * 32 / PER / 64;  // per 16 x 32 piece and lane
+  static constexpr int PARAM_BYTES = (C::WTM + 2 * C::WTN) * 4;    // row scales, col scales, bias
+  static constexpr int WAVE_BYTES = kPScrBytes + PARAM_BYTES;
+  static constexpr size_t STAGES_BYTES = 2 * static_cast<size_t>(C::STAGE_BYTES);
+  static constexpr size_t LDS_BYTES = STAGES_BYTES + static_cast<size_t>(C::WAVES) * WAVE_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
+  static_assert(C::WTM % 64 == 0 && C::WTN % 64 == 0, "parameter copies of 64 values");
+};
+
+// Copy this wavefront's row scales, column scales and bias (zeros without bias) for the tile
+// at (r0, c0) into `par` (direct-to-LDS, 64 values per instruction; indices clamped).  Int32
+// output uses none of them (and the scales may then be null): nothing is loaded.
+template <class C, int YT>
+__device__ __forceinline__ void persist_params(float* par, int lane,
+                                               const float* __restrict__ x_scale,
+                                               const float* __restrict__ w_scale,
+                                               const float* __restrict__ bias, int64_t m,
+                                               int64_t n, int64_t r0, int64_t c0) {
+  if constexpr (YT == I8QL_I32) return;
+#pragma unroll
+  for (int h = 0; h < C::WTM / 64; ++h) {
+    const int64_t r = r0 + h * 64 + lane;
+    __builtin_amdgcn_global_load_lds(x_scale + (r < m ? r : m - 1), par + h * 64, 4, 0, 0);
+  }
+#pragma unroll
+  for (int h = 0; h < C::WTN / 64; ++h) {
+    const int64_t c = c0 + h * 64 + lane;
+    const int64_t cc = c < n ? c : n - 1;
+    __builtin_amdgcn_global_load_lds(w_scale + cc, par + C::WTM + h * 64, 4, 0, 0);
+    if (bias) __builtin_amdgcn_global_load_lds(bias + cc, par + C::WTM + C::WTN + h * 64, 4, 0, 0);
+  }
+  if (!bias) {
+#pragma unroll
+    for (int h = 0; h < C::WTN / 64; ++h) par[C::WTM + C::WTN + h * 64 + lane] = 0.0f;
+  }
+}
+
+// The fused epilogue of the persistent kernel: 16 x 32 pieces through `scr`, scales and bias
+// from `par`, output through the buffer resource `yr` over the tile's rows (rows past m lie
+// past its end).  (r0, c0): the wavefront's first row and column relative to the tile's
+// first row and in the whole output.
+template <class C, int YT>
+__device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN],
+                                                 int8_t* lds_all, int area, int lane,
+                                                 __amdgpu_buffer_rsrc_t yr, int64_t n,
+                                                 int r0, int64_t c0, bool has_bias) {
+  using P = Persist<C, YT>;
+  // (the area's offset is opaque, so that the compiler derives the scratch and parameter
+  // addresses here instead of holding them in registers across the tile loop)
+  asm volatile("" : "+s"(area));
+  asm volatile("" : "+v"(lane));
+  int* scr = reinterpret_cast<int*>(lds_all + area);
+  const float* par = reinterpret_cast<const float*>(lds_all + area + kPScrBytes);
+  constexpr int PER = P::PER;
+  constexpr int CPR = 32 / PER;  // 16-byte chunks per row of a piece
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        // registers 8h .. 8h + 7 hold rows 16h .. 16h + 15 of the 32-row block
+        const float sw = par[C::WTM + j * 32 + lane % 32];
+        const float bj = par[C::WTM + C::WTN + j * 32 + lane % 32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 8 * h + q;
+          const int row = 8 * (q / 4) + 4 * (lane / 32) + q % 4;  // within the piece
+          int bits;
+          if constexpr (YT == I8QL_I32) {
+            bits = acc[i][j][r];
+          } else {
+            const float sx = par[i * 32 + 16 * h + row];
+            float v = epilogue_value<YT, false>(acc[i][j][r], sx, sw);
+            if (has_bias) v = __fadd_rn(v, bj);
+            bits = __float_as_int(v);
+          }
+          scr[row * kPScrWords + lane % 32] = bits;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < P::PIECE_STORES; ++u) {
+          const int qq = u * 64 + lane;
+          const int row = qq / CPR, cg = qq % CPR;
+          const int* src = scr + row * kPScrWords + cg * PER;
+          v4i out;
+          if constexpr (P::ES == 4) {
+            out = *reinterpret_cast<const v4i*>(src);
+          } else {
+            const v4i a = *reinterpret_cast<const v4i*>(src);
+            const v4i b = *reinterpret_cast<const v4i*>(src + 4);
+            const int w8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const v2f pair = {__int_as_float(w8[2 * e]), __int_as_float(w8[2 * e + 1])};
+              out[e] = __builtin_bit_cast(int, __builtin_convertvector(pair, v2bf));
+            }
+          }
+          const int64_t col = c0 + j * 32 + cg * PER;
+          const int64_t off = ((r0 + i * 32 + 16 * h + row) * n + col) * P::ES;
+          const int voff = col < n ? static_cast<int>(off) : -16;  // (past the end: dropped)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, out), yr, voff, 0, 0);
+        }
+        // the next piece overwrites the scratch: its reads must be done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+}
+
+// Operand rows of the persistent kernel, read through buffer resources over xq ([m, k]) and
+// wq ([n, k]).  Load j of a wavefront covers stacked rows ROWS_PER_LOAD * (wave + WAVES * j)
+// + lrow (lrow = lane / CHUNKS): A rows for the first BM / (WAVES * ROWS_PER_LOAD) loads,
+// then B rows.  A multiple of 32 rows apart, they share this lane's swizzled chunk offset
+// `colb`, so a lane's offset for load j is its (clamped) row times k plus colb, and step s
+// adds s * BK as the scalar offset: no address arithmetic per step.  Chunks past k read the
+// next row's codes (or zeros past the buffer's end): the A chunks are zeroed in LDS before
+// use, so whatever B holds there adds nothing.
+template <class C>
+__device__ __forceinline__ void persist_offsets(int (&voff)[C::LOADS], int64_t m0, int64_t n0,
+                                                int64_t m, int64_t n, int64_t k, int wave,
+                                                int lrow, int colb) {
+  constexpr int kRowsPerRound = C::WAVES * C::ROWS_PER_LOAD;
+  static_assert(kRowsPerRound % 32 == 0 && C::BM % kRowsPerRound == 0, "load rows");
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int trow = (wave + C::WAVES * j) * C::ROWS_PER_LOAD + lrow;
+    const int64_t row = j < C::BM / kRowsPerRound ? min(m0 + trow, m - 1)
+                                                   : min(n0 + (trow - C::BM), n - 1);
+    voff[j] = static_cast<int>(row * k) + colb;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void persist_issue(int8_t* stage, __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb,
+                                              const int (&voff)[C::LOADS], int wave, int step) {
+  constexpr int kRowsPerRound = C::WAVES * C::ROWS_PER_LOAD;
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    int8_t* d = stage + (wave + C::WAVES * j) * C::ROWS_PER_LOAD * C::BK;
+    __attribute__((address_space(3))) void* dl = (__attribute__((address_space(3))) void*)d;
+    const __amdgpu_buffer_rsrc_t r = j < C::BM / kRowsPerRound ? ra : rb;
+    const int vo = voff[j];
+    // (builtin arguments are named values: clang rejects a value-dependent expression
+    // written directly into this builtin's argument list)
+    const int so = step * C::BK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dl, 16, vo, so, 0, 0);
+  }
+}
+
+// One steady k step of the persistent kernel: compute the step in `cur`, wait for the step
+// in `nxt` and barrier (optionally zero its tail), read its first slice, refill `cur` with
+// step `fstep` of the rows at offsets `fvoff`, and finish this step's last slice.
+template <class C, bool ZERO>
+__device__ __forceinline__ void persist_step(int8_t* cur, int8_t* nxt, __amdgpu_buffer_rsrc_t ra,
+                                             __amdgpu_buffer_rsrc_t rb,
+                                             const int (&fvoff)[C::LOADS], int wave, int fstep,
+                                             int tail_valid, int a_off, int b_off, int fx,
+                                             int lane, v4i (&fa)[2][C::TM], v4i (&fb)[2][C::TN],
+                                             v16i (&acc)[C::TM][C::TN]) {
+  step_inner<C>(cur, a_off, b_off, fx, lane, fa, fb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_and_barrier<C::VM>(0);
+  if (ZERO && tail_valid != 0) zero_tail<C>(nxt, tail_valid);
+  constexpr int last = (C::SLICES - 1) % 2;
+  read_slice<C>(nxt, 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+  persist_issue<C>(cur, ra, rb, fvoff, wave, fstep);
+  mfma_slice<C>(fa[last], fb[last], acc);
+  loads_under_mfmas<C, 1>();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int YT>
+__global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_persistent(
+    const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+    const int8_t* __restrict__ wq, const float* __restrict__ w_scale,
+    const float* __restrict__ bias, void* __restrict__ y, int64_t m, int64_t n, int64_t k) {
+  using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
+  using P = Persist<C, YT>;
+  constexpr int TM = C::TM, TN = C::TN;
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_all[];
+  const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+  const int64_t total = tiles_m * tiles_n;
+  const int64_t G = gridDim.x;
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int wm = wave / WN, wn = wave % WN;
+  const int area = static_cast<int>(P::STAGES_BYTES) + wave * P::WAVE_BYTES;  // scratch, params
+  const int ksteps = static_cast<int>((k + BK - 1) / BK);  // >= 2
+  const int tail_valid = static_cast<int>((k % BK) / 16);  // 0: none
+
+  // Tile id v in [0, vend): (m0, n0) in the XCD-contiguous grouped order of tile_of, or
+  // false for the ids of the per-XCD ranges' padding (total % 8 != 0).  With G a multiple of
+  // 8, the ids v, v + G, ... of a workgroup all belong to its XCD.
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t vend = per_xcd * kXcds;
+  auto tile_at = [&](int64_t v, int64_t& m0, int64_t& n0) -> bool {
+    // (opaque divisors: their division sequences are not hoisted into registers held
+    // across the tile loop)
+    int64_t pxc = per_xcd, tn_ = tiles_n, tm_ = tiles_m;
+    asm volatile("" : "+s"(pxc), "+s"(tn_), "+s"(tm_));
+    const int64_t u = (v % kXcds) * pxc + v / kXcds;
+    if (u >= total) return false;
+    const int64_t grp = u / (kGroupM * tn_);
+    const int64_t first_m = grp * kGroupM;
+    const int64_t gsize = min(tm_ - first_m, static_cast<int64_t>(kGroupM));
+    const int64_t in_group = u % (kGroupM * tn_);
+    m0 = (first_m + in_group % gsize) * BM;
+    n0 = (in_group / gsize) * BN;
+    return true;
+  };
+  const int lrow = lane / C::CHUNKS;
+  const int colb = ((lane % C::CHUNKS) ^ swizzle<BK>(wave * C::ROWS_PER_LOAD + lrow)) * 16;
+  // the first tile of this workgroup
+  int64_t v = blockIdx.x;
+  int64_t m0 = 0, n0 = 0;
+  while (v < vend && !tile_at(v, m0, n0)) v += G;
+  if (v >= vend) return;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(xq), 0, static_cast<int>(m * k), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(wq), 0, static_cast<int>(n * k), 0x00020000);
+  int voff[C::LOADS];
+  persist_offsets<C>(voff, m0, n0, m, n, k, wave, lrow, colb);
+  int sbase = 0;  // stage of the tile's step 0
+  persist_issue<C>(lds_all, ra, rb, voff, wave, 0);
+  persist_issue<C>(lds_all + C::STAGE_BYTES, ra, rb, voff, wave, 1);
+
+  const int frow = lane % 32;
+  const int fx = swizzle<BK>(frow);
+  const int a_off = (wm * C::WTM + frow) * BK;
+  const int b_off = (BM + wn * C::WTN + frow) * BK;
+  constexpr int last = (C::SLICES - 1) % 2;
+  while (true) {
+    // the next valid tile (or this one again: its loads are in bounds and never used)
+    int64_t vn = v + G, nm0 = m0, nn0 = n0;
+    while (vn < vend && !tile_at(vn, nm0, nn0)) vn += G;
+    const bool has_next = vn < vend;
+    if (!has_next) {
+      nm0 = m0;
+      nn0 = n0;
+    }
+    int nvoff[C::LOADS];
+    persist_offsets<C>(nvoff, nm0, nn0, m, n, k, wave, lrow, colb);
+    auto st = [&](int t) { return lds_all + ((sbase + t) & 1) * C::STAGE_BYTES; };
+
+    // Step 0 has landed once at most VM operations are outstanding: loads complete in issue
+    // order, so while step 0's were outstanding step 1's (issued later) would be too.  (The
+    // previous epilogue's stores count as well and may complete in any order relative to
+    // the loads, so the count cannot leave them out; they are waited for too.)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::VM, 15));
+    bare_barrier();
+    persist_params<C, YT>(reinterpret_cast<float*>(lds_all + area + kPScrBytes), lane, x_scale,
+                      w_scale, bias, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    v4i fa[2][TM], fb[2][TN];
+    read_slice<C>(st(0), 0, a_off, b_off, fx, lane, fa[0], fb[0]);
+    int t = 0;
+    for (; t + 2 < ksteps; ++t)
+      persist_step<C, false>(st(t), st(t + 1), ra, rb, voff, wave, t + 2, tail_valid, a_off,
+                             b_off, fx, lane, fa, fb, acc);
+    // second-to-last step: the freed stage takes the next tile's step 0
+    persist_step<C, true>(st(t), st(t + 1), ra, rb, nvoff, wave, 0, tail_valid, a_off, b_off,
+                          fx, lane, fa, fb, acc);
+    ++t;
+    // last step: once every wavefront has read its fragments, its stage takes the next
+    // tile's step 1
+    step_inner<C>(st(t), a_off, b_off, fx, lane, fa, fb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bare_barrier();
+    persist_issue<C>(st(t), ra, rb, nvoff, wave, 1);
+    mfma_slice<C>(fa[last], fb[last], acc);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t rows = min(static_cast<int64_t>(BM), m - m0);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(y) + m0 * n * P::ES, 0, static_cast<int>(rows * n * P::ES),
+        0x00020000);
+    persist_epilogue<C, YT>(acc, lds_all, area, lane, yr, n, wm * C::WTM, n0 + wn * C::WTN,
+                            bias != nullptr);
+    if (!has_next) break;
+    v = vn;
+    m0 = nm0;
+    n0 = nn0;
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) voff[j] = nvoff[j];
+    sbase = (sbase + ksteps) & 1;
+  }
+  // the last tile's refills and stores: nothing may land in LDS after the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+}
+
 // ---- two LDS slots for A, three for B ---------------------------------------------------
 // With two stages of both operands only one step of loads is in flight while a step
 // computes, and the weight rows (read once from HBM) arrive late.  A third stage of both
@@ -1088,8 +1412,41 @@ constexpr Candidate kCandidates[] = {
     {320, 256, 1, false, false, 1.5310, 26.719, -12.773},  // 11: 2 stages, 8 wavefronts 160x64
 };
 constexpr double kGsStep = 1.0;  // step-time factor of group-scale products
+// Configuration 0 with more tiles than one round runs the persistent kernel (see
+// launch_persistent), whose time per round of one tile per workgroup is modelled apart:
+// 1.63 us per k step plus 8.4 us, from MI355X graph timings at 16384 x 24576 x k (k 128 to
+// 4096, 24 rounds); it predicts the 8B prefill GEMMs at 16384 tokens within 3 %.
+constexpr double kPersistStep = 1.63, kPersistRound = 8.4;
 constexpr int kNumCandidates = static_cast<int>(sizeof(kCandidates) / sizeof(kCandidates[0]));
 constexpr double kFix0 = 0.0, kFix1 = 2.1;  // split fix-up cost model (us)
+
+int device_cus();
+
+// The persistent kernel for a two-stage configuration, when it applies (see
+// w8a8_kernel_persistent): one split, at least two k steps, more tiles than one round,
+// output rows of whole 16-byte chunks on a 16-byte aligned output, and operands and tile
+// row blocks that buffer resources can span.  Returns false when it does not apply (nothing launched).
+template <int BM, int BN, int BK, int WM, int WN, int YT>
+bool launch_persistent(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                       const float* w_scale, const float* bias, void* y, int64_t m, int64_t n,
+                       int64_t k, int splits, hipStream_t stream, hipError_t* err) {
+  using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
+  using P = Persist<C, YT>;
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int64_t g = device_cus() / kXcds * kXcds;
+  if (splits != 1 || k <= BK || tiles <= g || g < kXcds || (n * P::ES) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(y) % 16 != 0 ||
+      static_cast<int64_t>(BM) * n * P::ES >= (1ll << 31) || m * k >= (1ll << 31) ||
+      n * k >= (1ll << 31))
+    return false;
+  constexpr auto kern = w8a8_kernel_persistent<BM, BN, BK, WM, WN, YT>;
+  *err = allow_dynamic_lds<kern>(static_cast<int>(P::LDS_BYTES));
+  if (*err != hipSuccess) return true;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(g)), dim3(C::THREADS), P::LDS_BYTES,
+                     stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
+  *err = hipGetLastError();
+  return true;
+}
 
 template <int YT>
 hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const int8_t* wq,
@@ -1099,8 +1456,13 @@ hipError_t launch_candidate(int c, const int8_t* xq, const float* x_scale, const
   launch_cfg<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, splits, ws, stream)
 #define I8QL_W8A8_SPLIT(...) \
   launch_split<__VA_ARGS__>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream)
+  hipError_t perr = hipSuccess;
   switch (c) {
-    case 0: return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2, true);
+    case 0:
+      if (launch_persistent<256, 256, 128, 4, 2, YT>(xq, x_scale, wq, w_scale, bias, y, m, n, k,
+                                                      splits, stream, &perr))
+        return perr;
+      return I8QL_W8A8_CFG(256, 256, 128, 2, 1, YT, 4, 2, true);
     case 1: return I8QL_W8A8_CFG(256, 320, 128, 2, 1, YT, 4, 2, false);
     case 2: return I8QL_W8A8_SPLIT(256, 192, 128, YT, 4, 2);
     case 3: return I8QL_W8A8_SPLIT(128, 320, 128, YT, 4, 2);
@@ -1165,6 +1527,12 @@ double plan_time(int c, int splits, int64_t m, int64_t n, int64_t k, int cus) {
   if (units > kMaxGrid - kXcds) return -1.0;
   const double rounds = static_cast<double>((units + cus - 1) / cus);
   const double steps = static_cast<double>((ksteps / d.ks + splits - 1) / splits);
+  const int64_t g = cus / kXcds * kXcds;  // persistent workgroups
+  if (c == 0 && splits == 1 && ksteps >= 2 && g >= kXcds && tiles > g && n % 8 == 0 &&
+      m * k < (1ll << 31) && n * k < (1ll << 31) && 256 * n * 2 < (1ll << 31)) {
+    const double prounds = static_cast<double>((tiles + g - 1) / g);
+    return kPersistStep * prounds * steps + kPersistRound * prounds;
+  }
   double t = d.t_step * rounds * steps + d.t_round * rounds + d.t0;
   if (splits > 1) t += kFix0 + kFix1 * splits * (d.bm * d.bn / 16384.0);
   return t;

@@ -233,7 +233,10 @@ def test_w8a8_config_table_and_choices():
     assert pick(2048, 6144, 2560)[:3] == (256, 192, 1)
     assert pick(2048, 2560, 4096)[:3] == (128, 160, 1)
     assert pick(2048, 2560, 9728)[:3] == (128, 160, 1)
-    assert pick(16384, 12288, 4096)[:3] == (320, 256, 1)
+    # many rounds of tiles: the 256x256 tiles, whose persistent kernel keeps each compute
+    # unit's pipeline running from one tile into the next
+    assert pick(16384, 12288, 4096)[:3] == (256, 256, 1)
+    assert pick(16384, 24576, 4096)[:3] == (256, 256, 1)
     # few tiles and a long k: k split over k-groups inside the workgroup
     assert pick(128, 2560, 9728)[2] == 4
     assert pick(512, 2560, 9728)[2] == 2
