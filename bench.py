@@ -318,6 +318,12 @@ def measure_prefill(torch, wl, wk, args, label, clock=True):
                         "bound": bound, "frac_of_bound": frac,
                         "frac_mfma": o / sec / 1e12 / PEAK_INT8_TOPS,
                         "frac_hbm": b / sec / 1e9 / PEAK_HBM_GBS})
+    # the step's GEMMs alone, in step order with the step's weight rotation: the W8A8
+    # kernel's launches as the timed step runs them (back to back with other launches, not
+    # each repeated on its own), which the roofline's average launch duration is taken from
+    seq = mean_call(torch, lambda i: [wk.gemm(m, nm, i) for m in wk.tokens for nm in wk.names],
+                    reps)
+    out["w8a8_gemm_sequence_us_per_step"] = seq * 1e6
     t_gemm = sum(p["us"] for p in per) * 1e-6
     t_quant = sum(q["us"] for q in multi) * 1e-6
     t_sep = sum(q["us"] for q in quant) * 1e-6
@@ -334,13 +340,15 @@ def measure_prefill(torch, wl, wk, args, label, clock=True):
     return out
 
 
-def w8a8_roofline(per, traffic):
+def w8a8_roofline(per, traffic, seq_us):
     """The roofline entry of the W8A8 kernel over a step's GEMM launches: the bound that
-    holds for most of the kernel time, achieved = algorithmic work / summed average launch
-    durations (int8 TOPS against 5.0 POP/s, or GB/s against 8 TB/s)."""
-    t = sum(p["us"] for p in per) * 1e-6
+    holds for most of the kernel time (by each launch's own classification), achieved =
+    algorithmic work / the launches' durations in step order (seq_us per step: int8 TOPS
+    against 5.0 POP/s, or GB/s against 8 TB/s)."""
+    t_own = sum(p["us"] for p in per) * 1e-6
     t_mfma = sum(p["us"] for p in per if p["bound"] == "mfma") * 1e-6
-    bound = "mfma" if t_mfma >= t / 2 else "hbm"
+    bound = "mfma" if t_mfma >= t_own / 2 else "hbm"
+    t = seq_us * 1e-6
     n = len(per)
     if bound == "mfma":
         ach, peak, unit = sum(p["ops"] for p in per) / t / 1e12, PEAK_INT8_TOPS, "TOPS"
@@ -349,6 +357,7 @@ def w8a8_roofline(per, traffic):
     return {"kernel": "w8a8_kernel (all tile instantiations)", "bound": bound,
             "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
             "traffic": traffic, "avg_launch_us": t / n * 1e6, "launches_per_step": n,
+            "avg_launch_us_each_on_its_own": t_own / n * 1e6,
             "ops_per_launch": sum(p["ops"] for p in per) / n,
             "algorithmic_bytes_per_launch": sum(p["bytes"] for p in per) / n,
             "launches_by_bound": {b: sum(1 for p in per if p["bound"] == b)
@@ -379,7 +388,8 @@ def section_step(torch, i8, wl, dev, args, result):
     result["frac_mfma_step"] = out["TOPS"] / PEAK_INT8_TOPS
     result["frac_mfma_step_at_sustained_clock"] = (
         out["TOPS"] / (PEAK_INT8_TOPS * mhz / PEAK_GFX_MHZ) if mhz else None)
-    result["roofline"] = w8a8_roofline(out["per_launch"], traffic_for("w8a8_kernel", HEADLINE))
+    result["roofline"] = w8a8_roofline(out["per_launch"], traffic_for("w8a8_kernel", HEADLINE),
+                                       out["w8a8_gemm_sequence_us_per_step"])
     result["per_launch"] = out["per_launch"]
     result["quantize_per_token"] = out["quantize_per_token"]
     result["parts_us_per_step"] = {"w8a8_gemm": out["w8a8_gemm_us_per_step"],
@@ -394,7 +404,8 @@ def section_step(torch, i8, wl, dev, args, result):
 def section_prefill_8b_m4096(torch, i8, wl, dev, args, result):
     wk = prefill_8b(torch, i8, wl, dev, (4096,))
     out = measure_prefill(torch, wl, wk, args, "prefill_8b_m4096")
-    out["roofline"] = w8a8_roofline(out["per_launch"], None)
+    out["roofline"] = w8a8_roofline(out["per_launch"], None,
+                                    out["w8a8_gemm_sequence_us_per_step"])
     result["prefill_8b_m4096"] = {
         "workload": "dense 8B decoder layer, W8A8 prefill at 4096 tokens (the same step as the "
                     "headline at its other token count)", "unit": "TOPS", **out}
@@ -408,7 +419,8 @@ def section_prefill_8b_g128(torch, i8, wl, dev, args, result):
     wk = PrefillWorkload(torch, i8, wl, dev, wl.DENSE_8B, wl.DENSE_8B_FUSED, (16384,), 0.01,
                          True, seed=3, group_scales=True)
     out = measure_prefill(torch, wl, wk, args, "prefill_8b_g128", clock=False)
-    out["roofline"] = w8a8_roofline(out["per_launch"], None)
+    out["roofline"] = w8a8_roofline(out["per_launch"], None,
+                                    out["w8a8_gemm_sequence_us_per_step"])
     if result.get("per_launch"):
         pc = {(p["m"], p["proj"]): p["us"] for p in result["per_launch"]}
         for p in out["per_launch"]:
@@ -425,7 +437,8 @@ def section_prefill_4b(torch, i8, wl, dev, args, result):
     wk = prefill_4b(torch, i8, wl, dev)
     out = measure_prefill(torch, wl, wk, args, "prefill_4b", clock=False)
     out["roofline"] = w8a8_roofline(out["per_launch"],
-                                    traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"))
+                                    traffic_for("w8a8_kernel", "dense 4B W8A8 prefill step"),
+                                    out["w8a8_gemm_sequence_us_per_step"])
     result["prefill_4b"] = {
         "workload": "dense 4B decoder layer (q 2560->4096, k/v 2560->1024, o 4096->2560, "
                     "gate/up 2560->9728, down 9728->2560), W8A8 prefill at M in {128, 512, "
