@@ -330,10 +330,12 @@ def measure_prefill(torch, wl, wk, args, label, clock=True):
     qbytes = sum(quant_bytes(q["m"], q["k"]) for q in quant)
     out["per_launch"] = per
     out["quantize_per_token"] = {
-        "launches": multi, "us_per_step": t_quant * 1e6, "GBs": qbytes / t_quant / 1e9,
+        "per_token_count": multi, "us_per_step": t_quant * 1e6,
+        "GBs": qbytes / t_quant / 1e9,
         "frac_hbm": qbytes / t_quant / 1e9 / PEAK_HBM_GBS,
-        "what": "the step's four inputs of each token count: one quantize_per_token_int8_multi "
-                "launch below 4096 tokens, else one quantize_per_token_int8 each",
+        "what": "the step's four inputs of each token count, timed together: one "
+                "quantize_per_token_int8_multi launch below 4096 tokens, else one "
+                "quantize_per_token_int8 launch each",
         "separate": {"what": "one quantize_per_token_int8 launch per input", "launches": quant,
                      "us_per_step": t_sep * 1e6, "GBs": qbytes / t_sep / 1e9}}
     out["w8a8_gemm_us_per_step"] = t_gemm * 1e6
