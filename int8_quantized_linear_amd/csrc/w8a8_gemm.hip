@@ -72,6 +72,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
@@ -497,7 +498,8 @@ __device__ __forceinline__ float epilogue_value(int a, float sx, float sw) {
   return __fmul_rn(__fmul_rn(static_cast<float>(a), sx), sw);
 }
 
-template <class C, int YT, bool GS>
+// BIAS: bias is not null (a template flag, so that each output value costs no select).
+template <class C, int YT, bool GS, bool BIAS>
 __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], int* scr,
                                              int lane, const float* __restrict__ x_scale,
                                              const float* __restrict__ w_scale,
@@ -512,7 +514,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
     for (int j = 0; j < TN; ++j) {
       const int64_t c = c0 + j * 32 + lane % 32;
       sw[j] = GS ? 1.0f : w_scale[c < n ? c : n - 1];
-      bj[j] = bias ? bias[c < n ? c : n - 1] : 0.0f;
+      bj[j] = BIAS ? bias[c < n ? c : n - 1] : 0.0f;
     }
   }
 #pragma unroll
@@ -540,7 +542,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
             bits = acc[i][j][r];
           } else {
             float v = epilogue_value<YT, GS>(acc[i][j][r], sx[r], sw[j]);
-            if (bias) v = __fadd_rn(v, bj[j]);
+            if constexpr (BIAS) v = __fadd_rn(v, bj[j]);
             bits = __float_as_int(v);
           }
           scr[row * kScrWords + jj * 32 + lane % 32] = bits;
@@ -645,7 +647,10 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* s
                                          int64_t n, int64_t r0, int64_t c0) {
   constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
   if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
-    epilogue_lds<C, YT, GS>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+    if (bias)
+      epilogue_lds<C, YT, GS, true>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+    else
+      epilogue_lds<C, YT, GS, false>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
   } else {
     epilogue_regs<C, YT, GS>(acc, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
   }
@@ -850,8 +855,19 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
 // where the hardware drops them.  The last tile refills from itself (in-bounds loads of no
 // use) and the kernel drains every load before it ends.  Needs k > BK (two steps at least), output rows of whole
 // 16-byte chunks and a 16-byte aligned output.
-constexpr int kPScrWords = 40;                   // words per scratch row (32 + padding)
+constexpr int kPScrWords = 32;                   // words per scratch row (swizzled)
 constexpr int kPScrBytes = 16 * kPScrWords * 4;  // 16 rows of output values
+
+// Word of value (row, col) of a 16 x 32 piece in the scratch.  Rows r and r + 4 (written by
+// the two halves of one wavefront instruction) go to slots of opposite parity, i.e. opposite
+// halves of 64 banks; within the slots whose 4-word chunks a 16-byte read instruction takes
+// together (slots 2s and 2s + 1 with 32 banks, 4s .. 4s + 3 with 64), the chunk index is
+// XORed with a different parity, so the chunks those reads take never share a bank.
+__device__ __forceinline__ int pscr_word(int row, int col) {
+  const int slot = row ^ ((row >> 2) & 1);
+  const int g = (slot ^ (slot >> 1)) & 1;
+  return slot * kPScrWords + (col ^ (g << 2));
+}
 
 template <class C, int YT>
 struct Persist {
@@ -866,8 +882,8 @@ struct Persist {
   static_assert(C::WTM % 64 == 0 && C::WTN % 64 == 0, "parameter copies of 64 values");
 };
 
-// Copy this wavefront's row scales, column scales and bias (zeros without bias) for the tile
-// at (r0, c0) into `par` (direct-to-LDS, 64 values per instruction; indices clamped).  Int32
+// Copy this wavefront's row scales, column scales and bias (if any) for the tile at (r0, c0)
+// into `par` (direct-to-LDS, 64 values per instruction; indices clamped).  Int32
 // output uses none of them (and the scales may then be null): nothing is loaded.
 template <class C, int YT>
 __device__ __forceinline__ void persist_params(float* par, int lane,
@@ -888,21 +904,19 @@ __device__ __forceinline__ void persist_params(float* par, int lane,
     __builtin_amdgcn_global_load_lds(w_scale + cc, par + C::WTM + h * 64, 4, 0, 0);
     if (bias) __builtin_amdgcn_global_load_lds(bias + cc, par + C::WTM + C::WTN + h * 64, 4, 0, 0);
   }
-  if (!bias) {
-#pragma unroll
-    for (int h = 0; h < C::WTN / 64; ++h) par[C::WTM + C::WTN + h * 64 + lane] = 0.0f;
-  }
 }
 
 // The fused epilogue of the persistent kernel: 16 x 32 pieces through `scr`, scales and bias
 // from `par`, output through the buffer resource `yr` over the tile's rows (rows past m lie
 // past its end).  (r0, c0): the wavefront's first row and column relative to the tile's
-// first row and in the whole output.
-template <class C, int YT>
+// first row and in the whole output.  The lane's scales and biases are read once.  A
+// piece's reads follow its writes, and the next piece's writes its reads, without a wait:
+// the LDS executes one wavefront's instructions in issue order.  BIAS: the tile has a bias.
+template <class C, int YT, bool BIAS>
 __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN],
                                                  int8_t* lds_all, int area, int lane,
                                                  __amdgpu_buffer_rsrc_t yr, int64_t n,
-                                                 int r0, int64_t c0, bool has_bias) {
+                                                 int r0, int64_t c0) {
   using P = Persist<C, YT>;
   // (the area's offset is opaque, so that the compiler derives the scratch and parameter
   // addresses here instead of holding them in registers across the tile loop)
@@ -912,42 +926,56 @@ __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN]
   const float* par = reinterpret_cast<const float*>(lds_all + area + kPScrBytes);
   constexpr int PER = P::PER;
   constexpr int CPR = 32 / PER;  // 16-byte chunks per row of a piece
+  // register r = 8h + q of a 32 x 32 block holds row 16h + 8(q / 4) + 4(lane / 32) + q % 4
+  float sx[C::TM][2][8], sw[C::TN], bj[C::TN];
+  if constexpr (YT != I8QL_I32) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const v4f t =
+              *reinterpret_cast<const v4f*>(par + i * 32 + 16 * h + 8 * g + 4 * (lane / 32));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sx[i][h][4 * g + e] = t[e];
+        }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      sw[j] = par[C::WTM + j * 32 + lane % 32];
+      bj[j] = BIAS ? par[C::WTM + C::WTN + j * 32 + lane % 32] : 0.0f;
+    }
+  }
+  const int nb = static_cast<int>(n) * P::ES;  // bytes per output row
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        // registers 8h .. 8h + 7 hold rows 16h .. 16h + 15 of the 32-row block
-        const float sw = par[C::WTM + j * 32 + lane % 32];
-        const float bj = par[C::WTM + C::WTN + j * 32 + lane % 32];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int r = 8 * h + q;
           const int row = 8 * (q / 4) + 4 * (lane / 32) + q % 4;  // within the piece
           int bits;
           if constexpr (YT == I8QL_I32) {
-            bits = acc[i][j][r];
+            bits = acc[i][j][8 * h + q];
           } else {
-            const float sx = par[i * 32 + 16 * h + row];
-            float v = epilogue_value<YT, false>(acc[i][j][r], sx, sw);
-            if (has_bias) v = __fadd_rn(v, bj);
+            float v = epilogue_value<YT, false>(acc[i][j][8 * h + q], sx[i][h][q], sw[j]);
+            if constexpr (BIAS) v = __fadd_rn(v, bj[j]);
             bits = __float_as_int(v);
           }
-          scr[row * kPScrWords + lane % 32] = bits;
+          scr[pscr_word(row, lane % 32)] = bits;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int u = 0; u < P::PIECE_STORES; ++u) {
           const int qq = u * 64 + lane;
           const int row = qq / CPR, cg = qq % CPR;
-          const int* src = scr + row * kPScrWords + cg * PER;
           v4i out;
           if constexpr (P::ES == 4) {
-            out = *reinterpret_cast<const v4i*>(src);
+            out = *reinterpret_cast<const v4i*>(scr + pscr_word(row, cg * PER));
           } else {
-            const v4i a = *reinterpret_cast<const v4i*>(src);
-            const v4i b = *reinterpret_cast<const v4i*>(src + 4);
+            const v4i a = *reinterpret_cast<const v4i*>(scr + pscr_word(row, cg * PER));
+            const v4i b = *reinterpret_cast<const v4i*>(scr + pscr_word(row, cg * PER + 4));
             const int w8[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -956,12 +984,11 @@ __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN]
             }
           }
           const int64_t col = c0 + j * 32 + cg * PER;
-          const int64_t off = ((r0 + i * 32 + 16 * h + row) * n + col) * P::ES;
-          const int voff = col < n ? static_cast<int>(off) : -16;  // (past the end: dropped)
+          // (r0 + BM) * n * ES < 2^31: checked at launch)
+          const int off = (r0 + i * 32 + 16 * h + row) * nb + static_cast<int>(col) * P::ES;
+          const int voff = col < n ? off : -16;  // (past the end: dropped)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, out), yr, voff, 0, 0);
         }
-        // the next piece overwrites the scratch: its reads must be done
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
 }
 
@@ -1141,8 +1168,12 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_persistent(
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char*>(y) + m0 * n * P::ES, 0, static_cast<int>(rows * n * P::ES),
         0x00020000);
-    persist_epilogue<C, YT>(acc, lds_all, area, lane, yr, n, wm * C::WTM, n0 + wn * C::WTN,
-                            bias != nullptr);
+    if (bias)
+      persist_epilogue<C, YT, true>(acc, lds_all, area, lane, yr, n, wm * C::WTM,
+                                    n0 + wn * C::WTN);
+    else
+      persist_epilogue<C, YT, false>(acc, lds_all, area, lane, yr, n, wm * C::WTM,
+                                     n0 + wn * C::WTN);
     if (!has_next) break;
     v = vn;
     m0 = nm0;
