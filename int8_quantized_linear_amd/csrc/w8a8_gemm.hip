@@ -855,25 +855,26 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
 // where the hardware drops them.  The last tile refills from itself (in-bounds loads of no
 // use) and the kernel drains every load before it ends.  Needs k > BK (two steps at least), output rows of whole
 // 16-byte chunks and a 16-byte aligned output.
-constexpr int kPScrWords = 32;                   // words per scratch row (swizzled)
-constexpr int kPScrBytes = 16 * kPScrWords * 4;  // 16 rows of output values
+constexpr int kPScrWords = 64;                  // words per scratch row (swizzled)
+constexpr int kPScrBytes = 8 * kPScrWords * 4;  // 8 rows of output values
 
-// Word of value (row, col) of a 16 x 32 piece in the scratch.  Rows r and r + 4 (written by
-// the two halves of one wavefront instruction) go to slots of opposite parity, i.e. opposite
-// halves of 64 banks; within the slots whose 4-word chunks a 16-byte read instruction takes
-// together (slots 2s and 2s + 1 with 32 banks, 4s .. 4s + 3 with 64), the chunk index is
-// XORed with a different parity, so the chunks those reads take never share a bank.
+// Word of value (row, col) of an 8 x 64 piece in the scratch, by 4-word chunks.  A row's
+// 16-byte reads (8 or 16 lanes per row) take chunks 2c, 2c + 1 or c: flipping bit 0 of the
+// chunks with bit 3 set puts each read's chunks on distinct banks of 32; rows 2s and 2s + 1
+// (read in one pass of 64 banks) differ in bit 0 of the chunk, and rows r and r + 4
+// (written by the two halves of one instruction) in bit 3.
 __device__ __forceinline__ int pscr_word(int row, int col) {
-  const int slot = row ^ ((row >> 2) & 1);
-  const int g = (slot ^ (slot >> 1)) & 1;
-  return slot * kPScrWords + (col ^ (g << 2));
+  int c = col >> 2;
+  c ^= (c >> 3) & 1;
+  c ^= (row & 1) ^ (((row >> 2) & 1) << 3);
+  return row * kPScrWords + c * 4 + (col & 3);
 }
 
 template <class C, int YT>
 struct Persist {
   static constexpr int ES = YT == I8QL_BF16 ? 2 : 4;  // output element bytes
   static constexpr int PER = 16 / ES;                  // output elements per 16-byte store
-  static constexpr int PIECE_STORES = 16 * 32 / PER / 64;  // per 16 x 32 piece and lane
+  static constexpr int PIECE_STORES = 8 * 64 / PER / 64;   // per 8 x 64 piece and lane
   static constexpr int PARAM_BYTES = (C::WTM + 2 * C::WTN) * 4;    // row scales, col scales, bias
   static constexpr int WAVE_BYTES = kPScrBytes + PARAM_BYTES;
   static constexpr size_t STAGES_BYTES = 2 * static_cast<size_t>(C::STAGE_BYTES);
@@ -906,18 +907,20 @@ __device__ __forceinline__ void persist_params(float* par, int lane,
   }
 }
 
-// The fused epilogue of the persistent kernel: 16 x 32 pieces through `scr`, scales and bias
-// from `par`, output through the buffer resource `yr` over the tile's rows (rows past m lie
-// past its end).  (r0, c0): the wavefront's first row and column relative to the tile's
-// first row and in the whole output.  The lane's scales and biases are read once.  A
-// piece's reads follow its writes, and the next piece's writes its reads, without a wait:
-// the LDS executes one wavefront's instructions in issue order.  BIAS: the tile has a bias.
+// The fused epilogue of the persistent kernel: 8 x 64 pieces through `scr` (every store
+// instruction writes whole 128-byte lines of bf16 rows), scales and bias from `par`, output
+// through the buffer resource `yr` over the tile's rows (rows past m lie past its end).
+// (r0, c0): the wavefront's first row and column relative to the tile's first row and in
+// the whole output.  The lane's scales and biases are read once.  A piece's reads follow its
+// writes, and the next piece's writes its reads, without a wait: the LDS executes one
+// wavefront's instructions in issue order.  BIAS: the tile has a bias.
 template <class C, int YT, bool BIAS>
 __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN],
                                                  int8_t* lds_all, int area, int lane,
                                                  __amdgpu_buffer_rsrc_t yr, int64_t n,
                                                  int r0, int64_t c0) {
   using P = Persist<C, YT>;
+  static_assert(C::TN % 2 == 0, "pieces of two 32-column blocks");
   // (the area's offset is opaque, so that the compiler derives the scratch and parameter
   // addresses here instead of holding them in registers across the tile loop)
   asm volatile("" : "+s"(area));
@@ -925,21 +928,18 @@ __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN]
   int* scr = reinterpret_cast<int*>(lds_all + area);
   const float* par = reinterpret_cast<const float*>(lds_all + area + kPScrBytes);
   constexpr int PER = P::PER;
-  constexpr int CPR = 32 / PER;  // 16-byte chunks per row of a piece
-  // register r = 8h + q of a 32 x 32 block holds row 16h + 8(q / 4) + 4(lane / 32) + q % 4
-  float sx[C::TM][2][8], sw[C::TN], bj[C::TN];
+  constexpr int CPR = 64 / PER;  // 16-byte chunks per row of a piece
+  // register 4g + q of a 32 x 32 block holds row 8g + 4(lane / 32) + q
+  float sx[C::TM][4][4], sw[C::TN], bj[C::TN];
   if constexpr (YT != I8QL_I32) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int g = 0; g < 4; ++g) {
+        const v4f t = *reinterpret_cast<const v4f*>(par + i * 32 + 8 * g + 4 * (lane / 32));
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const v4f t =
-              *reinterpret_cast<const v4f*>(par + i * 32 + 16 * h + 8 * g + 4 * (lane / 32));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sx[i][h][4 * g + e] = t[e];
-        }
+        for (int q = 0; q < 4; ++q) sx[i][g][q] = t[q];
+      }
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       sw[j] = par[C::WTM + j * 32 + lane % 32];
@@ -950,22 +950,25 @@ __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN]
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
+      for (int jp = 0; jp < C::TN / 2; ++jp) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int row = 8 * (q / 4) + 4 * (lane / 32) + q % 4;  // within the piece
-          int bits;
-          if constexpr (YT == I8QL_I32) {
-            bits = acc[i][j][8 * h + q];
-          } else {
-            float v = epilogue_value<YT, false>(acc[i][j][8 * h + q], sx[i][h][q], sw[j]);
-            if constexpr (BIAS) v = __fadd_rn(v, bj[j]);
-            bits = __float_as_int(v);
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = 2 * jp + jj;
+            const int row = 4 * (lane / 32) + q;  // within the piece
+            int bits;
+            if constexpr (YT == I8QL_I32) {
+              bits = acc[i][j][4 * g + q];
+            } else {
+              float v = epilogue_value<YT, false>(acc[i][j][4 * g + q], sx[i][g][q], sw[j]);
+              if constexpr (BIAS) v = __fadd_rn(v, bj[j]);
+              bits = __float_as_int(v);
+            }
+            scr[pscr_word(row, jj * 32 + lane % 32)] = bits;
           }
-          scr[pscr_word(row, lane % 32)] = bits;
-        }
 #pragma unroll
         for (int u = 0; u < P::PIECE_STORES; ++u) {
           const int qq = u * 64 + lane;
@@ -983,9 +986,9 @@ __device__ __forceinline__ void persist_epilogue(const v16i (&acc)[C::TM][C::TN]
               out[e] = __builtin_bit_cast(int, __builtin_convertvector(pair, v2bf));
             }
           }
-          const int64_t col = c0 + j * 32 + cg * PER;
+          const int64_t col = c0 + jp * 64 + cg * PER;
           // (r0 + BM) * n * ES < 2^31: checked at launch)
-          const int off = (r0 + i * 32 + 16 * h + row) * nb + static_cast<int>(col) * P::ES;
+          const int off = (r0 + i * 32 + 8 * g + row) * nb + static_cast<int>(col) * P::ES;
           const int voff = col < n ? off : -16;  // (past the end: dropped)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, out), yr, voff, 0, 0);
         }

@@ -567,13 +567,21 @@ def test_grouped_single_token_repeated_expert(ref, dev):
 
 
 def test_grouped_one_expert_equals_w8a16(ref, dev):
+    """One expert that every row is routed to: the grouped kernel computes the dense W8A16
+    product.  Float32 outputs; the two kernels sum the k products (exact in float32) in
+    different orders and then scale, each within (k + 1) * 2^-24 * s * sum|x * q| of the exact
+    value, so they differ by at most twice that."""
     g = wl.rng(22)
     n, k = 100, 512
     qw, sw, _, _ = moe_stack(ref, dev, g, n, k, 1)
     x = wl.to_bf16(wl.activations(g, 19, k)).to(dev)
-    yg = i8.grouped_w8a16_gemm(x, qw, sw, torch.zeros((19, 1), dtype=torch.int32, device=dev))
-    yd = i8.w8a16_gemm(x, qw[0], sw[0])
-    check_float(yg, to_np(yd).astype(np.float64), np.abs(to_np(yd)) * 1e-2 + 1e-3, "E=1")
+    yg = i8.grouped_w8a16_gemm(x, qw, sw, torch.zeros((19, 1), dtype=torch.int32, device=dev),
+                               out_dtype=torch.float32)
+    yd = i8.w8a16_gemm(x, qw[0], sw[0], out_dtype=torch.float32)
+    xa = np.abs(to_np(x).astype(np.float64))
+    qa = np.abs(to_np(qw[0]).astype(np.float64))
+    bound = 2.0 * (k + 1) * 2.0**-24 * (xa @ qa.T) * to_np(sw[0]).astype(np.float64)[None, :]
+    check_float(yg, to_np(yd).astype(np.float64), bound + 1e-30, "E=1")
 
 
 def test_grouped_many_rows_per_expert(ref, dev):
