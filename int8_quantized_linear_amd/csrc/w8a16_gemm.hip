@@ -30,6 +30,7 @@ constexpr int kUnroll = 8;  // steps of k whose loads a wavefront keeps in fligh
 constexpr int kGlobalUnroll = 4;  // the same with activations loaded too (divided by MT)
 constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a function attribute
 constexpr size_t kMaxStageLds = 96 * 1024;  // staged rows up to this much LDS (attribute set)
+constexpr size_t kParamTableBytes = 64 * 4;  // the epilogue's scales and biases
 
 // Dynamic LDS: the partial tiles of the WAVES wavefronts ([WAVES][MT][64] v4f), then, when
 // the activation rows are staged, rows of 2k + 16 bytes (consecutive rows shifted by one
@@ -42,17 +43,31 @@ constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * MT * 64 * siz
 // step loop applies them per step (k % 128 == 0) and the epilogue applies bias only.  With
 // staged rows the tile's scales are staged too, as an LDS table [step][16 channels] after
 // the zero block (one direct-to-LDS dword per lane, issued before everything else).
+//
+// The epilogue's 16 channel scales and biases are copied to a 64-float LDS table at
+// `ptab_off` (the end of the dynamic LDS) by wavefront 0 when the kernel starts, so the
+// epilogue reads LDS instead of waiting for a memory round trip after the reduction (loads
+// issued as late as their use cost that round trip on every launch).
 template <int MT, int WAVES, int YT, bool XLDS, bool GS = false>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, const float* __restrict__ bias, void* __restrict__ y,
-    int64_t m, int64_t n, int64_t k) {
+    int64_t m, int64_t n, int64_t k, int ptab_off) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   v4f* red = reinterpret_cast<v4f*>(smem);
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+  float* ptab = reinterpret_cast<float*>(smem + ptab_off);
+  if (wave == 0) {
+    // lanes 0-15: scale of channel n0 + lane (clamped), 16-31: its bias; the other lanes
+    // re-read a scale (in bounds, never used).  With group scales the first slot is unused.
+    const int64_t c = min(n0 + lane % 16, n - 1);
+    const float* src = bias && lane >= 16 && lane < 32 ? bias + c
+                                                       : w_scale + c * (GS ? k / kStepK : 1);
+    __builtin_amdgcn_global_load_lds(src, ptab, 4, 0, 0);
+  }
 
   const int64_t wr = min(n0 + lane % 16, n - 1);
   const int8_t* wrow = wq + wr * k;
@@ -132,13 +147,17 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 
   // Channels 4*(lane/16) + r of the tile, activation row lane % 16 of each m-tile.
   const int64_t nc = n0 + 4 * (lane / 16);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // this wave's table copy has landed
   float sc[4], bs[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t c = min(nc + r, n - 1);
-    sc[r] = GS ? 1.0f : w_scale[c];  // group scales were applied per step
-    bs[r] = bias ? bias[c] : 0.0f;
+    sc[r] = GS ? 1.0f : ptab[4 * (lane / 16) + r];  // group scales were applied per step
+    bs[r] = bias ? ptab[16 + 4 * (lane / 16) + r] : 0.0f;
   }
+  // the 4 channels of a lane are adjacent: one 8-byte (bf16) or 16-byte (float32) store
+  // when they are all real and the output row offsets keep it aligned
+  constexpr int kES = YT == I8QL_F32 ? 4 : 2;
+  const bool vec_store = n % 4 == 0 && reinterpret_cast<uintptr_t>(y) % (4 * kES) == 0;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     v4f s = red[mt * 64 + lane];
@@ -146,16 +165,30 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     for (int w = 1; w < WAVES; ++w) s += red[(w * MT + mt) * 64 + lane];
     const int64_t row = m0 + mt * 16 + lane % 16;
     if (row >= m) continue;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = s[r] * sc[r];
+      if (bias) v[r] = v[r] + bs[r];
+    }
+    if (vec_store && nc + 3 < n) {
+      if constexpr (YT == I8QL_F32) {
+        *reinterpret_cast<v4f*>(static_cast<float*>(y) + row * n + nc) = v4f{v[0], v[1], v[2], v[3]};
+      } else {
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + row * n + nc) = make_uint2(lo, hi);
+      }
+      continue;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t c = nc + r;
       if (c >= n) continue;
-      float v = s[r] * sc[r];
-      if (bias) v = v + bs[r];
       if constexpr (YT == I8QL_F32) {
-        static_cast<float*>(y)[row * n + c] = v;
+        static_cast<float*>(y)[row * n + c] = v[r];
       } else {
-        static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v);
+        static_cast<uint16_t*>(y)[row * n + c] = f32_to_bf16_rne(v[r]);
       }
     }
   }
@@ -171,7 +204,8 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
   const int rows = static_cast<int>(min(static_cast<int64_t>(16 * MT), m));
   const size_t rbytes = red_bytes<MT, WAVES>();
   const size_t gs_bytes = GS ? 256 * static_cast<size_t>((k / kStepK + 3) / 4) : 0;
-  const size_t xlds = rbytes + 1024 * static_cast<size_t>(stage_insts(rows, k)) + 16 + gs_bytes;
+  const size_t xlds_tab = rbytes + 1024 * static_cast<size_t>(stage_insts(rows, k)) + 16 + gs_bytes;
+  const size_t xlds = xlds_tab + kParamTableBytes;
   // (with more than 16 KiB of partial tiles, the rows of the k that calls for that many
   // waves never fit)
   constexpr bool can_stage = red_bytes<MT, WAVES>() <= kMaxDefaultLds / 4;
@@ -182,10 +216,11 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), xlds, stream, xx, wq, w_scale, bias, y, m,
-                       n, k);
+                       n, k, static_cast<int>(xlds_tab));
   } else {
     hipLaunchKernelGGL((w8a16_kernel<MT, WAVES, YT, false, GS>), grid, dim3(64 * WAVES),
-                       rbytes, stream, xx, wq, w_scale, bias, y, m, n, k);
+                       rbytes + kParamTableBytes, stream, xx, wq, w_scale, bias, y, m, n, k,
+                       static_cast<int>(rbytes));
   }
   return hipGetLastError();
 }
