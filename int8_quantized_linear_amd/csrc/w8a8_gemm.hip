@@ -226,6 +226,17 @@ struct Cfg {
   static constexpr size_t GROUP_BYTES = static_cast<size_t>(STAGES) * STAGE_BYTES;
   static constexpr size_t RED_BYTES = static_cast<size_t>(KS / 2) * BM * BN * 4;
   static constexpr size_t LDS_BYTES = KS * GROUP_BYTES > RED_BYTES ? KS * GROUP_BYTES : RED_BYTES;
+  // the epilogue's parameter table per wavefront of the first k-group: row scales, column
+  // scales, bias, each in whole 64-value copies
+  static constexpr int PAR_RM = (WTM + 63) / 64 * 64, PAR_RN = (WTN + 63) / 64 * 64;
+  static constexpr int PAR_WORDS = PAR_RM + 2 * PAR_RN;
+  static constexpr size_t PAR_BYTES = static_cast<size_t>(WAVES) * PAR_WORDS * 4;
+  // whether a kernel whose stages take `stage_lds` bytes keeps the table: it must fit in the
+  // 160 KiB of LDS, and the tiles whose accumulators take more than 128 registers (their
+  // kernels use every register) keep reading the parameters from memory instead
+  static constexpr bool params_fit(size_t stage_lds) {
+    return stage_lds + PAR_BYTES <= 160 * 1024 && TM * TN <= 8;
+  }
   static_assert(KS == 1 || KS == 2 || KS == 4, "k-groups per workgroup");
   static_assert(BK == 64 || BK == 128, "BK is 64 or 128 bytes");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "sub-tile must be whole 32x32 blocks");
@@ -498,13 +509,42 @@ __device__ __forceinline__ float epilogue_value(int a, float sx, float sw) {
   return __fmul_rn(__fmul_rn(static_cast<float>(a), sx), sw);
 }
 
+// Copy the epilogue's row scales (rows r0 .. r0 + WTM), column scales (unless GS) and bias
+// (if any) of a wavefront's sub-tile into its table `par` (direct-to-LDS, 64 values per
+// instruction, indices clamped).  Issued before the first k step's loads, so every later
+// wait for those covers it too; int32 output needs none of it.
+template <class C, int YT, bool GS>
+__device__ __forceinline__ void epi_params(float* par, int lane, const float* __restrict__ x_scale,
+                                           const float* __restrict__ w_scale,
+                                           const float* __restrict__ bias, int64_t m, int64_t n,
+                                           int64_t r0, int64_t c0) {
+  if constexpr (YT == I8QL_I32) return;
+#pragma unroll
+  for (int h = 0; h < C::PAR_RM / 64; ++h) {
+    const int64_t r = r0 + h * 64 + lane;
+    __builtin_amdgcn_global_load_lds(x_scale + (r < m ? r : m - 1), par + h * 64, 4, 0, 0);
+  }
+#pragma unroll
+  for (int h = 0; h < C::PAR_RN / 64; ++h) {
+    const int64_t c = c0 + h * 64 + lane;
+    const int64_t cc = c < n ? c : n - 1;
+    if constexpr (!GS)
+      __builtin_amdgcn_global_load_lds(w_scale + cc, par + C::PAR_RM + h * 64, 4, 0, 0);
+    if (bias)
+      __builtin_amdgcn_global_load_lds(bias + cc, par + C::PAR_RM + C::PAR_RN + h * 64, 4, 0, 0);
+  }
+}
+
 // BIAS: bias is not null (a template flag, so that each output value costs no select).
-template <class C, int YT, bool GS, bool BIAS>
+// PAR: the parameters come from the wavefront's table `par` (epi_params, landed), else from
+// global memory here.
+template <class C, int YT, bool GS, bool BIAS, bool PAR>
 __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], int* scr,
                                              int lane, const float* __restrict__ x_scale,
                                              const float* __restrict__ w_scale,
                                              const float* __restrict__ bias, void* y,
-                                             int64_t m, int64_t n, int64_t r0, int64_t c0) {
+                                             int64_t m, int64_t n, int64_t r0, int64_t c0,
+                                             const float* par) {
   constexpr int TM = C::TM, TN = C::TN;
   constexpr int ES = YT == I8QL_BF16 ? 2 : 4;  // output element bytes
   constexpr int PER = 16 / ES;                  // output elements per 16-byte store
@@ -513,8 +553,13 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t c = c0 + j * 32 + lane % 32;
-      sw[j] = GS ? 1.0f : w_scale[c < n ? c : n - 1];
-      bj[j] = BIAS ? bias[c < n ? c : n - 1] : 0.0f;
+      if constexpr (PAR) {
+        sw[j] = GS ? 1.0f : par[C::PAR_RM + j * 32 + lane % 32];
+        bj[j] = BIAS ? par[C::PAR_RM + C::PAR_RN + j * 32 + lane % 32] : 0.0f;
+      } else {
+        sw[j] = GS ? 1.0f : w_scale[c < n ? c : n - 1];
+        bj[j] = BIAS ? bias[c < n ? c : n - 1] : 0.0f;
+      }
     }
   }
 #pragma unroll
@@ -523,8 +568,12 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[C::TM][C::TN], in
     if constexpr (YT != I8QL_I32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = r0 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-        sx[r] = x_scale[row < m ? row : m - 1];
+        if constexpr (PAR) {
+          sx[r] = par[i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4];
+        } else {
+          const int64_t row = r0 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+          sx[r] = x_scale[row < m ? row : m - 1];
+        }
       }
     }
 #pragma unroll
@@ -639,18 +688,21 @@ __device__ __forceinline__ void epilogue_regs(const v16i (&acc)[C::TM][C::TN], i
 // The fused epilogue of a wavefront's accumulators: through LDS with 16-byte stores when the
 // output allows it, else from registers.  `scr` is this wavefront's LDS scratch; the caller
 // has made sure no wavefront still reads the LDS it overlaps.
-template <class C, int YT, bool GS = false>
+template <class C, int YT, bool GS = false, bool PAR = false>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[C::TM][C::TN], int* scr, int lane,
                                          const float* __restrict__ x_scale,
                                          const float* __restrict__ w_scale,
                                          const float* __restrict__ bias, void* y, int64_t m,
-                                         int64_t n, int64_t r0, int64_t c0) {
+                                         int64_t n, int64_t r0, int64_t c0,
+                                         const float* par = nullptr) {
   constexpr int kES = YT == I8QL_BF16 ? 2 : 4;
   if (n % (16 / kES) == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
     if (bias)
-      epilogue_lds<C, YT, GS, true>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+      epilogue_lds<C, YT, GS, true, PAR>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0,
+                                         c0, par);
     else
-      epilogue_lds<C, YT, GS, false>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
+      epilogue_lds<C, YT, GS, false, PAR>(acc, scr, lane, x_scale, w_scale, bias, y, m, n, r0,
+                                          c0, par);
   } else {
     epilogue_regs<C, YT, GS>(acc, lane, x_scale, w_scale, bias, y, m, n, r0, c0);
   }
@@ -743,6 +795,18 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
         for (int r = 0; r < 16; ++r) gs.facc[i][j][r] = 0.0f;
   }
 
+  // the epilogue's parameters, copied to LDS past the stages before any step's loads (where
+  // they fit: PARAMS), so that the epilogue does not wait for a memory round trip; the first
+  // k-group runs the epilogue
+  constexpr bool PARAMS = C::params_fit(C::LDS_BYTES);
+  float* const par = PARAMS ? reinterpret_cast<float*>(lds_all + C::LDS_BYTES) + wave * C::PAR_WORDS
+                            : nullptr;
+  if constexpr (PARAMS) {
+    if (group == 0)
+      epi_params<C, YT, GS>(par, lane, x_scale, w_scale, bias, m, n, m0 + wm * C::WTM,
+                            n0 + wn * C::WTN);
+  }
+
   // steps issued ahead of the first: all stages, but with 3 or more stages the last one is
   // filled during step 0
   constexpr int kAhead = STAGES >= 3 ? STAGES - 1 : STAGES;
@@ -833,8 +897,10 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void w8a8_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     bare_barrier();
   }
-  epilogue<C, YT, GS>(acc, reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes),
-                      lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+  epilogue<C, YT, GS, PARAMS>(acc,
+                              reinterpret_cast<int*>(lds_all + C::RED_BYTES + wave * kScrBytes),
+                              lane, x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM,
+                              n0 + wn * C::WTN, par);
 }
 
 // ---- persistent variant (two stages of both operands, one k-group) ---------------------
@@ -1287,6 +1353,12 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_split(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   // prologue: A0 B0, then B1 A1 B2 (B1 before A1, so that A1 landing implies B1 has)
+  constexpr bool PARAMS = C::params_fit(P::LDS_BYTES);
+  float* const par = PARAMS ? reinterpret_cast<float*>(lds_all + P::LDS_BYTES) + wave * C::PAR_WORDS
+                            : nullptr;
+  if constexpr (PARAMS)
+    epi_params<C, YT, false>(par, lane, x_scale, w_scale, bias, m, n, m0 + wm * C::WTM,
+                             n0 + wn * C::WTN);
   issue_rows<C, 0, P::LA>(aslots, src, col, dst, 0, k);
   issue_rows<C, P::LA, C::LOADS>(bslots, src, col, dst, 0, k);
   if (ksteps > 1) {
@@ -1358,8 +1430,9 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel_split(
   // every wavefront is done reading the slots before any scratch is written
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   bare_barrier();
-  epilogue<C, YT>(acc, reinterpret_cast<int*>(lds_all + wave * kScrBytes), lane, x_scale,
-                  w_scale, bias, y, m, n, m0 + wm * C::WTM, n0 + wn * C::WTN);
+  epilogue<C, YT, false, PARAMS>(acc, reinterpret_cast<int*>(lds_all + wave * kScrBytes), lane,
+                                 x_scale, w_scale, bias, y, m, n, m0 + wm * C::WTM,
+                                 n0 + wn * C::WTN, par);
 }
 
 template <int BM, int BN, int BK, int YT, int WM, int WN>
@@ -1369,11 +1442,12 @@ hipError_t launch_split(const int8_t* xq, const float* x_scale, const int8_t* wq
   using C = Cfg<BM, BN, BK, 2, 1, WM, WN>;
   using P = SplitStages<C>;
   constexpr auto kern = w8a8_kernel_split<BM, BN, BK, WM, WN, YT>;
-  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(P::LDS_BYTES));
+  constexpr size_t kLds = C::params_fit(P::LDS_BYTES) ? P::LDS_BYTES + C::PAR_BYTES : P::LDS_BYTES;
+  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(kLds));
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), P::LDS_BYTES,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), kLds,
                      stream, xq, x_scale, wq, w_scale, bias, y, m, n, k);
   return hipGetLastError();
 }
@@ -1385,11 +1459,13 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       int64_t k, int splits, int* ws, hipStream_t stream) {
   using C = Cfg<BM, BN, BK, STAGES, KS, WM, WN, GS>;
   constexpr auto kern = w8a8_kernel<BM, BN, BK, STAGES, KS, WM, WN, YT, XS, GS>;
-  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(C::LDS_BYTES));
+  // (the parameter table past the stages where it fits, as the kernel decides)
+  constexpr size_t kLds = C::params_fit(C::LDS_BYTES) ? C::LDS_BYTES + C::PAR_BYTES : C::LDS_BYTES;
+  const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(kLds));
   if (e != hipSuccess) return e;
   const int64_t units = ((m + BM - 1) / BM) * ((n + BN - 1) / BN) * splits;
   const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), C::LDS_BYTES,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(C::THREADS), kLds,
                      stream, xq, x_scale, wq, w_scale, bias, y, m, n, k, splits, ws);
   return hipGetLastError();
 }
