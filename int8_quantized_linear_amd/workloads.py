@@ -120,6 +120,11 @@ def moe_weights(g: np.random.Generator, n: int, k: int,
     return (g.standard_normal((experts, n, k), dtype=np.float32) * np.float32(0.02))
 
 
+def norm_weight(g: np.random.Generator, k: int, std: float = 0.1) -> np.ndarray:
+    """[k] float32 RMS-norm weights ~ 1 + N(0, std^2), to be cast to bf16 by the caller."""
+    return (np.float32(1.0) + g.standard_normal(k, dtype=np.float32) * np.float32(std))
+
+
 def router_logits(g: np.random.Generator, t: int, routed: int = MOE_ROUTED) -> np.ndarray:
     """[t, routed] float32 router logits ~ N(0, 1): independent and identically distributed,
     so the top-k experts are uniform over the routed ones, as the uniform-random expert ids

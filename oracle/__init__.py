@@ -74,6 +74,8 @@ class Oracle:
         lib.ref_w8a16_grouped_scales.restype = None
         lib.ref_w8a8_grouped_scales.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ref_w8a8_grouped_scales.restype = None
+        lib.ref_rmsnorm.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _I64, _P, _P]
+        lib.ref_rmsnorm.restype = None
         lib.ref_set_threads.argtypes = [ctypes.c_int]
         lib.ref_get_threads.restype = ctypes.c_int
         self.lib = lib
@@ -247,6 +249,33 @@ class Oracle:
         y = np.empty((t, n), np.float64)
         self.lib.ref_moe_combine(self._ptr(dd), self._ptr(w), t, topk, n, self._ptr(y))
         return y
+
+    def rmsnorm(self, x_bf16_bits, gamma_bf16_bits, eps: float, residual_bf16_bits=None):
+        """RMS normalization of bf16 rows (reading in ``ref.c``).
+
+        Returns ``h`` (uint16 bf16 bits, [m, k]) and, with a residual, the updated residual
+        ``bf16(x + residual)`` as well: ``(h, res_out)``; ``res_out`` is None without one.
+        """
+        x = np.ascontiguousarray(x_bf16_bits, np.uint16)
+        g = np.ascontiguousarray(gamma_bf16_bits, np.uint16)
+        m, k = x.shape
+        assert g.shape == (k,)
+        res = None if residual_bf16_bits is None else np.ascontiguousarray(residual_bf16_bits,
+                                                                           np.uint16)
+        assert res is None or res.shape == (m, k)
+        h = np.empty((m, k), np.uint16)
+        res_out = None if res is None else np.empty((m, k), np.uint16)
+        self.lib.ref_rmsnorm(self._ptr(x), self._ptr(res), self._ptr(g), float(eps), m, k,
+                             self._ptr(res_out), self._ptr(h))
+        return h, res_out
+
+    def rmsnorm_quantize(self, x_bf16_bits, gamma_bf16_bits, eps: float,
+                         residual_bf16_bits=None):
+        """Per-token int8 quantization of the RMS-normalized rows: the row quantizer applied
+        to ``rmsnorm``'s bf16 output.  Returns ``(q, scale, res_out)``."""
+        h, res_out = self.rmsnorm(x_bf16_bits, gamma_bf16_bits, eps, residual_bf16_bits)
+        q, s = self.quantize_rows(h, "bf16")
+        return q, s, res_out
 
 
 _DEFAULT: Oracle | None = None

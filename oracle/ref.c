@@ -405,3 +405,57 @@ void ref_w8a8_grouped_scales(const int8_t* xq, const float* x_scale, const int8_
     }
   }
 }
+
+/* ---- the norm that produces a projection's input ------------------------------------- */
+
+/* Round a float32 to the nearest bfloat16, ties to the one whose last bit is zero (finite
+ * inputs; the result keeps the upper 16 bits). */
+static uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  const uint32_t low = u & 0xffffu;
+  uint32_t hi = u >> 16;
+  if (low > 0x8000u || (low == 0x8000u && (hi & 1u))) hi += 1u;
+  return (uint16_t)hi;
+}
+
+/*
+ * RMS normalization of bfloat16 rows, the step whose output a decoder layer quantizes per
+ * token before its q/k/v and gate/up products (dynamic per-token activation quantization:
+ * "feat(quantization): support compressed-tensors W8A8 and mixed modules", Design and
+ * Supported Execution Scheme, and its Weight footprint section, where normalization
+ * weights stay in higher precision; "Day 6 — Quantize It Yourself", Reading-share post,
+ * fact 2, on the forward-pass work that per-token quantization adds).  No page writes the
+ * norm out; the reading here:
+ *   u = x, or with a residual stream u = bf16(x + residual) (one float32 addition), which is
+ *       also the updated residual;
+ *   S = sum over the row of u^2, in double;  v = fl32(S / k);
+ *   r = fl32(1 / fl32(sqrt(fl32(v + eps))))  (three correctly rounded float32 operations);
+ *   h = bf16(fl32(fl32(u * r) * gamma)).
+ * x, residual: [m, k] bf16 bits (residual may be NULL); gamma: [k] bf16 bits;
+ * res_out: [m, k] (NULL when residual is NULL); h: [m, k] bf16 bits.
+ */
+void ref_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma, float eps,
+                 int64_t m, int64_t k, uint16_t* res_out, uint16_t* h) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    const int64_t base = i * k;
+    double sum_sq = 0.0;
+    for (int64_t c = 0; c < k; ++c) {
+      float u = bf16_to_f32(x[base + c]);
+      if (residual) {
+        const uint16_t ub = f32_to_bf16_bits(u + bf16_to_f32(residual[base + c]));
+        res_out[base + c] = ub;
+        u = bf16_to_f32(ub);
+      }
+      sum_sq += (double)u * (double)u;
+    }
+    const float v = (float)(sum_sq / (double)k);
+    const float r = 1.0f / sqrtf(v + eps);
+    for (int64_t c = 0; c < k; ++c) {
+      const float u = bf16_to_f32(residual ? res_out[base + c] : x[base + c]);
+      const float t = u * r;
+      h[base + c] = f32_to_bf16_bits(t * bf16_to_f32(gamma[c]));
+    }
+  }
+}

@@ -72,6 +72,12 @@ void ref_grouped_w8a16_silu(const uint16_t* x, int x_per_assignment, const int8_
 void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, int64_t n,
                      double* y);
 
+/* RMS normalization (optional residual add) of bf16 rows, output bf16: the producer of a
+ * decoder layer's quantized inputs.  The norm is not on the pages; its reading is stated in
+ * ref.c.  residual and res_out may be NULL (both or neither). */
+void ref_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma, float eps,
+                 int64_t m, int64_t k, uint16_t* res_out, uint16_t* h);
+
 #ifdef __cplusplus
 }
 #endif

@@ -692,3 +692,117 @@ def test_p17_w8a8_group_scales_quantization_error_bound(ref):
              + (H * sxf) * np.abs(qw * swf).sum(axis=1)[None, :]
              + (H * sxf) * (H * swf).sum(axis=1)[None, :])
     assert np.all(np.abs(y - exact) <= bound * (1 + 1e-9) + 1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# P18: the RMS norm that produces a quantized projection's input (reading in oracle/ref.c;
+# pinned against numpy float64 with an explicit bf16 rounding, exact power-of-two rows,
+# scale invariance and torch's own bfloat16 addition)
+
+def bf16_round_f64(v: np.ndarray):
+    """Round float64 values to the bfloat16 grid (normal range), ties to even, and flag the
+    values within 2^-12 of a bfloat16 ulp of a rounding midpoint (ambiguous at float32
+    precision)."""
+    v = np.asarray(v, np.float64)
+    out = np.zeros_like(v)
+    amb = np.zeros(v.shape, bool)
+    nz = v != 0
+    e = np.floor(np.log2(np.abs(v[nz])))
+    ulp = np.exp2(e - 7)
+    q = v[nz] / ulp
+    frac = np.abs(q - np.floor(q) - 0.5)
+    out[nz] = np.rint(q) * ulp
+    amb[nz] = frac < 2.0 ** -12
+    return out, amb
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _norm_case(g, m, k, scale=1.0, residual=False):
+    x = wl.bits16(wl.to_bf16(wl.activations(g, m, k, outlier_frac=0.01) * np.float32(scale)))
+    gamma = wl.bits16(wl.to_bf16(wl.norm_weight(g, k)))
+    res = wl.bits16(wl.to_bf16(wl.activations(g, m, k) * np.float32(scale))) if residual else None
+    return x, gamma, res
+
+
+@pytest.mark.parametrize("m,k,scale,eps,residual", [
+    (64, 4096, 1.0, 1e-6, False), (16, 2560, 1.0, 1e-6, True), (32, 12288, 1.0, 1e-5, True),
+    (8, 1024, 1e-3, 1e-6, False),   # mean square ~ eps: eps changes the result by ~1/sqrt(2)
+    (8, 1024, 3e-4, 1e-6, True), (5, 48, 1.0, 0.0, False)])
+def test_p18_rmsnorm_against_numpy_float64(ref, m, k, scale, eps, residual):
+    g = wl.rng(41)
+    x, gamma, res = _norm_case(g, m, k, scale, residual)
+    h, res_out = ref.rmsnorm(x, gamma, eps, res)
+    if residual:
+        u_bits = wl.bits16(torch_bf16_sum(x, res))
+        np.testing.assert_array_equal(res_out, u_bits)
+    else:
+        assert res_out is None
+        u_bits = x
+    u = bf16_values(u_bits)
+    want = u / np.sqrt(np.mean(u * u, axis=1, keepdims=True) + eps) * bf16_values(gamma)[None]
+    want_bf16, amb = bf16_round_f64(want)
+    got = bf16_values(h)
+    assert amb.mean() < 1e-2
+    np.testing.assert_array_equal(got[~amb], want_bf16[~amb])
+    assert np.all(np.abs(got - want) <= (2.0 ** -8 + 2.0 ** -20) * np.abs(want))
+
+
+def torch_bf16_sum(a_bits, b_bits):
+    """torch's own bfloat16 addition of two bf16 bit-pattern arrays."""
+    import torch
+    a = torch.from_numpy(a_bits.astype(np.int16)).view(torch.bfloat16)
+    b = torch.from_numpy(b_bits.astype(np.int16)).view(torch.bfloat16)
+    return a + b
+
+
+def test_p18_rmsnorm_of_power_of_two_rows_is_gamma(ref):
+    # |u| = 2^j for every element: mean square 4^j exactly, r = 2^-j exactly (eps = 0), so
+    # h = sign(u) * gamma with no rounding at all
+    g = wl.rng(43)
+    m, k = 6, 256
+    gamma = wl.bits16(wl.to_bf16(wl.norm_weight(g, k)))
+    js = np.array([-20, -3, 0, 1, 7, 30], np.float32)
+    signs = np.where(g.random((m, k)) < 0.5, -1.0, 1.0).astype(np.float32)
+    x = wl.bits16(wl.to_bf16(signs * np.exp2(js)[:, None]))
+    h, _ = ref.rmsnorm(x, gamma, 0.0)
+    np.testing.assert_array_equal(bf16_values(h), signs * bf16_values(gamma)[None])
+    # the same through the residual add: x + x = 2x, still a power of two
+    h2, res_out = ref.rmsnorm(x, gamma, 0.0, x)
+    np.testing.assert_array_equal(bf16_values(res_out), 2.0 * bf16_values(x))
+    np.testing.assert_array_equal(h2, h)
+
+
+def test_p18_rmsnorm_scale_invariance_and_zero_rows(ref):
+    g = wl.rng(47)
+    x, gamma, _ = _norm_case(g, 16, 2048)
+    h, _ = ref.rmsnorm(x, gamma, 0.0)
+    for j in (-8, 5):
+        xs = wl.bits16(wl.to_bf16(bf16_values(x).astype(np.float32) * np.float32(2.0 ** j)))
+        np.testing.assert_array_equal(ref.rmsnorm(xs, gamma, 0.0)[0], h)
+    # an all-zero row with eps > 0 normalizes to zeros and quantizes with the zero guard
+    x[3] = 0
+    q, s, _ = ref.rmsnorm_quantize(x, gamma, 1e-6)
+    assert np.all(ref.rmsnorm(x, gamma, 1e-6)[0][3] == 0)
+    assert s[3] == 1.0 and np.all(q[3] == 0)
+
+
+def test_p18_rmsnorm_residual_is_the_normalized_sum(ref):
+    g = wl.rng(53)
+    x, gamma, res = _norm_case(g, 12, 4096, residual=True)
+    h, res_out = ref.rmsnorm(x, gamma, 1e-6, res)
+    h_direct, none = ref.rmsnorm(res_out, gamma, 1e-6)
+    assert none is None
+    np.testing.assert_array_equal(h, h_direct)
+    # columns permuted together with gamma permute the output (the sum of squares is
+    # order-free at double precision here)
+    perm = g.permutation(4096)
+    hp, _ = ref.rmsnorm(x[:, perm], gamma[perm], 1e-6, res[:, perm])
+    np.testing.assert_array_equal(hp, h[:, perm])
+    # the fused quantization is the row quantizer on the normalized rows
+    q, s, _ = ref.rmsnorm_quantize(x, gamma, 1e-6, res)
+    q2, s2 = ref.quantize_rows(h, "bf16")
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(s, s2)
