@@ -878,11 +878,56 @@ def section_weight_quant(torch, i8, wl, dev, args, result):
     log(f"[weight_quant] {gbs:.0f} GB/s")
 
 
+def section_norm_quant(torch, i8, wl, dev, args, result):
+    """The per-token quantizer fused into the RMS norm that produces a projection's input
+    (with the residual add), against the same norm writing bf16 followed by the quantizer,
+    at the decoder layers' normed inputs: hidden 4096 at 4096 and 16384 tokens (8B), hidden
+    2560 at 128, 512 and 2048 tokens (4B).  Inputs rotate over >= ROTATE_BYTES."""
+    out = {"what": "rmsnorm_quantize_per_token_int8 (norm + residual add + per-token int8 in "
+                   "one pass) vs rmsnorm_bf16 then quantize_per_token_int8; algorithmic bytes: "
+                   "x, residual read and written, gamma, codes and scales (the unfused pair "
+                   "also writes and reads the bf16 norm output)", "per_shape": []}
+    g = wl.rng(77)
+    for label, m, k in (("8B", 16384, 4096), ("8B", 4096, 4096), ("4B", 2048, 2560),
+                        ("4B", 512, 2560), ("4B", 128, 2560)):
+        copies = int(min(1024, max(1, -(-ROTATE_BYTES // (m * k * 4)))))
+        x0 = wl.to_bf16(wl.activations(g, m, k, outlier_frac=0.01)).to(dev)
+        r0 = wl.to_bf16(wl.activations(g, m, k)).to(dev)
+        xs = [x0.clone() for _ in range(copies)]
+        rs = [r0.clone() for _ in range(copies)]
+        gamma = wl.to_bf16(wl.norm_weight(g, k)).to(dev)
+        q = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sc = torch.empty((m,), dtype=torch.float32, device=dev)
+        h = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+        reps = max(copies, 20)
+
+        def fused(i):
+            i8.rmsnorm_quantize_per_token_int8(xs[i % copies], gamma, 1e-6, rs[i % copies],
+                                               q_out=q, scale_out=sc)
+
+        def unfused(i):
+            i8.rmsnorm_bf16(xs[i % copies], gamma, 1e-6, rs[i % copies], y_out=h)
+            i8.quantize_per_token_int8(h, q_out=q, scale_out=sc)
+
+        t_f = per_call(torch, fused, reps)
+        t_u = per_call(torch, unfused, reps)
+        b_f = m * k * (2 + 2 + 2 + 1) + 4 * m + 2 * k
+        b_u = b_f + m * k * (2 + 2)
+        out["per_shape"].append({"model": label, "m": m, "k": k, "fused_us": t_f * 1e6,
+                                 "unfused_us": t_u * 1e6, "fused_GBs": b_f / t_f / 1e9,
+                                 "fused_frac_hbm": b_f / t_f / 1e9 / PEAK_HBM_GBS,
+                                 "unfused_GBs": b_u / t_u / 1e9, "saved_us": (t_u - t_f) * 1e6})
+        log(f"[norm_quant] {label} {m}x{k}: fused {t_f * 1e6:.1f} us "
+            f"({b_f / t_f / 1e9:.0f} GB/s), norm + quantizer {t_u * 1e6:.1f} us")
+        del xs, rs, x0, r0
+    result["norm_quant"] = out
+
+
 SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DEFAULT
     "step": section_step, "prefill_8b_m4096": section_prefill_8b_m4096,
     "prefill_8b_g128": section_prefill_8b_g128,
     "prefill_4b": section_prefill_4b, "decode": section_decode, "moe": section_moe,
-    "weight_quant": section_weight_quant,
+    "weight_quant": section_weight_quant, "norm_quant": section_norm_quant,
     # hardware-counter runs only (eager launches, nothing timed)
     "counters": section_counters, "counters_4b": section_counters_4b,
     "counters_decode": section_counters_decode,
@@ -890,7 +935,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters_moe": section_counters_moe,
 }
 DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
-           "weight_quant")
+           "weight_quant,norm_quant")
 
 
 def main():

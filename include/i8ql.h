@@ -133,6 +133,52 @@ i8ql_status quantize_per_token_int8_multi(const i8ql_quant_job* jobs, int count,
                                           i8ql_dtype x_dtype, void* stream);
 
 /*
+ * rmsnorm_quantize_per_token_int8 — the per-token int8 quantization of a projection's input
+ * fused into the RMS norm that produces it, so the activations make one trip through HBM
+ * as int8 codes instead of a bf16 write and read before the quantizer.
+ *
+ * Defines: [W8A8] "Design and Supported Execution Scheme" (dynamic symmetric INT8 per-token
+ * input activations) and its "Weight footprint" section (normalization weights stay in
+ * higher precision); [Day6] "Reading-share post" fact 2 (the per-token scale is extra work
+ * of every forward pass).  The norm is not written out on the pages; the reading used, per
+ * row i of k elements (bf16 inputs widened exactly to float32):
+ *   u = x[i, :], or with a residual stream u = bf16(x[i, :] + residual[i, :]) (one float32
+ *       addition rounded to nearest even), which is also written back to residual[i, :];
+ *   S = sum_j u_j^2 in float64;  v = fl32(S / k);
+ *   r = fl32(1 / fl32(sqrt(fl32(v + eps))))  (correctly rounded float32 operations);
+ *   h_j = bf16(fl32(fl32(u_j * r) * gamma[j]));
+ * then the row rule of quantize_per_channel_int8 on h: scale_out[i], q_out[i, :].  The
+ * codes and scales are bitwise those of rmsnorm_bf16 followed by quantize_per_token_int8.
+ * (The float64 sum makes the mean independent of the summation order except within about
+ * 2^-50 of a float32 rounding midpoint.)
+ *
+ * x          device, [m, k] bf16, 16-byte aligned.
+ * residual   device, [m, k] bf16, 16-byte aligned, read and overwritten with u; or NULL.
+ *            Must not overlap x or the outputs.
+ * gamma      device, [k] bf16 norm weights, 16-byte aligned.
+ * eps        > 0 and finite.
+ * q_out      device, [m, k] int8, 8-byte aligned.   scale_out  device, [m] float32.
+ * m >= 0; 8 <= k <= I8QL_NORM_MAX_K with k % 8 == 0.
+ * Errors: NULL x, gamma, q_out or scale_out -> I8QL_ERR_NULL; m < 0, k < 1, k % 8 != 0 or
+ * k > I8QL_NORM_MAX_K -> I8QL_ERR_SHAPE; eps not finite or <= 0 -> I8QL_ERR_ARG; alignment ->
+ * I8QL_ERR_ALIGN.
+ */
+#define I8QL_NORM_MAX_K 24576
+i8ql_status rmsnorm_quantize_per_token_int8(const void* x, void* residual, const void* gamma,
+                                            float eps, int64_t m, int64_t k, int8_t* q_out,
+                                            float* scale_out, void* stream);
+
+/*
+ * rmsnorm_bf16 — the same RMS norm (and residual update) writing h as bf16 y_out [m, k]
+ * (16-byte aligned, must not overlap the inputs): the unfused producer, whose output
+ * quantize_per_token_int8 turns into exactly the codes and scales of
+ * rmsnorm_quantize_per_token_int8.  Arguments and errors as there (y_out in place of q_out
+ * and scale_out).
+ */
+i8ql_status rmsnorm_bf16(const void* x, void* residual, const void* gamma, float eps, int64_t m,
+                         int64_t k, void* y_out, void* stream);
+
+/*
  * w8a8_gemm — int8 x int8 GEMM with int32 accumulation and a fused scale epilogue.
  *
  * Defines: [W8A8] "Design and Supported Execution Scheme" (per-channel int8 weights,

@@ -25,7 +25,8 @@ EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8",
            "w8a8_gemm_with_config", "w8a8_gemm_choose_plan", "w8a8_gemm_workspace_size",
            "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "w8a8_gemm_g128",
            "w8a8_gemm_g128_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
-           "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128", "i8ql_status_string",
+           "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128",
+           "rmsnorm_quantize_per_token_int8", "rmsnorm_bf16", "i8ql_status_string",
            "i8ql_last_hip_error")
 GROUP_SIZE = 128  # I8QL_GROUP_SIZE
 ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
@@ -34,6 +35,7 @@ W8A8_MAX_SPLITS = 8  # I8QL_W8A8_MAX_SPLITS
 W8A8_SPLIT_MAX_TILES = 4096  # I8QL_W8A8_SPLIT_MAX_TILES
 W8A8_SCRATCH_BYTES = 32 << 20  # I8QL_W8A8_SCRATCH_BYTES
 QUANT_MAX_JOBS = 8  # I8QL_QUANT_MAX_JOBS
+NORM_MAX_K = 24576  # I8QL_NORM_MAX_K
 
 
 class QuantJob(ctypes.Structure):
@@ -103,6 +105,11 @@ def load_library(path: str = LIB_PATH):
         lib.moe_route_topk.restype = I
         lib.moe_combine.argtypes = [P, I, P, I64, I64, I64, P, I, P]
         lib.moe_combine.restype = I
+        lib.rmsnorm_quantize_per_token_int8.argtypes = [P, P, P, ctypes.c_float, I64, I64, P,
+                                                         P, P]
+        lib.rmsnorm_quantize_per_token_int8.restype = I
+        lib.rmsnorm_bf16.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P]
+        lib.rmsnorm_bf16.restype = I
         lib.i8ql_status_string.argtypes = [I]
         lib.i8ql_status_string.restype = ctypes.c_char_p
         lib.i8ql_last_hip_error.argtypes = []
@@ -165,6 +172,53 @@ def quantize_per_channel_int8(w: torch.Tensor, q_out=None, scale_out=None):
 def quantize_per_token_int8(x: torch.Tensor, q_out=None, scale_out=None):
     """Dynamic per-token symmetric int8: ``x`` [M, K] -> (q int8 [M, K], scale fp32 [M])."""
     return _quantize("quantize_per_token_int8", x, q_out, scale_out)
+
+
+def _norm_args(x, gamma, residual):
+    _check(x, "x", (torch.bfloat16,), 2)
+    m, k = x.shape
+    _check(gamma, "gamma", (torch.bfloat16,), 1, x.device)
+    if gamma.shape[0] != k:
+        raise ValueError(f"gamma has {gamma.shape[0]} elements, x has {k} columns")
+    if residual is not None:
+        _check(residual, "residual", (torch.bfloat16,), 2, x.device)
+        if tuple(residual.shape) != (m, k):
+            raise ValueError("residual must have the shape of x")
+    return m, k
+
+
+def rmsnorm_quantize_per_token_int8(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                                    residual: torch.Tensor | None = None, q_out=None,
+                                    scale_out=None):
+    """RMS norm of bf16 rows ``x`` [M, K] with weights ``gamma`` [K] (after adding
+    ``residual`` in place, if given) fused with the per-token int8 quantization of the
+    result: (q int8 [M, K], scale fp32 [M]).  ``residual`` is overwritten with x + residual."""
+    m, k = _norm_args(x, gamma, residual)
+    q = q_out if q_out is not None else torch.empty((m, k), dtype=torch.int8, device=x.device)
+    s = scale_out if scale_out is not None else torch.empty((m,), dtype=torch.float32,
+                                                            device=x.device)
+    _check(q, "q_out", (torch.int8,), 2, x.device)
+    _check(s, "scale_out", (torch.float32,), 1, x.device)
+    if tuple(q.shape) != (m, k) or tuple(s.shape) != (m,):
+        raise ValueError("output shapes do not match the input")
+    with torch.cuda.device(x.device):
+        _call("rmsnorm_quantize_per_token_int8", _ptr(x), _ptr(residual), _ptr(gamma),
+              float(eps), m, k, _ptr(q), _ptr(s), _stream(x.device))
+    return q, s
+
+
+def rmsnorm_bf16(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                 residual: torch.Tensor | None = None, y_out=None):
+    """The same RMS norm written as bf16 [M, K] (the unfused producer)."""
+    m, k = _norm_args(x, gamma, residual)
+    y = y_out if y_out is not None else torch.empty((m, k), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y_out", (torch.bfloat16,), 2, x.device)
+    if tuple(y.shape) != (m, k):
+        raise ValueError("y_out must have the shape of x")
+    with torch.cuda.device(x.device):
+        _call("rmsnorm_bf16", _ptr(x), _ptr(residual), _ptr(gamma), float(eps), m, k, _ptr(y),
+              _stream(x.device))
+    return y
 
 
 def quantize_per_token_int8_multi(xs, outs=None):

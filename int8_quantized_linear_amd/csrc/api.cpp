@@ -61,6 +61,21 @@ i8ql_status quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t
                                                static_cast<hipStream_t>(stream)));
 }
 
+// The RMS norm entry points: quantized (q and scale) or bf16 (h) output.
+i8ql_status rmsnorm(const void* x, void* residual, const void* gamma, float eps, int64_t m,
+                    int64_t k, int8_t* q, float* scale, void* h, void* stream) {
+  if (m < 0 || k < 1 || k % 8 != 0 || k > I8QL_NORM_MAX_K) return I8QL_ERR_SHAPE;
+  if (!mul_ok(m, k) || m > kMaxGridX) return I8QL_ERR_SHAPE;
+  if (!(eps > 0.0f) || !(eps <= 3.4028234663852886e38f)) return I8QL_ERR_ARG;
+  if (m == 0) return I8QL_OK;
+  if (!x || !gamma || (h ? false : (!q || !scale))) return I8QL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+      (h && !aligned(h, 16)) || (q && !aligned(q, 8)) || (scale && !aligned(scale, 4)))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_rmsnorm(x, residual, gamma, eps, m, k, q, scale, h,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +110,17 @@ i8ql_status quantize_per_token_int8_multi(const i8ql_quant_job* jobs, int count,
   }
   return hip_status(i8ql::launch_quantize_rows_multi(jobs, count, x_dtype,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+i8ql_status rmsnorm_quantize_per_token_int8(const void* x, void* residual, const void* gamma,
+                                            float eps, int64_t m, int64_t k, int8_t* q_out,
+                                            float* scale_out, void* stream) {
+  return rmsnorm(x, residual, gamma, eps, m, k, q_out, scale_out, nullptr, stream);
+}
+
+i8ql_status rmsnorm_bf16(const void* x, void* residual, const void* gamma, float eps, int64_t m,
+                         int64_t k, void* y_out, void* stream) {
+  return rmsnorm(x, residual, gamma, eps, m, k, nullptr, nullptr, y_out, stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,13 @@ hipError_t allow_dynamic_lds(int bytes) {
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,
                                 int8_t* q, float* scale, hipStream_t stream);
 
+// RMS norm of bf16 rows (optional residual add, stored back) fused with the per-token int8
+// quantization (q and scale non-NULL), or written as bf16 rows h (q NULL); validated:
+// k % 8 == 0, k <= I8QL_NORM_MAX_K, 16-byte aligned rows.
+hipError_t launch_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
+                         int64_t rows, int64_t k, int8_t* q, float* scale, void* h,
+                         hipStream_t stream);
+
 // Several matrices (validated for the vector path) in one launch.
 hipError_t launch_quantize_rows_multi(const i8ql_quant_job* jobs, int count, i8ql_dtype dtype,
                                       hipStream_t stream);

@@ -382,6 +382,193 @@ __global__ __launch_bounds__(256) void quantize_groups128_kernel(const uint8_t* 
   if (threadIdx.x % 16 == 0) scale[e / 128] = s == 0.0f ? 1.0f : s;
 }
 
+// ---- RMS norm fused with the per-token quantization ----------------------------------
+// The producer of a decoder layer's q/k/v and gate/up inputs is an RMS norm of the residual
+// stream.  Quantizing inside it writes the int8 codes (1 byte per element) where a separate
+// quantizer would first write the bf16 norm output and read it back (2 + 2 bytes): dynamic
+// per-token activation quantization ("feat(quantization): support compressed-tensors W8A8
+// and mixed modules", Design and Supported Execution Scheme) then costs no extra pass over
+// the activations ("Day 6 — Quantize It Yourself", Reading-share post, fact 2, on the work
+// it adds to the forward pass).  The norm itself is not on the pages; the reading:
+//   u = x, or u = bf16(x + residual) (one float32 addition), also stored as the new residual;
+//   S = sum of u^2 in float64 (each square is exact, so the sum carries about 2^-50 relative
+//   error whatever its order and rounds to the same float32 mean as any other order except
+//   within that distance of a rounding midpoint);  v = fl32(S / k);
+//   r = fl32(1 / fl32(sqrt(fl32(v + eps))));   h = bf16(fl32(fl32(u * r) * gamma));
+// then the row rule above on h, which is bitwise what quantize_rows gives for the bf16 norm
+// output.  Layout as the row quantizer: W wavefronts per row, every chunk of the row (and of
+// gamma, and of the residual) loaded before any is used and kept in registers, rows of up to
+// kNormChunks * 64 * W chunks of 8 elements.
+constexpr int kNormChunks = 12;
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {  // finite f
+  uint32_t b = __float_as_uint(f);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+}
+
+// Sum over the 64 lanes in float64 (a butterfly: every lane ends with the same value).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <int W, bool QUANT, bool RES>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void rmsnorm_rows_kernel(
+    const uint4* __restrict__ x, uint4* __restrict__ res, const uint4* __restrict__ gamma,
+    float eps, int64_t rows, int64_t k, int8_t* __restrict__ q, float* __restrict__ scale,
+    uint4* __restrict__ h_out) {
+  constexpr int T = kWave * W;  // threads per row
+  __shared__ double wsum[kRowsPerBlock];
+  __shared__ float wmax[kRowsPerBlock];
+  const int t = threadIdx.x % T;
+  const int slot = threadIdx.x / T;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kRowsPerBlock / W) + slot;
+  const bool live = row < rows;  // a dead row still joins the barriers
+  const int64_t rr = live ? row : rows - 1;
+  const int64_t chunks = k / 8;
+  const int64_t base = rr * chunks;
+
+  // every load in flight first (chunks past the row end re-read its last chunk: never used)
+  uint4 u[kNormChunks], gm[kNormChunks], rv[kNormChunks];
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (static_cast<int64_t>(i) * T < chunks) {
+      const int64_t c0 = t + static_cast<int64_t>(i) * T;
+      const int64_t c = c0 < chunks ? c0 : chunks - 1;
+      u[i] = x[base + c];
+      if constexpr (RES) rv[i] = res[base + c];
+      gm[i] = gamma[c];
+    }
+  }
+  // residual add (stored back as the new residual) and the float64 sum of squares
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (static_cast<int64_t>(i) * T < chunks) {
+      const int64_t c0 = t + static_cast<int64_t>(i) * T;
+      float f[8];
+      widen_chunk<I8QL_BF16>(u[i], f);
+      if constexpr (RES) {
+        float r[8];
+        widen_chunk<I8QL_BF16>(rv[i], r);
+        u[i] = make_uint4(bf16_pack(f[0] + r[0], f[1] + r[1]), bf16_pack(f[2] + r[2], f[3] + r[3]),
+                          bf16_pack(f[4] + r[4], f[5] + r[5]), bf16_pack(f[6] + r[6], f[7] + r[7]));
+        widen_chunk<I8QL_BF16>(u[i], f);
+        if (live && c0 < chunks) res[base + c0] = u[i];
+      }
+      if (c0 < chunks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double d = static_cast<double>(f[e]);
+          ss += d * d;  // exact square; fused or not, the same sum
+        }
+      }
+    }
+  }
+  ss = wave_sum_f64(ss);
+  if constexpr (W > 1) {
+    if (threadIdx.x % kWave == 0) wsum[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    ss = wsum[slot * W];
+#pragma unroll
+    for (int w = 1; w < W; ++w) ss += wsum[slot * W + w];
+  }
+  const float v = static_cast<float>(ss / static_cast<double>(k));
+  const float rs = 1.0f / sqrtf(v + eps);
+
+  // h = bf16((u * r) * gamma), kept in u; its row maximum
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (static_cast<int64_t>(i) * T < chunks) {
+      float f[8], g[8];
+      widen_chunk<I8QL_BF16>(u[i], f);
+      widen_chunk<I8QL_BF16>(gm[i], g);
+      float hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (f[e] * rs) * g[e];
+      u[i] = make_uint4(bf16_pack(hv[0], hv[1]), bf16_pack(hv[2], hv[3]),
+                        bf16_pack(hv[4], hv[5]), bf16_pack(hv[6], hv[7]));
+      if constexpr (QUANT) {
+        widen_chunk<I8QL_BF16>(u[i], f);  // (re-read clamped chunks too: harmless to the max)
+        amax = chunk_absmax(f, 8, amax);
+      } else {
+        const int64_t c0 = t + static_cast<int64_t>(i) * T;
+        if (live && c0 < chunks) h_out[base + c0] = u[i];
+      }
+    }
+  }
+  if constexpr (QUANT) {
+    amax = wave_max(amax);
+    if constexpr (W > 1) {
+      if (threadIdx.x % kWave == 0) wmax[threadIdx.x / kWave] = amax;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < W; ++w) amax = fmaxf(amax, wmax[slot * W + w]);
+    }
+    if (!live) return;
+    const float s = amax / 127.0f;
+    int8_t* dst = q + rr * k;
+    auto emit_all = [&](auto code) {
+#pragma unroll
+      for (int i = 0; i < kNormChunks; ++i) {
+        const int64_t c0 = t + static_cast<int64_t>(i) * T;
+        if (static_cast<int64_t>(i) * T < chunks && c0 < chunks) {
+          float f[8];
+          widen_chunk<I8QL_BF16>(u[i], f);
+          uint32_t p[2];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              w |= (static_cast<uint32_t>(code(f[4 * g2 + b])) & 0xffu) << (8 * b);
+            p[g2] = w;
+          }
+          *reinterpret_cast<uint2*>(dst + c0 * 8) = make_uint2(p[0], p[1]);
+        }
+      }
+    };
+    if (s == 0.0f) {
+      emit_all([](float) { return 0; });
+      if (t == 0) scale[row] = 1.0f;
+      return;
+    }
+    if (s >= 0x1p-64f) {
+      const float y = 1.0f / s;
+      emit_all([&](float a) { return code_from_quotient(quotient_fma(a, s, y)); });
+    } else {
+      emit_all([&](float a) { return code_of(a, s); });
+    }
+    if (t == 0) scale[row] = s;
+  }
+}
+
+template <bool QUANT, bool RES>
+hipError_t launch_rmsnorm_t(const void* x, void* res, const void* gamma, float eps, int64_t rows,
+                            int64_t k, int8_t* q, float* scale, void* h, hipStream_t stream) {
+  const dim3 block(kWave * kRowsPerBlock);
+  const auto* xs = static_cast<const uint4*>(x);
+  auto* rs = static_cast<uint4*>(res);
+  const auto* gs = static_cast<const uint4*>(gamma);
+  auto* hs = static_cast<uint4*>(h);
+  if (four_waves_per_row<I8QL_BF16>(rows, k, rows)) {
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<4, QUANT, RES>), dim3(static_cast<unsigned>(rows)),
+                       block, 0, stream, xs, rs, gs, eps, rows, k, q, scale, hs);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<1, QUANT, RES>),
+                       dim3(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       block, 0, stream, xs, rs, gs, eps, rows, k, q, scale, hs);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_groups128(const void* a, i8ql_dtype dtype, int64_t n, int64_t k,
@@ -447,6 +634,21 @@ hipError_t launch_quantize_rows_multi(const i8ql_quant_job* jobs, int count, i8q
     case I8QL_F16: return launch_multi_dt<I8QL_F16>(jobs, count, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
+                         int64_t rows, int64_t k, int8_t* q, float* scale, void* h,
+                         hipStream_t stream) {
+  if (q) {
+    return residual ? launch_rmsnorm_t<true, true>(x, residual, gamma, eps, rows, k, q, scale,
+                                                   h, stream)
+                    : launch_rmsnorm_t<true, false>(x, residual, gamma, eps, rows, k, q, scale,
+                                                    h, stream);
+  }
+  return residual ? launch_rmsnorm_t<false, true>(x, residual, gamma, eps, rows, k, q, scale, h,
+                                                  stream)
+                  : launch_rmsnorm_t<false, false>(x, residual, gamma, eps, rows, k, q, scale,
+                                                   h, stream);
 }
 
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,

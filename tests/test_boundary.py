@@ -390,6 +390,31 @@ def _gpu_visible():
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="the fake pointers below must never reach a GPU")
+def test_rmsnorm_validation(lib):
+    fq, fb = lib.rmsnorm_quantize_per_token_int8, lib.rmsnorm_bf16
+    for f, outs in ((fq, (A16, A16)), (fb, (A16,))):
+        assert f(A16, NUL, A16, 1e-6, -1, 64, *outs, NUL) == SHAPE
+        assert f(A16, NUL, A16, 1e-6, 4, 0, *outs, NUL) == SHAPE
+        assert f(A16, NUL, A16, 1e-6, 4, 60, *outs, NUL) == SHAPE       # k % 8
+        assert f(A16, NUL, A16, 1e-6, 4, 24576 + 8, *outs, NUL) == SHAPE  # I8QL_NORM_MAX_K
+        assert f(A16, NUL, A16, 0.0, 4, 64, *outs, NUL) == ARG
+        assert f(A16, NUL, A16, -1e-6, 4, 64, *outs, NUL) == ARG
+        assert f(A16, NUL, A16, float("inf"), 4, 64, *outs, NUL) == ARG
+        assert f(A16, NUL, A16, float("nan"), 4, 64, *outs, NUL) == ARG
+        assert f(NUL, NUL, NUL, 1e-6, 0, 64, *[NUL] * len(outs), NUL) == OK  # no rows: no-op
+        assert f(NUL, NUL, A16, 1e-6, 4, 64, *outs, NUL) == NULL
+        assert f(A16, NUL, NUL, 1e-6, 4, 64, *outs, NUL) == NULL
+        assert f(A4, NUL, A16, 1e-6, 4, 64, *outs, NUL) == ALIGN
+        assert f(A16, A4, A16, 1e-6, 4, 64, *outs, NUL) == ALIGN
+        assert f(A16, NUL, A4, 1e-6, 4, 64, *outs, NUL) == ALIGN
+    assert fq(A16, NUL, A16, 1e-6, 4, 64, NUL, A16, NUL) == NULL
+    assert fq(A16, NUL, A16, 1e-6, 4, 64, A16, NUL, NUL) == NULL
+    assert fq(A16, NUL, A16, 1e-6, 4, 64, A4, A16, NUL) == ALIGN      # codes: 8-byte aligned
+    assert fq(A16, NUL, A16, 1e-6, 4, 64, A16, A2, NUL) == ALIGN
+    assert fb(A16, NUL, A16, 1e-6, 4, 64, NUL, NUL) == NULL
+    assert fb(A16, NUL, A16, 1e-6, 4, 64, A4, NUL) == ALIGN
+
+
 def test_valid_calls_without_a_device_report_hip_errors(lib):
     """With no device, a call that passes validation fails at its first HIP call with
     I8QL_ERR_HIP (and a recorded hipError), instead of crashing."""
@@ -413,6 +438,8 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
         lambda: lib.quantize_per_group_int8(A16, BF16, 4, 256, A16, A16, NUL),
         lambda: lib.w8a16_gemm_g128(A16, A16, A16, NUL, A16, BF16, 1, 16, 256, NUL),
         lambda: lib.moe_combine(A16, BF16, A16, 4, 8, 2048, A16, BF16, NUL),
+        lambda: lib.rmsnorm_quantize_per_token_int8(A16, A16, A16, 1e-6, 4, 64, A16, A16, NUL),
+        lambda: lib.rmsnorm_bf16(A16, NUL, A16, 1e-6, 4, 64, A16, NUL),
     ]
     for call in calls:
         assert call() == HIP
