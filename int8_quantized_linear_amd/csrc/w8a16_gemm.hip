@@ -27,6 +27,12 @@ namespace i8ql {
 namespace {
 
 constexpr int kUnroll = 8;  // steps of k whose loads a wavefront keeps in flight
+// The batch a wavefront issues at once: kUnroll steps, or 4 with 12 wavefronts (the longest
+// k), where each wavefront walks its 8 steps in two batches.  Measured on MI355X at M = 1:
+// 4096 x 12288 12.0 instead of 13.5 us; with 4, 8 or 16 wavefronts, or interleaved steps,
+// every decoder shape was as fast or slower.
+template <int WAVES>
+constexpr int batch_steps() { return WAVES == 12 ? 4 : kUnroll; }
 constexpr int kGlobalUnroll = 4;  // the same with activations loaded too (divided by MT)
 constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a function attribute
 constexpr size_t kMaxStageLds = 96 * 1024;  // staged rows up to this much LDS (attribute set)
@@ -101,11 +107,12 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     stage_rows<WAVES>(x + m0 * k, nullptr, 1, rows, k, xs);
     asm volatile("" ::: "memory");  // the weight loads stay behind the copy (wait count below)
     __builtin_amdgcn_sched_barrier(0);
-    v4u w[kUnroll][2];
-    load_weight_batch<kUnroll>(wrow, k, sb, se, w);
+    constexpr int U = batch_steps<WAVES>();
+    v4u w[U][2];
+    load_weight_batch<U>(wrow, k, sb, se, w);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kUnroll, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * U, 0));
     bare_barrier();
     const int64_t pitch = 2 * k + 16;
     const char* xrow[MT];
@@ -119,11 +126,11 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) xb[mt][c] = v4u{0u, 0u, 0u, 0u};
     }
-    mma_batch_lds<MT, kUnroll, GS>(w, xrow, live, xzero, k, sb, se, xb, acc, gs);
-    for (int s = sb + kUnroll; s < se; s += kUnroll) {
-      load_weight_batch<kUnroll>(wrow, k, s, se, w);
+    mma_batch_lds<MT, U, GS>(w, xrow, live, xzero, k, sb, se, xb, acc, gs);
+    for (int s = sb + U; s < se; s += U) {
+      load_weight_batch<U>(wrow, k, s, se, w);
       __builtin_amdgcn_sched_barrier(0);
-      mma_batch_lds<MT, kUnroll, GS>(w, xrow, live, xzero, k, s, se, xb, acc, gs);
+      mma_batch_lds<MT, U, GS>(w, xrow, live, xzero, k, s, se, xb, acc, gs);
     }
   } else {
     const uint16_t* xrow[MT];
@@ -226,10 +233,10 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
 }
 
 // Wavefronts per workgroup: the fewest of 4, 8 and 12 with which each streams at most
-// kUnroll steps of k (all its loads in flight at once; a wave with fewer real steps than
-// kUnroll still issues kUnroll steps of loads, so the count is matched to the steps).  Longer
-// k keeps 12 wavefronts, each walking several batches: 16 wavefronts of 1024 threads would
-// cap the kernel at 128 registers and spill.  One 16-channel tile per workgroup: with N / 16
+// kUnroll steps of k (with 4 or 8, all its loads in flight at once; a wave with fewer real
+// steps than kUnroll still issues kUnroll steps of loads, so the count is matched to the
+// steps).  Longer k keeps 12 wavefronts, each walking several batches of batch_steps: 16
+// wavefronts of 1024 threads would cap the kernel at 128 registers and spill.  One 16-channel tile per workgroup: with N / 16
 // such workgroups the whole weight matrix is in flight in about one occupancy round on 256
 // CUs for the decoder shapes.
 template <int MT, int YT, bool GS>
