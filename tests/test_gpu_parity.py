@@ -256,13 +256,15 @@ def test_w8a8_every_tile_config(ref, dev, config):
 
 
 @pytest.mark.parametrize("m,n,k", [(2100, 8200, 272), (4100, 4104, 256), (2310, 7700, 528),
-                                   (2100, 8196, 400)])
+                                   (2100, 8196, 400), (2100, 8200, 384), (2310, 7700, 1280),
+                                   (4353, 4360, 640)])
 def test_w8a8_persistent_tiles(ref, dev, m, n, k):
     """256 x 256 tiles (configuration 0) with more tiles than compute units, which runs the
     persistent kernel (one workgroup per compute unit walking tiles, the next tile's first
     two k steps loaded during the current tile's last two): ragged edges in m and n, partial
-    and whole last k steps, exactly two k steps, and an N whose float32 rows are whole
-    16-byte chunks but whose bf16 rows are not (bf16 then takes the per-tile kernel)."""
+    and whole last k steps, exactly two and three k steps, tile counts that leave some
+    workgroups one tile fewer, and an N whose float32 rows are whole 16-byte chunks but whose
+    bf16 rows are not (bf16 then takes the per-tile kernel)."""
     assert i8.w8a8_gemm_config_info(0)[:2] == (256, 256)
     assert ((m + 255) // 256) * ((n + 255) // 256) > 256
     print(f"w8a8 persistent 256x256: {m}x{n}x{k}", flush=True)
