@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "w8a16_kernel": "int8_quantized_linear_amd/csrc/w8a16_gemm.hip",
     "grouped_w8a16_kernel": "int8_quantized_linear_amd/csrc/grouped_w8a16.hip",
     "quantize_rows_vec_kernel": "int8_quantized_linear_amd/csrc/quantize_rows.hip",
+    "rmsnorm_rows_kernel": "int8_quantized_linear_amd/csrc/quantize_rows.hip",
 }
 
 
@@ -917,10 +918,44 @@ def section_norm_quant(torch, i8, wl, dev, args, result):
                                  "unfused_us": t_u * 1e6, "fused_GBs": b_f / t_f / 1e9,
                                  "fused_frac_hbm": b_f / t_f / 1e9 / PEAK_HBM_GBS,
                                  "unfused_GBs": b_u / t_u / 1e9, "saved_us": (t_u - t_f) * 1e6})
+        if (m, k) == (16384, 4096):
+            tr = traffic_for("rmsnorm_rows_kernel", NORM_TRAFFIC)
+            out["per_shape"][-1]["traffic_fused_bytes"] = tr
+            out["per_shape"][-1]["algorithmic_fused_bytes"] = b_f
         log(f"[norm_quant] {label} {m}x{k}: fused {t_f * 1e6:.1f} us "
             f"({b_f / t_f / 1e9:.0f} GB/s), norm + quantizer {t_u * 1e6:.1f} us")
         del xs, rs, x0, r0
     result["norm_quant"] = out
+
+
+NORM_TRAFFIC = "RMS norm + residual + per-token int8, 16384x4096"
+
+
+def section_counters_norm(torch, i8, wl, dev, args, result):
+    """Like `counters`, for the RMS norm fused with the per-token quantizer at 16384 x 4096
+    with the residual add: the calibration copy, then four fused launches over rotating
+    inputs, then two of the unfused pair (the norm writing bf16, then the quantizer)."""
+    g = wl.rng(77)
+    m, k = 16384, 4096
+    copies = 4
+    x0 = wl.to_bf16(wl.activations(g, m, k, outlier_frac=0.01)).to(dev)
+    r0 = wl.to_bf16(wl.activations(g, m, k)).to(dev)
+    xs = [x0.clone() for _ in range(copies)]
+    rs = [r0.clone() for _ in range(copies)]
+    gamma = wl.to_bf16(wl.norm_weight(g, k)).to(dev)
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    sc = torch.empty((m,), dtype=torch.float32, device=dev)
+    h = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    calibration_copy(torch, dev)
+    for i in range(copies):
+        i8.rmsnorm_quantize_per_token_int8(xs[i], gamma, 1e-6, rs[i], q_out=q, scale_out=sc)
+    for i in range(2):
+        i8.rmsnorm_bf16(xs[i], gamma, 1e-6, rs[i], y_out=h)
+        i8.quantize_per_token_int8(h, q_out=q, scale_out=sc)
+    torch.cuda.synchronize()
+    result["counters_norm"] = {"workload": NORM_TRAFFIC, "calibration_copy_bytes": CALIB_BYTES,
+                               "fused_launches": copies,
+                               "algorithmic_bytes_fused": m * k * 7 + 4 * m + 2 * k}
 
 
 SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DEFAULT
@@ -932,7 +967,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters": section_counters, "counters_4b": section_counters_4b,
     "counters_decode": section_counters_decode,
     "counters_w8a8_large": section_counters_w8a8_large,
-    "counters_moe": section_counters_moe,
+    "counters_moe": section_counters_moe, "counters_norm": section_counters_norm,
 }
 DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
            "weight_quant,norm_quant")
