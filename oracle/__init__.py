@@ -76,6 +76,10 @@ class Oracle:
         lib.ref_w8a8_grouped_scales.restype = None
         lib.ref_rmsnorm.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _I64, _P, _P]
         lib.ref_rmsnorm.restype = None
+        lib.ref_silu_mul.argtypes = [_P, _I64, _I64, ctypes.c_double, _P, _P, _P]
+        lib.ref_silu_mul.restype = None
+        lib.ref_codes_with_scale.argtypes = [_P, _P, _I64, _I64, _P]
+        lib.ref_codes_with_scale.restype = None
         lib.ref_set_threads.argtypes = [ctypes.c_int]
         lib.ref_get_threads.restype = ctypes.c_int
         self.lib = lib
@@ -276,6 +280,31 @@ class Oracle:
         h, res_out = self.rmsnorm(x_bf16_bits, gamma_bf16_bits, eps, residual_bf16_bits)
         q, s = self.quantize_rows(h, "bf16")
         return q, s, res_out
+
+    def silu_mul(self, gu_bf16_bits, rel: float = 0.0):
+        """SiLU·mul of a gate/up product ``gu`` [m, 2i] (bf16 bits, gate columns first):
+        returns ``(h, other, amb)``: h [m, i] the bf16 nearest to g / (1 + e^-g) * u (double),
+        other the bf16 on the other side of the exact value, amb where the exact value is
+        within ``rel`` of the halfway point between them."""
+        gu = np.ascontiguousarray(gu_bf16_bits, np.uint16)
+        m, i2 = gu.shape
+        assert i2 % 2 == 0
+        i = i2 // 2
+        h = np.empty((m, i), np.uint16)
+        other = np.empty((m, i), np.uint16)
+        amb = np.empty((m, i), np.uint8)
+        self.lib.ref_silu_mul(self._ptr(gu), m, i, float(rel), self._ptr(h), self._ptr(other),
+                              self._ptr(amb))
+        return h, other, amb.astype(bool)
+
+    def codes_with_scale(self, a_bf16_bits, scale):
+        """The row quantizer's code step with given per-row scales (bf16 rows)."""
+        a = np.ascontiguousarray(a_bf16_bits, np.uint16)
+        s = np.ascontiguousarray(scale, np.float32)
+        r, k = a.shape
+        q = np.empty((r, k), np.int8)
+        self.lib.ref_codes_with_scale(self._ptr(a), self._ptr(s), r, k, self._ptr(q))
+        return q
 
 
 _DEFAULT: Oracle | None = None

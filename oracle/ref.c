@@ -459,3 +459,92 @@ void ref_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* ga
     }
   }
 }
+
+/* ---- SiLU·mul that produces the down projection's input --------------------------------- */
+
+/* The two bfloat16 values around a finite double v and whether v is within `rel` (relative)
+ * of the point halfway between them.  near: the bf16 nearest to v (ties to even); other: the
+ * neighbour on the other side of v (equal to near when v is a bf16 value).  Every bf16 value
+ * is a double, and so is every halfway point, so the comparisons are exact. */
+static void bf16_neighbours(double v, double rel, uint16_t* near, uint16_t* other, int* amb) {
+  /* the float nearest to v lies within half a float ulp of v, so the bf16 values that
+   * bracket v are the truncation of that float toward zero and the next one away from zero
+   * (or the truncation and the previous one when the float sits on a bf16 value) */
+  const float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint32_t lo_bits = u & 0xffff0000u; /* toward zero */
+  float lo_f;
+  memcpy(&lo_f, &lo_bits, sizeof lo_f);
+  uint32_t hi_bits = lo_bits + 0x10000u; /* away from zero (same sign) */
+  float hi_f;
+  memcpy(&hi_f, &hi_bits, sizeof hi_f);
+  if ((u & 0xffffu) == 0 && fabs((double)lo_f) > fabs(v)) {
+    /* f is a bf16 value above |v|: the bracket is (previous, f) */
+    hi_bits = lo_bits;
+    hi_f = lo_f;
+    lo_bits = lo_bits - 0x10000u;
+    memcpy(&lo_f, &lo_bits, sizeof lo_f);
+  }
+  const double a = fabs(v), l = fabs((double)lo_f), h = fabs((double)hi_f);
+  const double mid = 0.5 * (l + h); /* exact: l and h differ in the 8th significant bit */
+  uint16_t pick, alt;
+  if (a == l) {
+    pick = (uint16_t)(lo_bits >> 16);
+    alt = pick;
+  } else if (a < mid || (a == mid && ((lo_bits >> 16) & 1u) == 0)) {
+    pick = (uint16_t)(lo_bits >> 16);
+    alt = (uint16_t)(hi_bits >> 16);
+  } else {
+    pick = (uint16_t)(hi_bits >> 16);
+    alt = (uint16_t)(lo_bits >> 16);
+  }
+  *near = pick;
+  *other = alt;
+  *amb = (a != l) && fabs(a - mid) <= rel * a;
+}
+
+/*
+ * SiLU·mul of a gate/up product, the step between a decoder MLP's gate/up projection and its
+ * down projection (the same activation as the mixture-of-experts block's, reading stated
+ * with ref_grouped_w8a16_silu; no page writes it out), written as the bf16 tensor that the
+ * down projection's per-token quantization reads: h = silu(g) * u = g / (1 + e^(-g)) * u in
+ * double, rounded to the nearest bf16 (ties to even).
+ * gu: [m, 2 i] bf16 bits, the gate values in columns [0, i) and the up values in [i, 2 i)
+ * (one GEMM over the stacked gate and up weights); h: [m, i] bf16 bits.  With `other` and
+ * `amb` (both or neither NULL): the bf16 on the other side of the exact value, and 1 where
+ * the exact value lies within `rel` (relative) of the halfway point between the two, i.e.
+ * where a float32 evaluation of the same formula may round to either.
+ */
+void ref_silu_mul(const uint16_t* gu, int64_t m, int64_t i, double rel, uint16_t* h,
+                  uint16_t* other, uint8_t* amb) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t c = 0; c < i; ++c) {
+      const double g = (double)bf16_to_f32(gu[r * 2 * i + c]);
+      const double u = (double)bf16_to_f32(gu[r * 2 * i + i + c]);
+      const double v = g / (1.0 + exp(-g)) * u;
+      uint16_t near, alt;
+      int a;
+      bf16_neighbours(v, rel, &near, &alt, &a);
+      h[r * i + c] = near;
+      if (other) {
+        other[r * i + c] = alt;
+        amb[r * i + c] = (uint8_t)a;
+      }
+    }
+  }
+}
+
+/* Codes of bf16 rows under given per-row scales: clamp(rne(fl32(a / s)), -127, 127), the
+ * code step of the row quantizer with the scale fixed (q: [r, k]). */
+void ref_codes_with_scale(const uint16_t* a, const float* s, int64_t r, int64_t k, int8_t* q) {
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < r; ++row)
+    for (int64_t j = 0; j < k; ++j) {
+      float c = round_half_even(bf16_to_f32(a[row * k + j]) / s[row]);
+      if (c > 127.0f) c = 127.0f;
+      if (c < -127.0f) c = -127.0f;
+      q[row * k + j] = (int8_t)c;
+    }
+}

@@ -78,6 +78,14 @@ void ref_moe_combine(const float* d, const float* w, int64_t t, int64_t topk, in
 void ref_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma, float eps,
                  int64_t m, int64_t k, uint16_t* res_out, uint16_t* h);
 
+/* SiLU·mul of a gate/up product [m, 2i] bf16 (gate columns first), rounded to bf16 h [m, i];
+ * optionally the bf16 on the other side of each exact value and a flag where the exact value
+ * is within rel of the halfway point (reading stated in ref.c). */
+void ref_silu_mul(const uint16_t* gu, int64_t m, int64_t i, double rel, uint16_t* h,
+                  uint16_t* other, uint8_t* amb);
+/* The row quantizer's code step under given scales: clamp(rne(fl32(a / s)), -127, 127). */
+void ref_codes_with_scale(const uint16_t* a, const float* s, int64_t r, int64_t k, int8_t* q);
+
 #ifdef __cplusplus
 }
 #endif

@@ -806,3 +806,72 @@ def test_p18_rmsnorm_residual_is_the_normalized_sum(ref):
     q2, s2 = ref.quantize_rows(h, "bf16")
     np.testing.assert_array_equal(q, q2)
     np.testing.assert_array_equal(s, s2)
+
+
+# ---------------------------------------------------------------------------------------
+# P19: SiLU·mul producing the down projection's input (reading in oracle/ref.c), pinned
+# against a 60-digit decimal evaluation with exact bf16 rounding by rational comparison
+
+def _bf16_nearest_exact(v):
+    """(nearest bf16 as float, the other neighbour, relative distance to the halfway point)
+    of a decimal value, by exact rational arithmetic."""
+    from decimal import Decimal
+    fr = Fraction(v)
+    if fr == 0:
+        return 0.0, 0.0, None
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - 7)           # bf16: 8 significant bits (normal range)
+    lo = (a // ulp) * ulp
+    hi = lo + ulp
+    mid = (lo + hi) / 2
+    if lo == a:
+        return float(sign * lo), float(sign * lo), None
+    if a < mid or (a == mid and (lo / ulp) % 2 == 0):
+        near, other = lo, hi
+    else:
+        near, other = hi, lo
+    return float(sign * near), float(sign * other), float(abs(a - mid) / a)
+
+
+def test_p19_silu_mul_against_high_precision(ref):
+    import decimal
+    from decimal import Decimal
+    decimal.getcontext().prec = 60
+    g = wl.rng(59)
+    n = 1500
+    gate = np.concatenate([g.standard_normal(n - 12).astype(np.float32) * np.float32(4.0),
+                           np.array([0.0, -0.0, 1e-3, -1e-3, 30.0, -30.0, 80.0, -80.0, 0.5,
+                                     -0.5, 7.25, -7.25], np.float32)])
+    up = g.standard_normal(n).astype(np.float32) * np.float32(3.0)
+    gb = wl.bits16(wl.to_bf16(gate))
+    ub = wl.bits16(wl.to_bf16(up))
+    gu = np.concatenate([gb, ub])[None, :]
+    h, other, amb = ref.silu_mul(gu, rel=2.0 ** -17)
+    hv = bf16_values(h[0])
+    ov = bf16_values(other[0])
+    gv, uv = bf16_values(gb), bf16_values(ub)
+    for j in range(n):
+        x = Decimal(float(gv[j]))
+        v = x / (1 + (-x).exp()) * Decimal(float(uv[j]))
+        near, oth, dist = _bf16_nearest_exact(v)
+        assert hv[j] == near, (j, gv[j], uv[j], hv[j], near)
+        if dist is not None:
+            assert ov[j] == oth
+            assert amb[0, j] == (dist <= 2.0 ** -17)
+        else:
+            assert not amb[0, j]
+    # silu(0) * u = 0 and g * u of one sign for a positive gate
+    assert np.all(hv[gv == 0] == 0)
+    pos = gv > 0
+    assert np.all(np.sign(hv[pos]) * np.sign(uv[pos]) >= 0)
+
+
+def test_p19_codes_with_scale_is_the_quantizer_code_step(ref):
+    g = wl.rng(61)
+    a = wl.bits16(wl.to_bf16(wl.activations(g, 40, 1024, outlier_frac=0.01)))
+    q, s = ref.quantize_rows(a, "bf16")
+    np.testing.assert_array_equal(ref.codes_with_scale(a, s), q)
