@@ -928,6 +928,50 @@ def section_norm_quant(torch, i8, wl, dev, args, result):
     result["norm_quant"] = out
 
 
+def section_silu_quant(torch, i8, wl, dev, args, result):
+    """The per-token quantizer fused into the SiLU·mul that produces a down projection's input
+    from the gate/up output, against SiLU·mul writing bf16 followed by the quantizer, at the
+    decoder MLPs' shapes: intermediate 12288 at 4096 and 16384 tokens (8B), 9728 at 128, 512
+    and 2048 tokens (4B).  Inputs rotate over >= ROTATE_BYTES."""
+    out = {"what": "silu_mul_quantize_per_token_int8 (SiLU·mul + per-token int8 in one pass) vs "
+                   "silu_mul_bf16 then quantize_per_token_int8; algorithmic bytes: the gate/up "
+                   "rows read, codes and scales written (the unfused pair also writes and reads "
+                   "the bf16 activation)", "per_shape": []}
+    g = wl.rng(79)
+    for label, m, n in (("8B", 16384, 12288), ("8B", 4096, 12288), ("4B", 2048, 9728),
+                        ("4B", 512, 9728), ("4B", 128, 9728)):
+        copies = int(min(1024, max(1, -(-ROTATE_BYTES // (m * n * 4)))))
+        gate = g.standard_normal((m, n), dtype=np.float32) * np.float32(4.0)
+        up = g.standard_normal((m, n), dtype=np.float32) * np.float32(3.0)
+        g0 = wl.to_bf16(np.concatenate([gate, up], axis=1)).to(dev)
+        del gate, up
+        gus = [g0.clone() for _ in range(copies)]
+        q = torch.empty((m, n), dtype=torch.int8, device=dev)
+        sc = torch.empty((m,), dtype=torch.float32, device=dev)
+        h = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        reps = max(copies, 20)
+
+        def fused(i):
+            i8.silu_mul_quantize_per_token_int8(gus[i % copies], q_out=q, scale_out=sc)
+
+        def unfused(i):
+            i8.silu_mul_bf16(gus[i % copies], h_out=h)
+            i8.quantize_per_token_int8(h, q_out=q, scale_out=sc)
+
+        t_f = per_call(torch, fused, reps)
+        t_u = per_call(torch, unfused, reps)
+        b_f = m * n * (2 + 2 + 1) + 4 * m
+        b_u = b_f + m * n * (2 + 2)
+        out["per_shape"].append({"model": label, "m": m, "n": n, "fused_us": t_f * 1e6,
+                                 "unfused_us": t_u * 1e6, "fused_GBs": b_f / t_f / 1e9,
+                                 "fused_frac_hbm": b_f / t_f / 1e9 / PEAK_HBM_GBS,
+                                 "unfused_GBs": b_u / t_u / 1e9, "saved_us": (t_u - t_f) * 1e6})
+        log(f"[silu_quant] {label} {m}x{n}: fused {t_f * 1e6:.1f} us "
+            f"({b_f / t_f / 1e9:.0f} GB/s), SiLU·mul + quantizer {t_u * 1e6:.1f} us")
+        del gus, g0
+    result["silu_quant"] = out
+
+
 NORM_TRAFFIC = "RMS norm + residual + per-token int8, 16384x4096"
 
 
@@ -963,6 +1007,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "prefill_8b_g128": section_prefill_8b_g128,
     "prefill_4b": section_prefill_4b, "decode": section_decode, "moe": section_moe,
     "weight_quant": section_weight_quant, "norm_quant": section_norm_quant,
+    "silu_quant": section_silu_quant,
     # hardware-counter runs only (eager launches, nothing timed)
     "counters": section_counters, "counters_4b": section_counters_4b,
     "counters_decode": section_counters_decode,
@@ -970,7 +1015,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters_moe": section_counters_moe, "counters_norm": section_counters_norm,
 }
 DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
-           "weight_quant,norm_quant")
+           "weight_quant,norm_quant,silu_quant")
 
 
 def main():

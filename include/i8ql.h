@@ -179,6 +179,40 @@ i8ql_status rmsnorm_bf16(const void* x, void* residual, const void* gamma, float
                          int64_t k, void* y_out, void* stream);
 
 /*
+ * silu_mul_quantize_per_token_int8 — the per-token int8 quantization of a down projection's
+ * input fused into the SiLU·mul that produces it from the gate/up projection's output, so
+ * the activation reaches HBM once, as int8 codes, instead of as bf16 written and read back.
+ *
+ * Defines: [W8A8] "Design and Supported Execution Scheme" (dynamic symmetric INT8 per-token
+ * input activations); [Day6] "Reading-share post" fact 2 (the per-token scale is extra work
+ * of every forward pass).  The activation is the one of the mixture-of-experts block's
+ * grouped_w8a16_silu_gemm (not written out on the pages; reading): per row i and column j,
+ *   h[i, j] = bf16(g * rcp(1 + e^-g) * u),  g = gu[i, j], u = gu[i, n + j] (bf16 widened),
+ * in float32 (in float64 where g < -80 or the nonzero product is below 2^-120 in
+ * magnitude), rounded to nearest even; then the row rule of quantize_per_channel_int8 on h.
+ * The codes and scales are bitwise those of silu_mul_bf16 followed by
+ * quantize_per_token_int8.  (h lies within about 5 float32 ulps of the exact value, so its
+ * bf16 rounding is that of the exact value except within that distance of a halfway point.)
+ *
+ * gu         device, [m, 2n] bf16, 16-byte aligned: the gate values in columns [0, n), the
+ *            up values in [n, 2n) (the output of one GEMM over gate and up weights stacked).
+ * q_out      device, [m, n] int8, 8-byte aligned.   scale_out  device, [m] float32.
+ * m >= 0; 8 <= n <= I8QL_SILU_MAX_N with n % 8 == 0.
+ * Errors: NULL gu, q_out or scale_out -> I8QL_ERR_NULL; m < 0, n < 1, n % 8 != 0 or
+ * n > I8QL_SILU_MAX_N -> I8QL_ERR_SHAPE; alignment -> I8QL_ERR_ALIGN.
+ */
+#define I8QL_SILU_MAX_N 24576
+i8ql_status silu_mul_quantize_per_token_int8(const void* gu, int64_t m, int64_t n,
+                                             int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * silu_mul_bf16 — the same SiLU·mul writing h as bf16 h_out [m, n] (16-byte aligned, must not
+ * overlap gu): the unfused producer, whose output quantize_per_token_int8 turns into exactly
+ * the codes and scales of silu_mul_quantize_per_token_int8.  Arguments and errors as there.
+ */
+i8ql_status silu_mul_bf16(const void* gu, int64_t m, int64_t n, void* h_out, void* stream);
+
+/*
  * w8a8_gemm — int8 x int8 GEMM with int32 accumulation and a fused scale epilogue.
  *
  * Defines: [W8A8] "Design and Supported Execution Scheme" (per-channel int8 weights,

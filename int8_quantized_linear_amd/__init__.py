@@ -4,7 +4,9 @@ Python names match the C ABI of ``include/i8ql.h``.  The HIP library ``libi8ql.s
 on first use (``load_library``); importing the package touches neither the GPU nor HIP.
 """
 from ._binding import (EXPORTS, GROUP_SIZE, NORM_MAX_K, ROUTE_MAX_EXPERTS,  # noqa: F401
-                       ROUTE_MAX_K, rmsnorm_bf16, rmsnorm_quantize_per_token_int8,
+                       ROUTE_MAX_K, SILU_MAX_N, rmsnorm_bf16,
+                       rmsnorm_quantize_per_token_int8, silu_mul_bf16,
+                       silu_mul_quantize_per_token_int8,
                        W8A8_MAX_SPLITS, W8A8_NUM_CONFIGS, W8A8_SCRATCH_BYTES, I8qlError,
                        grouped_w8a16_gemm,
                        grouped_w8a16_silu_gemm, load_library, moe_combine, moe_route_topk,

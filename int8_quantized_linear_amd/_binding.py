@@ -26,7 +26,8 @@ EXPORTS = ("quantize_per_channel_int8", "quantize_per_token_int8",
            "w8a8_gemm_with_plan", "w8a8_gemm_noalloc", "w8a8_gemm_g128",
            "w8a8_gemm_g128_with_config", "grouped_w8a16_silu_gemm", "moe_route_topk",
            "moe_combine", "quantize_per_group_int8", "w8a16_gemm_g128",
-           "rmsnorm_quantize_per_token_int8", "rmsnorm_bf16", "i8ql_status_string",
+           "rmsnorm_quantize_per_token_int8", "rmsnorm_bf16",
+           "silu_mul_quantize_per_token_int8", "silu_mul_bf16", "i8ql_status_string",
            "i8ql_last_hip_error")
 GROUP_SIZE = 128  # I8QL_GROUP_SIZE
 ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 256, 32  # I8QL_ROUTE_MAX_EXPERTS, I8QL_ROUTE_MAX_K
@@ -36,6 +37,7 @@ W8A8_SPLIT_MAX_TILES = 4096  # I8QL_W8A8_SPLIT_MAX_TILES
 W8A8_SCRATCH_BYTES = 32 << 20  # I8QL_W8A8_SCRATCH_BYTES
 QUANT_MAX_JOBS = 8  # I8QL_QUANT_MAX_JOBS
 NORM_MAX_K = 24576  # I8QL_NORM_MAX_K
+SILU_MAX_N = 24576  # I8QL_SILU_MAX_N
 
 
 class QuantJob(ctypes.Structure):
@@ -110,6 +112,10 @@ def load_library(path: str = LIB_PATH):
         lib.rmsnorm_quantize_per_token_int8.restype = I
         lib.rmsnorm_bf16.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P]
         lib.rmsnorm_bf16.restype = I
+        lib.silu_mul_quantize_per_token_int8.argtypes = [P, I64, I64, P, P, P]
+        lib.silu_mul_quantize_per_token_int8.restype = I
+        lib.silu_mul_bf16.argtypes = [P, I64, I64, P, P]
+        lib.silu_mul_bf16.restype = I
         lib.i8ql_status_string.argtypes = [I]
         lib.i8ql_status_string.restype = ctypes.c_char_p
         lib.i8ql_last_hip_error.argtypes = []
@@ -219,6 +225,43 @@ def rmsnorm_bf16(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
         _call("rmsnorm_bf16", _ptr(x), _ptr(residual), _ptr(gamma), float(eps), m, k, _ptr(y),
               _stream(x.device))
     return y
+
+
+def silu_mul_quantize_per_token_int8(gu: torch.Tensor, q_out=None, scale_out=None):
+    """SiLU·mul of a gate/up product ``gu`` [M, 2N] bf16 (gate columns first) fused with the
+    per-token int8 quantization of the result: (q int8 [M, N], scale fp32 [M])."""
+    _check(gu, "gu", (torch.bfloat16,), 2)
+    m, n2 = gu.shape
+    if n2 % 2:
+        raise ValueError("gu must hold gate and up halves of equal width")
+    n = n2 // 2
+    q = q_out if q_out is not None else torch.empty((m, n), dtype=torch.int8, device=gu.device)
+    s = scale_out if scale_out is not None else torch.empty((m,), dtype=torch.float32,
+                                                            device=gu.device)
+    _check(q, "q_out", (torch.int8,), 2, gu.device)
+    _check(s, "scale_out", (torch.float32,), 1, gu.device)
+    if tuple(q.shape) != (m, n) or tuple(s.shape) != (m,):
+        raise ValueError("output shapes do not match the input")
+    with torch.cuda.device(gu.device):
+        _call("silu_mul_quantize_per_token_int8", _ptr(gu), m, n, _ptr(q), _ptr(s),
+              _stream(gu.device))
+    return q, s
+
+
+def silu_mul_bf16(gu: torch.Tensor, h_out=None):
+    """The same SiLU·mul written as bf16 [M, N] (the unfused producer)."""
+    _check(gu, "gu", (torch.bfloat16,), 2)
+    m, n2 = gu.shape
+    if n2 % 2:
+        raise ValueError("gu must hold gate and up halves of equal width")
+    n = n2 // 2
+    h = h_out if h_out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=gu.device)
+    _check(h, "h_out", (torch.bfloat16,), 2, gu.device)
+    if tuple(h.shape) != (m, n):
+        raise ValueError("h_out must be [M, N]")
+    with torch.cuda.device(gu.device):
+        _call("silu_mul_bf16", _ptr(gu), m, n, _ptr(h), _stream(gu.device))
+    return h
 
 
 def quantize_per_token_int8_multi(xs, outs=None):

@@ -76,6 +76,20 @@ i8ql_status rmsnorm(const void* x, void* residual, const void* gamma, float eps,
                                          static_cast<hipStream_t>(stream)));
 }
 
+// The SiLU·mul entry points: quantized (q and scale) or bf16 (h) output.
+i8ql_status silu_mul(const void* gu, int64_t m, int64_t n, int8_t* q, float* scale, void* h,
+                     void* stream) {
+  if (m < 0 || n < 1 || n % 8 != 0 || n > I8QL_SILU_MAX_N) return I8QL_ERR_SHAPE;
+  if (!mul_ok(m, 2 * n) || m > kMaxGridX) return I8QL_ERR_SHAPE;
+  if (m == 0) return I8QL_OK;
+  if (!gu || (h ? false : (!q || !scale))) return I8QL_ERR_NULL;
+  if (!aligned(gu, 16) || (h && !aligned(h, 16)) || (q && !aligned(q, 8)) ||
+      (scale && !aligned(scale, 4)))
+    return I8QL_ERR_ALIGN;
+  return hip_status(i8ql::launch_silu_mul(gu, m, n, q, scale, h,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +135,15 @@ i8ql_status rmsnorm_quantize_per_token_int8(const void* x, void* residual, const
 i8ql_status rmsnorm_bf16(const void* x, void* residual, const void* gamma, float eps, int64_t m,
                          int64_t k, void* y_out, void* stream) {
   return rmsnorm(x, residual, gamma, eps, m, k, nullptr, nullptr, y_out, stream);
+}
+
+i8ql_status silu_mul_quantize_per_token_int8(const void* gu, int64_t m, int64_t n,
+                                             int8_t* q_out, float* scale_out, void* stream) {
+  return silu_mul(gu, m, n, q_out, scale_out, nullptr, stream);
+}
+
+i8ql_status silu_mul_bf16(const void* gu, int64_t m, int64_t n, void* h_out, void* stream) {
+  return silu_mul(gu, m, n, nullptr, nullptr, h_out, stream);
 }
 
 }  // extern "C"

@@ -47,6 +47,12 @@ hipError_t launch_rmsnorm(const void* x, void* residual, const void* gamma, floa
                          int64_t rows, int64_t k, int8_t* q, float* scale, void* h,
                          hipStream_t stream);
 
+// SiLU·mul of a gate/up product gu [rows, 2n] bf16 (gate columns first) fused with the
+// per-token int8 quantization (q and scale non-NULL), or written as bf16 rows h [rows, n]
+// (q NULL); validated: n % 8 == 0, n <= I8QL_SILU_MAX_N, 16-byte aligned rows.
+hipError_t launch_silu_mul(const void* gu, int64_t rows, int64_t n, int8_t* q, float* scale,
+                          void* h, hipStream_t stream);
+
 // Several matrices (validated for the vector path) in one launch.
 hipError_t launch_quantize_rows_multi(const i8ql_quant_job* jobs, int count, i8ql_dtype dtype,
                                       hipStream_t stream);

@@ -418,6 +418,61 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// The row rule on a bf16 row held in registers (u[i]: chunk t + i * 64 W of the row, for the
+// i with i * 64 W < chunks; chunks past the row end repeat its last chunk), given this lane's
+// share of the row maximum: the maximum over the W wavefronts of the row, then the codes
+// (8 per chunk, one 8-byte store each) and the scale, exactly as the row quantizer.
+template <int W>
+__device__ __forceinline__ void quantize_held_row(const uint4 (&u)[kNormChunks], float amax,
+                                                  int64_t chunks, int t, int slot, bool live,
+                                                  int64_t row, int64_t row_base,
+                                                  int8_t* __restrict__ q,
+                                                  float* __restrict__ scale, float* wmax) {
+  constexpr int T = kWave * W;
+  amax = wave_max(amax);
+  if constexpr (W > 1) {
+    if (threadIdx.x % kWave == 0) wmax[threadIdx.x / kWave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < W; ++w) amax = fmaxf(amax, wmax[slot * W + w]);
+  }
+  if (!live) return;
+  const float s = amax / 127.0f;
+  int8_t* dst = q + row_base;
+  auto emit_all = [&](auto code) {
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int64_t c0 = t + static_cast<int64_t>(i) * T;
+      if (static_cast<int64_t>(i) * T < chunks && c0 < chunks) {
+        float f[8];
+        widen_chunk<I8QL_BF16>(u[i], f);
+        uint32_t p[2];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            w |= (static_cast<uint32_t>(code(f[4 * g2 + b])) & 0xffu) << (8 * b);
+          p[g2] = w;
+        }
+        *reinterpret_cast<uint2*>(dst + c0 * 8) = make_uint2(p[0], p[1]);
+      }
+    }
+  };
+  if (s == 0.0f) {
+    emit_all([](float) { return 0; });
+    if (t == 0) scale[row] = 1.0f;
+    return;
+  }
+  if (s >= 0x1p-64f) {
+    const float y = 1.0f / s;
+    emit_all([&](float a) { return code_from_quotient(quotient_fma(a, s, y)); });
+  } else {
+    emit_all([&](float a) { return code_of(a, s); });
+  }
+  if (t == 0) scale[row] = s;
+}
+
 template <int W, bool QUANT, bool RES>
 __global__ __launch_bounds__(kWave* kRowsPerBlock) void rmsnorm_rows_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ res, const uint4* __restrict__ gamma,
@@ -504,50 +559,8 @@ __global__ __launch_bounds__(kWave* kRowsPerBlock) void rmsnorm_rows_kernel(
       }
     }
   }
-  if constexpr (QUANT) {
-    amax = wave_max(amax);
-    if constexpr (W > 1) {
-      if (threadIdx.x % kWave == 0) wmax[threadIdx.x / kWave] = amax;
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < W; ++w) amax = fmaxf(amax, wmax[slot * W + w]);
-    }
-    if (!live) return;
-    const float s = amax / 127.0f;
-    int8_t* dst = q + rr * k;
-    auto emit_all = [&](auto code) {
-#pragma unroll
-      for (int i = 0; i < kNormChunks; ++i) {
-        const int64_t c0 = t + static_cast<int64_t>(i) * T;
-        if (static_cast<int64_t>(i) * T < chunks && c0 < chunks) {
-          float f[8];
-          widen_chunk<I8QL_BF16>(u[i], f);
-          uint32_t p[2];
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-              w |= (static_cast<uint32_t>(code(f[4 * g2 + b])) & 0xffu) << (8 * b);
-            p[g2] = w;
-          }
-          *reinterpret_cast<uint2*>(dst + c0 * 8) = make_uint2(p[0], p[1]);
-        }
-      }
-    };
-    if (s == 0.0f) {
-      emit_all([](float) { return 0; });
-      if (t == 0) scale[row] = 1.0f;
-      return;
-    }
-    if (s >= 0x1p-64f) {
-      const float y = 1.0f / s;
-      emit_all([&](float a) { return code_from_quotient(quotient_fma(a, s, y)); });
-    } else {
-      emit_all([&](float a) { return code_of(a, s); });
-    }
-    if (t == 0) scale[row] = s;
-  }
+  if constexpr (QUANT)
+    quantize_held_row<W>(u, amax, chunks, t, slot, live, row, rr * k, q, scale, wmax);
 }
 
 template <bool QUANT, bool RES>
@@ -565,6 +578,96 @@ hipError_t launch_rmsnorm_t(const void* x, void* res, const void* gamma, float e
     hipLaunchKernelGGL((rmsnorm_rows_kernel<1, QUANT, RES>),
                        dim3(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                        block, 0, stream, xs, rs, gs, eps, rows, k, q, scale, hs);
+  }
+  return hipGetLastError();
+}
+
+// ---- SiLU·mul fused with the per-token quantization ------------------------------------
+// The down projection's input is silu(gate) * up of the gate/up projection's output, one row
+// per token: gu [m, 2 n] bf16 with the gate values in columns [0, n) and the up values in
+// [n, 2 n) (one GEMM over the stacked gate and up weights).  Quantizing while the activation
+// is formed writes the int8 codes (1 byte per element) instead of the bf16 activation that a
+// separate quantizer would read back (2 + 2 bytes).  Per element, in float32:
+//   h = g * rcp(1 + exp(-g)) * u,  then bf16 (ties to even),
+// the exponential correctly rounded to within about an ulp and the reciprocal within one, so
+// h lies within about 5 float32 ulps of the exact value; elements that float32 cannot
+// resolve (g < -80, where e^-g approaches the float range, and nonzero |h| < 2^-120, where
+// the product leaves the normal range) are formed in float64 instead.  The rounding to bf16
+// then differs from that of the exact value only for values within that distance of the
+// halfway point between two bf16 values.  Layout as the RMS norm above: W wavefronts per row,
+// every chunk of the row's gate and up halves loaded before any is used and h kept in
+// registers for the row rule.
+__device__ __forceinline__ float silu_mul_one(float g, float u) {
+  float h = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
+  if (g < -80.0f || (h != 0.0f && fabsf(h) < 0x1p-120f)) {
+    const double gd = g, ud = u;
+    h = static_cast<float>(gd / (1.0 + exp(-gd)) * ud);
+  }
+  return h;
+}
+
+template <int W, bool QUANT>
+__global__ __launch_bounds__(kWave* kRowsPerBlock) void silu_mul_rows_kernel(
+    const uint4* __restrict__ gu, int64_t rows, int64_t n, int8_t* __restrict__ q,
+    float* __restrict__ scale, uint4* __restrict__ h_out) {
+  constexpr int T = kWave * W;  // threads per row
+  __shared__ float wmax[kRowsPerBlock];
+  const int t = threadIdx.x % T;
+  const int slot = threadIdx.x / T;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kRowsPerBlock / W) + slot;
+  const bool live = row < rows;  // a dead row still joins the barriers
+  const int64_t rr = live ? row : rows - 1;
+  const int64_t chunks = n / 8;  // of each half
+  const uint4* gate = gu + rr * 2 * chunks;
+  const uint4* up = gate + chunks;
+
+  uint4 u[kNormChunks], ug[kNormChunks];
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (static_cast<int64_t>(i) * T < chunks) {
+      const int64_t c0 = t + static_cast<int64_t>(i) * T;
+      const int64_t c = c0 < chunks ? c0 : chunks - 1;
+      u[i] = gate[c];
+      ug[i] = up[c];
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (static_cast<int64_t>(i) * T < chunks) {
+      float g[8], v[8], hv[8];
+      widen_chunk<I8QL_BF16>(u[i], g);
+      widen_chunk<I8QL_BF16>(ug[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = silu_mul_one(g[e], v[e]);
+      u[i] = make_uint4(bf16_pack(hv[0], hv[1]), bf16_pack(hv[2], hv[3]),
+                        bf16_pack(hv[4], hv[5]), bf16_pack(hv[6], hv[7]));
+      if constexpr (QUANT) {
+        widen_chunk<I8QL_BF16>(u[i], hv);
+        amax = chunk_absmax(hv, 8, amax);
+      } else {
+        const int64_t c0 = t + static_cast<int64_t>(i) * T;
+        if (live && c0 < chunks) h_out[rr * chunks + c0] = u[i];
+      }
+    }
+  }
+  if constexpr (QUANT)
+    quantize_held_row<W>(u, amax, chunks, t, slot, live, row, rr * n, q, scale, wmax);
+}
+
+template <bool QUANT>
+hipError_t launch_silu_mul_t(const void* gu, int64_t rows, int64_t n, int8_t* q, float* scale,
+                             void* h, hipStream_t stream) {
+  const dim3 block(kWave * kRowsPerBlock);
+  const auto* src = static_cast<const uint4*>(gu);
+  auto* hs = static_cast<uint4*>(h);
+  if (four_waves_per_row<I8QL_BF16>(rows, n, rows)) {
+    hipLaunchKernelGGL((silu_mul_rows_kernel<4, QUANT>), dim3(static_cast<unsigned>(rows)),
+                       block, 0, stream, src, rows, n, q, scale, hs);
+  } else {
+    hipLaunchKernelGGL((silu_mul_rows_kernel<1, QUANT>),
+                       dim3(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       block, 0, stream, src, rows, n, q, scale, hs);
   }
   return hipGetLastError();
 }
@@ -649,6 +752,12 @@ hipError_t launch_rmsnorm(const void* x, void* residual, const void* gamma, floa
                                                   stream)
                   : launch_rmsnorm_t<false, false>(x, residual, gamma, eps, rows, k, q, scale,
                                                    h, stream);
+}
+
+hipError_t launch_silu_mul(const void* gu, int64_t rows, int64_t n, int8_t* q, float* scale,
+                          void* h, hipStream_t stream) {
+  return q ? launch_silu_mul_t<true>(gu, rows, n, q, scale, h, stream)
+           : launch_silu_mul_t<false>(gu, rows, n, q, scale, h, stream);
 }
 
 hipError_t launch_quantize_rows(const void* a, i8ql_dtype dtype, int64_t rows, int64_t k,

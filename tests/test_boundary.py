@@ -415,6 +415,24 @@ def test_rmsnorm_validation(lib):
     assert fb(A16, NUL, A16, 1e-6, 4, 64, A4, NUL) == ALIGN
 
 
+def test_silu_mul_validation(lib):
+    fq, fb = lib.silu_mul_quantize_per_token_int8, lib.silu_mul_bf16
+    for f, outs in ((fq, (A16, A16)), (fb, (A16,))):
+        assert f(A16, -1, 64, *outs, NUL) == SHAPE
+        assert f(A16, 4, 0, *outs, NUL) == SHAPE
+        assert f(A16, 4, 60, *outs, NUL) == SHAPE                 # n % 8
+        assert f(A16, 4, 24576 + 8, *outs, NUL) == SHAPE          # I8QL_SILU_MAX_N
+        assert f(NUL, 0, 64, *[NUL] * len(outs), NUL) == OK      # no rows: no-op
+        assert f(NUL, 4, 64, *outs, NUL) == NULL
+        assert f(A4, 4, 64, *outs, NUL) == ALIGN
+    assert fq(A16, 4, 64, NUL, A16, NUL) == NULL
+    assert fq(A16, 4, 64, A16, NUL, NUL) == NULL
+    assert fq(A16, 4, 64, A4, A16, NUL) == ALIGN
+    assert fq(A16, 4, 64, A16, A2, NUL) == ALIGN
+    assert fb(A16, 4, 64, NUL, NUL) == NULL
+    assert fb(A16, 4, 64, A4, NUL) == ALIGN
+
+
 def test_valid_calls_without_a_device_report_hip_errors(lib):
     """With no device, a call that passes validation fails at its first HIP call with
     I8QL_ERR_HIP (and a recorded hipError), instead of crashing."""
@@ -440,6 +458,8 @@ def test_valid_calls_without_a_device_report_hip_errors(lib):
         lambda: lib.moe_combine(A16, BF16, A16, 4, 8, 2048, A16, BF16, NUL),
         lambda: lib.rmsnorm_quantize_per_token_int8(A16, A16, A16, 1e-6, 4, 64, A16, A16, NUL),
         lambda: lib.rmsnorm_bf16(A16, NUL, A16, 1e-6, 4, 64, A16, NUL),
+        lambda: lib.silu_mul_quantize_per_token_int8(A16, 4, 64, A16, A16, NUL),
+        lambda: lib.silu_mul_bf16(A16, 4, 64, A16, NUL),
     ]
     for call in calls:
         assert call() == HIP
