@@ -972,6 +972,74 @@ def section_silu_quant(torch, i8, wl, dev, args, result):
     result["silu_quant"] = out
 
 
+def section_layer_8b(torch, i8, wl, dev, args, result):
+    """The dense 8B decoder layer's W8A8 projections in their data flow, attention left out:
+    the RMS norm (with the residual add) produces q/k/v's input, a synthetic attention output
+    is quantized for o, the second norm adds o's output to the residual stream and produces
+    gate/up's input, and SiLU·mul of the gate/up output produces down's input.  Once with
+    the quantizer fused into the norms and the SiLU·mul, once with them writing bf16 and the
+    quantizer apart.  4096 and 16384 tokens, bias, weights rotating as in the step."""
+    out = {"what": "norm+quant -> q/k/v GEMM; quant(attention output, synthetic) -> o GEMM; "
+                   "norm(residual + o)+quant -> gate/up GEMM; SiLU·mul+quant -> down GEMM; "
+                   "fused producers vs the same producers writing bf16 + quantize_per_token_int8",
+           "per_tokens": {}}
+    g = wl.rng(83)
+    eps = 1e-6
+    for m in (4096, 16384):
+        wk = prefill_8b(torch, i8, wl, dev, (m,))
+        hid = wk.kin["attn_in"]
+        inter = wk.kin["mlp_mid"]
+        x = wl.to_bf16(wl.activations(g, m, hid, 0.01)).to(dev)       # previous layer's output
+        res = wl.to_bf16(wl.activations(g, m, hid)).to(dev)          # residual stream
+        attn = wk.xs[m]["attn_out"]                                  # stands in for attention
+        g1 = wl.to_bf16(wl.norm_weight(g, hid)).to(dev)
+        g2 = wl.to_bf16(wl.norm_weight(g, hid)).to(dev)
+        hb = torch.empty((m, hid), dtype=torch.bfloat16, device=dev)
+        hm = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
+        qx = wk.qx[m]
+        outs = wk.outs[m]
+
+        def gemm(nm, src, i):
+            q, sx = qx[src]
+            i8.w8a8_gemm(q, sx, wk.qs[i % wk.copies][nm], wk.s[nm], wk.b[nm], out=outs[nm])
+
+        def layer(i, fused):
+            if fused:
+                i8.rmsnorm_quantize_per_token_int8(x, g1, eps, res, *qx["attn_in"])
+            else:
+                i8.rmsnorm_bf16(x, g1, eps, res, y_out=hb)
+                i8.quantize_per_token_int8(hb, *qx["attn_in"])
+            gemm("qkv", "attn_in", i)
+            i8.quantize_per_token_int8(attn, *qx["attn_out"])
+            gemm("o", "attn_out", i)
+            if fused:
+                i8.rmsnorm_quantize_per_token_int8(outs["o"], g2, eps, res, *qx["mlp_in"])
+            else:
+                i8.rmsnorm_bf16(outs["o"], g2, eps, res, y_out=hb)
+                i8.quantize_per_token_int8(hb, *qx["mlp_in"])
+            gemm("gate_up", "mlp_in", i)
+            if fused:
+                i8.silu_mul_quantize_per_token_int8(outs["gate_up"], *qx["mlp_mid"])
+            else:
+                i8.silu_mul_bf16(outs["gate_up"], h_out=hm)
+                i8.quantize_per_token_int8(hm, *qx["mlp_mid"])
+            gemm("down", "mlp_mid", i)
+
+        steps = max(5, args.steps // 5)
+        t_f = time_loop(torch, lambda i: layer(i, True), steps, 2) / steps
+        t_u = time_loop(torch, lambda i: layer(i, False), steps, 2) / steps
+        ops = wk.ops()
+        out["per_tokens"][str(m)] = {"fused_ms": t_f * 1e3, "unfused_ms": t_u * 1e3,
+                                     "fused_TOPS": ops / t_f / 1e12,
+                                     "unfused_TOPS": ops / t_u / 1e12,
+                                     "saved_us": (t_u - t_f) * 1e6}
+        log(f"[layer_8b] {m} tokens: fused producers {t_f * 1e3:.3f} ms "
+            f"({ops / t_f / 1e12:.0f} TOPS over the GEMMs' ops), unfused {t_u * 1e3:.3f} ms")
+        del wk, x, res, hb, hm
+        torch.cuda.empty_cache()
+    result["layer_8b"] = out
+
+
 NORM_TRAFFIC = "RMS norm + residual + per-token int8, 16384x4096"
 
 
@@ -1007,7 +1075,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "prefill_8b_g128": section_prefill_8b_g128,
     "prefill_4b": section_prefill_4b, "decode": section_decode, "moe": section_moe,
     "weight_quant": section_weight_quant, "norm_quant": section_norm_quant,
-    "silu_quant": section_silu_quant,
+    "silu_quant": section_silu_quant, "layer_8b": section_layer_8b,
     # hardware-counter runs only (eager launches, nothing timed)
     "counters": section_counters, "counters_4b": section_counters_4b,
     "counters_decode": section_counters_decode,
@@ -1015,7 +1083,7 @@ SECTIONS = {  # name -> (function, needs the GPU objects); the default run is DE
     "counters_moe": section_counters_moe, "counters_norm": section_counters_norm,
 }
 DEFAULT = ("step,cpu_baseline,prefill_8b_m4096,prefill_8b_g128,prefill_4b,decode,moe,"
-           "weight_quant,norm_quant,silu_quant")
+           "weight_quant,norm_quant,silu_quant,layer_8b")
 
 
 def main():
