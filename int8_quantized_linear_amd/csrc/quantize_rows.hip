@@ -589,8 +589,8 @@ hipError_t launch_rmsnorm_t(const void* x, void* res, const void* gamma, float e
 // is formed writes the int8 codes (1 byte per element) instead of the bf16 activation that a
 // separate quantizer would read back (2 + 2 bytes).  Per element, in float32:
 //   h = g * rcp(1 + exp(-g)) * u,  then bf16 (ties to even),
-// the exponential correctly rounded to within about an ulp and the reciprocal within one, so
-// h lies within about 5 float32 ulps of the exact value; elements that float32 cannot
+// the exponential within about 2^-19.5 (relative) and the reciprocal within an ulp, so h
+// lies within about 2^-19 of the exact value; elements that float32 cannot
 // resolve (g < -80, where e^-g approaches the float range, and nonzero |h| < 2^-120, where
 // the product leaves the normal range) are formed in float64 instead.  The rounding to bf16
 // then differs from that of the exact value only for values within that distance of the
@@ -598,7 +598,17 @@ hipError_t launch_rmsnorm_t(const void* x, void* res, const void* gamma, float e
 // every chunk of the row's gate and up halves loaded before any is used and h kept in
 // registers for the row rule.
 __device__ __forceinline__ float silu_mul_one(float g, float u) {
-  float h = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
+  // e^-g: for g >= -16 as 2^(-g log2 e) with the hardware exponential (the rounding of the
+  // product moves the result by at most |g| 2^-24 relative, the exponential by about an
+  // ulp; for g > 16 the term vanishes next to 1 anyway), below -16 the accurate expf (one
+  // branch per wavefront, taken only when some lane needs it)
+  float e;
+  if (__builtin_amdgcn_ballot_w64(g < -16.0f) == 0) {
+    e = __expf(-g);
+  } else {
+    e = g >= -16.0f ? __expf(-g) : expf(-g);
+  }
+  float h = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
   if (g < -80.0f || (h != 0.0f && fabsf(h) < 0x1p-120f)) {
     const double gd = g, ud = u;
     h = static_cast<float>(gd / (1.0 + exp(-gd)) * ud);
