@@ -188,8 +188,9 @@ i8ql_status rmsnorm_bf16(const void* x, void* residual, const void* gamma, float
  * of every forward pass).  The activation is the one of the mixture-of-experts block's
  * grouped_w8a16_silu_gemm (not written out on the pages; reading): per row i and column j,
  *   h[i, j] = bf16(g * rcp(1 + e^-g) * u),  g = gu[i, j], u = gu[i, n + j] (bf16 widened),
- * in float32 (the hardware exponential for g >= -16; float64 where g < -80 or the nonzero product is below 2^-120 in
- * magnitude), rounded to nearest even; then the row rule of quantize_per_channel_int8 on h.
+ * in float32 (the hardware exponential for g >= -16; float64 where g < -80 or the nonzero
+ * product is below 2^-120 in magnitude), rounded to nearest even; then the row rule of
+ * quantize_per_channel_int8 on h.
  * The codes and scales are bitwise those of silu_mul_bf16 followed by
  * quantize_per_token_int8.  (h lies within about 2^-19 (relative) of the exact value, so its
  * bf16 rounding is that of the exact value except within that distance of a halfway point.)
