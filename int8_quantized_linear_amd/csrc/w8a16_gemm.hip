@@ -37,6 +37,7 @@ constexpr int kGlobalUnroll = 4;  // the same with activations loaded too (divid
 constexpr size_t kMaxDefaultLds = 65536;  // dynamic LDS usable without a function attribute
 constexpr size_t kMaxStageLds = 96 * 1024;  // staged rows up to this much LDS (attribute set)
 constexpr size_t kParamTableBytes = 64 * 4;  // the epilogue's scales and biases
+constexpr bool kRowKernel = true;  // one activation row: one wavefront per output channel
 
 // Dynamic LDS: the partial tiles of the WAVES wavefronts ([WAVES][MT][64] v4f), then, when
 // the activation rows are staged, rows of 2k + 16 bytes (consecutive rows shifted by one
@@ -201,6 +202,100 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
   }
 }
 
+// ---- one activation row (batch-1 decode) ------------------------------------------------
+// With a 16-row tile a wavefront can multiply nothing until all 16 rows' bytes of a step have
+// landed, and a row's bytes arrive from its own memory channel at its own time, so the
+// multiplies of a launch pile up after the last bytes.  With one activation row the matrix
+// cores would also use one of their 16 columns.  Here a wavefront owns one output channel:
+// each load instruction reads 1 KiB of the row (8 whole 128-byte lines), every load of the
+// row is in flight at once (up to kRowChunks 16-byte chunks per lane, k <= 64 * 16 *
+// kRowChunks), the codes expand exactly to bf16 (as in dequant_mma.hpp) and meet the bf16
+// activations in v_dot2_f32_bf16 (two exact products and their sum into the float32
+// accumulator), then the lanes' sums are added by a butterfly of shuffles (fixed order,
+// deterministic) and the channel's scale and bias are applied once.  A wavefront finishes as
+// soon as its own row is in.  Longer rows (k > 8192) keep the tiled kernel: there its
+// batches of loads kept more of each row in flight and ran faster than one wavefront holding
+// 12 or 16 chunks per lane.
+constexpr int kRowChunks = 8;
+typedef short v2s __attribute__((ext_vector_type(2)));  // a bf16 pair, as the builtin takes it
+
+template <int KC, int YT>
+__global__ __launch_bounds__(256) void w8a16_row_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, const float* __restrict__ bias, void* __restrict__ y,
+    int64_t n, int64_t k) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (row >= n) return;  // (uniform over the wavefront)
+  const int64_t chunks = k / 16;
+  const v4u* wr = reinterpret_cast<const v4u*>(wq + row * k);
+  const v4u* xr = reinterpret_cast<const v4u*>(x);  // 8 activations per 16 bytes
+  // each wavefront reads the activations itself (every wavefront reads the same 2k bytes, so
+  // they come from the caches); a chunk's codes and its 16 activations are loaded together
+  v4u w[KC], xv[KC][2];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int64_t c = lane + 64 * static_cast<int64_t>(i);
+    const int64_t cc = c < chunks ? c : 0;  // in bounds; multiplied by nothing below
+    w[i] = wr[cc];
+    xv[i][0] = xr[2 * cc];
+    xv[i][1] = xr[2 * cc + 1];
+  }
+  asm volatile("" ::: "memory");  // the loads stay here, in order, ahead of every use
+  __builtin_amdgcn_sched_barrier(0);
+  // every chunk is multiplied (a chunk past the row's end by zero activations), so the loads
+  // keep their issue order and each chunk waits only for its own
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const uint32_t in = lane + 64 * i < chunks ? 0xffffffffu : 0u;
+    v8bf a[2];
+    i8x16_to_bf16(w[i], a[0], a[1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4u xm = xv[i][h] & in;
+      const v4u av = __builtin_bit_cast(v4u, a[h]);
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w};  // bf16 pairs of codes
+      const uint32_t xw[4] = {xm.x, xm.y, xm.z, xm.w};  // bf16 pairs of activations
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
+                                              __builtin_bit_cast(v2s, xw[e]), acc, false);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane != 0) return;
+  float v = acc * w_scale[row];
+  if (bias) v = v + bias[row];
+  if constexpr (YT == I8QL_F32) {
+    static_cast<float*>(y)[row] = v;
+  } else {
+    static_cast<uint16_t*>(y)[row] = f32_to_bf16_rne(v);
+  }
+}
+
+template <int YT>
+bool launch_row(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
+                void* y, int64_t n, int64_t k, hipStream_t stream, hipError_t* err) {
+  const int64_t per_lane = (k / 16 + 63) / 64;
+  const dim3 grid(static_cast<unsigned>((n + 3) / 4));
+  const auto* xx = static_cast<const uint16_t*>(x);
+#define I8QL_ROW(KC)                                                                         \
+  hipLaunchKernelGGL((w8a16_row_kernel<KC, YT>), grid, dim3(256), 0, stream, xx, wq, w_scale, \
+                     bias, y, n, k)
+  if (per_lane <= 4) {
+    I8QL_ROW(4);
+  } else if (per_lane <= kRowChunks) {
+    I8QL_ROW(8);
+  } else {
+    return false;
+  }
+#undef I8QL_ROW
+  *err = hipGetLastError();
+  return true;
+}
+
 template <int MT, int WAVES, int YT, bool GS>
 hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
                         const float* bias, void* y, int64_t m, int64_t n, int64_t k,
@@ -263,6 +358,13 @@ hipError_t launch_yt(const void* x, const int8_t* wq, const float* w_scale, cons
 hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
                              int64_t n, int64_t k, hipStream_t stream) {
+  if (m == 1 && kRowKernel) {
+    hipError_t err = hipSuccess;
+    const bool done = y_dtype == I8QL_F32
+                          ? launch_row<I8QL_F32>(x, wq, w_scale, bias, y, n, k, stream, &err)
+                          : launch_row<I8QL_BF16>(x, wq, w_scale, bias, y, n, k, stream, &err);
+    if (done) return err;
+  }
   if (y_dtype == I8QL_F32)
     return launch_yt<I8QL_F32, false>(x, wq, w_scale, bias, y, m, n, k, stream);
   return launch_yt<I8QL_BF16, false>(x, wq, w_scale, bias, y, m, n, k, stream);

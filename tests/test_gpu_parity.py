@@ -489,7 +489,10 @@ def run_w8a16(ref, dev, m, n, k, bias, out_dtype, seed):
     return y
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 16), (1, 50, 208), (3, 130, 1040), (8, 256, 4096),
+# one activation row: the one-wavefront-per-channel kernel at 4 and 8 chunks per lane (full,
+# ragged, and channels not a multiple of the workgroup's 4), and past its k limit
+@pytest.mark.parametrize("m,n,k", [(1, 16, 16), (1, 50, 208), (1, 7, 1040), (1, 37, 4112),
+                                   (1, 1003, 8192), (1, 9, 8208), (3, 130, 1040), (8, 256, 4096),
                                    (16, 1000, 4096), (17, 100, 512), (33, 70, 272),
                                    (70, 100, 256), (130, 45, 128)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
