@@ -38,18 +38,69 @@ constexpr int kMaxPassRows = 8;  // activation rows staged in LDS per pass
 constexpr size_t kMaxStageBytes = 128 * 1024;  // LDS for the staged rows of one pass
 constexpr int kMaxTileSeq = 16;   // 16-channel tiles one workgroup walks, at most
 constexpr int64_t kCusPerGpu = 256;  // MI355X compute units (sizes the tiles per workgroup)
+constexpr int kMaxExtraRows = 32;     // rows of workgroups that take experts' later passes
+constexpr int64_t kHistMaxExperts = 4096;  // experts counted in LDS for that split
 
 template <int WAVES>
 constexpr size_t red_bytes() { return static_cast<size_t>(WAVES) * 64 * sizeof(v4f); }
 
 // Dynamic LDS: [WAVES][64] v4f partial tiles, the staged rows of one pass (pass_rows rows,
 // see stage_rows), a 16-byte zero block, the expert bitmap (one bit per expert, 16-byte
-// multiple).
+// multiple) or, when later passes are split over extra workgroups, the rows per expert (one
+// int per expert).
 __host__ __device__ inline size_t xs_bytes(int pass_rows, int64_t k) {
   return 1024 * static_cast<size_t>(stage_insts(pass_rows, k)) + 16;
 }
 __host__ __device__ inline size_t bitmap_bytes(int64_t experts) {
   return 16 * static_cast<size_t>((experts + 127) / 128);
+}
+__host__ __device__ inline size_t hist_bytes(int64_t experts) {
+  return 16 * static_cast<size_t>((experts + 3) / 4);
+}
+
+// Later passes split over extra workgroups.  An expert with c rows takes ceil(c / pass_rows)
+// passes; its own workgroup runs the first, and its later ones (ex = passes - 1 of them) are
+// numbered globally from the highest expert id down.  Extra row j runs later pass number j;
+// the expert's own workgroup runs the ones numbered xrows and beyond.  From the rows per
+// expert in hist[], wavefront-uniformly: for `mine` < 0 (an extra row, j = -mine - 1) the
+// expert and its pass index (>= 1), or expert -1 when fewer later passes exist; for an
+// expert's own workgroup (mine = e) the global number of its first later pass.
+__device__ __forceinline__ void later_pass(const int* hist, int64_t experts, int pass_rows,
+                                           int64_t mine, int lane, int64_t& e_out,
+                                           int& pass_out, int64_t& first_out) {
+  int64_t before = 0;  // later passes of the experts above the current group
+  for (int64_t top = experts - 1; top >= 0; top -= 64) {
+    const int64_t e = top - lane;  // lane 0 holds the highest expert of this group
+    const int c = e >= 0 ? hist[e] : 0;
+    const int ex = c > pass_rows ? (c + pass_rows - 1) / pass_rows - 1 : 0;
+    int incl = ex;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    if (mine >= 0) {
+      if (mine > top - 64) {  // this group holds the expert
+        const int src = static_cast<int>(top - mine);
+        first_out = before + __shfl(incl - ex, src);
+        return;
+      }
+    } else {
+      const int64_t j = -mine - 1;
+      const int in_group = __shfl(incl, 63);
+      if (j < before + in_group) {
+        const uint64_t here = __ballot(before + incl > j && before + incl - ex <= j);
+        const int src = __ffsll(static_cast<unsigned long long>(here)) - 1;
+        e_out = top - src;
+        pass_out = static_cast<int>(j - (before + __shfl(incl - ex, src))) + 1;
+        return;
+      }
+    }
+    before += __shfl(incl, 63);
+  }
+  e_out = -1;
+  pass_out = 0;
+  first_out = before;
 }
 
 // Ids [p, p + 64 * kScanBatch) for this lane, 64 apart: idv[j] = ids[p + 64 j + lane].
@@ -106,12 +157,15 @@ __device__ __forceinline__ int nth_present_from_top(const uint32_t* present, int
 // every expert has its own row of workgroups.  SILU: each expert's weights are [2n, k], gate
 // rows then up rows; the workgroup computes the 16 gate channels with wavefronts [0, KS) and
 // the 16 matching up channels with [KS, 2 KS), and stores silu(gate) * up.
+// (Three wavefronts per SIMD for the one-row-per-expert form, which the compiler otherwise
+// missed by a few registers; the bitmap form needs more than a third of them.)
 template <int KS, bool BITMAP, bool SILU, int YT>
-__global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel(
+__global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1))
+__attribute__((amdgpu_waves_per_eu(BITMAP ? 1 : 3))) void grouped_w8a16_kernel(
     const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
     int64_t total, int64_t topk, void* __restrict__ y, int64_t n, int64_t k, int pass_rows,
-    int tseq) {
+    int tseq, int xrows) {
   constexpr int TILES = SILU ? 2 : 1;
   constexpr int WAVES = KS * TILES;
   constexpr int kEpiWave = WAVES - 1;  // reduces the partial tiles and stores the outputs
@@ -124,6 +178,7 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   char* xs = smem + red_bytes<WAVES>();
   char* xzero = xs + 1024 * stage_insts(pass_rows, k);
   uint32_t* present = reinterpret_cast<uint32_t*>(xzero + 16);
+  int* hist = reinterpret_cast<int*>(xzero + 16);  // (the bitmap's place; never both)
 
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: a scalar
@@ -138,11 +193,61 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   int32_t idv[kScanBatch];
   bool idv_loaded = false;
   int64_t e = num_experts;  // the invalid-id row matches ids outside [0, num_experts)
+  // The passes this workgroup runs: pass index gi when gi == pass_a or gi > pass_b (every
+  // pass by default).  With later passes split over extra rows (!BITMAP, xrows > 0, all
+  // ids in one scan window) an extra row runs its one pass, and an expert's own row its
+  // first pass and the later ones that no extra row took.
+  int pass_a = 0, pass_b = 0;
   if constexpr (!BITMAP) {
     // every expert has a row of workgroups, highest id first: the always-on shared experts
     // are appended after the routed ones and receive every token, so they start first
-    // instead of forming the tail
-    if (!invalid_row) e = num_experts - static_cast<int64_t>(blockIdx.y);
+    // instead of forming the tail.  The extra rows come before them, for the same reason.
+    const int64_t y_row = static_cast<int64_t>(blockIdx.y);
+    if (!invalid_row) e = y_row > xrows ? num_experts - (y_row - xrows) : -1;
+    if (!invalid_row && xrows > 0) {
+      // ---- rows per expert, then this workgroup's passes ------------------------------
+      for (int64_t i = threadIdx.x; i < num_experts; i += 64 * WAVES) hist[i] = 0;
+      lds_barrier();
+      // (every id load in flight at once: total <= kList here)
+      constexpr int kPer = (kList + 64 * WAVES - 1) / (64 * WAVES);
+      int32_t hv[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int64_t q = threadIdx.x + static_cast<int64_t>(j) * 64 * WAVES;
+        hv[j] = q < total ? ids[q] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (hv[j] >= 0 && hv[j] < num_experts) atomicAdd(hist + hv[j], 1);
+      lds_barrier();
+      if (wave == 0) {
+        int64_t pe = 0, first = 0;
+        int pp = 0;
+        later_pass(hist, num_experts, pass_rows, e >= 0 ? e : -y_row, lane, pe, pp, first);
+        if (lane == 0) {
+          if (e < 0) {
+            s_expert = pe;
+            s_count = pp;
+          } else {
+            s_next = first;
+          }
+        }
+      }
+      lds_barrier();
+      if (e < 0) {
+        e = s_expert;
+        pass_a = s_count;
+        pass_b = 0x7fffffff;
+        if (e < 0) return;  // fewer later passes than extra rows (uniform)
+      } else {
+        // later passes numbered below xrows went to the extra rows
+        pass_b = static_cast<int>(max(static_cast<int64_t>(0),
+                                      static_cast<int64_t>(xrows) - s_next));
+      }
+      pass_a = __builtin_amdgcn_readfirstlane(pass_a);
+      pass_b = __builtin_amdgcn_readfirstlane(pass_b);
+      __syncthreads();  // s_count and s_next are written again by the scan
+    }
   } else if (!invalid_row) {
     // ---- the expert of this slot: mark every expert named by an id, then pick ---------
     const int words = static_cast<int>((num_experts + 31) / 32);
@@ -181,6 +286,9 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
     e = s_expert;
     if (e < 0) return;  // fewer distinct experts than slots (uniform over the workgroup)
   }
+  // (uniform; a value read from LDS is not known to be, and the addresses built from it
+  // would be computed per lane)
+  e = __builtin_amdgcn_readfirstlane(static_cast<int>(e));
 
   // Weight rows per expert: TILES * n; this wavefront's tile (0: the channels themselves or
   // the gate rows, 1: the up rows) starts at row tile * n of its expert.  Per 16-channel
@@ -280,6 +388,10 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
       const int64_t pitch = 2 * k + 16;
       const int div = x_per_assignment ? 1 : static_cast<int>(topk);
       for (int g = 0; g < count; g += pass_rows) {
+        {
+          const int gi = g / pass_rows;  // (the whole list is one window when split)
+          if (gi != pass_a && gi <= pass_b) continue;  // uniform
+        }
         // Activation rows of this pass, then the tiles one after the other.  For each tile
         // (unless its first batch of weight loads is already in flight) its scales and first
         // batch of weight loads (a later pass re-reads the same weights, from cache); on the
@@ -369,6 +481,53 @@ __global__ __launch_bounds__(64 * KS * (SILU ? 2 : 1)) void grouped_w8a16_kernel
   }
 }
 
+// Compute units of the current device (cached per device; kCusPerGpu when the query fails).
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];  // static storage: starts at zero
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kCusPerGpu;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();  // (not the next launch's error)
+      cus = kCusPerGpu;
+    }
+    cached[dev].store(cus, std::memory_order_relaxed);  // a race only repeats the query
+  }
+  return cus;
+}
+
+// Workgroups of KERN (`threads` threads, `lds` bytes of dynamic LDS) that one compute unit
+// holds at once: the runtime's occupancy query, which counts registers, wavefront slots and
+// LDS (its static part included).  Cached per device for the last LDS size asked; 1 when
+// the query fails.
+template <auto KERN>
+int resident_per_cu(int threads, size_t lds) {
+  static std::atomic<int64_t> cached[kMaxDevices];  // (lds << 16) | count; 0: none
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked) {
+    const int64_t c = cached[dev].load(std::memory_order_relaxed);
+    if (c != 0 && static_cast<size_t>(c >> 16) == lds) return static_cast<int>(c & 0xffff);
+  }
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(KERN),
+                                                   threads, lds) != hipSuccess ||
+      blocks < 1) {
+    (void)hipGetLastError();
+    blocks = 1;
+  }
+  blocks = blocks > 0xffff ? 0xffff : blocks;
+  if (tracked)
+    cached[dev].store((static_cast<int64_t>(lds) << 16) | blocks, std::memory_order_relaxed);
+  return blocks;
+}
+
 template <int KS, bool BITMAP, bool SILU, int YT>
 hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
                        const float* w_scale, int64_t num_experts, const int32_t* ids,
@@ -381,7 +540,17 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
   // fewer per pass so that they fit the LDS budget (the caller bounds k so one row does).
   int pass_rows = static_cast<int>(min(static_cast<int64_t>(kMaxPassRows), t));
   while (pass_rows > 1 && xs_bytes(pass_rows, k) > kMaxStageBytes) --pass_rows;
-  const size_t lds = red_bytes<WAVES>() + xs_bytes(pass_rows, k) + bitmap_bytes(num_experts);
+  // Extra rows of workgroups for experts' later passes, when experts can need more than two
+  // passes (fewer take the two-tile walk below), every id fits one scan window and the rows
+  // per expert fit LDS: at most one per pass that the assignments could fill, and 32.
+  int xrows = 0;
+  if (!BITMAP && t > 2 * pass_rows && t * topk <= kList && num_experts <= kHistMaxExperts) {
+    xrows = static_cast<int>(min(static_cast<int64_t>(kMaxExtraRows),
+                                 (t * topk + pass_rows - 1) / pass_rows));
+    xrows = static_cast<int>(min(static_cast<int64_t>(xrows), 65535 - 1 - num_experts));
+  }
+  const size_t lds = red_bytes<WAVES>() + xs_bytes(pass_rows, k) +
+                     (xrows > 0 ? hist_bytes(num_experts) : bitmap_bytes(num_experts));
   const hipError_t e = allow_dynamic_lds<kern>(static_cast<int>(lds));
   if (e != hipSuccess) return e;
   // One row of workgroups per slot, after the row that handles invalid ids: one slot per
@@ -392,20 +561,28 @@ hipError_t launch_mode(const void* x, int x_per_assignment, const int8_t* wq,
   // row scan and staged rows serve more output channels.  With fewer assignments than
   // experts (every expert has at most t rows, one pass) as many as keep about four
   // workgroups per compute unit over the grid (at most 16).  Otherwise an expert with many
-  // rows takes several passes, and walking tiles multiplies those passes in one workgroup:
-  // two tiles while no expert can need more than two passes (an expert that each token picks
-  // at most once gets at most t rows), else one (at T = 64, 2 tiles per workgroup made the
-  // 16B MoE gate projection 9 % slower and 4 tiles 1.7x slower, the shared experts' 8-pass
-  // workgroups becoming the tail; at T = 16, 2 tiles made gate and down 12-15 % faster).
+  // rows takes several passes, and walking tiles multiplies the passes of a workgroup that
+  // runs them all: two tiles while no expert can need more than two passes (an expert that
+  // each token picks at most once gets at most t rows; at T = 16 on the 16B MoE, 2 tiles
+  // made gate and down 12-15 % faster than one).  With later passes on extra rows each
+  // workgroup runs about one pass, and the walk is as long as brings the grid within one
+  // round of the workgroups that the compute units hold at once (16B MoE at T = 64: gate
+  // 80.1 -> 53.7 us, down 87.6 -> 65.1 us; a grid just past one round, or far below it, was
+  // up to 1.5x slower).
   const int64_t tiles = (n + 15) / 16;
   int64_t per = BITMAP ? tiles * slots / (4 * kCusPerGpu) : (t <= 2 * pass_rows ? 2 : 1);
+  if (xrows > 0) {
+    const int64_t fit = static_cast<int64_t>(resident_per_cu<kern>(64 * WAVES, lds)) *
+                        device_cus() / (slots + 1 + xrows);  // workgroups per grid row
+    per = fit >= 1 ? (tiles + fit - 1) / fit : kMaxTileSeq;
+  }
   if (per > kMaxTileSeq) per = kMaxTileSeq;
   const int tseq = per < 1 ? 1 : static_cast<int>(per);
   const dim3 grid(static_cast<unsigned>((tiles + tseq - 1) / tseq),
-                  static_cast<unsigned>(slots + 1));
+                  static_cast<unsigned>(slots + 1 + xrows));
   hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, stream,
                      static_cast<const uint16_t*>(x), x_per_assignment, wq, w_scale,
-                     num_experts, ids, t * topk, topk, y, n, k, pass_rows, tseq);
+                     num_experts, ids, t * topk, topk, y, n, k, pass_rows, tseq, xrows);
   return hipGetLastError();
 }
 

@@ -146,6 +146,17 @@ def test_silu_few_tokens_and_long_k(ref, dev):
     run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, False, torch.bfloat16)
 
 
+def test_silu_later_passes_split(ref, dev):
+    """More tokens than two passes of 8 rows: later passes on extra rows of workgroups."""
+    g = wl.rng(94)
+    e, n, k = 5, 24, 256
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, 2 * n, k, e)
+    ids = np.stack([g.choice(e, 2, replace=False) for _ in range(48)]).astype(np.int32)
+    ids[9, 1] = e
+    xt, xv = _bf16_rows(g, 48, k)
+    run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, False, torch.bfloat16)
+
+
 @pytest.mark.parametrize("t", wl.MOE_TOKENS)
 def test_silu_moe_16b_full(ref, dev, t):
     g = wl.rng(93 + t)

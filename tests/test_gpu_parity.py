@@ -559,6 +559,37 @@ def test_grouped_small_edge_cases(ref, dev, out_dtype):
                     out_dtype, g)
 
 
+def test_grouped_later_passes_split(ref, dev):
+    """More tokens than two passes of 8 rows: an expert's later passes go to extra rows of
+    workgroups (highest expert first, at most 32 rows), the rest stay with the expert's own
+    workgroup.  Every later pass taken by an extra row (6 experts, 40 tokens, some extra
+    rows idle), more later passes than extra rows (one expert receives every one of 300
+    tokens), later passes only on experts of two different 64-expert groups with most
+    experts empty (100 experts), and all ids beyond one scan window (no split)."""
+    g = wl.rng(25)
+    e, n, k = 6, 40, 272
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.stack([g.choice(e, 3, replace=False) for _ in range(40)]).astype(np.int32)
+    ids[3, 2] = -1
+    ids[7, 0] = e
+    for per_assign in (False, True):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, 120 if per_assign else 40, per_assign,
+                    torch.bfloat16, g)
+    e, n, k = 4, 24, 128
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.stack([np.r_[3, g.choice(3, 2, replace=False)] for _ in range(300)]).astype(np.int32)
+    run_grouped(ref, dev, qw, sw, qwr, swr, ids, 300, False, torch.float32, g)
+    e, n, k = 100, 20, 256
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.array([[99, 70, 1, g.integers(0, e)] for _ in range(40)], dtype=np.int32)
+    ids[5, 3] = -1
+    run_grouped(ref, dev, qw, sw, qwr, swr, ids, 40, False, torch.bfloat16, g)
+    e, n, k = 3, 16, 64
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.stack([g.choice(e, 3, replace=False) for _ in range(400)]).astype(np.int32)
+    run_grouped(ref, dev, qw, sw, qwr, swr, ids, 400, False, torch.bfloat16, g)
+
+
 def test_grouped_single_token_repeated_expert(ref, dev):
     """One token routed three times to one expert: the expert's rows exceed the token count
     that sizes the staged passes, so it takes several passes."""
