@@ -481,6 +481,124 @@ __attribute__((amdgpu_waves_per_eu(BITMAP ? 1 : 3))) void grouped_w8a16_kernel(
   }
 }
 
+// ---- one token (T = 1) ------------------------------------------------------------------
+// With one token every assignment is a product of one activation row with one expert's
+// matrix, and its expert is the id itself: no bitmap, no row scan, no staged rows.
+// Workgroup (4 channels, assignment p): its wavefronts read the id (one scalar load), then,
+// as the dense one-row kernel does, each lane issues every 16-byte code chunk of its
+// channel's row (SILU: the gate row and the matching up row) with the chunk's 16 bf16
+// activations beside it, expands the codes exactly to bf16, adds bf16 pairs of products
+// into a float32 sum with v_dot2_f32_bf16, the lanes' sums meet in a fixed shuffle
+// butterfly, and lane 0 applies the channel's scale (SILU: silu(g) * u as the tiled kernel
+// computes it) and stores.  Ids outside [0, num_experts) store zeros.  k <= 64 * 16 *
+// kOneTokenChunks.
+constexpr int kOneTokenChunks = 8;
+typedef short v2s __attribute__((ext_vector_type(2)));  // a bf16 pair, as the builtin takes it
+
+template <int KC, bool SILU, int YT>
+__global__ __launch_bounds__(256) void grouped_one_token_kernel(
+    const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
+    int64_t topk, void* __restrict__ y, int64_t n, int64_t k) {
+  constexpr int TILES = SILU ? 2 : 1;
+  const int lane = threadIdx.x % 64;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (c >= n) return;  // (uniform over the wavefront)
+  const int64_t p = blockIdx.y;
+  const int32_t id = __builtin_amdgcn_readfirstlane(ids[p]);
+  if (id < 0 || id >= num_experts) {
+    if (lane == 0) {
+      if constexpr (YT == I8QL_F32) {
+        static_cast<float*>(y)[p * n + c] = 0.0f;
+      } else {
+        static_cast<uint16_t*>(y)[p * n + c] = 0;
+      }
+    }
+    return;
+  }
+  const int64_t chunks = k / 16;
+  const v4u* xr = reinterpret_cast<const v4u*>(x + (x_per_assignment ? p : p / topk) * k);
+  const v4u* wr[TILES];
+#pragma unroll
+  for (int ti = 0; ti < TILES; ++ti)
+    wr[ti] = reinterpret_cast<const v4u*>(wq + ((id * TILES + ti) * n + c) * k);
+  v4u w[TILES][KC], xv[KC][2];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int64_t ch = lane + 64 * static_cast<int64_t>(i);
+    const int64_t cc = ch < chunks ? ch : 0;  // in bounds; multiplied by nothing below
+#pragma unroll
+    for (int ti = 0; ti < TILES; ++ti) w[ti][i] = wr[ti][cc];
+    xv[i][0] = xr[2 * cc];
+    xv[i][1] = xr[2 * cc + 1];
+  }
+  asm volatile("" ::: "memory");  // the loads stay here, in order, ahead of every use
+  __builtin_amdgcn_sched_barrier(0);
+  float acc[TILES] = {};
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const uint32_t in = lane + 64 * i < chunks ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ti = 0; ti < TILES; ++ti) {
+      v8bf a[2];
+      i8x16_to_bf16(w[ti][i], a[0], a[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4u xm = xv[i][h] & in;
+        const v4u av = __builtin_bit_cast(v4u, a[h]);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};  // bf16 pairs of codes
+        const uint32_t xw[4] = {xm.x, xm.y, xm.z, xm.w};  // bf16 pairs of activations
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[ti] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
+                                                    __builtin_bit_cast(v2s, xw[e]), acc[ti],
+                                                    false);
+      }
+    }
+  }
+#pragma unroll
+  for (int ti = 0; ti < TILES; ++ti)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[ti] += __shfl_xor(acc[ti], off, 64);
+  if (lane != 0) return;
+  float v = acc[0] * w_scale[(id * TILES) * n + c];
+  if constexpr (SILU) {
+    // silu(gate) * up, with silu(v) = v / (1 + exp(-v))
+    v = v / (1.0f + expf(-v)) * (acc[1] * w_scale[(id * TILES + 1) * n + c]);
+  }
+  if constexpr (YT == I8QL_F32) {
+    static_cast<float*>(y)[p * n + c] = v;
+  } else {
+    static_cast<uint16_t*>(y)[p * n + c] = f32_to_bf16_rne(v);
+  }
+}
+
+// Launches the one-token kernel when it applies (t == 1, k within its chunks); false when
+// it does not (nothing launched).
+template <bool SILU, int YT>
+bool launch_one_token(const void* x, int x_per_assignment, const int8_t* wq,
+                      const float* w_scale, int64_t num_experts, const int32_t* ids,
+                      int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
+                      hipStream_t stream, hipError_t* err) {
+  const int64_t per_lane = (k / 16 + 63) / 64;
+  if (t != 1 || per_lane > kOneTokenChunks) return false;
+  const dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(t * topk));
+  const auto* xx = static_cast<const uint16_t*>(x);
+#define I8QL_ONE(KC)                                                                       \
+  hipLaunchKernelGGL((grouped_one_token_kernel<KC, SILU, YT>), grid, dim3(256), 0, stream, \
+                     xx, x_per_assignment, wq, w_scale, num_experts, ids, topk, y, n, k)
+  if (per_lane <= 2) {
+    I8QL_ONE(2);
+  } else if (per_lane <= 4) {
+    I8QL_ONE(4);
+  } else {
+    I8QL_ONE(8);
+  }
+#undef I8QL_ONE
+  *err = hipGetLastError();
+  return true;
+}
+
 // Compute units of the current device (cached per device; kCusPerGpu when the query fails).
 int device_cus() {
   static std::atomic<int> cached[kMaxDevices];  // static storage: starts at zero
@@ -605,6 +723,10 @@ template <bool SILU, int YT>
 hipError_t launch_yt(const void* x, int x_per_assignment, const int8_t* wq,
                      const float* w_scale, int64_t num_experts, const int32_t* ids, int64_t t,
                      int64_t topk, void* y, int64_t n, int64_t k, hipStream_t stream) {
+  hipError_t err = hipSuccess;
+  if (launch_one_token<SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk,
+                                 y, n, k, stream, &err))
+    return err;
   const int64_t steps = (k + kStepK - 1) / kStepK;
   if (steps <= kUnroll)
     return launch_waves<1, SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t,

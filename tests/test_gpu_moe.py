@@ -146,6 +146,19 @@ def test_silu_few_tokens_and_long_k(ref, dev):
     run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, False, torch.bfloat16)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_silu_one_token(ref, dev, out_dtype):
+    """One token: the per-assignment kernel with gate and up rows together (ragged k), an
+    invalid id and a repeated expert."""
+    g = wl.rng(95)
+    e, n, k = 6, 36, 1040
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, 2 * n, k, e)
+    ids = np.array([[5, 2, -1, 2, 0]], dtype=np.int32)
+    for per_assign in (False, True):
+        xt, xv = _bf16_rows(g, 5 if per_assign else 1, k)
+        run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, per_assign, out_dtype)
+
+
 def test_silu_later_passes_split(ref, dev):
     """More tokens than two passes of 8 rows: later passes on extra rows of workgroups."""
     g = wl.rng(94)

@@ -559,6 +559,19 @@ def test_grouped_small_edge_cases(ref, dev, out_dtype):
                     out_dtype, g)
 
 
+@pytest.mark.parametrize("e,n,k", [(5, 30, 1040), (3, 7, 16), (4, 64, 8192), (3, 9, 8208)])
+def test_grouped_one_token(ref, dev, e, n, k):
+    """One token: the per-assignment kernel (ragged k, one chunk, its longest k, and past
+    it), with an invalid id, an out-of-range id and a repeated expert, both activation
+    layouts and both output types."""
+    g = wl.rng(26 + k)
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.array([[e - 1, -1, 0, e, 0, 1]], dtype=np.int32)
+    for per_assign, out_dtype in ((False, torch.bfloat16), (True, torch.float32)):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, 6 if per_assign else 1, per_assign,
+                    out_dtype, g)
+
+
 def test_grouped_later_passes_split(ref, dev):
     """More tokens than two passes of 8 rows: an expert's later passes go to extra rows of
     workgroups (highest expert first, at most 32 rows), the rest stay with the expert's own
