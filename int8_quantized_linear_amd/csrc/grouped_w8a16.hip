@@ -495,6 +495,27 @@ __attribute__((amdgpu_waves_per_eu(BITMAP ? 1 : 3))) void grouped_w8a16_kernel(
 constexpr int kOneTokenChunks = 8;
 typedef short v2s __attribute__((ext_vector_type(2)));  // a bf16 pair, as the builtin takes it
 
+// acc + the 16 products of a 16-byte code chunk w with its activations x[0..1] (8 bf16
+// each; masked to zero by `in` for a chunk past the row's end): the codes expand exactly to
+// bf16 and v_dot2_f32_bf16 adds each bf16 pair of products into the float32 sum, in order.
+__device__ __forceinline__ float dot_chunk(const v4u w, const v4u (&x)[2], uint32_t in,
+                                           float acc) {
+  v8bf a[2];
+  i8x16_to_bf16(w, a[0], a[1]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const v4u xm = x[h] & in;
+    const v4u av = __builtin_bit_cast(v4u, a[h]);
+    const uint32_t aw[4] = {av.x, av.y, av.z, av.w};  // bf16 pairs of codes
+    const uint32_t xw[4] = {xm.x, xm.y, xm.z, xm.w};  // bf16 pairs of activations
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
+                                            __builtin_bit_cast(v2s, xw[e]), acc, false);
+  }
+  return acc;
+}
+
 template <int KC, bool SILU, int YT>
 __global__ __launch_bounds__(256) void grouped_one_token_kernel(
     const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
@@ -539,22 +560,7 @@ __global__ __launch_bounds__(256) void grouped_one_token_kernel(
   for (int i = 0; i < KC; ++i) {
     const uint32_t in = lane + 64 * i < chunks ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int ti = 0; ti < TILES; ++ti) {
-      v8bf a[2];
-      i8x16_to_bf16(w[ti][i], a[0], a[1]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const v4u xm = xv[i][h] & in;
-        const v4u av = __builtin_bit_cast(v4u, a[h]);
-        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};  // bf16 pairs of codes
-        const uint32_t xw[4] = {xm.x, xm.y, xm.z, xm.w};  // bf16 pairs of activations
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[ti] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
-                                                    __builtin_bit_cast(v2s, xw[e]), acc[ti],
-                                                    false);
-      }
-    }
+    for (int ti = 0; ti < TILES; ++ti) acc[ti] = dot_chunk(w[ti][i], xv[i], in, acc[ti]);
   }
 #pragma unroll
   for (int ti = 0; ti < TILES; ++ti)
@@ -595,6 +601,128 @@ bool launch_one_token(const void* x, int x_per_assignment, const int8_t* wq,
     I8QL_ONE(8);
   }
 #undef I8QL_ONE
+  *err = hipGetLastError();
+  return true;
+}
+
+// ---- a few tokens (2 <= t <= kFewMaxTokens, t * topk <= 64) -----------------------------
+// With at most 64 assignments one wavefront holds every id (one load per lane), so a
+// workgroup finds its expert and that expert's rows without a bitmap, a row scan or staged
+// rows.  Workgroup (4 channels, assignment p): p's id is the expert; the workgroup runs it
+// only when p is the expert's first assignment (the lowest lane of the ballot of equal ids;
+// the expert's other workgroups exit).  Each lane issues every code chunk of its channel's
+// row (SILU: and of the matching up row) and the channel's scales once, then takes the
+// expert's rows in ascending order, one at a time: the chunks' activations, dot_chunk, the
+// shuffle butterfly, and lane 0 scales (SILU: silu(g) * u) and stores, as the one-token
+// kernel does.  An id outside [0, num_experts) stores zeros for its own assignment.
+// (Measured on the 16B MoE and dropped: four rows' activations loaded together whether or
+// not the expert has them, 1.5-1.8x slower at 1 and 4 tokens, every wavefront reading rows
+// that most experts do not have; four rows together only while four remain, 1.3x slower at
+// 4 tokens, the registers they hold costing occupancy.)
+constexpr int64_t kFewMaxTokens = 4;
+constexpr int kFewAssignments = 64;
+
+template <int KC, bool SILU, int YT>
+__global__ __launch_bounds__(256) void grouped_few_kernel(
+    const uint16_t* __restrict__ x, int x_per_assignment, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int64_t num_experts, const int32_t* __restrict__ ids,
+    int total, int64_t topk, void* __restrict__ y, int64_t n, int64_t k) {
+  constexpr int TILES = SILU ? 2 : 1;
+  const int lane = threadIdx.x % 64;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (c >= n) return;  // (uniform over the wavefront)
+  const int p = static_cast<int>(blockIdx.y);
+  const int32_t my_id = lane < total ? ids[lane] : -1;
+  const int32_t id = __builtin_amdgcn_readfirstlane(__shfl(my_id, p));
+  if (id < 0 || id >= num_experts) {
+    if (lane == 0) {
+      if constexpr (YT == I8QL_F32) {
+        static_cast<float*>(y)[p * n + c] = 0.0f;
+      } else {
+        static_cast<uint16_t*>(y)[p * n + c] = 0;
+      }
+    }
+    return;
+  }
+  uint64_t rows = __ballot(lane < total && my_id == id);  // the expert's assignments
+  if (__ffsll(static_cast<unsigned long long>(rows)) - 1 != p) return;  // not the first
+  const int64_t chunks = k / 16;
+  v4u w[TILES][KC];
+#pragma unroll
+  for (int ti = 0; ti < TILES; ++ti) {
+    const v4u* wr = reinterpret_cast<const v4u*>(wq + ((id * TILES + ti) * n + c) * k);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int64_t ch = lane + 64 * static_cast<int64_t>(i);
+      w[ti][i] = wr[ch < chunks ? ch : 0];  // in bounds; multiplied by nothing below
+    }
+  }
+  float sc[TILES];  // (loaded with the weights: read at the end, each row waited for them)
+#pragma unroll
+  for (int ti = 0; ti < TILES; ++ti) sc[ti] = w_scale[(id * TILES + ti) * n + c];
+  const int div = x_per_assignment ? 1 : static_cast<int>(topk);
+  while (rows != 0) {
+    const int r = __ffsll(static_cast<unsigned long long>(rows)) - 1;
+    rows &= rows - 1;
+    const v4u* xr = reinterpret_cast<const v4u*>(x + static_cast<int64_t>(r / div) * k);
+    v4u xv[KC][2];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int64_t ch = lane + 64 * static_cast<int64_t>(i);
+      const int64_t cc = ch < chunks ? ch : 0;
+      xv[i][0] = xr[2 * cc];
+      xv[i][1] = xr[2 * cc + 1];
+    }
+    asm volatile("" ::: "memory");  // the loads stay here, in order, ahead of every use
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[TILES] = {};
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const uint32_t in = lane + 64 * i < chunks ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int ti = 0; ti < TILES; ++ti) acc[ti] = dot_chunk(w[ti][i], xv[i], in, acc[ti]);
+    }
+#pragma unroll
+    for (int ti = 0; ti < TILES; ++ti)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc[ti] += __shfl_xor(acc[ti], off, 64);
+    if (lane != 0) continue;
+    float v = acc[0] * sc[0];
+    if constexpr (SILU) {
+      // silu(gate) * up, with silu(v) = v / (1 + exp(-v))
+      v = v / (1.0f + expf(-v)) * (acc[1] * sc[1]);
+    }
+    if constexpr (YT == I8QL_F32) {
+      static_cast<float*>(y)[r * n + c] = v;
+    } else {
+      static_cast<uint16_t*>(y)[r * n + c] = f32_to_bf16_rne(v);
+    }
+  }
+}
+
+// Launches the few-token kernel when it applies (2 <= t <= kFewMaxTokens, t * topk <= 64,
+// k within its chunks); false when it does not (nothing launched).
+template <bool SILU, int YT>
+bool launch_few(const void* x, int x_per_assignment, const int8_t* wq, const float* w_scale,
+                int64_t num_experts, const int32_t* ids, int64_t t, int64_t topk, void* y,
+                int64_t n, int64_t k, hipStream_t stream, hipError_t* err) {
+  const int64_t per_lane = (k / 16 + 63) / 64;
+  if (t < 2 || t > kFewMaxTokens || t * topk > kFewAssignments || per_lane > kOneTokenChunks)
+    return false;
+  const dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(t * topk));
+  const auto* xx = static_cast<const uint16_t*>(x);
+  const int total = static_cast<int>(t * topk);
+#define I8QL_FEW(KC)                                                                     \
+  hipLaunchKernelGGL((grouped_few_kernel<KC, SILU, YT>), grid, dim3(256), 0, stream, xx, \
+                     x_per_assignment, wq, w_scale, num_experts, ids, total, topk, y, n, k)
+  if (per_lane <= 2) {
+    I8QL_FEW(2);
+  } else if (per_lane <= 4) {
+    I8QL_FEW(4);
+  } else {
+    I8QL_FEW(8);
+  }
+#undef I8QL_FEW
   *err = hipGetLastError();
   return true;
 }
@@ -725,7 +853,9 @@ hipError_t launch_yt(const void* x, int x_per_assignment, const int8_t* wq,
                      int64_t topk, void* y, int64_t n, int64_t k, hipStream_t stream) {
   hipError_t err = hipSuccess;
   if (launch_one_token<SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk,
-                                 y, n, k, stream, &err))
+                                 y, n, k, stream, &err) ||
+      launch_few<SILU, YT>(x, x_per_assignment, wq, w_scale, num_experts, ids, t, topk, y, n,
+                           k, stream, &err))
     return err;
   const int64_t steps = (k + kStepK - 1) / kStepK;
   if (steps <= kUnroll)

@@ -159,6 +159,18 @@ def test_silu_one_token(ref, dev, out_dtype):
         run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, per_assign, out_dtype)
 
 
+def test_silu_few_tokens(ref, dev):
+    """Three tokens: the few-token kernel with gate and up rows together, an invalid id and
+    an expert shared by every token."""
+    g = wl.rng(96)
+    e, n, k = 8, 20, 1040
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, 2 * n, k, e)
+    ids = np.array([[7, 1, 4], [7, -1, 1], [7, 3, 3]], dtype=np.int32)
+    for per_assign in (False, True):
+        xt, xv = _bf16_rows(g, 9 if per_assign else 3, k)
+        run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, per_assign, torch.bfloat16)
+
+
 def test_silu_later_passes_split(ref, dev):
     """More tokens than two passes of 8 rows: later passes on extra rows of workgroups."""
     g = wl.rng(94)

@@ -572,6 +572,23 @@ def test_grouped_one_token(ref, dev, e, n, k):
                     out_dtype, g)
 
 
+@pytest.mark.parametrize("e,n,k,t,topk", [(9, 30, 1040, 3, 4), (20, 13, 8192, 4, 16),
+                                          (6, 24, 512, 2, 33), (70, 40, 2048, 4, 6)])
+def test_grouped_few_tokens(ref, dev, e, n, k, t, topk):
+    """Two to four tokens with at most 64 assignments: the few-token kernel (an expert's
+    first assignment runs all its rows); ragged k, its longest k, 64 assignments, and 66
+    (past it); invalid and out-of-range ids, an expert repeated within a token."""
+    g = wl.rng(27 + k + t)
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
+    ids = np.stack([g.choice(e, topk, replace=topk > e) for _ in range(t)]).astype(np.int32)
+    ids[0, 0] = -1
+    ids[t - 1, topk - 1] = e
+    ids[1, :2] = ids[0, 1]
+    for per_assign, out_dtype in ((False, torch.bfloat16), (True, torch.float32)):
+        run_grouped(ref, dev, qw, sw, qwr, swr, ids, t * topk if per_assign else t, per_assign,
+                    out_dtype, g)
+
+
 def test_grouped_later_passes_split(ref, dev):
     """More tokens than two passes of 8 rows: an expert's later passes go to extra rows of
     workgroups (highest expert first, at most 32 rows), the rest stay with the expert's own
