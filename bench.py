@@ -815,7 +815,7 @@ def section_counters_decode(torch, i8, wl, dev, args, result):
     result["counters_decode"] = {"calibration_copy_bytes": CALIB_BYTES, "passes": 2}
 
 
-MOE_COUNTER_TOKENS = (16, 64)
+MOE_COUNTER_TOKENS = (1, 4, 16, 64)
 
 
 def moe_traffic_workload(t):
