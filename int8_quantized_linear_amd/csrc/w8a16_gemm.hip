@@ -181,10 +181,13 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
     }
     if (vec_store && nc + 3 < n) {
       if constexpr (YT == I8QL_F32) {
-        *reinterpret_cast<v4f*>(static_cast<float*>(y) + row * n + nc) = v4f{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<v4f*>(static_cast<float*>(y) + row * n + nc) =
+            v4f{v[0], v[1], v[2], v[3]};
       } else {
-        const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+        const uint32_t lo =
+            f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+        const uint32_t hi =
+            f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + row * n + nc) = make_uint2(lo, hi);
       }
       continue;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_kernel(
 constexpr int kRowChunks = 8;
 typedef short v2s __attribute__((ext_vector_type(2)));  // a bf16 pair, as the builtin takes it
 
-template <int KC, int YT>
+template <int KC, int YT, bool GS>
 __global__ __launch_bounds__(256) void w8a16_row_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, const float* __restrict__ bias, void* __restrict__ y,
@@ -241,6 +244,17 @@ __global__ __launch_bounds__(256) void w8a16_row_kernel(
     xv[i][0] = xr[2 * cc];
     xv[i][1] = xr[2 * cc + 1];
   }
+  // GS: the scale of each chunk's group of 128 input channels (8 chunks; the 8 lanes
+  // 8j .. 8j + 7 hold one group's chunks at each i)
+  float gsc[GS ? KC : 1];
+  if constexpr (GS) {
+    const float* srow = w_scale + row * (k / 128);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int64_t c = lane + 64 * static_cast<int64_t>(i);
+      gsc[i] = srow[(c < chunks ? c : 0) / 8];
+    }
+  }
   asm volatile("" ::: "memory");  // the loads stay here, in order, ahead of every use
   __builtin_amdgcn_sched_barrier(0);
   // every chunk is multiplied (a chunk past the row's end by zero activations), so the loads
@@ -251,6 +265,7 @@ __global__ __launch_bounds__(256) void w8a16_row_kernel(
     const uint32_t in = lane + 64 * i < chunks ? 0xffffffffu : 0u;
     v8bf a[2];
     i8x16_to_bf16(w[i], a[0], a[1]);
+    float part = GS ? 0.0f : acc;  // GS: this chunk's products alone
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const v4u xm = xv[i][h] & in;
@@ -259,14 +274,24 @@ __global__ __launch_bounds__(256) void w8a16_row_kernel(
       const uint32_t xw[4] = {xm.x, xm.y, xm.z, xm.w};  // bf16 pairs of activations
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
-                                              __builtin_bit_cast(v2s, xw[e]), acc, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s, aw[e]),
+                                               __builtin_bit_cast(v2s, xw[e]), part, false);
+    }
+    if constexpr (GS) {
+      // the group's sum over its 8 lanes, times the group's scale, added by the group's
+      // first lane
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 4, 64);
+      acc += lane % 8 == 0 ? part * gsc[i] : 0.0f;
+    } else {
+      acc = part;
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane != 0) return;
-  float v = acc * w_scale[row];
+  float v = GS ? acc : acc * w_scale[row];
   if (bias) v = v + bias[row];
   if constexpr (YT == I8QL_F32) {
     static_cast<float*>(y)[row] = v;
@@ -275,15 +300,15 @@ __global__ __launch_bounds__(256) void w8a16_row_kernel(
   }
 }
 
-template <int YT>
+template <int YT, bool GS>
 bool launch_row(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                 void* y, int64_t n, int64_t k, hipStream_t stream, hipError_t* err) {
   const int64_t per_lane = (k / 16 + 63) / 64;
   const dim3 grid(static_cast<unsigned>((n + 3) / 4));
   const auto* xx = static_cast<const uint16_t*>(x);
 #define I8QL_ROW(KC)                                                                         \
-  hipLaunchKernelGGL((w8a16_row_kernel<KC, YT>), grid, dim3(256), 0, stream, xx, wq, w_scale, \
-                     bias, y, n, k)
+  hipLaunchKernelGGL((w8a16_row_kernel<KC, YT, GS>), grid, dim3(256), 0, stream, xx, wq,      \
+                     w_scale, bias, y, n, k)
   if (per_lane <= 4) {
     I8QL_ROW(4);
   } else if (per_lane <= kRowChunks) {
@@ -331,9 +356,9 @@ hipError_t launch_waves(const void* x, const int8_t* wq, const float* w_scale,
 // kUnroll steps of k (with 4 or 8, all its loads in flight at once; a wave with fewer real
 // steps than kUnroll still issues kUnroll steps of loads, so the count is matched to the
 // steps).  Longer k keeps 12 wavefronts, each walking several batches of batch_steps: 16
-// wavefronts of 1024 threads would cap the kernel at 128 registers and spill.  One 16-channel tile per workgroup: with N / 16
-// such workgroups the whole weight matrix is in flight in about one occupancy round on 256
-// CUs for the decoder shapes.
+// wavefronts of 1024 threads would cap the kernel at 128 registers and spill.  One
+// 16-channel tile per workgroup: with N / 16 such workgroups the whole weight matrix is in
+// flight in about one occupancy round on 256 CUs for the decoder shapes.
 template <int MT, int YT, bool GS>
 hipError_t launch_mt(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
                      void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
@@ -353,29 +378,36 @@ hipError_t launch_yt(const void* x, const int8_t* wq, const float* w_scale, cons
   return launch_mt<4, YT, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
 }
 
+// One activation row takes the one-row kernel when its k fits; otherwise the tiled kernel.
+template <bool GS>
+hipError_t launch_gs(const void* x, const int8_t* wq, const float* w_scale, const float* bias,
+                     void* y, i8ql_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream) {
+  if (m == 1 && kRowKernel) {
+    hipError_t err = hipSuccess;
+    const bool done =
+        y_dtype == I8QL_F32
+            ? launch_row<I8QL_F32, GS>(x, wq, w_scale, bias, y, n, k, stream, &err)
+            : launch_row<I8QL_BF16, GS>(x, wq, w_scale, bias, y, n, k, stream, &err);
+    if (done) return err;
+  }
+  if (y_dtype == I8QL_F32)
+    return launch_yt<I8QL_F32, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_yt<I8QL_BF16, GS>(x, wq, w_scale, bias, y, m, n, k, stream);
+}
+
 }  // namespace
 
 hipError_t launch_w8a16_gemm(const void* x, const int8_t* wq, const float* w_scale,
                              const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
                              int64_t n, int64_t k, hipStream_t stream) {
-  if (m == 1 && kRowKernel) {
-    hipError_t err = hipSuccess;
-    const bool done = y_dtype == I8QL_F32
-                          ? launch_row<I8QL_F32>(x, wq, w_scale, bias, y, n, k, stream, &err)
-                          : launch_row<I8QL_BF16>(x, wq, w_scale, bias, y, n, k, stream, &err);
-    if (done) return err;
-  }
-  if (y_dtype == I8QL_F32)
-    return launch_yt<I8QL_F32, false>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_yt<I8QL_BF16, false>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_gs<false>(x, wq, w_scale, bias, y, y_dtype, m, n, k, stream);
 }
 
 hipError_t launch_w8a16_gemm_g128(const void* x, const int8_t* wq, const float* w_scale,
                                   const float* bias, void* y, i8ql_dtype y_dtype, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream) {
-  if (y_dtype == I8QL_F32)
-    return launch_yt<I8QL_F32, true>(x, wq, w_scale, bias, y, m, n, k, stream);
-  return launch_yt<I8QL_BF16, true>(x, wq, w_scale, bias, y, m, n, k, stream);
+  return launch_gs<true>(x, wq, w_scale, bias, y, y_dtype, m, n, k, stream);
 }
 
 }  // namespace i8ql

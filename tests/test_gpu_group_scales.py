@@ -76,6 +76,14 @@ def test_w8a16_g128_small(ref, dev, m, n, k, out_dtype):
     run_g128(ref, dev, wl.rng(150 + m), m, n, k, m % 2 == 0, out_dtype)
 
 
+# one activation row: the one-row kernel's group-scale form (a group's 8 chunks summed
+# across 8 lanes), ragged in the last 64-chunk block, at 8 chunks per lane, and past it
+@pytest.mark.parametrize("n,k", [(7, 1152), (33, 8192), (5, 8320), (3, 128)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_w8a16_g128_one_row(ref, dev, n, k, out_dtype):
+    run_g128(ref, dev, wl.rng(170 + n), 1, n, k, True, out_dtype)
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 @pytest.mark.parametrize("n,k", [(4096, 4096), (4096, 12288)])
 def test_w8a16_g128_dense_8b_decode(ref, dev, m, n, k):
