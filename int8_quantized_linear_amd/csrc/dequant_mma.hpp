@@ -87,7 +87,7 @@ __device__ __forceinline__ void load_weight_batch(const int8_t* __restrict__ wro
 // that is 4 of 64 lanes, so the fragment reads cost a sixteenth of the LDS bandwidth.
 //
 // GS (one weight scale per step of 128 input channels, "Day 6 — Quantize It Yourself", The
-// mechanism, block 1: a scale per group of 128 weights along the input dimension): each
+// mechanism, block 1: each run of 128 consecutive input channels of a row has its own scale): each
 // step's four MFMAs go into a zeroed partial tile, which is then multiplied by the step's
 // scales of the lane's 4 channels (gs: the workgroup's LDS table [step][16 channels]) and
 // added to the accumulator; steps past s_end add nothing.

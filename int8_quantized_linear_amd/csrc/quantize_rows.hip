@@ -6,8 +6,9 @@
 // weight-only quantization", Summary: float32 arithmetic and an all-zero-channel guard).
 //
 // Work layout: one 64-lane wavefront per row, four rows per 256-thread workgroup, or, for
-// fewer than 1024 rows or rows of more than 768 chunks, a whole workgroup per row.  Pass 1 streams the row with 16-byte
-// loads (kept in registers when the row fits, up to 24 KiB per wavefront), reduces |a| to
+// fewer than 1024 rows or rows of more than 768 chunks, a whole workgroup per row.  Pass 1
+// streams the row with 16-byte loads (kept in registers when the row fits, up to 24 KiB per
+// wavefront), reduces |a| to
 // the row maximum with cross-lane shuffles (and LDS across wavefronts); pass 2 divides,
 // rounds and packs 4 or 8 codes per store.  The row is read from HBM once; the op is HBM-bound
 // (2 + 1 bytes per bf16 element).
@@ -327,8 +328,8 @@ hipError_t launch_dt(const void* a, int64_t rows, int64_t k, int8_t* q, float* s
 }
 
 // ---- one scale per group of 128 input channels ------------------------------------------
-// "Day 6 — Quantize It Yourself" (The mechanism, block 1): below per-output-channel scales
-// lies one scale per group of 128 weights along the input dimension.  The rule per group is
+// "Day 6 — Quantize It Yourself" (The mechanism, block 1): finer than one scale per output
+// channel, each run of 128 consecutive input channels of a row gets its own.  The rule per group is
 // the row rule above.  Since k is a multiple of 128, the [n, k] matrix is a plain sequence
 // of groups and the [n, k / 128] scale matrix lists them in the same order: thread i takes
 // elements 8i .. 8i + 7, sixteen consecutive lanes (one DPP row) hold one group, and the
