@@ -17,8 +17,15 @@
 // (split-K across the wavefronts, every weight load of a wave in flight at once,
 // live-row-only fragment reads, ordered reduction through LDS).  The first row of
 // workgroups collects assignments whose id is outside [0, num_experts) and writes zeros for
-// them.  A second entry point fuses the SiLU·mul between the gate/up and down projections of
-// the mixture-of-experts block: gate and up are one call over weights stacked [2n, k] per
+// them.  When experts can need more than two passes, up to 32 extra rows of workgroups take
+// the experts' later passes (numbered from the highest expert down, from the rows per expert
+// that every workgroup counts in LDS), and a workgroup walks as many tiles as bring the grid
+// within one round of resident workgroups.  One token (every assignment a single row, its
+// expert the id itself) and two to four tokens with at most 64 assignments (every id in one
+// wavefront) take kernels without the bitmap, the scan and the staged rows: a wavefront per
+// output channel streams its row of codes and meets each activation row with v_dot2.  A
+// second entry point fuses the SiLU·mul between the gate/up and down projections of the
+// mixture-of-experts block: gate and up are one call over weights stacked [2n, k] per
 // expert, each workgroup computes 16 gate and the 16 matching up channels and stores
 // silu(gate) * up (the block's activation step is a reading: no page spells it out).
 #include <hip/hip_runtime.h>
@@ -491,8 +498,8 @@ __attribute__((amdgpu_waves_per_eu(BITMAP ? 1 : 3))) void grouped_w8a16_kernel(
 // into a float32 sum with v_dot2_f32_bf16, the lanes' sums meet in a fixed shuffle
 // butterfly, and lane 0 applies the channel's scale (SILU: silu(g) * u as the tiled kernel
 // computes it) and stores.  Ids outside [0, num_experts) store zeros.  k <= 64 * 16 *
-// kOneTokenChunks.
-constexpr int kOneTokenChunks = 8;
+// kRowChunks.
+constexpr int kRowChunks = 8;
 typedef short v2s __attribute__((ext_vector_type(2)));  // a bf16 pair, as the builtin takes it
 
 // acc + the 16 products of a 16-byte code chunk w with its activations x[0..1] (8 bf16
@@ -587,7 +594,7 @@ bool launch_one_token(const void* x, int x_per_assignment, const int8_t* wq,
                       int64_t t, int64_t topk, void* y, int64_t n, int64_t k,
                       hipStream_t stream, hipError_t* err) {
   const int64_t per_lane = (k / 16 + 63) / 64;
-  if (t != 1 || per_lane > kOneTokenChunks) return false;
+  if (t != 1 || per_lane > kRowChunks) return false;
   const dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(t * topk));
   const auto* xx = static_cast<const uint16_t*>(x);
 #define I8QL_ONE(KC)                                                                       \
@@ -707,7 +714,7 @@ bool launch_few(const void* x, int x_per_assignment, const int8_t* wq, const flo
                 int64_t num_experts, const int32_t* ids, int64_t t, int64_t topk, void* y,
                 int64_t n, int64_t k, hipStream_t stream, hipError_t* err) {
   const int64_t per_lane = (k / 16 + 63) / 64;
-  if (t < 2 || t > kFewMaxTokens || t * topk > kFewAssignments || per_lane > kOneTokenChunks)
+  if (t < 2 || t > kFewMaxTokens || t * topk > kFewAssignments || per_lane > kRowChunks)
     return false;
   const dim3 grid(static_cast<unsigned>((n + 3) / 4), static_cast<unsigned>(t * topk));
   const auto* xx = static_cast<const uint16_t*>(x);
