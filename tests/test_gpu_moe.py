@@ -171,6 +171,20 @@ def test_silu_few_tokens(ref, dev):
         run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, per_assign, torch.bfloat16)
 
 
+@pytest.mark.parametrize("e,n,k,t,topk", [(20, 13, 8192, 4, 16), (6, 24, 512, 2, 33),
+                                          (9, 30, 2064, 3, 4)])
+def test_silu_few_tokens_shapes(ref, dev, e, n, k, t, topk):
+    """The few-token kernel's SiLU·mul form at its longest k (8 chunks per lane), 4 chunks,
+    64 assignments, and 66 (past it: the tiled kernel); invalid and repeated ids."""
+    g = wl.rng(97 + k)
+    qw, sw, qwr, swr = moe_stack(ref, dev, g, 2 * n, k, e)
+    ids = np.stack([g.choice(e, topk, replace=topk > e) for _ in range(t)]).astype(np.int32)
+    ids[0, 0] = -1
+    ids[1, :2] = ids[0, 1]
+    xt, xv = _bf16_rows(g, t, k)
+    run_silu(ref, dev, qw, sw, qwr, swr, ids, xt, xv, False, torch.float32)
+
+
 def test_silu_later_passes_split(ref, dev):
     """More tokens than two passes of 8 rows: later passes on extra rows of workgroups."""
     g = wl.rng(94)

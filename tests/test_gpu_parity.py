@@ -575,9 +575,9 @@ def test_grouped_one_token(ref, dev, e, n, k):
 @pytest.mark.parametrize("e,n,k,t,topk", [(9, 30, 1040, 3, 4), (20, 13, 8192, 4, 16),
                                           (6, 24, 512, 2, 33), (70, 40, 2048, 4, 6)])
 def test_grouped_few_tokens(ref, dev, e, n, k, t, topk):
-    """Two to four tokens with at most 64 assignments: the few-token kernel (an expert's
-    first assignment runs all its rows); ragged k, its longest k, 64 assignments, and 66
-    (past it); invalid and out-of-range ids, an expert repeated within a token."""
+    """Two to four tokens with at most 64 assignments (the SiLU·mul form of this call takes
+    the few-token kernel; the plain call keeps the tiled one): ragged k, a long k, 64
+    assignments and 66; invalid and out-of-range ids, an expert repeated within a token."""
     g = wl.rng(27 + k + t)
     qw, sw, qwr, swr = moe_stack(ref, dev, g, n, k, e)
     ids = np.stack([g.choice(e, topk, replace=topk > e) for _ in range(t)]).astype(np.int32)
