@@ -267,7 +267,7 @@ def test_combine_element_path(ref, dev):
 # ---------------------------------------------------------------------------------------
 # the block, chained at the 16B MoE shapes
 
-@pytest.mark.parametrize("t", [1, 16])
+@pytest.mark.parametrize("t", [1, 4, 16, 64])
 def test_moe_block_chain_16b(ref, dev, t):
     """logits -> route -> gate/up with SiLU·mul -> down -> combine, each stage against the
     oracle on the GPU's output of the stage before."""
@@ -296,6 +296,49 @@ def test_moe_block_chain_16b(ref, dev, t):
 
 # ---------------------------------------------------------------------------------------
 # the block and the group-scale path replayed from a HIP graph
+
+def test_graph_replays_of_the_grouped_row_paths_match_eager(ref, dev):
+    """The one-token kernel (plain and SiLU·mul), the few-token kernel (SiLU·mul, 3 tokens)
+    and the later-pass split with the occupancy-sized tile walk (40 tokens), captured in one
+    graph and replayed three times with eager work between the replays."""
+    g = wl.rng(171)
+    e, n_i, hid = 6, 32, 256
+    qgu, sgu, _, _ = moe_stack(ref, dev, g, 2 * n_i, hid, e)
+    qd, sd, _, _ = moe_stack(ref, dev, g, hid, n_i, e)
+    cases = []
+    for t, topk in ((1, 4), (3, 4), (40, 4)):
+        ids = torch.from_numpy(np.stack([g.choice(e, topk, replace=False)
+                                         for _ in range(t)]).astype(np.int32)).to(dev)
+        x = wl.to_bf16(wl.activations(g, t, hid)).to(dev)
+        h = torch.empty((t * topk, n_i), dtype=torch.bfloat16, device=dev)
+        d = torch.empty((t * topk, hid), dtype=torch.bfloat16, device=dev)
+        yp = torch.empty((t * topk, n_i), dtype=torch.float32, device=dev)
+        cases.append((ids, x, h, d, yp))
+
+    def path():
+        for ids, x, h, d, yp in cases:
+            i8.grouped_w8a16_silu_gemm(x, qgu, sgu, ids, out=h)
+            i8.grouped_w8a16_gemm(h, qd, sd, ids, x_per_assignment=True, out=d)
+            i8.grouped_w8a16_gemm(x, qgu[:, :n_i].contiguous(), sgu[:, :n_i].contiguous(), ids,
+                                  out_dtype=torch.float32, out=yp)
+
+    outs = [o for c in cases for o in c[2:]]
+    path()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        path()  # eager work between replays
+        torch.cuda.synchronize()
+
 
 def test_graph_replays_of_the_block_match_eager(ref, dev):
     g = wl.rng(170)
