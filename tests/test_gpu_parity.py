@@ -726,6 +726,10 @@ def test_graph_replays_match_eager(ref, dev):
 
     ys = torch.empty((96, 320), dtype=torch.float32, device=dev)
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    # one activation row: the one-row kernel, per-channel and group-128 scales
+    qg, sg = i8.quantize_per_group_int8(w)
+    y1 = torch.empty((1, 320), dtype=torch.bfloat16, device=dev)
+    y1g = torch.empty((1, 320), dtype=torch.float32, device=dev)
 
     def path():
         i8.quantize_per_token_int8(x, qx, sx)
@@ -733,12 +737,14 @@ def test_graph_replays_match_eager(ref, dev):
         i8.w8a8_gemm_with_plan(6, 4, qx, sx, qw, sw, out_dtype=torch.float32, out=ys,
                                workspace=ws)
         i8.w8a16_gemm(xd, qw, sw, out=y16)
+        i8.w8a16_gemm(xd[:1], qw, sw, out=y1)
+        i8.w8a16_gemm_g128(xd[1:2], qg, sg, out_dtype=torch.float32, out=y1g)
         i8.grouped_w8a16_gemm(xg, qe.view(5, 64, 1024), se.view(5, 64), ids,
                               out_dtype=torch.float32, out=yg)
 
     path()
     torch.cuda.synchronize()
-    outs = (qx, sx, y8, ys, y16, yg)
+    outs = (qx, sx, y8, ys, y16, y1, y1g, yg)
     eager = [t.clone() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
