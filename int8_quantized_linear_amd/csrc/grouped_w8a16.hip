@@ -626,7 +626,7 @@ bool launch_one_token(const void* x, int x_per_assignment, const int8_t* wq,
 // not the expert has them, 1.5-1.8x slower at 1 and 4 tokens, every wavefront reading rows
 // that most experts do not have; four rows together only while four remain, 1.3x slower at
 // 4 tokens, the registers they hold costing occupancy.)
-constexpr int64_t kFewMaxTokens = 4;
+constexpr int64_t kFewMaxTokens = 8;
 constexpr int kFewAssignments = 64;
 
 template <int KC, bool SILU, int YT>
@@ -712,7 +712,8 @@ __global__ __launch_bounds__(256) void grouped_few_kernel(
 // plain call keeps the tiled kernel: at 4 tokens on the 16B MoE the few-token kernel made
 // the gate, up and down layer 60.4 -> 62.7 us (each launch alone was faster, with the
 // touched weights left in the Infinity Cache between launches), while the SiLU·mul call
-// goes 41.4 -> 26.2 us and the block 75.6 -> 60.0 us.
+// goes 41.4 -> 26.2 us and the block 75.6 -> 60.0 us; the SiLU·mul call at 6 and 8 tokens
+// 50.8 -> 36.5 and 68.0 -> 49.3 us.
 template <bool SILU, int YT>
 bool launch_few(const void* x, int x_per_assignment, const int8_t* wq, const float* w_scale,
                 int64_t num_experts, const int32_t* ids, int64_t t, int64_t topk, void* y,

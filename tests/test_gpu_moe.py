@@ -172,10 +172,12 @@ def test_silu_few_tokens(ref, dev):
 
 
 @pytest.mark.parametrize("e,n,k,t,topk", [(20, 13, 8192, 4, 16), (6, 24, 512, 2, 33),
-                                          (9, 30, 2064, 3, 4)])
+                                          (9, 30, 2064, 3, 4), (40, 24, 2048, 8, 8),
+                                          (12, 20, 1040, 6, 5), (30, 16, 256, 9, 6)])
 def test_silu_few_tokens_shapes(ref, dev, e, n, k, t, topk):
     """The few-token kernel's SiLU·mul form at its longest k (8 chunks per lane), 4 chunks,
-    64 assignments, and 66 (past it: the tiled kernel); invalid and repeated ids."""
+    64 assignments, and 66 (past it: the tiled kernel); 6 and 8 tokens, and 9 (past the
+    token limit); invalid and repeated ids."""
     g = wl.rng(97 + k)
     qw, sw, qwr, swr = moe_stack(ref, dev, g, 2 * n, k, e)
     ids = np.stack([g.choice(e, topk, replace=topk > e) for _ in range(t)]).astype(np.int32)
